@@ -1,0 +1,238 @@
+"""Pins for the oracle's block, config-1 and cross-entropy evaluations (CPU).
+
+* The reparameterised (contract) evaluation with rounding switched off, in
+  float64, equals the canonical unfused evaluation (the CODA paper, §3.2.1
+  identity and the delayed-r rewrite) - forward and every gradient.
+* The canonical backward equals central finite differences of the canonical
+  forward and torch's float64 autograd.
+* Special cases reduce the block to its parts; brute-force scalar loops
+  evaluate a two-token block.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import coda_inputs as ci
+from oracle import block as ob
+from oracle import numerics as nm
+from oracle import ops
+
+TINY = ci.BlockShape(M=6, D=16, F=24, head_dim=8, seq_len=4, theta=10.0, eps=1e-6)
+
+
+def tiny_inputs(seed=0, shape=TINY):
+    rng = np.random.default_rng(seed)
+    M, D, F, hd = shape.M, shape.D, shape.F, shape.head_dim
+    n = lambda *s: rng.standard_normal(s)
+    return dict(x=n(M, D), o=n(M, D), g1=1 + 0.1 * n(D), g2=1 + 0.1 * n(D),
+                gq=1 + 0.1 * n(hd), gk=1 + 0.1 * n(hd),
+                Wqkv=n(D, 3 * D) / math.sqrt(D), Wo=n(D, D) / math.sqrt(D),
+                Wg=n(D, F) / math.sqrt(D), Wu=n(D, F) / math.sqrt(D), Wd=n(F, D) / math.sqrt(F),
+                dY=0.1 * n(M, D), dq=0.1 * n(M, D), dk=0.1 * n(M, D), dv=0.1 * n(M, D))
+
+
+def _ident(x):
+    return x
+
+
+def test_reparameterised_forward_equals_canonical():
+    P = tiny_inputs(1)
+    can = ob.block_forward_canonical(P, TINY)
+    rep = ob.block_forward_contract(P, TINY, rnd=_ident, dt=np.float64)
+    for k in ("q", "k", "v", "q_pre", "k_pre", "h1", "hg", "hu", "a", "y", "sumsq_y"):
+        np.testing.assert_allclose(rep[k], can[k], rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+def test_reparameterised_backward_equals_canonical():
+    P = tiny_inputs(2)
+    can_f = ob.block_forward_canonical(P, TINY)
+    can_b = ob.block_backward_canonical(P, can_f, TINY)
+    rep_f = ob.block_forward_contract(P, TINY, rnd=_ident, dt=np.float64)
+    rep_b = ob.block_backward_contract(P, rep_f, TINY, rnd=_ident, dt=np.float64)
+    for k in can_b:
+        np.testing.assert_allclose(rep_b[k], can_b[k], rtol=1e-11, atol=1e-12, err_msg=k)
+
+
+def _loss(P):
+    f = ob.block_forward_canonical(P, TINY)
+    return (np.sum(f["y"] * P["dY"]) + np.sum(f["q"] * P["dq"]) + np.sum(f["k"] * P["dk"])
+            + np.sum(f["v"] * P["dv"]))
+
+
+@pytest.mark.parametrize("name,grad", [("x", "dx"), ("o", "do"), ("Wqkv", "dWqkv"), ("Wo", "dWo"),
+                                       ("Wg", "dWg"), ("Wu", "dWu"), ("Wd", "dWd"), ("g1", "dg1"),
+                                       ("g2", "dg2"), ("gq", "dgq"), ("gk", "dgk")])
+def test_canonical_backward_finite_differences(name, grad):
+    P = tiny_inputs(3)
+    B = ob.block_backward_canonical(P, ob.block_forward_canonical(P, TINY), TINY)
+    rng = np.random.default_rng(11)
+    flat = P[name].reshape(-1)
+    idx = rng.choice(flat.size, size=min(flat.size, 24), replace=False)
+    h = 1e-6
+    for i in idx:
+        old = flat[i]
+        flat[i] = old + h
+        lp = _loss(P)
+        flat[i] = old - h
+        lm = _loss(P)
+        flat[i] = old
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - B[grad].reshape(-1)[i]) <= 1e-6 * (1 + abs(fd)), (name, i)
+
+
+def _torch_block(T, shape):
+    D, hd, eps = shape.D, shape.head_dim, shape.eps
+    M = T["x"].shape[0]
+    cos, sin = ops.rope_tables(shape.seq_len, hd, shape.theta)
+    pos = np.arange(M) % shape.seq_len
+    c = torch.tensor(cos[pos], dtype=torch.float64)
+    s = torch.tensor(sin[pos], dtype=torch.float64)
+
+    def rope(t):
+        v = t.reshape(M, -1, hd // 2, 2)
+        a, b = v[..., 0], v[..., 1]
+        cc, ss = c[:, None, :], s[:, None, :]
+        return torch.stack([a * cc - b * ss, a * ss + b * cc], dim=-1).reshape(M, -1)
+
+    def qkn(t, g):
+        return torch.nn.functional.rms_norm(t.reshape(M, -1, hd), (hd,), g, eps).reshape(M, -1)
+
+    rms = torch.nn.functional.rms_norm
+    qkv = rms(T["x"], (D,), T["g1"], eps) @ T["Wqkv"]
+    q = rope(qkn(qkv[:, :D], T["gq"]))
+    k = rope(qkn(qkv[:, D:2 * D], T["gk"]))
+    v = qkv[:, 2 * D:]
+    h1 = T["x"] + T["o"] @ T["Wo"]
+    xn2 = rms(h1, (D,), T["g2"], eps)
+    a = torch.nn.functional.silu(xn2 @ T["Wg"]) * (xn2 @ T["Wu"])
+    y = h1 + a @ T["Wd"]
+    return q, k, v, y
+
+
+def test_canonical_backward_matches_torch_autograd():
+    P = tiny_inputs(4)
+    B = ob.block_backward_canonical(P, ob.block_forward_canonical(P, TINY), TINY)
+    T = {k: torch.tensor(v, requires_grad=True) for k, v in P.items()}
+    q, k, v, y = _torch_block(T, TINY)
+    loss = (y * T["dY"]).sum() + (q * T["dq"]).sum() + (k * T["dk"]).sum() + (v * T["dv"]).sum()
+    loss.backward()
+    pairs = dict(dx="x", do="o", dWqkv="Wqkv", dWo="Wo", dWg="Wg", dWu="Wu", dWd="Wd",
+                 dg1="g1", dg2="g2", dgq="gq", dgk="gk")
+    for g, n in pairs.items():
+        np.testing.assert_allclose(B[g], T[n].grad.numpy(), rtol=1e-10, atol=1e-13, err_msg=g)
+
+
+def test_block_special_cases():
+    P = tiny_inputs(5)
+    P0 = dict(P, Wo=np.zeros_like(P["Wo"]))
+    f = ob.block_forward_canonical(P0, TINY)
+    assert np.array_equal(f["h1"], P["x"])
+    P1 = dict(P, Wu=np.zeros_like(P["Wu"]))
+    f = ob.block_forward_canonical(P1, TINY)
+    assert np.all(f["a"] == 0) and np.array_equal(f["y"], f["h1"])
+    f = ob.block_forward_canonical(P, TINY)
+    # rows at position 0 (rows 0 and 4 with seq_len 4) are not rotated
+    qn = ops.qk_norm(f["q_pre"], P["gq"], TINY.eps, TINY.head_dim)
+    np.testing.assert_array_equal(f["q"][[0, 4]], qn[[0, 4]])
+    assert not np.allclose(f["q"][1], qn[1])
+
+
+def test_block_brute_force_two_tokens():
+    shape = ci.BlockShape(M=2, D=4, F=3, head_dim=2, seq_len=2, theta=10.0, eps=1e-6)
+    P = tiny_inputs(6, shape)
+    f = ob.block_forward_canonical(P, shape)
+    D, F, hd, eps = 4, 3, 2, 1e-6
+    for i in range(2):
+        x = [float(v) for v in P["x"][i]]
+        r = 1 / math.sqrt(sum(v * v for v in x) / D + eps)
+        xn = [x[k] * r * P["g1"][k] for k in range(D)]
+        qkv = [sum(xn[k] * P["Wqkv"][k, j] for k in range(D)) for j in range(3 * D)]
+        out_q = []
+        for hh in range(D // hd):
+            seg = qkv[hh * hd:(hh + 1) * hd]
+            rr = 1 / math.sqrt(sum(v * v for v in seg) / hd + eps)
+            n = [seg[j] * rr * P["gq"][j] for j in range(hd)]
+            ang = i * 10.0 ** 0.0     # one pair per head: frequency theta^0 = 1
+            cs, sn = float(np.float32(math.cos(ang))), float(np.float32(math.sin(ang)))
+            out_q += [n[0] * cs - n[1] * sn, n[0] * sn + n[1] * cs]
+        np.testing.assert_allclose(f["q"][i], out_q, rtol=1e-12)
+        np.testing.assert_allclose(f["v"][i], qkv[2 * D:], rtol=1e-12)
+        h1 = [x[j] + sum(P["o"][i, k] * P["Wo"][k, j] for k in range(D)) for j in range(D)]
+        r2 = 1 / math.sqrt(sum(v * v for v in h1) / D + eps)
+        xn2 = [h1[k] * r2 * P["g2"][k] for k in range(D)]
+        hg = [sum(xn2[k] * P["Wg"][k, j] for k in range(D)) for j in range(F)]
+        hu = [sum(xn2[k] * P["Wu"][k, j] for k in range(D)) for j in range(F)]
+        a = [hg[j] / (1 + math.exp(-hg[j])) * hu[j] for j in range(F)]
+        y = [h1[j] + sum(a[k] * P["Wd"][k, j] for k in range(F)) for j in range(D)]
+        np.testing.assert_allclose(f["y"][i], y, rtol=1e-12)
+
+
+def test_contract_bf16_close_to_ideal():
+    shape = ci.BlockShape(M=64, D=256, F=320, head_dim=128, seq_len=32)
+    P = ci.block_inputs(shape, seed=0)
+    ideal_f = ob.block_forward_canonical(P, shape)
+    ideal_b = ob.block_backward_canonical(P, ideal_f, shape)
+    con_f = ob.block_forward_contract(P, shape)
+    con_b = ob.block_backward_contract(P, con_f, shape)
+    for k in ("q", "k", "v", "h1", "a", "y"):
+        d = np.abs(con_f[k] - ideal_f[k]) / (1 + np.abs(ideal_f[k]))
+        assert d.max() < 2e-2, k
+    for k in ("dWqkv", "dWo", "dWg", "dWu", "dWd", "dg1", "dg2", "dgq", "dgk", "dx", "do"):
+        rel = np.linalg.norm(con_b[k] - ideal_b[k]) / np.linalg.norm(ideal_b[k])
+        assert rel < 2e-2, (k, rel)
+
+
+def test_swiglu_config1_forms_agree():
+    s = ci.SwiGLUShape(M=8, K=64, F=32)
+    P = ci.swiglu_inputs(s, 0)
+    P64 = {k: v.astype(np.float64) for k, v in P.items()}
+    can = ob.swiglu_forward_canonical(P64["x"], P64["g"], P64["Wg"], P64["Wu"], s.eps)
+    rep = ob.swiglu_forward_contract(P64["x"], P64["g"], P64["Wg"], P64["Wu"], s.eps, rnd=_ident)
+    np.testing.assert_allclose(rep, can, rtol=1e-12, atol=1e-13)
+    con = ob.swiglu_forward_contract(P["x"], P["g"], P["Wg"], P["Wu"], s.eps)
+    assert np.all(nm.bf16(con) == con)
+    assert (np.abs(con - can) / (1 + np.abs(can))).max() < 2e-2
+
+
+def test_fp8_mm_error_bound_and_axes():
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((16, 64)).astype(np.float32)
+    A[3] *= 1e-6                       # a tiny row keeps its own scale
+    B = rng.standard_normal((64, 24)).astype(np.float32)
+    B[:, 5] *= 1e3                     # a huge column keeps its own scale
+    got = ob.mm(A, B, fp8=True)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    bound = 2 * 2.0 ** -4 * (np.abs(A).astype(np.float64) @ np.abs(B)) + 1e-30
+    assert np.all(np.abs(got - exact) <= bound * 1.01)
+    # one scale for the whole of A flushes the tiny row to zero: the bound fails
+    QA, sA = nm.quantize_e4m3(A.reshape(1, -1), axis=1)
+    QB, sB = nm.quantize_e4m3(B, axis=0)
+    whole = (QA.reshape(A.shape) @ QB) * sA[0] * sB[None, :]
+    assert np.all(whole[3] == 0) and np.any(np.abs(whole - exact) > bound * 1.01)
+
+
+def test_ce_contract_matches_canonical():
+    rng = np.random.default_rng(13)
+    h = ci.to_bf16_values(rng.standard_normal((40, 32)).astype(np.float32))
+    W = ci.to_bf16_values((rng.standard_normal((32, 300)) / math.sqrt(32)).astype(np.float32))
+    labels = rng.integers(0, 300, 40).astype(np.int32)
+    labels[[3, 17]] = -100
+    f = ob.ce_forward_contract(h, W, labels)
+    loss, per_row, lse, n, dz = ops.cross_entropy(h.astype(np.float64) @ W.astype(np.float64), labels)
+    assert f["n_valid"] == n == 38
+    assert abs(f["loss"] - loss) / loss < 1e-6
+    b = ob.ce_backward_contract(h, W, labels, f["lse"], f["n_valid"], rnd=_ident)
+    np.testing.assert_allclose(b["G"] * b["scale"], dz, atol=1e-7)
+    np.testing.assert_allclose(b["dh"], dz @ W.T.astype(np.float64), rtol=1e-4, atol=1e-7)
+    np.testing.assert_allclose(b["dW"], h.T.astype(np.float64) @ dz, rtol=1e-4, atol=1e-7)
+    assert np.all(b["dh"][[3, 17]] == 0)
+    # the tile-wise online (max, sum-exp) combine gives the same lse
+    z = f["z"].astype(np.float64)
+    m_t = ob.tile_partials(z, 64, np.max)
+    s_t = np.stack([np.sum(np.exp(z[:, t * 64:(t + 1) * 64] - m_t[t][:, None]), axis=1)
+                    for t in range(m_t.shape[0])])
+    mstar = m_t.max(axis=0)
+    lse_c = mstar + np.log(np.sum(s_t * np.exp(m_t - mstar), axis=0))
+    np.testing.assert_allclose(lse_c, ops.logsumexp_rows(z), rtol=1e-13)
