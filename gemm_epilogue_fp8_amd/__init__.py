@@ -1,0 +1,284 @@
+"""MI355X (gfx950) GEMM + epilogue library: Python binding of libcoda.so.
+
+Every function here only marshals arguments (torch tensors -> matrix
+descriptors, the current HIP stream, a cached workspace buffer) and calls
+the C ABI declared in include/coda.h; all computation runs in the library's
+HIP kernels.  There is no CPU fallback: a missing library raises.
+
+Layouts: weights are [K_in, N_out] row-major; the gate/up weight is packed
+with pack_gate_up (64-column blocks of 32 gate then 32 up columns).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Iterable, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (CODA_BF16, CODA_E4M3, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8,
+                   EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
+                   EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
+
+__all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "rope_table", "row_sumsq",
+           "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols",
+           "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
+           "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
+           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8"]
+
+
+class CodaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_lib.STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib():
+    return _lib.load()
+
+
+_DT = {torch.bfloat16: CODA_BF16, torch.float32: CODA_F32, torch.float8_e4m3fn: CODA_E4M3,
+       torch.int32: CODA_I32}
+
+
+def mat(t: Optional[torch.Tensor]) -> _lib.CodaMat:
+    """Descriptor of a 1-D (as 1 x n) or 2-D row-major tensor; None -> absent."""
+    m = _lib.CodaMat()
+    if t is None:
+        return m
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() == 1:
+        rows, cols, ld = 1, t.shape[0], t.shape[0]
+        if t.numel() > 1 and t.stride(0) != 1:
+            raise ValueError("vector must be contiguous")
+    elif t.dim() == 2:
+        rows, cols = t.shape
+        if cols > 1 and t.stride(1) != 1:
+            raise ValueError("matrix rows must be contiguous")
+        ld = t.stride(0) if rows > 1 else cols
+    else:
+        raise ValueError("only 1-D and 2-D tensors")
+    m.ptr = t.data_ptr() if t.numel() > 0 or t.data_ptr() else None
+    m.dtype, m.rows, m.cols, m.ld = _DT[t.dtype], rows, cols, ld
+    return m
+
+
+def _p(t):
+    return C.byref(mat(t)) if t is not None else None
+
+
+class Weight:
+    """A weight W [K_in, N_out] (bf16) and its optional E4M3 copies."""
+
+    def __init__(self, w: torch.Tensor, q_fwd=None, s_fwd=None, q_bwd=None, s_bwd=None):
+        self.w, self.q_fwd, self.s_fwd, self.q_bwd, self.s_bwd = w, q_fwd, s_fwd, q_bwd, s_bwd
+
+    def c(self) -> _lib.CodaWeight:
+        cw = _lib.CodaWeight()
+        cw.w = mat(self.w)
+        cw.q_fwd, cw.s_fwd = mat(self.q_fwd), mat(self.s_fwd)
+        cw.q_bwd, cw.s_bwd = mat(self.q_bwd), mat(self.s_bwd)
+        return cw
+
+    def prepare_fp8(self):
+        """Allocate and fill the per-output-channel (transposed) and
+        per-input-channel E4M3 copies (coda_quantize_weight)."""
+        K, N = self.w.shape
+        dev = self.w.device
+        self.q_fwd = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=dev)
+        self.s_fwd = torch.empty(N, dtype=torch.float32, device=dev)
+        self.q_bwd = torch.empty((K, N), dtype=torch.float8_e4m3fn, device=dev)
+        self.s_bwd = torch.empty(K, dtype=torch.float32, device=dev)
+        quantize_weight(self)
+        return self
+
+
+def _wref(w):
+    if w is None:
+        return None
+    if isinstance(w, torch.Tensor):
+        w = Weight(w)
+    return C.byref(w.c())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+_WS = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    """A per-device workspace buffer, grown on demand and reused by calls
+    that run in order on one stream."""
+    key = str(device)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def _check(st: int):
+    if st != 0:
+        raise CodaError(st, lib().coda_last_error().decode())
+
+
+def _ws_call(size_fn, size_args, device):
+    n = C.c_size_t(0)
+    _check(size_fn(*size_args, C.byref(n)))
+    if n.value == 0:
+        return None, 0
+    buf = _workspace(n.value, device)
+    return C.c_void_p(buf.data_ptr()), n.value
+
+
+# ---------------------------------------------------------------- prep
+def fold_gain(W, g, W_out):
+    _check(lib().coda_fold_gain(_p(W), _p(g), _p(W_out), _stream()))
+    return W_out
+
+
+def pack_gate_up(Wg, Wu, g, out):
+    _check(lib().coda_pack_gate_up(_p(Wg), _p(Wu), _p(g), _p(out), _stream()))
+    return out
+
+
+def rope_table(seq_len: int, out, head_dim: int = 128, theta: float = 5e5):
+    _check(lib().coda_rope_table(seq_len, head_dim, theta, _p(out), _stream()))
+    return out
+
+
+def row_sumsq(x, out):
+    _check(lib().coda_row_sumsq(_p(x), _p(out), _stream()))
+    return out
+
+
+def quantize_e4m3(X, axis: int, Q, scale):
+    ws, n = _ws_call(lib().coda_quantize_e4m3_workspace, (_p(X), axis), X.device)
+    _check(lib().coda_quantize_e4m3(_p(X), axis, _p(Q), _p(scale), ws, n, _stream()))
+    return Q, scale
+
+
+def quantize_weight(wt: Weight):
+    cw = wt.c()
+    ws, n = _ws_call(lib().coda_quantize_weight_workspace, (C.byref(cw),), wt.w.device)
+    _check(lib().coda_quantize_weight(C.byref(cw), ws, n, _stream()))
+    return wt
+
+
+def partials_cols(N: int) -> int:
+    return int(lib().coda_partials_cols(N))
+
+
+# ---------------------------------------------------------------- generic
+def gemm_epi(program: Sequence[tuple], A, transA: int, B, transB: int, D, aux: Iterable = ()):
+    """program: sequence of (opcode, slot, fparam) tuples (see coda.h)."""
+    prog = _lib.EpiProgram()
+    prog.n_ops = len(program)
+    for i, (op, slot, fparam) in enumerate(program):
+        prog.ops[i].op, prog.ops[i].slot, prog.ops[i].fparam = op, slot, fparam
+    aux = list(aux)
+    arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    _check(lib().coda_gemm_epi(C.byref(prog), _p(A), transA, _p(B), transB, _p(D),
+                               arr if aux else None, len(aux), _stream()))
+    return D
+
+
+# ---------------------------------------------------------------- forward
+def linear_swiglu_fwd(x, Wgu, eps, out, sumsq_partials=None, save_hgu=None, r_out=None,
+                      precision: int = PREC_BF16):
+    L = lib()
+    wc = Wgu if isinstance(Wgu, Weight) else Weight(Wgu)
+    M, K = x.shape
+    ws, n = _ws_call(L.coda_linear_swiglu_fwd_workspace, (M, K, int(sumsq_partials is not None), precision),
+                     x.device)
+    _check(L.coda_linear_swiglu_fwd(_p(x), _p(sumsq_partials), C.byref(wc.c()), eps, _p(out), _p(save_hgu),
+                                    _p(r_out), precision, ws, n, _stream()))
+    return out
+
+
+def linear_rmsnorm_residual_fwd(a, W, residual, out, sumsq_partials_out=None, precision: int = PREC_BF16):
+    L = lib()
+    M, K = a.shape
+    wc = W if isinstance(W, Weight) else Weight(W)
+    ws, n = _ws_call(L.coda_linear_rmsnorm_residual_fwd_workspace, (M, K, wc.w.shape[1], precision), a.device)
+    _check(L.coda_linear_rmsnorm_residual_fwd(_p(a), C.byref(wc.c()), _p(residual), _p(out),
+                                              _p(sumsq_partials_out), precision, ws, n, _stream()))
+    return out
+
+
+def linear_qknorm_rope_fwd(x, Wqkv, gq, gk, rope, seq_len, eps, q, k, v, sumsq_partials=None,
+                           save_qk_pre=None, r_out=None, precision: int = PREC_BF16):
+    L = lib()
+    M, D = x.shape
+    wc = Wqkv if isinstance(Wqkv, Weight) else Weight(Wqkv)
+    ws, n = _ws_call(L.coda_linear_qknorm_rope_fwd_workspace,
+                     (M, D, int(sumsq_partials is not None), precision), x.device)
+    _check(L.coda_linear_qknorm_rope_fwd(_p(x), _p(sumsq_partials), C.byref(wc.c()), _p(gq), _p(gk), _p(rope),
+                                         seq_len, eps, _p(q), _p(k), _p(v), _p(save_qk_pre), _p(r_out),
+                                         precision, ws, n, _stream()))
+    return q, k, v
+
+
+# ---------------------------------------------------------------- backward
+def linear_swiglu_bwd(dY, Wd, saved_hgu, r, u, Wgu, Wgu_unfolded, g, dres, du, dWgu, dg, beta=0.0,
+                      dh_gu_out=None, precision: int = PREC_BF16):
+    L = lib()
+    M, D = dY.shape
+    wd = Wd if isinstance(Wd, Weight) else Weight(Wd)
+    wgu = Wgu if isinstance(Wgu, Weight) else Weight(Wgu)
+    F = wd.w.shape[0]
+    ws, n = _ws_call(L.coda_linear_swiglu_bwd_workspace, (M, D, F, precision), dY.device)
+    _check(L.coda_linear_swiglu_bwd(_p(dY), C.byref(wd.c()), _p(saved_hgu), _p(r), _p(u), C.byref(wgu.c()),
+                                    _p(Wgu_unfolded), _p(g), _p(dres), _p(du), _p(dWgu), _p(dg), beta,
+                                    _p(dh_gu_out), precision, ws, n, _stream()))
+    return du, dWgu, dg
+
+
+def linear_rmsnorm_residual_bwd(d_out, a, W, dW, da=None, beta=0.0, precision: int = PREC_BF16):
+    L = lib()
+    M, N = d_out.shape
+    wc = W if isinstance(W, Weight) else Weight(W)
+    ws, n = _ws_call(L.coda_linear_rmsnorm_residual_bwd_workspace, (M, a.shape[1], N, precision), d_out.device)
+    _check(L.coda_linear_rmsnorm_residual_bwd(_p(d_out), _p(a), C.byref(wc.c()), _p(da), _p(dW), beta,
+                                              precision, ws, n, _stream()))
+    return da, dW
+
+
+def linear_qknorm_rope_bwd(dq, dk, dv, x, r, qk_pre, v, Wqkv, Wqkv_unfolded, g, gq, gk, rope, seq_len, eps,
+                           dres, dx, dW, dg, dgq, dgk, beta=0.0, precision: int = PREC_BF16):
+    L = lib()
+    M, D = x.shape
+    wc = Wqkv if isinstance(Wqkv, Weight) else Weight(Wqkv)
+    ws, n = _ws_call(L.coda_linear_qknorm_rope_bwd_workspace, (M, D, precision), x.device)
+    _check(L.coda_linear_qknorm_rope_bwd(_p(dq), _p(dk), _p(dv), _p(x), _p(r), _p(qk_pre), _p(v), C.byref(wc.c()),
+                                         _p(Wqkv_unfolded), _p(g), _p(gq), _p(gk), _p(rope), seq_len, eps, _p(dres),
+                                         _p(dx), _p(dW), _p(dg), _p(dgq), _p(dgk), beta, precision, ws, n,
+                                         _stream()))
+    return dx, dW, dg, dgq, dgk
+
+
+# ---------------------------------------------------------------- cross-entropy
+def linear_cross_entropy_fwd(h, W, labels, loss, lse, n_valid, per_row=None, n_bad=None, ignore_index=-100,
+                             precision: int = PREC_BF16):
+    L = lib()
+    wc = W if isinstance(W, Weight) else Weight(W)
+    ws, n = _ws_call(L.coda_linear_cross_entropy_fwd_workspace, (h.shape[0], h.shape[1], wc.w.shape[1], precision),
+                     h.device)
+    _check(L.coda_linear_cross_entropy_fwd(_p(h), C.byref(wc.c()), _p(labels), ignore_index, _p(loss), _p(lse),
+                                           _p(per_row), _p(n_valid), _p(n_bad), precision, ws, n, _stream()))
+    return loss
+
+
+def linear_cross_entropy_bwd(h, W, labels, lse, n_valid, dloss, dh, dW, beta=0.0, chunk_rows=0, ignore_index=-100,
+                             precision: int = PREC_BF16):
+    L = lib()
+    wc = W if isinstance(W, Weight) else Weight(W)
+    M, D = h.shape
+    ws, n = _ws_call(L.coda_linear_cross_entropy_bwd_workspace, (M, D, wc.w.shape[1], chunk_rows, precision),
+                     h.device)
+    _check(L.coda_linear_cross_entropy_bwd(_p(h), C.byref(wc.c()), _p(labels), ignore_index, _p(lse), _p(n_valid),
+                                           dloss, _p(dh), _p(dW), beta, chunk_rows, precision, ws, n, _stream()))
+    return dh, dW

@@ -1,0 +1,332 @@
+// Auxiliary kernels (see aux_kernels.hpp for the contract of each).
+#include "aux_kernels.hpp"
+
+namespace coda {
+
+__global__ void fold_gain_kernel(const uint16_t* W, int64_t ldw, const float* g, uint16_t* out,
+                                 int64_t ldo, int K, int N) {
+  const int k = blockIdx.y;
+  const float gk = g[k];
+  for (int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4; n < N; n += gridDim.x * blockDim.x * 4) {
+    uint2 w = *reinterpret_cast<const uint2*>(W + (int64_t)k * ldw + n);
+    uint2 o = {pack_bf2(gk * bf_lo(w.x), gk * bf_hi(w.x)), pack_bf2(gk * bf_lo(w.y), gk * bf_hi(w.y))};
+    *reinterpret_cast<uint2*>(out + (int64_t)k * ldo + n) = o;
+  }
+}
+
+__global__ void pack_gate_up_kernel(const uint16_t* Wg, int64_t ldg, const uint16_t* Wu, int64_t ldu,
+                                    const float* g, uint16_t* out, int64_t ldo, int K, int F) {
+  const int k = blockIdx.y;
+  const float gk = g ? g[k] : 1.0f;
+  const int N = 2 * F;
+  for (int n = (blockIdx.x * blockDim.x + threadIdx.x) * 4; n < N; n += gridDim.x * blockDim.x * 4) {
+    const int b = n >> 6, t = n & 63;
+    const bool up = t >= 32;
+    const int f = b * 32 + (t & 31);
+    const uint16_t* src = up ? Wu + (int64_t)k * ldu : Wg + (int64_t)k * ldg;
+    uint2 w = *reinterpret_cast<const uint2*>(src + f);
+    uint2 o = w;
+    if (g) o = uint2{pack_bf2(gk * bf_lo(w.x), gk * bf_hi(w.x)), pack_bf2(gk * bf_lo(w.y), gk * bf_hi(w.y))};
+    *reinterpret_cast<uint2*>(out + (int64_t)k * ldo + n) = o;
+  }
+}
+
+__global__ void rope_table_kernel(int seq_len, int head_dim, double theta, float* out) {
+  const int half = head_dim / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= seq_len * half) return;
+  const int p = idx / half, i = idx % half;
+  const double ang = (double)p * pow(theta, -2.0 * (double)i / (double)head_dim);
+  out[2 * idx] = (float)cos(ang);
+  out[2 * idx + 1] = (float)sin(ang);
+}
+
+__global__ void row_sumsq_kernel(const uint16_t* x, int64_t ld, int M, int K, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const uint16_t* row = x + (int64_t)m * ld;
+  float s = 0.0f;
+  for (int k = lane * 8; k < K; k += 512) {
+    uint4 w = *reinterpret_cast<const uint4*>(row + k);
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float a = bf_lo(ws[t]), b = bf_hi(ws[t]);
+      s += a * a + b * b;
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[m] = s;
+}
+
+__global__ void rows_finish_kernel(const float* P, int nP, int M, int mode, const float* rowvec,
+                                   int D, float eps, float* out) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int t = 0;
+  for (; t + 8 <= nP; t += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += P[(int64_t)(t + u) * M + m];
+  for (; t < nP; ++t) acc[0] += P[(int64_t)t * M + m];
+  float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  if (mode == 1) s = rsqrtf(s / (float)D + eps);
+  else if (mode == 2) s = rowvec[m] * s / (float)D;
+  out[m] = s;
+}
+
+__global__ void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out) {
+  // block: 64 columns x 4 partial groups
+  __shared__ float red[4][64];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int grp = threadIdx.x >> 6;
+  float s = 0.0f;
+  if (c < K)
+    for (int t = grp; t < nP; t += 4) s += P[(int64_t)t * K + c];
+  red[grp][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (grp == 0 && c < K) {
+    float v = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    out[c] = (beta != 0.0f ? beta * out[c] : 0.0f) + v;
+  }
+}
+
+__global__ void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+                                       int64_t ld_g, const uint16_t* qk_pre, int64_t ld_pre,
+                                       const uint16_t* v, int64_t ld_v, const float* r1,
+                                       const float* gq, const float* gk, const float* table,
+                                       int seq_len, float eps, int M, int D, int rows_per_wave,
+                                       uint16_t* dh, int64_t ld_dh, float* T1,
+                                       float* pgq, float* pgk) {
+  // one wave per row; lane l owns the RoPE pair (2l, 2l+1) of every head
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = D / 128;
+  const float g2[2][2] = {{gq[2 * lane], gq[2 * lane + 1]}, {gk[2 * lane], gk[2 * lane + 1]}};
+  float dgacc[2][2] = {{0, 0}, {0, 0}};
+  for (int rr = 0; rr < rows_per_wave; ++rr) {
+    const int m = (blockIdx.x * 4 + wave) * rows_per_wave + rr;
+    if (m >= M) break;
+    const float r = r1[m];
+    const int pos = m % seq_len;
+    const float cs = table[((int64_t)pos * 64 + lane) * 2], sn = table[((int64_t)pos * 64 + lane) * 2 + 1];
+    float T = 0.0f;
+#pragma unroll
+    for (int reg = 0; reg < 2; ++reg) {
+      const uint16_t* G = reg == 0 ? dq : dk;
+      for (int h = 0; h < H; ++h) {
+        const int col = h * 128 + 2 * lane;
+        uint32_t gw = *reinterpret_cast<const uint32_t*>(G + (int64_t)m * ld_g + col);
+        uint32_t pw = *reinterpret_cast<const uint32_t*>(qk_pre + (int64_t)m * ld_pre + reg * D + col);
+        const float d0 = bf_lo(gw), d1 = bf_hi(gw);
+        const float u0 = bf_lo(pw), u1 = bf_hi(pw);
+        // inverse rotation (transpose of the forward RoPE matrix)
+        const float n0 = d0 * cs + d1 * sn;
+        const float n1 = -d0 * sn + d1 * cs;
+        const float rho = rsqrtf(wave_sum(u0 * u0 + u1 * u1) / 128.0f + eps);
+        const float t0 = g2[reg][0] * n0, t1 = g2[reg][1] * n1;
+        const float st = wave_sum(u0 * t0 + u1 * t1);
+        const float k3 = rho * rho * rho / 128.0f * st;
+        const float p0 = rho * t0 - k3 * u0, p1 = rho * t1 - k3 * u1;
+        const float h0 = round_bf(r * p0), h1 = round_bf(r * p1);
+        *reinterpret_cast<uint32_t*>(dh + (int64_t)m * ld_dh + reg * D + col) = pack_bf2(h0, h1);
+        T += h0 * u0 + h1 * u1;
+        dgacc[reg][0] += rho * u0 * n0;
+        dgacc[reg][1] += rho * u1 * n1;
+      }
+    }
+    for (int col = lane * 8; col < D; col += 512) {
+      uint4 gw = *reinterpret_cast<const uint4*>(dv + (int64_t)m * ld_g + col);
+      uint4 vw = *reinterpret_cast<const uint4*>(v + (int64_t)m * ld_v + col);
+      uint32_t ga[4] = {gw.x, gw.y, gw.z, gw.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float h0 = round_bf(r * bf_lo(ga[t])), h1 = round_bf(r * bf_hi(ga[t]));
+        T += h0 * bf_lo(va[t]) + h1 * bf_hi(va[t]);
+        o[t] = pack_bf2(h0, h1);
+      }
+      *reinterpret_cast<uint4*>(dh + (int64_t)m * ld_dh + 2 * D + col) = uint4{o[0], o[1], o[2], o[3]};
+    }
+    T = wave_sum(T);
+    if (lane == 0) T1[m] = T;
+  }
+  // gain-gradient partials of this block: fixed-order sum over its 4 waves
+  __shared__ float red[4][2][128];
+  red[wave][0][2 * lane] = dgacc[0][0];
+  red[wave][0][2 * lane + 1] = dgacc[0][1];
+  red[wave][1][2 * lane] = dgacc[1][0];
+  red[wave][1][2 * lane + 1] = dgacc[1][1];
+  __syncthreads();
+  const int t = threadIdx.x;   // 256 threads: (region, column)
+  const int reg = t >> 7, cidx = t & 127;
+  float s = (red[0][reg][cidx] + red[1][reg][cidx]) + (red[2][reg][cidx] + red[3][reg][cidx]);
+  (reg == 0 ? pgq : pgk)[(int64_t)blockIdx.x * 128 + cidx] = s;
+}
+
+__device__ __forceinline__ void lse_merge_(float& m, float& s, float m2, float s2) {
+  float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
+  m = mm;
+}
+
+__global__ void ce_finish_rows_kernel(const float* Pm, const float* Ps, int nT, int M,
+                                      const float* zy, const int* labels, int V, int ignore_index,
+                                      float* lse, float* per_row, int* status) {
+  // 256 threads = 64 rows x 4 partial groups
+  __shared__ float rm[4][64], rs[4][64];
+  const int rloc = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int m = blockIdx.x * 64 + rloc;
+  float mx = -INFINITY, s = 0.0f;
+  if (m < M)
+    for (int t = grp; t < nT; t += 4) lse_merge_(mx, s, Pm[(int64_t)t * M + m], Ps[(int64_t)t * M + m]);
+  rm[grp][rloc] = mx;
+  rs[grp][rloc] = s;
+  __syncthreads();
+  if (grp == 0 && m < M) {
+    for (int g = 1; g < 4; ++g) lse_merge_(mx, s, rm[g][rloc], rs[g][rloc]);
+    const float l = mx + __logf(s);
+    lse[m] = l;
+    const int y = labels[m];
+    int st = 0;
+    float pr = 0.0f;
+    if (y == ignore_index) st = 1;
+    else if (y < 0 || y >= V) st = 2;
+    else pr = l - zy[m];
+    per_row[m] = pr;
+    status[m] = st;
+  }
+}
+
+__global__ void ce_finish_loss_kernel(const float* per_row, const int* status, int M, float* loss,
+                                      int* n_valid, int* n_bad) {
+  __shared__ float rsum[1024];
+  __shared__ int rcnt[1024], rbad[1024];
+  const int t = threadIdx.x;
+  float s = 0.0f;
+  int cnt = 0, bad = 0;
+  for (int m = t; m < M; m += blockDim.x) {
+    const int st = status[m];
+    if (st == 0) { s += per_row[m]; ++cnt; }
+    else if (st == 2) ++bad;
+  }
+  rsum[t] = s; rcnt[t] = cnt; rbad[t] = bad;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (t < w) { rsum[t] += rsum[t + w]; rcnt[t] += rcnt[t + w]; rbad[t] += rbad[t + w]; }
+    __syncthreads();
+  }
+  if (t == 0) {
+    *loss = rsum[0] / (float)rcnt[0];   // 0 / 0 = NaN for an empty batch
+    *n_valid = rcnt[0];
+    if (n_bad) *n_bad = rbad[0];
+  }
+}
+
+__global__ void ce_scale_kernel(const int* n_valid, float dloss, float* scale) {
+  const int n = *n_valid;
+  *scale = n > 0 ? dloss / (float)n : 0.0f;
+}
+
+// ---------------------------------------------------------------- fp8 quantisation
+__device__ __forceinline__ float absmax_bf2(uint32_t w, float m) {
+  return fmaxf(m, fmaxf(fabsf(bf_lo(w)), fabsf(bf_hi(w))));
+}
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+// 4 floats -> 4 E4M3 bytes (round to nearest even by the hardware convert)
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return (uint32_t)w;
+}
+
+__global__ void amax_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, float* amax) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;
+  float m = 0.0f;
+  for (int c = lane * 8; c < C; c += 512) {
+    uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, m))));
+  }
+  m = wave_max(m);
+  if (lane == 0) amax[r] = m;
+}
+
+__global__ void amax_cols_partial_kernel(const uint16_t* X, int64_t ld, int R, int C, int rows_per_block,
+                                         float* part) {
+  // thread owns 2 columns; block covers 512 columns x rows_per_block rows
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 2;
+  const int r0 = blockIdx.y * rows_per_block;
+  if (c >= C) return;
+  float m0 = 0.0f, m1 = 0.0f;
+  for (int r = r0; r < min(R, r0 + rows_per_block); ++r) {
+    uint32_t v = *reinterpret_cast<const uint32_t*>(X + (int64_t)r * ld + c);
+    m0 = fmaxf(m0, fabsf(bf_lo(v)));
+    m1 = fmaxf(m1, fabsf(bf_hi(v)));
+  }
+  part[(int64_t)blockIdx.y * C + c] = m0;
+  part[(int64_t)blockIdx.y * C + c + 1] = m1;
+}
+
+__global__ void amax_cols_finish_kernel(const float* part, int nparts, int C, float* amax) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float m = 0.0f;
+  for (int t = 0; t < nparts; ++t) m = fmaxf(m, part[(int64_t)t * C + c]);
+  amax[c] = m;
+}
+
+__global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
+                                  uint8_t* Q, int64_t ldq, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;
+  float a = amax[r];
+  if (!(a > 0.0f)) a = 448.0f;
+  const float mult = 448.0f / a;
+  if (lane == 0) scale[r] = a / 448.0f;
+  for (int c = lane * 8; c < C; c += 512) {
+    uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    uint32_t lo = cvt4_e4m3(bf_lo(w.x) * mult, bf_hi(w.x) * mult, bf_lo(w.y) * mult, bf_hi(w.y) * mult);
+    uint32_t hi = cvt4_e4m3(bf_lo(w.z) * mult, bf_hi(w.z) * mult, bf_lo(w.w) * mult, bf_hi(w.w) * mult);
+    *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + c) = uint2{lo, hi};
+  }
+}
+
+__global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
+                                    uint8_t* QT, int64_t ldq, float* scale) {
+  // 64 x 64 tile through LDS: read X[r0.., c0..] rows, write QT[c][r0..r0+63]
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 256 threads: 64 x 4
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = r0 + rr, c = c0 + tx;
+    tile[rr][tx] = (r < R && c < C) ? bf2f(X[(int64_t)r * ld + c]) : 0.0f;
+  }
+  __syncthreads();
+  // thread -> (column cc, 16 consecutive rows)
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int c = c0 + cc;
+  if (c >= C) return;
+  float a = amax[c];
+  if (!(a > 0.0f)) a = 448.0f;
+  const float mult = 448.0f / a;
+  if (blockIdx.y == 0 && part == 0) scale[c] = a / 448.0f;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = part * 16 + 4 * k;
+    w[k] = cvt4_e4m3(tile[rr][cc] * mult, tile[rr + 1][cc] * mult, tile[rr + 2][cc] * mult, tile[rr + 3][cc] * mult);
+  }
+  const int rbase = r0 + part * 16;
+  if (rbase + 16 <= R) {
+    *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
+  } else {
+    for (int k = 0; k < 16 && rbase + k < R; ++k)
+      QT[(int64_t)c * ldq + rbase + k] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+  }
+}
+
+}  // namespace coda

@@ -1,0 +1,1108 @@
+// C ABI of the GEMM+epilogue library: host-side validation, workspace
+// carving and the launch sequences of the functional entry points.  See
+// include/coda.h for the contract of every entry point.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/coda.h"
+#include "aux_kernels.hpp"
+#include "launch.hpp"
+
+using namespace coda;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+coda_status fail(coda_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define TRY(expr)                          \
+  do {                                     \
+    coda_status _s = (expr);               \
+    if (_s != CODA_OK) return _s;          \
+  } while (0)
+
+int esize(int dt) { return dt == CODA_BF16 ? 2 : dt == CODA_E4M3 ? 1 : 4; }
+int vec_elems(int dt) { return 16 / esize(dt); }
+
+bool present(const coda_mat* m) { return m != nullptr && m->ptr != nullptr; }
+
+// Checks a matrix argument.  rows/cols < 0 = any.  A 1 x n vector only needs
+// 16-byte alignment; a matrix needs cols and ld to be multiples of 16 bytes.
+coda_status check_mat(const coda_mat* m, const char* name, int dtype, int64_t rows, int64_t cols,
+                      bool optional = false) {
+  if (!present(m)) {
+    if (optional) return CODA_OK;
+    return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
+  }
+  if (m->dtype != dtype) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected %d", name, m->dtype, dtype);
+  if (m->rows < 0 || m->cols < 0) return fail(CODA_ERR_SHAPE, "%s: negative size", name);
+  if (rows >= 0 && m->rows != rows)
+    return fail(CODA_ERR_SHAPE, "%s: %lld rows, expected %lld", name, (long long)m->rows, (long long)rows);
+  if (cols >= 0 && m->cols != cols)
+    return fail(CODA_ERR_SHAPE, "%s: %lld cols, expected %lld", name, (long long)m->cols, (long long)cols);
+  if (reinterpret_cast<uintptr_t>(m->ptr) % 16 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
+  if (m->rows > 1) {
+    if (m->ld < m->cols) return fail(CODA_ERR_LAYOUT, "%s: ld %lld < cols %lld", name, (long long)m->ld, (long long)m->cols);
+    const int v = vec_elems(dtype);
+    if (m->cols % v != 0 || m->ld % v != 0)
+      return fail(CODA_ERR_LAYOUT, "%s: cols and ld must be multiples of %d elements", name, v);
+  }
+  if (m->rows > 0x7FFFFFFF || m->cols > 0x7FFFFFFF) return fail(CODA_ERR_SHAPE, "%s: too large", name);
+  return CODA_OK;
+}
+
+coda_status check_vec(const coda_mat* m, const char* name, int dtype, int64_t n, bool optional = false) {
+  TRY(check_mat(m, name, dtype, -1, -1, optional));
+  if (!present(m)) return CODA_OK;
+  if (m->rows * m->cols != n || (m->rows != 1 && m->cols != 1))
+    return fail(CODA_ERR_SHAPE, "%s: expected a vector of %lld elements", name, (long long)n);
+  return CODA_OK;
+}
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+coda_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    if (e == hipErrorInvalidValue) return fail(CODA_ERR_UNSUPPORTED, "%s: program not compiled", what);
+    return fail(CODA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  }
+  return CODA_OK;
+}
+coda_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CODA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return CODA_OK;
+}
+
+// Workspace carver: the same sequence of take() calls sizes (base == null)
+// and then carves (base != null) the caller's buffer; 256-byte alignment.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+coda_status ws_check(const Carver& c, size_t have, void* ws) {
+  if (c.off > 0 && (ws == nullptr || have < c.off))
+    return fail(CODA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", c.off, have);
+  if (ws != nullptr && reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(CODA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return CODA_OK;
+}
+
+EpiArgs epi0() {
+  EpiArgs e;
+  memset(&e, 0, sizeof(e));
+  e.alpha = 1.0f;
+  return e;
+}
+
+GemmArgs gemm_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K) {
+  GemmArgs g;
+  g.A = A; g.B = B; g.lda = lda; g.ldb = ldb;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.tiles_m = g.tiles_n = 0;
+  return g;
+}
+
+// ---------------------------------------------------------------- fp8 operand staging
+struct Q8 { uint8_t* q; float* s; int64_t ld; };
+
+// Quantise X [R, C] (bf16) along `axis` into workspace-carved buffers.
+// axis 1: Q [R, C], scale per row.  axis 0: Q^T [C, R], scale per column.
+Q8 take_q8(Carver& cv, int64_t R, int64_t C, int axis) {
+  Q8 q;
+  const int64_t rows = axis == 1 ? R : C, cols = axis == 1 ? C : R;
+  q.ld = (cols + 15) / 16 * 16;
+  q.q = cv.take<uint8_t>((size_t)rows * q.ld);
+  q.s = cv.take<float>(rows);
+  return q;
+}
+float* take_amax_ws(Carver& cv, int64_t R, int64_t C, int axis) {
+  if (axis == 1) return cv.take<float>(R);
+  const int64_t parts = (R + 255) / 256;
+  cv.take<float>(C);                       // amax
+  return cv.take<float>((size_t)parts * C);  // partials
+}
+
+coda_status run_quant(const void* X, int64_t ldx, int64_t R, int64_t C, int axis, uint8_t* Q, int64_t ldq,
+                      float* scale, float* amax, float* parts, hipStream_t s) {
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (axis == 1) {
+    hipLaunchKernelGGL(amax_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, amax);
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, amax, Q, ldq, scale);
+  } else {
+    const int rpb = 256;
+    const int nparts = (int)((R + rpb - 1) / rpb);
+    hipLaunchKernelGGL(amax_cols_partial_kernel, dim3((C / 2 + 255) / 256, nparts), dim3(256), 0, s, x, ldx,
+                       (int)R, (int)C, rpb, parts);
+    hipLaunchKernelGGL(amax_cols_finish_kernel, dim3((C + 255) / 256), dim3(256), 0, s, parts, nparts, (int)C, amax);
+    hipLaunchKernelGGL(quant_cols_t_kernel, dim3((C + 63) / 64, (R + 63) / 64), dim3(256), 0, s, x, ldx, (int)R,
+                       (int)C, amax, Q, ldq, scale);
+  }
+  return check_launch("quantize_e4m3");
+}
+
+// Activation operand of a GEMM in fp8: quantised into the workspace.
+struct ActQ {
+  Q8 q;
+  float* amax;
+  float* parts;
+};
+ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis) {
+  ActQ a;
+  a.q = take_q8(cv, R, C, axis);
+  if (axis == 1) { a.amax = cv.take<float>(R); a.parts = nullptr; }
+  else { a.amax = cv.take<float>(C); a.parts = cv.take<float>((size_t)((R + 255) / 256) * C); }
+  return a;
+}
+coda_status quant_act(const ActQ& a, const void* X, int64_t ldx, int64_t R, int64_t C, int axis, hipStream_t s) {
+  return run_quant(X, ldx, R, C, axis, a.q.q, a.q.ld, a.q.s, a.amax, a.parts, s);
+}
+
+coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int64_t N, int precision) {
+  if (!wt) return fail(CODA_ERR_NULL, "%s: NULL weight", name);
+  TRY(check_mat(&wt->w, name, CODA_BF16, K, N));
+  if (precision == CODA_PREC_FP8) {
+    TRY(check_mat(&wt->q_fwd, "q_fwd", CODA_E4M3, N, K));
+    TRY(check_vec(&wt->s_fwd, "s_fwd", CODA_F32, N));
+    TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E4M3, K, N));
+    TRY(check_vec(&wt->s_bwd, "s_bwd", CODA_F32, K));
+  } else if (precision != CODA_PREC_BF16) {
+    return fail(CODA_ERR_VALUE, "precision %d", precision);
+  }
+  return CODA_OK;
+}
+coda_status check_precision(int p) {
+  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8) return fail(CODA_ERR_VALUE, "precision %d", p);
+  return CODA_OK;
+}
+
+const float* fptr(const coda_mat* m) { return present(m) ? static_cast<const float*>(m->ptr) : nullptr; }
+
+// Forward-direction GEMM of an activation a [M, K] with a weight [K, N].
+// bf16: NN with the stored weight.  fp8: quantise a per row, NT with q_fwd.
+struct FwdOperands {
+  GemmArgs g;
+  int layout;
+  bool fp8;
+};
+
+}  // namespace
+
+// ======================================================================== misc
+extern "C" int coda_abi_version(void) { return CODA_ABI_VERSION; }
+
+extern "C" const char* coda_status_string(int st) {
+  switch (st) {
+    case CODA_OK: return "ok";
+    case CODA_ERR_NULL: return "null pointer";
+    case CODA_ERR_DTYPE: return "wrong dtype";
+    case CODA_ERR_SHAPE: return "bad shape";
+    case CODA_ERR_LAYOUT: return "bad layout";
+    case CODA_ERR_ALIGN: return "misaligned pointer";
+    case CODA_ERR_WORKSPACE: return "workspace too small";
+    case CODA_ERR_UNSUPPORTED: return "unsupported";
+    case CODA_ERR_LAUNCH: return "kernel launch failed";
+    case CODA_ERR_VALUE: return "invalid value";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* coda_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int64_t coda_partials_cols(int64_t N) { return (N + kBN - 1) / kBN; }
+
+// ======================================================================== prep
+extern "C" coda_status coda_fold_gain(const coda_mat* W, const coda_mat* g, const coda_mat* W_out, void* stream) {
+  TRY(check_mat(W, "W", CODA_BF16, -1, -1));
+  TRY(check_vec(g, "g", CODA_F32, W->rows));
+  TRY(check_mat(W_out, "W_out", CODA_BF16, W->rows, W->cols));
+  if (W->rows == 0 || W->cols == 0) return CODA_OK;
+  hipLaunchKernelGGL(fold_gain_kernel, dim3((unsigned)((W->cols / 4 + 255) / 256), (unsigned)W->rows), dim3(256), 0,
+                     S(stream), static_cast<const uint16_t*>(W->ptr), W->ld, static_cast<const float*>(g->ptr),
+                     static_cast<uint16_t*>(W_out->ptr), W_out->ld, (int)W->rows, (int)W->cols);
+  return check_launch("fold_gain");
+}
+
+extern "C" coda_status coda_pack_gate_up(const coda_mat* Wg, const coda_mat* Wu, const coda_mat* g_or_null,
+                                         const coda_mat* Wgu_out, void* stream) {
+  TRY(check_mat(Wg, "Wg", CODA_BF16, -1, -1));
+  TRY(check_mat(Wu, "Wu", CODA_BF16, Wg->rows, Wg->cols));
+  TRY(check_vec(g_or_null, "g", CODA_F32, Wg->rows, true));
+  TRY(check_mat(Wgu_out, "Wgu_out", CODA_BF16, Wg->rows, 2 * Wg->cols));
+  if (Wg->cols % 32 != 0) return fail(CODA_ERR_SHAPE, "pack_gate_up: F must be a multiple of 32");
+  if (Wg->rows == 0 || Wg->cols == 0) return CODA_OK;
+  hipLaunchKernelGGL(pack_gate_up_kernel, dim3((unsigned)((2 * Wg->cols / 4 + 255) / 256), (unsigned)Wg->rows),
+                     dim3(256), 0, S(stream), static_cast<const uint16_t*>(Wg->ptr), Wg->ld,
+                     static_cast<const uint16_t*>(Wu->ptr), Wu->ld, fptr(g_or_null),
+                     static_cast<uint16_t*>(Wgu_out->ptr), Wgu_out->ld, (int)Wg->rows, (int)Wg->cols);
+  return check_launch("pack_gate_up");
+}
+
+extern "C" coda_status coda_rope_table(int32_t seq_len, int32_t head_dim, double theta, const coda_mat* out,
+                                       void* stream) {
+  if (head_dim != 128) return fail(CODA_ERR_UNSUPPORTED, "rope_table: head_dim must be 128");
+  if (seq_len <= 0 || !(theta > 1.0)) return fail(CODA_ERR_VALUE, "rope_table: bad seq_len or theta");
+  TRY(check_mat(out, "rope", CODA_F32, seq_len, head_dim));
+  if (out->ld != head_dim) return fail(CODA_ERR_LAYOUT, "rope_table: ld must equal head_dim");
+  const int n = seq_len * head_dim / 2;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, S(stream), seq_len, head_dim, theta,
+                     static_cast<float*>(out->ptr));
+  return check_launch("rope_table");
+}
+
+static coda_status row_sumsq_launch(const void* x, int64_t ld, int64_t M, int64_t K, float* out, hipStream_t s) {
+  if (M == 0) return CODA_OK;
+  hipLaunchKernelGGL(row_sumsq_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), ld, (int)M, (int)K, out);
+  return check_launch("row_sumsq");
+}
+
+extern "C" coda_status coda_row_sumsq(const coda_mat* x, const coda_mat* out, void* stream) {
+  TRY(check_mat(x, "x", CODA_BF16, -1, -1));
+  TRY(check_vec(out, "out", CODA_F32, x->rows));
+  return row_sumsq_launch(x->ptr, x->ld, x->rows, x->cols, static_cast<float*>(out->ptr), S(stream));
+}
+
+extern "C" coda_status coda_quantize_e4m3_workspace(const coda_mat* X, int32_t axis, size_t* bytes) {
+  if (!X || !bytes) return fail(CODA_ERR_NULL, "quantize_e4m3_workspace: NULL argument");
+  if (axis != 0 && axis != 1) return fail(CODA_ERR_VALUE, "axis must be 0 or 1");
+  Carver cv(nullptr);
+  take_amax_ws(cv, X->rows, X->cols, axis);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_quantize_e4m3(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* scale,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_mat(X, "X", CODA_BF16, -1, -1));
+  if (axis != 0 && axis != 1) return fail(CODA_ERR_VALUE, "axis must be 0 or 1");
+  const int64_t R = X->rows, C = X->cols;
+  if (axis == 1) {
+    TRY(check_mat(Q, "Q", CODA_E4M3, R, C));
+    TRY(check_vec(scale, "scale", CODA_F32, R));
+  } else {
+    TRY(check_mat(Q, "Q", CODA_E4M3, C, R));
+    TRY(check_vec(scale, "scale", CODA_F32, C));
+  }
+  Carver cv(ws);
+  float* amax = nullptr;
+  float* parts = nullptr;
+  if (axis == 1) amax = cv.take<float>(R);
+  else { amax = cv.take<float>(C); parts = cv.take<float>((size_t)((R + 255) / 256) * C); }
+  TRY(ws_check(cv, ws_bytes, ws));
+  return run_quant(X->ptr, X->ld, R, C, axis, static_cast<uint8_t*>(Q->ptr), Q->ld, static_cast<float*>(scale->ptr),
+                   amax, parts, S(stream));
+}
+
+extern "C" coda_status coda_quantize_weight_workspace(const coda_weight* wt, size_t* bytes) {
+  if (!wt || !bytes) return fail(CODA_ERR_NULL, "quantize_weight_workspace: NULL argument");
+  Carver cv(nullptr);
+  const int64_t K = wt->w.rows, N = wt->w.cols;
+  cv.take<float>(std::max(K, N));
+  cv.take<float>((size_t)((K + 255) / 256) * N);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream) {
+  if (!wt) return fail(CODA_ERR_NULL, "quantize_weight: NULL weight");
+  const int64_t K = wt->w.rows, N = wt->w.cols;
+  TRY(check_weight(wt, "W", K, N, CODA_PREC_FP8));
+  Carver cv(ws);
+  float* amax = cv.take<float>(std::max(K, N));
+  float* parts = cv.take<float>((size_t)((K + 255) / 256) * N);
+  TRY(ws_check(cv, ws_bytes, ws));
+  // forward copy: contracted axis K_in -> one scale per output channel, Q^T [N, K]
+  TRY(run_quant(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
+                static_cast<float*>(wt->s_fwd.ptr), amax, parts, S(stream)));
+  // input-gradient copy: contracted axis N_out -> one scale per input channel, Q [K, N]
+  return run_quant(wt->w.ptr, wt->w.ld, K, N, 1, static_cast<uint8_t*>(wt->q_bwd.ptr), wt->q_bwd.ld,
+                   static_cast<float*>(wt->s_bwd.ptr), amax, parts, S(stream));
+}
+
+// ======================================================================== generic
+extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
+                                     const coda_mat* B, int32_t transB, const coda_mat* D, const coda_mat* aux,
+                                     uint32_t n_aux, void* stream) {
+  if (!prog) return fail(CODA_ERR_NULL, "gemm_epi: NULL program");
+  if (prog->n_ops == 0 || prog->n_ops > CODA_MAX_EPI_OPS) return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: empty or too long program");
+  TRY(check_mat(A, "A", CODA_BF16, -1, -1));
+  TRY(check_mat(B, "B", CODA_BF16, -1, -1));
+  const int64_t M = transA ? A->cols : A->rows, K = transA ? A->rows : A->cols;
+  const int64_t Kb = transB ? B->cols : B->rows, N = transB ? B->rows : B->cols;
+  if (K != Kb) return fail(CODA_ERR_SHAPE, "gemm_epi: inner sizes %lld and %lld differ", (long long)K, (long long)Kb);
+  const int layout = (transA ? 2 : 0) + (transB ? 1 : 0);
+  // decode the chain
+  const coda_epi_op* op = prog->ops;
+  const uint32_t n = prog->n_ops;
+  auto auxm = [&](uint16_t slot) -> const coda_mat* { return (aux && slot < n_aux) ? &aux[slot] : nullptr; };
+  for (uint32_t i = 0; i < n; ++i)
+    if (op[i].flags != 0) return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: op %u has flags set", i);
+  EpiArgs e = epi0();
+  e.out = D ? D->ptr : nullptr;
+  e.ld_out = D ? D->ld : 0;
+  Prog p;
+  int64_t out_cols = N;
+  int out_dtype = CODA_BF16;
+  if (n == 1 && op[0].op == CODA_EPI_STORE_BF16) {
+    p = Prog::Store;
+  } else if (n == 1 && op[0].op == CODA_EPI_ACCUM_F32) {
+    p = Prog::StoreF32; e.beta = op[0].fparam; out_dtype = CODA_F32;
+  } else if (n == 3 && op[0].op == CODA_EPI_ROW_SCALE && op[1].op == CODA_EPI_COL_SCALE && op[2].op == CODA_EPI_STORE_BF16) {
+    p = Prog::RowColStore;
+    TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
+    TRY(check_vec(auxm(op[1].slot), "col scale", CODA_F32, N));
+    e.rowvec = fptr(auxm(op[0].slot));
+    e.colvec = fptr(auxm(op[1].slot));
+  } else if ((n == 2 || n == 3) && op[0].op == CODA_EPI_ADD_TILE && op[1].op == CODA_EPI_STORE_BF16 &&
+             (n == 2 || op[2].op == CODA_EPI_ROW_SUMSQ_PARTIAL)) {
+    p = Prog::ResidSumsq;
+    TRY(check_mat(auxm(op[0].slot), "tile", CODA_BF16, M, N));
+    e.aux0 = auxm(op[0].slot)->ptr;
+    e.ld_aux0 = auxm(op[0].slot)->ld;
+    if (n == 3) {
+      TRY(check_mat(auxm(op[2].slot), "partials", CODA_F32, coda_partials_cols(N), M));
+      if (auxm(op[2].slot)->rows > 1 && auxm(op[2].slot)->ld != M)
+        return fail(CODA_ERR_LAYOUT, "gemm_epi: partials ld must be M");
+      e.partial_out = static_cast<float*>(auxm(op[2].slot)->ptr);
+    } else {
+      p = Prog::Resid;
+    }
+  } else if (n == 3 && (op[0].op == CODA_EPI_ROW_SCALE || op[0].op == CODA_EPI_ROW_RMS_FROM_PARTIALS) &&
+             op[1].op == CODA_EPI_SWIGLU && op[2].op == CODA_EPI_STORE_BF16) {
+    p = Prog::SwiGLU;
+    if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "gemm_epi: SWIGLU needs N % 64 == 0");
+    out_cols = N / 2;
+    if (op[0].op == CODA_EPI_ROW_SCALE) {
+      TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
+      e.rowvec = fptr(auxm(op[0].slot));
+    } else {
+      const coda_mat* P = auxm(op[0].slot);
+      TRY(check_mat(P, "partials", CODA_F32, -1, M));
+      if (P->rows < 1 || P->rows > RowPartials<GemmCfg<kBM, kBN, 2, 4, true, false>>::MAX_PARTIALS || P->ld != M)
+        return fail(CODA_ERR_SHAPE, "gemm_epi: partials must be [1..32, M] with ld == M");
+      e.row_partials = fptr(P);
+      e.n_row_partials = (int)P->rows;
+      e.norm_dim = (int)K;
+      e.eps = op[0].fparam;
+    }
+  } else {
+    return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: epilogue program not in the compiled set");
+  }
+  if (p != Prog::Store && p != Prog::StoreF32 && layout != LAYOUT_NN)
+    return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: this program is compiled for transA = transB = 0 only");
+  TRY(check_mat(D, "D", out_dtype, M, out_cols));
+  GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
+  return launched(launch_gemm(p, layout, false, g, e, S(stream)), "gemm_epi");
+}
+
+// ======================================================================== functional forward
+extern "C" coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, int32_t have_partials,
+                                                        int32_t precision, size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  Carver cv(nullptr);
+  if (!have_partials) cv.take<float>(M);
+  if (precision == CODA_PREC_FP8) take_act(cv, M, K, 1);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+namespace {
+// Sizes and carves what an fp8 activation operand of the forward needs.
+size_t fwd_fp8_bytes(int64_t M, int64_t K) {
+  Carver cv(nullptr);
+  take_act(cv, M, K, 1);
+  return cv.off;
+}
+}  // namespace
+
+static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, float eps,
+                                   const coda_mat* out, const coda_mat* save, const coda_mat* r_out, int precision,
+                                   void* ws, size_t ws_bytes, void* stream, bool size_only, size_t* bytes) {
+  const int64_t M = x->rows, K = x->cols, N = Wgu->w.cols, F = N / 2;
+  Carver cv(size_only ? nullptr : ws);
+  float* sumsq = present(P) ? nullptr : cv.take<float>(M);
+  ActQ aq{};
+  if (precision == CODA_PREC_FP8) aq = take_act(cv, M, K, 1);
+  if (size_only) { *bytes = cv.off; return CODA_OK; }
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  if (!present(P)) TRY(row_sumsq_launch(x->ptr, x->ld, M, K, sumsq, s));
+  EpiArgs e = epi0();
+  e.out = out->ptr; e.ld_out = out->ld;
+  if (present(save)) { e.save = save->ptr; e.ld_save = save->ld; }
+  e.row_partials = present(P) ? fptr(P) : sumsq;
+  e.n_row_partials = present(P) ? (int)P->rows : 1;
+  e.norm_dim = (int)K;
+  e.eps = eps;
+  e.rowvec_out = present(r_out) ? static_cast<float*>(r_out->ptr) : nullptr;
+  GemmArgs g;
+  int layout;
+  const bool fp8 = precision == CODA_PREC_FP8;
+  if (fp8) {
+    TRY(quant_act(aq, x->ptr, x->ld, M, K, 1, s));
+    g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, K);
+    e.rowscale = aq.q.s;
+    e.colscale = fptr(&Wgu->s_fwd);
+    layout = LAYOUT_NT;
+  } else {
+    g = gemm_args(x->ptr, x->ld, Wgu->w.ptr, Wgu->w.ld, M, N, K);
+    layout = LAYOUT_NN;
+  }
+  (void)F;
+  return launched(launch_gemm(Prog::SwiGLU, layout, fp8, g, e, s), "linear_swiglu_fwd");
+}
+
+static coda_status swiglu_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, const coda_mat* out,
+                                    const coda_mat* save, const coda_mat* r_out, int precision) {
+  TRY(check_precision(precision));
+  TRY(check_mat(x, "x", CODA_BF16, -1, -1));
+  const int64_t M = x->rows, K = x->cols;
+  if (!Wgu) return fail(CODA_ERR_NULL, "Wgu: NULL");
+  const int64_t N = Wgu->w.cols;
+  TRY(check_weight(Wgu, "Wgu", K, N, precision));
+  if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "Wgu: 2F must be a multiple of 64");
+  TRY(check_mat(P, "sumsq_partials", CODA_F32, -1, M, true));
+  if (present(P) && (P->rows < 1 || P->rows > 32 || (P->rows > 1 && P->ld != M)))
+    return fail(CODA_ERR_SHAPE, "sumsq_partials: 1..32 rows of M with ld == M");
+  TRY(check_mat(out, "out", CODA_BF16, M, N / 2));
+  TRY(check_mat(save, "save_hgu", CODA_BF16, M, N, true));
+  TRY(check_vec(r_out, "r_out", CODA_F32, M, true));
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_swiglu_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* Wgu,
+                                              float eps, const coda_mat* out, const coda_mat* save_hgu,
+                                              const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  TRY(swiglu_fwd_check(x, sumsq_partials, Wgu, out, save_hgu, r_out, precision));
+  if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
+  return swiglu_fwd_impl(x, sumsq_partials, Wgu, eps, out, save_hgu, r_out, precision, ws, ws_bytes, stream, false,
+                         nullptr);
+}
+
+extern "C" coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
+                                                                  size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  (void)N;
+  *bytes = precision == CODA_PREC_FP8 ? fwd_fp8_bytes(M, K) : 0;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weight* W, const coda_mat* residual,
+                                                        const coda_mat* out, const coda_mat* P_out, int32_t precision,
+                                                        void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  TRY(check_mat(a, "a", CODA_BF16, -1, -1));
+  const int64_t M = a->rows, K = a->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t N = W->w.cols;
+  TRY(check_weight(W, "W", K, N, precision));
+  TRY(check_mat(residual, "residual", CODA_BF16, M, N));
+  TRY(check_mat(out, "out", CODA_BF16, M, N));
+  TRY(check_mat(P_out, "sumsq_partials_out", CODA_F32, coda_partials_cols(N), M, true));
+  if (present(P_out) && P_out->rows > 1 && P_out->ld != M) return fail(CODA_ERR_LAYOUT, "partials: ld must be M");
+  Carver cv(ws);
+  ActQ aq{};
+  const bool fp8 = precision == CODA_PREC_FP8;
+  if (fp8) aq = take_act(cv, M, K, 1);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  EpiArgs e = epi0();
+  e.out = out->ptr; e.ld_out = out->ld;
+  e.aux0 = residual->ptr; e.ld_aux0 = residual->ld;
+  const Prog prog = present(P_out) ? Prog::ResidSumsq : Prog::Resid;
+  if (present(P_out)) e.partial_out = static_cast<float*>(P_out->ptr);
+  GemmArgs g;
+  int layout;
+  if (fp8) {
+    TRY(quant_act(aq, a->ptr, a->ld, M, K, 1, s));
+    g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, K);
+    e.rowscale = aq.q.s; e.colscale = fptr(&W->s_fwd);
+    layout = LAYOUT_NT;
+  } else {
+    g = gemm_args(a->ptr, a->ld, W->w.ptr, W->w.ld, M, N, K);
+    layout = LAYOUT_NN;
+  }
+  return launched(launch_gemm(prog, layout, fp8, g, e, s), "linear_rmsnorm_residual_fwd");
+}
+
+extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t D, int32_t have_partials,
+                                                             int32_t precision, size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  Carver cv(nullptr);
+  if (!have_partials) cv.take<float>(M);
+  if (precision == CODA_PREC_FP8) take_act(cv, M, D, 1);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda_mat* P, const coda_weight* Wqkv,
+                                                   const coda_mat* gq, const coda_mat* gk, const coda_mat* rope,
+                                                   int32_t seq_len, float eps, const coda_mat* q, const coda_mat* k,
+                                                   const coda_mat* v, const coda_mat* save, const coda_mat* r_out,
+                                                   int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  TRY(check_mat(x, "x", CODA_BF16, -1, -1));
+  const int64_t M = x->rows, D = x->cols;
+  if (D % 128 != 0) return fail(CODA_ERR_SHAPE, "qknorm_rope: D must be a multiple of 128");
+  if (!Wqkv) return fail(CODA_ERR_NULL, "Wqkv: NULL");
+  TRY(check_weight(Wqkv, "Wqkv", D, 3 * D, precision));
+  TRY(check_mat(P, "sumsq_partials", CODA_F32, -1, M, true));
+  if (present(P) && (P->rows < 1 || P->rows > 32 || (P->rows > 1 && P->ld != M)))
+    return fail(CODA_ERR_SHAPE, "sumsq_partials: 1..32 rows of M with ld == M");
+  TRY(check_vec(gq, "gq", CODA_F32, 128));
+  TRY(check_vec(gk, "gk", CODA_F32, 128));
+  if (seq_len <= 0) return fail(CODA_ERR_VALUE, "seq_len must be > 0");
+  TRY(check_mat(rope, "rope", CODA_F32, seq_len, 128));
+  if (rope->ld != 128) return fail(CODA_ERR_LAYOUT, "rope: ld must be 128");
+  TRY(check_mat(q, "q", CODA_BF16, M, D));
+  TRY(check_mat(k, "k", CODA_BF16, M, D));
+  TRY(check_mat(v, "v", CODA_BF16, M, D));
+  TRY(check_mat(save, "save_qk_pre", CODA_BF16, M, 2 * D, true));
+  TRY(check_vec(r_out, "r_out", CODA_F32, M, true));
+  if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
+  Carver cv(ws);
+  float* sumsq = present(P) ? nullptr : cv.take<float>(M);
+  const bool fp8 = precision == CODA_PREC_FP8;
+  ActQ aq{};
+  if (fp8) aq = take_act(cv, M, D, 1);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  if (!present(P)) TRY(row_sumsq_launch(x->ptr, x->ld, M, D, sumsq, s));
+  EpiArgs e = epi0();
+  e.out = q->ptr; e.ld_out = q->ld;
+  e.out2 = k->ptr; e.ld_out2 = k->ld;
+  e.out3 = v->ptr; e.ld_out3 = v->ld;
+  if (present(save)) { e.save = save->ptr; e.ld_save = save->ld; }
+  e.row_partials = present(P) ? fptr(P) : sumsq;
+  e.n_row_partials = present(P) ? (int)P->rows : 1;
+  e.norm_dim = (int)D;
+  e.eps = eps;
+  e.rowvec_out = present(r_out) ? static_cast<float*>(r_out->ptr) : nullptr;
+  e.colvec = fptr(gq); e.colvec2 = fptr(gk);
+  e.table = fptr(rope);
+  e.region = (int)D;
+  e.seq_len = seq_len;
+  GemmArgs g;
+  int layout;
+  if (fp8) {
+    TRY(quant_act(aq, x->ptr, x->ld, M, D, 1, s));
+    g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, D);
+    e.rowscale = aq.q.s; e.colscale = fptr(&Wqkv->s_fwd);
+    layout = LAYOUT_NT;
+  } else {
+    g = gemm_args(x->ptr, x->ld, Wqkv->w.ptr, Wqkv->w.ld, M, 3 * D, D);
+    layout = LAYOUT_NN;
+  }
+  return launched(launch_gemm(Prog::QKRope, layout, fp8, g, e, s), "linear_qknorm_rope_fwd");
+}
+
+// ======================================================================== functional backward
+namespace {
+// The two GEMM forms of a backward: input gradient (dgrad) and weight gradient (wgrad).
+//   dgrad: C[M, Kin] = G[M, Nout] W^T   (bf16: NT with the stored weight; fp8: NT with q_bwd)
+//   wgrad: C[Kin, Nout] = X^T[Kin, M] G[M, Nout]  (bf16: TN; fp8: NT with both transposed-quantised)
+struct Bwd8 {
+  ActQ grow;   // G per row (dgrad A operand)
+  ActQ xcol;   // X per column, transposed (wgrad A operand)
+  ActQ gcol;   // G per column, transposed (wgrad B operand)
+};
+}  // namespace
+
+static coda_status dgrad_args(bool fp8, const ActQ* grow, const void* G, int64_t ldG, const coda_weight* W,
+                              int64_t M, int64_t Kin, int64_t Nout, GemmArgs* g, EpiArgs* e) {
+  if (fp8) {
+    *g = gemm_args(grow->q.q, grow->q.ld, W->q_bwd.ptr, W->q_bwd.ld, M, Kin, Nout);
+    e->rowscale = grow->q.s;
+    e->colscale = fptr(&W->s_bwd);
+  } else {
+    *g = gemm_args(G, ldG, W->w.ptr, W->w.ld, M, Kin, Nout);
+  }
+  return CODA_OK;
+}
+
+static void wgrad_args(bool fp8, const Bwd8& q8, const void* X, int64_t ldX, const void* G, int64_t ldG, int64_t M,
+                       int64_t Kin, int64_t Nout, GemmArgs* g, EpiArgs* e, int* layout) {
+  if (fp8) {
+    *g = gemm_args(q8.xcol.q.q, q8.xcol.q.ld, q8.gcol.q.q, q8.gcol.q.ld, Kin, Nout, M);
+    e->rowscale = q8.xcol.q.s;
+    e->colscale = q8.gcol.q.s;
+    *layout = LAYOUT_NT;
+  } else {
+    *g = gemm_args(X, ldX, G, ldG, Kin, Nout, M);
+    *layout = LAYOUT_TN;
+  }
+}
+
+static coda_status sum_partials_launch(const float* P, int nP, int K, float beta, float* out, hipStream_t s) {
+  if (K == 0) return CODA_OK;
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((K + 63) / 64), dim3(256), 0, s, P, nP, K, beta, out);
+  return check_launch("sum_partials");
+}
+
+static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, const coda_mat* hgu, const coda_mat* r,
+                                   const coda_mat* u, const coda_weight* Wgu, const coda_mat* Wunf, const coda_mat* gvec,
+                                   const coda_mat* dres, const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg,
+                                   float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
+                                   void* stream, int64_t M, int64_t D, int64_t F, bool size_only, size_t* bytes) {
+  const int64_t N2 = 2 * F;
+  const bool fp8 = precision == CODA_PREC_FP8;
+  Carver cv(size_only ? nullptr : ws);
+  const int nT2 = (int)coda_partials_cols(F);
+  const int nTg = (int)coda_partials_cols(N2);
+  float* T2 = cv.take<float>((size_t)nT2 * M);
+  float* T2c = cv.take<float>(M);
+  float* dgp = cv.take<float>((size_t)nTg * D);
+  uint16_t* dh = present(dh_out) ? nullptr : cv.take<uint16_t>((size_t)M * N2);
+  Bwd8 q8{};
+  ActQ dYrow{};
+  if (fp8) {
+    dYrow = take_act(cv, M, D, 1);
+    q8.grow = take_act(cv, M, N2, 1);
+    q8.xcol = take_act(cv, M, D, 0);
+    q8.gcol = take_act(cv, M, N2, 0);
+  }
+  if (size_only) { *bytes = cv.off; return CODA_OK; }
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  void* dhp = present(dh_out) ? dh_out->ptr : dh;
+  const int64_t lddh = present(dh_out) ? dh_out->ld : N2;
+  // B1: da = dY Wd^T with dSwiGLU, r scale, T partials
+  {
+    EpiArgs e = epi0();
+    e.out = dhp; e.ld_out = lddh;
+    e.aux0 = hgu->ptr; e.ld_aux0 = hgu->ld;
+    e.rowvec = fptr(r);
+    e.partial_out = T2;
+    GemmArgs g;
+    if (fp8) TRY(quant_act(dYrow, dY->ptr, dY->ld, M, D, 1, s));
+    dgrad_args(fp8, &dYrow, dY->ptr, dY->ld, Wd, M, F, D, &g, &e);
+    TRY(launched(launch_gemm(Prog::DSwiGLU, LAYOUT_NT, fp8, g, e, s), "swiglu_bwd: dSwiGLU"));
+  }
+  // collapse the T partials (F / 256 of them) to one per row
+  hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, T2, nT2, (int)M, 0,
+                     (const float*)nullptr, 0, 0.0f, T2c);
+  TRY(check_launch("swiglu_bwd: finish T"));
+  if (fp8) {
+    TRY(quant_act(q8.grow, dhp, lddh, M, N2, 1, s));
+    TRY(quant_act(q8.xcol, u->ptr, u->ld, M, D, 0, s));
+    TRY(quant_act(q8.gcol, dhp, lddh, M, N2, 0, s));
+  }
+  // B3: du = dh~ W~gu^T - c u + dres
+  {
+    EpiArgs e = epi0();
+    e.out = du->ptr; e.ld_out = du->ld;
+    e.aux0 = u->ptr; e.ld_aux0 = u->ld;
+    if (present(dres)) { e.aux1 = dres->ptr; e.ld_aux1 = dres->ld; }
+    else return fail(CODA_ERR_UNSUPPORTED, "swiglu_bwd: dres is required in this build");
+    e.rowvec = fptr(r);
+    e.row_partials = T2c;
+    e.n_row_partials = 1;
+    e.norm_dim = (int)D;
+    GemmArgs g;
+    dgrad_args(fp8, &q8.grow, dhp, lddh, Wgu, M, D, N2, &g, &e);
+    TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, fp8, g, e, s), "swiglu_bwd: du"));
+  }
+  // B4: dW = beta dW + g (u^T dh~), gain partials
+  {
+    EpiArgs e = epi0();
+    e.out = dWgu->ptr; e.ld_out = dWgu->ld;
+    e.beta = beta;
+    e.aux0 = Wunf->ptr; e.ld_aux0 = Wunf->ld;
+    e.rowvec = fptr(gvec);
+    e.partial_out = dgp;
+    GemmArgs g;
+    int layout;
+    wgrad_args(fp8, q8, u->ptr, u->ld, dhp, lddh, M, D, N2, &g, &e, &layout);
+    TRY(launched(launch_gemm(Prog::WgradGain, layout, fp8, g, e, s), "swiglu_bwd: dW"));
+  }
+  return sum_partials_launch(dgp, nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
+}
+
+static coda_status swiglu_bwd_check(const coda_mat* dY, const coda_weight* Wd, const coda_mat* hgu, const coda_mat* r,
+                                    const coda_mat* u, const coda_weight* Wgu, const coda_mat* Wunf, const coda_mat* g,
+                                    const coda_mat* dres, const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg,
+                                    const coda_mat* dh_out, int precision, int64_t* M, int64_t* D, int64_t* F) {
+  TRY(check_precision(precision));
+  TRY(check_mat(dY, "dY", CODA_BF16, -1, -1));
+  *M = dY->rows; *D = dY->cols;
+  if (!Wd || !Wgu) return fail(CODA_ERR_NULL, "weights: NULL");
+  *F = Wd->w.rows;
+  if (*F % 32 != 0) return fail(CODA_ERR_SHAPE, "F must be a multiple of 32");
+  TRY(check_weight(Wd, "Wd", *F, *D, precision));
+  TRY(check_weight(Wgu, "Wgu", *D, 2 * *F, precision));
+  TRY(check_mat(hgu, "saved_hgu", CODA_BF16, *M, 2 * *F));
+  TRY(check_vec(r, "r", CODA_F32, *M));
+  TRY(check_mat(u, "u", CODA_BF16, *M, *D));
+  TRY(check_mat(Wunf, "Wgu_unfolded", CODA_BF16, *D, 2 * *F));
+  TRY(check_vec(g, "g", CODA_F32, *D));
+  TRY(check_mat(dres, "dres", CODA_BF16, *M, *D));
+  TRY(check_mat(du, "du", CODA_BF16, *M, *D));
+  TRY(check_mat(dWgu, "dWgu", CODA_F32, *D, 2 * *F));
+  TRY(check_vec(dg, "dg", CODA_F32, *D));
+  TRY(check_mat(dh_out, "dh_gu_out", CODA_BF16, *M, 2 * *F, true));
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_swiglu_bwd_workspace(int64_t M, int64_t D, int64_t F, int32_t precision,
+                                                        size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  return swiglu_bwd_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, 0.0f, nullptr, precision, nullptr, 0, nullptr, M, D, F, true, bytes);
+}
+
+extern "C" coda_status coda_linear_swiglu_bwd(const coda_mat* dY, const coda_weight* Wd, const coda_mat* saved_hgu,
+                                              const coda_mat* r, const coda_mat* u, const coda_weight* Wgu,
+                                              const coda_mat* Wgu_unfolded, const coda_mat* g, const coda_mat* dres,
+                                              const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg, float beta,
+                                              const coda_mat* dh_gu_out, int32_t precision, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  int64_t M, D, F;
+  TRY(swiglu_bwd_check(dY, Wd, saved_hgu, r, u, Wgu, Wgu_unfolded, g, dres, du, dWgu, dg, dh_gu_out, precision, &M,
+                       &D, &F));
+  return swiglu_bwd_impl(dY, Wd, saved_hgu, r, u, Wgu, Wgu_unfolded, g, dres, du, dWgu, dg, beta, dh_gu_out,
+                         precision, ws, ws_bytes, stream, M, D, F, false, nullptr);
+}
+
+extern "C" coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
+                                                                  size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  Carver cv(nullptr);
+  if (precision == CODA_PREC_FP8) {
+    take_act(cv, M, N, 1);
+    take_act(cv, M, K, 0);
+    take_act(cv, M, N, 0);
+  }
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, const coda_mat* a, const coda_weight* W,
+                                                        const coda_mat* da, const coda_mat* dW, float beta,
+                                                        int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  TRY(check_mat(d_out, "d_out", CODA_BF16, -1, -1));
+  const int64_t M = d_out->rows, N = d_out->cols;
+  TRY(check_mat(a, "a", CODA_BF16, M, -1));
+  const int64_t K = a->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  TRY(check_weight(W, "W", K, N, precision));
+  TRY(check_mat(da, "da", CODA_BF16, M, K, true));
+  TRY(check_mat(dW, "dW", CODA_F32, K, N));
+  const bool fp8 = precision == CODA_PREC_FP8;
+  Carver cv(ws);
+  Bwd8 q8{};
+  if (fp8) {
+    q8.grow = take_act(cv, M, N, 1);
+    q8.xcol = take_act(cv, M, K, 0);
+    q8.gcol = take_act(cv, M, N, 0);
+  }
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  if (fp8) {
+    if (present(da)) TRY(quant_act(q8.grow, d_out->ptr, d_out->ld, M, N, 1, s));
+    TRY(quant_act(q8.xcol, a->ptr, a->ld, M, K, 0, s));
+    TRY(quant_act(q8.gcol, d_out->ptr, d_out->ld, M, N, 0, s));
+  }
+  if (present(da)) {
+    EpiArgs e = epi0();
+    e.out = da->ptr; e.ld_out = da->ld;
+    GemmArgs g;
+    dgrad_args(fp8, &q8.grow, d_out->ptr, d_out->ld, W, M, K, N, &g, &e);
+    TRY(launched(launch_gemm(Prog::Store, LAYOUT_NT, fp8, g, e, s), "rmsnorm_residual_bwd: da"));
+  }
+  EpiArgs e = epi0();
+  e.out = dW->ptr; e.ld_out = dW->ld;
+  e.beta = beta;
+  GemmArgs g;
+  int layout;
+  wgrad_args(fp8, q8, a->ptr, a->ld, d_out->ptr, d_out->ld, M, K, N, &g, &e, &layout);
+  return launched(launch_gemm(Prog::StoreF32, layout, fp8, g, e, s), "rmsnorm_residual_bwd: dW");
+}
+
+static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv, const coda_mat* x,
+                               const coda_mat* r, const coda_mat* qk_pre, const coda_mat* v, const coda_weight* Wqkv,
+                               const coda_mat* Wunf, const coda_mat* gvec, const coda_mat* gq, const coda_mat* gk,
+                               const coda_mat* rope, int seq_len, float eps, const coda_mat* dres, const coda_mat* dx,
+                               const coda_mat* dW, const coda_mat* dg, const coda_mat* dgq, const coda_mat* dgk,
+                               float beta, int precision, void* ws, size_t ws_bytes, void* stream, int64_t M,
+                               int64_t D, bool size_only, size_t* bytes) {
+  const bool fp8 = precision == CODA_PREC_FP8;
+  const int64_t N3 = 3 * D;
+  const int rows_per_wave = 4;
+  const int nblk = (int)((M + 4 * rows_per_wave - 1) / (4 * rows_per_wave));
+  Carver cv(size_only ? nullptr : ws);
+  uint16_t* dh = cv.take<uint16_t>((size_t)M * N3);
+  float* T1 = cv.take<float>(M);
+  float* pgq = cv.take<float>((size_t)std::max(nblk, 1) * 128);
+  float* pgk = cv.take<float>((size_t)std::max(nblk, 1) * 128);
+  const int nTg = (int)coda_partials_cols(N3);
+  float* dgp = cv.take<float>((size_t)nTg * D);
+  Bwd8 q8{};
+  if (fp8) {
+    q8.grow = take_act(cv, M, N3, 1);
+    q8.xcol = take_act(cv, M, D, 0);
+    q8.gcol = take_act(cv, M, N3, 0);
+  }
+  if (size_only) { *bytes = cv.off; return CODA_OK; }
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  if (M > 0) {
+    hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(nblk), dim3(256), 0, s, static_cast<const uint16_t*>(dq->ptr),
+                       static_cast<const uint16_t*>(dk->ptr), static_cast<const uint16_t*>(dv->ptr), dq->ld,
+                       static_cast<const uint16_t*>(qk_pre->ptr), qk_pre->ld, static_cast<const uint16_t*>(v->ptr),
+                       v->ld, fptr(r), fptr(gq), fptr(gk), fptr(rope), seq_len, eps, (int)M, (int)D, rows_per_wave,
+                       dh, N3, T1, pgq, pgk);
+    TRY(check_launch("qknorm_rope_bwd: glue"));
+  }
+  TRY(sum_partials_launch(pgq, nblk, 128, beta, static_cast<float*>(dgq->ptr), s));
+  TRY(sum_partials_launch(pgk, nblk, 128, beta, static_cast<float*>(dgk->ptr), s));
+  if (fp8) {
+    TRY(quant_act(q8.grow, dh, N3, M, N3, 1, s));
+    TRY(quant_act(q8.xcol, x->ptr, x->ld, M, D, 0, s));
+    TRY(quant_act(q8.gcol, dh, N3, M, N3, 0, s));
+  }
+  {
+    EpiArgs e = epi0();
+    e.out = dx->ptr; e.ld_out = dx->ld;
+    e.aux0 = x->ptr; e.ld_aux0 = x->ld;
+    e.aux1 = dres->ptr; e.ld_aux1 = dres->ld;
+    e.rowvec = fptr(r);
+    e.row_partials = T1;
+    e.n_row_partials = 1;
+    e.norm_dim = (int)D;
+    GemmArgs g;
+    dgrad_args(fp8, &q8.grow, dh, N3, Wqkv, M, D, N3, &g, &e);
+    TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, fp8, g, e, s), "qknorm_rope_bwd: dx"));
+  }
+  {
+    EpiArgs e = epi0();
+    e.out = dW->ptr; e.ld_out = dW->ld;
+    e.beta = beta;
+    e.aux0 = Wunf->ptr; e.ld_aux0 = Wunf->ld;
+    e.rowvec = fptr(gvec);
+    e.partial_out = dgp;
+    GemmArgs g;
+    int layout;
+    wgrad_args(fp8, q8, x->ptr, x->ld, dh, N3, M, D, N3, &g, &e, &layout);
+    TRY(launched(launch_gemm(Prog::WgradGain, layout, fp8, g, e, s), "qknorm_rope_bwd: dW"));
+  }
+  return sum_partials_launch(dgp, nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
+}
+
+extern "C" coda_status coda_linear_qknorm_rope_bwd_workspace(int64_t M, int64_t D, int32_t precision, size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  return qk_bwd_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, 1, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, precision,
+                     nullptr, 0, nullptr, M, D, true, bytes);
+}
+
+extern "C" coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv,
+                                                   const coda_mat* x, const coda_mat* r, const coda_mat* qk_pre,
+                                                   const coda_mat* v, const coda_weight* Wqkv, const coda_mat* Wunf,
+                                                   const coda_mat* g, const coda_mat* gq, const coda_mat* gk,
+                                                   const coda_mat* rope, int32_t seq_len, float eps, const coda_mat* dres,
+                                                   const coda_mat* dx, const coda_mat* dW, const coda_mat* dg,
+                                                   const coda_mat* dgq, const coda_mat* dgk, float beta,
+                                                   int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  TRY(check_mat(x, "x", CODA_BF16, -1, -1));
+  const int64_t M = x->rows, D = x->cols;
+  if (D % 128 != 0) return fail(CODA_ERR_SHAPE, "D must be a multiple of 128");
+  TRY(check_mat(dq, "dq", CODA_BF16, M, D));
+  TRY(check_mat(dk, "dk", CODA_BF16, M, D));
+  TRY(check_mat(dv, "dv", CODA_BF16, M, D));
+  if (dk->ld != dq->ld || dv->ld != dq->ld) return fail(CODA_ERR_LAYOUT, "dq, dk, dv must share ld");
+  TRY(check_vec(r, "r", CODA_F32, M));
+  TRY(check_mat(qk_pre, "qk_pre", CODA_BF16, M, 2 * D));
+  TRY(check_mat(v, "v", CODA_BF16, M, D));
+  if (!Wqkv) return fail(CODA_ERR_NULL, "Wqkv: NULL");
+  TRY(check_weight(Wqkv, "Wqkv", D, 3 * D, precision));
+  TRY(check_mat(Wunf, "Wqkv_unfolded", CODA_BF16, D, 3 * D));
+  TRY(check_vec(g, "g", CODA_F32, D));
+  TRY(check_vec(gq, "gq", CODA_F32, 128));
+  TRY(check_vec(gk, "gk", CODA_F32, 128));
+  if (seq_len <= 0) return fail(CODA_ERR_VALUE, "seq_len must be > 0");
+  TRY(check_mat(rope, "rope", CODA_F32, seq_len, 128));
+  TRY(check_mat(dres, "dres", CODA_BF16, M, D));
+  TRY(check_mat(dx, "dx", CODA_BF16, M, D));
+  TRY(check_mat(dW, "dW", CODA_F32, D, 3 * D));
+  TRY(check_vec(dg, "dg", CODA_F32, D));
+  TRY(check_vec(dgq, "dgq", CODA_F32, 128));
+  TRY(check_vec(dgk, "dgk", CODA_F32, 128));
+  return qk_bwd_impl(dq, dk, dv, x, r, qk_pre, v, Wqkv, Wunf, g, gq, gk, rope, seq_len, eps, dres, dx, dW, dg, dgq, dgk,
+                     beta, precision, ws, ws_bytes, stream, M, D, false, nullptr);
+}
+
+// ======================================================================== cross-entropy
+static size_t ce_fwd_layout(Carver& cv, int64_t M, int64_t V, int64_t D, int precision, float** Pm, float** Ps,
+                            float** zy, float** per_row, int** status, ActQ* aq) {
+  const int nT = (int)coda_partials_cols(V);
+  *Pm = cv.take<float>((size_t)nT * M);
+  *Ps = cv.take<float>((size_t)nT * M);
+  *zy = cv.take<float>(M);
+  *per_row = cv.take<float>(M);
+  *status = cv.take<int>(M);
+  if (precision == CODA_PREC_FP8) *aq = take_act(cv, M, D, 1);
+  return cv.off;
+}
+
+extern "C" coda_status coda_linear_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t precision,
+                                                               size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  Carver cv(nullptr);
+  float *a, *b, *c, *d;
+  int* st;
+  ActQ aq;
+  ce_fwd_layout(cv, M, V, D, precision, &a, &b, &c, &d, &st, &aq);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
+                                                     int32_t ignore_index, const coda_mat* loss, const coda_mat* lse,
+                                                     const coda_mat* per_row, const coda_mat* n_valid,
+                                                     const coda_mat* n_bad, int32_t precision, void* ws,
+                                                     size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  TRY(check_mat(h, "h", CODA_BF16, -1, -1));
+  const int64_t M = h->rows, D = h->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t V = W->w.cols;
+  TRY(check_weight(W, "W", D, V, precision));
+  TRY(check_vec(labels, "labels", CODA_I32, M));
+  TRY(check_vec(loss, "loss", CODA_F32, 1));
+  TRY(check_vec(lse, "lse", CODA_F32, M));
+  TRY(check_vec(per_row, "per_row", CODA_F32, M, true));
+  TRY(check_vec(n_valid, "n_valid", CODA_I32, 1));
+  TRY(check_vec(n_bad, "n_bad", CODA_I32, 1, true));
+  if (ignore_index >= 0 && ignore_index < V) return fail(CODA_ERR_VALUE, "ignore_index must lie outside [0, V)");
+  Carver cv(ws);
+  float *Pm, *Ps, *zy, *pr;
+  int* st;
+  ActQ aq{};
+  ce_fwd_layout(cv, M, V, D, precision, &Pm, &Ps, &zy, &pr, &st, &aq);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  float* per = present(per_row) ? static_cast<float*>(per_row->ptr) : pr;
+  if (M > 0) {
+    EpiArgs e = epi0();
+    e.labels = static_cast<const int*>(labels->ptr);
+    e.partial_out = Pm;
+    e.partial_out2 = Ps;
+    e.rowvec_out = zy;
+    e.vocab = (int)V;
+    GemmArgs g = gemm_args(h->ptr, h->ld, W->w.ptr, W->w.ld, M, V, D);
+    TRY(launched(launch_gemm(Prog::CrossEntropy, LAYOUT_NN, false, g, e, s), "cross_entropy_fwd: logits"));
+    hipLaunchKernelGGL(ce_finish_rows_kernel, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, Pm, Ps,
+                       (int)coda_partials_cols(V), (int)M, zy, static_cast<const int*>(labels->ptr), (int)V,
+                       ignore_index, static_cast<float*>(lse->ptr), per, st);
+    TRY(check_launch("cross_entropy_fwd: rows"));
+  }
+  hipLaunchKernelGGL(ce_finish_loss_kernel, dim3(1), dim3(1024), 0, s, per, st, (int)M, static_cast<float*>(loss->ptr),
+                     static_cast<int*>(n_valid->ptr), present(n_bad) ? static_cast<int*>(n_bad->ptr) : nullptr);
+  return check_launch("cross_entropy_fwd: loss");
+}
+
+static size_t ce_bwd_layout(Carver& cv, int64_t M, int64_t V, int64_t chunk, float** scale, uint16_t** G) {
+  *scale = cv.take<float>(1);
+  *G = cv.take<uint16_t>((size_t)chunk * ((V + 7) / 8 * 8));
+  return cv.off;
+}
+
+extern "C" coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
+                                                               int32_t precision, size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  (void)D;
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  Carver cv(nullptr);
+  float* sc;
+  uint16_t* G;
+  ce_bwd_layout(cv, M, V, chunk, &sc, &G);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
+                                                     int32_t ignore_index, const coda_mat* lse, const coda_mat* n_valid,
+                                                     float dloss, const coda_mat* dh, const coda_mat* dW, float beta,
+                                                     int64_t chunk_rows, int32_t precision, void* ws, size_t ws_bytes,
+                                                     void* stream) {
+  TRY(check_precision(precision));
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  TRY(check_mat(h, "h", CODA_BF16, -1, -1));
+  const int64_t M = h->rows, D = h->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t V = W->w.cols;
+  TRY(check_weight(W, "W", D, V, precision));
+  TRY(check_vec(labels, "labels", CODA_I32, M));
+  TRY(check_vec(lse, "lse", CODA_F32, M));
+  TRY(check_vec(n_valid, "n_valid", CODA_I32, 1));
+  TRY(check_mat(dh, "dh", CODA_BF16, M, D));
+  TRY(check_mat(dW, "dW", CODA_F32, D, V));
+  if (ignore_index != -100) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy_bwd: ignore_index must be -100 in this build");
+  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  Carver cv(ws);
+  float* scale;
+  uint16_t* G;
+  ce_bwd_layout(cv, M, V, chunk, &scale, &G);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  const int64_t ldG = (V + 7) / 8 * 8;
+  hipLaunchKernelGGL(ce_scale_kernel, dim3(1), dim3(1), 0, s, static_cast<const int*>(n_valid->ptr), dloss, scale);
+  TRY(check_launch("cross_entropy_bwd: scale"));
+  const uint16_t* hp = static_cast<const uint16_t*>(h->ptr);
+  const int* lab = static_cast<const int*>(labels->ptr);
+  const float* lsep = static_cast<const float*>(lse->ptr);
+  for (int64_t c0 = 0; c0 < M; c0 += chunk) {
+    const int64_t mc = std::min(chunk, M - c0);
+    {  // recompute the logits of the chunk into G
+      EpiArgs e = epi0();
+      e.out = G; e.ld_out = ldG;
+      e.labels = lab + c0;
+      e.rowvec = lsep + c0;
+      GemmArgs g = gemm_args(hp + c0 * h->ld, h->ld, W->w.ptr, W->w.ld, mc, V, D);
+      TRY(launched(launch_gemm(Prog::CrossEntropyG, LAYOUT_NN, false, g, e, s), "cross_entropy_bwd: G"));
+    }
+    {  // dh = s G W^T
+      EpiArgs e = epi0();
+      e.out = static_cast<uint16_t*>(dh->ptr) + c0 * dh->ld; e.ld_out = dh->ld;
+      e.alpha_dev = scale;
+      GemmArgs g = gemm_args(G, ldG, W->w.ptr, W->w.ld, mc, D, V);
+      TRY(launched(launch_gemm(Prog::StoreAlphaDev, LAYOUT_NT, false, g, e, s), "cross_entropy_bwd: dh"));
+    }
+    {  // dW = beta dW + s h^T G
+      EpiArgs e = epi0();
+      e.out = dW->ptr; e.ld_out = dW->ld;
+      e.beta = c0 == 0 ? beta : 1.0f;
+      e.alpha_dev = scale;
+      GemmArgs g = gemm_args(hp + c0 * h->ld, h->ld, G, ldG, D, V, mc);
+      TRY(launched(launch_gemm(Prog::F32AlphaDev, LAYOUT_TN, false, g, e, s), "cross_entropy_bwd: dW"));
+    }
+  }
+  return CODA_OK;
+}

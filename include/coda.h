@@ -1,0 +1,296 @@
+/*
+ * coda.h - C ABI of the MI355X (gfx950) GEMM+epilogue library.
+ *
+ * The method: the CODA paper "Rewriting Transformer Blocks as GEMM-Epilogue
+ * Programs" (arXiv 2605.19269).  §2.2 splits a GEMM into a fixed mainloop and
+ * a programmable epilogue that runs on each output tile while it is still on
+ * chip; §3.1 lists five epilogue primitive classes (elementwise / pairwise
+ * maps, rank-1 vector loads and stores, rank-2 tile loads and stores, tile
+ * row reductions merged later, running state such as online log-sum-exp);
+ * §3.2 writes the non-attention parts of a Transformer block as
+ * GEMM + epilogue programs, and §3.2.1 gives the reparameterisation
+ *     RMSNorm(x W0 + z, g) W1 = (r (x W0 + z) * g) W1,   r = 1 / rms(x W0 + z),
+ * whose per-row factor r is applied behind the second GEMM (the "delayed r"
+ * described in the KuCoin news summary of CODA, section on the epilogue).
+ * The functional entry points follow the kernel-granular API named by the
+ * papers.ananclaw.com CODA guide (section on the functional API):
+ * linear_swiglu, linear_cross_entropy, linear_qknorm_rope, plus
+ * linear_rmsnorm_residual for the O- and down-projections.
+ *
+ * Conventions for every entry point
+ *  - Matrices are described by coda_mat: a DEVICE pointer, an element type,
+ *    rows, cols and a leading dimension `ld` in elements (row-major: element
+ *    (i, j) lives at ptr + i * ld + j).  Vectors are 1 x n coda_mats.
+ *  - Weights are stored [K_in, N_out] row-major.
+ *  - The caller owns all device memory (inputs, outputs, workspace).  The
+ *    library never allocates, frees or synchronises; every call enqueues
+ *    kernels on `stream` (a hipStream_t, NULL = default stream) and returns.
+ *  - Validation (null pointers, dtypes, shapes, ld, 16-byte alignment,
+ *    workspace size) runs on the host BEFORE any HIP call; a failed check
+ *    returns a status code and leaves device memory untouched.
+ *    coda_last_error() gives a human-readable message (thread-local).
+ *  - A kernel launch failure returns CODA_ERR_LAUNCH.  Data errors that only
+ *    the device can see (a label outside [0, V) that is not the ignore index)
+ *    are reported through a device-side counter output.
+ *  - Contiguous rows: bf16 matrices need cols % 8 == 0 and ld % 8 == 0,
+ *    fp32 matrices cols % 4 == 0 and ld % 4 == 0, E4M3 matrices
+ *    cols % 16 == 0 and ld % 16 == 0; every pointer 16-byte aligned.
+ *  - Results are bitwise deterministic: reductions run in a fixed order.
+ */
+#ifndef CODA_H_
+#define CODA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CODA_ABI_VERSION 1
+
+typedef enum coda_status {
+  CODA_OK = 0,
+  CODA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CODA_ERR_DTYPE = 2,       /* wrong element type */
+  CODA_ERR_SHAPE = 3,       /* inconsistent or unsupported sizes */
+  CODA_ERR_LAYOUT = 4,      /* ld smaller than cols, or not a multiple of the vector width */
+  CODA_ERR_ALIGN = 5,       /* pointer not 16-byte aligned */
+  CODA_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  CODA_ERR_UNSUPPORTED = 7, /* epilogue program or option not compiled in */
+  CODA_ERR_LAUNCH = 8,      /* a kernel launch failed */
+  CODA_ERR_VALUE = 9        /* an invalid scalar argument */
+} coda_status;
+
+typedef enum coda_dtype { CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4 } coda_dtype;
+
+/* GEMM operand precision of the functional entry points. */
+typedef enum coda_precision {
+  CODA_PREC_BF16 = 0, /* bf16 operands, fp32 accumulate */
+  CODA_PREC_FP8 = 1   /* OCP E4M3 operands with amax scales, fp32 accumulate */
+} coda_precision;
+
+typedef struct coda_mat {
+  void* ptr;       /* device pointer (NULL = absent where optional) */
+  int32_t dtype;   /* coda_dtype */
+  int32_t reserved;
+  int64_t rows, cols, ld;
+} coda_mat;
+
+/* A weight W [K_in, N_out] and, for fp8 precision, its two E4M3 copies made
+ * by coda_quantize_weight: q_fwd [N_out, K_in] with one scale per output
+ * channel (forward GEMM, contracted axis K_in contiguous) and q_bwd
+ * [K_in, N_out] with one scale per input channel (input-gradient GEMM).
+ * bf16 precision reads only `w`. */
+typedef struct coda_weight {
+  coda_mat w;
+  coda_mat q_fwd, s_fwd;
+  coda_mat q_bwd, s_bwd;
+} coda_weight;
+
+int coda_abi_version(void);
+const char* coda_status_string(int status);
+const char* coda_last_error(void);
+
+/* ===================================================================== prep */
+
+/* W_out[k, n] = bf16(g[k] * W[k, n]): the RMSNorm gain folded into the weight
+ * of the GEMM that consumes the norm (the §3.2.1 identity with g moved onto
+ * W1).  W, W_out: bf16 [K, N] (may alias); g: fp32 1 x K. */
+coda_status coda_fold_gain(const coda_mat* W, const coda_mat* g, const coda_mat* W_out, void* stream);
+
+/* Packs the gate and up weights [K, F] into W_gu [K, 2F]: each 64-column
+ * block holds 32 gate columns then the matching 32 up columns, so one lane
+ * of the SwiGLU epilogue holds gate_f and up_f.  g (fp32 1 x K) is folded
+ * when non-NULL.  F % 32 == 0. */
+coda_status coda_pack_gate_up(const coda_mat* Wg, const coda_mat* Wu, const coda_mat* g_or_null,
+                              const coda_mat* Wgu_out, void* stream);
+
+/* RoPE table [seq_len, head_dim/2, 2] fp32 (out is seq_len x head_dim):
+ * (cos, sin) of p * theta^(-2i/head_dim), angles in float64.  head_dim = 128. */
+coda_status coda_rope_table(int32_t seq_len, int32_t head_dim, double theta, const coda_mat* out,
+                            void* stream);
+
+/* out[m] = sum_k x[m, k]^2 (fp32 1 x M): one row partial, usable wherever an
+ * entry point takes sum-of-squares partials (with n = 1). */
+coda_status coda_row_sumsq(const coda_mat* x, const coda_mat* out, void* stream);
+
+/* E4M3 quantisation of a bf16 matrix X [R, C] with the amax taken over the
+ * contracted axis `axis`:
+ *   axis = 1: Q [R, C], scale fp32 1 x R   (Q = e4m3(clamp(X * 448/amax_r)))
+ *   axis = 0: Q [C, R] (written transposed), scale fp32 1 x C
+ * scale = amax / 448 (1 when amax = 0); dequantised value Q * scale.
+ * Workspace (axis 0 only): coda_quantize_e4m3_workspace. */
+coda_status coda_quantize_e4m3_workspace(const coda_mat* X, int32_t axis, size_t* bytes);
+coda_status coda_quantize_e4m3(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* scale,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Fills wt->q_fwd/s_fwd (per output channel, Q transposed) and
+ * wt->q_bwd/s_bwd (per input channel) from wt->w. */
+coda_status coda_quantize_weight_workspace(const coda_weight* wt, size_t* bytes);
+coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream);
+
+/* ===================================================================== generic GEMM + epilogue */
+
+/* One epilogue primitive.  Programs are ordered chains; the library checks a
+ * program against the set it has compiled and returns CODA_ERR_UNSUPPORTED
+ * otherwise.  Compiled chains (A: [M,K] (transA 0) or [K,M] (transA 1),
+ * B: [K,N] (transB 0) or [N,K] (transB 1), bf16):
+ *   STORE_BF16                                       D bf16 [M,N]
+ *   ACCUM_F32(beta)                                  D fp32 = beta D + acc
+ *   ROW_SCALE(v) COL_SCALE(w) STORE_BF16              NN only
+ *   ADD_TILE(z) STORE_BF16 [ROW_SUMSQ_PARTIAL(P)]     NN only (residual + next-norm partials)
+ *   ROW_SCALE(r) SWIGLU STORE_BF16                    NN only, D [M, N/2]
+ *   ROW_RMS_FROM_PARTIALS(P, fparam = eps) SWIGLU STORE_BF16   NN only
+ * `slot` indexes the aux array; ROW_SUMSQ_PARTIAL writes P[tiles_n][M] with
+ * tiles_n = ceil(N / 256) (see coda_partials_cols). */
+typedef enum coda_epi_opcode {
+  CODA_EPI_STORE_BF16 = 1,            /* P3 store */
+  CODA_EPI_ACCUM_F32 = 2,             /* fp32 beta-accumulate (fparam = beta) */
+  CODA_EPI_ROW_SCALE = 3,             /* P2 row vector (fp32 1 x M) */
+  CODA_EPI_COL_SCALE = 4,             /* P2 column vector (fp32 1 x N) */
+  CODA_EPI_ADD_TILE = 5,              /* P3 tile load (bf16 [M, N]) and add */
+  CODA_EPI_ROW_SUMSQ_PARTIAL = 6,     /* P4 row partial of bf16(value)^2 (fp32 [tiles_n, M]) */
+  CODA_EPI_SWIGLU = 7,                /* P1 pairwise gate/up (packed layout) */
+  CODA_EPI_ROW_RMS_FROM_PARTIALS = 8  /* P2 row vector finished from P4 partials ([n, M]) */
+} coda_epi_opcode;
+
+typedef struct coda_epi_op {
+  uint16_t op;     /* coda_epi_opcode */
+  uint16_t slot;   /* aux index */
+  uint16_t flags;  /* reserved, 0 */
+  uint16_t reserved;
+  float fparam;
+} coda_epi_op;
+
+#define CODA_MAX_EPI_OPS 8
+typedef struct coda_epi_program {
+  uint32_t n_ops;
+  coda_epi_op ops[CODA_MAX_EPI_OPS];
+} coda_epi_program;
+
+/* Number of N tiles (partial rows) an epilogue reduction writes for N columns. */
+int64_t coda_partials_cols(int64_t N);
+
+coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
+                          const coda_mat* B, int32_t transB, const coda_mat* D,
+                          const coda_mat* aux, uint32_t n_aux, void* stream);
+
+/* ===================================================================== functional: forward */
+
+/* RMSNorm -> Linear -> SwiGLU (config-1 op and the block's gate/up GEMM):
+ *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r * (x W~_gu),
+ *   out = SiLU(h_gate) * h_up
+ * x: bf16 [M, K].  sumsq_partials: fp32 [n, M] sum-of-squares partials of x
+ * (n <= 32) or NULL (the library computes them; workspace needed).
+ * Wgu: packed, gain-folded weight (coda_pack_gate_up).  out: bf16 [M, F].
+ * save_hgu (bf16 [M, 2F], packed order) and r_out (fp32 1 x M) are optional
+ * saves for the backward. */
+coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, int32_t have_partials, int32_t precision,
+                                             size_t* bytes);
+coda_status coda_linear_swiglu_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* Wgu,
+                                   float eps, const coda_mat* out, const coda_mat* save_hgu,
+                                   const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Residual linear (O-projection, down-projection): out = residual + a W,
+ * stored bf16, plus the sum-of-squares partials of the stored out for the
+ * next RMSNorm (fp32 [coda_partials_cols(N), M], optional). */
+coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
+                                                       size_t* bytes);
+coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weight* W, const coda_mat* residual,
+                                             const coda_mat* out, const coda_mat* sumsq_partials_out,
+                                             int32_t precision, void* ws, size_t ws_bytes, void* stream);
+
+/* QKV projection with the delayed RMSNorm factor, per-head QK-RMSNorm and
+ * RoPE (MHA, head_dim 128, D = heads * 128):
+ *   h = r1 * (x W~_qkv) [M, 3D];  q = RoPE(QKnorm(h_q; gq)), k likewise, v = h_v
+ * positions p = m mod seq_len.  rope: coda_rope_table output.  Optional
+ * saves: qk_pre bf16 [M, 2D] (pre-norm q | k), r_out fp32 1 x M. */
+coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t D, int32_t have_partials,
+                                                  int32_t precision, size_t* bytes);
+coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda_mat* sumsq_partials,
+                                        const coda_weight* Wqkv, const coda_mat* gq, const coda_mat* gk,
+                                        const coda_mat* rope, int32_t seq_len, float eps, const coda_mat* q,
+                                        const coda_mat* k, const coda_mat* v, const coda_mat* save_qk_pre,
+                                        const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/* ===================================================================== functional: backward */
+
+/* Backward of RMSNorm -> gate/up Linear -> SwiGLU, fused behind the GEMM
+ * that produces the SwiGLU output gradient da = dY Wd^T (never materialised):
+ *   dSwiGLU with the saved (packed) hg/hu, dh~ = bf16(r * [dhg, dhu]),
+ *   T = sum_j dh~ h,  c = r T / D,
+ *   du = dh~ W~_gu^T - c u + dres          (bf16 [M, D]; dres optional)
+ *   dW_gu = beta dW_gu + g * (u^T dh~)     (fp32 [D, 2F], packed order)
+ *   dg = beta dg + sum_n W_gu * (u^T dh~)  (fp32 1 x D)
+ * Wd: down weight [F, D]; Wgu: folded packed weight; Wgu_unfolded: the same
+ * packing without the gain; u: the norm input (h1).  dh_gu_out: optional
+ * bf16 [M, 2F] copy of dh~ (else held in the workspace). */
+coda_status coda_linear_swiglu_bwd_workspace(int64_t M, int64_t D, int64_t F, int32_t precision,
+                                             size_t* bytes);
+coda_status coda_linear_swiglu_bwd(const coda_mat* dY, const coda_weight* Wd, const coda_mat* saved_hgu,
+                                   const coda_mat* r, const coda_mat* u, const coda_weight* Wgu,
+                                   const coda_mat* Wgu_unfolded, const coda_mat* g, const coda_mat* dres,
+                                   const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg, float beta,
+                                   const coda_mat* dh_gu_out, int32_t precision, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Backward of a residual linear out = residual + a W:
+ *   dW = beta dW + a^T d_out (fp32 [K, N]);  da = d_out W^T (bf16 [M, K], optional). */
+coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
+                                                       size_t* bytes);
+coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, const coda_mat* a, const coda_weight* W,
+                                             const coda_mat* da, const coda_mat* dW, float beta,
+                                             int32_t precision, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the QKV projection with QK-norm and RoPE, given the attention
+ * gradients dq, dk (of the rotated q, k) and dv:
+ *   inverse RoPE, per-head RMSNorm backward from the saved pre-norm q, k,
+ *   dh~ = bf16(r1 [dq_pre, dk_pre, dv]),  T = sum_j dh~ h,  c = r1 T / D,
+ *   dx = dh~ W~^T - c x + dres (bf16 [M, D]),
+ *   dW = beta dW + g1 * (x^T dh~) (fp32 [D, 3D]),  dg1 = beta dg1 + sum_n W * (x^T dh~),
+ *   dgq, dgk = beta dg + per-head gain gradients (fp32 1 x 128). */
+coda_status coda_linear_qknorm_rope_bwd_workspace(int64_t M, int64_t D, int32_t precision, size_t* bytes);
+coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv,
+                                        const coda_mat* x, const coda_mat* r, const coda_mat* qk_pre,
+                                        const coda_mat* v, const coda_weight* Wqkv, const coda_mat* Wqkv_unfolded,
+                                        const coda_mat* g, const coda_mat* gq, const coda_mat* gk,
+                                        const coda_mat* rope, int32_t seq_len, float eps, const coda_mat* dres,
+                                        const coda_mat* dx, const coda_mat* dW, const coda_mat* dg,
+                                        const coda_mat* dgq, const coda_mat* dgk, float beta,
+                                        int32_t precision, void* ws, size_t ws_bytes, void* stream);
+
+/* ===================================================================== cross-entropy */
+
+/* Linear + cross-entropy forward without materialising the logits:
+ *   z = h W (per N tile: online max / sum-exp partials, label-logit gather),
+ *   lse[m], per-row loss, loss = sum_valid / n_valid (NaN if n_valid = 0).
+ * h: bf16 [M, D]; W: [D, V]; labels: int32 1 x M; rows whose label equals
+ * ignore_index are skipped.  Outputs: loss fp32 1 x 1, lse fp32 1 x M,
+ * per_row fp32 1 x M (optional), n_valid int32 1 x 1 (required),
+ * n_bad int32 1 x 1 (optional; count of labels outside [0, V)). */
+coda_status coda_linear_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t precision,
+                                                    size_t* bytes);
+coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
+                                          int32_t ignore_index, const coda_mat* loss, const coda_mat* lse,
+                                          const coda_mat* per_row, const coda_mat* n_valid,
+                                          const coda_mat* n_bad, int32_t precision, void* ws, size_t ws_bytes,
+                                          void* stream);
+
+/* Backward: recompute z per chunk of `chunk_rows` rows (0 = all rows),
+ * G = bf16(exp(z - lse) - onehot(label)) (0 on ignored rows), s = dloss / n_valid,
+ *   dh = bf16(s * G W^T) [M, D],  dW = beta dW + s * h^T G (fp32 [D, V]). */
+coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
+                                                    int32_t precision, size_t* bytes);
+coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
+                                          int32_t ignore_index, const coda_mat* lse, const coda_mat* n_valid,
+                                          float dloss, const coda_mat* dh, const coda_mat* dW, float beta,
+                                          int64_t chunk_rows, int32_t precision, void* ws, size_t ws_bytes,
+                                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CODA_H_ */

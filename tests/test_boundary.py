@@ -1,0 +1,134 @@
+"""The C-ABI library loads on a GPU-less host, exports every function that
+include/coda.h declares, and rejects bad arguments before any HIP call.
+
+No compute call is made here: every call fails host-side validation (fake,
+never-dereferenced device pointers are used for the shape checks)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gemm_epilogue_fp8_amd as g
+from gemm_epilogue_fp8_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "coda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = g.lib()
+    names = header_functions()
+    assert len(names) >= 25
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in coda.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+    assert L.coda_abi_version() == 1
+
+
+def test_status_strings():
+    L = g.lib()
+    for st in range(10):
+        assert L.coda_status_string(st)
+    assert L.coda_status_string(0) == b"ok"
+
+
+FAKE = 1 << 40     # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def fake(dtype, rows, cols, ld=None, ptr=FAKE):
+    m = _lib.CodaMat()
+    m.ptr, m.dtype, m.rows, m.cols, m.ld = ptr, dtype, rows, cols, cols if ld is None else ld
+    return m
+
+
+def call_sumsq(x, out):
+    L = g.lib()
+    return L.coda_row_sumsq(C.byref(x) if x else None, C.byref(out) if out else None, None)
+
+
+def test_validation_codes():
+    L = g.lib()
+    BF, F32 = _lib.CODA_BF16, _lib.CODA_F32
+    x = fake(BF, 4, 8)
+    assert call_sumsq(None, fake(F32, 1, 4)) == 1                      # NULL
+    assert call_sumsq(fake(F32, 4, 8), fake(F32, 1, 4)) == 2           # dtype
+    assert call_sumsq(x, fake(F32, 1, 5)) == 3                         # shape
+    assert call_sumsq(fake(BF, 4, 8, ld=6), fake(F32, 1, 4)) == 4      # ld < cols
+    assert call_sumsq(fake(BF, 4, 12, ld=12), fake(F32, 1, 4)) == 4    # cols not a multiple of 8
+    assert call_sumsq(fake(BF, 4, 8, ptr=FAKE + 2), fake(F32, 1, 4)) == 5   # alignment
+    assert b"aligned" in L.coda_last_error()
+
+
+def test_gemm_epi_rejects_unknown_programs():
+    L = g.lib()
+    BF = _lib.CODA_BF16
+    A, B, D = fake(BF, 64, 64), fake(BF, 64, 64), fake(BF, 64, 64)
+    prog = _lib.EpiProgram()
+    prog.n_ops = 2
+    prog.ops[0].op = _lib.EPI_SWIGLU
+    prog.ops[1].op = _lib.EPI_ROW_SCALE
+    st = L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None)
+    assert st == 7 and b"not in the compiled set" in L.coda_last_error()
+    prog.n_ops = 0
+    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None) == 7
+    prog.n_ops = 1
+    prog.ops[0].op = _lib.EPI_STORE_BF16
+    Bbad = fake(BF, 32, 64)
+    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(Bbad), 0, C.byref(D), None, 0, None) == 3
+
+
+def test_functional_validation():
+    L = g.lib()
+    BF, F32, I32 = _lib.CODA_BF16, _lib.CODA_F32, _lib.CODA_I32
+    x = fake(BF, 16, 64)
+    w = _lib.CodaWeight()
+    w.w = fake(BF, 64, 96)                 # 2F = 96 is not a multiple of 64
+    out = fake(BF, 16, 48)
+    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 0, None, 0, None)
+    assert st == 3
+    w.w = fake(BF, 64, 128)
+    out = fake(BF, 16, 64)
+    # workspace required (no partials given) but none passed
+    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 0, None, 0, None)
+    assert st == 6
+    # bad precision
+    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 5, None, 0, None)
+    assert st == 9
+    # fp8 without quantised copies
+    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 1, None, 0, None)
+    assert st == 1
+    # cross-entropy: ignore index inside [0, V)
+    h = fake(BF, 16, 64)
+    wv = _lib.CodaWeight()
+    wv.w = fake(BF, 64, 256)
+    lab, loss, lse, nv = fake(I32, 1, 16), fake(F32, 1, 1), fake(F32, 1, 16), fake(I32, 1, 1)
+    st = L.coda_linear_cross_entropy_fwd(C.byref(h), C.byref(wv), C.byref(lab), 3, C.byref(loss), C.byref(lse),
+                                         None, C.byref(nv), None, 0, None, 0, None)
+    assert st == 9
+    # QKV needs D % 128 == 0
+    xq = fake(BF, 16, 64)
+    wq = _lib.CodaWeight()
+    wq.w = fake(BF, 64, 192)
+    st = L.coda_linear_qknorm_rope_fwd(C.byref(xq), None, C.byref(wq), None, None, None, 16, 1e-6, None, None,
+                                       None, None, None, 0, None, 0, None)
+    assert st == 3
+
+
+def test_workspace_queries():
+    L = g.lib()
+    n = C.c_size_t(0)
+    assert L.coda_linear_swiglu_bwd_workspace(8192, 4096, 11008, 0, C.byref(n)) == 0
+    # T partials + collapsed T + gain partials + dh~ copy
+    assert n.value >= 8192 * 2 * 11008 * 2
+    m = C.c_size_t(0)
+    assert L.coda_linear_swiglu_bwd_workspace(8192, 4096, 11008, 1, C.byref(m)) == 0
+    assert m.value > n.value               # fp8 adds the quantised operands
+    assert L.coda_linear_cross_entropy_bwd_workspace(8192, 2048, 128256, 1024, 0, C.byref(n)) == 0
+    assert n.value >= 1024 * 128256 * 2
+    assert g.partials_cols(128256) == 501 and g.partials_cols(1) == 1

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails."""
+import math
+
+import numpy as np
+import pytest
+
+import coda_inputs as ci
+from oracle import block as ob
+from oracle import numerics as nm
+from tests.helpers import (BF16_TOL, assert_bf16, assert_grad, rel_norm, to_dev, to_np, unpack_gu)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogue_fp8_amd as coda  # noqa: E402
+from gemm_epilogue_fp8_amd.block import Block  # noqa: E402
+
+BF = torch.bfloat16
+DEV = "cuda"
+
+
+def bf(a):
+    return to_dev(np.asarray(a, np.float32), BF)
+
+
+def f32(a):
+    return to_dev(np.asarray(a, np.float32))
+
+
+def rand_bf16(rng, *shape, std=1.0):
+    return ci.to_bf16_values(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
+
+
+# ------------------------------------------------------------------ mainloop / generic program
+@pytest.mark.parametrize("transA,transB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 200), (517, 520, 392), (64, 8, 8)])
+def test_gemm_store_layouts(transA, transB, M, N, K):
+    if transA:
+        M += -M % 8            # a transposed A is stored [K, M]: M is its contiguous axis
+    rng = np.random.default_rng(M + N + K + 10 * transA + transB)
+    A = rand_bf16(rng, M, K)
+    B = rand_bf16(rng, K, N, std=K ** -0.5)
+    At = bf(A.T.copy() if transA else A)
+    Bt = bf(B.T.copy() if transB else B)
+    D = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_epi([(coda.EPI_STORE_BF16, 0, 0.0)], At, transA, Bt, transB, D)
+    torch.cuda.synchronize()
+    ref = nm.bf16(ob.mm(A, B))
+    assert_bf16("D", to_np(D), ref)
+
+
+def test_gemm_accum_f32_beta():
+    rng = np.random.default_rng(5)
+    M, N, K = 264, 136, 330
+    A, B = rand_bf16(rng, K, M), rand_bf16(rng, K, N)
+    prior = ci.fp32_prior((M, N), 3)
+    D = f32(prior)
+    coda.gemm_epi([(coda.EPI_ACCUM_F32, 0, 1.0)], bf(A), 1, bf(B), 0, D)
+    torch.cuda.synchronize()
+    assert_grad("D", to_np(D), prior + ob.mm(A.T.copy(), B))
+
+
+def test_gemm_row_col_scale_and_residual_partials():
+    rng = np.random.default_rng(6)
+    M, N, K = 300, 520, 136
+    A, B = rand_bf16(rng, M, K), rand_bf16(rng, K, N, std=K ** -0.5)
+    rv = rng.uniform(0.5, 2, M).astype(np.float32)
+    cv = rng.uniform(0.5, 2, N).astype(np.float32)
+    D = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_epi([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_COL_SCALE, 1, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)],
+                  bf(A), 0, bf(B), 0, D, aux=[f32(rv), f32(cv)])
+    Z = rand_bf16(rng, M, N)
+    nT = coda.partials_cols(N)
+    P = torch.empty((nT, M), dtype=torch.float32, device=DEV)
+    D2 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_epi([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0),
+                   (coda.EPI_ROW_SUMSQ_PARTIAL, 1, 0.0)], bf(A), 0, bf(B), 0, D2, aux=[bf(Z), P])
+    torch.cuda.synchronize()
+    acc = ob.mm(A, B)
+    assert_bf16("scaled", to_np(D), nm.bf16((acc * rv[:, None]) * cv[None, :]))
+    y = nm.bf16(Z + acc)
+    assert_bf16("residual", to_np(D2), y)
+    assert_grad("sumsq partials", to_np(P), ob.tile_partials(y.astype(np.float64) ** 2, 256))
+
+
+# ------------------------------------------------------------------ config 1: RMSNorm -> Linear -> SwiGLU
+def _swiglu_case(shape, seed, use_partials=False, saves=False):
+    P = ci.swiglu_inputs(shape, seed)
+    x = bf(P["x"])
+    Wgu = torch.empty((shape.K, 2 * shape.F), dtype=BF, device=DEV)
+    coda.pack_gate_up(bf(P["Wg"]), bf(P["Wu"]), f32(P["g"]), Wgu)
+    out = torch.empty((shape.M, shape.F), dtype=BF, device=DEV)
+    partials = None
+    if use_partials:
+        partials = torch.empty((1, shape.M), dtype=torch.float32, device=DEV)
+        coda.row_sumsq(x, partials)
+    save = torch.empty((shape.M, 2 * shape.F), dtype=BF, device=DEV) if saves else None
+    r_out = torch.empty(shape.M, dtype=torch.float32, device=DEV) if saves else None
+    coda.linear_swiglu_fwd(x, Wgu, shape.eps, out, sumsq_partials=partials, save_hgu=save, r_out=r_out)
+    torch.cuda.synchronize()
+    ref = ob.swiglu_forward_contract(P["x"], P["g"], P["Wg"], P["Wu"], shape.eps)
+    assert_bf16("out", to_np(out), ref)
+    if saves:
+        from oracle import ops
+        r = ops.inv_rms(P["x"], shape.eps)
+        assert_grad("r", to_np(r_out), r)
+        Wg_t = nm.bf16(P["g"][:, None] * P["Wg"])
+        hg = r[:, None] * ob.mm(P["x"], Wg_t)
+        sg, su = unpack_gu(to_np(save))
+        assert_bf16("saved hg", sg, nm.bf16(hg))
+
+
+def test_config1_exact_shape():
+    _swiglu_case(ci.CFG1, ci.SEEDS["cfg1"])
+
+
+def test_swiglu_ragged_with_partials_and_saves():
+    _swiglu_case(ci.SwiGLUShape(M=333, K=264, F=352), 3, use_partials=True, saves=True)
+
+
+# ------------------------------------------------------------------ block forward / backward
+SMALL = ci.BlockShape(M=300, D=256, F=352, seq_len=128)
+MEDIUM = ci.BlockShape(M=520, D=384, F=480, seq_len=200)
+
+
+def _run_block(shape, seed, precision=coda.PREC_BF16):
+    P = ci.block_inputs(shape, seed)
+    params = {k: (f32(v) if k in ("g1", "g2", "gq", "gk") else bf(v)) for k, v in P.items()}
+    blk = Block(params, shape.D, shape.F, seq_len=shape.seq_len, theta=shape.theta, eps=shape.eps,
+                precision=precision)
+    f = blk.forward(params["x"], params["o"])
+    b = blk.backward(params["x"], params["o"], f, params["dY"], params["dq"], params["dk"], params["dv"])
+    torch.cuda.synchronize()
+    return P, {k: to_np(v) for k, v in f.items()}, {k: to_np(v) for k, v in b.items()}
+
+
+@pytest.mark.parametrize("shape,seed", [(SMALL, 0), (MEDIUM, 1)])
+def test_block_forward_backward(shape, seed):
+    P, f, b = _run_block(shape, seed)
+    F = ob.block_forward_contract(P, shape)
+    B = ob.block_backward_contract(P, F, shape)
+    D = shape.D
+    # forward outputs and saves
+    for k in ("q", "k", "v", "h1", "a", "y"):
+        assert_bf16(k, f[k], F[k])
+    assert_bf16("q_pre", f["qk_pre"][:, :D], F["q_pre"])
+    assert_bf16("k_pre", f["qk_pre"][:, D:], F["k_pre"])
+    hg, hu = unpack_gu(f["hgu"])
+    assert_bf16("hg", hg, F["hg"])
+    assert_bf16("hu", hu, F["hu"])
+    assert_grad("r1", f["r1"], F["r1"])
+    assert_grad("r2", f["r2"], F["r2"])
+    assert_grad("next-norm sumsq", f["P4"].sum(axis=0), F["sumsq_y"])
+    # backward
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    assert_bf16("dh~_gu", np.concatenate([dg_, du_], axis=1), B["dht_gu"])
+    for k in ("dh1", "do", "dx"):
+        assert_bf16(k, b[k], B[k])
+    dWg, dWu = unpack_gu(b["dWgu"])
+    assert_grad("dWg", dWg, B["dWg"])
+    assert_grad("dWu", dWu, B["dWu"])
+    for k in ("dWqkv", "dWo", "dWd", "dg1", "dg2", "dgq", "dgk"):
+        assert_grad(k, b[k], B[k])
+
+
+def test_block_deterministic():
+    _, f1, b1 = _run_block(SMALL, 4)
+    _, f2, b2 = _run_block(SMALL, 4)
+    for k in f1:
+        assert np.array_equal(f1[k], f2[k], equal_nan=True), k
+    for k in b1:
+        assert np.array_equal(b1[k], b2[k], equal_nan=True), k
+
+
+# ------------------------------------------------------------------ cross-entropy
+@pytest.mark.parametrize("M,D,V,chunk", [(300, 256, 1000, 0), (257, 128, 777 + 7, 100)])
+def test_cross_entropy(M, D, V, chunk):
+    V = V - V % 8
+    shape = ci.CEShape(M=M, D=D, V=V)
+    P = ci.ce_inputs(shape, 0)
+    labels = P["labels"].copy()
+    labels[[0, 1, 2]] = [0, V - 1, 255 if V > 256 else 1]      # tile-boundary labels
+    h, W = bf(P["h"]), bf(P["W"])
+    lab = to_dev(labels)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    per_row = torch.empty(M, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    nbad = torch.empty(1, dtype=torch.int32, device=DEV)
+    coda.linear_cross_entropy_fwd(h, W, lab, loss, lse, nv, per_row=per_row, n_bad=nbad)
+    prior = ci.fp32_prior((D, V), 9)
+    dh = torch.empty((M, D), dtype=BF, device=DEV)
+    dW = f32(prior)
+    coda.linear_cross_entropy_bwd(h, W, lab, lse, nv, 1.0, dh, dW, beta=1.0, chunk_rows=chunk)
+    torch.cuda.synchronize()
+    Fr = ob.ce_forward_contract(P["h"], P["W"], labels)
+    assert int(nv.item()) == Fr["n_valid"] and int(nbad.item()) == 0
+    assert abs(loss.item() - Fr["loss"]) <= 1e-4 * abs(Fr["loss"])
+    assert_grad("lse", to_np(lse), Fr["lse"])
+    assert_grad("per-row loss", to_np(per_row), Fr["per_row"])
+    Br = ob.ce_backward_contract(P["h"], P["W"], labels, Fr["lse"], Fr["n_valid"], dW_prior=prior, beta=1.0)
+    assert_bf16("dh", to_np(dh), Br["dh"])
+    assert_grad("dh (norm)", to_np(dh), Br["dh"], rel=5e-3)
+    assert_grad("dW", to_np(dW), Br["dW"])
+    ignored = labels == -100
+    assert np.all(to_np(dh)[ignored] == 0)
+
+
+def test_cross_entropy_bad_label_and_empty():
+    M, D, V = 64, 128, 512
+    rng = np.random.default_rng(2)
+    h, W = bf(rand_bf16(rng, M, D)), bf(rand_bf16(rng, D, V, std=D ** -0.5))
+    labels = np.full(M, -100, np.int32)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    nbad = torch.empty(1, dtype=torch.int32, device=DEV)
+    coda.linear_cross_entropy_fwd(h, W, to_dev(labels), loss, lse, nv, n_bad=nbad)
+    torch.cuda.synchronize()
+    assert nv.item() == 0 and math.isnan(loss.item())
+    labels[5], labels[9] = V, -3
+    coda.linear_cross_entropy_fwd(h, W, to_dev(labels), loss, lse, nv, n_bad=nbad)
+    torch.cuda.synchronize()
+    assert nbad.item() == 2
+
+
+# ------------------------------------------------------------------ fp8 quantiser
+@pytest.mark.parametrize("axis", [1, 0])
+def test_quantize_e4m3_bit_exact(axis):
+    rng = np.random.default_rng(11 + axis)
+    R, C = 304, 272            # E4M3 rows are whole 16-byte vectors
+    X = rand_bf16(rng, R, C) * np.float32(3)
+    X[7] = 0.0
+    X = ci.to_bf16_values(X)
+    Q = torch.empty((R, C) if axis == 1 else (C, R), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty(R if axis == 1 else C, dtype=torch.float32, device=DEV)
+    coda.quantize_e4m3(bf(X), axis, Q, s)
+    torch.cuda.synchronize()
+    Qr, sr = nm.quantize_e4m3(X, axis=1 if axis == 1 else 0)
+    got_q = Q.view(torch.uint8).cpu().numpy()
+    ref_q = nm.e4m3_codes(Qr if axis == 1 else Qr.T)
+    assert np.array_equal(got_q, ref_q)
+    assert np.array_equal(to_np(s), sr)
