@@ -79,6 +79,16 @@ SIGNATURES = {
     "coda_linear_cross_entropy_fwd": [M_, W_, M_, i32, M_, M_, M_, M_, M_, i32, vp, sz, vp],
     "coda_linear_cross_entropy_bwd_workspace": [i64, i64, i64, i64, i32, szp],
     "coda_linear_cross_entropy_bwd": [M_, W_, M_, i32, M_, M_, f32, M_, M_, f32, i64, i32, vp, sz, vp],
+    # unfused baseline (include/coda_unfused.h)
+    "coda_unfused_rmsnorm_fwd": [M_, M_, f32, M_, M_, vp],
+    "coda_unfused_rmsnorm_bwd_workspace": [i64, i64, szp],
+    "coda_unfused_rmsnorm_bwd": [M_, M_, M_, M_, M_, M_, M_, f32, vp, sz, vp],
+    "coda_unfused_add": [M_, M_, M_, vp],
+    "coda_unfused_swiglu_fwd": [M_, M_, vp],
+    "coda_unfused_swiglu_bwd": [M_, M_, M_, vp],
+    "coda_unfused_qknorm_rope_fwd": [M_, M_, M_, M_, i32, f32, M_, M_, vp],
+    "coda_unfused_qknorm_rope_bwd_workspace": [i64, i64, szp],
+    "coda_unfused_qknorm_rope_bwd": [M_, M_, M_, M_, M_, M_, M_, i32, f32, M_, M_, M_, f32, vp, sz, vp],
 }
 _RET = {"coda_status_string": C.c_char_p, "coda_last_error": C.c_char_p, "coda_partials_cols": C.c_int64}
 

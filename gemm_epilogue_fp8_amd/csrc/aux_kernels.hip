@@ -107,7 +107,7 @@ __global__ void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, c
   for (int rr = 0; rr < rows_per_wave; ++rr) {
     const int m = (blockIdx.x * 4 + wave) * rows_per_wave + rr;
     if (m >= M) break;
-    const float r = r1[m];
+    const float r = r1 ? r1[m] : 1.0f;     // no r1: plain (unfused) QK-norm backward
     const int pos = m % seq_len;
     const float cs = table[((int64_t)pos * 64 + lane) * 2], sn = table[((int64_t)pos * 64 + lane) * 2 + 1];
     float T = 0.0f;

@@ -263,15 +263,26 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     if (kt + 1 < nk) issue_stage(kt + 1, 1 - p);   // that buffer was released by the last barrier
     const char* As = smem + p * Cfg::STAGE_BYTES;
     const char* Bs = As + Cfg::BM * 128;
-    Frags<Cfg> f[2];
-    load_frags<Cfg>(As, Bs, 0, f[0], wm0, wn0, lane);
+    if constexpr (Cfg::FP8) {
+      // fp8 fragments are 8 registers each: one set, read just before use
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + 1 < NS) load_frags<Cfg>(As, Bs, s + 1, f[(s + 1) & 1], wm0, wn0, lane);
-      // keep the reads of substep s+1 ahead of the MFMAs of substep s
-      __builtin_amdgcn_sched_barrier(0);
-      mma_frags<Cfg>(f[s & 1], acc);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < NS; ++s) {
+        Frags<Cfg> f;
+        load_frags<Cfg>(As, Bs, s, f, wm0, wn0, lane);
+        mma_frags<Cfg>(f, acc);
+        __builtin_amdgcn_sched_barrier(0);   // do not hoist the next substep's reads
+      }
+    } else {
+      Frags<Cfg> f[2];
+      load_frags<Cfg>(As, Bs, 0, f[0], wm0, wn0, lane);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) load_frags<Cfg>(As, Bs, s + 1, f[(s + 1) & 1], wm0, wn0, lane);
+        // keep the reads of substep s+1 ahead of the MFMAs of substep s
+        __builtin_amdgcn_sched_barrier(0);
+        mma_frags<Cfg>(f[s & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): stage kt+1 has landed in LDS
     __syncthreads();

@@ -8,7 +8,9 @@ Two evaluations of every path:
 
 * ``*_canonical``: the unfused textbook sequence (RMSNorm, then GEMM, then
   SwiGLU, residual, QK-norm, RoPE, softmax cross-entropy) and its analytic
-  gradients, no rounding.  Run in float64 this is the "ideal" result.
+  gradients.  Run in float64 without rounding this is the "ideal" result;
+  with bf16 rounding of every operator output it is the operator-by-operator
+  pipeline that the unfused baseline implements.
 
 * ``*_contract``: the reparameterised sequence of the CODA paper, §3.2.1: the
   identity RMSNorm(xW0 + z, g) W1 = (r (xW0 + z) * g) W1, with the per-row
@@ -79,54 +81,62 @@ def _positions(M, seq_len):
     return np.arange(M) % seq_len
 
 
-def block_forward_canonical(P: Dict[str, np.ndarray], shape, dt=np.float64):
+def block_forward_canonical(P: Dict[str, np.ndarray], shape, dt=np.float64, rnd: Callable = _ident):
     """Unfused block forward: pre-norm QKV (with QK-norm and RoPE on q, k),
     O-projection with residual, pre-norm gate/up with SwiGLU, down-projection
-    with residual.  ``o`` stands in for the attention output."""
+    with residual.  ``o`` stands in for the attention output.
+
+    ``rnd`` rounds the output of every operator (identity: the ideal
+    evaluation; bf16 with float32 data: the operator-by-operator bf16
+    pipeline, where each norm, GEMM, activation and residual add writes its
+    result to memory)."""
     c = {k: np.asarray(v, dtype=dt) for k, v in P.items() if k != "labels"}
     D, hd, eps = shape.D, shape.head_dim, shape.eps
     cos, sin = ops.rope_tables(shape.seq_len, hd, shape.theta)
     pos = _positions(c["x"].shape[0], shape.seq_len)
-    xn1 = ops.rms_norm(c["x"], c["g1"], eps)
-    qkv = xn1 @ c["Wqkv"]
+    xn1 = rnd(ops.rms_norm(c["x"], c["g1"], eps))
+    qkv = rnd(xn1 @ c["Wqkv"])
     q_pre, k_pre, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
-    q = ops.rope(ops.qk_norm(q_pre, c["gq"], eps, hd), pos, cos, sin, hd)
-    k = ops.rope(ops.qk_norm(k_pre, c["gk"], eps, hd), pos, cos, sin, hd)
-    h1 = c["x"] + c["o"] @ c["Wo"]
-    xn2 = ops.rms_norm(h1, c["g2"], eps)
-    hg, hu = xn2 @ c["Wg"], xn2 @ c["Wu"]
-    a = ops.swiglu(hg, hu)
-    y = h1 + a @ c["Wd"]
+    q = rnd(ops.rope(ops.qk_norm(q_pre, c["gq"], eps, hd), pos, cos, sin, hd))
+    k = rnd(ops.rope(ops.qk_norm(k_pre, c["gk"], eps, hd), pos, cos, sin, hd))
+    h1 = rnd(c["x"] + rnd(c["o"] @ c["Wo"]))
+    xn2 = rnd(ops.rms_norm(h1, c["g2"], eps))
+    hg, hu = rnd(xn2 @ c["Wg"]), rnd(xn2 @ c["Wu"])
+    a = rnd(ops.swiglu(hg, hu))
+    y = rnd(h1 + rnd(a @ c["Wd"]))
     return dict(q=q, k=k, v=v, q_pre=q_pre, k_pre=k_pre, h1=h1, xn1=xn1, xn2=xn2,
                 hg=hg, hu=hu, a=a, y=y, sumsq_y=np.sum(y * y, axis=1))
 
 
-def block_backward_canonical(P, F, shape, dt=np.float64):
+def block_backward_canonical(P, F, shape, dt=np.float64, rnd: Callable = _ident):
     """Analytic gradients of block_forward_canonical given dY (for y) and
-    dq, dk, dv (for the post-RoPE q, k and for v)."""
+    dq, dk, dv (for the post-RoPE q, k and for v).  ``rnd`` rounds every
+    activation gradient an operator writes (weight and gain gradients are
+    never rounded)."""
     c = {k: np.asarray(v, dtype=dt) for k, v in P.items()}
     D, hd, eps = shape.D, shape.head_dim, shape.eps
     cos, sin = ops.rope_tables(shape.seq_len, hd, shape.theta)
     pos = _positions(c["x"].shape[0], shape.seq_len)
     dY = c["dY"]
-    da = dY @ c["Wd"].T
+    da = rnd(dY @ c["Wd"].T)
     dWd = F["a"].T @ dY
     dhg, dhu = ops.swiglu_bwd(F["hg"], F["hu"], da)
-    dxn2 = dhg @ c["Wg"].T + dhu @ c["Wu"].T
+    dhg, dhu = rnd(dhg), rnd(dhu)
+    dxn2 = rnd(dhg @ c["Wg"].T + dhu @ c["Wu"].T)
     dWg, dWu = F["xn2"].T @ dhg, F["xn2"].T @ dhu
     du2, dg2 = ops.rms_norm_bwd(F["h1"], c["g2"], eps, dxn2)
-    dh1 = dY + du2
-    do = dh1 @ c["Wo"].T
+    dh1 = rnd(dY + du2)
+    do = rnd(dh1 @ c["Wo"].T)
     dWo = c["o"].T @ dh1
     dqn = ops.rope(c["dq"], pos, cos, sin, hd, inverse=True)
     dkn = ops.rope(c["dk"], pos, cos, sin, hd, inverse=True)
     dq_pre, dgq = ops.qk_norm_bwd(F["q_pre"], c["gq"], eps, dqn, hd)
     dk_pre, dgk = ops.qk_norm_bwd(F["k_pre"], c["gk"], eps, dkn, hd)
-    dqkv = np.concatenate([dq_pre, dk_pre, c["dv"]], axis=1)
-    dxn1 = dqkv @ c["Wqkv"].T
+    dqkv = rnd(np.concatenate([dq_pre, dk_pre, c["dv"]], axis=1))
+    dxn1 = rnd(dqkv @ c["Wqkv"].T)
     dWqkv = F["xn1"].T @ dqkv
     du1, dg1 = ops.rms_norm_bwd(c["x"], c["g1"], eps, dxn1)
-    dx = dh1 + du1
+    dx = rnd(dh1 + du1)
     return dict(dx=dx, do=do, dWqkv=dWqkv, dWo=dWo, dWg=dWg, dWu=dWu, dWd=dWd,
                 dg1=dg1, dg2=dg2, dgq=dgq, dgk=dgk)
 

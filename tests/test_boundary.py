@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "coda.h")).read()
+    text = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("coda.h", "coda_unfused.h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", text)))
 

@@ -246,3 +246,97 @@ def test_quantize_e4m3_bit_exact(axis):
     ref_q = nm.e4m3_codes(Qr if axis == 1 else Qr.T)
     assert np.array_equal(got_q, ref_q)
     assert np.array_equal(to_np(s), sr)
+
+
+# ------------------------------------------------------------------ fp8 (E4M3 operands, amax scales)
+@pytest.mark.parametrize("shape,seed", [(ci.BlockShape(M=304, D=256, F=352, seq_len=128), 2)])
+def test_block_fp8_forward_backward(shape, seed):
+    from tests.helpers import FP8_TOL
+    P, f, b = _run_block(shape, seed, precision=coda.PREC_FP8)
+    F = ob.block_forward_contract(P, shape, fp8=True)
+    B = ob.block_backward_contract(P, F, shape, fp8=True)
+    D = shape.D
+    for k in ("q", "k", "v", "h1", "a", "y"):
+        assert_bf16(k, f[k], F[k], tol=FP8_TOL, norm_rel=2e-2)
+    hg, hu = unpack_gu(f["hgu"])
+    assert_bf16("hg", hg, F["hg"], tol=FP8_TOL, norm_rel=2e-2)
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    assert_bf16("dh~_gu", np.concatenate([dg_, du_], axis=1), B["dht_gu"], tol=FP8_TOL, norm_rel=2e-2)
+    for k in ("dh1", "do", "dx"):
+        assert_bf16(k, b[k], B[k], tol=FP8_TOL, norm_rel=2e-2)
+    # Weight and gain gradients pass through column-wise amax quantisers fed by
+    # bf16 tensors that the two sides round in different accumulation orders:
+    # a one-ulp move of a column's amax element shifts every code of that
+    # column.  So besides the norm-wise bound, the elementwise fp8 rule must
+    # hold on all but a small, bounded fraction of elements.
+    dWg, dWu = unpack_gu(b["dWgu"])
+    grads = dict(dWg=dWg, dWu=dWu, dWqkv=b["dWqkv"], dWo=b["dWo"], dWd=b["dWd"], dg1=b["dg1"], dg2=b["dg2"],
+                 dgq=b["dgq"], dgk=b["dgk"])
+    for k, v in grads.items():
+        ref = np.asarray(B[k], np.float64)
+        d = np.abs(np.asarray(v, np.float64) - ref) / (1 + np.abs(ref))
+        assert np.all(np.isfinite(v)), k
+        assert rel_norm(v, ref) <= 2e-2, (k, rel_norm(v, ref))
+        assert (d > FP8_TOL).mean() <= 5e-3, (k, (d > FP8_TOL).mean())
+        assert d.max() <= 0.25, (k, d.max())
+
+
+@pytest.mark.parametrize("with_da", [True, False])
+def test_fp8_residual_linear_backward_same_inputs(with_da):
+    """One fp8 stage from identical seeded bf16 inputs: every quantiser sees the
+    same bits on both sides, so the elementwise fp8 rule holds everywhere."""
+    from tests.helpers import FP8_TOL
+    rng = np.random.default_rng(31)
+    M, K, N = 304, 256, 384
+    dout, a = rand_bf16(rng, M, N, std=0.1), rand_bf16(rng, M, K)
+    W = rand_bf16(rng, K, N, std=K ** -0.5)
+    wt = coda.Weight(bf(W)).prepare_fp8()
+    dW = torch.empty((K, N), dtype=torch.float32, device=DEV)
+    da = torch.empty((M, K), dtype=BF, device=DEV) if with_da else None
+    coda.linear_rmsnorm_residual_bwd(bf(dout), bf(a), wt, dW, da=da, precision=coda.PREC_FP8)
+    torch.cuda.synchronize()
+    assert_bf16("dW", to_np(dW), ob.mm(a.T.copy(), dout, fp8=True), tol=FP8_TOL, norm_rel=1e-3)
+    if with_da:
+        assert_bf16("da", to_np(da), nm.bf16(ob.mm(dout, W.T.copy(), fp8=True)), tol=FP8_TOL, norm_rel=3e-3)
+
+
+def test_quantize_weight_copies():
+    rng = np.random.default_rng(21)
+    K, N = 272, 400          # E4M3 rows are whole 16-byte vectors
+    W = rand_bf16(rng, K, N, std=K ** -0.5)
+    wt = coda.Weight(bf(W)).prepare_fp8()
+    torch.cuda.synchronize()
+    Qf, sf = nm.quantize_e4m3(W, axis=0)          # per output channel
+    Qb, sb = nm.quantize_e4m3(W, axis=1)          # per input channel
+    assert np.array_equal(wt.q_fwd.view(torch.uint8).cpu().numpy(), nm.e4m3_codes(Qf.T))
+    assert np.array_equal(wt.q_bwd.view(torch.uint8).cpu().numpy(), nm.e4m3_codes(Qb))
+    assert np.array_equal(to_np(wt.s_fwd), sf) and np.array_equal(to_np(wt.s_bwd), sb)
+
+
+# ------------------------------------------------------------------ unfused baseline
+def test_unfused_baseline_block():
+    """The unfused operator-by-operator block (the timing baseline) computes
+    the canonical block with every operator output written in bf16: checked
+    against the oracle's canonical evaluation with the same rounding points."""
+    from gemm_epilogue_fp8_amd.unfused import UnfusedBlock
+    shape = ci.BlockShape(M=300, D=256, F=352, seq_len=128)
+    P = ci.block_inputs(shape, 5)
+    params = {k: (f32(v) if k in ("g1", "g2", "gq", "gk") else bf(v)) for k, v in P.items()}
+    ub = UnfusedBlock(params, shape.D, shape.F, seq_len=shape.seq_len, theta=shape.theta, eps=shape.eps)
+    b = ub.alloc(shape.M, DEV)
+    ub.forward(params["x"], params["o"], b)
+    ub.backward(params["x"], params["o"], b, params["dY"], params["dq"], params["dk"], params["dv"])
+    torch.cuda.synchronize()
+    F = ob.block_forward_canonical(P, shape, dt=np.float32, rnd=nm.bf16)
+    B = ob.block_backward_canonical(P, F, shape, dt=np.float32, rnd=nm.bf16)
+    D = shape.D
+    got = {k: to_np(v) for k, v in b.items()}
+    for k, g in (("q", got["q"]), ("k", got["k"]), ("v", got["qkv"][:, 2 * D:]), ("h1", got["h1"]),
+                 ("a", got["a"]), ("y", got["y"])):
+        assert_bf16(k, g, F[k])
+    for k in ("dx", "do"):
+        assert_bf16(k, got[k], B[k])
+    dWg, dWu = unpack_gu(got["dWgu"])
+    for k, g in (("dWg", dWg), ("dWu", dWu), ("dWqkv", got["dWqkv"]), ("dWo", got["dWo"]), ("dWd", got["dWd"]),
+                 ("dg1", got["dg1"]), ("dg2", got["dg2"]), ("dgq", got["dgq"]), ("dgk", got["dgk"])):
+        assert_grad(k, g, B[k])
