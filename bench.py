@@ -1,19 +1,27 @@
 #!/usr/bin/env python3
-"""Benchmark: one step = forward + backward of the reparameterised LLaMA-style
-non-attention block at hidden 2048 (M = 8192 tokens = 4 x 2048, F = 8192,
-16 heads x 128) through the GEMM + epilogue library, on one MI355X.
+"""Benchmark of the GEMM + epilogue library on one MI355X.
 
-Prints one JSON line with the step throughput (algorithmic TFLOP/s of the
-step's GEMMs), the roofline of the dominant kernel (the gate/up GEMM with the
-SwiGLU epilogue, timed with HIP events on the stream it runs on), and the CPU
-oracle timed on the host on a bounded sample of the same workload.
+One step = forward + backward of the reparameterised LLaMA-style
+non-attention block (QKV with delayed RMSNorm + QK-norm + RoPE, O-projection
++ residual + next-norm partials, gate/up + SwiGLU, down-projection +
+residual; backward with dSwiGLU, RMSNorm-backward corrections and fp32
+weight-gradient accumulation) on synthetic inputs resident in HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--hidden 2048|4096]
-                       [--precision bf16|fp8] [--no-cpu]
+Default workload: hidden 2048, MLP 8192, 16 heads x 128, M = 8192 tokens
+(4 x 2048).  --config cfg3 runs hidden 4096 (MLP 11008, 32 heads), --config
+cfg5 hidden 8192 (MLP 28672, 64 heads, M = 4096) with E4M3 operands.
+
+Prints one JSON line: step throughput (algorithmic TFLOP/s = 2MNK over the
+step's GEMMs), block fwd+bwd ms, the unfused baseline (same mainloop with
+plain stores + separate elementwise kernels) timed in the same run, a per-call
+breakdown, the roofline of the dominant kernel (gate/up GEMM + SwiGLU epilogue,
+timed with HIP events on the stream it runs on) and the CPU oracle timed on
+the host on the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,7 +30,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MI355X_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA, published
+HBM_GBPS = 8000.0
 
 
 def block_flops(M, D, F):
@@ -31,54 +40,83 @@ def block_flops(M, D, F):
     return fwd, 2 * fwd
 
 
+def kernel_source_hash():
+    """Hash of the HIP sources, to tell whether stored counter data is current."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "gemm_epilogue_fp8_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config, precision):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(f"{config}_{precision}")
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e["bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--hidden", type=int, default=2048, choices=(2048, 4096))
-    ap.add_argument("--precision", default="bf16", choices=("bf16", "fp8"))
+    ap.add_argument("--config", default="cfg2", choices=("cfg2", "cfg3", "cfg5"))
+    ap.add_argument("--precision", default=None, choices=("bf16", "fp8"))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows of the CPU-oracle sample")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
     return ap.parse_args()
 
 
-def cpu_baseline(shape_full, seed, rows):
+def cpu_baseline(shape_full, seed, rows, fp8):
     """The oracle (numpy, contract mode) forward + backward on the first
     `rows` tokens of the same workload, timed on the host cores."""
-    import numpy as np
     import coda_inputs as ci
     from oracle import block as ob
     shape = ci.BlockShape(M=rows, D=shape_full.D, F=shape_full.F, seq_len=shape_full.seq_len)
     P = ci.block_inputs(shape, seed)
     t0 = time.perf_counter()
-    F = ob.block_forward_contract(P, shape)
-    ob.block_backward_contract(P, F, shape)
+    F = ob.block_forward_contract(P, shape, fp8=fp8)
+    ob.block_backward_contract(P, F, shape, fp8=fp8)
     dt = time.perf_counter() - t0
     fwd, bwd = block_flops(rows, shape.D, shape.F)
     cores = len(os.sched_getaffinity(0))
-    return {"value": (fwd + bwd) / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {shape_full.M} token rows, block fwd+bwd (numpy fp32 contract mode, "
-                      f"BLAS threads = {os.environ.get('OMP_NUM_THREADS', 'default')}), {dt:.1f} s"}
+    threads = os.environ.get("OMP_NUM_THREADS") or os.environ.get("OPENBLAS_NUM_THREADS") or str(cores)
+    return {"value": round((fwd + bwd) / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {shape_full.M} token rows of the same workload, block fwd+bwd, numpy "
+                      f"float32 contract mode{' with E4M3 operands' if fp8 else ''}, {dt:.1f} s"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
+              f"run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    cpu = None
     import coda_inputs as ci
-    cfg = ci.CFG2 if args.hidden == 2048 else ci.CFG3
-    seed = ci.SEEDS["cfg2" if args.hidden == 2048 else "cfg3"]
+    cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[args.config]
+    seed = ci.SEEDS[args.config]
+    precision = args.precision or ("fp8" if args.config == "cfg5" else "bf16")
+    fp8 = precision == "fp8"
+    cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, seed, args.cpu_rows)
+        cpu = cpu_baseline(cfg, seed, args.cpu_rows or cfg.M, fp8)
 
     import numpy as np
     import torch
     import gemm_epilogue_fp8_amd as coda
     from gemm_epilogue_fp8_amd.block import Block
+    from gemm_epilogue_fp8_amd.unfused import UnfusedBlock
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -86,8 +124,12 @@ def main():
     to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
     params = {k: to(v, torch.float32 if k in ("g1", "g2", "gq", "gk") else torch.bfloat16) for k, v in P.items()}
     del P
-    prec = coda.PREC_FP8 if args.precision == "fp8" else coda.PREC_BF16
+    prec = coda.PREC_FP8 if fp8 else coda.PREC_BF16
+    torch.cuda.synchronize()
+    t_prep = time.perf_counter()
     blk = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, theta=cfg.theta, eps=cfg.eps, precision=prec)
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t_prep) * 1e3
     M = cfg.M
     f = blk.alloc_forward(M, dev)
     g = blk.alloc_backward(M, dev)
@@ -96,49 +138,98 @@ def main():
     x, o = params["x"], params["o"]
     dY, dq, dk, dv = params["dY"], params["dq"], params["dk"], params["dv"]
 
-    # the dominant kernel (gate/up GEMM + SwiGLU epilogue) is bracketed by
-    # events on the stream the library launches on (torch's current stream)
+    # The step as a list of library calls, so each can be bracketed by events
+    # on the stream the library launches on (torch's current stream).
+    calls = [
+        ("aux row_sumsq(x)", lambda: coda.row_sumsq(x, f["P_x"])),
+        ("F1 qkv+qknorm+rope", lambda: coda.linear_qknorm_rope_fwd(
+            x, blk.w["qkv"], blk.gq, blk.gk, blk.rope, blk.seq_len, blk.eps, f["q"], f["k"], f["v"],
+            sumsq_partials=f["P_x"], save_qk_pre=f["qk_pre"], r_out=f["r1"], precision=prec)),
+        ("F2 o-proj+residual+sumsq", lambda: coda.linear_rmsnorm_residual_fwd(
+            o, blk.w["o"], x, f["h1"], sumsq_partials_out=f["P2"], precision=prec)),
+        ("F3 gate/up+swiglu", lambda: coda.linear_swiglu_fwd(
+            f["h1"], blk.w["gu"], blk.eps, f["a"], sumsq_partials=f["P2"], save_hgu=f["hgu"], r_out=f["r2"],
+            precision=prec)),
+        ("F4 down+residual+sumsq", lambda: coda.linear_rmsnorm_residual_fwd(
+            f["a"], blk.w["d"], f["h1"], f["y"], sumsq_partials_out=f["P4"], precision=prec)),
+        ("B1+B3+B4 swiglu bwd", lambda: coda.linear_swiglu_bwd(
+            dY, blk.w["d"], f["hgu"], f["r2"], f["h1"], blk.w["gu"], blk.Wgu, blk.g2, dY, g["dh1"], g["dWgu"],
+            g["dg2"], beta=1.0, dh_gu_out=g["dht_gu"], precision=prec)),
+        ("B2 dW_down", lambda: coda.linear_rmsnorm_residual_bwd(dY, f["a"], blk.w["d"], g["dWd"], beta=1.0,
+                                                                 precision=prec)),
+        ("B5+B6 o-proj bwd", lambda: coda.linear_rmsnorm_residual_bwd(g["dh1"], o, blk.w["o"], g["dWo"],
+                                                                       da=g["do"], beta=1.0, precision=prec)),
+        ("G1+B7+B8 qkv bwd", lambda: coda.linear_qknorm_rope_bwd(
+            dq, dk, dv, x, f["r1"], f["qk_pre"], f["v"], blk.w["qkv"], blk.Wqkv, blk.g1, blk.gq, blk.gk,
+            blk.rope, blk.seq_len, blk.eps, g["dh1"], g["dx"], g["dWqkv"], g["dg1"], g["dgq"], g["dgk"],
+            beta=1.0, precision=prec)),
+    ]
     f3_events = []
 
     def step(record=False):
-        f_ = f
-        coda.row_sumsq(x, f_["P_x"])
-        coda.linear_qknorm_rope_fwd(x, blk.w["qkv"], blk.gq, blk.gk, blk.rope, blk.seq_len, blk.eps,
-                                    f_["q"], f_["k"], f_["v"], sumsq_partials=f_["P_x"],
-                                    save_qk_pre=f_["qk_pre"], r_out=f_["r1"], precision=prec)
-        coda.linear_rmsnorm_residual_fwd(o, blk.w["o"], x, f_["h1"], sumsq_partials_out=f_["P2"], precision=prec)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        coda.linear_swiglu_fwd(f_["h1"], blk.w["gu"], blk.eps, f_["a"], sumsq_partials=f_["P2"],
-                               save_hgu=f_["hgu"], r_out=f_["r2"], precision=prec)
-        if record:
-            e1.record()
-            f3_events.append((e0, e1))
-        coda.linear_rmsnorm_residual_fwd(f_["a"], blk.w["d"], f_["h1"], f_["y"], sumsq_partials_out=f_["P4"],
-                                         precision=prec)
-        blk.backward(x, o, f_, dY, dq, dk, dv, grads=g, beta=1.0)
+        for name, fn in calls:
+            if record and name.startswith("F3"):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                f3_events.append((e0, e1))
+            else:
+                fn()
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return max(wall, a.elapsed_time(b) / steps)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
-        step(record=True)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps
-    ms = max(wall * 1e3 / args.steps, gpu_ms)
+    ms = timed(lambda: step(record=True), args.steps)
+    f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
 
+    # per-call breakdown (one extra, untimed-for-the-metric step)
+    evs = []
+    torch.cuda.synchronize()
+    for name, fn in calls:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((name, a, b))
+    torch.cuda.synchronize()
+    breakdown = {n: round(a.elapsed_time(b), 4) for n, a, b in evs}
+
+    unfused = None
+    if not args.no_unfused and not fp8:
+        ub = UnfusedBlock(params, cfg.D, cfg.F, seq_len=cfg.seq_len, theta=cfg.theta, eps=cfg.eps)
+        bufs = ub.alloc(M, dev)
+        for k in ("dWqkv", "dWo", "dWgu", "dWd", "dg1", "dg2", "dgq", "dgk"):
+            bufs[k].zero_()
+
+        def ustep():
+            ub.forward(x, o, bufs)
+            ub.backward(x, o, bufs, dY, dq, dk, dv, beta=1.0)
+
+        for _ in range(args.warmup):
+            ustep()
+        ums = timed(ustep, args.steps)
+        ufwd = timed(lambda: ub.forward(x, o, bufs), max(1, args.steps // 2))
+        unfused = {"block_fwd_bwd_ms": round(ums, 4), "fwd_ms": round(ufwd, 4),
+                   "speedup_fused_over_unfused": round(ums / ms, 4)}
+
+    fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
     fwd, bwd = block_flops(M, cfg.D, cfg.F)
     tflops = (fwd + bwd) / (ms * 1e-3) / 1e12
-    f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
     f3_flop = 2 * M * (2 * cfg.F) * cfg.D
     f3_tflops = f3_flop / (f3_ms * 1e-3) / 1e12
-    peak = MI355X_PEAK_TFLOPS[args.precision]
+    peak = PEAK_TFLOPS[precision]
     out = {
         "metric": "fused GEMM+epilogue TFLOP/s & % MFMA peak; block fwd+bwd ms, hidden 2048/4096",
         "value": round(tflops, 2),
@@ -150,16 +241,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": args.precision,
+        "dtype": precision,
         "data": "synthetic",
-        "config": {"workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}",
+        "config": {"workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}, "
+                               f"MLP {cfg.F}, {cfg.heads}x128 heads, {M} tokens",
                    "tokens": M, "hidden": cfg.D, "mlp": cfg.F, "heads": cfg.heads, "head_dim": 128,
                    "seq_len": cfg.seq_len, "grad_accumulate_beta": 1.0},
         "block_fwd_bwd_ms": round(ms, 4),
+        "block_fwd_ms": round(fwd_ms, 4),
         "pct_of_peak": round(100 * tflops / peak, 2),
+        "unfused_baseline": unfused,
+        "weight_prep_ms": round(prep_ms, 3),
+        "breakdown_ms": breakdown,
         "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU epilogue (M x 2F x D)",
                      "achieved": round(f3_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4), "traffic": None},
+                     "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4),
+                     "flop_per_launch": f3_flop, "traffic": stored_traffic(args.config, precision)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

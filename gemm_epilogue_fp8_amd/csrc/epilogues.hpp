@@ -11,20 +11,23 @@
 // consistently indexed auxiliaries only, so a reduction wider than the tile
 // becomes per-tile partials finished elsewhere.
 //
-// Here each primitive is a small device function over the accumulator
-// fragment that the mainloop leaves in registers.  Lane l of the wave at
-// (wm0, wn0) holds, for MFMA tile (i, j) and group q, row
-//   m = m0 + wm0 + 32 i + (l & 31)
-// and the 4 consecutive columns
-//   n = n0 + wn0 + 32 j + 8 q + 4 (l >> 5) + {0,1,2,3}
-// in acc.c[i][j][4 q + {0..3}].  A row of the workgroup tile is spread over
-// lanes l and l ^ 32 of WAVES_N waves: row reductions add in-lane, then
-// across the lane pair, then across waves through LDS in a fixed order (no
-// atomics, bitwise deterministic).
+// Register layout.  Lane l of the wave at (wm0, wn0) holds, for MFMA tile
+// (i, j) and group q, row m = m0 + wm0 + 32 i + (l & 31) and the 4 consecutive
+// columns n = n0 + wn0 + 32 j + 8 q + 4 (l >> 5) + {0..3} in
+// acc.c[i][j][4 q + {0..3}].  A row of the workgroup tile is spread over lanes
+// l and l ^ 32 of WAVES_N waves: row reductions add in-lane, then across the
+// lane pair, then across waves through LDS in a fixed order (no atomics,
+// bitwise deterministic).
 //
-// The programs (structs below) compose the primitives for the GEMMs of the
-// reparameterised block (forward F1-F4, backward B1-B8), config-1 SwiGLU,
-// and linear + cross-entropy (C1-C4).
+// Tile I/O (P3) is staged through LDS.  Stored straight from the register
+// layout, one wave instruction would touch 32 rows x 16 bytes; here the tile
+// goes to an LDS staging tile (8-byte writes in the register layout, 16-byte
+// chunks XOR-swizzled by row) and the whole workgroup then moves it with
+// row-contiguous 16-byte accesses (64 lanes = two full 512-byte rows), which
+// is what keeps epilogue traffic near HBM speed.  Auxiliary tiles (residual,
+// saved activations, weights) come in the same way and are read back in the
+// register layout.  After the mainloop the 128 KB of pipeline LDS is free for
+// staging; row vectors and reduction scratch live in a separate 10 KB.
 #pragma once
 #include "gemm_core.hpp"
 
@@ -58,34 +61,29 @@ struct EpiArgs {
 };
 
 template <class Cfg>
+constexpr int scratch_bytes() { return (2 + 2 * Cfg::WAVES_N) * Cfg::BM * 4; }
+
+template <class Cfg>
 struct Ctx {
   int m0, n0, wm0, wn0, lane, tid, wn, M, N, tn;
   char* smem;
   __device__ __forceinline__ int lrow(int i) const { return wm0 + 32 * i + (lane & 31); }
   __device__ __forceinline__ int row(int i) const { return m0 + lrow(i); }
-  __device__ __forceinline__ int col(int j, int q) const { return n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5); }
-  // LDS after the mainloop: [0, 2 BM) row vectors, then [WAVES_N][BM] reduction scratch
-  __device__ __forceinline__ float* rowv() const { return reinterpret_cast<float*>(smem); }
-  __device__ __forceinline__ float* rowv2() const { return reinterpret_cast<float*>(smem) + Cfg::BM; }
-  __device__ __forceinline__ float* red() const { return reinterpret_cast<float*>(smem) + 2 * Cfg::BM; }
-  __device__ __forceinline__ float* red2() const { return reinterpret_cast<float*>(smem) + (2 + Cfg::WAVES_N) * Cfg::BM; }
+  __device__ __forceinline__ int lcol(int j, int q) const { return wn0 + 32 * j + 8 * q + 4 * (lane >> 5); }
+  __device__ __forceinline__ int col(int j, int q) const { return n0 + lcol(j, q); }
+  // indices clamped into the matrix, for vector loads whose values only reach
+  // positions that are never stored (keeps the loads unconditional)
+  __device__ __forceinline__ int rowc(int i) const { return min(row(i), M - 1); }
+  __device__ __forceinline__ int colc(int j, int q) const { return min(col(j, q), N - 4); }
+  __device__ __forceinline__ char* stage() const { return smem; }
+  // scratch after the pipeline buffers: two row vectors, two [WAVES_N][BM] arrays
+  __device__ __forceinline__ float* scratch() const { return reinterpret_cast<float*>(smem + Cfg::LDS_BYTES); }
+  __device__ __forceinline__ float* rowv() const { return scratch(); }
+  __device__ __forceinline__ float* rowv2() const { return scratch() + Cfg::BM; }
+  __device__ __forceinline__ float* red() const { return scratch() + 2 * Cfg::BM; }
+  __device__ __forceinline__ float* red2() const { return scratch() + (2 + Cfg::WAVES_N) * Cfg::BM; }
 };
 
-// ---------------------------------------------------------------- P3 tile loads / stores
-__device__ __forceinline__ f32x4_t load_bf16x4(const void* base, int64_t ld, int m, int n) {
-  uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + (int64_t)m * ld + n);
-  return f32x4_t{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
-}
-__device__ __forceinline__ void store_bf16x4(void* base, int64_t ld, int m, int n, f32x4_t v) {
-  uint2 w = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + (int64_t)m * ld + n) = w;
-}
-__device__ __forceinline__ f32x4_t load_f32x4(const void* base, int64_t ld, int m, int n) {
-  return *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(base) + (int64_t)m * ld + n);
-}
-__device__ __forceinline__ void store_f32x4(void* base, int64_t ld, int m, int n, f32x4_t v) {
-  *reinterpret_cast<f32x4_t*>(static_cast<float*>(base) + (int64_t)m * ld + n) = v;
-}
 __device__ __forceinline__ f32x4_t round_bf4(f32x4_t v) {
   return f32x4_t{round_bf(v[0]), round_bf(v[1]), round_bf(v[2]), round_bf(v[3])};
 }
@@ -100,31 +98,150 @@ __device__ __forceinline__ void set_frag(Acc<Cfg>& acc, int i, int j, int q, f32
   for (int t = 0; t < 4; ++t) acc.c[i][j][4 * q + t] = v[t];
 }
 
+// ---------------------------------------------------------------- P3 staging tiles in LDS
+// bf16 tile [R][C]: C * 2 bytes a row, 16-byte chunks XOR-swizzled by row.
+template <int R, int C>
+struct StageBF {
+  static constexpr int CPR = C / 8;
+  static_assert((CPR & (CPR - 1)) == 0, "chunks a row must be a power of two");
+  static constexpr int BYTES = R * C * 2;
+  __device__ __forceinline__ static uint32_t off(int r, int chunk) {
+    return (uint32_t)(r * C * 2 + ((chunk ^ (r & (CPR - 1))) << 4));
+  }
+  // 4 consecutive bf16 at (r, col), col % 4 == 0
+  __device__ __forceinline__ static uint32_t off4(int r, int col) { return off(r, col >> 3) + ((col & 4) << 1); }
+  __device__ __forceinline__ static void put4(char* s, int r, int col, f32x4_t v) {
+    *reinterpret_cast<uint2*>(s + off4(r, col)) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  }
+  __device__ __forceinline__ static f32x4_t get4(const char* s, int r, int col) {
+    uint2 w = *reinterpret_cast<const uint2*>(s + off4(r, col));
+    return f32x4_t{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+  }
+};
+
+// fp32 tile [R][C]: C * 4 bytes a row, 16-byte chunks XOR-swizzled by row.
+template <int R, int C>
+struct StageF32 {
+  static constexpr int CPR = C / 4;
+  static_assert((CPR & (CPR - 1)) == 0, "chunks a row must be a power of two");
+  static constexpr int BYTES = R * C * 4;
+  __device__ __forceinline__ static uint32_t off(int r, int chunk) {
+    return (uint32_t)(r * C * 4 + ((chunk ^ (r & (CPR - 1))) << 4));
+  }
+};
+
+// Workgroup-wide row-contiguous moves between a staging tile and global
+// memory.  dst(m_local, n_local) returns the global address of the 16-byte
+// chunk that starts at local (row, column), or nullptr to skip it.
+template <class Cfg, int R, int C, class Dst>
+__device__ __forceinline__ void stage_store_bf(const char* s, int tid, Dst dst) {
+  using S = StageBF<R, C>;
+#pragma unroll 4
+  for (int id = tid; id < R * S::CPR; id += Cfg::T) {
+    const int r = id / S::CPR, ch = id % S::CPR;
+    uint16_t* p = dst(r, ch * 8);
+    if (p) *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(s + S::off(r, ch));
+  }
+}
+template <class Cfg, int R, int C, class Src>
+__device__ __forceinline__ void stage_load_bf(char* s, int tid, Src src) {
+  using S = StageBF<R, C>;
+#pragma unroll 4
+  for (int id = tid; id < R * S::CPR; id += Cfg::T) {
+    const int r = id / S::CPR, ch = id % S::CPR;
+    const uint16_t* p = src(r, ch * 8);
+    *reinterpret_cast<uint4*>(s + S::off(r, ch)) = p ? *reinterpret_cast<const uint4*>(p) : uint4{0, 0, 0, 0};
+  }
+}
+
+// bf16 matrix at (m0 + r, n0 + col), with bounds (rows < M, cols < N); N % 8 == 0
+struct MatBF {
+  uint16_t* base; int64_t ld; int m0, n0, M, N;
+  __device__ __forceinline__ uint16_t* operator()(int r, int col) const {
+    const int m = m0 + r, n = n0 + col;
+    return (m < M && n < N) ? base + (int64_t)m * ld + n : nullptr;
+  }
+};
+struct CMatBF {
+  const uint16_t* base; int64_t ld; int m0, n0, M, N;
+  __device__ __forceinline__ const uint16_t* operator()(int r, int col) const {
+    const int m = m0 + r, n = n0 + col;
+    return (m < M && n < N) ? base + (int64_t)m * ld + n : nullptr;
+  }
+};
+
+// Register values -> bf16 staging tile (rows of this wave, all its columns).
+template <class Cfg, int C>
+__device__ __forceinline__ void put_tile(const Ctx<Cfg>& c, const Acc<Cfg>& acc) {
+  char* s = c.stage();
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) StageBF<Cfg::BM, C>::put4(s, c.lrow(i), c.lcol(j, q), frag(acc, i, j, q));
+}
+
+// fp32 output D = beta D + v for the tile, staged through LDS in row halves
+// (128 KB each); v is in the register layout in acc.
+template <class Cfg>
+__device__ __forceinline__ void store_f32_tile(const EpiArgs& e, const Ctx<Cfg>& c, const Acc<Cfg>& acc) {
+  constexpr int HR = Cfg::BM / 2;
+  using S = StageF32<HR, Cfg::BN>;
+  static_assert(S::BYTES <= Cfg::LDS_BYTES, "half tile must fit the staging area");
+  char* s = c.stage();
+  float* out = static_cast<float*>(e.out);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const int r = c.lrow(i) - h * HR;
+      if (r < 0 || r >= HR) continue;
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(s + S::off(r, c.lcol(j, q) >> 2)) = frag(acc, i, j, q);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int id = c.tid; id < HR * S::CPR; id += Cfg::T) {
+      const int r = id / S::CPR, ch = id % S::CPR;
+      const int m = c.m0 + h * HR + r, n = c.n0 + ch * 4;
+      if (m >= c.M || n >= c.N) continue;
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(s + S::off(r, ch));
+      f32x4_t* p = reinterpret_cast<f32x4_t*>(out + (int64_t)m * e.ld_out + n);
+      if (e.beta != 0.0f) v = v + e.beta * *p;
+      *p = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- P2 vector loads: fp8 dequant scales
 // acc <- acc * s_row[m] * s_col[n] (the per-token and per-channel E4M3 scales)
 template <class Cfg>
 __device__ __forceinline__ void apply_fp8_scales(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc) {
   if constexpr (Cfg::FP8) {
+    float sr[Cfg::TM];
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) {
-      int m = c.row(i);
-      float sr = m < c.M ? e.rowscale[m] : 0.0f;
+    for (int i = 0; i < Cfg::TM; ++i) sr[i] = e.rowscale[c.rowc(i)];
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
+    for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int n = c.col(j, q);
-          f32x4_t sc = n < c.N ? *reinterpret_cast<const f32x4_t*>(e.colscale + n) : f32x4_t{0, 0, 0, 0};
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(e.colscale + c.colc(j, q));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc.c[i][j][4 * q + t] = (acc.c[i][j][4 * q + t] * sr) * sc[t];
-        }
-    }
+        for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc.c[i][j][4 * q + t] = (acc.c[i][j][4 * q + t] * sr[i]) * sc[t];
+      }
   }
 }
 
 // ---------------------------------------------------------------- P4 row reduction over the tile
 // part[i] is this lane's share of local row lrow(i); writes the tile total of
-// every local row to out[BM] (LDS) in a fixed order.
+// every local row to out[BM] (LDS scratch) in a fixed order.
 template <class Cfg>
 __device__ __forceinline__ void row_sum_tile(const Ctx<Cfg>& c, float (&part)[Cfg::TM], float* out) {
   float* red = c.red();
@@ -187,6 +304,22 @@ struct RowPartials {
   }
 };
 
+// Finishes the per-row factor of the tile's rows into c.rowv():
+// r = (sum of partials / D + eps)^(-1/2), or a given row vector.
+template <class Cfg>
+__device__ __forceinline__ void finish_inv_rms(const EpiArgs& e, const Ctx<Cfg>& c, const RowPartials<Cfg>& rp) {
+  float* rv = c.rowv();
+  if (e.row_partials) {
+    rp.reduce(c, rv);
+    if (c.tid < Cfg::BM) rv[c.tid] = rsqrtf(rv[c.tid] / (float)e.norm_dim + e.eps);
+  } else if (c.tid < Cfg::BM) {
+    int m = c.m0 + c.tid;
+    rv[c.tid] = m < c.M ? e.rowvec[m] : 0.0f;
+  }
+  __syncthreads();
+  if (e.rowvec_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M) e.rowvec_out[c.m0 + c.tid] = rv[c.tid];
+}
+
 // ================================================================ programs
 
 // --- Linear chain: [row scale] [col scale] [alpha] [+ tile] -> store [+ sum-of-squares partial]
@@ -204,44 +337,54 @@ struct EpiLinear {
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
     apply_fp8_scales<Cfg>(e, c, acc);
     float alpha = e.alpha;
     if constexpr (FLAGS & EL_ALPHADEV) alpha *= *e.alpha_dev;
+    if constexpr (FLAGS & EL_TILEADD) {
+      stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
+          CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
+      __syncthreads();
+    }
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       part[i] = 0.0f;
       const int m = c.row(i);
-      const bool mok = m < c.M;
       float rv = 1.0f;
-      if constexpr (FLAGS & EL_ROWVEC) rv = mok ? e.rowvec[m] : 0.0f;
+      if constexpr (FLAGS & EL_ROWVEC) rv = e.rowvec[c.rowc(i)];
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = c.col(j, q);
-          if (!mok || n >= c.N) continue;
           f32x4_t v = frag(acc, i, j, q);
           if constexpr (FLAGS & EL_ROWVEC) v = v * rv;
-          if constexpr (FLAGS & EL_COLVEC) v = v * *reinterpret_cast<const f32x4_t*>(e.colvec + n);
+          if constexpr (FLAGS & EL_COLVEC)
+            v = v * *reinterpret_cast<const f32x4_t*>(e.colvec + c.colc(j, q));
           v = v * alpha;
-          if constexpr (FLAGS & EL_TILEADD) v = v + load_bf16x4(e.aux0, e.ld_aux0, m, n);
-          if constexpr (FLAGS & EL_F32OUT) {
-            if (e.beta != 0.0f) v = v + e.beta * load_f32x4(e.out, e.ld_out, m, n);
-            store_f32x4(e.out, e.ld_out, m, n, v);
-          } else {
-            store_bf16x4(e.out, e.ld_out, m, n, v);
-            if constexpr (FLAGS & EL_SUMSQ) {
-              f32x4_t s = round_bf4(v);
-              part[i] += s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
-            }
+          if constexpr (FLAGS & EL_TILEADD) v = v + S::get4(c.stage(), c.lrow(i), c.lcol(j, q));
+          if constexpr (!(FLAGS & EL_F32OUT)) {
+            v = round_bf4(v);
+            if constexpr (FLAGS & EL_SUMSQ)
+              if (m < c.M && n < c.N) part[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
           }
+          set_frag(acc, i, j, q, v);
         }
     }
-    if constexpr (FLAGS & EL_SUMSQ) {
-      float* tot = c.rowv();
-      row_sum_tile<Cfg>(c, part, tot);
-      write_row_partial<Cfg>(c, tot, e.partial_out);
+    if constexpr (FLAGS & EL_F32OUT) {
+      store_f32_tile<Cfg>(e, c, acc);
+    } else {
+      if constexpr (FLAGS & EL_TILEADD) __syncthreads();   // every lane has read its residual
+      put_tile<Cfg, Cfg::BN>(c, acc);
+      __syncthreads();
+      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
+          MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
+      if constexpr (FLAGS & EL_SUMSQ) {
+        float* tot = c.rowv();
+        row_sum_tile<Cfg>(c, part, tot);
+        write_row_partial<Cfg>(c, tot, e.partial_out);
+      }
     }
   }
 };
@@ -258,42 +401,40 @@ struct EpiSwiGLU {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
-    float* rv = c.rowv();
-    if (e.row_partials) {
-      p.rp.reduce(c, rv);
-      if (c.tid < Cfg::BM) rv[c.tid] = rsqrtf(rv[c.tid] / (float)e.norm_dim + e.eps);
-    } else if (c.tid < Cfg::BM) {
-      int m = c.m0 + c.tid;
-      rv[c.tid] = m < c.M ? e.rowvec[m] : 0.0f;
-    }
-    __syncthreads();
-    if (e.rowvec_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M)
-      e.rowvec_out[c.m0 + c.tid] = rv[c.tid];
+    finish_inv_rms<Cfg>(e, c, p.rp);
     apply_fp8_scales<Cfg>(e, c, acc);
-    const int F = c.N / 2;
+    const float* rv = c.rowv();
+    // h = r * acc (kept in acc); a = SiLU(h_gate) * h_up staged as [BM][BN/2]
+    constexpr int CA = Cfg::BN / 2;
+    char* s = c.stage();
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
-      const int m = c.row(i);
-      if (m >= c.M) continue;
       const float r = rv[c.lrow(i)];
 #pragma unroll
       for (int p2 = 0; p2 < Cfg::TN / 2; ++p2)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ng = c.col(2 * p2, q);              // packed gate column
-          const int f = (ng >> 6) * 32 + (ng & 31);     // output column
-          if (f >= F) continue;
           f32x4_t hg = frag(acc, i, 2 * p2, q) * r;
           f32x4_t hu = frag(acc, i, 2 * p2 + 1, q) * r;
           f32x4_t a;
 #pragma unroll
           for (int t = 0; t < 4; ++t) a[t] = hg[t] * sigmoidf_(hg[t]) * hu[t];
-          store_bf16x4(e.out, e.ld_out, m, f, a);
-          if (e.save) {
-            store_bf16x4(e.save, e.ld_save, m, ng, hg);
-            store_bf16x4(e.save, e.ld_save, m, ng + 32, hu);
-          }
+          set_frag(acc, i, 2 * p2, q, hg);
+          set_frag(acc, i, 2 * p2 + 1, q, hu);
+          // local output column of gate column lcol: 32 per 64-column block
+          const int lc = c.lcol(2 * p2, q);
+          StageBF<Cfg::BM, CA>::put4(s, c.lrow(i), (lc >> 6) * 32 + (lc & 31), a);
         }
+    }
+    __syncthreads();
+    const int F = c.N / 2;
+    stage_store_bf<Cfg, Cfg::BM, CA>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0 / 2, c.M, F});
+    if (e.save) {
+      __syncthreads();
+      put_tile<Cfg, Cfg::BN>(c, acc);
+      __syncthreads();
+      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+          MatBF{static_cast<uint16_t*>(e.save), e.ld_save, c.m0, c.n0, c.M, c.N});
     }
   }
 };
@@ -309,22 +450,13 @@ struct EpiQKNormRope {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
-    float* rv = c.rowv();
-    if (e.row_partials) {
-      p.rp.reduce(c, rv);
-      if (c.tid < Cfg::BM) rv[c.tid] = rsqrtf(rv[c.tid] / (float)e.norm_dim + e.eps);
-    } else if (c.tid < Cfg::BM) {
-      int m = c.m0 + c.tid;
-      rv[c.tid] = m < c.M ? e.rowvec[m] : 0.0f;
-    }
-    __syncthreads();
-    if (e.rowvec_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M)
-      e.rowvec_out[c.m0 + c.tid] = rv[c.tid];
+    finish_inv_rms<Cfg>(e, c, p.rp);
     apply_fp8_scales<Cfg>(e, c, acc);
+    const float* rv = c.rowv();
     const int D = e.region;
-    const int head_base = c.n0 + c.wn0;                 // wave's first column
-    const int reg = head_base / D;                       // 0 q, 1 k, 2 v (whole wave)
-    // pre-norm values h = r1 * acc, and per-head partial sums of squares
+    const int reg = (c.n0 + c.wn0) / D;                  // 0 q, 1 k, 2 v (whole wave)
+    char* s = c.stage();
+    // pre-norm values h = r1 * acc and per-head partial sums of squares
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
@@ -339,52 +471,65 @@ struct EpiQKNormRope {
           part[i] += h * h;
         }
     }
+    // save of the pre-norm q, k (columns < 2D)
+    if (e.save) {
+      put_tile<Cfg, Cfg::BN>(c, acc);
+      __syncthreads();
+      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+          MatBF{static_cast<uint16_t*>(e.save), e.ld_save, c.m0, c.n0, c.M, 2 * D});
+      __syncthreads();
+    }
     // combine the lane pair, then the waves covering the same head
     constexpr int WPH = 128 / Cfg::WN;                   // waves per head
     float* red = c.red();
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
-      float s = part[i] + __shfl_xor(part[i], 32, 64);
-      if ((c.lane >> 5) == 0) red[c.wn * Cfg::BM + c.lrow(i)] = s;
+      float sp = part[i] + __shfl_xor(part[i], 32, 64);
+      if ((c.lane >> 5) == 0) red[c.wn * Cfg::BM + c.lrow(i)] = sp;
     }
     __syncthreads();
     const int w0 = (c.wn / WPH) * WPH;
     const float* g = reg == 0 ? e.colvec : e.colvec2;
+    if (reg < 2) {
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) {
-      const int m = c.row(i);
-      if (m >= c.M) continue;
-      float ss = 0.0f;
+      for (int i = 0; i < Cfg::TM; ++i) {
+        const int m = c.row(i);
+        float ss = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WPH; ++w) ss += red[(w0 + w) * Cfg::BM + c.lrow(i)];
-      const float rho = rsqrtf(ss / 128.0f + e.eps);
-      const int pos = m % e.seq_len;
+        for (int w = 0; w < WPH; ++w) ss += red[(w0 + w) * Cfg::BM + c.lrow(i)];
+        const float rho = rsqrtf(ss / 128.0f + e.eps);
+        const int pos = (m < c.M ? m : 0) % e.seq_len;
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
+        for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = c.col(j, q);
-          if (n >= c.N) continue;
-          f32x4_t h = frag(acc, i, j, q);
-          if (reg == 2) {
-            store_bf16x4(e.out3, e.ld_out3, m, n - 2 * D, h);
-            continue;
+          for (int q = 0; q < 4; ++q) {
+            const int cc = c.col(j, q) & 127;                // column inside the head
+            f32x4_t h = frag(acc, i, j, q);
+            f32x4_t gg = *reinterpret_cast<const f32x4_t*>(g + cc);
+            f32x4_t y = h * rho * gg;
+            // pairs (cc, cc+1) and (cc+2, cc+3) -> frequencies cc/2, cc/2 + 1
+            f32x4_t cs = *reinterpret_cast<const f32x4_t*>(e.table + ((int64_t)pos * 64 + (cc >> 1)) * 2);
+            f32x4_t o;
+            o[0] = y[0] * cs[0] - y[1] * cs[1];
+            o[1] = y[0] * cs[1] + y[1] * cs[0];
+            o[2] = y[2] * cs[2] - y[3] * cs[3];
+            o[3] = y[2] * cs[3] + y[3] * cs[2];
+            set_frag(acc, i, j, q, o);
           }
-          const int cc = n & 127;                          // column inside the head
-          if (e.save) store_bf16x4(e.save, e.ld_save, m, n, h);
-          f32x4_t gg = *reinterpret_cast<const f32x4_t*>(g + cc);
-          f32x4_t y = h * rho * gg;
-          // pairs (cc, cc+1) and (cc+2, cc+3) -> frequencies cc/2, cc/2 + 1
-          f32x4_t cs = *reinterpret_cast<const f32x4_t*>(e.table + ((int64_t)pos * 64 + (cc >> 1)) * 2);
-          f32x4_t o;
-          o[0] = y[0] * cs[0] - y[1] * cs[1];
-          o[1] = y[0] * cs[1] + y[1] * cs[0];
-          o[2] = y[2] * cs[2] - y[3] * cs[3];
-          o[3] = y[2] * cs[3] + y[3] * cs[2];
-          if (reg == 0) store_bf16x4(e.out, e.ld_out, m, n, o);
-          else store_bf16x4(e.out2, e.ld_out2, m, n - D, o);
-        }
+      }
     }
+    put_tile<Cfg, Cfg::BN>(c, acc);
+    __syncthreads();
+    // split store: each 16-byte chunk lies inside one of q, k, v (D % 8 == 0)
+    uint16_t* outs[3] = {static_cast<uint16_t*>(e.out), static_cast<uint16_t*>(e.out2), static_cast<uint16_t*>(e.out3)};
+    const int64_t lds_[3] = {e.ld_out, e.ld_out2, e.ld_out3};
+    const int m0 = c.m0, n0 = c.n0, M = c.M, N = c.N;
+    stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, [&](int r, int col) -> uint16_t* {
+      const int m = m0 + r, n = n0 + col;
+      if (m >= M || n >= N) return nullptr;
+      const int rg = n / D;
+      return outs[rg] + (int64_t)m * lds_[rg] + (n - rg * D);
+    });
   }
 };
 
@@ -392,40 +537,61 @@ struct EpiQKNormRope {
 // loads the saved gate/up pre-activations (packed layout), forms dhg, dhu,
 // scales by r2 and stores dh~ (bf16, packed), plus the partials
 // T[tn][m] = sum over the tile of dh~ . h (for the RMSNorm backward).
+// The tile's F columns [n0, n0 + BN) are the packed columns [2 n0, 2 n0 + 2 BN),
+// handled in two phases of BN packed columns (waves of half the tile each).
 template <class Cfg>
 struct EpiDSwiGLU {
+  static_assert(Cfg::WAVES_N % 2 == 0, "two column phases");
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
     apply_fp8_scales<Cfg>(e, c, acc);
+    char* s = c.stage();
+    const int HN = Cfg::BN / 2;                          // F columns a phase
+    const int N2 = 2 * c.N;                              // packed width
     float part[Cfg::TM];
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) {
-      part[i] = 0.0f;
-      const int m = c.row(i);
-      if (m >= c.M) continue;
-      const float r = e.rowvec[m];
+    for (int i = 0; i < Cfg::TM; ++i) part[i] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
+    for (int ph = 0; ph < 2; ++ph) {
+      const int pc0 = 2 * c.n0 + ph * Cfg::BN;           // first packed column of the phase
+      stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+          CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, pc0, c.M, N2});
+      __syncthreads();
+      if (c.wn0 / HN == ph) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = c.col(j, q);
-          if (f >= c.N) continue;
-          const int pg = (f >> 5) * 64 + (f & 31);
-          f32x4_t hg = load_bf16x4(e.aux0, e.ld_aux0, m, pg);
-          f32x4_t hu = load_bf16x4(e.aux0, e.ld_aux0, m, pg + 32);
-          f32x4_t da = frag(acc, i, j, q);
-          f32x4_t dg, du;
+        for (int i = 0; i < Cfg::TM; ++i) {
+          const int m = c.row(i);
+          const float r = e.rowvec[c.rowc(i)];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float s = sigmoidf_(hg[t]);
-            dg[t] = round_bf(r * (da[t] * hu[t] * s * (1.0f + hg[t] * (1.0f - s))));
-            du[t] = round_bf(r * (da[t] * hg[t] * s));
-            part[i] += dg[t] * hg[t] + du[t] * hu[t];
-          }
-          store_bf16x4(e.out, e.ld_out, m, pg, dg);
-          store_bf16x4(e.out, e.ld_out, m, pg + 32, du);
+          for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int fl = c.lcol(j, q) - ph * HN;        // F column inside the phase
+              const int pg = (fl >> 5) * 64 + (fl & 31);    // its packed gate column
+              const f32x4_t hg = S::get4(s, c.lrow(i), pg);
+              const f32x4_t hu = S::get4(s, c.lrow(i), pg + 32);
+              const f32x4_t da = frag(acc, i, j, q);
+              f32x4_t dg, du;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float sg = sigmoidf_(hg[t]);
+                dg[t] = round_bf(r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg))));
+                du[t] = round_bf(r * (da[t] * hg[t] * sg));
+              }
+              if (m < c.M && c.col(j, q) < c.N)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) part[i] += dg[t] * hg[t] + du[t] * hu[t];
+              S::put4(s, c.lrow(i), pg, dg);                 // in place: this lane owns both slots
+              S::put4(s, c.lrow(i), pg + 32, du);
+            }
         }
+      }
+      __syncthreads();
+      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+          MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, pc0, c.M, N2});
+      __syncthreads();
     }
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
@@ -442,30 +608,44 @@ struct EpiNormCorrection {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
     float* cv = c.rowv();
     p.rp.reduce(c, cv);
     if (c.tid < Cfg::BM) {
       int m = c.m0 + c.tid;
       cv[c.tid] = m < c.M ? e.rowvec[m] * cv[c.tid] / (float)e.norm_dim : 0.0f;
     }
-    __syncthreads();
     apply_fp8_scales<Cfg>(e, c, acc);
+    char* s = c.stage();
+    // phase 1: - c u
+    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+        CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
-      const int m = c.row(i);
-      if (m >= c.M) continue;
       const float cc = cv[c.lrow(i)];
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = c.col(j, q);
-          if (n >= c.N) continue;
-          f32x4_t v = frag(acc, i, j, q) - cc * load_bf16x4(e.aux0, e.ld_aux0, m, n);
-          v = v + load_bf16x4(e.aux1, e.ld_aux1, m, n);
-          store_bf16x4(e.out, e.ld_out, m, n, v);
-        }
+        for (int q = 0; q < 4; ++q)
+          set_frag(acc, i, j, q, frag(acc, i, j, q) - cc * S::get4(s, c.lrow(i), c.lcol(j, q)));
     }
+    __syncthreads();
+    // phase 2: + res, round, store
+    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+        CMatBF{static_cast<const uint16_t*>(e.aux1), e.ld_aux1, c.m0, c.n0, c.M, c.N});
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          set_frag(acc, i, j, q, frag(acc, i, j, q) + S::get4(s, c.lrow(i), c.lcol(j, q)));
+    __syncthreads();
+    put_tile<Cfg, Cfg::BN>(c, acc);
+    __syncthreads();
+    stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }
 };
 
@@ -476,31 +656,33 @@ struct EpiWgradGain {
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
     apply_fp8_scales<Cfg>(e, c, acc);
+    char* s = c.stage();
+    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+        CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
+    __syncthreads();
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       part[i] = 0.0f;
       const int m = c.row(i);
-      if (m >= c.M) continue;
-      const float g = e.rowvec[m];
+      const float g = e.rowvec[c.rowc(i)];
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = c.col(j, q);
-          if (n >= c.N) continue;
-          f32x4_t a = frag(acc, i, j, q);
-          f32x4_t w = load_bf16x4(e.aux0, e.ld_aux0, m, n);
+          const f32x4_t a = frag(acc, i, j, q);
+          const f32x4_t w = S::get4(s, c.lrow(i), c.lcol(j, q));   // zero outside the matrix
           part[i] += w[0] * a[0] + w[1] * a[1] + w[2] * a[2] + w[3] * a[3];
-          f32x4_t v = g * a;
-          if (e.beta != 0.0f) v = v + e.beta * load_f32x4(e.out, e.ld_out, m, n);
-          store_f32x4(e.out, e.ld_out, m, n, v);
+          set_frag(acc, i, j, q, g * a);
         }
     }
+    // the reduction first: partials kept live across the staged store cost spills
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
     write_row_partial<Cfg>(c, tot, e.partial_out);
+    store_f32_tile<Cfg>(e, c, acc);
   }
 };
 
@@ -525,7 +707,8 @@ struct EpiCrossEntropy {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       const int m = c.row(i);
-      const int y = m < c.M ? e.labels[m] : -1;
+      const int yl = e.labels[c.rowc(i)];
+      const int y = m < c.M ? yl : -1;
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
@@ -583,32 +766,35 @@ struct EpiCrossEntropyGrad {
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       const int m = c.row(i);
-      if (m >= c.M) continue;
-      const int y = e.labels[m];
-      const bool valid = y != -100;
-      const float lse = e.rowvec[m];
+      const int y = e.labels[c.rowc(i)];
+      const bool valid = m < c.M && y != -100;
+      const float lse = e.rowvec[c.rowc(i)];
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = c.col(j, q);
-          if (n >= c.N) continue;
           f32x4_t gv;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             float p = __expf(acc.c[i][j][4 * q + t] - lse) - (n + t == y ? 1.0f : 0.0f);
             gv[t] = valid ? p : 0.0f;
           }
-          store_bf16x4(e.out, e.ld_out, m, n, gv);
+          set_frag(acc, i, j, q, gv);
         }
     }
+    put_tile<Cfg, Cfg::BN>(c, acc);
+    __syncthreads();
+    stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
+        MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }
 };
 
 // ================================================================ the kernel
+// One output tile per workgroup; the XCD-aware tile order lives in tile_coord.
 template <class Cfg, class Epi>
 __global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES + scratch_bytes<Cfg>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TileCoord tc = tile_coord(blockIdx.x, g.tiles_m, g.tiles_n, 8);
   Ctx<Cfg> c;

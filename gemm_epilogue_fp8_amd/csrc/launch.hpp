@@ -43,9 +43,9 @@ template <class Cfg, class Epi>
 hipError_t launch_one(GemmArgs g, const EpiArgs& e, hipStream_t s) {
   g.tiles_m = tiles(g.M, Cfg::BM);
   g.tiles_n = tiles(g.N, Cfg::BN);
-  const int grid = g.tiles_m * g.tiles_n;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_epi_kernel<Cfg, Epi>), dim3(grid), dim3(Cfg::T), 0, s, g, e);
+  const int ntiles = g.tiles_m * g.tiles_n;
+  if (ntiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_epi_kernel<Cfg, Epi>), dim3(ntiles), dim3(Cfg::T), 0, s, g, e);
   return hipGetLastError();
 }
 
