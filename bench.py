@@ -74,7 +74,23 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Three copies of exactly 1 GiB between two device buffers: a kernel whose
+    HBM traffic is known (1 GiB read + 1 GiB written per launch)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 3}))
 
 
 def cpu_baseline(shape_full, seed, rows, fp8):
@@ -99,6 +115,9 @@ def cpu_baseline(shape_full, seed, rows, fp8):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
               f"run with --gpus 1", file=sys.stderr)
