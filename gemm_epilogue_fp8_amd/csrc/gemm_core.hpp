@@ -6,19 +6,32 @@
 // mainloop fixed and programs only the epilogue; this file is that fixed part.
 //
 // Design (CDNA4-first, not a port of the paper's Hopper kernels):
-//  * Workgroup tile BM x BN, 128 bytes of K per stage (64 bf16 or 128 fp8),
-//    two LDS stages: while the MFMAs of stage k run, stage k+1 streams from
-//    global memory straight into the other LDS buffer (buffer_load ... lds:
-//    lane l of a wave instruction writes 16 bytes at lds + 16 l), so no
-//    registers stage the operands.  One barrier per stage.
-//  * A K-contiguous operand tile is [rows][128 bytes] with its 16-byte chunks
-//    XOR-swizzled by (r ^ r>>2 ^ r>>3) & 7; each lane picks the global chunk
-//    that belongs at its fixed LDS slot.  gfx950 LDS serves a 16-byte access
-//    16 lanes at a time over 64 banks: the fragment reads (16 rows, one
-//    chunk) and the stores (2 rows, 8 chunks) both hit 16 distinct slots.
+//  * Workgroup tile BM x BN = 256 x 256, 8 waves in two groups of four.  Group
+//    g owns rows [128 g, 128 g + 128) of the tile; wave w of a group owns the
+//    64 columns [64 w, 64 w + 64).  The hardware deals a workgroup's waves
+//    round-robin over the CU's 4 SIMDs, so each SIMD holds one wave of each
+//    group.
+//  * Wave-group ping-pong.  The K loop runs in phases separated by
+//    workgroup barriers.  In a "memory" phase a wave reads its MFMA fragments
+//    of one K step from LDS into registers and issues its group's share of a
+//    future stage's global->LDS copies; in a "compute" phase it only issues
+//    MFMAs.  Group 1 starts one phase late, so on every SIMD one wave keeps
+//    the matrix core busy while the other one moves data, and the barriers
+//    cost no MFMA time.  (The paper's Hopper design gets the same overlap
+//    from two consumer warpgroups, §1; here it is two waves per SIMD.)
+//  * K step 64 bytes (32 bf16 or 64 fp8); 4 LDS stages of (256 + 256) x 64 B.
+//    Stage s streams from global memory straight into LDS (buffer_load ...
+//    lds: lane l of a wave instruction writes 16 bytes at lds + 16 l, no
+//    registers), issued 3 steps ahead: group 0 copies the A tile, group 1 the
+//    B tile.  Each wave waits (vmcnt) only for the stage that is read next.
+//  * A K-contiguous operand tile is [rows][64 bytes] with its 16-byte chunks
+//    XOR-swizzled by (r >> 2) & 3; each lane picks the global chunk that
+//    belongs at its fixed LDS slot.  gfx950 LDS serves a 16-byte access 16
+//    lanes at a time over 64 banks: a fragment read (16 rows, one chunk)
+//    touches 16 distinct 16-byte bank groups.
 //  * An M/N-contiguous operand (the weight of a forward NN product, both
 //    operands of a TN weight gradient) keeps its storage order in LDS:
-//    [64 k rows][R columns], chunks XOR-swizzled by 4 (k & 3).  Its MFMA
+//    [32 k rows][256 columns], chunks XOR-swizzled by 4 (k & 3).  Its MFMA
 //    fragments come from ds_read_b64_tr_b16: in each 16-lane group, lane i
 //    receives element i % 4 of the 4-element loads of lanes 4u + i/4, so
 //    lanes pointing at (row kb + j/4, column c0 + 4 (j % 4)) deliver to lane
@@ -29,8 +42,6 @@
 //  * MFMA operands are swapped (the B tile feeds the instruction's A port),
 //    which leaves each lane holding 4 consecutive output columns of one row:
 //    8-byte bf16 stores and in-lane pairwise transforms (RoPE pairs).
-//  * Fragments of substep s+1 are read while substep s multiplies (pinned
-//    with scheduling barriers).
 //  * Workgroup ids are remapped so that the tiles one XCD (8 per chip, each
 //    with its own L2) runs are neighbours, then grouped along M.
 #pragma once
@@ -48,11 +59,13 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 __device__ void raw_ptr_buffer_load_lds(__amdgpu_buffer_rsrc_t rsrc, lds_void_t* lds, int size, int voffset,
                                         int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.lds");
 
-__device__ __forceinline__ int kc_swz(int row) { return (row ^ (row >> 2) ^ (row >> 3)) & 7; }
+constexpr int kRowBytes = 64;   // bytes of K a stage holds per operand row
 
-// byte offset of (row, 16-byte chunk) in a K-contiguous [rows][128 B] tile
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
+
+// byte offset of (row, 16-byte chunk) in a K-contiguous [rows][64 B] tile
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ kc_swz(row)) << 4));
+  return (uint32_t)(row * kRowBytes + ((chunk ^ kc_swz(row)) << 4));
 }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool A_KC_, bool B_KC_, bool FP8_ = false>
@@ -63,10 +76,12 @@ struct GemmCfg {
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr bool A_KC = A_KC_, B_KC = B_KC_, FP8 = FP8_;
   static constexpr int ESIZE = FP8 ? 1 : 2;
-  static constexpr int BK = 128 / ESIZE;
-  static constexpr int STAGE_BYTES = (BM + BN) * 128;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int BK = kRowBytes / ESIZE;     // K per stage: 32 bf16 or 64 fp8
+  static constexpr int NS = 4;                     // LDS stages
+  static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(WAVES_M == 2, "the two wave groups are the two row halves of the tile");
   static_assert(!FP8 || (A_KC && B_KC), "fp8 operands are K-contiguous");
 };
 
@@ -79,22 +94,23 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- operand tiles
-// K-contiguous operand stored [rows, K]: tile = R rows x 128 bytes of K.
+// K-contiguous operand stored [rows, K]: tile = R rows x 64 bytes of K,
+// copied by the WAVES_N waves of one group.
 template <class Cfg, int R>
 struct TileKC {
-  static constexpr int NI = R * 128 / 1024 / Cfg::NWAVES;   // 1 KB wave instructions per wave
-  static_assert(R * 128 % (1024 * Cfg::NWAVES) == 0, "tile must split into 1 KB wave loads");
+  static constexpr int NI = R * kRowBytes / 1024 / Cfg::WAVES_N;   // 1 KB wave instructions per wave
+  static_assert(R * kRowBytes % (1024 * Cfg::WAVES_N) == 0, "tile must split into 1 KB wave loads");
 
   __device__ __forceinline__ static void issue(const char* base, int64_t ld_bytes, int row0, int nrows,
-                                               int64_t kbyte0, int64_t kbytes, char* lds, int wave, int lane) {
+                                               int64_t kbyte0, int64_t kbytes, char* lds, int w, int lane) {
     const char* p = base + (int64_t)row0 * ld_bytes + kbyte0;
     const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld_bytes + (uint64_t)(kbytes - kbyte0);
     const auto rs = make_rsrc(p, rem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = wave + Cfg::NWAVES * i;            // 8 rows per instruction
-      const int row = 8 * q + (lane >> 3);
-      const int chunk = (lane & 7) ^ kc_swz(row);      // the chunk that lives at this slot
+      const int q = w + Cfg::WAVES_N * i;              // 16 rows per instruction
+      const int row = 16 * q + (lane >> 2);
+      const int chunk = (lane & 3) ^ kc_swz(row);      // the chunk that lives at this slot
       const bool ok = (row0 + row < nrows) && (kbyte0 + chunk * 16 < kbytes);
       const uint32_t off = ok ? (uint32_t)(row * ld_bytes + chunk * 16) : kOobOffset;
       raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)off, 0, 0, 0);
@@ -102,26 +118,28 @@ struct TileKC {
   }
 };
 
-// M/N-contiguous bf16 operand stored [K, cols]: tile = 64 k rows x R columns.
+// M/N-contiguous bf16 operand stored [K, cols]: tile = BK k rows x R columns,
+// copied by the WAVES_N waves of one group.
 template <class Cfg, int R>
 struct TileMN {
   static constexpr int ROWB = 2 * R;                       // bytes per k row
   static constexpr int CPR = ROWB / 16;                    // chunks per k row
   static constexpr int RPI = 1024 / ROWB;                  // k rows per wave instruction
-  static constexpr int NI = 64 * ROWB / 1024 / Cfg::NWAVES;
-  static_assert(64 * ROWB % (1024 * Cfg::NWAVES) == 0, "tile must split into 1 KB wave loads");
+  static constexpr int NI = Cfg::BK * ROWB / 1024 / Cfg::WAVES_N;
+  static_assert(Cfg::BK * ROWB % (1024 * Cfg::WAVES_N) == 0, "tile must split into 1 KB wave loads");
+  static_assert(Cfg::FP8 || 2 * Cfg::BK == kRowBytes, "an M/N tile has the bytes of a K-contiguous one");
   static_assert(CPR >= 16, "swizzle needs at least 16 chunks a row");
 
   __device__ __forceinline__ static int swz(int krow) { return 4 * (krow & 3); }
 
   __device__ __forceinline__ static void issue(const char* base, int64_t ld_bytes, int k0, int K, int col0,
-                                               int ncols, char* lds, int wave, int lane) {
+                                               int ncols, char* lds, int w, int lane) {
     const char* p = base + (int64_t)k0 * ld_bytes + (int64_t)col0 * 2;
     const uint64_t rem = (uint64_t)(K - k0 - 1) * (uint64_t)ld_bytes + (uint64_t)(ncols - col0) * 2;
     const auto rs = make_rsrc(p, rem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = wave + Cfg::NWAVES * i;
+      const int q = w + Cfg::WAVES_N * i;
       const int krow = RPI * q + lane / CPR;
       const int chunk = (lane % CPR) ^ swz(krow);
       const bool ok = (k0 + krow < K) && (col0 + chunk * 8 < ncols);
@@ -181,13 +199,14 @@ struct Frags {
 };
 
 template <class Cfg>
-constexpr int substeps() { return Cfg::FP8 ? 2 : 4; }
+constexpr int substeps() { return Cfg::FP8 ? 1 : 2; }
 
 template <class Cfg, bool KC, int R>
 __device__ __forceinline__ typename Frags<Cfg>::T read_frag(const char* tile, int r0, int s, int lane) {
   if constexpr (Cfg::FP8) {
     const int row = r0 + (lane & 31);
-    const int chunk = 4 * s + 2 * (lane >> 5);
+    const int chunk = 2 * (lane >> 5);
+    (void)s;
     i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, chunk));
     i32x4_t up = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, chunk + 1));
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
@@ -222,7 +241,37 @@ __device__ __forceinline__ void mma_frags(const Frags<Cfg>& f, Acc<Cfg>& acc) {
     }
 }
 
-// Runs the whole K loop for the tile at (m0, n0); acc starts at zero.
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8]; the other counters at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// s_waitcnt lgkmcnt(0), vmcnt and expcnt unconstrained
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that neither waits for outstanding memory operations nor
+// lets the compiler move instructions across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Waits until at most `stages` stages of this wave's copies are in flight.
+template <int LPS, int NS>
+__device__ __forceinline__ void wait_stages(int stages) {
+  static_assert(NS == 4, "three stages of look-ahead");
+  if (stages <= 0) wait_vmcnt<0>();
+  else if (stages == 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<2 * LPS>();
+}
+
+// Runs the whole K loop for the tile at (m0, n0); acc starts at zero.  Every
+// wave of the workgroup passes the same number of barriers (2 nk + 1).
 template <class Cfg>
 __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>& acc,
                                          int m0, int n0, int wm0, int wn0, int tid, int lane) {
@@ -239,54 +288,59 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
   const int64_t kbytes = (int64_t)g.K * Cfg::ESIZE;
   const int nk = (g.K + Cfg::BK - 1) / Cfg::BK;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int NS = substeps<Cfg>();
+  const int grp = wave / Cfg::WAVES_N;     // 0 copies A and leads; 1 copies B and trails one phase
+  const int w = wave % Cfg::WAVES_N;
+  constexpr int NS = Cfg::NS;
+  constexpr int SUB = substeps<Cfg>();
+  // copies one stage issues per wave (each group copies one operand tile)
+  constexpr int LPS = Cfg::A_KC ? TileKC<Cfg, Cfg::BM>::NI : TileMN<Cfg, Cfg::BM>::NI;
+  static_assert(LPS == (Cfg::B_KC ? TileKC<Cfg, Cfg::BN>::NI : TileMN<Cfg, Cfg::BN>::NI),
+                "both groups issue the same number of copies");
 
-  auto issue_stage = [&](int kt, int buf) {
-    char* As = smem + buf * Cfg::STAGE_BYTES;
-    char* Bs = As + Cfg::BM * 128;
+  auto issue_stage = [&](int kt) {
+    char* As = smem + (kt % NS) * Cfg::STAGE_BYTES;
+    char* Bs = As + Cfg::BM * kRowBytes;
     const int k0 = kt * Cfg::BK;
-    if constexpr (Cfg::A_KC)
-      TileKC<Cfg, Cfg::BM>::issue(A, lda_b, m0, g.M, (int64_t)k0 * Cfg::ESIZE, kbytes, As, wave, lane);
-    else
-      TileMN<Cfg, Cfg::BM>::issue(A, lda_b, k0, g.K, m0, g.M, As, wave, lane);
-    if constexpr (Cfg::B_KC)
-      TileKC<Cfg, Cfg::BN>::issue(B, ldb_b, n0, g.N, (int64_t)k0 * Cfg::ESIZE, kbytes, Bs, wave, lane);
-    else
-      TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, k0, g.K, n0, g.N, Bs, wave, lane);
+    if (grp == 0) {
+      if constexpr (Cfg::A_KC)
+        TileKC<Cfg, Cfg::BM>::issue(A, lda_b, m0, g.M, (int64_t)k0 * Cfg::ESIZE, kbytes, As, w, lane);
+      else
+        TileMN<Cfg, Cfg::BM>::issue(A, lda_b, k0, g.K, m0, g.M, As, w, lane);
+    } else {
+      if constexpr (Cfg::B_KC)
+        TileKC<Cfg, Cfg::BN>::issue(B, ldb_b, n0, g.N, (int64_t)k0 * Cfg::ESIZE, kbytes, Bs, w, lane);
+      else
+        TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, k0, g.K, n0, g.N, Bs, w, lane);
+    }
   };
 
-  issue_stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's stage-0 copies are in LDS
-  __syncthreads();
+  const int npre = nk < NS - 1 ? nk : NS - 1;
+  for (int s = 0; s < npre; ++s) issue_stage(s);
+  wait_stages<LPS, NS>(npre - 1);          // this wave's part of stage 0 has landed
+  phase_barrier();                         // stage 0 is complete
+  if (grp == 1) phase_barrier();           // group 1 trails by one phase
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int p = kt & 1;
-    if (kt + 1 < nk) issue_stage(kt + 1, 1 - p);   // that buffer was released by the last barrier
-    const char* As = smem + p * Cfg::STAGE_BYTES;
-    const char* Bs = As + Cfg::BM * 128;
-    if constexpr (Cfg::FP8) {
-      // fp8 fragments are 8 registers each: one set, read just before use
+    // ---- memory phase: fragments of stage kt, copies of stage kt + NS - 1
+    const char* As = smem + (kt % NS) * Cfg::STAGE_BYTES;
+    const char* Bs = As + Cfg::BM * kRowBytes;
+    Frags<Cfg> f[SUB];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        Frags<Cfg> f;
-        load_frags<Cfg>(As, Bs, s, f, wm0, wn0, lane);
-        mma_frags<Cfg>(f, acc);
-        __builtin_amdgcn_sched_barrier(0);   // do not hoist the next substep's reads
-      }
-    } else {
-      Frags<Cfg> f[2];
-      load_frags<Cfg>(As, Bs, 0, f[0], wm0, wn0, lane);
+    for (int s = 0; s < SUB; ++s) load_frags<Cfg>(As, Bs, s, f[s], wm0, wn0, lane);
+    if (kt + NS - 1 < nk) issue_stage(kt + NS - 1);
+    wait_lgkmcnt0();                        // fragments in registers, stage kt released
+    // stages after kt + 1 this wave has in flight; stage kt + 1 must land before
+    // the barrier that ends the phase in which group 1 reads stage kt
+    const int ahead = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
+    if (grp == 1) wait_stages<LPS, NS>(ahead);
+    phase_barrier();
+    // ---- compute phase
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) load_frags<Cfg>(As, Bs, s + 1, f[(s + 1) & 1], wm0, wn0, lane);
-        // keep the reads of substep s+1 ahead of the MFMAs of substep s
-        __builtin_amdgcn_sched_barrier(0);
-        mma_frags<Cfg>(f[s & 1], acc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): stage kt+1 has landed in LDS
-    __syncthreads();
+    for (int s = 0; s < SUB; ++s) mma_frags<Cfg>(f[s], acc);
+    if (grp == 0) wait_stages<LPS, NS>(ahead);
+    phase_barrier();
   }
+  if (grp == 0) phase_barrier();           // realign: both groups have passed 2 nk + 1 barriers
 }
 
 }  // namespace coda
