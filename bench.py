@@ -181,7 +181,7 @@ def main():
         ("G1+B7+B8 qkv bwd", lambda: coda.linear_qknorm_rope_bwd(
             dq, dk, dv, x, f["r1"], f["qk_pre"], f["v"], blk.w["qkv"], blk.Wqkv, blk.g1, blk.gq, blk.gk,
             blk.rope, blk.seq_len, blk.eps, g["dh1"], g["dx"], g["dWqkv"], g["dg1"], g["dgq"], g["dgk"],
-            beta=1.0, precision=prec)),
+            beta=1.0, dh_qkv_out=g["dht_qkv"], precision=prec)),
     ]
     f3_events = []
 

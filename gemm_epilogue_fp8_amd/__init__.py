@@ -248,15 +248,15 @@ def linear_rmsnorm_residual_bwd(d_out, a, W, dW, da=None, beta=0.0, precision: i
 
 
 def linear_qknorm_rope_bwd(dq, dk, dv, x, r, qk_pre, v, Wqkv, Wqkv_unfolded, g, gq, gk, rope, seq_len, eps,
-                           dres, dx, dW, dg, dgq, dgk, beta=0.0, precision: int = PREC_BF16):
+                           dres, dx, dW, dg, dgq, dgk, beta=0.0, dh_qkv_out=None, precision: int = PREC_BF16):
     L = lib()
     M, D = x.shape
     wc = Wqkv if isinstance(Wqkv, Weight) else Weight(Wqkv)
     ws, n = _ws_call(L.coda_linear_qknorm_rope_bwd_workspace, (M, D, precision), x.device)
     _check(L.coda_linear_qknorm_rope_bwd(_p(dq), _p(dk), _p(dv), _p(x), _p(r), _p(qk_pre), _p(v), C.byref(wc.c()),
                                          _p(Wqkv_unfolded), _p(g), _p(gq), _p(gk), _p(rope), seq_len, eps, _p(dres),
-                                         _p(dx), _p(dW), _p(dg), _p(dgq), _p(dgk), beta, precision, ws, n,
-                                         _stream()))
+                                         _p(dx), _p(dW), _p(dg), _p(dgq), _p(dgk), beta, _p(dh_qkv_out), precision,
+                                         ws, n, _stream()))
     return dx, dW, dg, dgq, dgk
 
 

@@ -74,7 +74,7 @@ SIGNATURES = {
     "coda_linear_rmsnorm_residual_bwd": [M_, M_, W_, M_, M_, f32, i32, vp, sz, vp],
     "coda_linear_qknorm_rope_bwd_workspace": [i64, i64, i32, szp],
     "coda_linear_qknorm_rope_bwd": [M_, M_, M_, M_, M_, M_, M_, W_, M_, M_, M_, M_, M_, i32, f32, M_,
-                                    M_, M_, M_, M_, M_, f32, i32, vp, sz, vp],
+                                    M_, M_, M_, M_, M_, f32, M_, i32, vp, sz, vp],
     "coda_linear_cross_entropy_fwd_workspace": [i64, i64, i64, i32, szp],
     "coda_linear_cross_entropy_fwd": [M_, W_, M_, i32, M_, M_, M_, M_, M_, i32, vp, sz, vp],
     "coda_linear_cross_entropy_bwd_workspace": [i64, i64, i64, i64, i32, szp],

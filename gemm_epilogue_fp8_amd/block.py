@@ -87,7 +87,7 @@ class Block:
         D, F = self.D, self.F
         bf, f32 = torch.bfloat16, torch.float32
         e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=device)
-        return dict(dh1=e(M, D), dht_gu=e(M, 2 * F), do=e(M, D), dx=e(M, D),
+        return dict(dh1=e(M, D), dht_gu=e(M, 2 * F), dht_qkv=e(M, 3 * D), do=e(M, D), dx=e(M, D),
                     dWqkv=e(D, 3 * D, dt=f32), dWo=e(D, D, dt=f32), dWgu=e(D, 2 * F, dt=f32),
                     dWd=e(F, D, dt=f32), dg1=e(D, dt=f32), dg2=e(D, dt=f32), dgq=e(128, dt=f32),
                     dgk=e(128, dt=f32))
@@ -102,7 +102,7 @@ class Block:
         linear_rmsnorm_residual_bwd(b["dh1"], o, self.w["o"], b["dWo"], da=b["do"], beta=beta, precision=p)
         linear_qknorm_rope_bwd(dq, dk, dv, x, f["r1"], f["qk_pre"], f["v"], self.w["qkv"], self.Wqkv, self.g1,
                                self.gq, self.gk, self.rope, self.seq_len, self.eps, b["dh1"], b["dx"], b["dWqkv"],
-                               b["dg1"], b["dgq"], b["dgk"], beta=beta, precision=p)
+                               b["dg1"], b["dgq"], b["dgk"], beta=beta, dh_qkv_out=b["dht_qkv"], precision=p)
         return b
 
 

@@ -92,47 +92,91 @@ __global__ void sum_partials_kernel(const float* P, int nP, int K, float beta, f
   }
 }
 
-__global__ void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
-                                       int64_t ld_g, const uint16_t* qk_pre, int64_t ld_pre,
-                                       const uint16_t* v, int64_t ld_v, const float* r1,
-                                       const float* gq, const float* gk, const float* table,
-                                       int seq_len, float eps, int M, int D, int rows_per_wave,
-                                       uint16_t* dh, int64_t ld_dh, float* T1,
-                                       float* pgq, float* pgk) {
-  // one wave per row; lane l owns the RoPE pair (2l, 2l+1) of every head
+__device__ __forceinline__ float sum16(float v) {   // sum over the 16-lane group of this lane
+  v += __shfl_xor(v, 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) { x[2 * t] = bf_lo(a[t]); x[2 * t + 1] = bf_hi(a[t]); }
+}
+
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
+    const uint16_t* dq, const uint16_t* dk, const uint16_t* dv, int64_t ld_g, const uint16_t* qk_pre,
+    int64_t ld_pre, const uint16_t* v, int64_t ld_v, const float* r1, const float* gq, const float* gk,
+    const float* table, int seq_len, float eps, int M, int D, int rows_per_wave, uint16_t* dh, int64_t ld_dh,
+    float* T1, float* pgq, float* pgk) {
+  // One wave per row.  A head (128 columns) is handled by 16 lanes, 8
+  // consecutive columns (4 RoPE pairs) a lane, so a wave covers 4 heads per
+  // 16-byte access; per-head sums reduce over the 16-lane group.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 15, slot = lane >> 4;
   const int H = D / 128;
-  const float g2[2][2] = {{gq[2 * lane], gq[2 * lane + 1]}, {gk[2 * lane], gk[2 * lane + 1]}};
-  float dgacc[2][2] = {{0, 0}, {0, 0}};
+  float g[2][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { g[0][e] = gq[8 * sub + e]; g[1][e] = gk[8 * sub + e]; }
+  float dgacc[2][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dgacc[0][e] = dgacc[1][e] = 0.0f;
   for (int rr = 0; rr < rows_per_wave; ++rr) {
     const int m = (blockIdx.x * 4 + wave) * rows_per_wave + rr;
     if (m >= M) break;
     const float r = r1 ? r1[m] : 1.0f;     // no r1: plain (unfused) QK-norm backward
     const int pos = m % seq_len;
-    const float cs = table[((int64_t)pos * 64 + lane) * 2], sn = table[((int64_t)pos * 64 + lane) * 2 + 1];
+    // (cos, sin) of the lane's 4 frequencies 4 sub .. 4 sub + 3
+    const float4 cs01 = *reinterpret_cast<const float4*>(table + ((int64_t)pos * 64 + 4 * sub) * 2);
+    const float4 cs23 = *reinterpret_cast<const float4*>(table + ((int64_t)pos * 64 + 4 * sub) * 2 + 4);
+    const float cs[4][2] = {{cs01.x, cs01.y}, {cs01.z, cs01.w}, {cs23.x, cs23.y}, {cs23.z, cs23.w}};
     float T = 0.0f;
 #pragma unroll
     for (int reg = 0; reg < 2; ++reg) {
       const uint16_t* G = reg == 0 ? dq : dk;
-      for (int h = 0; h < H; ++h) {
-        const int col = h * 128 + 2 * lane;
-        uint32_t gw = *reinterpret_cast<const uint32_t*>(G + (int64_t)m * ld_g + col);
-        uint32_t pw = *reinterpret_cast<const uint32_t*>(qk_pre + (int64_t)m * ld_pre + reg * D + col);
-        const float d0 = bf_lo(gw), d1 = bf_hi(gw);
-        const float u0 = bf_lo(pw), u1 = bf_hi(pw);
+      for (int h0 = 0; h0 < H; h0 += 4) {
+        const int h = h0 + slot;
+        const bool on = h < H;                 // whole 16-lane groups switch off together
+        const int col = h * 128 + 8 * sub;
+        float d[8], u[8];
+        if (on) {
+          unpack8(*reinterpret_cast<const uint4*>(G + (int64_t)m * ld_g + col), d);
+          unpack8(*reinterpret_cast<const uint4*>(qk_pre + (int64_t)m * ld_pre + reg * D + col), u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d[e] = u[e] = 0.0f;
+        }
         // inverse rotation (transpose of the forward RoPE matrix)
-        const float n0 = d0 * cs + d1 * sn;
-        const float n1 = -d0 * sn + d1 * cs;
-        const float rho = rsqrtf(wave_sum(u0 * u0 + u1 * u1) / 128.0f + eps);
-        const float t0 = g2[reg][0] * n0, t1 = g2[reg][1] * n1;
-        const float st = wave_sum(u0 * t0 + u1 * t1);
+        float n[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          n[2 * p] = d[2 * p] * cs[p][0] + d[2 * p + 1] * cs[p][1];
+          n[2 * p + 1] = -d[2 * p] * cs[p][1] + d[2 * p + 1] * cs[p][0];
+        }
+        float ss = 0.0f, st = 0.0f, t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          t[e] = g[reg][e] * n[e];
+          ss += u[e] * u[e];
+          st += u[e] * t[e];
+        }
+        ss = sum16(ss);
+        st = sum16(st);
+        const float rho = rsqrtf(ss / 128.0f + eps);
         const float k3 = rho * rho * rho / 128.0f * st;
-        const float p0 = rho * t0 - k3 * u0, p1 = rho * t1 - k3 * u1;
-        const float h0 = round_bf(r * p0), h1 = round_bf(r * p1);
-        *reinterpret_cast<uint32_t*>(dh + (int64_t)m * ld_dh + reg * D + col) = pack_bf2(h0, h1);
-        T += h0 * u0 + h1 * u1;
-        dgacc[reg][0] += rho * u0 * n0;
-        dgacc[reg][1] += rho * u1 * n1;
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a0 = round_bf(r * (rho * t[2 * q] - k3 * u[2 * q]));
+          const float a1 = round_bf(r * (rho * t[2 * q + 1] - k3 * u[2 * q + 1]));
+          T += a0 * u[2 * q] + a1 * u[2 * q + 1];
+          o[q] = pack_bf2(a0, a1);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dgacc[reg][e] += rho * u[e] * n[e];
+        if (on) *reinterpret_cast<uint4*>(dh + (int64_t)m * ld_dh + reg * D + col) = uint4{o[0], o[1], o[2], o[3]};
       }
     }
     for (int col = lane * 8; col < D; col += 512) {
@@ -141,27 +185,38 @@ __global__ void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, c
       uint32_t ga[4] = {gw.x, gw.y, gw.z, gw.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
       uint32_t o[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float h0 = round_bf(r * bf_lo(ga[t])), h1 = round_bf(r * bf_hi(ga[t]));
-        T += h0 * bf_lo(va[t]) + h1 * bf_hi(va[t]);
-        o[t] = pack_bf2(h0, h1);
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = round_bf(r * bf_lo(ga[q])), a1 = round_bf(r * bf_hi(ga[q]));
+        T += a0 * bf_lo(va[q]) + a1 * bf_hi(va[q]);
+        o[q] = pack_bf2(a0, a1);
       }
       *reinterpret_cast<uint4*>(dh + (int64_t)m * ld_dh + 2 * D + col) = uint4{o[0], o[1], o[2], o[3]};
     }
     T = wave_sum(T);
     if (lane == 0) T1[m] = T;
   }
-  // gain-gradient partials of this block: fixed-order sum over its 4 waves
+  // gain-gradient partials of this block, in a fixed order: the 4 head slots
+  // of a wave (lanes sub, sub + 16, sub + 32, sub + 48), then the 4 waves
+#pragma unroll
+  for (int reg = 0; reg < 2; ++reg)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = dgacc[reg][e];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      dgacc[reg][e] = x;
+    }
   __shared__ float red[4][2][128];
-  red[wave][0][2 * lane] = dgacc[0][0];
-  red[wave][0][2 * lane + 1] = dgacc[0][1];
-  red[wave][1][2 * lane] = dgacc[1][0];
-  red[wave][1][2 * lane + 1] = dgacc[1][1];
+  if (slot == 0)
+#pragma unroll
+    for (int reg = 0; reg < 2; ++reg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][reg][8 * sub + e] = dgacc[reg][e];
   __syncthreads();
-  const int t = threadIdx.x;   // 256 threads: (region, column)
-  const int reg = t >> 7, cidx = t & 127;
-  float s = (red[0][reg][cidx] + red[1][reg][cidx]) + (red[2][reg][cidx] + red[3][reg][cidx]);
-  (reg == 0 ? pgq : pgk)[(int64_t)blockIdx.x * 128 + cidx] = s;
+  const int tt = threadIdx.x;   // 256 threads: (region, column)
+  const int reg = tt >> 7, cidx = tt & 127;
+  float sacc = (red[0][reg][cidx] + red[1][reg][cidx]) + (red[2][reg][cidx] + red[3][reg][cidx]);
+  (reg == 0 ? pgq : pgk)[(int64_t)blockIdx.x * 128 + cidx] = sacc;
 }
 
 __device__ __forceinline__ void lse_merge_(float& m, float& s, float m2, float s2) {

@@ -33,7 +33,7 @@ __global__ void sum_partials_kernel(const float* P, int nP, int K, float beta, f
 // RoPE of dq, dk, per-head RMSNorm backward (from the saved pre-norm q, k),
 // r1 row scale -> dh~_qkv (bf16 [M, 3D]); T1[m] = sum_j dh~ h; gain-gradient
 // partials for g_q and g_k per block.  r1 == nullptr means r1 = 1.
-__global__ void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(const uint16_t* dq, const uint16_t* dk, const uint16_t* dv,
                                        int64_t ld_g, const uint16_t* qk_pre, int64_t ld_pre,
                                        const uint16_t* v, int64_t ld_v, const float* r1,
                                        const float* gq, const float* gk, const float* table,

@@ -739,14 +739,19 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
                                const coda_mat* Wunf, const coda_mat* gvec, const coda_mat* gq, const coda_mat* gk,
                                const coda_mat* rope, int seq_len, float eps, const coda_mat* dres, const coda_mat* dx,
                                const coda_mat* dW, const coda_mat* dg, const coda_mat* dgq, const coda_mat* dgk,
-                               float beta, int precision, void* ws, size_t ws_bytes, void* stream, int64_t M,
-                               int64_t D, bool size_only, size_t* bytes) {
+                               float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
+                               void* stream, int64_t M, int64_t D, bool size_only, size_t* bytes) {
   const bool fp8 = precision == CODA_PREC_FP8;
   const int64_t N3 = 3 * D;
   const int rows_per_wave = 4;
   const int nblk = (int)((M + 4 * rows_per_wave - 1) / (4 * rows_per_wave));
   Carver cv(size_only ? nullptr : ws);
   uint16_t* dh = cv.take<uint16_t>((size_t)M * N3);
+  int64_t ldh = N3;
+  if (!size_only && present(dh_out)) {   // the caller keeps dh~ (same traffic, its own buffer)
+    dh = static_cast<uint16_t*>(dh_out->ptr);
+    ldh = dh_out->ld;
+  }
   float* T1 = cv.take<float>(M);
   float* pgq = cv.take<float>((size_t)std::max(nblk, 1) * 128);
   float* pgk = cv.take<float>((size_t)std::max(nblk, 1) * 128);
@@ -766,15 +771,15 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
                        static_cast<const uint16_t*>(dk->ptr), static_cast<const uint16_t*>(dv->ptr), dq->ld,
                        static_cast<const uint16_t*>(qk_pre->ptr), qk_pre->ld, static_cast<const uint16_t*>(v->ptr),
                        v->ld, fptr(r), fptr(gq), fptr(gk), fptr(rope), seq_len, eps, (int)M, (int)D, rows_per_wave,
-                       dh, N3, T1, pgq, pgk);
+                       dh, ldh, T1, pgq, pgk);
     TRY(check_launch("qknorm_rope_bwd: glue"));
   }
   TRY(sum_partials_launch(pgq, nblk, 128, beta, static_cast<float*>(dgq->ptr), s));
   TRY(sum_partials_launch(pgk, nblk, 128, beta, static_cast<float*>(dgk->ptr), s));
   if (fp8) {
-    TRY(quant_act(q8.grow, dh, N3, M, N3, 1, s));
+    TRY(quant_act(q8.grow, dh, ldh, M, N3, 1, s));
     TRY(quant_act(q8.xcol, x->ptr, x->ld, M, D, 0, s));
-    TRY(quant_act(q8.gcol, dh, N3, M, N3, 0, s));
+    TRY(quant_act(q8.gcol, dh, ldh, M, N3, 0, s));
   }
   {
     EpiArgs e = epi0();
@@ -786,7 +791,7 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
     e.n_row_partials = 1;
     e.norm_dim = (int)D;
     GemmArgs g;
-    dgrad_args(fp8, &q8.grow, dh, N3, Wqkv, M, D, N3, &g, &e);
+    dgrad_args(fp8, &q8.grow, dh, ldh, Wqkv, M, D, N3, &g, &e);
     TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, fp8, g, e, s), "qknorm_rope_bwd: dx"));
   }
   {
@@ -798,7 +803,7 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
     e.partial_out = dgp;
     GemmArgs g;
     int layout;
-    wgrad_args(fp8, q8, x->ptr, x->ld, dh, N3, M, D, N3, &g, &e, &layout);
+    wgrad_args(fp8, q8, x->ptr, x->ld, dh, ldh, M, D, N3, &g, &e, &layout);
     TRY(launched(launch_gemm(Prog::WgradGain, layout, fp8, g, e, s), "qknorm_rope_bwd: dW"));
   }
   return sum_partials_launch(dgp, nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
@@ -807,8 +812,8 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
 extern "C" coda_status coda_linear_qknorm_rope_bwd_workspace(int64_t M, int64_t D, int32_t precision, size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   return qk_bwd_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, 1, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, precision,
-                     nullptr, 0, nullptr, M, D, true, bytes);
+                     nullptr, nullptr, 1, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, nullptr,
+                     precision, nullptr, 0, nullptr, M, D, true, bytes);
 }
 
 extern "C" coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv,
@@ -818,7 +823,8 @@ extern "C" coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const cod
                                                    const coda_mat* rope, int32_t seq_len, float eps, const coda_mat* dres,
                                                    const coda_mat* dx, const coda_mat* dW, const coda_mat* dg,
                                                    const coda_mat* dgq, const coda_mat* dgk, float beta,
-                                                   int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+                                                   const coda_mat* dh_qkv_out, int32_t precision, void* ws,
+                                                   size_t ws_bytes, void* stream) {
   TRY(check_precision(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, D = x->cols;
@@ -844,8 +850,9 @@ extern "C" coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const cod
   TRY(check_vec(dg, "dg", CODA_F32, D));
   TRY(check_vec(dgq, "dgq", CODA_F32, 128));
   TRY(check_vec(dgk, "dgk", CODA_F32, 128));
+  TRY(check_mat(dh_qkv_out, "dh_qkv_out", CODA_BF16, M, 3 * D, true));
   return qk_bwd_impl(dq, dk, dv, x, r, qk_pre, v, Wqkv, Wunf, g, gq, gk, rope, seq_len, eps, dres, dx, dW, dg, dgq, dgk,
-                     beta, precision, ws, ws_bytes, stream, M, D, false, nullptr);
+                     beta, dh_qkv_out, precision, ws, ws_bytes, stream, M, D, false, nullptr);
 }
 
 // ======================================================================== cross-entropy

@@ -251,7 +251,9 @@ coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, const coda_m
  *   dh~ = bf16(r1 [dq_pre, dk_pre, dv]),  T = sum_j dh~ h,  c = r1 T / D,
  *   dx = dh~ W~^T - c x + dres (bf16 [M, D]),
  *   dW = beta dW + g1 * (x^T dh~) (fp32 [D, 3D]),  dg1 = beta dg1 + sum_n W * (x^T dh~),
- *   dgq, dgk = beta dg + per-head gain gradients (fp32 1 x 128). */
+ *   dgq, dgk = beta dg + per-head gain gradients (fp32 1 x 128).
+ * dh_qkv_out: optional bf16 [M, 3D] that receives dh~ (else it is held in
+ * the workspace). */
 coda_status coda_linear_qknorm_rope_bwd_workspace(int64_t M, int64_t D, int32_t precision, size_t* bytes);
 coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv,
                                         const coda_mat* x, const coda_mat* r, const coda_mat* qk_pre,
@@ -260,7 +262,8 @@ coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, 
                                         const coda_mat* rope, int32_t seq_len, float eps, const coda_mat* dres,
                                         const coda_mat* dx, const coda_mat* dW, const coda_mat* dg,
                                         const coda_mat* dgq, const coda_mat* dgk, float beta,
-                                        int32_t precision, void* ws, size_t ws_bytes, void* stream);
+                                        const coda_mat* dh_qkv_out, int32_t precision, void* ws, size_t ws_bytes,
+                                        void* stream);
 
 /* ===================================================================== cross-entropy */
 

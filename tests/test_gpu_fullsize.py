@@ -1,0 +1,155 @@
+"""GPU parity at the workloads' full sizes, through the same library calls
+bench.py times, against the CPU oracle run over the whole workload in
+contract mode.
+
+These take tens of seconds each: the oracle (numpy, fp32 BLAS) evaluates the
+complete block or cross-entropy on the host.  Every tensor is compared in
+full, with the same bars as the small parity tests."""
+import numpy as np
+import pytest
+
+import coda_inputs as ci
+from oracle import block as ob
+from tests.helpers import assert_bf16, assert_grad, to_dev, to_np, unpack_gu
+from tests.test_gpu_parity import check_block_fp8
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogue_fp8_amd as coda  # noqa: E402
+from gemm_epilogue_fp8_amd.block import Block  # noqa: E402
+
+BF = torch.bfloat16
+DEV = "cuda"
+
+
+def _block_gpu(shape, P, precision):
+    params = {k: to_dev(v) if k in ("g1", "g2", "gq", "gk") else to_dev(v, BF) for k, v in P.items()}
+    blk = Block(params, shape.D, shape.F, seq_len=shape.seq_len, theta=shape.theta, eps=shape.eps,
+                precision=precision)
+    f = blk.forward(params["x"], params["o"])
+    b = blk.backward(params["x"], params["o"], f, params["dY"], params["dq"], params["dk"], params["dv"])
+    torch.cuda.synchronize()
+    f = {k: to_np(v) for k, v in f.items()}
+    b = {k: to_np(v) for k, v in b.items()}
+    del blk, params
+    torch.cuda.empty_cache()
+    return f, b
+
+
+def _check_block(shape, P, f, b, fp8):
+    F = ob.block_forward_contract(P, shape, fp8=fp8)
+    B = ob.block_backward_contract(P, F, shape, fp8=fp8)
+    if fp8:
+        check_block_fp8(shape, f, b, F, B)
+        return
+    D = shape.D
+    for k in ("q", "k", "v", "h1", "a", "y"):
+        assert_bf16(k, f[k], F[k])
+    assert_bf16("q_pre", f["qk_pre"][:, :D], F["q_pre"])
+    assert_bf16("k_pre", f["qk_pre"][:, D:], F["k_pre"])
+    hg, hu = unpack_gu(f["hgu"])
+    assert_bf16("hg", hg, F["hg"])
+    assert_bf16("hu", hu, F["hu"])
+    del hg, hu
+    assert_grad("r1", f["r1"], F["r1"])
+    assert_grad("r2", f["r2"], F["r2"])
+    assert_grad("next-norm sumsq", f["P4"].sum(axis=0), F["sumsq_y"])
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    assert_bf16("dh~_gu", np.concatenate([dg_, du_], axis=1), B["dht_gu"])
+    del dg_, du_
+    assert_bf16("dh~_qkv", b["dht_qkv"], B["dht_qkv"])
+    for k in ("dh1", "do", "dx"):
+        assert_bf16(k, b[k], B[k])
+    dWg, dWu = unpack_gu(b["dWgu"])
+    grads = dict(dWg=dWg, dWu=dWu, dWqkv=b["dWqkv"], dWo=b["dWo"], dWd=b["dWd"], dg1=b["dg1"], dg2=b["dg2"],
+                 dgq=b["dgq"], dgk=b["dgk"])
+    for k, v in grads.items():
+        assert_grad(k, v, B[k])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["cfg2", "cfg3"])
+def test_block_full_size_bf16(name):
+    """Hidden 2048 (the default bench workload) and hidden 4096, M = 8192."""
+    shape = {"cfg2": ci.CFG2, "cfg3": ci.CFG3}[name]
+    P = ci.block_inputs(shape, ci.SEEDS[name])
+    f, b = _block_gpu(shape, P, coda.PREC_BF16)
+    _check_block(shape, P, f, b, fp8=False)
+
+
+@pytest.mark.timeout(1200)
+def test_block_full_size_fp8():
+    """Hidden 8192, MLP 28672, 64 heads, M = 4096 with E4M3 operands."""
+    shape = ci.CFG5
+    P = ci.block_inputs(shape, ci.SEEDS["cfg5"])
+    f, b = _block_gpu(shape, P, coda.PREC_FP8)
+    _check_block(shape, P, f, b, fp8=True)
+
+
+@pytest.mark.timeout(900)
+def test_fp8_stage_full_size():
+    """One fp8 stage from seeded inputs at the hidden-8192 down-projection
+    shape (M 4096, K 28672, N 8192): forward out = z + a W, backward
+    dW = a^T dout and da = dout W^T.  Every quantiser sees identical bits on
+    both sides, so the elementwise fp8 bound holds on every element."""
+    from oracle import numerics as nm
+    from tests.helpers import FP8_TOL
+    M, K, N = 4096, 28672, 8192
+    rng = np.random.default_rng(55)
+    a = ci.to_bf16_values(rng.standard_normal((M, K), dtype=np.float32))
+    W = ci.to_bf16_values(rng.standard_normal((K, N), dtype=np.float32) * np.float32(K ** -0.5))
+    z = ci.to_bf16_values(rng.standard_normal((M, N), dtype=np.float32))
+    dout = ci.to_bf16_values(rng.standard_normal((M, N), dtype=np.float32) * np.float32(0.1))
+    wt = coda.Weight(to_dev(W, BF)).prepare_fp8()
+    ag, zg, dg = to_dev(a, BF), to_dev(z, BF), to_dev(dout, BF)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.linear_rmsnorm_residual_fwd(ag, wt, zg, out, precision=coda.PREC_FP8)
+    dW = torch.empty((K, N), dtype=torch.float32, device=DEV)
+    da = torch.empty((M, K), dtype=BF, device=DEV)
+    coda.linear_rmsnorm_residual_bwd(dg, ag, wt, dW, da=da, precision=coda.PREC_FP8)
+    torch.cuda.synchronize()
+    got = dict(out=to_np(out), dW=to_np(dW), da=to_np(da))
+    del wt, ag, zg, dg, out, dW, da
+    torch.cuda.empty_cache()
+    assert_bf16("out", got["out"], nm.bf16(z + ob.mm(a, W, fp8=True)), tol=FP8_TOL)
+    assert_bf16("dW", got["dW"], ob.mm(a.T.copy(), dout, fp8=True), tol=FP8_TOL, norm_rel=1e-3)
+    assert_bf16("da", got["da"], nm.bf16(ob.mm(dout, W.T.copy(), fp8=True)), tol=FP8_TOL)
+
+
+@pytest.mark.timeout(900)
+def test_cross_entropy_full_size():
+    """h [8192, 2048], W_vocab [2048, 128256], 410 ignored rows; the backward
+    recomputes the logits in chunks of 1024 rows."""
+    shape = ci.CFG4
+    P = ci.ce_inputs(shape, ci.SEEDS["cfg4"])
+    M, D, V = shape.M, shape.D, shape.V
+    labels = P["labels"]
+    h, W = to_dev(P["h"], BF), to_dev(P["W"], BF)
+    lab = to_dev(labels)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    per_row = torch.empty(M, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    nbad = torch.empty(1, dtype=torch.int32, device=DEV)
+    coda.linear_cross_entropy_fwd(h, W, lab, loss, lse, nv, per_row=per_row, n_bad=nbad)
+    dh = torch.empty((M, D), dtype=BF, device=DEV)
+    dW = torch.zeros((D, V), dtype=torch.float32, device=DEV)
+    coda.linear_cross_entropy_bwd(h, W, lab, lse, nv, 1.0, dh, dW, beta=0.0, chunk_rows=1024)
+    torch.cuda.synchronize()
+    got = dict(loss=loss.item(), lse=to_np(lse), per_row=to_np(per_row), dh=to_np(dh), dW=to_np(dW),
+               nv=int(nv.item()), nbad=int(nbad.item()))
+    del h, W, dh, dW
+    torch.cuda.empty_cache()
+    Fr = ob.ce_forward_contract(P["h"], P["W"], labels)
+    assert got["nv"] == Fr["n_valid"] == M - 410 and got["nbad"] == 0
+    assert abs(got["loss"] - Fr["loss"]) <= 1e-4 * abs(Fr["loss"])
+    assert_grad("lse", got["lse"], Fr["lse"])
+    assert_grad("per-row loss", got["per_row"], Fr["per_row"])
+    Br = ob.ce_backward_contract(P["h"], P["W"], labels, Fr["lse"], Fr["n_valid"])
+    assert_bf16("dh", got["dh"], Br["dh"])
+    assert_grad("dW", got["dW"], Br["dW"])
+    assert np.all(got["dh"][labels == -100] == 0)
