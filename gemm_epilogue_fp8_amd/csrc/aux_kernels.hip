@@ -76,19 +76,26 @@ __global__ void rows_finish_kernel(const float* P, int nP, int M, int mode, cons
   out[m] = s;
 }
 
-__global__ void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out) {
-  // block: 64 columns x 4 partial groups
-  __shared__ float red[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int grp = threadIdx.x >> 6;
+__global__ __launch_bounds__(1024) void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out) {
+  // block of 1024 threads: 64 columns x 16 partial groups; group j adds
+  // partials j, j + 16, ...
+  // and the 16 group sums are combined in a fixed tree
+  __shared__ float red[16][64];
+  const int cl = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
   float s = 0.0f;
-  if (c < K)
-    for (int t = grp; t < nP; t += 4) s += P[(int64_t)t * K + c];
-  red[grp][threadIdx.x & 63] = s;
+  if (c < K) {
+#pragma unroll 4
+    for (int t = grp; t < nP; t += 16) s += P[(int64_t)t * K + c];
+  }
+  red[grp][cl] = s;
   __syncthreads();
   if (grp == 0 && c < K) {
-    float v = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
-    out[c] = (beta != 0.0f ? beta * out[c] : 0.0f) + v;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = red[2 * j][cl] + red[2 * j + 1][cl];
+    const float w = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    out[c] = (beta != 0.0f ? beta * out[c] : 0.0f) + w;
   }
 }
 

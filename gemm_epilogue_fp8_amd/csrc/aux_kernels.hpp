@@ -28,7 +28,7 @@ __global__ void row_sumsq_kernel(const uint16_t* x, int64_t ld, int M, int K, fl
 __global__ void rows_finish_kernel(const float* P, int nP, int M, int mode, const float* rowvec,
                                    int D, float eps, float* out);
 // out[k] = beta * out[k] + sum_{t < nP} P[t][k]
-__global__ void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out);
+__global__ __launch_bounds__(1024) void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out);
 // Backward glue between attention and the QKV dgrad / wgrad GEMMs: inverse
 // RoPE of dq, dk, per-head RMSNorm backward (from the saved pre-norm q, k),
 // r1 row scale -> dh~_qkv (bf16 [M, 3D]); T1[m] = sum_j dh~ h; gain-gradient

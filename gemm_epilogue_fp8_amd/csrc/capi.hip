@@ -550,7 +550,7 @@ static void wgrad_args(bool fp8, const Bwd8& q8, const void* X, int64_t ldX, con
 
 static coda_status sum_partials_launch(const float* P, int nP, int K, float beta, float* out, hipStream_t s) {
   if (K == 0) return CODA_OK;
-  hipLaunchKernelGGL(sum_partials_kernel, dim3((K + 63) / 64), dim3(256), 0, s, P, nP, K, beta, out);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((K + 63) / 64), dim3(1024), 0, s, P, nP, K, beta, out);
   return check_launch("sum_partials");
 }
 

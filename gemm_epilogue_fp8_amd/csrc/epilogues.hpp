@@ -182,6 +182,25 @@ __device__ __forceinline__ void put_tile(const Ctx<Cfg>& c, const Acc<Cfg>& acc)
       for (int q = 0; q < 4; ++q) StageBF<Cfg::BM, C>::put4(s, c.lrow(i), c.lcol(j, q), frag(acc, i, j, q));
 }
 
+// A rank-2 bf16 operand tile read straight into registers in the MFMA
+// layout, one 32-row block (i) at a time: lane values at (row(i), col(j, q)
+// .. + 3).  Indices are clamped into the matrix, so every load is in bounds;
+// positions outside it carry values that are never stored.
+template <class Cfg>
+struct RowBlock {
+  uint2 v[Cfg::TN][4];
+  __device__ __forceinline__ void load(const void* base, int64_t ld, const Ctx<Cfg>& c, int i) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + (int64_t)c.rowc(i) * ld;
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[j][q] = *reinterpret_cast<const uint2*>(p + c.colc(j, q));
+  }
+  __device__ __forceinline__ f32x4_t get(int j, int q) const {
+    return f32x4_t{bf_lo(v[j][q].x), bf_hi(v[j][q].x), bf_lo(v[j][q].y), bf_hi(v[j][q].y)};
+  }
+};
+
 // fp32 output D = beta D + v for the tile, staged through LDS in row halves
 // (128 KB each); v is in the register layout in acc.
 template <class Cfg>
@@ -341,14 +360,16 @@ struct EpiLinear {
     apply_fp8_scales<Cfg>(e, c, acc);
     float alpha = e.alpha;
     if constexpr (FLAGS & EL_ALPHADEV) alpha *= *e.alpha_dev;
-    if constexpr (FLAGS & EL_TILEADD) {
-      stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
-          CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
-      __syncthreads();
+    constexpr bool ADD = (FLAGS & EL_TILEADD) != 0;
+    RowBlock<Cfg> res[ADD ? 2 : 1];
+    if constexpr (ADD) {
+      res[0].load(e.aux0, e.ld_aux0, c, 0);
+      if (Cfg::TM > 1) res[1].load(e.aux0, e.ld_aux0, c, 1);
     }
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
       part[i] = 0.0f;
       const int m = c.row(i);
       float rv = 1.0f;
@@ -363,20 +384,23 @@ struct EpiLinear {
           if constexpr (FLAGS & EL_COLVEC)
             v = v * *reinterpret_cast<const f32x4_t*>(e.colvec + c.colc(j, q));
           v = v * alpha;
-          if constexpr (FLAGS & EL_TILEADD) v = v + S::get4(c.stage(), c.lrow(i), c.lcol(j, q));
+          if constexpr (ADD) v = v + res[i & 1].get(j, q);
           if constexpr (!(FLAGS & EL_F32OUT)) {
             v = round_bf4(v);
             if constexpr (FLAGS & EL_SUMSQ)
               if (m < c.M && n < c.N) part[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            S::put4(c.stage(), c.lrow(i), c.lcol(j, q), v);   // the stage is free after the mainloop
+          } else {
+            set_frag(acc, i, j, q, v);
           }
-          set_frag(acc, i, j, q, v);
         }
+      if constexpr (ADD)
+        if (i + 2 < Cfg::TM) res[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (FLAGS & EL_F32OUT) {
       store_f32_tile<Cfg>(e, c, acc);
     } else {
-      if constexpr (FLAGS & EL_TILEADD) __syncthreads();   // every lane has read its residual
-      put_tile<Cfg, Cfg::BN>(c, acc);
       __syncthreads();
       stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
           MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
@@ -537,62 +561,72 @@ struct EpiQKNormRope {
 // loads the saved gate/up pre-activations (packed layout), forms dhg, dhu,
 // scales by r2 and stores dh~ (bf16, packed), plus the partials
 // T[tn][m] = sum over the tile of dh~ . h (for the RMSNorm backward).
-// The tile's F columns [n0, n0 + BN) are the packed columns [2 n0, 2 n0 + 2 BN),
-// handled in two phases of BN packed columns (waves of half the tile each).
+// The saved hg / hu come straight into registers in the MFMA layout, one
+// 32-row block (i) at a time with the next block's loads in flight, and dh~
+// goes straight back out from the registers: a lane pair (l, l + 32) writes
+// 16 contiguous bytes of gate and 16 of up, which the L2 merges into whole
+// lines.  No LDS staging and no barrier until the row reduction.
 template <class Cfg>
 struct EpiDSwiGLU {
-  static_assert(Cfg::WAVES_N % 2 == 0, "two column phases");
   struct Pro {};
+  struct Block { uint2 g[Cfg::TN][4], u[Cfg::TN][4]; };   // one row block of hg, hu (4 bf16 each)
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
-  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
-    using S = StageBF<Cfg::BM, Cfg::BN>;
-    apply_fp8_scales<Cfg>(e, c, acc);
-    char* s = c.stage();
-    const int HN = Cfg::BN / 2;                          // F columns a phase
-    const int N2 = 2 * c.N;                              // packed width
-    float part[Cfg::TM];
+
+  __device__ __forceinline__ static int packed_gate(int f) { return (f >> 5) * 64 + (f & 31); }
+
+  __device__ __forceinline__ static void load_block(const EpiArgs& e, const Ctx<Cfg>& c, int i, Block& b) {
+    const uint16_t* H = static_cast<const uint16_t*>(e.aux0) + (int64_t)c.rowc(i) * e.ld_aux0;
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) part[i] = 0.0f;
+    for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-      const int pc0 = 2 * c.n0 + ph * Cfg::BN;           // first packed column of the phase
-      stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
-          CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, pc0, c.M, N2});
-      __syncthreads();
-      if (c.wn0 / HN == ph) {
-#pragma unroll
-        for (int i = 0; i < Cfg::TM; ++i) {
-          const int m = c.row(i);
-          const float r = e.rowvec[c.rowc(i)];
-#pragma unroll
-          for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int fl = c.lcol(j, q) - ph * HN;        // F column inside the phase
-              const int pg = (fl >> 5) * 64 + (fl & 31);    // its packed gate column
-              const f32x4_t hg = S::get4(s, c.lrow(i), pg);
-              const f32x4_t hu = S::get4(s, c.lrow(i), pg + 32);
-              const f32x4_t da = frag(acc, i, j, q);
-              f32x4_t dg, du;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const float sg = sigmoidf_(hg[t]);
-                dg[t] = round_bf(r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg))));
-                du[t] = round_bf(r * (da[t] * hg[t] * sg));
-              }
-              if (m < c.M && c.col(j, q) < c.N)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) part[i] += dg[t] * hg[t] + du[t] * hu[t];
-              S::put4(s, c.lrow(i), pg, dg);                 // in place: this lane owns both slots
-              S::put4(s, c.lrow(i), pg + 32, du);
-            }
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int pg = packed_gate(c.colc(j, q));   // clamped: lanes past N read a valid, unused value
+        b.g[j][q] = *reinterpret_cast<const uint2*>(H + pg);
+        b.u[j][q] = *reinterpret_cast<const uint2*>(H + pg + 32);
       }
-      __syncthreads();
-      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
-          MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, pc0, c.M, N2});
-      __syncthreads();
+  }
+
+  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+    apply_fp8_scales<Cfg>(e, c, acc);
+    float part[Cfg::TM];
+    Block blk[2];
+    load_block(e, c, 0, blk[0]);
+    if (Cfg::TM > 1) load_block(e, c, 1, blk[1]);
+    uint16_t* out = static_cast<uint16_t*>(e.out);
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      Block& b = blk[i & 1];
+      part[i] = 0.0f;
+      const int m = c.row(i);
+      const float r = e.rowvec[c.rowc(i)];
+      uint16_t* orow = out + (int64_t)m * e.ld_out;
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t hg = f32x4_t{bf_lo(b.g[j][q].x), bf_hi(b.g[j][q].x), bf_lo(b.g[j][q].y), bf_hi(b.g[j][q].y)};
+          const f32x4_t hu = f32x4_t{bf_lo(b.u[j][q].x), bf_hi(b.u[j][q].x), bf_lo(b.u[j][q].y), bf_hi(b.u[j][q].y)};
+          const f32x4_t da = frag(acc, i, j, q);
+          f32x4_t dg, du;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float sg = sigmoidf_(hg[t]);
+            dg[t] = round_bf(r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg))));
+            du[t] = round_bf(r * (da[t] * hg[t] * sg));
+          }
+          const int f = c.col(j, q);
+          if (m < c.M && f < c.N) {   // F % 32 == 0: the 4 columns are all in or all out
+#pragma unroll
+            for (int t = 0; t < 4; ++t) part[i] += dg[t] * hg[t] + du[t] * hu[t];
+            const int pg = packed_gate(f);
+            *reinterpret_cast<uint2*>(orow + pg) = uint2{pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3])};
+            *reinterpret_cast<uint2*>(orow + pg + 32) = uint2{pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3])};
+          }
+        }
+      if (i + 2 < Cfg::TM) load_block(e, c, i + 2, b);
     }
+    __builtin_amdgcn_sched_barrier(0);
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
     write_row_partial<Cfg>(c, tot, e.partial_out);
@@ -609,41 +643,39 @@ struct EpiNormCorrection {
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
     using S = StageBF<Cfg::BM, Cfg::BN>;
+    // u and res come into registers one 32-row block at a time
+    RowBlock<Cfg> u[2], z[2];
+    u[0].load(e.aux0, e.ld_aux0, c, 0);
+    z[0].load(e.aux1, e.ld_aux1, c, 0);
+    if (Cfg::TM > 1) {
+      u[1].load(e.aux0, e.ld_aux0, c, 1);
+      z[1].load(e.aux1, e.ld_aux1, c, 1);
+    }
     float* cv = c.rowv();
     p.rp.reduce(c, cv);
     if (c.tid < Cfg::BM) {
       int m = c.m0 + c.tid;
       cv[c.tid] = m < c.M ? e.rowvec[m] * cv[c.tid] / (float)e.norm_dim : 0.0f;
     }
+    __syncthreads();
     apply_fp8_scales<Cfg>(e, c, acc);
     char* s = c.stage();
-    // phase 1: - c u
-    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
-        CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
       const float cc = cv[c.lrow(i)];
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          set_frag(acc, i, j, q, frag(acc, i, j, q) - cc * S::get4(s, c.lrow(i), c.lcol(j, q)));
+          S::put4(s, c.lrow(i), c.lcol(j, q),
+                  round_bf4(frag(acc, i, j, q) - cc * u[i & 1].get(j, q) + z[i & 1].get(j, q)));
+      if (i + 2 < Cfg::TM) {
+        u[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
+        z[i & 1].load(e.aux1, e.ld_aux1, c, i + 2);
+      }
     }
-    __syncthreads();
-    // phase 2: + res, round, store
-    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
-        CMatBF{static_cast<const uint16_t*>(e.aux1), e.ld_aux1, c.m0, c.n0, c.M, c.N});
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          set_frag(acc, i, j, q, frag(acc, i, j, q) + S::get4(s, c.lrow(i), c.lcol(j, q)));
-    __syncthreads();
-    put_tile<Cfg, Cfg::BN>(c, acc);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }
@@ -656,15 +688,14 @@ struct EpiWgradGain {
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
-    using S = StageBF<Cfg::BM, Cfg::BN>;
+    RowBlock<Cfg> w[2];
+    w[0].load(e.aux0, e.ld_aux0, c, 0);
+    if (Cfg::TM > 1) w[1].load(e.aux0, e.ld_aux0, c, 1);
     apply_fp8_scales<Cfg>(e, c, acc);
-    char* s = c.stage();
-    stage_load_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
-        CMatBF{static_cast<const uint16_t*>(e.aux0), e.ld_aux0, c.m0, c.n0, c.M, c.N});
-    __syncthreads();
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
       part[i] = 0.0f;
       const int m = c.row(i);
       const float g = e.rowvec[c.rowc(i)];
@@ -673,11 +704,13 @@ struct EpiWgradGain {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4_t a = frag(acc, i, j, q);
-          const f32x4_t w = S::get4(s, c.lrow(i), c.lcol(j, q));   // zero outside the matrix
-          part[i] += w[0] * a[0] + w[1] * a[1] + w[2] * a[2] + w[3] * a[3];
+          const f32x4_t wv = w[i & 1].get(j, q);
+          if (m < c.M && c.col(j, q) < c.N) part[i] += wv[0] * a[0] + wv[1] * a[1] + wv[2] * a[2] + wv[3] * a[3];
           set_frag(acc, i, j, q, g * a);
         }
+      if (i + 2 < Cfg::TM) w[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // the reduction first: partials kept live across the staged store cost spills
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);

@@ -224,7 +224,7 @@ extern "C" coda_status coda_unfused_rmsnorm_bwd(const coda_mat* u, const coda_ma
                        dy->ld, (int)M, (int)D, kDgRows, part);
     TRY(check_launch("unfused_rmsnorm_bwd"));
   }
-  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((D + 63) / 64)), dim3(256), 0, s, part, nblk, (int)D, beta,
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((D + 63) / 64)), dim3(1024), 0, s, part, nblk, (int)D, beta,
                      static_cast<float*>(dg->ptr));
   return check_launch("unfused_rmsnorm_bwd: dg");
 }
@@ -335,7 +335,7 @@ extern "C" coda_status coda_unfused_qknorm_rope_bwd(const coda_mat* dq, const co
                        T, pgq, pgk);
     TRY(check_launch("unfused_qknorm_rope_bwd"));
   }
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(2), dim3(256), 0, s, pgq, nblk, 128, beta, static_cast<float*>(dgq->ptr));
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(2), dim3(256), 0, s, pgk, nblk, 128, beta, static_cast<float*>(dgk->ptr));
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(2), dim3(1024), 0, s, pgq, nblk, 128, beta, static_cast<float*>(dgq->ptr));
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(2), dim3(1024), 0, s, pgk, nblk, 128, beta, static_cast<float*>(dgk->ptr));
   return check_launch("unfused_qknorm_rope_bwd: dg");
 }
