@@ -76,6 +76,21 @@ __global__ void rows_finish_kernel(const float* P, int nP, int M, int mode, cons
   out[m] = s;
 }
 
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* P, int nslices, int64_t slice, int rows, int cols,
+                                                        float beta, float* out, int64_t ld) {
+  // out[r][c..c+3] = beta out + sum over s (ascending) of P[s][r][c..c+3]
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cq = cols / 4;
+  if (q >= (int64_t)rows * cq) return;
+  const int r = (int)(q / cq), c = (int)(q % cq) * 4;
+  const float* p = P + (int64_t)r * cols + c;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(p);
+  for (int s = 1; s < nslices; ++s) acc = acc + *reinterpret_cast<const f32x4_t*>(p + s * slice);
+  f32x4_t* o = reinterpret_cast<f32x4_t*>(out + (int64_t)r * ld + c);
+  if (beta != 0.0f) acc = acc + beta * *o;
+  *o = acc;
+}
+
 __global__ __launch_bounds__(1024) void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out) {
   // block of 1024 threads: 64 columns x 16 partial groups; group j adds
   // partials j, j + 16, ...

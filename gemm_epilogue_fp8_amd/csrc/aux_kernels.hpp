@@ -27,6 +27,10 @@ __global__ void row_sumsq_kernel(const uint16_t* x, int64_t ld, int M, int K, fl
 //        = rowvec[m] * sum / D                  (mode 2)
 __global__ void rows_finish_kernel(const float* P, int nP, int M, int mode, const float* rowvec,
                                    int D, float eps, float* out);
+// Split-K finish: out[r][c] = beta out[r][c] + sum_{s < nslices} P[s * slice + r * cols + c],
+// slices added in ascending order; cols % 4 == 0, 16-byte aligned rows.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* P, int nslices, int64_t slice, int rows, int cols,
+                                                        float beta, float* out, int64_t ld);
 // out[k] = beta * out[k] + sum_{t < nP} P[t][k]
 __global__ __launch_bounds__(1024) void sum_partials_kernel(const float* P, int nP, int K, float beta, float* out);
 // Backward glue between attention and the QKV dgrad / wgrad GEMMs: inverse

@@ -548,6 +548,54 @@ static void wgrad_args(bool fp8, const Bwd8& q8, const void* X, int64_t ldX, con
   }
 }
 
+// Weight-gradient GEMMs contract over the tokens.  When the output has too
+// few 256 x 256 tiles to fill the chip (a 2048 x 2048 weight has 64), the
+// tokens are cut into up to 4 slices (a multiple of 64 each) that run as
+// extra workgroups and write fp32 partial products to the workspace; a
+// second pass adds the slices in order (bitwise deterministic).
+struct Split {
+  int n = 1;         // slices
+  int64_t kchunk;    // tokens per slice
+};
+
+static Split wgrad_split(int64_t Kin, int64_t Nout, int64_t M) {
+  Split sp;
+  sp.kchunk = M;
+  const int64_t tiles = ((Kin + 255) / 256) * ((Nout + 255) / 256);
+  int want = 1;
+  if (tiles * 4 <= 256 && M >= 4096) want = 4;
+  else if (tiles * 2 <= 256 && M >= 2048) want = 2;
+  if (want > 1) {
+    sp.kchunk = ((M + want - 1) / want + 63) / 64 * 64;
+    sp.n = (int)((M + sp.kchunk - 1) / sp.kchunk);
+  }
+  return sp;
+}
+
+// Launches a weight-gradient GEMM whose epilogue writes D = beta D + value
+// (fp32, e->out / e->ld_out / e->beta) and, optionally, row partials
+// (e->partial_out, `pstride` floats per slice).  With sp.n > 1 the slices go
+// to `part` (sp.n x Kin x Nout floats) and split_sum_kernel finishes D.
+static coda_status launch_wgrad(Prog p, int layout, bool fp8, GemmArgs g, EpiArgs e, const Split& sp, float* part,
+                                int64_t pstride, hipStream_t s, const char* what) {
+  if (sp.n <= 1) return launched(launch_gemm(p, layout, fp8, g, e, s), what);
+  float* out = static_cast<float*>(e.out);
+  const int64_t ld = e.ld_out;
+  const float beta = e.beta;
+  const int64_t slice = (int64_t)g.M * g.N;
+  e.out = part;
+  e.ld_out = g.N;
+  e.beta = 0.0f;
+  e.split_stride = slice;
+  e.split_pstride = pstride;
+  g.kchunk = (int)sp.kchunk;
+  TRY(launched(launch_gemm(p, layout, fp8, g, e, s), what));
+  const int64_t quads = slice / 4;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, part, sp.n, slice, g.M,
+                     g.N, beta, out, ld);
+  return check_launch(what);
+}
+
 static coda_status sum_partials_launch(const float* P, int nP, int K, float beta, float* out, hipStream_t s) {
   if (K == 0) return CODA_OK;
   hipLaunchKernelGGL(sum_partials_kernel, dim3((K + 63) / 64), dim3(1024), 0, s, P, nP, K, beta, out);
@@ -566,7 +614,9 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   const int nTg = (int)coda_partials_cols(N2);
   float* T2 = cv.take<float>((size_t)nT2 * M);
   float* T2c = cv.take<float>(M);
-  float* dgp = cv.take<float>((size_t)nTg * D);
+  const Split sp = wgrad_split(D, N2, M);
+  float* dgp = cv.take<float>((size_t)sp.n * nTg * D);
+  float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N2) : nullptr;
   uint16_t* dh = present(dh_out) ? nullptr : cv.take<uint16_t>((size_t)M * N2);
   Bwd8 q8{};
   ActQ dYrow{};
@@ -628,9 +678,9 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     GemmArgs g;
     int layout;
     wgrad_args(fp8, q8, u->ptr, u->ld, dhp, lddh, M, D, N2, &g, &e, &layout);
-    TRY(launched(launch_gemm(Prog::WgradGain, layout, fp8, g, e, s), "swiglu_bwd: dW"));
+    TRY(launch_wgrad(Prog::WgradGain, layout, fp8, g, e, sp, part, (int64_t)nTg * D, s, "swiglu_bwd: dW"));
   }
-  return sum_partials_launch(dgp, nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
+  return sum_partials_launch(dgp, sp.n * nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }
 
 static coda_status swiglu_bwd_check(const coda_mat* dY, const coda_weight* Wd, const coda_mat* hgu, const coda_mat* r,
@@ -687,6 +737,8 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int
     take_act(cv, M, K, 0);
     take_act(cv, M, N, 0);
   }
+  const Split sp = wgrad_split(K, N, M);
+  if (sp.n > 1) cv.take<float>((size_t)sp.n * K * N);
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -711,6 +763,8 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
     q8.xcol = take_act(cv, M, K, 0);
     q8.gcol = take_act(cv, M, N, 0);
   }
+  const Split sp = wgrad_split(K, N, M);
+  float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * K * N) : nullptr;
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   if (fp8) {
@@ -731,7 +785,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   GemmArgs g;
   int layout;
   wgrad_args(fp8, q8, a->ptr, a->ld, d_out->ptr, d_out->ld, M, K, N, &g, &e, &layout);
-  return launched(launch_gemm(Prog::StoreF32, layout, fp8, g, e, s), "rmsnorm_residual_bwd: dW");
+  return launch_wgrad(Prog::StoreF32, layout, fp8, g, e, sp, part, 0, s, "rmsnorm_residual_bwd: dW");
 }
 
 static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv, const coda_mat* x,
@@ -756,7 +810,9 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
   float* pgq = cv.take<float>((size_t)std::max(nblk, 1) * 128);
   float* pgk = cv.take<float>((size_t)std::max(nblk, 1) * 128);
   const int nTg = (int)coda_partials_cols(N3);
-  float* dgp = cv.take<float>((size_t)nTg * D);
+  const Split sp = wgrad_split(D, N3, M);
+  float* dgp = cv.take<float>((size_t)sp.n * nTg * D);
+  float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N3) : nullptr;
   Bwd8 q8{};
   if (fp8) {
     q8.grow = take_act(cv, M, N3, 1);
@@ -804,9 +860,9 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
     GemmArgs g;
     int layout;
     wgrad_args(fp8, q8, x->ptr, x->ld, dh, ldh, M, D, N3, &g, &e, &layout);
-    TRY(launched(launch_gemm(Prog::WgradGain, layout, fp8, g, e, s), "qknorm_rope_bwd: dW"));
+    TRY(launch_wgrad(Prog::WgradGain, layout, fp8, g, e, sp, part, (int64_t)nTg * D, s, "qknorm_rope_bwd: dW"));
   }
-  return sum_partials_launch(dgp, nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
+  return sum_partials_launch(dgp, sp.n * nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }
 
 extern "C" coda_status coda_linear_qknorm_rope_bwd_workspace(int64_t M, int64_t D, int32_t precision, size_t* bytes) {

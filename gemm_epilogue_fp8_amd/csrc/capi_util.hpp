@@ -124,6 +124,7 @@ GemmArgs gemm_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64
   g.A = A; g.B = B; g.lda = lda; g.ldb = ldb;
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
   g.tiles_m = g.tiles_n = 0;
+  g.kchunk = (int)K;
   return g;
 }
 

@@ -58,6 +58,8 @@ struct EpiArgs {
   int region;                          // QKV: width D of each of q, k, v
   int seq_len;
   int vocab;                           // CE: valid column count
+  int64_t split_stride;                // split K: fp32 elements between the slices' outputs
+  int64_t split_pstride;               // split K: floats between the slices' row partials
 };
 
 template <class Cfg>
@@ -829,6 +831,16 @@ template <class Cfg, class Epi>
 __global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES + scratch_bytes<Cfg>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (gridDim.y > 1) {
+    // split K (fp32 outputs only): slice y covers K [y kchunk, min(K, (y + 1) kchunk)) and
+    // writes its own output and partials, which a separate pass adds up in a fixed order
+    const int kb = blockIdx.y * g.kchunk;
+    g.K = min(g.kchunk, g.K - kb);
+    g.A = static_cast<const char*>(g.A) + (Cfg::A_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.lda * Cfg::ESIZE);
+    g.B = static_cast<const char*>(g.B) + (Cfg::B_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.ldb * Cfg::ESIZE);
+    e.out = static_cast<float*>(e.out) + blockIdx.y * e.split_stride;
+    if (e.partial_out) e.partial_out += blockIdx.y * e.split_pstride;
+  }
   const TileCoord tc = tile_coord(blockIdx.x, g.tiles_m, g.tiles_n, 8);
   Ctx<Cfg> c;
   c.m0 = tc.tm * Cfg::BM;

@@ -91,6 +91,7 @@ struct GemmArgs {
   int64_t lda, ldb;
   int M, N, K;
   int tiles_m, tiles_n;
+  int kchunk;      // split K: workgroup (x, y) runs K slice [y kchunk, (y + 1) kchunk); gridDim.y slices
 };
 
 // ---------------------------------------------------------------- operand tiles

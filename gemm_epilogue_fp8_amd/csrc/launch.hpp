@@ -45,7 +45,8 @@ hipError_t launch_one(GemmArgs g, const EpiArgs& e, hipStream_t s) {
   g.tiles_n = tiles(g.N, Cfg::BN);
   const int ntiles = g.tiles_m * g.tiles_n;
   if (ntiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_epi_kernel<Cfg, Epi>), dim3(ntiles), dim3(Cfg::T), 0, s, g, e);
+  const int slices = g.kchunk > 0 && g.kchunk < g.K ? (g.K + g.kchunk - 1) / g.kchunk : 1;
+  hipLaunchKernelGGL((gemm_epi_kernel<Cfg, Epi>), dim3(ntiles, slices), dim3(Cfg::T), 0, s, g, e);
   return hipGetLastError();
 }
 

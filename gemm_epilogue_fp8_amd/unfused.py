@@ -15,8 +15,8 @@ from typing import Dict
 
 import torch
 
-from . import (EPI_ACCUM_F32, EPI_STORE_BF16, _check, _p, _stream, _ws_call, gemm_epi, lib, pack_gate_up,
-               rope_table)
+from . import (EPI_ACCUM_F32, EPI_STORE_BF16, _check, _p, _stream, _ws_call, gemm_epi, lib,
+               linear_rmsnorm_residual_bwd, pack_gate_up, rope_table)
 
 
 def rmsnorm_fwd(x, g, eps, out, r_out=None):
@@ -61,6 +61,12 @@ def qknorm_rope_bwd(dq, dk, dv, qkv, gq, gk, rope, seq_len, eps, dqkv, dgq, dgk,
 
 
 STORE = [(EPI_STORE_BF16, 0, 0.0)]
+
+
+def _wgrad(a, dout, W, dW, beta):
+    """dW = beta dW + a^T dout: the plain fp32-accumulate weight-gradient GEMM
+    (the same kernel, token-axis split included, that the fused path uses)."""
+    linear_rmsnorm_residual_bwd(dout, a, W, dW, beta=beta)
 
 
 def _acc(beta):
@@ -111,16 +117,16 @@ class UnfusedBlock:
     def backward(self, x, o, b, dY, dq, dk, dv, beta=0.0):
         D = self.D
         gemm_epi(STORE, dY, 0, self.Wd, 1, b["da"])                    # da = dY Wd^T
-        gemm_epi(_acc(beta), b["a"], 1, dY, 0, b["dWd"])               # dWd = a^T dY
+        _wgrad(b["a"], dY, self.Wd, b["dWd"], beta)                      # dWd = a^T dY
         swiglu_bwd(b["da"], b["hgu"], b["dhgu"])
         gemm_epi(STORE, b["dhgu"], 0, self.Wgu, 1, b["dxn2"])          # dxn2 = dh Wgu^T
-        gemm_epi(_acc(beta), b["xn2"], 1, b["dhgu"], 0, b["dWgu"])     # dWgu = xn2^T dh
+        _wgrad(b["xn2"], b["dhgu"], self.Wgu, b["dWgu"], beta)           # dWgu = xn2^T dh
         rmsnorm_bwd(b["h1"], self.g2, b["r2"], b["dxn2"], b["dh1"], b["dg2"], dres=dY, beta=beta)
         gemm_epi(STORE, b["dh1"], 0, self.Wo, 1, b["do"])              # do = dh1 Wo^T
-        gemm_epi(_acc(beta), o, 1, b["dh1"], 0, b["dWo"])              # dWo = o^T dh1
+        _wgrad(o, b["dh1"], self.Wo, b["dWo"], beta)                     # dWo = o^T dh1
         qknorm_rope_bwd(dq, dk, dv, b["qkv"], self.gq, self.gk, self.rope, self.seq_len, self.eps, b["dqkv"],
                         b["dgq"], b["dgk"], beta=beta)
         gemm_epi(STORE, b["dqkv"], 0, self.Wqkv, 1, b["dxn1"])        # dxn1 = dqkv Wqkv^T
-        gemm_epi(_acc(beta), b["xn1"], 1, b["dqkv"], 0, b["dWqkv"])   # dWqkv = xn1^T dqkv
+        _wgrad(b["xn1"], b["dqkv"], self.Wqkv, b["dWqkv"], beta)         # dWqkv = xn1^T dqkv
         rmsnorm_bwd(x, self.g1, b["r1"], b["dxn1"], b["dx"], b["dg1"], dres=b["dh1"], beta=beta)
         return b

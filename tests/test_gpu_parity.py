@@ -308,6 +308,46 @@ def check_block_fp8(shape, f, b, F, B):
         assert rel_norm(v, B[k]) <= 2e-2, (k, rel_norm(v, B[k]))
 
 
+@pytest.mark.parametrize("shape,seed", [(ci.BlockShape(M=4096, D=256, F=352, seq_len=2048), 5)])
+def test_block_backward_split_k(shape, seed):
+    """Many tokens, small weights: every weight-gradient GEMM has at most 3
+    output tiles, so the library splits the token axis (4 slices) and adds the
+    slices in a second pass."""
+    P, f, b = _run_block(shape, seed)
+    F = ob.block_forward_contract(P, shape)
+    B = ob.block_backward_contract(P, F, shape)
+    dWg, dWu = unpack_gu(b["dWgu"])
+    assert_grad("dWg", dWg, B["dWg"])
+    assert_grad("dWu", dWu, B["dWu"])
+    for k in ("dWqkv", "dWo", "dWd", "dg1", "dg2", "dgq", "dgk"):
+        assert_grad(k, b[k], B[k])
+    assert_bf16("dx", b["dx"], B["dx"])
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_residual_backward_split_k_ragged(precision):
+    """4100 tokens (slices of 1088, 1088, 1088 and 836) with beta = 1 over a
+    seeded fp32 prior; bf16 and fp8 operands."""
+    from tests.helpers import FP8_TOL
+    rng = np.random.default_rng(41)
+    M, K, N = 4100, 256, 384
+    dout, a = rand_bf16(rng, M, N, std=0.1), rand_bf16(rng, M, K)
+    W = rand_bf16(rng, K, N, std=K ** -0.5)
+    prior = ci.fp32_prior((K, N), 12)
+    wt = coda.Weight(bf(W))
+    if precision == coda.PREC_FP8:
+        wt.prepare_fp8()
+    dW = f32(prior)
+    coda.linear_rmsnorm_residual_bwd(bf(dout), bf(a), wt, dW, beta=1.0, precision=precision)
+    torch.cuda.synchronize()
+    fp8 = precision == coda.PREC_FP8
+    ref = prior + ob.mm(a.T.copy(), dout, fp8=fp8)
+    if fp8:
+        assert_bf16("dW", to_np(dW), ref, tol=FP8_TOL, norm_rel=1e-3)
+    else:
+        assert_grad("dW", to_np(dW), ref)
+
+
 @pytest.mark.parametrize("with_da", [True, False])
 def test_fp8_residual_linear_backward_same_inputs(with_da):
     """One fp8 stage from identical seeded bf16 inputs: every quantiser sees the
