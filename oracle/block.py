@@ -274,6 +274,82 @@ def ce_backward_contract(h, W, labels, lse, n_valid, dloss=1.0, ignore_index=-10
     return dict(G=G, dh=dh, dW=dW, scale=s)
 
 
+# --------------------------------------------------------------------------- final RMSNorm -> LM head -> CE
+# The third occurrence of the GEMM-residual-RMSNorm-GEMM pattern in the CODA
+# paper (§3.2.1, final down-projection -> residual -> final RMSNorm -> LM
+# head): the norm's r becomes a row scale of the logits, the gain folds into
+# W_vocab, and the loss is the cross-entropy above.
+def norm_ce_canonical(y, g, W, labels, eps, ignore_index=-100, dres=None, dt=np.float64):
+    """Canonical evaluation: xn = RMSNorm(y, g), z = xn W, mean cross-entropy
+    over the rows whose label is not ignored, and the analytic gradients
+    dz (softmax - onehot) / n_valid, dxn = dz W^T, dW = xn^T dz, then the
+    RMSNorm backward for (dy, dg); dy also receives the residual-stream
+    gradient dres when given."""
+    y = np.asarray(y, dt)
+    g = np.asarray(g, dt)
+    W = np.asarray(W, dt)
+    xn = ops.rms_norm(y, g, eps)
+    z = xn @ W
+    loss, per_row, lse, n_valid, dz = ops.cross_entropy(z, labels, ignore_index)
+    dxn = dz @ W.T
+    dW = xn.T @ dz
+    dy, dg = ops.rms_norm_bwd(y, g, eps, dxn)
+    if dres is not None:
+        dy = dy + np.asarray(dres, dt)
+    return dict(loss=loss, per_row=per_row, lse=lse, n_valid=n_valid, z=z, dy=dy, dW=dW, dg=dg)
+
+
+def norm_ce_forward_contract(y, g, W, labels, eps, ignore_index=-100, rnd: Callable = nm.bf16, dt=np.float32):
+    """Reparameterised forward: W~ = rnd(g W), r = inv_rms(y), z = r (y W~);
+    lse, per-row loss and the mean are reduced in float64 from z."""
+    y = np.asarray(y, dt)
+    Wt = rnd(np.asarray(g, dt)[:, None] * np.asarray(W, dt))
+    r = ops.inv_rms(y, eps)
+    z = r[:, None] * mm(y, Wt)
+    loss, per_row, lse, n_valid, _ = ops.cross_entropy(z.astype(np.float64), labels, ignore_index)
+    return dict(loss=np.float32(loss) if dt == np.float32 else loss, per_row=per_row.astype(dt),
+                lse=lse.astype(dt), n_valid=n_valid, z=z, r=r, Wt=Wt)
+
+
+def norm_ce_backward_contract(y, g, W, labels, lse, r, n_valid, eps, dloss=1.0, ignore_index=-100,
+                              rnd: Callable = nm.bf16, dres=None, priors=None, beta: float = 0.0, dt=np.float32):
+    """Reparameterised backward with the fused path's rounding points.
+
+    z is recomputed as r (y W~).  The stored gradient tile is
+    G~ = rnd(r (exp(z - lse) - onehot)) on valid rows (0 on ignored rows);
+    with s = dloss / n_valid (float32) and T = s sum_v G~ z (from the stored
+    G~), dy = rnd(s G~ W~^T - (r T / D) y + dres), dW = beta prior +
+    s g (y^T G~) and dg = beta prior + s sum_v W (y^T G~).
+    """
+    y = np.asarray(y, dt)
+    g = np.asarray(g, dt)
+    W = np.asarray(W, dt)
+    Wt = rnd(g[:, None] * W)
+    labels = np.asarray(labels)
+    r = np.asarray(r, dt)
+    z = r[:, None] * mm(y, Wt)
+    valid = labels != ignore_index
+    p = np.exp(z - np.asarray(lse, dt)[:, None]).astype(dt)
+    rows = np.nonzero(valid)[0]
+    p[rows, labels[rows]] -= dt(1.0)
+    p[~valid] = 0
+    Gt = rnd(r[:, None] * p)
+    s = dt(dloss) / dt(max(n_valid, 1)) if n_valid > 0 else dt(0)
+    T = s * np.sum(Gt * z, axis=1, dtype=dt)
+    D = y.shape[1]
+    dy = s * mm(Gt, Wt.T) - (r * T / dt(D))[:, None] * y
+    if dres is not None:
+        dy = dy + np.asarray(dres, dt)
+    dy = rnd(dy)
+    acc = mm(y.T, Gt)
+    dW = s * (g[:, None] * acc)
+    dg = s * np.sum(W * acc, axis=1, dtype=dt)
+    if priors is not None:
+        dW = dt(beta) * priors["dW"] + dW
+        dg = dt(beta) * priors["dg"] + dg
+    return dict(G=Gt, dy=dy, dW=dW, dg=dg, T=T, scale=s)
+
+
 def tile_partials(values, BN: int, reduce: Callable = np.sum):
     """Per-(column tile, row) partial reductions P[t, i] over columns
     [t BN, (t+1) BN) of ``values`` (the ragged last tile is shorter)."""

@@ -236,3 +236,65 @@ def test_ce_contract_matches_canonical():
     mstar = m_t.max(axis=0)
     lse_c = mstar + np.log(np.sum(s_t * np.exp(m_t - mstar), axis=0))
     np.testing.assert_allclose(lse_c, ops.logsumexp_rows(z), rtol=1e-13)
+
+
+# ------------------------------------------------------------------ final RMSNorm -> LM head -> CE
+def _norm_ce_tiny(seed=21, M=12, D=16, V=40):
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((M, D))
+    g = 1 + 0.1 * rng.standard_normal(D)
+    W = rng.standard_normal((D, V)) / math.sqrt(D)
+    labels = rng.integers(0, V, M)
+    labels[[2, 7]] = -100
+    dres = 0.1 * rng.standard_normal((M, D))
+    return y, g, W, labels, dres
+
+
+def test_norm_ce_canonical_matches_torch_autograd():
+    y, g, W, labels, dres = _norm_ce_tiny()
+    C = ob.norm_ce_canonical(y, g, W, labels, 1e-6, dres=dres)
+    Y, G_, W_ = (torch.tensor(a, requires_grad=True) for a in (y, g, W))
+    r = torch.rsqrt((Y * Y).mean(dim=1, keepdim=True) + 1e-6)
+    z = (Y * r * G_) @ W_
+    loss = torch.nn.functional.cross_entropy(z, torch.tensor(labels), ignore_index=-100)
+    (loss + (Y * torch.tensor(dres)).sum()).backward()
+    assert abs(C["loss"] - loss.item()) <= 1e-12 * abs(loss.item())
+    np.testing.assert_allclose(C["dy"], Y.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dW"], W_.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dg"], G_.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_norm_ce_reparameterised_equals_canonical():
+    """With rounding off, in float64, the delayed-r form (z = r (y W~), the
+    stored gradient r (p - onehot), the T correction, dW and dg through the
+    fold) equals the canonical RMSNorm -> linear -> CE and its autograd."""
+    y, g, W, labels, dres = _norm_ce_tiny(22)
+    eps = 1e-6
+    C = ob.norm_ce_canonical(y, g, W, labels, eps, dres=dres)
+    F = ob.norm_ce_forward_contract(y, g, W, labels, eps, rnd=_ident, dt=np.float64)
+    assert abs(F["loss"] - C["loss"]) <= 1e-12 * abs(C["loss"]) and F["n_valid"] == C["n_valid"] == 10
+    np.testing.assert_allclose(F["z"], C["z"], rtol=1e-12, atol=1e-14)
+    B = ob.norm_ce_backward_contract(y, g, W, labels, F["lse"], F["r"], F["n_valid"], eps, rnd=_ident,
+                                     dres=dres, dt=np.float64)
+    for k in ("dy", "dW", "dg"):
+        np.testing.assert_allclose(B[k], C[k], rtol=1e-10, atol=1e-14, err_msg=k)
+    assert np.all(B["G"][[2, 7]] == 0)
+
+
+def test_norm_ce_reduces_to_plain_ce():
+    """Rows of unit mean square with g = 1 and eps = 0 make the norm an
+    identity: the loss, lse and dW equal the plain cross-entropy's, and with
+    every row on the unit sphere dy is the plain dh minus its radial part."""
+    rng = np.random.default_rng(23)
+    M, D, V = 9, 8, 30
+    y = rng.standard_normal((M, D))
+    y /= np.sqrt(np.mean(y * y, axis=1, keepdims=True))
+    W = rng.standard_normal((D, V)) / math.sqrt(D)
+    labels = rng.integers(0, V, M)
+    C = ob.norm_ce_canonical(y, np.ones(D), W, labels, 0.0)
+    loss, per_row, lse, n, dz = ops.cross_entropy(y @ W, labels)
+    assert abs(C["loss"] - loss) <= 1e-13 * abs(loss)
+    np.testing.assert_allclose(C["dW"], y.T @ dz, rtol=1e-12, atol=1e-15)
+    dh = dz @ W.T
+    radial = np.sum(dh * y, axis=1, keepdims=True) / D * y
+    np.testing.assert_allclose(C["dy"], dh - radial, rtol=1e-10, atol=1e-14)
