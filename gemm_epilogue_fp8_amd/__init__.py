@@ -282,3 +282,30 @@ def linear_cross_entropy_bwd(h, W, labels, lse, n_valid, dloss, dh, dW, beta=0.0
     _check(L.coda_linear_cross_entropy_bwd(_p(h), C.byref(wc.c()), _p(labels), ignore_index, _p(lse), _p(n_valid),
                                            dloss, _p(dh), _p(dW), beta, chunk_rows, precision, ws, n, _stream()))
     return dh, dW
+
+
+def linear_rmsnorm_cross_entropy_fwd(y, W, eps, labels, loss, lse, n_valid, sumsq_partials=None, per_row=None,
+                                     n_bad=None, r_out=None, ignore_index=-100, precision: int = PREC_BF16):
+    """Final RMSNorm (gain folded into W) -> LM head -> mean cross-entropy."""
+    L = lib()
+    wc = W if isinstance(W, Weight) else Weight(W)
+    M, D = y.shape
+    ws, n = _ws_call(L.coda_linear_rmsnorm_cross_entropy_fwd_workspace,
+                     (M, D, wc.w.shape[1], int(sumsq_partials is not None), precision), y.device)
+    _check(L.coda_linear_rmsnorm_cross_entropy_fwd(_p(y), _p(sumsq_partials), C.byref(wc.c()), eps, _p(labels),
+                                                   ignore_index, _p(loss), _p(lse), _p(per_row), _p(n_valid),
+                                                   _p(n_bad), _p(r_out), precision, ws, n, _stream()))
+    return loss
+
+
+def linear_rmsnorm_cross_entropy_bwd(y, r, W, W_unfolded, g, labels, lse, n_valid, dloss, dy, dW, dg, dres=None,
+                                     beta=0.0, chunk_rows=0, ignore_index=-100, precision: int = PREC_BF16):
+    L = lib()
+    wc = W if isinstance(W, Weight) else Weight(W)
+    M, D = y.shape
+    ws, n = _ws_call(L.coda_linear_rmsnorm_cross_entropy_bwd_workspace, (M, D, wc.w.shape[1], chunk_rows, precision),
+                     y.device)
+    _check(L.coda_linear_rmsnorm_cross_entropy_bwd(_p(y), _p(r), C.byref(wc.c()), _p(W_unfolded), _p(g), _p(labels),
+                                                   ignore_index, _p(lse), _p(n_valid), dloss, _p(dres), _p(dy),
+                                                   _p(dW), _p(dg), beta, chunk_rows, precision, ws, n, _stream()))
+    return dy, dW, dg

@@ -1061,3 +1061,206 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
   }
   return CODA_OK;
 }
+
+// ======================================================================== final RMSNorm -> LM head -> CE
+// The third GEMM-residual-RMSNorm-GEMM occurrence of the CODA paper
+// (§3.2.1): the final norm's r is a row scale of the logits, its gain is
+// folded into W_vocab (W~ = bf16(g W)), and the cross-entropy epilogues of
+// coda_linear_cross_entropy run on z = r (y W~).
+static size_t nce_fwd_layout(Carver& cv, int64_t M, int64_t V, bool need_sumsq, float** Pm, float** Ps, float** zy,
+                             float** per_row, int** status, float** P1, float** r) {
+  const int nT = (int)coda_partials_cols(V);
+  *Pm = cv.take<float>((size_t)nT * M);
+  *Ps = cv.take<float>((size_t)nT * M);
+  *zy = cv.take<float>(M);
+  *per_row = cv.take<float>(M);
+  *status = cv.take<int>(M);
+  *P1 = need_sumsq ? cv.take<float>(M) : nullptr;
+  *r = cv.take<float>(M);
+  return cv.off;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V,
+                                                                       int32_t have_partials, int32_t precision,
+                                                                       size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  (void)D;
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  Carver cv(nullptr);
+  float *a, *b, *c, *d, *e, *f;
+  int* st;
+  nce_fwd_layout(cv, M, V, !have_partials, &a, &b, &c, &d, &st, &e, &f);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
+    const coda_mat* y, const coda_mat* sumsq_partials, const coda_weight* W, float eps, const coda_mat* labels,
+    int32_t ignore_index, const coda_mat* loss, const coda_mat* lse, const coda_mat* per_row, const coda_mat* n_valid,
+    const coda_mat* n_bad, const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  TRY(check_mat(y, "y", CODA_BF16, -1, -1));
+  const int64_t M = y->rows, D = y->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t V = W->w.cols;
+  TRY(check_weight(W, "W", D, V, precision));
+  const coda_mat* P = sumsq_partials;
+  if (present(P)) {
+    TRY(check_mat(P, "sumsq_partials", CODA_F32, -1, M));
+    if (P->rows < 1 || P->rows > RowPartials<GemmCfg<kBM, kBN, 2, 4, true, false>>::MAX_PARTIALS || P->ld != M)
+      return fail(CODA_ERR_SHAPE, "sumsq_partials: 1..32 rows of M, ld == M");
+  }
+  TRY(check_vec(labels, "labels", CODA_I32, M));
+  TRY(check_vec(loss, "loss", CODA_F32, 1));
+  TRY(check_vec(lse, "lse", CODA_F32, M));
+  TRY(check_vec(per_row, "per_row", CODA_F32, M, true));
+  TRY(check_vec(n_valid, "n_valid", CODA_I32, 1));
+  TRY(check_vec(n_bad, "n_bad", CODA_I32, 1, true));
+  TRY(check_vec(r_out, "r_out", CODA_F32, M, true));
+  if (ignore_index >= 0 && ignore_index < V) return fail(CODA_ERR_VALUE, "ignore_index must lie outside [0, V)");
+  Carver cv(ws);
+  float *Pm, *Ps, *zy, *pr, *P1, *rws;
+  int* st;
+  nce_fwd_layout(cv, M, V, !present(P), &Pm, &Ps, &zy, &pr, &st, &P1, &rws);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  float* per = present(per_row) ? static_cast<float*>(per_row->ptr) : pr;
+  if (M > 0) {
+    const float* parts = present(P) ? static_cast<const float*>(P->ptr) : P1;
+    const int nP = present(P) ? (int)P->rows : 1;
+    if (!present(P)) {
+      hipLaunchKernelGGL(row_sumsq_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(y->ptr), y->ld, (int)M, (int)D, P1);
+      TRY(check_launch("rmsnorm_cross_entropy_fwd: sumsq"));
+    }
+    EpiArgs e = epi0();
+    e.labels = static_cast<const int*>(labels->ptr);
+    e.partial_out = Pm;
+    e.partial_out2 = Ps;
+    e.rowvec_out = zy;
+    e.rowvec_out2 = present(r_out) ? static_cast<float*>(r_out->ptr) : rws;
+    e.row_partials = parts;
+    e.n_row_partials = nP;
+    e.norm_dim = (int)D;
+    e.eps = eps;
+    e.vocab = (int)V;
+    GemmArgs g = gemm_args(y->ptr, y->ld, W->w.ptr, W->w.ld, M, V, D);
+    TRY(launched(launch_gemm(Prog::CrossEntropyNorm, LAYOUT_NN, false, g, e, s), "rmsnorm_cross_entropy_fwd: logits"));
+    hipLaunchKernelGGL(ce_finish_rows_kernel, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, Pm, Ps,
+                       (int)coda_partials_cols(V), (int)M, zy, static_cast<const int*>(labels->ptr), (int)V,
+                       ignore_index, static_cast<float*>(lse->ptr), per, st);
+    TRY(check_launch("rmsnorm_cross_entropy_fwd: rows"));
+  }
+  hipLaunchKernelGGL(ce_finish_loss_kernel, dim3(1), dim3(1024), 0, s, per, st, (int)M, static_cast<float*>(loss->ptr),
+                     static_cast<int*>(n_valid->ptr), present(n_bad) ? static_cast<int*>(n_bad->ptr) : nullptr);
+  return check_launch("rmsnorm_cross_entropy_fwd: loss");
+}
+
+static size_t nce_bwd_layout(Carver& cv, int64_t M, int64_t D, int64_t V, int64_t chunk, float** scale, uint16_t** G,
+                             float** Tp, float** Tc, float** dgp) {
+  *scale = cv.take<float>(1);
+  *G = cv.take<uint16_t>((size_t)chunk * ((V + 7) / 8 * 8));
+  *Tp = cv.take<float>((size_t)coda_partials_cols(V) * chunk);
+  *Tc = cv.take<float>(chunk);
+  *dgp = cv.take<float>((size_t)coda_partials_cols(V) * D);
+  return cv.off;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V,
+                                                                       int64_t chunk_rows, int32_t precision,
+                                                                       size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  Carver cv(nullptr);
+  float *sc, *Tp, *Tc, *dgp;
+  uint16_t* G;
+  nce_bwd_layout(cv, M, D, V, chunk, &sc, &G, &Tp, &Tc, &dgp);
+  *bytes = cv.off;
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
+    const coda_mat* y, const coda_mat* r, const coda_weight* W, const coda_mat* W_unfolded, const coda_mat* gvec,
+    const coda_mat* labels, int32_t ignore_index, const coda_mat* lse, const coda_mat* n_valid, float dloss,
+    const coda_mat* dres, const coda_mat* dy, const coda_mat* dW, const coda_mat* dg, float beta, int64_t chunk_rows,
+    int32_t precision, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_precision(precision));
+  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  TRY(check_mat(y, "y", CODA_BF16, -1, -1));
+  const int64_t M = y->rows, D = y->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t V = W->w.cols;
+  TRY(check_weight(W, "W", D, V, precision));
+  TRY(check_mat(W_unfolded, "W_unfolded", CODA_BF16, D, V));
+  TRY(check_vec(gvec, "g", CODA_F32, D));
+  TRY(check_vec(r, "r", CODA_F32, M));
+  TRY(check_vec(labels, "labels", CODA_I32, M));
+  TRY(check_vec(lse, "lse", CODA_F32, M));
+  TRY(check_vec(n_valid, "n_valid", CODA_I32, 1));
+  TRY(check_mat(dres, "dres", CODA_BF16, M, D, true));
+  TRY(check_mat(dy, "dy", CODA_BF16, M, D));
+  TRY(check_mat(dW, "dW", CODA_F32, D, V));
+  TRY(check_vec(dg, "dg", CODA_F32, D));
+  if (ignore_index != -100)
+    return fail(CODA_ERR_UNSUPPORTED, "rmsnorm_cross_entropy_bwd: ignore_index must be -100 in this build");
+  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  Carver cv(ws);
+  float *scale, *Tp, *Tc, *dgp;
+  uint16_t* G;
+  nce_bwd_layout(cv, M, D, V, chunk, &scale, &G, &Tp, &Tc, &dgp);
+  TRY(ws_check(cv, ws_bytes, ws));
+  hipStream_t s = S(stream);
+  const int64_t ldG = (V + 7) / 8 * 8;
+  const int nT = (int)coda_partials_cols(V);
+  hipLaunchKernelGGL(ce_scale_kernel, dim3(1), dim3(1), 0, s, static_cast<const int*>(n_valid->ptr), dloss, scale);
+  TRY(check_launch("rmsnorm_cross_entropy_bwd: scale"));
+  const uint16_t* yp = static_cast<const uint16_t*>(y->ptr);
+  const int* lab = static_cast<const int*>(labels->ptr);
+  const float* lsep = static_cast<const float*>(lse->ptr);
+  const float* rp = static_cast<const float*>(r->ptr);
+  for (int64_t c0 = 0; c0 < M; c0 += chunk) {
+    const int64_t mc = std::min(chunk, M - c0);
+    {  // recompute z = r (y W~) for the chunk: G~ = bf16(r (p - onehot)), T partials
+      EpiArgs e = epi0();
+      e.out = G; e.ld_out = ldG;
+      e.labels = lab + c0;
+      e.rowvec = lsep + c0;
+      e.rowvec2 = rp + c0;
+      e.partial_out = Tp;
+      GemmArgs g = gemm_args(yp + c0 * y->ld, y->ld, W->w.ptr, W->w.ld, mc, V, D);
+      TRY(launched(launch_gemm(Prog::CrossEntropyGNorm, LAYOUT_NN, false, g, e, s), "rmsnorm_cross_entropy_bwd: G"));
+    }
+    hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((mc + 255) / 256)), dim3(256), 0, s, Tp, nT, (int)mc, 0,
+                       (const float*)nullptr, 0, 0.0f, Tc);
+    TRY(check_launch("rmsnorm_cross_entropy_bwd: finish T"));
+    {  // dy = s (G~ W~^T - (r T / D) y) + dres
+      EpiArgs e = epi0();
+      e.out = static_cast<uint16_t*>(dy->ptr) + c0 * dy->ld; e.ld_out = dy->ld;
+      e.aux0 = yp + c0 * y->ld; e.ld_aux0 = y->ld;
+      if (present(dres)) { e.aux1 = static_cast<const uint16_t*>(dres->ptr) + c0 * dres->ld; e.ld_aux1 = dres->ld; }
+      e.rowvec = rp + c0;
+      e.row_partials = Tc;
+      e.n_row_partials = 1;
+      e.norm_dim = (int)D;
+      e.alpha_dev = scale;
+      GemmArgs g = gemm_args(G, ldG, W->w.ptr, W->w.ld, mc, D, V);
+      TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, false, g, e, s), "rmsnorm_cross_entropy_bwd: dy"));
+    }
+    const float b = c0 == 0 ? beta : 1.0f;
+    {  // dW = b dW + s g (y^T G~), gain partials s sum_v W (y^T G~)
+      EpiArgs e = epi0();
+      e.out = dW->ptr; e.ld_out = dW->ld;
+      e.beta = b;
+      e.aux0 = W_unfolded->ptr; e.ld_aux0 = W_unfolded->ld;
+      e.rowvec = fptr(gvec);
+      e.partial_out = dgp;
+      e.alpha_dev = scale;
+      GemmArgs g = gemm_args(yp + c0 * y->ld, y->ld, G, ldG, D, V, mc);
+      TRY(launched(launch_gemm(Prog::WgradGain, LAYOUT_TN, false, g, e, s), "rmsnorm_cross_entropy_bwd: dW"));
+    }
+    TRY(sum_partials_launch(dgp, nT, (int)D, b, static_cast<float*>(dg->ptr), s));
+  }
+  return CODA_OK;
+}

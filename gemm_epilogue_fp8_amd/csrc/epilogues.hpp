@@ -58,6 +58,8 @@ struct EpiArgs {
   int region;                          // QKV: width D of each of q, k, v
   int seq_len;
   int vocab;                           // CE: valid column count
+  const float* rowvec2;                // second row vector (CE backward through a norm: r)
+  float* rowvec_out2;                  // second row vector output (CE forward through a norm: r)
   int64_t split_stride;                // split K: fp32 elements between the slices' outputs
   int64_t split_pstride;               // split K: floats between the slices' row partials
 };
@@ -326,9 +328,11 @@ struct RowPartials {
 };
 
 // Finishes the per-row factor of the tile's rows into c.rowv():
-// r = (sum of partials / D + eps)^(-1/2), or a given row vector.
+// r = (sum of partials / D + eps)^(-1/2), or a given row vector; the tiles of
+// the first N tile also write it to r_out when given.
 template <class Cfg>
-__device__ __forceinline__ void finish_inv_rms(const EpiArgs& e, const Ctx<Cfg>& c, const RowPartials<Cfg>& rp) {
+__device__ __forceinline__ void finish_inv_rms(const EpiArgs& e, const Ctx<Cfg>& c, const RowPartials<Cfg>& rp,
+                                               float* r_out) {
   float* rv = c.rowv();
   if (e.row_partials) {
     rp.reduce(c, rv);
@@ -338,7 +342,7 @@ __device__ __forceinline__ void finish_inv_rms(const EpiArgs& e, const Ctx<Cfg>&
     rv[c.tid] = m < c.M ? e.rowvec[m] : 0.0f;
   }
   __syncthreads();
-  if (e.rowvec_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M) e.rowvec_out[c.m0 + c.tid] = rv[c.tid];
+  if (r_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M) r_out[c.m0 + c.tid] = rv[c.tid];
 }
 
 // ================================================================ programs
@@ -427,7 +431,7 @@ struct EpiSwiGLU {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
-    finish_inv_rms<Cfg>(e, c, p.rp);
+    finish_inv_rms<Cfg>(e, c, p.rp, e.rowvec_out);
     apply_fp8_scales<Cfg>(e, c, acc);
     const float* rv = c.rowv();
     // h = r * acc (kept in acc); a = SiLU(h_gate) * h_up staged as [BM][BN/2]
@@ -476,7 +480,7 @@ struct EpiQKNormRope {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
   }
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
-    finish_inv_rms<Cfg>(e, c, p.rp);
+    finish_inv_rms<Cfg>(e, c, p.rp, e.rowvec_out);
     apply_fp8_scales<Cfg>(e, c, acc);
     const float* rv = c.rowv();
     const int D = e.region;
@@ -646,13 +650,16 @@ struct EpiNormCorrection {
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
     using S = StageBF<Cfg::BM, Cfg::BN>;
     // u and res come into registers one 32-row block at a time
+    // out = sc (acc - c u) + res, with sc = alpha (* *alpha_dev) and res optional
     RowBlock<Cfg> u[2], z[2];
+    const bool has_res = e.aux1 != nullptr;
     u[0].load(e.aux0, e.ld_aux0, c, 0);
-    z[0].load(e.aux1, e.ld_aux1, c, 0);
+    if (has_res) z[0].load(e.aux1, e.ld_aux1, c, 0);
     if (Cfg::TM > 1) {
       u[1].load(e.aux0, e.ld_aux0, c, 1);
-      z[1].load(e.aux1, e.ld_aux1, c, 1);
+      if (has_res) z[1].load(e.aux1, e.ld_aux1, c, 1);
     }
+    const float sc = e.alpha_dev ? e.alpha * *e.alpha_dev : e.alpha;
     float* cv = c.rowv();
     p.rp.reduce(c, cv);
     if (c.tid < Cfg::BM) {
@@ -671,10 +678,11 @@ struct EpiNormCorrection {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           S::put4(s, c.lrow(i), c.lcol(j, q),
-                  round_bf4(frag(acc, i, j, q) - cc * u[i & 1].get(j, q) + z[i & 1].get(j, q)));
+                  round_bf4(sc * (frag(acc, i, j, q) - cc * u[i & 1].get(j, q)) +
+                            (has_res ? z[i & 1].get(j, q) : f32x4_t{0, 0, 0, 0})));
       if (i + 2 < Cfg::TM) {
         u[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
-        z[i & 1].load(e.aux1, e.ld_aux1, c, i + 2);
+        if (has_res) z[i & 1].load(e.aux1, e.ld_aux1, c, i + 2);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -694,6 +702,7 @@ struct EpiWgradGain {
     w[0].load(e.aux0, e.ld_aux0, c, 0);
     if (Cfg::TM > 1) w[1].load(e.aux0, e.ld_aux0, c, 1);
     apply_fp8_scales<Cfg>(e, c, acc);
+    const float sc = e.alpha_dev ? e.alpha * *e.alpha_dev : e.alpha;   // scales dW and the gain partials
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
@@ -708,8 +717,9 @@ struct EpiWgradGain {
           const f32x4_t a = frag(acc, i, j, q);
           const f32x4_t wv = w[i & 1].get(j, q);
           if (m < c.M && c.col(j, q) < c.N) part[i] += wv[0] * a[0] + wv[1] * a[1] + wv[2] * a[2] + wv[3] * a[3];
-          set_frag(acc, i, j, q, g * a);
+          set_frag(acc, i, j, q, (g * a) * sc);
         }
+      part[i] *= sc;
       if (i + 2 < Cfg::TM) w[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -731,12 +741,27 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mm;
 }
 
-template <class Cfg>
+// NORM: the logits pass through a final RMSNorm folded into the weight
+// (the third GEMM-residual-RMSNorm-GEMM occurrence of the CODA paper,
+// §3.2.1): z = r acc with r finished from sum-of-squares partials in the
+// prologue (written to rowvec_out2 when given).
+template <class Cfg, bool NORM = false>
 struct EpiCrossEntropy {
-  struct Pro {};
-  __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
-  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+  struct Pro { RowPartials<Cfg> rp; };
+  __device__ static void issue(const EpiArgs& e, const Ctx<Cfg>& c, Pro& p) {
+    if constexpr (NORM) p.rp.issue(e.row_partials, e.n_row_partials, c);
+  }
+  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
     apply_fp8_scales<Cfg>(e, c, acc);
+    if constexpr (NORM) {
+      finish_inv_rms<Cfg>(e, c, p.rp, e.rowvec_out2);
+#pragma unroll
+      for (int i = 0; i < Cfg::TM; ++i) {
+        const float r = c.rowv()[c.lrow(i)];
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j) acc.c[i][j] = acc.c[i][j] * r;
+      }
+    }
     float* redm = c.red();
     float* reds = c.red2();
 #pragma unroll
@@ -792,18 +817,25 @@ struct EpiCrossEntropy {
 
 // --- cross-entropy backward recompute: G = bf16(exp(z - lse) - [n == y]) on
 // rows whose label is not ignored, 0 on ignored rows.
-template <class Cfg>
+// NORM: z = r acc with the given r (rowvec2); the stored tile is
+// G~ = bf16(r (p - onehot)) and T[tn][m] = sum over the tile of G~ z is
+// written as row partials (the RMSNorm-backward statistic).
+template <class Cfg, bool NORM = false>
 struct EpiCrossEntropyGrad {
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
     apply_fp8_scales<Cfg>(e, c, acc);
+    float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      part[i] = 0.0f;
       const int m = c.row(i);
       const int y = e.labels[c.rowc(i)];
       const bool valid = m < c.M && y != -100;
       const float lse = e.rowvec[c.rowc(i)];
+      const float r = NORM ? e.rowvec2[c.rowc(i)] : 1.0f;
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
@@ -812,14 +844,23 @@ struct EpiCrossEntropyGrad {
           f32x4_t gv;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            float p = __expf(acc.c[i][j][4 * q + t] - lse) - (n + t == y ? 1.0f : 0.0f);
-            gv[t] = valid ? p : 0.0f;
+            const float z = NORM ? r * acc.c[i][j][4 * q + t] : acc.c[i][j][4 * q + t];
+            const float p = __expf(z - lse) - (n + t == y ? 1.0f : 0.0f);
+            gv[t] = valid ? (NORM ? round_bf(r * p) : p) : 0.0f;
+            if constexpr (NORM)
+              if (n + t < c.N) part[i] += gv[t] * z;
           }
-          set_frag(acc, i, j, q, gv);
+          StageBF<Cfg::BM, Cfg::BN>::put4(c.stage(), c.lrow(i), c.lcol(j, q), gv);
         }
     }
-    put_tile<Cfg, Cfg::BN>(c, acc);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NORM) {   // the reduction first: partials kept live across the store cost spills
+      float* tot = c.rowv();
+      row_sum_tile<Cfg>(c, part, tot);   // its barriers also order the staging writes
+      write_row_partial<Cfg>(c, tot, e.partial_out);
+    } else {
+      __syncthreads();
+    }
     stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), c.tid,
         MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }

@@ -24,6 +24,8 @@ enum class Prog : int {
   CrossEntropyG,  // G = exp(z - lse) - onehot
   StoreAlphaDev,  // bf16 store of (*alpha_dev) * acc
   F32AlphaDev,    // fp32 beta-accumulate of (*alpha_dev) * acc
+  CrossEntropyNorm,   // z = r acc (r from sum-of-squares partials), then as CrossEntropy
+  CrossEntropyGNorm,  // z = r acc (given r), G~ = r (exp(z - lse) - onehot), T partials
 };
 
 constexpr int kBM = 256, kBN = 256;

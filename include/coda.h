@@ -293,6 +293,46 @@ coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* 
                                           int64_t chunk_rows, int32_t precision, void* ws, size_t ws_bytes,
                                           void* stream);
 
+/* ===================================================================== final RMSNorm -> LM head -> CE */
+
+/* The third GEMM-residual-RMSNorm-GEMM occurrence of the CODA paper (§3.2.1,
+ * final down-projection -> residual -> final RMSNorm -> LM head), fused with
+ * the cross-entropy above:
+ *   r = (sum_t P[t, m] / D + eps)^(-1/2),  z = r (y W~),  W~ = bf16(g W)
+ *   (coda_fold_gain), then lse, per-row loss and the mean loss as in
+ *   coda_linear_cross_entropy_fwd.
+ * y: bf16 [M, D] (the final residual stream); sumsq_partials: fp32 [n, M]
+ * (n <= 32) sum-of-squares partials of y (the last down-projection's
+ * coda_linear_rmsnorm_residual_fwd output) or NULL (computed here;
+ * workspace).  W: the folded weight [D, V].  r_out: optional fp32 1 x M
+ * (needed by the backward).  Other outputs as in the plain cross-entropy.
+ * bf16 only (fp8 returns CODA_ERR_UNSUPPORTED). */
+coda_status coda_linear_rmsnorm_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t have_partials,
+                                                            int32_t precision, size_t* bytes);
+coda_status coda_linear_rmsnorm_cross_entropy_fwd(const coda_mat* y, const coda_mat* sumsq_partials,
+                                                  const coda_weight* W, float eps, const coda_mat* labels,
+                                                  int32_t ignore_index, const coda_mat* loss, const coda_mat* lse,
+                                                  const coda_mat* per_row, const coda_mat* n_valid,
+                                                  const coda_mat* n_bad, const coda_mat* r_out, int32_t precision,
+                                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Backward, recomputing z per chunk of `chunk_rows` rows (0 = all rows):
+ *   G~ = bf16(r (exp(z - lse) - onehot)) (0 on ignored rows), s = dloss / n_valid,
+ *   T = s sum_v G~ z,  dy = bf16(s G~ W~^T - (r T / D) y + dres),
+ *   dW = beta dW + s g (y^T G~) (fp32 [D, V]),  dg = beta dg + s sum_v W (y^T G~) (fp32 1 x D).
+ * r: the forward's r_out; W_unfolded: W without the gain; g: fp32 1 x D;
+ * dres: optional bf16 [M, D] gradient arriving along the residual stream.
+ * With M = 0, dW and dg are left unchanged.  ignore_index must be -100. */
+coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
+                                                            int32_t precision, size_t* bytes);
+coda_status coda_linear_rmsnorm_cross_entropy_bwd(const coda_mat* y, const coda_mat* r, const coda_weight* W,
+                                                  const coda_mat* W_unfolded, const coda_mat* g,
+                                                  const coda_mat* labels, int32_t ignore_index, const coda_mat* lse,
+                                                  const coda_mat* n_valid, float dloss, const coda_mat* dres,
+                                                  const coda_mat* dy, const coda_mat* dW, const coda_mat* dg,
+                                                  float beta, int64_t chunk_rows, int32_t precision, void* ws,
+                                                  size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,25 @@ def test_cross_entropy_full_size():
     assert_bf16("dh", got["dh"], Br["dh"])
     assert_grad("dW", got["dW"], Br["dW"])
     assert np.all(got["dh"][labels == -100] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_rmsnorm_cross_entropy_full_size():
+    """The cross-entropy workload with the final RMSNorm folded in: y
+    [8192, 2048] (the h of the cross-entropy inputs), gain 1 + 0.1 N(0, 1),
+    W_vocab [2048, 128256], 410 ignored rows, chunks of 1024 rows."""
+    from tests.test_gpu_parity import run_rmsnorm_ce
+    shape = ci.CFG4
+    P = ci.ce_inputs(shape, ci.SEEDS["cfg4"])
+    g = (1 + 0.1 * np.random.default_rng(77).standard_normal(shape.D)).astype(np.float32)
+    got = run_rmsnorm_ce(P["h"], g, P["W"], P["labels"], None, 1024, None)
+    torch.cuda.empty_cache()
+    F = ob.norm_ce_forward_contract(P["h"], g, P["W"], P["labels"], 1e-6)
+    assert got["n_valid"] == F["n_valid"] == shape.M - 410 and got["n_bad"] == 0
+    assert abs(got["loss"] - F["loss"]) <= 1e-4 * abs(F["loss"])
+    assert_grad("lse", got["lse"], F["lse"])
+    assert_grad("r", got["r"], F["r"])
+    B = ob.norm_ce_backward_contract(P["h"], g, P["W"], P["labels"], F["lse"], F["r"], F["n_valid"], 1e-6)
+    assert_bf16("dy", got["dy"], B["dy"])
+    assert_grad("dW", got["dW"], B["dW"])
+    assert_grad("dg", got["dg"], B["dg"])

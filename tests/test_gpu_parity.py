@@ -212,6 +212,66 @@ def test_cross_entropy(M, D, V, chunk):
     assert np.all(to_np(dh)[ignored] == 0)
 
 
+def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_dg=None, beta=0.0):
+    """GPU final RMSNorm -> LM head -> CE forward and backward; returns host arrays."""
+    M, D = y.shape
+    V = W.shape[1]
+    Wd, gd = bf(W), f32(g)
+    Wt = coda.fold_gain(Wd, gd, torch.empty_like(Wd))
+    yd, lab = bf(y), to_dev(labels)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    per_row = torch.empty(M, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    nbad = torch.empty(1, dtype=torch.int32, device=DEV)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    P = f32(partials) if partials is not None else None
+    coda.linear_rmsnorm_cross_entropy_fwd(yd, Wt, 1e-6, lab, loss, lse, nv, sumsq_partials=P, per_row=per_row,
+                                          n_bad=nbad, r_out=r)
+    dy = torch.empty((M, D), dtype=BF, device=DEV)
+    dW = f32(prior_dW) if prior_dW is not None else torch.empty((D, V), dtype=torch.float32, device=DEV)
+    dg = f32(prior_dg) if prior_dg is not None else torch.empty(D, dtype=torch.float32, device=DEV)
+    coda.linear_rmsnorm_cross_entropy_bwd(yd, r, Wt, Wd, gd, lab, lse, nv, 1.0, dy, dW, dg,
+                                          dres=bf(dres) if dres is not None else None, beta=beta, chunk_rows=chunk)
+    torch.cuda.synchronize()
+    return dict(loss=loss.item(), lse=to_np(lse), per_row=to_np(per_row), n_valid=int(nv.item()),
+                n_bad=int(nbad.item()), r=to_np(r), dy=to_np(dy), dW=to_np(dW), dg=to_np(dg))
+
+
+@pytest.mark.parametrize("M,D,V,chunk,use_partials", [(300, 256, 1000, 0, False), (260, 128, 784, 100, True)])
+def test_rmsnorm_cross_entropy(M, D, V, chunk, use_partials):
+    """Final RMSNorm folded into the LM head: z = r (y W~).  The ragged case
+    recomputes the logits in 3 chunks, takes 3 given sum-of-squares partials,
+    adds a residual-stream gradient and accumulates onto fp32 priors."""
+    V = V - V % 8
+    rng = np.random.default_rng(M)
+    y = rand_bf16(rng, M, D)
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    W = rand_bf16(rng, D, V, std=D ** -0.5)
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[[0, 1, 2, 5]] = [0, V - 1, -100, -100]
+    parts = None
+    if use_partials:
+        y2 = y.astype(np.float64) ** 2
+        parts = np.stack([y2[:, :40].sum(1), y2[:, 40:90].sum(1), y2[:, 90:].sum(1)]).astype(np.float32)
+    dres = rand_bf16(rng, M, D, std=0.1) if use_partials else None
+    pW = ci.fp32_prior((D, V), 3) if use_partials else None
+    pg = ci.fp32_prior((D,), 4) if use_partials else None
+    beta = 1.0 if use_partials else 0.0
+    got = run_rmsnorm_ce(y, g, W, labels, dres, chunk, parts, pW, pg, beta)
+    F = ob.norm_ce_forward_contract(y, g, W, labels, 1e-6)
+    assert got["n_valid"] == F["n_valid"] == M - 2 and got["n_bad"] == 0
+    assert abs(got["loss"] - F["loss"]) <= 1e-4 * abs(F["loss"])
+    assert_grad("lse", got["lse"], F["lse"])
+    assert_grad("per-row loss", got["per_row"], F["per_row"])
+    assert_grad("r", got["r"], F["r"])
+    B = ob.norm_ce_backward_contract(y, g, W, labels, F["lse"], F["r"], F["n_valid"], 1e-6, dres=dres,
+                                     priors=dict(dW=pW, dg=pg) if use_partials else None, beta=beta)
+    assert_bf16("dy", got["dy"], B["dy"])
+    assert_grad("dW", got["dW"], B["dW"])
+    assert_grad("dg", got["dg"], B["dg"])
+
+
 def test_cross_entropy_bad_label_and_empty():
     M, D, V = 64, 128, 512
     rng = np.random.default_rng(2)
