@@ -298,3 +298,43 @@ def test_norm_ce_reduces_to_plain_ce():
     dh = dz @ W.T
     radial = np.sum(dh * y, axis=1, keepdims=True) / D * y
     np.testing.assert_allclose(C["dy"], dh - radial, rtol=1e-10, atol=1e-14)
+
+
+# ------------------------------------------------------------------ RMSNorm -> Linear -> sigmoid
+def _sigmoid_tiny(seed=31, M=10, D=16, N=24):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((M, D)), 1 + 0.1 * rng.standard_normal(D),
+            rng.standard_normal((D, N)) / math.sqrt(D), rng.standard_normal((N, D)) / math.sqrt(N),
+            0.1 * rng.standard_normal((M, D)), 0.1 * rng.standard_normal((M, D)))
+
+
+def test_sigmoid_layer_canonical_matches_torch_autograd():
+    x, g, W, Wn, dY, dres = _sigmoid_tiny()
+    C = ob.sigmoid_layer_canonical(x, g, W, Wn, dY, 1e-6, dres=dres)
+    X, G_, W_ = (torch.tensor(a, requires_grad=True) for a in (x, g, W))
+    r = torch.rsqrt((X * X).mean(dim=1, keepdim=True) + 1e-6)
+    y = torch.sigmoid((X * r * G_) @ W_) @ torch.tensor(Wn)
+    ((y * torch.tensor(dY)).sum() + (X * torch.tensor(dres)).sum()).backward()
+    np.testing.assert_allclose(C["dx"], X.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dW"], W_.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dg"], G_.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_sigmoid_reparameterised_equals_canonical():
+    x, g, W, Wn, dY, dres = _sigmoid_tiny(32)
+    C = ob.sigmoid_layer_canonical(x, g, W, Wn, dY, 1e-6, dres=dres)
+    F = ob.sigmoid_forward_contract(x, g, W, 1e-6, rnd=_ident, dt=np.float64)
+    np.testing.assert_allclose(F["a"], C["a"], rtol=1e-13)
+    B = ob.sigmoid_backward_contract(x, g, W, Wn, dY, F, 1e-6, dres=dres, rnd=_ident, dt=np.float64)
+    for k in ("dx", "dW", "dg"):
+        np.testing.assert_allclose(B[k], C[k], rtol=1e-10, atol=1e-14, err_msg=k)
+
+
+def test_sigmoid_special_values():
+    """sigmoid(0) = 1/2 with slope 1/4; symmetric: s(-t) = 1 - s(t)."""
+    t = np.linspace(-30, 30, 61)
+    s = ops.sigmoid(t)
+    assert s[30] == 0.5
+    np.testing.assert_allclose(s[::-1], 1 - s, atol=1e-15)
+    h = 1e-6
+    assert abs((ops.sigmoid(np.array(h)) - ops.sigmoid(np.array(-h))) / (2 * h) - 0.25) < 1e-9
