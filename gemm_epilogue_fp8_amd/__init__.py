@@ -309,3 +309,28 @@ def linear_rmsnorm_cross_entropy_bwd(y, r, W, W_unfolded, g, labels, lse, n_vali
                                                    ignore_index, _p(lse), _p(n_valid), dloss, _p(dres), _p(dy),
                                                    _p(dW), _p(dg), beta, chunk_rows, precision, ws, n, _stream()))
     return dy, dW, dg
+
+
+# ---------------------------------------------------------------- RMSNorm -> Linear -> sigmoid
+def linear_sigmoid_fwd(x, W, eps, out, sumsq_partials=None, save_h=None, r_out=None, precision: int = PREC_BF16):
+    L = lib()
+    wc = W if isinstance(W, Weight) else Weight(W)
+    M, K = x.shape
+    ws, n = _ws_call(L.coda_linear_sigmoid_fwd_workspace, (M, K, int(sumsq_partials is not None), precision),
+                     x.device)
+    _check(L.coda_linear_sigmoid_fwd(_p(x), _p(sumsq_partials), C.byref(wc.c()), eps, _p(out), _p(save_h),
+                                     _p(r_out), precision, ws, n, _stream()))
+    return out
+
+
+def linear_sigmoid_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta=0.0, dh_out=None,
+                       precision: int = PREC_BF16):
+    L = lib()
+    wn = Wn if isinstance(Wn, Weight) else Weight(Wn)
+    wc = W if isinstance(W, Weight) else Weight(W)
+    M, D = dY.shape
+    ws, n = _ws_call(L.coda_linear_sigmoid_bwd_workspace, (M, D, wn.w.shape[0], precision), dY.device)
+    _check(L.coda_linear_sigmoid_bwd(_p(dY), C.byref(wn.c()), _p(saved_h), _p(r), _p(u), C.byref(wc.c()),
+                                     _p(W_unfolded), _p(g), _p(dres), _p(du), _p(dW), _p(dg), beta, _p(dh_out),
+                                     precision, ws, n, _stream()))
+    return du, dW, dg

@@ -329,9 +329,14 @@ size_t fwd_fp8_bytes(int64_t M, int64_t K) {
 }
 }  // namespace
 
+// The pre-norm activation layers: SwiGLU over packed gate/up columns, or an
+// elementwise sigmoid.
+enum class Act { SwiGLU, Sigmoid };
+
 static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, float eps,
                                    const coda_mat* out, const coda_mat* save, const coda_mat* r_out, int precision,
-                                   void* ws, size_t ws_bytes, void* stream, bool size_only, size_t* bytes) {
+                                   void* ws, size_t ws_bytes, void* stream, bool size_only, size_t* bytes,
+                                   Act act = Act::SwiGLU) {
   const int64_t M = x->rows, K = x->cols, N = Wgu->w.cols, F = N / 2;
   Carver cv(size_only ? nullptr : ws);
   float* sumsq = present(P) ? nullptr : cv.take<float>(M);
@@ -363,6 +368,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
     layout = LAYOUT_NN;
   }
   (void)F;
+  if (act == Act::Sigmoid) return launched(launch_gemm(Prog::Sigmoid, layout, fp8, g, e, s), "linear_sigmoid_fwd");
   return launched(launch_gemm(Prog::SwiGLU, layout, fp8, g, e, s), "linear_swiglu_fwd");
 }
 
@@ -606,8 +612,11 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
                                    const coda_mat* u, const coda_weight* Wgu, const coda_mat* Wunf, const coda_mat* gvec,
                                    const coda_mat* dres, const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg,
                                    float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
-                                   void* stream, int64_t M, int64_t D, int64_t F, bool size_only, size_t* bytes) {
-  const int64_t N2 = 2 * F;
+                                   void* stream, int64_t M, int64_t D, int64_t F, bool size_only, size_t* bytes,
+                                   Act act = Act::SwiGLU) {
+  // F is the width of the activation's output; the pre-activations are 2F
+  // wide for SwiGLU (packed gate/up) and F wide for the sigmoid
+  const int64_t N2 = act == Act::SwiGLU ? 2 * F : F;
   const bool fp8 = precision == CODA_PREC_FP8;
   Carver cv(size_only ? nullptr : ws);
   const int nT2 = (int)coda_partials_cols(F);
@@ -641,7 +650,8 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     GemmArgs g;
     if (fp8) TRY(quant_act(dYrow, dY->ptr, dY->ld, M, D, 1, s));
     dgrad_args(fp8, &dYrow, dY->ptr, dY->ld, Wd, M, F, D, &g, &e);
-    TRY(launched(launch_gemm(Prog::DSwiGLU, LAYOUT_NT, fp8, g, e, s), "swiglu_bwd: dSwiGLU"));
+    TRY(launched(launch_gemm(act == Act::SwiGLU ? Prog::DSwiGLU : Prog::DSigmoid, LAYOUT_NT, fp8, g, e, s),
+                 "swiglu_bwd: activation backward"));
   }
   // collapse the T partials (F / 256 of them) to one per row
   hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, T2, nT2, (int)M, 0,
@@ -1263,4 +1273,72 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
     TRY(sum_partials_launch(dgp, nT, (int)D, b, static_cast<float*>(dg->ptr), s));
   }
   return CODA_OK;
+}
+
+// ======================================================================== RMSNorm -> Linear -> sigmoid
+static coda_status sigmoid_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* W, const coda_mat* out,
+                                     const coda_mat* save, const coda_mat* r_out, int precision) {
+  TRY(check_precision(precision));
+  TRY(check_mat(x, "x", CODA_BF16, -1, -1));
+  const int64_t M = x->rows, K = x->cols;
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  const int64_t N = W->w.cols;
+  TRY(check_weight(W, "W", K, N, precision));
+  TRY(check_mat(P, "sumsq_partials", CODA_F32, -1, M, true));
+  if (present(P) && (P->rows < 1 || P->rows > 32 || (P->rows > 1 && P->ld != M)))
+    return fail(CODA_ERR_SHAPE, "sumsq_partials: 1..32 rows of M with ld == M");
+  TRY(check_mat(out, "out", CODA_BF16, M, N));
+  TRY(check_mat(save, "save_h", CODA_BF16, M, N, true));
+  TRY(check_vec(r_out, "r_out", CODA_F32, M, true));
+  return CODA_OK;
+}
+
+extern "C" coda_status coda_linear_sigmoid_fwd_workspace(int64_t M, int64_t K, int32_t have_partials,
+                                                         int32_t precision, size_t* bytes) {
+  return coda_linear_swiglu_fwd_workspace(M, K, have_partials, precision, bytes);
+}
+
+extern "C" coda_status coda_linear_sigmoid_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
+                                               float eps, const coda_mat* out, const coda_mat* save_h,
+                                               const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  TRY(sigmoid_fwd_check(x, sumsq_partials, W, out, save_h, r_out, precision));
+  if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
+  return swiglu_fwd_impl(x, sumsq_partials, W, eps, out, save_h, r_out, precision, ws, ws_bytes, stream, false,
+                         nullptr, Act::Sigmoid);
+}
+
+extern "C" coda_status coda_linear_sigmoid_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision,
+                                                         size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
+  return swiglu_bwd_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, 0.0f, nullptr, precision, nullptr, 0, nullptr, M, D, N, true, bytes,
+                         Act::Sigmoid);
+}
+
+extern "C" coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
+                                               const coda_mat* r, const coda_mat* u, const coda_weight* W,
+                                               const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
+                                               const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                                               const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  TRY(check_precision(precision));
+  TRY(check_mat(dY, "dY", CODA_BF16, -1, -1));
+  const int64_t M = dY->rows, D = dY->cols;
+  if (!Wn || !W) return fail(CODA_ERR_NULL, "weights: NULL");
+  const int64_t N = Wn->w.rows;
+  TRY(check_weight(Wn, "Wn", N, D, precision));
+  TRY(check_weight(W, "W", D, N, precision));
+  TRY(check_mat(saved_h, "saved_h", CODA_BF16, M, N));
+  TRY(check_vec(r, "r", CODA_F32, M));
+  TRY(check_mat(u, "u", CODA_BF16, M, D));
+  TRY(check_mat(W_unfolded, "W_unfolded", CODA_BF16, D, N));
+  TRY(check_vec(g, "g", CODA_F32, D));
+  TRY(check_mat(dres, "dres", CODA_BF16, M, D));
+  TRY(check_mat(du, "du", CODA_BF16, M, D));
+  TRY(check_mat(dW, "dW", CODA_F32, D, N));
+  TRY(check_vec(dg, "dg", CODA_F32, D));
+  TRY(check_mat(dh_out, "dh_out", CODA_BF16, M, N, true));
+  return swiglu_bwd_impl(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision, ws,
+                         ws_bytes, stream, M, D, N, false, nullptr, Act::Sigmoid);
 }

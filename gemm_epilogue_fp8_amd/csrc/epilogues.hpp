@@ -469,6 +469,46 @@ struct EpiSwiGLU {
   }
 };
 
+// --- row scale r from partials (or a given vector), then the sigmoid map:
+// h = r acc, out = sigmoid(h), optional save of h (for the backward).
+template <class Cfg>
+struct EpiSigmoid {
+  struct Pro { RowPartials<Cfg> rp; };
+  __device__ static void issue(const EpiArgs& e, const Ctx<Cfg>& c, Pro& p) {
+    p.rp.issue(e.row_partials, e.n_row_partials, c);
+  }
+  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro& p) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
+    finish_inv_rms<Cfg>(e, c, p.rp, e.rowvec_out);
+    apply_fp8_scales<Cfg>(e, c, acc);
+    char* s = c.stage();
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const float r = c.rowv()[c.lrow(i)];
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t h = frag(acc, i, j, q) * r;
+          f32x4_t a;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[t] = sigmoidf_(h[t]);
+          S::put4(s, c.lrow(i), c.lcol(j, q), a);
+          set_frag(acc, i, j, q, h);
+        }
+    }
+    __syncthreads();
+    stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
+    if (e.save) {
+      __syncthreads();
+      put_tile<Cfg, Cfg::BN>(c, acc);
+      __syncthreads();
+      stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid,
+          MatBF{static_cast<uint16_t*>(e.save), e.ld_save, c.m0, c.n0, c.M, c.N});
+    }
+  }
+};
+
 // --- QKV: row scale r1, per-head RMSNorm of q and k (128 columns, one gain
 // vector per q / k shared by the heads), RoPE on adjacent column pairs, split
 // store of q, k, v, and optional save of the pre-norm q, k.
@@ -636,6 +676,53 @@ struct EpiDSwiGLU {
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
     write_row_partial<Cfg>(c, tot, e.partial_out);
+  }
+};
+
+// --- sigmoid backward in the epilogue of da = dY Wn^T: with the saved h (read
+// into registers one 32-row block ahead) and s = sigmoid(h),
+// dh~ = bf16(r da s (1 - s)) is stored and T[tn][m] = sum over the tile of
+// dh~ h is written as row partials.
+template <class Cfg>
+struct EpiDSigmoid {
+  struct Pro {};
+  __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
+  __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
+    using S = StageBF<Cfg::BM, Cfg::BN>;
+    apply_fp8_scales<Cfg>(e, c, acc);
+    RowBlock<Cfg> hb[2];
+    hb[0].load(e.aux0, e.ld_aux0, c, 0);
+    if (Cfg::TM > 1) hb[1].load(e.aux0, e.ld_aux0, c, 1);
+    char* s = c.stage();
+    float part[Cfg::TM];
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      part[i] = 0.0f;
+      const int m = c.row(i);
+      const float r = e.rowvec[c.rowc(i)];
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t h = hb[i & 1].get(j, q);
+          const f32x4_t da = frag(acc, i, j, q);
+          f32x4_t d;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float sg = sigmoidf_(h[t]);
+            d[t] = round_bf(r * (da[t] * sg * (1.0f - sg)));
+          }
+          if (m < c.M && c.col(j, q) < c.N) part[i] += d[0] * h[0] + d[1] * h[1] + d[2] * h[2] + d[3] * h[3];
+          S::put4(s, c.lrow(i), c.lcol(j, q), d);
+        }
+      if (i + 2 < Cfg::TM) hb[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float* tot = c.rowv();
+    row_sum_tile<Cfg>(c, part, tot);   // its barriers also order the staging writes
+    write_row_partial<Cfg>(c, tot, e.partial_out);
+    stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }
 };
 

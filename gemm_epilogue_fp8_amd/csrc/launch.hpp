@@ -26,6 +26,8 @@ enum class Prog : int {
   F32AlphaDev,    // fp32 beta-accumulate of (*alpha_dev) * acc
   CrossEntropyNorm,   // z = r acc (r from sum-of-squares partials), then as CrossEntropy
   CrossEntropyGNorm,  // z = r acc (given r), G~ = r (exp(z - lse) - onehot), T partials
+  Sigmoid,        // row scale (finished from partials or given), sigmoid, store, save h
+  DSigmoid,       // sigmoid backward with the saved h, r scale, store dh~, T partials
 };
 
 constexpr int kBM = 256, kBN = 256;

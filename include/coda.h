@@ -293,6 +293,35 @@ coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* 
                                           int64_t chunk_rows, int32_t precision, void* ws, size_t ws_bytes,
                                           void* stream);
 
+/* ===================================================================== RMSNorm -> Linear -> sigmoid */
+
+/* The elementwise-map primitive of the CODA paper (§3.1 item 1) with the
+ * delayed RMSNorm of §3.2.1, as in coda_linear_swiglu but with a sigmoid on
+ * every column (the linear_sigmoid of the papers.ananclaw.com CODA guide):
+ *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r (x W~),  out = sigmoid(h)
+ * x: bf16 [M, K]; W: the gain-folded weight [K, N]; out: bf16 [M, N];
+ * save_h (bf16 [M, N]) and r_out (fp32 1 x M) are optional saves for the
+ * backward.  Partials and workspace as in coda_linear_swiglu_fwd. */
+coda_status coda_linear_sigmoid_fwd_workspace(int64_t M, int64_t K, int32_t have_partials, int32_t precision,
+                                              size_t* bytes);
+coda_status coda_linear_sigmoid_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
+                                    float eps, const coda_mat* out, const coda_mat* save_h, const coda_mat* r_out,
+                                    int32_t precision, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward fused behind the consumer GEMM da = dY Wn^T (Wn [N, D], never
+ * materialising da): with s = sigmoid(saved h),
+ *   dh~ = bf16(r da s (1 - s)),  T = sum_j dh~ h,  c = r T / D,
+ *   du = dh~ W~^T - c u + dres (bf16 [M, D]),
+ *   dW = beta dW + g (u^T dh~) (fp32 [D, N]),  dg = beta dg + sum_n W (u^T dh~).
+ * Arguments as in coda_linear_swiglu_bwd with N in place of 2F. */
+coda_status coda_linear_sigmoid_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision, size_t* bytes);
+coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
+                                    const coda_mat* r, const coda_mat* u, const coda_weight* W,
+                                    const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
+                                    const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                                    const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* ===================================================================== final RMSNorm -> LM head -> CE */
 
 /* The third GEMM-residual-RMSNorm-GEMM occurrence of the CODA paper (§3.2.1,

@@ -123,6 +123,76 @@ def test_swiglu_ragged_with_partials_and_saves():
     _swiglu_case(ci.SwiGLUShape(M=333, K=264, F=352), 3, use_partials=True, saves=True)
 
 
+# ------------------------------------------------------------------ RMSNorm -> Linear -> sigmoid
+def _run_sigmoid(M, D, N, seed, precision, beta=0.0):
+    """Forward then the backward behind the consumer GEMM dY Wn^T; returns the
+    host inputs and every device result."""
+    rng = np.random.default_rng(seed)
+    P = dict(x=rand_bf16(rng, M, D), W=rand_bf16(rng, D, N, std=D ** -0.5),
+             Wn=rand_bf16(rng, N, D, std=N ** -0.5), dY=rand_bf16(rng, M, D, std=0.1),
+             dres=rand_bf16(rng, M, D, std=0.1),
+             g=(1 + 0.1 * rng.standard_normal(D)).astype(np.float32),
+             dW0=rng.standard_normal((D, N)).astype(np.float32), dg0=rng.standard_normal(D).astype(np.float32))
+    fp8 = precision == coda.PREC_FP8
+    Wu, g = bf(P["W"]), f32(P["g"])
+    Wt = coda.Weight(coda.fold_gain(Wu, g, torch.empty_like(Wu)))
+    Wn = coda.Weight(bf(P["Wn"]))
+    if fp8:
+        Wt.prepare_fp8()
+        Wn.prepare_fp8()
+    x = bf(P["x"])
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    h = torch.empty((M, N), dtype=BF, device=DEV)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    coda.linear_sigmoid_fwd(x, Wt, 1e-6, out, save_h=h, r_out=r, precision=precision)
+    du = torch.empty((M, D), dtype=BF, device=DEV)
+    dW, dg = f32(P["dW0"]), f32(P["dg0"])
+    dht = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.linear_sigmoid_bwd(bf(P["dY"]), Wn, h, r, x, Wt, Wu, g, bf(P["dres"]), du, dW, dg, beta=beta,
+                            dh_out=dht, precision=precision)
+    torch.cuda.synchronize()
+    got = dict(a=to_np(out), h=to_np(h), r=to_np(r), du=to_np(du), dW=to_np(dW), dg=to_np(dg), dht=to_np(dht))
+    return P, got
+
+
+@pytest.mark.parametrize("M,D,N,beta", [(333, 264, 352, 0.0), (520, 384, 600, 1.0)])
+def test_sigmoid_forward_backward(M, D, N, beta):
+    P, got = _run_sigmoid(M, D, N, 11, coda.PREC_BF16, beta)
+    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6)
+    for k in ("a", "h"):
+        assert_bf16(k, got[k], F[k])
+    assert_grad("r", got["r"], F["r"])
+    priors = dict(dW=P["dW0"], dg=P["dg0"])
+    B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], F, 1e-6, dres=P["dres"],
+                                     priors=priors, beta=beta)
+    assert_bf16("dh~", got["dht"], B["dht"])
+    assert_bf16("dx", got["du"], B["dx"])
+    assert_grad("dW", got["dW"], B["dW"])
+    assert_grad("dg", got["dg"], B["dg"])
+
+
+def test_sigmoid_fp8():
+    """E4M3 operands.  The backward reference starts from the device's saved
+    h and r, so dh~ differs only where the two sides round dY Wn^T sums taken
+    in different orders to bf16; rows where that moved dh~'s amax are
+    flagged for dx."""
+    from tests.helpers import amax_flip_rows, assert_fp8_rows
+    M, D, N = 304, 256, 352
+    P, got = _run_sigmoid(M, D, N, 12, coda.PREC_FP8)
+    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6, fp8=True)
+    none = np.zeros(0, np.int64)
+    assert_fp8_rows("h", got["h"], F["h"], none)
+    assert_fp8_rows("a", got["a"], F["a"], none)
+    Fg = dict(F, h=got["h"], r=got["r"])
+    B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], Fg, 1e-6, dres=P["dres"],
+                                     fp8=True)
+    assert_fp8_rows("dh~", got["dht"], B["dht"], none)
+    assert_fp8_rows("dx", got["du"], B["dx"], amax_flip_rows([(got["dht"], B["dht"])]))
+    for k in ("dW", "dg"):
+        assert np.all(np.isfinite(got[k])), k
+        assert rel_norm(got[k], B[k]) <= 2e-2, (k, rel_norm(got[k], B[k]))
+
+
 # ------------------------------------------------------------------ block forward / backward
 SMALL = ci.BlockShape(M=300, D=256, F=352, seq_len=128)
 MEDIUM = ci.BlockShape(M=520, D=384, F=480, seq_len=200)
