@@ -191,10 +191,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
         uint32_t o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float a0 = round_bf(r * (rho * t[2 * q] - k3 * u[2 * q]));
-          const float a1 = round_bf(r * (rho * t[2 * q + 1] - k3 * u[2 * q + 1]));
-          T += a0 * u[2 * q] + a1 * u[2 * q + 1];
-          o[q] = pack_bf2(a0, a1);
+          o[q] = pack_bf2(r * (rho * t[2 * q] - k3 * u[2 * q]), r * (rho * t[2 * q + 1] - k3 * u[2 * q + 1]));
+          T += bf_lo(o[q]) * u[2 * q] + bf_hi(o[q]) * u[2 * q + 1];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) dgacc[reg][e] += rho * u[e] * n[e];
@@ -208,9 +206,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float a0 = round_bf(r * bf_lo(ga[q])), a1 = round_bf(r * bf_hi(ga[q]));
-        T += a0 * bf_lo(va[q]) + a1 * bf_hi(va[q]);
-        o[q] = pack_bf2(a0, a1);
+        o[q] = pack_bf2(r * bf_lo(ga[q]), r * bf_hi(ga[q]));
+        T += bf_lo(o[q]) * bf_lo(va[q]) + bf_hi(o[q]) * bf_hi(va[q]);
       }
       *reinterpret_cast<uint4*>(dh + (int64_t)m * ld_dh + 2 * D + col) = uint4{o[0], o[1], o[2], o[3]};
     }

@@ -7,6 +7,8 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -35,19 +37,19 @@ __device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> a packed bf16 pair (lo in bits 0-15), round to nearest even;
+// NaN stays NaN.  One v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf2(f, 0.0f) & 0xFFFFu; }
 // value of f after rounding to bf16
-__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ float round_bf(float f) { return bf_lo(pack_bf2(f, 0.0f)); }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
-__device__ __forceinline__ float sigmoidf_(float t) { return 1.0f / (1.0f + __expf(-t)); }
+// sigmoid through the hardware reciprocal (v_rcp_f32, 1 ulp) instead of a
+// correctly rounded fp32 division, which costs about ten instructions
+__device__ __forceinline__ float sigmoidf_(float t) { return __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

@@ -88,9 +88,10 @@ struct Ctx {
   __device__ __forceinline__ float* red2() const { return scratch() + (2 + Cfg::WAVES_N) * Cfg::BM; }
 };
 
-__device__ __forceinline__ f32x4_t round_bf4(f32x4_t v) {
-  return f32x4_t{round_bf(v[0]), round_bf(v[1]), round_bf(v[2]), round_bf(v[3])};
-}
+// 4 floats -> 4 packed bf16 (two conversions), and back
+__device__ __forceinline__ uint2 pack_bf4(f32x4_t v) { return uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])}; }
+__device__ __forceinline__ f32x4_t unpack_bf4(uint2 w) { return f32x4_t{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)}; }
+__device__ __forceinline__ f32x4_t round_bf4(f32x4_t v) { return unpack_bf4(pack_bf4(v)); }
 
 template <class Cfg>
 __device__ __forceinline__ f32x4_t frag(const Acc<Cfg>& acc, int i, int j, int q) {
@@ -114,8 +115,9 @@ struct StageBF {
   }
   // 4 consecutive bf16 at (r, col), col % 4 == 0
   __device__ __forceinline__ static uint32_t off4(int r, int col) { return off(r, col >> 3) + ((col & 4) << 1); }
-  __device__ __forceinline__ static void put4(char* s, int r, int col, f32x4_t v) {
-    *reinterpret_cast<uint2*>(s + off4(r, col)) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  __device__ __forceinline__ static void put4(char* s, int r, int col, f32x4_t v) { put4p(s, r, col, pack_bf4(v)); }
+  __device__ __forceinline__ static void put4p(char* s, int r, int col, uint2 w) {
+    *reinterpret_cast<uint2*>(s + off4(r, col)) = w;
   }
   __device__ __forceinline__ static f32x4_t get4(const char* s, int r, int col) {
     uint2 w = *reinterpret_cast<const uint2*>(s + off4(r, col));
@@ -392,10 +394,12 @@ struct EpiLinear {
           v = v * alpha;
           if constexpr (ADD) v = v + res[i & 1].get(j, q);
           if constexpr (!(FLAGS & EL_F32OUT)) {
-            v = round_bf4(v);
-            if constexpr (FLAGS & EL_SUMSQ)
-              if (m < c.M && n < c.N) part[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-            S::put4(c.stage(), c.lrow(i), c.lcol(j, q), v);   // the stage is free after the mainloop
+            const uint2 pk = pack_bf4(v);
+            if constexpr (FLAGS & EL_SUMSQ) {
+              const f32x4_t w = unpack_bf4(pk);   // the stored values
+              if (m < c.M && n < c.N) part[i] += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+            }
+            S::put4p(c.stage(), c.lrow(i), c.lcol(j, q), pk);   // the stage is free after the mainloop
           } else {
             set_frag(acc, i, j, q, v);
           }
@@ -658,16 +662,18 @@ struct EpiDSwiGLU {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const float sg = sigmoidf_(hg[t]);
-            dg[t] = round_bf(r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg))));
-            du[t] = round_bf(r * (da[t] * hg[t] * sg));
+            dg[t] = r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg)));
+            du[t] = r * (da[t] * hg[t] * sg);
           }
+          const uint2 pdg = pack_bf4(dg), pdu = pack_bf4(du);
           const int f = c.col(j, q);
           if (m < c.M && f < c.N) {   // F % 32 == 0: the 4 columns are all in or all out
+            const f32x4_t rg = unpack_bf4(pdg), ru = unpack_bf4(pdu);   // the stored values
 #pragma unroll
-            for (int t = 0; t < 4; ++t) part[i] += dg[t] * hg[t] + du[t] * hu[t];
+            for (int t = 0; t < 4; ++t) part[i] += rg[t] * hg[t] + ru[t] * hu[t];
             const int pg = packed_gate(f);
-            *reinterpret_cast<uint2*>(orow + pg) = uint2{pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3])};
-            *reinterpret_cast<uint2*>(orow + pg + 32) = uint2{pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3])};
+            *reinterpret_cast<uint2*>(orow + pg) = pdg;
+            *reinterpret_cast<uint2*>(orow + pg + 32) = pdu;
           }
         }
       if (i + 2 < Cfg::TM) load_block(e, c, i + 2, b);
@@ -711,10 +717,12 @@ struct EpiDSigmoid {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const float sg = sigmoidf_(h[t]);
-            d[t] = round_bf(r * (da[t] * sg * (1.0f - sg)));
+            d[t] = r * (da[t] * sg * (1.0f - sg));
           }
-          if (m < c.M && c.col(j, q) < c.N) part[i] += d[0] * h[0] + d[1] * h[1] + d[2] * h[2] + d[3] * h[3];
-          S::put4(s, c.lrow(i), c.lcol(j, q), d);
+          const uint2 pk = pack_bf4(d);
+          const f32x4_t dr = unpack_bf4(pk);   // the stored values
+          if (m < c.M && c.col(j, q) < c.N) part[i] += dr[0] * h[0] + dr[1] * h[1] + dr[2] * h[2] + dr[3] * h[3];
+          S::put4p(s, c.lrow(i), c.lcol(j, q), pk);
         }
       if (i + 2 < Cfg::TM) hb[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
@@ -765,8 +773,8 @@ struct EpiNormCorrection {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           S::put4(s, c.lrow(i), c.lcol(j, q),
-                  round_bf4(sc * (frag(acc, i, j, q) - cc * u[i & 1].get(j, q)) +
-                            (has_res ? z[i & 1].get(j, q) : f32x4_t{0, 0, 0, 0})));
+                  sc * (frag(acc, i, j, q) - cc * u[i & 1].get(j, q)) +
+                      (has_res ? z[i & 1].get(j, q) : f32x4_t{0, 0, 0, 0}));
       if (i + 2 < Cfg::TM) {
         u[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
         if (has_res) z[i & 1].load(e.aux1, e.ld_aux1, c, i + 2);
@@ -928,16 +936,21 @@ struct EpiCrossEntropyGrad {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = c.col(j, q);
-          f32x4_t gv;
+          f32x4_t gv, zv;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float z = NORM ? r * acc.c[i][j][4 * q + t] : acc.c[i][j][4 * q + t];
-            const float p = __expf(z - lse) - (n + t == y ? 1.0f : 0.0f);
-            gv[t] = valid ? (NORM ? round_bf(r * p) : p) : 0.0f;
-            if constexpr (NORM)
-              if (n + t < c.N) part[i] += gv[t] * z;
+            zv[t] = NORM ? r * acc.c[i][j][4 * q + t] : acc.c[i][j][4 * q + t];
+            const float p = __expf(zv[t] - lse) - (n + t == y ? 1.0f : 0.0f);
+            gv[t] = valid ? (NORM ? r * p : p) : 0.0f;
           }
-          StageBF<Cfg::BM, Cfg::BN>::put4(c.stage(), c.lrow(i), c.lcol(j, q), gv);
+          const uint2 pk = pack_bf4(gv);
+          if constexpr (NORM) {
+            const f32x4_t gr = unpack_bf4(pk);   // the stored values
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (n + t < c.N) part[i] += gr[t] * zv[t];
+          }
+          StageBF<Cfg::BM, Cfg::BN>::put4p(c.stage(), c.lrow(i), c.lcol(j, q), pk);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
