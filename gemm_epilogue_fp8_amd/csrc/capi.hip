@@ -163,6 +163,22 @@ extern "C" coda_status coda_rope_table(int32_t seq_len, int32_t head_dim, double
   return check_launch("rope_table");
 }
 
+// Partial rows a consumer GEMM's prologue reduces itself (they stay in
+// registers through its mainloop).
+constexpr int kProloguePartials = RowPartials<GemmCfg<kBM, kBN, 2, 4, true, false>>::MAX_PARTIALS;
+
+// A wider set of row partials is first summed to one row, in a fixed order,
+// by a small kernel (the light merge step of the paper, §3.1) into `tmp` [M].
+static coda_status narrow_partials(const float** P, int* nP, int64_t M, float* tmp, hipStream_t s) {
+  if (*nP <= kProloguePartials || M == 0) return CODA_OK;
+  hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, *P, *nP, (int)M, 0,
+                     (const float*)nullptr, 0, 0.0f, tmp);
+  TRY(check_launch("merge row partials"));
+  *P = tmp;
+  *nP = 1;
+  return CODA_OK;
+}
+
 static coda_status row_sumsq_launch(const void* x, int64_t ld, int64_t M, int64_t K, float* out, hipStream_t s) {
   if (M == 0) return CODA_OK;
   hipLaunchKernelGGL(row_sumsq_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s,
@@ -292,8 +308,8 @@ extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_ma
     } else {
       const coda_mat* P = auxm(op[0].slot);
       TRY(check_mat(P, "partials", CODA_F32, -1, M));
-      if (P->rows < 1 || P->rows > RowPartials<GemmCfg<kBM, kBN, 2, 4, true, false>>::MAX_PARTIALS || P->ld != M)
-        return fail(CODA_ERR_SHAPE, "gemm_epi: partials must be [1..32, M] with ld == M");
+      if (P->rows < 1 || P->rows > kProloguePartials || P->ld != M)
+        return fail(CODA_ERR_SHAPE, "gemm_epi: partials must be [1..8, M] with ld == M");
       e.row_partials = fptr(P);
       e.n_row_partials = (int)P->rows;
       e.norm_dim = (int)K;
@@ -314,7 +330,8 @@ extern "C" coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, in
                                                         int32_t precision, size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   Carver cv(nullptr);
-  if (!have_partials) cv.take<float>(M);
+  (void)have_partials;
+  cv.take<float>(M);   // row sum of squares, or the merged partials
   if (precision == CODA_PREC_FP8) take_act(cv, M, K, 1);
   *bytes = cv.off;
   return CODA_OK;
@@ -339,7 +356,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
                                    Act act = Act::SwiGLU) {
   const int64_t M = x->rows, K = x->cols, N = Wgu->w.cols, F = N / 2;
   Carver cv(size_only ? nullptr : ws);
-  float* sumsq = present(P) ? nullptr : cv.take<float>(M);
+  float* sumsq = cv.take<float>(M);
   ActQ aq{};
   if (precision == CODA_PREC_FP8) aq = take_act(cv, M, K, 1);
   if (size_only) { *bytes = cv.off; return CODA_OK; }
@@ -351,6 +368,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   if (present(save)) { e.save = save->ptr; e.ld_save = save->ld; }
   e.row_partials = present(P) ? fptr(P) : sumsq;
   e.n_row_partials = present(P) ? (int)P->rows : 1;
+  TRY(narrow_partials(&e.row_partials, &e.n_row_partials, M, sumsq, s));
   e.norm_dim = (int)K;
   e.eps = eps;
   e.rowvec_out = present(r_out) ? static_cast<float*>(r_out->ptr) : nullptr;
@@ -450,7 +468,8 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t 
                                                              int32_t precision, size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   Carver cv(nullptr);
-  if (!have_partials) cv.take<float>(M);
+  (void)have_partials;
+  cv.take<float>(M);   // row sum of squares, or the merged partials
   if (precision == CODA_PREC_FP8) take_act(cv, M, D, 1);
   *bytes = cv.off;
   return CODA_OK;
@@ -482,7 +501,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   TRY(check_vec(r_out, "r_out", CODA_F32, M, true));
   if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
   Carver cv(ws);
-  float* sumsq = present(P) ? nullptr : cv.take<float>(M);
+  float* sumsq = cv.take<float>(M);
   const bool fp8 = precision == CODA_PREC_FP8;
   ActQ aq{};
   if (fp8) aq = take_act(cv, M, D, 1);
@@ -496,6 +515,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   if (present(save)) { e.save = save->ptr; e.ld_save = save->ld; }
   e.row_partials = present(P) ? fptr(P) : sumsq;
   e.n_row_partials = present(P) ? (int)P->rows : 1;
+  TRY(narrow_partials(&e.row_partials, &e.n_row_partials, M, sumsq, s));
   e.norm_dim = (int)D;
   e.eps = eps;
   e.rowvec_out = present(r_out) ? static_cast<float*>(r_out->ptr) : nullptr;
@@ -1085,7 +1105,8 @@ static size_t nce_fwd_layout(Carver& cv, int64_t M, int64_t V, bool need_sumsq, 
   *zy = cv.take<float>(M);
   *per_row = cv.take<float>(M);
   *status = cv.take<int>(M);
-  *P1 = need_sumsq ? cv.take<float>(M) : nullptr;
+  (void)need_sumsq;
+  *P1 = cv.take<float>(M);   // row sum of squares, or the merged partials
   *r = cv.take<float>(M);
   return cv.off;
 }
@@ -1118,7 +1139,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
   const coda_mat* P = sumsq_partials;
   if (present(P)) {
     TRY(check_mat(P, "sumsq_partials", CODA_F32, -1, M));
-    if (P->rows < 1 || P->rows > RowPartials<GemmCfg<kBM, kBN, 2, 4, true, false>>::MAX_PARTIALS || P->ld != M)
+    if (P->rows < 1 || P->rows > 32 || P->ld != M)
       return fail(CODA_ERR_SHAPE, "sumsq_partials: 1..32 rows of M, ld == M");
   }
   TRY(check_vec(labels, "labels", CODA_I32, M));
@@ -1152,6 +1173,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
     e.rowvec_out2 = present(r_out) ? static_cast<float*>(r_out->ptr) : rws;
     e.row_partials = parts;
     e.n_row_partials = nP;
+    TRY(narrow_partials(&e.row_partials, &e.n_row_partials, M, P1, s));
     e.norm_dim = (int)D;
     e.eps = eps;
     e.vocab = (int)V;

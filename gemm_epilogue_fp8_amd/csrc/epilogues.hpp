@@ -296,11 +296,14 @@ __device__ __forceinline__ void write_row_partial(const Ctx<Cfg>& c, const float
 
 // ---------------------------------------------------------------- prologue: finish row partials
 // Loads P[t][m0 + r] for every t < nP before the mainloop (up to MAXP values a
-// thread, all loads independent) and after it reduces them into LDS.
+// thread, all loads independent) and after it reduces them into LDS.  The
+// values stay in registers through the mainloop, so their number is kept
+// small; a wider set of partials is first summed to one row by an auxiliary
+// kernel (the light merge step of the paper, §3.1).
 template <class Cfg>
 struct RowPartials {
   static constexpr int TPR = Cfg::T / Cfg::BM;   // threads per row
-  static constexpr int MAXP = 16;                // partials per thread
+  static constexpr int MAXP = 4;                 // partials per thread
   static constexpr int MAX_PARTIALS = MAXP * TPR;
   float v[MAXP];
   __device__ __forceinline__ void issue(const float* P, int nP, const Ctx<Cfg>& c) {

@@ -13,30 +13,40 @@
 //    group.
 //  * Wave-group ping-pong.  The K loop runs in phases separated by
 //    workgroup barriers.  In a "memory" phase a wave reads its MFMA fragments
-//    of one K step from LDS into registers and issues its group's share of a
-//    future stage's global->LDS copies; in a "compute" phase it only issues
-//    MFMAs.  Group 1 starts one phase late, so on every SIMD one wave keeps
-//    the matrix core busy while the other one moves data, and the barriers
-//    cost no MFMA time.  (The paper's Hopper design gets the same overlap
-//    from two consumer warpgroups, §1; here it is two waves per SIMD.)
-//  * K step 64 bytes (32 bf16 or 64 fp8); 4 LDS stages of (256 + 256) x 64 B.
-//    Stage s streams from global memory straight into LDS (buffer_load ...
-//    lds: lane l of a wave instruction writes 16 bytes at lds + 16 l, no
-//    registers), issued 3 steps ahead: group 0 copies the A tile, group 1 the
-//    B tile.  Each wave waits (vmcnt) only for the stage that is read next.
+//    of one stage pair (two 64-byte K stages) from LDS into registers and
+//    issues its group's share of future global->LDS copies; in a "compute"
+//    phase it only issues MFMAs (32 of them, 1024 matrix-core cycles a wave).
+//    Group 1 starts one phase late, so on every SIMD one wave keeps the
+//    matrix core busy while the other one moves data.  (The paper's Hopper
+//    design gets the same overlap from two consumer warpgroups, §1; here it
+//    is two waves per SIMD.)  A phase of two K stages rather than one halves
+//    the barriers per MFMA; on MI355X that took plain-store GEMMs at 8192^3
+//    from 1.09 to 1.20 PFLOP/s (row-major operands) and 1.16 to 1.24
+//    (K-contiguous operands).
+//  * 4 LDS stages of (256 + 256) x 64 B (64 B = 32 bf16 or 64 fp8 of K), i.e.
+//    two stage pairs.  Stages stream from global memory straight into LDS
+//    (buffer_load ... lds: lane l of a wave instruction writes 16 bytes at
+//    lds + 16 l, no registers).  Group 0 copies the A tile of pair p + 1 in
+//    its memory phase p, into the slots of pair p - 1.  Group 1, which reads
+//    pair p last, copies the B tile of pair p + 2 into pair p's slots as soon
+//    as its own fragment reads have landed; this is safe only because wave w
+//    copies exactly the B columns that wave w of each group reads (its
+//    partner in group 0 finished with them one phase earlier).  Each wave
+//    waits (vmcnt) only for the pair that is read next.
 //  * A K-contiguous operand tile is [rows][64 bytes] with its 16-byte chunks
 //    XOR-swizzled by (r >> 2) & 3; each lane picks the global chunk that
 //    belongs at its fixed LDS slot.  gfx950 LDS serves a 16-byte access 16
 //    lanes at a time over 64 banks: a fragment read (16 rows, one chunk)
 //    touches 16 distinct 16-byte bank groups.
 //  * An M/N-contiguous operand (the weight of a forward NN product, both
-//    operands of a TN weight gradient) keeps its storage order in LDS:
-//    [32 k rows][256 columns], chunks XOR-swizzled by 4 (k & 3).  Its MFMA
-//    fragments come from ds_read_b64_tr_b16: in each 16-lane group, lane i
-//    receives element i % 4 of the 4-element loads of lanes 4u + i/4, so
-//    lanes pointing at (row kb + j/4, column c0 + 4 (j % 4)) deliver to lane
-//    i the 4 K values kb..kb+3 of column c0 + i.  Two such reads make one
-//    8-deep K fragment; 32 lanes read 4 rows x 64 bytes, bank-conflict free.
+//    operands of a TN weight gradient) is kept in LDS as four column blocks
+//    of [32 k rows][64 columns] (128-byte rows), chunks XOR-swizzled by
+//    4 ((k >> 1) & 1).  Its MFMA fragments come from ds_read_b64_tr_b16: in
+//    each 16-lane group, lane i receives element i % 4 of the 4-element loads
+//    of lanes 4u + i/4, so lanes pointing at (row kb + j/4, column
+//    c0 + 4 (j % 4)) deliver to lane i the 4 K values kb..kb+3 of column
+//    c0 + i.  Two such reads make one 8-deep K fragment; 32 lanes read 4 rows
+//    x 64 bytes, which the swizzle spreads over all 64 banks.
 //  * Global loads go through buffer resources: out-of-range rows, columns and
 //    K tails read as zero, so ragged M, N and K need no branches.
 //  * MFMA operands are swapped (the B tile feeds the instruction's A port),
@@ -96,7 +106,8 @@ struct GemmArgs {
 
 // ---------------------------------------------------------------- operand tiles
 // K-contiguous operand stored [rows, K]: tile = R rows x 64 bytes of K,
-// copied by the WAVES_N waves of one group.
+// copied by the WAVES_N waves of one group; wave w copies the quarter of the
+// rows that wave w of each group reads when the tile is the B operand.
 template <class Cfg, int R>
 struct TileKC {
   static constexpr int NI = R * kRowBytes / 1024 / Cfg::WAVES_N;   // 1 KB wave instructions per wave
@@ -109,7 +120,7 @@ struct TileKC {
     const auto rs = make_rsrc(p, rem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + Cfg::WAVES_N * i;              // 16 rows per instruction
+      const int q = NI * w + i;                        // 16 rows per instruction; wave w: rows [R/4 w, R/4 (w+1))
       const int row = 16 * q + (lane >> 2);
       const int chunk = (lane & 3) ^ kc_swz(row);      // the chunk that lives at this slot
       const bool ok = (row0 + row < nrows) && (kbyte0 + chunk * 16 < kbytes);
@@ -120,19 +131,22 @@ struct TileKC {
 };
 
 // M/N-contiguous bf16 operand stored [K, cols]: tile = BK k rows x R columns,
-// copied by the WAVES_N waves of one group.
+// copied by the WAVES_N waves of one group.  LDS holds it as R/64 column
+// blocks of [BK k rows][64 columns] (128-byte rows, 4 KB a block), so that
+// the 64 columns one wave reads as the B operand are one contiguous block,
+// and wave w copies exactly block w.  16-byte chunks are XOR-swizzled by
+// 4 ((k >> 1) & 1).
 template <class Cfg, int R>
 struct TileMN {
-  static constexpr int ROWB = 2 * R;                       // bytes per k row
-  static constexpr int CPR = ROWB / 16;                    // chunks per k row
-  static constexpr int RPI = 1024 / ROWB;                  // k rows per wave instruction
-  static constexpr int NI = Cfg::BK * ROWB / 1024 / Cfg::WAVES_N;
-  static_assert(Cfg::BK * ROWB % (1024 * Cfg::WAVES_N) == 0, "tile must split into 1 KB wave loads");
+  static constexpr int ROWB = 128;                         // bytes per k row of a block
+  static constexpr int BLOCK = Cfg::BK * ROWB;             // bytes per 64-column block
+  static constexpr int NI = BLOCK / 1024;                  // wave instructions per block (8 k rows each)
   static_assert(Cfg::FP8 || 2 * Cfg::BK == kRowBytes, "an M/N tile has the bytes of a K-contiguous one");
-  static_assert(CPR >= 16, "swizzle needs at least 16 chunks a row");
+  static_assert(R == 64 * Cfg::WAVES_N, "one 64-column block per wave");
 
-  __device__ __forceinline__ static int swz(int krow) { return 4 * (krow & 3); }
+  __device__ __forceinline__ static int swz(int krow) { return 4 * ((krow >> 1) & 1); }
 
+  // lane l of instruction i of wave w: k row 8 i + l / 8, LDS chunk slot l % 8
   __device__ __forceinline__ static void issue(const char* base, int64_t ld_bytes, int k0, int K, int col0,
                                                int ncols, char* lds, int w, int lane) {
     const char* p = base + (int64_t)k0 * ld_bytes + (int64_t)col0 * 2;
@@ -140,25 +154,26 @@ struct TileMN {
     const auto rs = make_rsrc(p, rem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = w + Cfg::WAVES_N * i;
-      const int krow = RPI * q + lane / CPR;
-      const int chunk = (lane % CPR) ^ swz(krow);
-      const bool ok = (k0 + krow < K) && (col0 + chunk * 8 < ncols);
-      const uint32_t off = ok ? (uint32_t)(krow * ld_bytes + chunk * 16) : kOobOffset;
-      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)off, 0, 0, 0);
+      const int krow = 8 * i + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz(krow);            // the chunk that lives at this slot
+      const int col = 64 * w + 8 * chunk;
+      const bool ok = (k0 + krow < K) && (col0 + col < ncols);
+      const uint32_t off = ok ? (uint32_t)(krow * ld_bytes + col * 2) : kOobOffset;
+      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + w * BLOCK + i * 1024), 16, (int)off, 0, 0, 0);
     }
   }
 
   // bf16x8 fragment: column r0 + (lane & 31), K values 16 s + 8 (lane >> 5) + 0..7
   __device__ __forceinline__ static bf16x8_t frag(const char* lds, int r0, int s, int lane) {
     const int j = lane & 15, g = lane >> 4;
-    const int col = r0 + 16 * (g & 1) + 4 * (j & 3);
+    const int lc = (r0 & 63) + 16 * (g & 1) + 4 * (j & 3);
+    const char* blk = lds + (r0 >> 6) * BLOCK;
     short4_t h[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int krow = 16 * s + 8 * (g >> 1) + 4 * half + (j >> 2);
-      const int chunk = (col >> 3) ^ swz(krow);
-      const char* a = lds + krow * ROWB + chunk * 16 + (col & 7) * 2;
+      const int chunk = (lc >> 3) ^ swz(krow);
+      const char* a = blk + krow * ROWB + chunk * 16 + (lc & 7) * 2;
       h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)a);
     }
     short8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
@@ -262,17 +277,10 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Waits until at most `stages` stages of this wave's copies are in flight.
-template <int LPS, int NS>
-__device__ __forceinline__ void wait_stages(int stages) {
-  static_assert(NS == 4, "three stages of look-ahead");
-  if (stages <= 0) wait_vmcnt<0>();
-  else if (stages == 1) wait_vmcnt<LPS>();
-  else wait_vmcnt<2 * LPS>();
-}
-
 // Runs the whole K loop for the tile at (m0, n0); acc starts at zero.  Every
-// wave of the workgroup passes the same number of barriers (2 nk + 1).
+// wave of the workgroup passes the same number of barriers (2 np + 1, np =
+// stage pairs).  An odd stage count ends with a stage past K, which the buffer
+// bounds read as zeros.
 template <class Cfg>
 __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>& acc,
                                          int m0, int n0, int wm0, int wn0, int tid, int lane) {
@@ -288,11 +296,14 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
   const int64_t lda_b = g.lda * Cfg::ESIZE, ldb_b = g.ldb * Cfg::ESIZE;
   const int64_t kbytes = (int64_t)g.K * Cfg::ESIZE;
   const int nk = (g.K + Cfg::BK - 1) / Cfg::BK;
+  const int np = (nk + 1) / 2;             // stage pairs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / Cfg::WAVES_N;     // 0 copies A and leads; 1 copies B and trails one phase
   const int w = wave % Cfg::WAVES_N;
   constexpr int NS = Cfg::NS;
+  static_assert(NS == 4, "two stage pairs");
   constexpr int SUB = substeps<Cfg>();
+
   // copies one stage issues per wave (each group copies one operand tile)
   constexpr int LPS = Cfg::A_KC ? TileKC<Cfg, Cfg::BM>::NI : TileMN<Cfg, Cfg::BM>::NI;
   static_assert(LPS == (Cfg::B_KC ? TileKC<Cfg, Cfg::BN>::NI : TileMN<Cfg, Cfg::BN>::NI),
@@ -314,34 +325,57 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
         TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, k0, g.K, n0, g.N, Bs, w, lane);
     }
   };
+  auto issue_pair = [&](int p) { issue_stage(2 * p); issue_stage(2 * p + 1); };
 
-  const int npre = nk < NS - 1 ? nk : NS - 1;
-  for (int s = 0; s < npre; ++s) issue_stage(s);
-  wait_stages<LPS, NS>(npre - 1);          // this wave's part of stage 0 has landed
-  phase_barrier();                         // stage 0 is complete
+  // prologue: group 0 copies the A tiles of pair 0, group 1 the B tiles of
+  // pairs 0 and 1; pair 0 must land
+  issue_pair(0);
+  if (grp == 1 && np > 1) {
+    issue_pair(1);
+    wait_vmcnt<2 * LPS>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  phase_barrier();                         // pair 0 is complete
   if (grp == 1) phase_barrier();           // group 1 trails by one phase
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // ---- memory phase: fragments of stage kt, copies of stage kt + NS - 1
-    const char* As = smem + (kt % NS) * Cfg::STAGE_BYTES;
-    const char* Bs = As + Cfg::BM * kRowBytes;
-    Frags<Cfg> f[SUB];
+  for (int p = 0; p < np; ++p) {
+    // ---- memory phase: fragments of pair p
+    const char* S0 = smem + ((2 * p) % NS) * Cfg::STAGE_BYTES;
+    const char* S1 = smem + ((2 * p + 1) % NS) * Cfg::STAGE_BYTES;
+    Frags<Cfg> f[2 * SUB];
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) load_frags<Cfg>(As, Bs, s, f[s], wm0, wn0, lane);
-    if (kt + NS - 1 < nk) issue_stage(kt + NS - 1);
-    wait_lgkmcnt0();                        // fragments in registers, stage kt released
-    // stages after kt + 1 this wave has in flight; stage kt + 1 must land before
-    // the barrier that ends the phase in which group 1 reads stage kt
-    const int ahead = nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2;
-    if (grp == 1) wait_stages<LPS, NS>(ahead);
+    for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S0, S0 + Cfg::BM * kRowBytes, s, f[s], wm0, wn0, lane);
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, f[SUB + s], wm0, wn0, lane);
+    // Pair p + 1 must land before the barrier that ends the phase in which
+    // group 1 reads pair p (group 0 reads pair p + 1 in the next one).
+    if (grp == 0) {
+      // A of pair p + 1 into the slots of pair p - 1, which group 1 finished
+      // reading in the previous phase
+      if (p + 1 < np) issue_pair(p + 1);
+      wait_lgkmcnt0();                     // fragments in registers
+    } else {
+      // B of pair p + 2 into the slots of pair p.  Wave w copies exactly the
+      // B columns that wave w of either group reads: group 0 read them in the
+      // previous phase and this wave's own reads have landed, so no other
+      // wave still needs what is overwritten.
+      wait_lgkmcnt0();
+      if (p + 2 < np) {
+        issue_pair(p + 2);
+        wait_vmcnt<2 * LPS>();             // pair p + 1 has landed
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
     phase_barrier();
     // ---- compute phase
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) mma_frags<Cfg>(f[s], acc);
-    if (grp == 0) wait_stages<LPS, NS>(ahead);
+    for (int s = 0; s < 2 * SUB; ++s) mma_frags<Cfg>(f[s], acc);
+    if (grp == 0) wait_vmcnt<0>();         // A of pair p + 1 has landed
     phase_barrier();
   }
-  if (grp == 0) phase_barrier();           // realign: both groups have passed 2 nk + 1 barriers
+  if (grp == 0) phase_barrier();           // realign: both groups have passed 2 np + 1 barriers
 }
 
 }  // namespace coda

@@ -141,7 +141,7 @@ coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_byte
  *   ROW_SCALE(v) COL_SCALE(w) STORE_BF16              NN only
  *   ADD_TILE(z) STORE_BF16 [ROW_SUMSQ_PARTIAL(P)]     NN only (residual + next-norm partials)
  *   ROW_SCALE(r) SWIGLU STORE_BF16                    NN only, D [M, N/2]
- *   ROW_RMS_FROM_PARTIALS(P, fparam = eps) SWIGLU STORE_BF16   NN only
+ *   ROW_RMS_FROM_PARTIALS(P, fparam = eps) SWIGLU STORE_BF16   NN only, P [1..8, M]
  * `slot` indexes the aux array; ROW_SUMSQ_PARTIAL writes P[tiles_n][M] with
  * tiles_n = ceil(N / 256) (see coda_partials_cols). */
 typedef enum coda_epi_opcode {
@@ -182,7 +182,10 @@ coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32
  *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r * (x W~_gu),
  *   out = SiLU(h_gate) * h_up
  * x: bf16 [M, K].  sumsq_partials: fp32 [n, M] sum-of-squares partials of x
- * (n <= 32) or NULL (the library computes them; workspace needed).
+ * (n <= 32) or NULL (the library computes them).  More than 8 partial rows
+ * are first merged to one by a small kernel.  The workspace (always needed,
+ * sized by the query; have_partials is accepted for compatibility and does
+ * not change the size) holds that row.
  * Wgu: packed, gain-folded weight (coda_pack_gate_up).  out: bf16 [M, F].
  * save_hgu (bf16 [M, 2F], packed order) and r_out (fp32 1 x M) are optional
  * saves for the backward. */
@@ -206,7 +209,8 @@ coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weigh
  * RoPE (MHA, head_dim 128, D = heads * 128):
  *   h = r1 * (x W~_qkv) [M, 3D];  q = RoPE(QKnorm(h_q; gq)), k likewise, v = h_v
  * positions p = m mod seq_len.  rope: coda_rope_table output.  Optional
- * saves: qk_pre bf16 [M, 2D] (pre-norm q | k), r_out fp32 1 x M. */
+ * saves: qk_pre bf16 [M, 2D] (pre-norm q | k), r_out fp32 1 x M.
+ * sumsq_partials and the workspace as in coda_linear_swiglu_fwd. */
 coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t D, int32_t have_partials,
                                                   int32_t precision, size_t* bytes);
 coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda_mat* sumsq_partials,
@@ -332,8 +336,9 @@ coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, c
  *   coda_linear_cross_entropy_fwd.
  * y: bf16 [M, D] (the final residual stream); sumsq_partials: fp32 [n, M]
  * (n <= 32) sum-of-squares partials of y (the last down-projection's
- * coda_linear_rmsnorm_residual_fwd output) or NULL (computed here;
- * workspace).  W: the folded weight [D, V].  r_out: optional fp32 1 x M
+ * coda_linear_rmsnorm_residual_fwd output) or NULL (computed here).  More
+ * than 8 partial rows are merged to one first, in the workspace.  W: the
+ * folded weight [D, V].  r_out: optional fp32 1 x M
  * (needed by the backward).  Other outputs as in the plain cross-entropy.
  * bf16 only (fp8 returns CODA_ERR_UNSUPPORTED). */
 coda_status coda_linear_rmsnorm_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t have_partials,

@@ -89,16 +89,23 @@ def test_gemm_row_col_scale_and_residual_partials():
 
 
 # ------------------------------------------------------------------ config 1: RMSNorm -> Linear -> SwiGLU
-def _swiglu_case(shape, seed, use_partials=False, saves=False):
+def _swiglu_case(shape, seed, use_partials=False, saves=False, n_partials=1):
     P = ci.swiglu_inputs(shape, seed)
     x = bf(P["x"])
     Wgu = torch.empty((shape.K, 2 * shape.F), dtype=BF, device=DEV)
     coda.pack_gate_up(bf(P["Wg"]), bf(P["Wu"]), f32(P["g"]), Wgu)
     out = torch.empty((shape.M, shape.F), dtype=BF, device=DEV)
     partials = None
-    if use_partials:
+    if use_partials and n_partials == 1:
         partials = torch.empty((1, shape.M), dtype=torch.float32, device=DEV)
         coda.row_sumsq(x, partials)
+    elif use_partials:
+        # the row sums of squares split over n column slices, as a producer's
+        # epilogue would hand them over (more than 8 go through the merge kernel)
+        xs = P["x"].astype(np.float64) ** 2
+        bounds = np.linspace(0, shape.K, n_partials + 1).astype(int)
+        parts = np.stack([xs[:, a:b].sum(axis=1) for a, b in zip(bounds[:-1], bounds[1:])])
+        partials = f32(parts.astype(np.float32))
     save = torch.empty((shape.M, 2 * shape.F), dtype=BF, device=DEV) if saves else None
     r_out = torch.empty(shape.M, dtype=torch.float32, device=DEV) if saves else None
     coda.linear_swiglu_fwd(x, Wgu, shape.eps, out, sumsq_partials=partials, save_hgu=save, r_out=r_out)
@@ -121,6 +128,13 @@ def test_config1_exact_shape():
 
 def test_swiglu_ragged_with_partials_and_saves():
     _swiglu_case(ci.SwiGLUShape(M=333, K=264, F=352), 3, use_partials=True, saves=True)
+
+
+@pytest.mark.parametrize("n_partials", [8, 12, 32])
+def test_swiglu_many_partials(n_partials):
+    """Up to 8 partial rows are reduced in the GEMM prologue; more are merged
+    to one row by the auxiliary kernel first."""
+    _swiglu_case(ci.SwiGLUShape(M=300, K=512, F=352), 4, use_partials=True, saves=True, n_partials=n_partials)
 
 
 # ------------------------------------------------------------------ RMSNorm -> Linear -> sigmoid
