@@ -24,10 +24,15 @@
 // goes to an LDS staging tile (8-byte writes in the register layout, 16-byte
 // chunks XOR-swizzled by row) and the whole workgroup then moves it with
 // row-contiguous 16-byte accesses (64 lanes = two full 512-byte rows), which
-// is what keeps epilogue traffic near HBM speed.  Auxiliary tiles (residual,
-// saved activations, weights) come in the same way and are read back in the
-// register layout.  After the mainloop the 128 KB of pipeline LDS is free for
-// staging; row vectors and reduction scratch live in a separate 10 KB.
+// is what keeps epilogue traffic near HBM speed.  Auxiliary tiles that share
+// the output tile's layout (residual, saved pre-activations) are copied
+// global -> LDS into the staging tile by buffer_load ... lds, all copies in
+// flight at once; each lane then replaces its values by its outputs in place.
+// Auxiliary tiles beside a second operand (the norm correction's u and res,
+// the unfolded weight of the gain gradient) stream straight into registers
+// one 32-row block ahead.  After the mainloop the 128 KB of pipeline LDS is
+// free for staging; row vectors and reduction scratch live in a separate
+// 10 KB.
 #pragma once
 #include "gemm_core.hpp"
 
@@ -157,6 +162,36 @@ __device__ __forceinline__ void stage_load_bf(char* s, int tid, Src src) {
     const int r = id / S::CPR, ch = id % S::CPR;
     const uint16_t* p = src(r, ch * 8);
     *reinterpret_cast<uint4*>(s + S::off(r, ch)) = p ? *reinterpret_cast<const uint4*>(p) : uint4{0, 0, 0, 0};
+  }
+}
+
+// bf16 tile [R][C] of the matrix at (m0 + r, col0 + c), rows < M and
+// columns < N (N % 8 == 0), copied global -> LDS into the StageBF<R, C>
+// layout by buffer_load ... lds: no registers, every copy of the workgroup in
+// flight at once, positions outside the matrix read as zero.  Lane l of a
+// copy writes the 16-byte LDS slot l of its row(s); it fetches the chunk that
+// the row swizzle puts there.  The caller waits (vmcnt) and syncs.
+template <class Cfg, int R, int C>
+__device__ __forceinline__ void stage_dma_bf(char* s, const void* base, int64_t ld, int m0, int col0, int M, int N,
+                                             int tid) {
+  using S = StageBF<R, C>;
+  constexpr int RPI = 64 / S::CPR;                       // rows per wave copy
+  static_assert(S::CPR <= 64 && 64 % S::CPR == 0, "a wave copy covers whole rows");
+  constexpr int NI = R / RPI;                             // copies of the workgroup
+  static_assert(NI % Cfg::NWAVES == 0, "copies split evenly over the waves");
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const uint16_t* p = static_cast<const uint16_t*>(base) + (int64_t)m0 * ld + col0;
+  const int64_t rows = M - m0 < R ? M - m0 : R;
+  const uint64_t bytes = rows <= 0 ? 0 : (uint64_t)((rows - 1) * ld + (N - col0)) * 2;
+  const auto rs = make_rsrc(p, bytes);
+#pragma unroll
+  for (int k = 0; k < NI / Cfg::NWAVES; ++k) {
+    const int q = wave + Cfg::NWAVES * k;                 // copy index
+    const int r = RPI * q + lane / S::CPR;
+    const int chunk = (lane % S::CPR) ^ (r & (S::CPR - 1));
+    const bool ok = m0 + r < M && col0 + chunk * 8 < N;
+    const uint32_t off = ok ? (uint32_t)(((int64_t)r * ld + chunk * 8) * 2) : kOobOffset;
+    raw_ptr_buffer_load_lds(rs, (lds_void_t*)(s + q * 1024), 16, (int)off, 0, 0, 0);
   }
 }
 
@@ -372,10 +407,13 @@ struct EpiLinear {
     float alpha = e.alpha;
     if constexpr (FLAGS & EL_ALPHADEV) alpha *= *e.alpha_dev;
     constexpr bool ADD = (FLAGS & EL_TILEADD) != 0;
-    RowBlock<Cfg> res[ADD ? 2 : 1];
+    static_assert(!ADD || !(FLAGS & EL_F32OUT), "the residual is added to bf16 outputs");
     if constexpr (ADD) {
-      res[0].load(e.aux0, e.ld_aux0, c, 0);
-      if (Cfg::TM > 1) res[1].load(e.aux0, e.ld_aux0, c, 1);
+      // the residual tile comes into the staging tile; each lane replaces its
+      // values by the outputs (the stage is free after the mainloop)
+      stage_dma_bf<Cfg, Cfg::BM, Cfg::BN>(c.stage(), e.aux0, e.ld_aux0, c.m0, c.n0, c.M, c.N, c.tid);
+      wait_vmcnt<0>();
+      __syncthreads();
     }
     float part[Cfg::TM];
 #pragma unroll
@@ -395,7 +433,7 @@ struct EpiLinear {
           if constexpr (FLAGS & EL_COLVEC)
             v = v * *reinterpret_cast<const f32x4_t*>(e.colvec + c.colc(j, q));
           v = v * alpha;
-          if constexpr (ADD) v = v + res[i & 1].get(j, q);
+          if constexpr (ADD) v = v + S::get4(c.stage(), c.lrow(i), c.lcol(j, q));
           if constexpr (!(FLAGS & EL_F32OUT)) {
             const uint2 pk = pack_bf4(v);
             if constexpr (FLAGS & EL_SUMSQ) {
@@ -407,8 +445,6 @@ struct EpiLinear {
             set_frag(acc, i, j, q, v);
           }
         }
-      if constexpr (ADD)
-        if (i + 2 < Cfg::TM) res[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FLAGS & EL_F32OUT) {
@@ -614,84 +650,82 @@ struct EpiQKNormRope {
 // loads the saved gate/up pre-activations (packed layout), forms dhg, dhu,
 // scales by r2 and stores dh~ (bf16, packed), plus the partials
 // T[tn][m] = sum over the tile of dh~ . h (for the RMSNorm backward).
-// The saved hg / hu come straight into registers in the MFMA layout, one
-// 32-row block (i) at a time with the next block's loads in flight, and dh~
-// goes straight back out from the registers: a lane pair (l, l + 32) writes
-// 16 contiguous bytes of gate and 16 of up, which the L2 merges into whole
-// lines.  No LDS staging and no barrier until the row reduction.
+// The 256 da columns of a tile map to 512 packed columns of hg/hu and dh~, so
+// the tile is done in two 128-row halves (one per wave group) of 128 KB: the
+// half of the saved tile is copied into LDS (stage_dma_bf), the group that
+// owns those rows replaces every hg/hu pair by dhg/dhu in place, and the
+// workgroup stores the half with row-contiguous 16-byte writes.
 template <class Cfg>
 struct EpiDSwiGLU {
   struct Pro {};
-  struct Block { uint2 g[Cfg::TN][4], u[Cfg::TN][4]; };   // one row block of hg, hu (4 bf16 each)
+  static constexpr int HR = Cfg::BM / 2, PC = 2 * Cfg::BN;   // half rows, packed columns
+  using S = StageBF<HR, PC>;
+  static_assert(S::BYTES <= Cfg::LDS_BYTES, "a half tile must fit the staging area");
+  static_assert(HR == Cfg::WM, "each wave group owns one half");
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
 
   __device__ __forceinline__ static int packed_gate(int f) { return (f >> 5) * 64 + (f & 31); }
 
-  __device__ __forceinline__ static void load_block(const EpiArgs& e, const Ctx<Cfg>& c, int i, Block& b) {
-    const uint16_t* H = static_cast<const uint16_t*>(e.aux0) + (int64_t)c.rowc(i) * e.ld_aux0;
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int pg = packed_gate(c.colc(j, q));   // clamped: lanes past N read a valid, unused value
-        b.g[j][q] = *reinterpret_cast<const uint2*>(H + pg);
-        b.u[j][q] = *reinterpret_cast<const uint2*>(H + pg + 32);
-      }
-  }
-
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
     apply_fp8_scales<Cfg>(e, c, acc);
     float part[Cfg::TM];
-    Block blk[2];
-    load_block(e, c, 0, blk[0]);
-    if (Cfg::TM > 1) load_block(e, c, 1, blk[1]);
-    uint16_t* out = static_cast<uint16_t*>(e.out);
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      Block& b = blk[i & 1];
-      part[i] = 0.0f;
-      const int m = c.row(i);
-      const float r = e.rowvec[c.rowc(i)];
-      uint16_t* orow = out + (int64_t)m * e.ld_out;
+    for (int i = 0; i < Cfg::TM; ++i) part[i] = 0.0f;
+    char* s = c.stage();
+    const int grp = c.wm0 / Cfg::WM;
+    const int F2 = 2 * c.N;
 #pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j)
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();   // the staging area is free
+      stage_dma_bf<Cfg, HR, PC>(s, e.aux0, e.ld_aux0, c.m0 + h * HR, 2 * c.n0, c.M, F2, c.tid);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (grp == h) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t hg = f32x4_t{bf_lo(b.g[j][q].x), bf_hi(b.g[j][q].x), bf_lo(b.g[j][q].y), bf_hi(b.g[j][q].y)};
-          const f32x4_t hu = f32x4_t{bf_lo(b.u[j][q].x), bf_hi(b.u[j][q].x), bf_lo(b.u[j][q].y), bf_hi(b.u[j][q].y)};
-          const f32x4_t da = frag(acc, i, j, q);
-          f32x4_t dg, du;
+        for (int i = 0; i < Cfg::TM; ++i) {
+          const int lr = c.lrow(i) - h * HR;
+          const int m = c.row(i);
+          const float r = e.rowvec[c.rowc(i)];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float sg = sigmoidf_(hg[t]);
-            dg[t] = r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg)));
-            du[t] = r * (da[t] * hg[t] * sg);
-          }
-          const uint2 pdg = pack_bf4(dg), pdu = pack_bf4(du);
-          const int f = c.col(j, q);
-          if (m < c.M && f < c.N) {   // F % 32 == 0: the 4 columns are all in or all out
-            const f32x4_t rg = unpack_bf4(pdg), ru = unpack_bf4(pdu);   // the stored values
+          for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) part[i] += rg[t] * hg[t] + ru[t] * hu[t];
-            const int pg = packed_gate(f);
-            *reinterpret_cast<uint2*>(orow + pg) = pdg;
-            *reinterpret_cast<uint2*>(orow + pg + 32) = pdu;
-          }
+            for (int q = 0; q < 4; ++q) {
+              const int pg = packed_gate(c.lcol(j, q));
+              const f32x4_t hg = S::get4(s, lr, pg);
+              const f32x4_t hu = S::get4(s, lr, pg + 32);
+              const f32x4_t da = frag(acc, i, j, q);
+              f32x4_t dg, du;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float sg = sigmoidf_(hg[t]);
+                dg[t] = r * (da[t] * hu[t] * sg * (1.0f + hg[t] * (1.0f - sg)));
+                du[t] = r * (da[t] * hg[t] * sg);
+              }
+              const uint2 pdg = pack_bf4(dg), pdu = pack_bf4(du);
+              if (m < c.M && c.col(j, q) < c.N) {   // F % 32 == 0: the 4 columns are all in or all out
+                const f32x4_t rg = unpack_bf4(pdg), ru = unpack_bf4(pdu);   // the stored values
+#pragma unroll
+                for (int t = 0; t < 4; ++t) part[i] += rg[t] * hg[t] + ru[t] * hu[t];
+              }
+              S::put4p(s, lr, pg, pdg);
+              S::put4p(s, lr, pg + 32, pdu);
+            }
         }
-      if (i + 2 < Cfg::TM) load_block(e, c, i + 2, b);
+      }
+      __syncthreads();
+      stage_store_bf<Cfg, HR, PC>(s, c.tid,
+          MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0 + h * HR, 2 * c.n0, c.M, F2});
     }
-    __builtin_amdgcn_sched_barrier(0);
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
     write_row_partial<Cfg>(c, tot, e.partial_out);
   }
 };
 
-// --- sigmoid backward in the epilogue of da = dY Wn^T: with the saved h (read
-// into registers one 32-row block ahead) and s = sigmoid(h),
-// dh~ = bf16(r da s (1 - s)) is stored and T[tn][m] = sum over the tile of
-// dh~ h is written as row partials.
+// --- sigmoid backward in the epilogue of da = dY Wn^T: with the saved h
+// (copied into the staging tile) and s = sigmoid(h), dh~ = bf16(r da s (1 - s))
+// replaces h in place and is stored; T[tn][m] = sum over the tile of dh~ h is
+// written as row partials.
 template <class Cfg>
 struct EpiDSigmoid {
   struct Pro {};
@@ -699,10 +733,10 @@ struct EpiDSigmoid {
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
     using S = StageBF<Cfg::BM, Cfg::BN>;
     apply_fp8_scales<Cfg>(e, c, acc);
-    RowBlock<Cfg> hb[2];
-    hb[0].load(e.aux0, e.ld_aux0, c, 0);
-    if (Cfg::TM > 1) hb[1].load(e.aux0, e.ld_aux0, c, 1);
     char* s = c.stage();
+    stage_dma_bf<Cfg, Cfg::BM, Cfg::BN>(s, e.aux0, e.ld_aux0, c.m0, c.n0, c.M, c.N, c.tid);
+    wait_vmcnt<0>();
+    __syncthreads();
     float part[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
@@ -714,7 +748,7 @@ struct EpiDSigmoid {
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4_t h = hb[i & 1].get(j, q);
+          const f32x4_t h = S::get4(s, c.lrow(i), c.lcol(j, q));
           const f32x4_t da = frag(acc, i, j, q);
           f32x4_t d;
 #pragma unroll
@@ -727,7 +761,6 @@ struct EpiDSigmoid {
           if (m < c.M && c.col(j, q) < c.N) part[i] += dr[0] * h[0] + dr[1] * h[1] + dr[2] * h[2] + dr[3] * h[3];
           S::put4p(s, c.lrow(i), c.lcol(j, q), pk);
         }
-      if (i + 2 < Cfg::TM) hb[i & 1].load(e.aux0, e.ld_aux0, c, i + 2);
     }
     __builtin_amdgcn_sched_barrier(0);
     float* tot = c.rowv();
