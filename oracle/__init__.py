@@ -12,4 +12,4 @@ Every function is pinned by tests/test_oracle_*.py against something other
 than itself (brute force, closed forms, finite differences, torch CPU library
 routines, exhaustive format round trips).
 """
-from . import numerics, ops, block  # noqa: F401
+from . import numerics, ops, block, mx  # noqa: F401
