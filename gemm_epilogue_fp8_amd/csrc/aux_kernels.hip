@@ -367,6 +367,10 @@ __global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, c
     uint32_t hi = cvt4_e4m3(bf_lo(w.z) * mult, bf_hi(w.z) * mult, bf_lo(w.w) * mult, bf_hi(w.w) * mult);
     *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + c) = uint2{lo, hi};
   }
+  // C is a multiple of 8: zero the bytes up to the row's next 16-byte
+  // boundary, which the GEMM's last 16-byte K chunk reads (ldq >= that
+  // boundary: ldq is a multiple of 16)
+  if ((C & 15) != 0 && lane == 0) *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + C) = uint2{0u, 0u};
 }
 
 __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
@@ -394,13 +398,12 @@ __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C,
     const int rr = part * 16 + 4 * k;
     w[k] = cvt4_e4m3(tile[rr][cc] * mult, tile[rr + 1][cc] * mult, tile[rr + 2][cc] * mult, tile[rr + 3][cc] * mult);
   }
+  // Rows at or past R were loaded as 0 and encode as byte 0, so the last
+  // 16-byte group of a QT row also zeroes the bytes between R and the next
+  // 16-byte boundary, which the GEMM's last 16-byte K chunk reads (ldq is a
+  // multiple of 16, so that boundary lies inside the row).
   const int rbase = r0 + part * 16;
-  if (rbase + 16 <= R) {
-    *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
-  } else {
-    for (int k = 0; k < 16 && rbase + k < R; ++k)
-      QT[(int64_t)c * ldq + rbase + k] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
-  }
+  if (rbase < R) *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
 }
 
 }  // namespace coda

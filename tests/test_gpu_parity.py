@@ -32,6 +32,14 @@ def f32(a):
     return to_dev(np.asarray(a, np.float32))
 
 
+def poison_workspace(nbytes=64 << 20):
+    """Replace the binding's cached workspace by one filled with byte 0xFF
+    (an E4M3 NaN), so that any workspace byte a kernel reads without writing
+    it first shows up as a non-finite result."""
+    coda._WS.clear()
+    coda._workspace(nbytes, torch.device(DEV)).fill_(255)
+
+
 def rand_bf16(rng, *shape, std=1.0):
     return ci.to_bf16_values(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
 
@@ -471,7 +479,10 @@ def test_block_backward_split_k(shape, seed):
 @pytest.mark.parametrize("precision", [0, 1])
 def test_residual_backward_split_k_ragged(precision):
     """4100 tokens (slices of 1088, 1088, 1088 and 836) with beta = 1 over a
-    seeded fp32 prior; bf16 and fp8 operands."""
+    seeded fp32 prior; bf16 and fp8 operands.  The workspace starts as NaN
+    bytes: the fp8 path's transposed copies have rows of 4100 bytes in a
+    16-byte-padded stride, and the GEMM's last K chunk reads the 12 pad
+    bytes, which the quantiser must have zeroed."""
     from tests.helpers import FP8_TOL
     rng = np.random.default_rng(41)
     M, K, N = 4100, 256, 384
@@ -482,6 +493,7 @@ def test_residual_backward_split_k_ragged(precision):
     if precision == coda.PREC_FP8:
         wt.prepare_fp8()
     dW = f32(prior)
+    poison_workspace()
     coda.linear_rmsnorm_residual_bwd(bf(dout), bf(a), wt, dW, beta=1.0, precision=precision)
     torch.cuda.synchronize()
     fp8 = precision == coda.PREC_FP8
@@ -492,13 +504,16 @@ def test_residual_backward_split_k_ragged(precision):
         assert_grad("dW", to_np(dW), ref)
 
 
-@pytest.mark.parametrize("with_da", [True, False])
-def test_fp8_residual_linear_backward_same_inputs(with_da):
+@pytest.mark.parametrize("with_da,M", [(True, 304), (False, 304), (True, 300)])
+def test_fp8_residual_linear_backward_same_inputs(with_da, M):
     """One fp8 stage from identical seeded bf16 inputs: every quantiser sees the
-    same bits on both sides, so the elementwise fp8 rule holds everywhere."""
+    same bits on both sides, so the elementwise fp8 rule holds everywhere.
+    M = 300 gives transposed copies whose rows end 4 bytes short of a 16-byte
+    boundary, read over a workspace of NaN bytes."""
     from tests.helpers import FP8_TOL
     rng = np.random.default_rng(31)
-    M, K, N = 304, 256, 384
+    K, N = 256, 384
+    poison_workspace()
     dout, a = rand_bf16(rng, M, N, std=0.1), rand_bf16(rng, M, K)
     W = rand_bf16(rng, K, N, std=K ** -0.5)
     wt = coda.Weight(bf(W)).prepare_fp8()
