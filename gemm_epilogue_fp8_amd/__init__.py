@@ -16,12 +16,12 @@ from typing import Iterable, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (CODA_BF16, CODA_E4M3, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8,
+from ._lib import (CODA_BF16, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
 
 __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "rope_table", "row_sumsq",
-           "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols",
+           "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
            "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8"]
@@ -38,7 +38,7 @@ def lib():
 
 
 _DT = {torch.bfloat16: CODA_BF16, torch.float32: CODA_F32, torch.float8_e4m3fn: CODA_E4M3,
-       torch.int32: CODA_I32}
+       torch.int32: CODA_I32, torch.uint8: CODA_E8M0, torch.float8_e8m0fnu: CODA_E8M0}
 
 
 def mat(t: Optional[torch.Tensor]) -> _lib.CodaMat:
@@ -175,14 +175,44 @@ def partials_cols(N: int) -> int:
 # ---------------------------------------------------------------- generic
 def gemm_epi(program: Sequence[tuple], A, transA: int, B, transB: int, D, aux: Iterable = ()):
     """program: sequence of (opcode, slot, fparam) tuples (see coda.h)."""
-    prog = _lib.EpiProgram()
-    prog.n_ops = len(program)
-    for i, (op, slot, fparam) in enumerate(program):
-        prog.ops[i].op, prog.ops[i].slot, prog.ops[i].fparam = op, slot, fparam
+    prog = _program(program)
     aux = list(aux)
     arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
     _check(lib().coda_gemm_epi(C.byref(prog), _p(A), transA, _p(B), transB, _p(D),
                                arr if aux else None, len(aux), _stream()))
+    return D
+
+
+def _program(program):
+    prog = _lib.EpiProgram()
+    prog.n_ops = len(program)
+    for i, (op, slot, fparam) in enumerate(program):
+        prog.ops[i].op, prog.ops[i].slot, prog.ops[i].fparam = op, slot, fparam
+    return prog
+
+
+# ---------------------------------------------------------------- MXFP8
+def quantize_mxfp8(X, axis: int, Q=None, S=None):
+    """MXFP8 copy of X [R, C] (bf16): axis 1 -> Q [R, C], S [R, C/32];
+    axis 0 -> Q [C, R] (transposed), S [C, R/32].  S holds E8M0 codes (uint8)."""
+    R, Cc = X.shape
+    rows, L = (R, Cc) if axis == 1 else (Cc, R)
+    if Q is None:
+        Q = torch.empty((rows, L), dtype=torch.float8_e4m3fn, device=X.device)
+    if S is None:   # rows of whole 4-byte words, as the block-scaled GEMM reads them
+        S = torch.empty((rows, (L // 32 + 3) // 4 * 4), dtype=torch.uint8, device=X.device)[:, :L // 32]
+    _check(lib().coda_quantize_mxfp8(_p(X), axis, _p(Q), _p(S), _stream()))
+    return Q, S
+
+
+def gemm_mx(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
+    """D = epilogue(A~ B~^T) with MXFP8 operands A [M, K], B [N, K] and their
+    E8M0 block scales SA [M, K/32], SB [N, K/32]; program as in gemm_epi."""
+    prog = _program(program)
+    aux = list(aux)
+    arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    _check(lib().coda_gemm_mx(C.byref(prog), _p(A), _p(SA), _p(B), _p(SB), _p(D),
+                              arr if aux else None, len(aux), _stream()))
     return D
 
 

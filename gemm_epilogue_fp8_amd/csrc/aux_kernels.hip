@@ -406,4 +406,75 @@ __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C,
   if (rbase < R) *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
 }
 
+// ---------------------------------------------------------------- MXFP8 (block-scaled E4M3)
+// OCP Microscaling Formats (MX) v1.0, MXFP8 with E4M3 elements: a block of 32
+// consecutive values along the contracted axis shares one E8M0 scale 2^e.
+// e = floor(log2(max |v|)) - 8 (8 = the exponent of E4M3's largest power of
+// two), clamped to [-127, 127]; a block whose max is zero or an fp32
+// subnormal takes -127.  Elements are E4M3(v / 2^e), round to nearest even,
+// saturated at +-448.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int be = (int)((__float_as_uint(amax) >> 23) & 0xFF);   // biased exponent, 0 for zero / subnormal
+  return be == 0 ? -127 : min(max(be - 127 - 8, -127), 127);
+}
+
+// 4 floats scaled by 2^-e (exact) -> 4 E4M3 bytes
+__device__ __forceinline__ uint32_t cvt4_mx(float a, float b, float c, float d, int e) {
+  return cvt4_e4m3(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
+}
+
+// Blocks along the columns: X [R, C] -> Q [R, C], S [R, C / 32] (C % 32 == 0).
+// One wave a row, 8 values a lane, a block = 4 consecutive lanes.
+__global__ void quant_mx_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                     uint8_t* S, int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;                      // r is uniform over the wave
+  for (int c = lane * 8; c < C; c += 512) {
+    // C % 32 == 0: the 4 lanes of a block run the same iterations
+    const uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    float m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, 0.0f))));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int e = mx_exponent(m);
+    const uint32_t lo = cvt4_mx(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), e);
+    const uint32_t hi = cvt4_mx(bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w), e);
+    *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + c) = uint2{lo, hi};
+    if ((lane & 3) == 0) S[(int64_t)r * lds + c / 32] = (uint8_t)(e + 127);
+  }
+}
+
+// Blocks along the rows, written transposed: X [R, C] -> Q^T [C, R],
+// S [C, R / 32] (R % 32 == 0).  A 64 x 64 tile goes through LDS; thread
+// (column cc, part) encodes rows [16 part, 16 part + 16) of its column, and
+// a block is the two parts of one lane pair.
+__global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                       uint8_t* S, int64_t lds) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = r0 + rr, c = c0 + tx;
+    tile[rr][tx] = (r < R && c < C) ? bf2f(X[(int64_t)r * ld + c]) : 0.0f;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    v[k] = tile[part * 16 + k][cc];
+    m = fmaxf(m, fabsf(v[k]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));      // every lane is still active here
+  const int e = mx_exponent(m);
+  const int c = c0 + cc, rbase = r0 + part * 16;
+  if (c >= C || rbase >= R) return;        // R % 32 == 0: rows rbase .. rbase + 15 all exist
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = cvt4_mx(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], e);
+  *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
+  if ((part & 1) == 0) S[(int64_t)c * lds + rbase / 32] = (uint8_t)(e + 127);
+}
+
 }  // namespace coda

@@ -67,5 +67,12 @@ __global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, c
                                   uint8_t* Q, int64_t ldq, float* scale);
 __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
                                     uint8_t* QT, int64_t ldq, float* scale);
+// MXFP8 quantisation (E4M3 elements, one E8M0 scale per 32 values of the
+// contracted axis): blocks along the columns, or along the rows written
+// transposed.
+__global__ void quant_mx_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                     uint8_t* S, int64_t lds);
+__global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                       uint8_t* S, int64_t lds);
 
 }  // namespace coda

@@ -250,33 +250,29 @@ extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, siz
 }
 
 // ======================================================================== generic
-extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
-                                     const coda_mat* B, int32_t transB, const coda_mat* D, const coda_mat* aux,
-                                     uint32_t n_aux, void* stream) {
-  if (!prog) return fail(CODA_ERR_NULL, "gemm_epi: NULL program");
-  if (prog->n_ops == 0 || prog->n_ops > CODA_MAX_EPI_OPS) return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: empty or too long program");
-  TRY(check_mat(A, "A", CODA_BF16, -1, -1));
-  TRY(check_mat(B, "B", CODA_BF16, -1, -1));
-  const int64_t M = transA ? A->cols : A->rows, K = transA ? A->rows : A->cols;
-  const int64_t Kb = transB ? B->cols : B->rows, N = transB ? B->rows : B->cols;
-  if (K != Kb) return fail(CODA_ERR_SHAPE, "gemm_epi: inner sizes %lld and %lld differ", (long long)K, (long long)Kb);
-  const int layout = (transA ? 2 : 0) + (transB ? 1 : 0);
-  // decode the chain
+namespace {
+// Decodes an epilogue program for a product C [M, N] with contracted size K
+// into the compiled program, its epilogue arguments and the shape and type of
+// D.  Checks the program's auxiliary operands.
+coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, int64_t K, const coda_mat* aux,
+                           uint32_t n_aux, const char* who, Prog* p_out, EpiArgs* e_out, int64_t* out_cols,
+                           int* out_dtype) {
+  if (!prog) return fail(CODA_ERR_NULL, "%s: NULL program", who);
+  if (prog->n_ops == 0 || prog->n_ops > CODA_MAX_EPI_OPS)
+    return fail(CODA_ERR_UNSUPPORTED, "%s: empty or too long program", who);
   const coda_epi_op* op = prog->ops;
   const uint32_t n = prog->n_ops;
   auto auxm = [&](uint16_t slot) -> const coda_mat* { return (aux && slot < n_aux) ? &aux[slot] : nullptr; };
   for (uint32_t i = 0; i < n; ++i)
-    if (op[i].flags != 0) return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: op %u has flags set", i);
+    if (op[i].flags != 0) return fail(CODA_ERR_UNSUPPORTED, "%s: op %u has flags set", who, i);
   EpiArgs e = epi0();
-  e.out = D ? D->ptr : nullptr;
-  e.ld_out = D ? D->ld : 0;
   Prog p;
-  int64_t out_cols = N;
-  int out_dtype = CODA_BF16;
+  *out_cols = N;
+  *out_dtype = CODA_BF16;
   if (n == 1 && op[0].op == CODA_EPI_STORE_BF16) {
     p = Prog::Store;
   } else if (n == 1 && op[0].op == CODA_EPI_ACCUM_F32) {
-    p = Prog::StoreF32; e.beta = op[0].fparam; out_dtype = CODA_F32;
+    p = Prog::StoreF32; e.beta = op[0].fparam; *out_dtype = CODA_F32;
   } else if (n == 3 && op[0].op == CODA_EPI_ROW_SCALE && op[1].op == CODA_EPI_COL_SCALE && op[2].op == CODA_EPI_STORE_BF16) {
     p = Prog::RowColStore;
     TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
@@ -292,7 +288,7 @@ extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_ma
     if (n == 3) {
       TRY(check_mat(auxm(op[2].slot), "partials", CODA_F32, coda_partials_cols(N), M));
       if (auxm(op[2].slot)->rows > 1 && auxm(op[2].slot)->ld != M)
-        return fail(CODA_ERR_LAYOUT, "gemm_epi: partials ld must be M");
+        return fail(CODA_ERR_LAYOUT, "%s: partials ld must be M", who);
       e.partial_out = static_cast<float*>(auxm(op[2].slot)->ptr);
     } else {
       p = Prog::Resid;
@@ -300,8 +296,8 @@ extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_ma
   } else if (n == 3 && (op[0].op == CODA_EPI_ROW_SCALE || op[0].op == CODA_EPI_ROW_RMS_FROM_PARTIALS) &&
              op[1].op == CODA_EPI_SWIGLU && op[2].op == CODA_EPI_STORE_BF16) {
     p = Prog::SwiGLU;
-    if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "gemm_epi: SWIGLU needs N % 64 == 0");
-    out_cols = N / 2;
+    if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "%s: SWIGLU needs N %% 64 == 0", who);
+    *out_cols = N / 2;
     if (op[0].op == CODA_EPI_ROW_SCALE) {
       TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
       e.rowvec = fptr(auxm(op[0].slot));
@@ -309,20 +305,112 @@ extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_ma
       const coda_mat* P = auxm(op[0].slot);
       TRY(check_mat(P, "partials", CODA_F32, -1, M));
       if (P->rows < 1 || P->rows > kProloguePartials || P->ld != M)
-        return fail(CODA_ERR_SHAPE, "gemm_epi: partials must be [1..8, M] with ld == M");
+        return fail(CODA_ERR_SHAPE, "%s: partials must be [1..8, M] with ld == M", who);
       e.row_partials = fptr(P);
       e.n_row_partials = (int)P->rows;
       e.norm_dim = (int)K;
       e.eps = op[0].fparam;
     }
   } else {
-    return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: epilogue program not in the compiled set");
+    return fail(CODA_ERR_UNSUPPORTED, "%s: epilogue program not in the compiled set", who);
   }
+  *p_out = p;
+  *e_out = e;
+  return CODA_OK;
+}
+
+// E8M0 block-exponent matrix: one byte per 32 values of the contracted
+// axis; rows of 4-byte words (ld % 4 == 0, pointer 4-byte aligned), since the
+// GEMM moves the exponents of 128 K values as one word.
+coda_status check_scales(const coda_mat* S, const char* name, int64_t rows, int64_t cols) {
+  if (!present(S)) return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
+  if (S->dtype != CODA_E8M0) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected E8M0", name, S->dtype);
+  if (S->rows != rows || S->cols != cols)
+    return fail(CODA_ERR_SHAPE, "%s: %lld x %lld, expected %lld x %lld", name, (long long)S->rows,
+                (long long)S->cols, (long long)rows, (long long)cols);
+  if (reinterpret_cast<uintptr_t>(S->ptr) % 4 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 4-byte aligned", name);
+  if (S->rows > 1 && (S->ld < S->cols || S->ld % 4 != 0))
+    return fail(CODA_ERR_LAYOUT, "%s: ld must be >= cols and a multiple of 4", name);
+  return CODA_OK;
+}
+}  // namespace
+
+extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
+                                     const coda_mat* B, int32_t transB, const coda_mat* D, const coda_mat* aux,
+                                     uint32_t n_aux, void* stream) {
+  if (!prog) return fail(CODA_ERR_NULL, "gemm_epi: NULL program");
+  TRY(check_mat(A, "A", CODA_BF16, -1, -1));
+  TRY(check_mat(B, "B", CODA_BF16, -1, -1));
+  const int64_t M = transA ? A->cols : A->rows, K = transA ? A->rows : A->cols;
+  const int64_t Kb = transB ? B->cols : B->rows, N = transB ? B->rows : B->cols;
+  if (K != Kb) return fail(CODA_ERR_SHAPE, "gemm_epi: inner sizes %lld and %lld differ", (long long)K, (long long)Kb);
+  const int layout = (transA ? 2 : 0) + (transB ? 1 : 0);
+  Prog p;
+  EpiArgs e;
+  int64_t out_cols;
+  int out_dtype;
+  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_epi", &p, &e, &out_cols, &out_dtype));
   if (p != Prog::Store && p != Prog::StoreF32 && layout != LAYOUT_NN)
     return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: this program is compiled for transA = transB = 0 only");
   TRY(check_mat(D, "D", out_dtype, M, out_cols));
+  e.out = D->ptr;
+  e.ld_out = D->ld;
   GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
   return launched(launch_gemm(p, layout, false, g, e, S(stream)), "gemm_epi");
+}
+
+// ======================================================================== MXFP8
+extern "C" coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* Sc,
+                                           void* stream) {
+  TRY(check_mat(X, "X", CODA_BF16, -1, -1));
+  if (axis != 0 && axis != 1) return fail(CODA_ERR_VALUE, "axis must be 0 or 1");
+  const int64_t R = X->rows, C = X->cols;
+  const int64_t L = axis == 1 ? C : R;     // length of the blocked (contracted) axis
+  if (L % 32 != 0) return fail(CODA_ERR_SHAPE, "quantize_mxfp8: the blocked axis (%lld) must be a multiple of 32",
+                               (long long)L);
+  const int64_t rows = axis == 1 ? R : C;
+  TRY(check_mat(Q, "Q", CODA_E4M3, rows, L));
+  TRY(check_scales(Sc, "S", rows, L / 32));
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X->ptr);
+  uint8_t* q = static_cast<uint8_t*>(Q->ptr);
+  uint8_t* sc = static_cast<uint8_t*>(Sc->ptr);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, S(stream), x, X->ld,
+                       (int)R, (int)C, q, Q->ld, sc, Sc->ld);
+  else
+    hipLaunchKernelGGL(quant_mx_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)), dim3(256),
+                       0, S(stream), x, X->ld, (int)R, (int)C, q, Q->ld, sc, Sc->ld);
+  return check_launch("quantize_mxfp8");
+}
+
+extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
+                                    const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
+                                    uint32_t n_aux, void* stream) {
+  if (!prog) return fail(CODA_ERR_NULL, "gemm_mx: NULL program");
+  TRY(check_mat(A, "A", CODA_E4M3, -1, -1));
+  TRY(check_mat(B, "B", CODA_E4M3, -1, -1));
+  const int64_t M = A->rows, K = A->cols, N = B->rows;
+  if (B->cols != K) return fail(CODA_ERR_SHAPE, "gemm_mx: inner sizes %lld and %lld differ", (long long)K,
+                                (long long)B->cols);
+  if (K <= 0 || K % 128 != 0) return fail(CODA_ERR_SHAPE, "gemm_mx: K (%lld) must be a positive multiple of 128",
+                                          (long long)K);
+  TRY(check_scales(SA, "SA", M, K / 32));
+  TRY(check_scales(SB, "SB", N, K / 32));
+  Prog p;
+  EpiArgs e;
+  int64_t out_cols;
+  int out_dtype;
+  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_mx", &p, &e, &out_cols, &out_dtype));
+  TRY(check_mat(D, "D", out_dtype, M, out_cols));
+  e.out = D->ptr;
+  e.ld_out = D->ld;
+  GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
+  g.sA = SA->ptr;
+  g.sB = SB->ptr;
+  g.lds_a = SA->rows > 1 ? SA->ld : SA->cols;
+  g.lds_b = SB->rows > 1 ? SB->ld : SB->cols;
+  return launched(launch_gemm_mx(p, g, e, S(stream)), "gemm_mx");
 }
 
 // ======================================================================== functional forward

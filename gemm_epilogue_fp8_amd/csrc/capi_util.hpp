@@ -125,6 +125,8 @@ GemmArgs gemm_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
   g.tiles_m = g.tiles_n = 0;
   g.kchunk = (int)K;
+  g.sA = g.sB = nullptr;
+  g.lds_a = g.lds_b = 0;
   return g;
 }
 

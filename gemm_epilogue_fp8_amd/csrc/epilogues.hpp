@@ -282,7 +282,7 @@ __device__ __forceinline__ void store_f32_tile(const EpiArgs& e, const Ctx<Cfg>&
 // acc <- acc * s_row[m] * s_col[n] (the per-token and per-channel E4M3 scales)
 template <class Cfg>
 __device__ __forceinline__ void apply_fp8_scales(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc) {
-  if constexpr (Cfg::FP8) {
+  if constexpr (Cfg::FP8 && !Cfg::MX) {   // MXFP8 blocks are scaled inside the MFMA
     float sr[Cfg::TM];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) sr[i] = e.rowscale[c.rowc(i)];
@@ -1015,6 +1015,10 @@ __global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e)
     g.K = min(g.kchunk, g.K - kb);
     g.A = static_cast<const char*>(g.A) + (Cfg::A_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.lda * Cfg::ESIZE);
     g.B = static_cast<const char*>(g.B) + (Cfg::B_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.ldb * Cfg::ESIZE);
+    if constexpr (Cfg::MX) {   // kchunk is a multiple of 128: whole scale words
+      g.sA = static_cast<const char*>(g.sA) + kb / 32;
+      g.sB = static_cast<const char*>(g.sB) + kb / 32;
+    }
     e.out = static_cast<float*>(e.out) + blockIdx.y * e.split_stride;
     if (e.partial_out) e.partial_out += blockIdx.y * e.split_pstride;
   }

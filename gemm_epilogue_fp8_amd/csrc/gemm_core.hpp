@@ -1,6 +1,10 @@
 // The fixed GEMM mainloop: C[M,N] (fp32) = sum_k A[m,k] B[k,n] on gfx950
 // matrix cores, bf16 (v_mfma_f32_32x32x16_bf16) or OCP E4M3
-// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales).
+// (v_mfma_scale_f32_32x32x64_f8f6f4), the latter either with unit block
+// scales (per-row / per-column scales are applied by the epilogue) or with
+// one E8M0 power-of-two scale per 32 consecutive K values of every row of A
+// and every column of B (MXFP8, the OCP Microscaling format), applied by the
+// matrix core itself.
 //
 // The CODA paper (arXiv 2605.19269), §2.2 and §3.1, keeps an expert-tuned
 // mainloop fixed and programs only the epilogue; this file is that fixed part.
@@ -54,8 +58,19 @@
 //    8-byte bf16 stores and in-lane pairwise transforms (RoPE pairs).
 //  * Workgroup ids are remapped so that the tiles one XCD (8 per chip, each
 //    with its own L2) runs are neighbours, then grouped along M.
+//  * MXFP8 block scales travel like the tiles: the E8M0 bytes of one stage
+//    pair (128 K = 4 blocks) are one 4-byte word per operand row, copied
+//    global->LDS beside the pair (buffer_load_dword ... lds, one wave
+//    instruction covers 64 rows) into two 2 KB slots, read in the memory
+//    phase with the fragments and handed to the MFMA as its per-lane scale
+//    operand.  A lane of the 32x32x64 MFMA supplies 16 K values of each of
+//    the two 32-value blocks of its row, and the scale operand of lane
+//    l holds the scale of block l >> 5 of row l % 32 (lane layout probed on
+//    MI355X with one-hot operands and lane-distinct scales); the
+//    instruction's byte select picks the block of stage 0 or 1 of the pair.
 #pragma once
 #include <type_traits>
+#include <utility>
 #include "coda_device.hpp"
 
 namespace coda {
@@ -65,7 +80,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-// global -> LDS, 16 bytes a lane, lane l at lds + 16 l (lds is wave-uniform)
+// global -> LDS, `size` (16 or 4) bytes a lane, lane l at lds + size l (lds is wave-uniform)
 __device__ void raw_ptr_buffer_load_lds(__amdgpu_buffer_rsrc_t rsrc, lds_void_t* lds, int size, int voffset,
                                         int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.lds");
 
@@ -78,21 +93,26 @@ __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
   return (uint32_t)(row * kRowBytes + ((chunk ^ kc_swz(row)) << 4));
 }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool A_KC_, bool B_KC_, bool FP8_ = false>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool A_KC_, bool B_KC_, bool FP8_ = false,
+          bool MX_ = false>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NWAVES = WAVES_M * WAVES_N, T = 64 * NWAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr bool A_KC = A_KC_, B_KC = B_KC_, FP8 = FP8_;
+  static constexpr bool A_KC = A_KC_, B_KC = B_KC_, FP8 = FP8_, MX = MX_;
   static constexpr int ESIZE = FP8 ? 1 : 2;
   static constexpr int BK = kRowBytes / ESIZE;     // K per stage: 32 bf16 or 64 fp8
   static constexpr int NS = 4;                     // LDS stages
   static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  // MXFP8: two slots of (BM + BN) 4-byte scale words after the stages
+  static constexpr int SCALE_OFF = NS * STAGE_BYTES;
+  static constexpr int SCALE_SLOT = (BM + BN) * 4;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + (MX ? 2 * SCALE_SLOT : 0);
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(WAVES_M == 2, "the two wave groups are the two row halves of the tile");
   static_assert(!FP8 || (A_KC && B_KC), "fp8 operands are K-contiguous");
+  static_assert(!MX || FP8, "block scales come with E4M3 operands");
 };
 
 struct GemmArgs {
@@ -102,6 +122,11 @@ struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;
   int kchunk;      // split K: workgroup (x, y) runs K slice [y kchunk, (y + 1) kchunk); gridDim.y slices
+  // MXFP8 only: E8M0 block exponents, [M, K / 32] and [N, K / 32] bytes
+  // (row strides lds_a, lds_b bytes, multiples of 4; K a multiple of 128)
+  const void* sA;
+  const void* sB;
+  int64_t lds_a, lds_b;
 };
 
 // ---------------------------------------------------------------- operand tiles
@@ -113,19 +138,26 @@ struct TileKC {
   static constexpr int NI = R * kRowBytes / 1024 / Cfg::WAVES_N;   // 1 KB wave instructions per wave
   static_assert(R * kRowBytes % (1024 * Cfg::WAVES_N) == 0, "tile must split into 1 KB wave loads");
 
+  // One lane offset serves every instruction: a lane reads row lane / 4 of
+  // a 16-row group and the chunk that lives at its slot, which does not
+  // depend on the group.  The group's first row moves into the buffer
+  // resource (base and record count, scalar arithmetic), whose range check
+  // turns rows past the matrix into zeros; K-tail chunks get the
+  // out-of-range offset.  Keeping one vector register instead of one per
+  // instruction matters to kernels that use all 256.
   __device__ __forceinline__ static void issue(const char* base, int64_t ld_bytes, int row0, int nrows,
                                                int64_t kbyte0, int64_t kbytes, char* lds, int w, int lane) {
-    const char* p = base + (int64_t)row0 * ld_bytes + kbyte0;
-    const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld_bytes + (uint64_t)(kbytes - kbyte0);
-    const auto rs = make_rsrc(p, rem);
+    const int rl = lane >> 2;
+    const int chunk = (lane & 3) ^ ((rl >> 2) & 3);    // = the chunk of row 16 q + rl at this slot, any q
+    const uint32_t voff = (kbyte0 + chunk * 16 < kbytes) ? (uint32_t)(rl * ld_bytes + chunk * 16) : kOobOffset;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q = NI * w + i;                        // 16 rows per instruction; wave w: rows [R/4 w, R/4 (w+1))
-      const int row = 16 * q + (lane >> 2);
-      const int chunk = (lane & 3) ^ kc_swz(row);      // the chunk that lives at this slot
-      const bool ok = (row0 + row < nrows) && (kbyte0 + chunk * 16 < kbytes);
-      const uint32_t off = ok ? (uint32_t)(row * ld_bytes + chunk * 16) : kOobOffset;
-      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)off, 0, 0, 0);
+      const int r0 = row0 + 16 * q;
+      // bytes from the group's first row to the end of the last row's K range
+      const int64_t rem = (int64_t)(nrows - r0 - 1) * ld_bytes + (kbytes - kbyte0);
+      const auto rs = make_rsrc(base + (int64_t)r0 * ld_bytes + kbyte0, rem > 0 ? (uint64_t)rem : 0);
+      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)voff, 0, 0, 0);
     }
   }
 };
@@ -220,11 +252,15 @@ constexpr int substeps() { return Cfg::FP8 ? 1 : 2; }
 template <class Cfg, bool KC, int R>
 __device__ __forceinline__ typename Frags<Cfg>::T read_frag(const char* tile, int r0, int s, int lane) {
   if constexpr (Cfg::FP8) {
+    // K bytes [16 h, 16 h + 16) and [32 + 16 h, 32 + 16 h + 16) of the row,
+    // h = lane >> 5: the matrix core reads a lane's first 16 bytes as part of
+    // K block 0 (of 32) and its last 16 as part of block 1, and scales block
+    // b of row l % 32 with the scale operand of lane l % 32 + 32 b
     const int row = r0 + (lane & 31);
-    const int chunk = 2 * (lane >> 5);
+    const int h = lane >> 5;
     (void)s;
-    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, chunk));
-    i32x4_t up = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, chunk + 1));
+    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, h));
+    i32x4_t up = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 + h));
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
   } else if constexpr (KC) {
     return *reinterpret_cast<const bf16x8_t*>(tile + lds_off(r0 + (lane & 31), 2 * s + (lane >> 5)));
@@ -255,6 +291,58 @@ __device__ __forceinline__ void mma_frags(const Frags<Cfg>& f, Acc<Cfg>& acc) {
         acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc.c[i][j],
                                                                        0, 0, 0, 127, 0, 127);
     }
+}
+
+// MXFP8: per-lane scale bytes of one stage pair, two operand tiles a
+// register: word t of A holds (tile 2t, stage 0), (tile 2t + 1, stage 0),
+// (tile 2t, stage 1), (tile 2t + 1, stage 1) in bytes 0..3, and likewise B.
+// The MFMA's byte select then picks tile and stage with no further moves.
+template <class Cfg>
+struct Scales {
+  static_assert(Cfg::TM % 2 == 0 && Cfg::TN == 2, "scale bytes are packed two tiles a word");
+  int a[Cfg::TM / 2], b[Cfg::TN / 2];
+};
+
+// two rows' words (bytes = blocks 4p .. 4p + 3) -> the packed word of the
+// lane's K half h: blocks h (stage 0) and 2 + h (stage 1) of each row
+__device__ __forceinline__ int pack_scales(uint32_t w0, uint32_t w1, int sh) {
+  return (int)(((w0 >> sh) & 0x00FF00FFu) | (((w1 >> sh) & 0x00FF00FFu) << 8));
+}
+
+template <class Cfg>
+__device__ __forceinline__ void load_scales(const char* slot, Scales<Cfg>& sc, int wm0, int wn0, int lane) {
+  // slot: BM words of A rows, then BN words of B rows
+  const int sh = 8 * (lane >> 5);
+  auto word = [&](int row) { return *reinterpret_cast<const uint32_t*>(slot + 4 * (row + (lane & 31))); };
+#pragma unroll
+  for (int t = 0; t < Cfg::TM / 2; ++t) sc.a[t] = pack_scales(word(wm0 + 64 * t), word(wm0 + 64 * t + 32), sh);
+#pragma unroll
+  for (int t = 0; t < Cfg::TN / 2; ++t)
+    sc.b[t] = pack_scales(word(Cfg::BM + wn0 + 64 * t), word(Cfg::BM + wn0 + 64 * t + 32), sh);
+}
+
+// One MFMA of stage S with block scales; the byte selects are immediates, so
+// tile indices are template arguments.  Operands swapped as in mma_frags:
+// B's scale goes with the instruction's first operand.
+template <class Cfg, int S, int I, int J>
+__device__ __forceinline__ void mma_mx_one(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc) {
+  acc.c[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[J], f.a[I], acc.c[I][J], 0, 0,
+                                                                2 * S + (J & 1), sc.b[J >> 1],
+                                                                2 * S + (I & 1), sc.a[I >> 1]);
+}
+template <class Cfg, int S, int I, int... J>
+__device__ __forceinline__ void mma_mx_row(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc,
+                                           std::integer_sequence<int, J...>) {
+  (mma_mx_one<Cfg, S, I, J>(f, sc, acc), ...);
+}
+template <class Cfg, int S, int... I>
+__device__ __forceinline__ void mma_mx_all(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc,
+                                           std::integer_sequence<int, I...>) {
+  (mma_mx_row<Cfg, S, I>(f, sc, acc, std::make_integer_sequence<int, Cfg::TN>{}), ...);
+}
+template <class Cfg, int S>
+__device__ __forceinline__ void mma_frags_mx(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc) {
+  mma_mx_all<Cfg, S>(f, sc, acc, std::make_integer_sequence<int, Cfg::TM>{});
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
@@ -325,14 +413,35 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
         TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, k0, g.K, n0, g.N, Bs, w, lane);
     }
   };
-  auto issue_pair = [&](int p) { issue_stage(2 * p); issue_stage(2 * p + 1); };
+  // MXFP8: the 4 block exponents (one word) of stage pair p for rows
+  // [64 w, 64 w + 64) of this group's operand tile; wave w of group 1 copies
+  // the words of exactly the B rows that wave w of each group reads
+  auto issue_scales = [&](int p) {
+    if constexpr (Cfg::MX) {
+      const bool a = grp == 0;
+      const char* base = static_cast<const char*>(a ? g.sA : g.sB);
+      const int64_t ld = a ? g.lds_a : g.lds_b;
+      const int row0 = a ? m0 : n0, nrows = a ? g.M : g.N;
+      const int r = 64 * w + lane;
+      const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld + (uint64_t)(g.K / 32);
+      const auto rs = make_rsrc(base + (int64_t)row0 * ld, rem);
+      const uint32_t off = (row0 + r < nrows) ? (uint32_t)(r * ld + 4 * p) : kOobOffset;
+      char* dst = smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT + (a ? 0 : 4 * Cfg::BM) + 256 * w;
+      raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (int)off, 0, 0, 0);
+    }
+  };
+  auto issue_pair = [&](int p) { issue_stage(2 * p); issue_stage(2 * p + 1); issue_scales(p); };
+  // copies a wave issues per stage pair
+  constexpr int PAIR_LOADS = 2 * LPS + (Cfg::MX ? 1 : 0);
+  static_assert(!Cfg::MX || (Cfg::BM == 256 && Cfg::BN == 256 && Cfg::WAVES_N == 4),
+                "one 64-row scale instruction per wave covers a 256-row tile");
 
   // prologue: group 0 copies the A tiles of pair 0, group 1 the B tiles of
   // pairs 0 and 1; pair 0 must land
   issue_pair(0);
   if (grp == 1 && np > 1) {
     issue_pair(1);
-    wait_vmcnt<2 * LPS>();
+    wait_vmcnt<PAIR_LOADS>();
   } else {
     wait_vmcnt<0>();
   }
@@ -348,6 +457,8 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S0, S0 + Cfg::BM * kRowBytes, s, f[s], wm0, wn0, lane);
 #pragma unroll
     for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, f[SUB + s], wm0, wn0, lane);
+    Scales<Cfg> sc;
+    if constexpr (Cfg::MX) load_scales<Cfg>(smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT, sc, wm0, wn0, lane);
     // Pair p + 1 must land before the barrier that ends the phase in which
     // group 1 reads pair p (group 0 reads pair p + 1 in the next one).
     if (grp == 0) {
@@ -363,15 +474,20 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
       wait_lgkmcnt0();
       if (p + 2 < np) {
         issue_pair(p + 2);
-        wait_vmcnt<2 * LPS>();             // pair p + 1 has landed
+        wait_vmcnt<PAIR_LOADS>();          // pair p + 1 has landed
       } else {
         wait_vmcnt<0>();
       }
     }
     phase_barrier();
     // ---- compute phase
+    if constexpr (Cfg::MX) {
+      mma_frags_mx<Cfg, 0>(f[0], sc, acc);
+      mma_frags_mx<Cfg, 1>(f[1], sc, acc);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 2 * SUB; ++s) mma_frags<Cfg>(f[s], acc);
+      for (int s = 0; s < 2 * SUB; ++s) mma_frags<Cfg>(f[s], acc);
+    }
     if (grp == 0) wait_vmcnt<0>();         // A of pair p + 1 has landed
     phase_barrier();
   }

@@ -62,7 +62,9 @@ typedef enum coda_status {
   CODA_ERR_VALUE = 9        /* an invalid scalar argument */
 } coda_status;
 
-typedef enum coda_dtype { CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4 } coda_dtype;
+/* CODA_E8M0: one byte 2^(code - 127) (code 255 = NaN, never written here),
+ * the shared block scale of the OCP Microscaling (MX) formats. */
+typedef enum coda_dtype { CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4, CODA_E8M0 = 5 } coda_dtype;
 
 /* GEMM operand precision of the functional entry points. */
 typedef enum coda_precision {
@@ -175,6 +177,44 @@ int64_t coda_partials_cols(int64_t N);
 coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
                           const coda_mat* B, int32_t transB, const coda_mat* D,
                           const coda_mat* aux, uint32_t n_aux, void* stream);
+
+/* ===================================================================== MXFP8 block-scaled operands */
+
+/* The CODA paper (§1) names the move of GEMM operands to 8- and 4-bit types
+ * as one reason epilogue work grows in relative cost; gfx950's scaled MFMA
+ * takes the block-scaled form of the OCP Microscaling Formats (MX) v1.0
+ * specification, MXFP8 with E4M3 elements: every block of 32 consecutive
+ * values along the contracted axis shares one E8M0 scale 2^e, and the
+ * value the block stands for is 2^e * E4M3 element.
+ *
+ * Quantiser.  X: bf16 [R, C].  For each block with absolute max a:
+ *   e = floor(log2 a) - 8, clamped to [-127, 127] (-127 when a is 0 or an
+ *   fp32 subnormal);  element = E4M3(x / 2^e), round to nearest even,
+ *   saturated at +-448.
+ *   axis = 1: blocks along C:  Q E4M3 [R, C],  S E8M0 [R, C / 32]; C % 32 == 0
+ *   axis = 0: blocks along R, written transposed (the contracted axis
+ *             contiguous):     Q E4M3 [C, R],  S E8M0 [C, R / 32]; R % 32 == 0
+ * S byte = e + 127.  S needs a 4-byte aligned pointer and ld % 4 == 0 (it
+ * may be a uint8 tensor); Q follows the E4M3 rules above.  No workspace.
+ * Errors: CODA_ERR_SHAPE when the blocked axis is not a multiple of 32. */
+coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
+                                void* stream);
+
+/* D = epilogue(sum_k A~[m, k] B~[n, k]) with MXFP8 operands
+ *   A~ = A (E4M3 [M, K]) scaled by SA (E8M0 [M, K / 32]),
+ *   B~ = B (E4M3 [N, K], i.e. the second operand stored with K contiguous)
+ *        scaled by SB (E8M0 [N, K / 32]);
+ * products and sums in fp32 on the matrix cores, the block scales applied
+ * by the scaled MFMA.  K must be a positive multiple of 128 (the exponents
+ * of 128 K values travel as one 4-byte word).  The epilogue program is any of
+ * the chains coda_gemm_epi compiles (STORE_BF16, ACCUM_F32, ROW_SCALE
+ * COL_SCALE STORE_BF16, ADD_TILE STORE_BF16 [ROW_SUMSQ_PARTIAL], the two
+ * SWIGLU chains), with D shaped as there.  Errors as coda_gemm_epi, plus
+ * CODA_ERR_DTYPE / CODA_ERR_SHAPE / CODA_ERR_ALIGN / CODA_ERR_LAYOUT for the
+ * scale matrices. */
+coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
+                         const coda_mat* B, const coda_mat* SB, const coda_mat* D,
+                         const coda_mat* aux, uint32_t n_aux, void* stream);
 
 /* ===================================================================== functional: forward */
 

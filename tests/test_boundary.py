@@ -132,3 +132,35 @@ def test_workspace_queries():
     assert L.coda_linear_cross_entropy_bwd_workspace(8192, 2048, 128256, 1024, 0, C.byref(n)) == 0
     assert n.value >= 1024 * 128256 * 2
     assert g.partials_cols(128256) == 501 and g.partials_cols(1) == 1
+
+
+def test_mx_validation_codes():
+    """MXFP8 entry points: block-multiple sizes, E8M0 scale shapes, dtype and
+    4-byte layout, checked before any HIP call."""
+    L = g.lib()
+    BF, E4, E8 = _lib.CODA_BF16, _lib.CODA_E4M3, _lib.CODA_E8M0
+    q = lambda X, axis, Q, S: L.coda_quantize_mxfp8(C.byref(X), axis, C.byref(Q), C.byref(S), None)
+    assert q(fake(BF, 40, 48), 1, fake(E4, 40, 48), fake(E8, 40, 1)) == 3      # 48 not a multiple of 32
+    assert q(fake(BF, 40, 64), 0, fake(E4, 64, 40), fake(E8, 64, 1)) == 3      # 40 rows: not a multiple of 32
+    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 3, ld=4)) == 3   # wrong scale count
+    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E4, 40, 2, ld=16)) == 2  # scale dtype
+    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 2, ld=6)) == 4   # ld not a multiple of 4
+    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 2, ld=4, ptr=FAKE + 2)) == 5
+    assert q(fake(BF, 40, 64), 2, fake(E4, 40, 64), fake(E8, 40, 2, ld=4)) == 9   # axis
+
+    prog = _lib.EpiProgram()
+    prog.n_ops = 1
+    prog.ops[0].op = _lib.EPI_STORE_BF16
+    gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
+                                                C.byref(D), None, 0, None)
+    M, N = 64, 32
+    assert gm(fake(E4, M, 192), fake(E8, M, 6, ld=8), fake(E4, N, 192), fake(E8, N, 6, ld=8),
+              fake(BF, M, N)) == 3                                             # K = 192: not a multiple of 128
+    assert gm(fake(E4, M, 256), fake(E8, M, 8), fake(E4, N, 128), fake(E8, N, 4),
+              fake(BF, M, N)) == 3                                             # inner sizes differ
+    assert gm(fake(E4, M, 256), fake(E8, M, 4), fake(E4, N, 256), fake(E8, N, 8),
+              fake(BF, M, N)) == 3                                             # SA is not [M, K/32]
+    assert gm(fake(BF, M, 256), fake(E8, M, 8), fake(E4, N, 256), fake(E8, N, 8),
+              fake(BF, M, N)) == 2                                             # A not E4M3
+    assert gm(fake(E4, M, 256), fake(E8, M, 8), fake(E4, N, 256), fake(E8, N, 8),
+              fake(BF, M, N + 8)) == 3                                         # D shape

@@ -1,0 +1,231 @@
+"""GPU parity of the MXFP8 path (E4M3 elements with one E8M0 scale per 32
+values of the contracted axis, OCP Microscaling v1.0) through the C ABI:
+the quantiser bit for bit against oracle/mx.py, and the block-scaled GEMM
+with each compiled epilogue against the oracle's float64 product of the
+dequantised operands."""
+import numpy as np
+import pytest
+
+import coda_inputs as ci
+from oracle import block as ob
+from oracle import mx
+from oracle import numerics as nm
+from oracle import ops
+from tests.helpers import assert_bf16, assert_grad, to_dev, to_np, unpack_gu
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gemm_epilogue_fp8_amd as coda  # noqa: E402
+
+BF = torch.bfloat16
+DEV = "cuda"
+FINITE_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def bf(a):
+    return to_dev(np.asarray(a, np.float32), BF)
+
+
+def f32(a):
+    return to_dev(np.asarray(a, np.float32))
+
+
+def u8(a):
+    return to_dev(np.ascontiguousarray(a, dtype=np.uint8))
+
+
+def e4m3_dev(codes):
+    return u8(codes).view(torch.float8_e4m3fn)
+
+
+def varied_bf16(rng, R, C, axis):
+    """bf16 values whose magnitude changes by powers of two from block to
+    block along `axis`, with one all-zero block and one block of large values,
+    so that the shared exponents cover a wide range."""
+    X = rng.standard_normal((R, C)).astype(np.float32)
+    if axis == 1:
+        X *= np.exp2(rng.integers(-24, 24, size=(R, C // 32))).repeat(32, axis=1).astype(np.float32)
+        X[0, :32] = 0.0
+        X[-1, -32:] *= np.float32(2.0 ** 60)
+    else:
+        X *= np.exp2(rng.integers(-24, 24, size=(R // 32, C))).repeat(32, axis=0).astype(np.float32)
+        X[:32, 0] = 0.0
+        X[-32:, -1] *= np.float32(2.0 ** 60)
+    return ci.to_bf16_values(X)
+
+
+# ------------------------------------------------------------------ quantiser
+@pytest.mark.parametrize("axis,R,C", [(1, 37, 320), (1, 1, 32), (0, 320, 72), (0, 96, 200)])
+def test_quantize_mxfp8_bit_exact(axis, R, C):
+    rng = np.random.default_rng(R * 7 + C + axis)
+    X = varied_bf16(rng, R, C, axis)
+    Q, S = coda.quantize_mxfp8(bf(X), axis)
+    torch.cuda.synchronize()
+    P, e = mx.quantize(X if axis == 1 else X.T.copy())
+    assert np.array_equal(Q.view(torch.uint8).cpu().numpy(), mx.codes(P))
+    assert np.array_equal(S.cpu().numpy(), mx.e8m0_codes(e))
+
+
+def test_quantize_mxfp8_rejects_ragged_blocks():
+    X = torch.zeros((40, 48), dtype=BF, device=DEV)
+    with pytest.raises(coda.CodaError):
+        coda.quantize_mxfp8(X, 1)
+    with pytest.raises(coda.CodaError):
+        coda.quantize_mxfp8(X, 0)
+
+
+# ------------------------------------------------------------------ GEMM
+def random_mx(rng, rows, K, emin=117, emax=137):
+    """An MXFP8 operand drawn directly: uniform finite E4M3 codes and E8M0
+    codes uniform in [emin, emax] (2^-10 .. 2^10), independent per block."""
+    codes = rng.choice(FINITE_CODES, size=(rows, K))
+    scales = rng.integers(emin, emax + 1, size=(rows, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def mx_values(codes, scales):
+    """float64 values an MXFP8 operand stands for (oracle decode)."""
+    return mx.dequantize(nm.e4m3_decode(codes), scales.astype(np.int64) - 127)
+
+
+def mfma_fp8_bound(A, B):
+    """Bound on the difference between the matrix core's sum of
+    sum_k A[m,k] B[n,k] and the exact sum: 2^-10 sum_k |A B|.  The E4M3
+    MFMA does not round like a sequence of fp32 additions: on MI355X its
+    error, with unit scales and with block scales alike, reaches about
+    5000 u sum_k |A B| (u = 2^-24, K = 384), i.e. 3e-4 sum_k |A B|, and
+    5e-5 norm-wise; products of two E4M3 values times powers of two are
+    exact, so only the accumulation contributes."""
+    return 2.0 ** -10 * (np.abs(A) @ np.abs(B).T)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 384), (517, 520, 1024), (64, 8, 128)])
+def test_gemm_mx_accum_and_store(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    ca, sa = random_mx(rng, M, K)
+    cb, sb = random_mx(rng, N, K)
+    A, B = mx_values(ca, sa), mx_values(cb, sb)
+    ref = A @ B.T
+    prior = ci.fp32_prior((M, N), 4)
+    D32 = f32(prior)
+    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 1.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D32)
+    D16 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx([(coda.EPI_STORE_BF16, 0, 0.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D16)
+    torch.cuda.synchronize()
+    bound = mfma_fp8_bound(A, B)
+    got32 = to_np(D32).astype(np.float64) - prior
+    # the prior add is one more fp32 rounding
+    assert np.all(np.abs(got32 - ref) <= bound + 2.0 ** -23 * (np.abs(ref) + np.abs(prior))), \
+        float(np.max(np.abs(got32 - ref) - bound))
+    got16 = to_np(D16).astype(np.float64)
+    assert np.all(np.abs(got16 - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), \
+        float(np.max(np.abs(got16 - ref) - bound))
+    assert np.linalg.norm(got32 - ref) <= 1e-3 * np.linalg.norm(ref)
+    # elementwise |d| / (1 + |ref|) means little at these magnitudes (block
+    # scales 2^-10 .. 2^10 and cancelling sums); the bound above is per element
+    assert np.linalg.norm(got16 - nm.bf16(ref)) <= 3e-3 * np.linalg.norm(ref)
+
+
+def test_gemm_mx_one_scale_per_block():
+    """Scales that differ only between the four blocks of one 128-K word and
+    between rows: a scale taken from the wrong block, stage or row moves the
+    result by a power of two."""
+    rng = np.random.default_rng(17)
+    M, N, K = 256, 256, 256
+    ca, _ = random_mx(rng, M, K)
+    cb, _ = random_mx(rng, N, K)
+    sa = (120 + (np.arange(K // 32)[None, :] * 3 + np.arange(M)[:, None]) % 15).astype(np.uint8)
+    sb = (121 + (np.arange(K // 32)[None, :] * 5 + 2 * np.arange(N)[:, None]) % 13).astype(np.uint8)
+    A, B = mx_values(ca, sa), mx_values(cb, sb)
+    D32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 0.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D32)
+    torch.cuda.synchronize()
+    ref = A @ B.T
+    assert np.all(np.abs(to_np(D32) - ref) <= mfma_fp8_bound(A, B))
+    assert np.linalg.norm(to_np(D32) - ref) <= 1e-3 * np.linalg.norm(ref)
+
+
+def test_gemm_mx_epilogues_from_bf16():
+    """bf16 inputs quantised by the library and by the oracle (bit-exact, as
+    tested above), then the row/column-scale, residual + sum-of-squares and
+    SwiGLU programs on the block-scaled product."""
+    rng = np.random.default_rng(23)
+    M, N, K = 300, 576, 384
+    a = ci.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    W = ci.to_bf16_values((rng.standard_normal((K, N)) * K ** -0.5).astype(np.float32))
+    Qa, Sa = coda.quantize_mxfp8(bf(a), 1)
+    Qw, Sw = coda.quantize_mxfp8(bf(W), 0)          # [N, K]: K contiguous
+    Pa, ea = mx.quantize(a)
+    Pw, ew = mx.quantize(W.T.copy())
+    acc = mx.matmul_nt(Pa, ea, Pw, ew)
+    bound = mfma_fp8_bound(mx.dequantize(Pa, ea), mx.dequantize(Pw, ew))
+
+    rv = rng.uniform(0.5, 2, M).astype(np.float32)
+    cv = rng.uniform(0.5, 2, N).astype(np.float32)
+    D1 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_COL_SCALE, 1, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)],
+                 Qa, Sa, Qw, Sw, D1, aux=[f32(rv), f32(cv)])
+    Z = ci.to_bf16_values(rng.standard_normal((M, N)).astype(np.float32))
+    nT = coda.partials_cols(N)
+    P = torch.empty((nT, M), dtype=torch.float32, device=DEV)
+    D2 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0), (coda.EPI_ROW_SUMSQ_PARTIAL, 1, 0.0)],
+                 Qa, Sa, Qw, Sw, D2, aux=[bf(Z), P])
+    r = rng.uniform(0.5, 2, M).astype(np.float32)
+    D3 = torch.empty((M, N // 2), dtype=BF, device=DEV)
+    coda.gemm_mx([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_SWIGLU, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)],
+                 Qa, Sa, Qw, Sw, D3, aux=[f32(r)])
+    torch.cuda.synchronize()
+
+    # codes on both sides agree, so what is left is the matrix core's
+    # accumulation and the epilogue's fp32 roundings before the bf16 store
+    sref = (acc * rv[:, None]) * cv[None, :]
+    sbound = bound * rv[:, None] * cv[None, :]
+    assert np.all(np.abs(to_np(D1).astype(np.float64) - sref) <= 1.01 * sbound + 2.0 ** -8 * np.abs(sref))
+    assert_bf16("scaled", to_np(D1), nm.bf16((acc * rv[:, None]) * cv[None, :]))
+    y = nm.bf16(Z + acc)
+    assert_bf16("residual", to_np(D2), y)
+    assert_grad("sumsq partials", to_np(P), ob.tile_partials(y.astype(np.float64) ** 2, 256))
+    hg, hu = unpack_gu(r[:, None] * acc)
+    assert_bf16("swiglu", to_np(D3), nm.bf16(ops.swiglu(hg, hu)))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_gemm_mx_full_size_sampled():
+    """The hidden-8192 down-projection shape (M 4096, K 28672, N 8192) with
+    residual: the library quantises a and W; 128 sampled outputs are
+    recomputed by the oracle from its own MXFP8 copies of the sampled rows of
+    a and columns of W (whose codes must equal the library's bit for bit)."""
+    M, K, N = 4096, 28672, 8192
+    rng = np.random.default_rng(71)
+    a = ci.to_bf16_values(rng.standard_normal((M, K), dtype=np.float32))
+    W = ci.to_bf16_values(rng.standard_normal((K, N), dtype=np.float32) * np.float32(K ** -0.5))
+    z = ci.to_bf16_values(rng.standard_normal((M, N), dtype=np.float32))
+    ag, Wg, zg = bf(a), bf(W), bf(z)
+    Qa, Sa = coda.quantize_mxfp8(ag, 1)
+    Qw, Sw = coda.quantize_mxfp8(Wg, 0)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)], Qa, Sa, Qw, Sw, out, aux=[zg])
+    torch.cuda.synchronize()
+    ms = rng.integers(0, M, 128)
+    ns = rng.integers(0, N, 128)
+    um, un = np.unique(ms), np.unique(ns)
+    Pa, ea = mx.quantize(a[um])
+    Pw, ew = mx.quantize(W[:, un].T.copy())
+    assert np.array_equal(Qa.view(torch.uint8)[torch.from_numpy(um).to(DEV)].cpu().numpy(), mx.codes(Pa))
+    assert np.array_equal(Sa[torch.from_numpy(um).to(DEV)].cpu().numpy(), mx.e8m0_codes(ea))
+    assert np.array_equal(Qw.view(torch.uint8)[torch.from_numpy(un).to(DEV)].cpu().numpy(), mx.codes(Pw))
+    assert np.array_equal(Sw[torch.from_numpy(un).to(DEV)].cpu().numpy(), mx.e8m0_codes(ew))
+    Ad, Bd = mx.dequantize(Pa, ea), mx.dequantize(Pw, ew)
+    im, jn = np.searchsorted(um, ms), np.searchsorted(un, ns)
+    acc = np.einsum("ik,ik->i", Ad[im], Bd[jn])
+    bound = 2.0 ** -10 * np.einsum("ik,ik->i", np.abs(Ad[im]), np.abs(Bd[jn]))
+    ref = z[ms, ns].astype(np.float64) + acc
+    got = out[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), float(np.max(np.abs(got - ref) - bound))
+    assert_bf16("sampled out", got, nm.bf16(ref))
