@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
+    ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -91,6 +92,52 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 3}))
+
+
+def mx_leg(warmup, steps):
+    """The block-scaled E4M3 GEMM (one E8M0 scale per 32 K values, applied by
+    the scaled MFMA) with the residual epilogue, out = z + a W, at the
+    hidden-8192 down-projection shape (M 4096, K 28672, N 8192), against the
+    per-token x per-channel amax-scaled E4M3 path of the same layer; both
+    include the quantisation of the activation a.  Synthetic inputs drawn on
+    the device from a seeded generator."""
+    import torch
+    import gemm_epilogue_fp8_amd as coda
+    M, K, N = 4096, 28672, 8192
+    gen = torch.Generator(device="cuda:0").manual_seed(7)
+    a = torch.randn((M, K), generator=gen, device="cuda:0").to(torch.bfloat16)
+    W = (torch.randn((K, N), generator=gen, device="cuda:0") * K ** -0.5).to(torch.bfloat16)
+    z = torch.randn((M, N), generator=gen, device="cuda:0").to(torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    Qw, Sw = coda.quantize_mxfp8(W, 0)
+    Qa, Sa = coda.quantize_mxfp8(a, 1)
+    wt = coda.Weight(W).prepare_fp8()
+    prog = [(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)]
+
+    def ev_ms(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    gemm_ms = ev_ms(lambda: coda.gemm_mx(prog, Qa, Sa, Qw, Sw, out, aux=[z]))
+    quant_ms = ev_ms(lambda: coda.quantize_mxfp8(a, 1, Qa, Sa))
+    rowcol_ms = ev_ms(lambda: coda.linear_rmsnorm_residual_fwd(a, wt, z, out, precision=coda.PREC_FP8))
+    flop = 2 * M * N * K
+    tf = flop / (gemm_ms * 1e-3) / 1e12
+    del a, W, z, out, Qw, Sw, Qa, Sa, wt
+    torch.cuda.empty_cache()
+    return {"workload": f"out = z + a W, M {M}, K {K}, N {N}, MXFP8 operands (E4M3, E8M0 per 32 K)",
+            "gemm_ms": round(gemm_ms, 4), "tflops": round(tf, 1), "frac_of_fp8_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
+            "quantize_a_ms": round(quant_ms, 4),
+            "gemm_plus_quantize_ms": round(gemm_ms + quant_ms, 4),
+            "per_row_col_fp8_layer_ms": round(rowcol_ms, 4)}
 
 
 def cpu_baseline(shape_full, seed, rows, fp8):
@@ -244,6 +291,7 @@ def main():
                    "speedup_fused_over_unfused": round(ums / ms, 4)}
 
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
+    mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
     fwd, bwd = block_flops(M, cfg.D, cfg.F)
     tflops = (fwd + bwd) / (ms * 1e-3) / 1e12
     f3_flop = 2 * M * (2 * cfg.F) * cfg.D
@@ -277,6 +325,7 @@ def main():
                      "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4),
                      "flop_per_launch": f3_flop, "traffic": stored_traffic(args.config, precision)},
         "cpu_baseline": cpu,
+        "mxfp8_gemm": mx,
     }
     print(json.dumps(out))
 
