@@ -193,21 +193,23 @@ def _program(program):
 
 # ---------------------------------------------------------------- MXFP8
 def quantize_mxfp8(X, axis: int, Q=None, S=None):
-    """MXFP8 copy of X [R, C] (bf16): axis 1 -> Q [R, C], S [R, C/32];
-    axis 0 -> Q [C, R] (transposed), S [C, R/32].  S holds E8M0 codes (uint8)."""
+    """MXFP8 copy of X [R, C] (bf16): axis 1 -> Q [R, C] with the exponents
+    of R rows; axis 0 -> Q [C, R] (transposed) with those of C rows.  S holds
+    E8M0 codes (uint8) in word layout, [ceil(L/128), 4 rows] (see coda.h)."""
     R, Cc = X.shape
     rows, L = (R, Cc) if axis == 1 else (Cc, R)
     if Q is None:
         Q = torch.empty((rows, L), dtype=torch.float8_e4m3fn, device=X.device)
-    if S is None:   # rows of whole 4-byte words, as the block-scaled GEMM reads them
-        S = torch.empty((rows, (L // 32 + 3) // 4 * 4), dtype=torch.uint8, device=X.device)[:, :L // 32]
+    if S is None:
+        S = torch.empty(((L + 127) // 128, 4 * rows), dtype=torch.uint8, device=X.device)
     _check(lib().coda_quantize_mxfp8(_p(X), axis, _p(Q), _p(S), _stream()))
     return Q, S
 
 
 def gemm_mx(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     """D = epilogue(A~ B~^T) with MXFP8 operands A [M, K], B [N, K] and their
-    E8M0 block scales SA [M, K/32], SB [N, K/32]; program as in gemm_epi."""
+    E8M0 block exponents SA [K/128, 4M], SB [K/128, 4N] in word layout;
+    program as in gemm_epi."""
     prog = _program(program)
     aux = list(aux)
     arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])

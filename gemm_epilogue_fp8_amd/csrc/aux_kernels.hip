@@ -423,8 +423,12 @@ __device__ __forceinline__ uint32_t cvt4_mx(float a, float b, float c, float d, 
   return cvt4_e4m3(ldexpf(a, -e), ldexpf(b, -e), ldexpf(c, -e), ldexpf(d, -e));
 }
 
-// Blocks along the columns: X [R, C] -> Q [R, C], S [R, C / 32] (C % 32 == 0).
-// One wave a row, 8 values a lane, a block = 4 consecutive lanes.
+// Exponents go to word layout: block b of operand row r is byte
+// S[(b / 4) lds + 4 r + b % 4], so the words of one 128-value K range of
+// consecutive rows are contiguous.
+// Blocks along the columns: X [R, C] -> Q [R, C], exponents of R rows
+// (C % 32 == 0).  One wave a row, 8 values a lane, a block = 4 consecutive
+// lanes.
 __global__ void quant_mx_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
                                      uint8_t* S, int64_t lds) {
   const int lane = threadIdx.x & 63;
@@ -440,12 +444,13 @@ __global__ void quant_mx_rows_kernel(const uint16_t* X, int64_t ld, int R, int C
     const uint32_t lo = cvt4_mx(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), e);
     const uint32_t hi = cvt4_mx(bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w), e);
     *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + c) = uint2{lo, hi};
-    if ((lane & 3) == 0) S[(int64_t)r * lds + c / 32] = (uint8_t)(e + 127);
+    const int b = c / 32;
+    if ((lane & 3) == 0) S[(int64_t)(b >> 2) * lds + 4 * r + (b & 3)] = (uint8_t)(e + 127);
   }
 }
 
 // Blocks along the rows, written transposed: X [R, C] -> Q^T [C, R],
-// S [C, R / 32] (R % 32 == 0).  A 64 x 64 tile goes through LDS; thread
+// exponents of C rows (R % 32 == 0).  A 64 x 64 tile goes through LDS; thread
 // (column cc, part) encodes rows [16 part, 16 part + 16) of its column, and
 // a block is the two parts of one lane pair.
 __global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
@@ -474,7 +479,8 @@ __global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = cvt4_mx(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], e);
   *reinterpret_cast<uint4*>(QT + (int64_t)c * ldq + rbase) = uint4{w[0], w[1], w[2], w[3]};
-  if ((part & 1) == 0) S[(int64_t)c * lds + rbase / 32] = (uint8_t)(e + 127);
+  const int b = rbase / 32;
+  if ((part & 1) == 0) S[(int64_t)(b >> 2) * lds + 4 * c + (b & 3)] = (uint8_t)(e + 127);
 }
 
 }  // namespace coda

@@ -319,14 +319,17 @@ coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, i
   return CODA_OK;
 }
 
-// E8M0 block-exponent matrix: one byte per 32 values of the contracted
-// axis; rows of 4-byte words (ld % 4 == 0, pointer 4-byte aligned), since the
-// GEMM moves the exponents of 128 K values as one word.
-coda_status check_scales(const coda_mat* S, const char* name, int64_t rows, int64_t cols) {
+// E8M0 block exponents of an operand with `nrows` rows and a contracted
+// axis of L values, in word layout: ceil(L / 128) word rows of 4 nrows
+// bytes; byte (g, 4 r + j) is the exponent of block 4 g + j of row r.
+// Word rows are whole 4-byte words (ld % 4 == 0, pointer 4-byte aligned):
+// the GEMM moves the exponents of 128 K values of a row as one word.
+coda_status check_scales(const coda_mat* S, const char* name, int64_t nrows, int64_t L) {
   if (!present(S)) return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
   if (S->dtype != CODA_E8M0) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected E8M0", name, S->dtype);
+  const int64_t rows = (L + 127) / 128, cols = 4 * nrows;
   if (S->rows != rows || S->cols != cols)
-    return fail(CODA_ERR_SHAPE, "%s: %lld x %lld, expected %lld x %lld", name, (long long)S->rows,
+    return fail(CODA_ERR_SHAPE, "%s: %lld x %lld, expected %lld x %lld (word layout)", name, (long long)S->rows,
                 (long long)S->cols, (long long)rows, (long long)cols);
   if (reinterpret_cast<uintptr_t>(S->ptr) % 4 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 4-byte aligned", name);
   if (S->rows > 1 && (S->ld < S->cols || S->ld % 4 != 0))
@@ -370,7 +373,7 @@ extern "C" coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, cons
                                (long long)L);
   const int64_t rows = axis == 1 ? R : C;
   TRY(check_mat(Q, "Q", CODA_E4M3, rows, L));
-  TRY(check_scales(Sc, "S", rows, L / 32));
+  TRY(check_scales(Sc, "S", rows, L));
   if (R == 0 || C == 0) return CODA_OK;
   const uint16_t* x = static_cast<const uint16_t*>(X->ptr);
   uint8_t* q = static_cast<uint8_t*>(Q->ptr);
@@ -395,8 +398,8 @@ extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat
                                 (long long)B->cols);
   if (K <= 0 || K % 128 != 0) return fail(CODA_ERR_SHAPE, "gemm_mx: K (%lld) must be a positive multiple of 128",
                                           (long long)K);
-  TRY(check_scales(SA, "SA", M, K / 32));
-  TRY(check_scales(SB, "SB", N, K / 32));
+  TRY(check_scales(SA, "SA", M, K));
+  TRY(check_scales(SB, "SB", N, K));
   Prog p;
   EpiArgs e;
   int64_t out_cols;

@@ -59,9 +59,12 @@
 //  * Workgroup ids are remapped so that the tiles one XCD (8 per chip, each
 //    with its own L2) runs are neighbours, then grouped along M.
 //  * MXFP8 block scales travel like the tiles: the E8M0 bytes of one stage
-//    pair (128 K = 4 blocks) are one 4-byte word per operand row, copied
-//    global->LDS beside the pair (buffer_load_dword ... lds, one wave
-//    instruction covers 64 rows) into two 2 KB slots, read in the memory
+//    pair (128 K = 4 blocks) are one 4-byte word per operand row, stored
+//    word row by word row so that the words of consecutive rows are
+//    contiguous; they are copied global->LDS beside the pair
+//    (buffer_load_dword ... lds, one wave instruction covers 64 rows = 256
+//    contiguous bytes; with the exponents stored row by row the same copy
+//    touched 64 cache lines and cost 10%) into two 2 KB slots, read in the memory
 //    phase with the fragments and handed to the MFMA as its per-lane scale
 //    operand.  A lane of the 32x32x64 MFMA supplies 16 K values of each of
 //    the two 32-value blocks of its row, and the scale operand of lane
@@ -122,8 +125,10 @@ struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n;
   int kchunk;      // split K: workgroup (x, y) runs K slice [y kchunk, (y + 1) kchunk); gridDim.y slices
-  // MXFP8 only: E8M0 block exponents, [M, K / 32] and [N, K / 32] bytes
-  // (row strides lds_a, lds_b bytes, multiples of 4; K a multiple of 128)
+  // MXFP8 only: E8M0 block exponents of A and B in word layout: word row
+  // g (stride lds_a / lds_b bytes, a multiple of 4) holds one 4-byte word per
+  // operand row r, bytes = the exponents of blocks 4 g .. 4 g + 3 (K values
+  // 128 g .. 128 g + 127) of row r; K a multiple of 128
   const void* sA;
   const void* sB;
   int64_t lds_a, lds_b;
@@ -436,8 +441,9 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     }
   };
   // MXFP8: the 4 block exponents (one word) of stage pair p for rows
-  // [64 w, 64 w + 64) of this group's operand tile; wave w of group 1 copies
-  // the words of exactly the B rows that wave w of each group reads
+  // [64 w, 64 w + 64) of this group's operand tile, from word row p; wave w
+  // of group 1 copies the words of exactly the B rows that wave w of each
+  // group reads
   auto issue_scales = [&](int p) {
     if constexpr (Cfg::MX) {
       const bool a = grp == 0;
@@ -445,9 +451,8 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
       const int64_t ld = a ? g.lds_a : g.lds_b;
       const int row0 = a ? m0 : n0, nrows = a ? g.M : g.N;
       const int r = 64 * w + lane;
-      const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld + (uint64_t)(g.K / 32);
-      const auto rs = make_rsrc(base + (int64_t)row0 * ld, rem);
-      const uint32_t off = (row0 + r < nrows) ? (uint32_t)(r * ld + 4 * p) : kOobOffset;
+      const auto rs = make_rsrc(base + (int64_t)p * ld + 4 * (int64_t)row0, 4 * (uint64_t)(nrows - row0));
+      const uint32_t off = (row0 + r < nrows) ? (uint32_t)(4 * r) : kOobOffset;
       char* dst = smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT + (a ? 0 : 4 * Cfg::BM) + 256 * w;
       raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (int)off, 0, 0, 0);
     }

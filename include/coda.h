@@ -187,23 +187,33 @@ coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32
  * values along the contracted axis shares one E8M0 scale 2^e, and the
  * value the block stands for is 2^e * E4M3 element.
  *
+ * Exponent layout ("word layout").  The exponents of an operand with n rows
+ * and a contracted axis of L values form an E8M0 matrix S of
+ * ceil(L / 128) x 4n bytes: word row g holds one 4-byte word per operand
+ * row r, whose bytes j = 0..3 are the exponents of blocks 4 g + j (values
+ * 128 g + 32 j .. 128 g + 32 j + 31) of row r:  S[g, 4 r + j].  The words of
+ * consecutive rows are contiguous, so the GEMM copies the exponents of 64
+ * rows for 128 K values with one 256-byte read.  S needs a 4-byte aligned
+ * pointer and ld % 4 == 0 (it may be a uint8 tensor).  S byte = e + 127.
+ *
  * Quantiser.  X: bf16 [R, C].  For each block with absolute max a:
  *   e = floor(log2 a) - 8, clamped to [-127, 127] (-127 when a is 0 or an
  *   fp32 subnormal);  element = E4M3(x / 2^e), round to nearest even,
  *   saturated at +-448.
- *   axis = 1: blocks along C:  Q E4M3 [R, C],  S E8M0 [R, C / 32]; C % 32 == 0
+ *   axis = 1: blocks along C:  Q E4M3 [R, C], S of R rows and L = C;  C % 32 == 0
  *   axis = 0: blocks along R, written transposed (the contracted axis
- *             contiguous):     Q E4M3 [C, R],  S E8M0 [C, R / 32]; R % 32 == 0
- * S byte = e + 127.  S needs a 4-byte aligned pointer and ld % 4 == 0 (it
- * may be a uint8 tensor); Q follows the E4M3 rules above.  No workspace.
- * Errors: CODA_ERR_SHAPE when the blocked axis is not a multiple of 32. */
+ *             contiguous):     Q E4M3 [C, R], S of C rows and L = R;  R % 32 == 0
+ * When L is not a multiple of 128 the bytes of the last word row past the
+ * last block are not written.  Q follows the E4M3 rules above.  No
+ * workspace.  Errors: CODA_ERR_SHAPE when the blocked axis is not a
+ * multiple of 32 or S is not ceil(L / 128) x 4n. */
 coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
                                 void* stream);
 
 /* D = epilogue(sum_k A~[m, k] B~[n, k]) with MXFP8 operands
- *   A~ = A (E4M3 [M, K]) scaled by SA (E8M0 [M, K / 32]),
+ *   A~ = A (E4M3 [M, K]) scaled by SA (E8M0 [K / 128, 4 M], word layout),
  *   B~ = B (E4M3 [N, K], i.e. the second operand stored with K contiguous)
- *        scaled by SB (E8M0 [N, K / 32]);
+ *        scaled by SB (E8M0 [K / 128, 4 N], word layout);
  * products and sums in fp32 on the matrix cores, the block scales applied
  * by the scaled MFMA.  K must be a positive multiple of 128 (the exponents
  * of 128 K values travel as one 4-byte word).  The epilogue program is any of

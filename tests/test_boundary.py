@@ -135,18 +135,20 @@ def test_workspace_queries():
 
 
 def test_mx_validation_codes():
-    """MXFP8 entry points: block-multiple sizes, E8M0 scale shapes, dtype and
-    4-byte layout, checked before any HIP call."""
+    """MXFP8 entry points: block-multiple sizes, E8M0 exponent matrices in
+    word layout ([ceil(L/128), 4 rows]), dtype and 4-byte layout, checked
+    before any HIP call."""
     L = g.lib()
     BF, E4, E8 = _lib.CODA_BF16, _lib.CODA_E4M3, _lib.CODA_E8M0
     q = lambda X, axis, Q, S: L.coda_quantize_mxfp8(C.byref(X), axis, C.byref(Q), C.byref(S), None)
-    assert q(fake(BF, 40, 48), 1, fake(E4, 40, 48), fake(E8, 40, 1)) == 3      # 48 not a multiple of 32
-    assert q(fake(BF, 40, 64), 0, fake(E4, 64, 40), fake(E8, 64, 1)) == 3      # 40 rows: not a multiple of 32
-    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 3, ld=4)) == 3   # wrong scale count
-    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E4, 40, 2, ld=16)) == 2  # scale dtype
-    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 2, ld=6)) == 4   # ld not a multiple of 4
-    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 40, 2, ld=4, ptr=FAKE + 2)) == 5
-    assert q(fake(BF, 40, 64), 2, fake(E4, 40, 64), fake(E8, 40, 2, ld=4)) == 9   # axis
+    assert q(fake(BF, 40, 48), 1, fake(E4, 40, 48), fake(E8, 1, 160)) == 3      # 48 not a multiple of 32
+    assert q(fake(BF, 40, 64), 0, fake(E4, 64, 40), fake(E8, 1, 256)) == 3      # 40 rows: not a multiple of 32
+    assert q(fake(BF, 40, 64), 1, fake(E4, 40, 64), fake(E8, 1, 156)) == 3      # wrong byte count
+    assert q(fake(BF, 40, 256), 1, fake(E4, 40, 256), fake(E8, 1, 160)) == 3    # 256 values = 2 word rows
+    assert q(fake(BF, 40, 256), 1, fake(E4, 40, 256), fake(E4, 2, 160, ld=160)) == 2  # exponent dtype
+    assert q(fake(BF, 40, 256), 1, fake(E4, 40, 256), fake(E8, 2, 160, ld=162)) == 4  # ld not a multiple of 4
+    assert q(fake(BF, 40, 256), 1, fake(E4, 40, 256), fake(E8, 2, 160, ptr=FAKE + 2)) == 5
+    assert q(fake(BF, 40, 256), 2, fake(E4, 40, 256), fake(E8, 2, 160)) == 9   # axis
 
     prog = _lib.EpiProgram()
     prog.n_ops = 1
@@ -154,13 +156,15 @@ def test_mx_validation_codes():
     gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
                                                 C.byref(D), None, 0, None)
     M, N = 64, 32
-    assert gm(fake(E4, M, 192), fake(E8, M, 6, ld=8), fake(E4, N, 192), fake(E8, N, 6, ld=8),
+    assert gm(fake(E4, M, 192), fake(E8, 2, 4 * M), fake(E4, N, 192), fake(E8, 2, 4 * N),
               fake(BF, M, N)) == 3                                             # K = 192: not a multiple of 128
-    assert gm(fake(E4, M, 256), fake(E8, M, 8), fake(E4, N, 128), fake(E8, N, 4),
+    assert gm(fake(E4, M, 256), fake(E8, 2, 4 * M), fake(E4, N, 128), fake(E8, 1, 4 * N),
               fake(BF, M, N)) == 3                                             # inner sizes differ
-    assert gm(fake(E4, M, 256), fake(E8, M, 4), fake(E4, N, 256), fake(E8, N, 8),
-              fake(BF, M, N)) == 3                                             # SA is not [M, K/32]
-    assert gm(fake(BF, M, 256), fake(E8, M, 8), fake(E4, N, 256), fake(E8, N, 8),
+    assert gm(fake(E4, M, 256), fake(E8, 1, 4 * M), fake(E4, N, 256), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 3                                             # SA has 1 word row, K needs 2
+    assert gm(fake(E4, M, 256), fake(E8, 2, M), fake(E4, N, 256), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 3                                             # SA is not 4 M bytes wide
+    assert gm(fake(BF, M, 256), fake(E8, 2, 4 * M), fake(E4, N, 256), fake(E8, 2, 4 * N),
               fake(BF, M, N)) == 2                                             # A not E4M3
-    assert gm(fake(E4, M, 256), fake(E8, M, 8), fake(E4, N, 256), fake(E8, N, 8),
+    assert gm(fake(E4, M, 256), fake(E8, 2, 4 * M), fake(E4, N, 256), fake(E8, 2, 4 * N),
               fake(BF, M, N + 8)) == 3                                         # D shape

@@ -42,6 +42,23 @@ def e4m3_dev(codes):
     return u8(codes).view(torch.float8_e4m3fn)
 
 
+def to_words(e8):
+    """[rows, nblocks] exponent bytes -> the library's word layout
+    [ceil(nblocks / 4), 4 rows]: byte (g, 4 r + j) = block 4 g + j of row r."""
+    rows, nb = e8.shape
+    G = (nb + 3) // 4
+    full = np.zeros((rows, 4 * G), np.uint8)
+    full[:, :nb] = e8
+    return np.ascontiguousarray(full.reshape(rows, G, 4).transpose(1, 0, 2).reshape(G, 4 * rows))
+
+
+def from_words(S, rows, nb):
+    """Inverse of to_words, keeping the nb blocks that exist."""
+    S = np.asarray(S)
+    G = S.shape[0]
+    return S.reshape(G, rows, 4).transpose(1, 0, 2).reshape(rows, 4 * G)[:, :nb]
+
+
 def varied_bf16(rng, R, C, axis):
     """bf16 values whose magnitude changes by powers of two from block to
     block along `axis`, with one all-zero block and one block of large values,
@@ -67,7 +84,8 @@ def test_quantize_mxfp8_bit_exact(axis, R, C):
     torch.cuda.synchronize()
     P, e = mx.quantize(X if axis == 1 else X.T.copy())
     assert np.array_equal(Q.view(torch.uint8).cpu().numpy(), mx.codes(P))
-    assert np.array_equal(S.cpu().numpy(), mx.e8m0_codes(e))
+    assert S.shape == ((e.shape[1] + 3) // 4, 4 * e.shape[0])
+    assert np.array_equal(from_words(S.cpu().numpy(), *e.shape), mx.e8m0_codes(e))
 
 
 def test_quantize_mxfp8_rejects_ragged_blocks():
@@ -112,9 +130,9 @@ def test_gemm_mx_accum_and_store(M, N, K):
     ref = A @ B.T
     prior = ci.fp32_prior((M, N), 4)
     D32 = f32(prior)
-    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 1.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D32)
+    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 1.0)], e4m3_dev(ca), u8(to_words(sa)), e4m3_dev(cb), u8(to_words(sb)), D32)
     D16 = torch.empty((M, N), dtype=BF, device=DEV)
-    coda.gemm_mx([(coda.EPI_STORE_BF16, 0, 0.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D16)
+    coda.gemm_mx([(coda.EPI_STORE_BF16, 0, 0.0)], e4m3_dev(ca), u8(to_words(sa)), e4m3_dev(cb), u8(to_words(sb)), D16)
     torch.cuda.synchronize()
     bound = mfma_fp8_bound(A, B)
     got32 = to_np(D32).astype(np.float64) - prior
@@ -142,7 +160,7 @@ def test_gemm_mx_one_scale_per_block():
     sb = (121 + (np.arange(K // 32)[None, :] * 5 + 2 * np.arange(N)[:, None]) % 13).astype(np.uint8)
     A, B = mx_values(ca, sa), mx_values(cb, sb)
     D32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 0.0)], e4m3_dev(ca), u8(sa), e4m3_dev(cb), u8(sb), D32)
+    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 0.0)], e4m3_dev(ca), u8(to_words(sa)), e4m3_dev(cb), u8(to_words(sb)), D32)
     torch.cuda.synchronize()
     ref = A @ B.T
     assert np.all(np.abs(to_np(D32) - ref) <= mfma_fp8_bound(A, B))
@@ -218,9 +236,9 @@ def test_gemm_mx_full_size_sampled():
     Pa, ea = mx.quantize(a[um])
     Pw, ew = mx.quantize(W[:, un].T.copy())
     assert np.array_equal(Qa.view(torch.uint8)[torch.from_numpy(um).to(DEV)].cpu().numpy(), mx.codes(Pa))
-    assert np.array_equal(Sa[torch.from_numpy(um).to(DEV)].cpu().numpy(), mx.e8m0_codes(ea))
+    assert np.array_equal(from_words(Sa.cpu().numpy(), M, K // 32)[um], mx.e8m0_codes(ea))
     assert np.array_equal(Qw.view(torch.uint8)[torch.from_numpy(un).to(DEV)].cpu().numpy(), mx.codes(Pw))
-    assert np.array_equal(Sw[torch.from_numpy(un).to(DEV)].cpu().numpy(), mx.e8m0_codes(ew))
+    assert np.array_equal(from_words(Sw.cpu().numpy(), N, K // 32)[un], mx.e8m0_codes(ew))
     Ad, Bd = mx.dequantize(Pa, ea), mx.dequantize(Pw, ew)
     im, jn = np.searchsorted(um, ms), np.searchsorted(un, ns)
     acc = np.einsum("ik,ik->i", Ad[im], Bd[jn])
