@@ -35,6 +35,7 @@ from typing import Callable, Dict, Optional
 
 import numpy as np
 
+from . import mx
 from . import numerics as nm
 from . import ops
 
@@ -44,13 +45,22 @@ def _ident(x):
 
 
 # --------------------------------------------------------------------------- GEMM
-def mm(A, B, fp8: bool = False):
+def mm(A, B, fp8=False):
     """A @ B with float32 (or float64) accumulation.
 
-    With fp8, each operand is quantised to E4M3 with one scale per index of its
-    non-contracted axis (per row of A, per column of B) and the product is
-    dequantised as (QA @ QB) * s_A[m] * s_B[n].
+    With fp8 = True, each operand is quantised to E4M3 with one scale per index
+    of its non-contracted axis (per row of A, per column of B) and the product
+    is dequantised as (QA @ QB) * s_A[m] * s_B[n].
+
+    With fp8 = "mx", each operand is quantised to MXFP8 (E4M3 elements, one
+    E8M0 scale per 32 consecutive values of the contracted axis K: along the
+    rows of A and down the columns of B; OCP Microscaling Formats v1.0) and the
+    product of the dequantised operands is taken in float64, then float32.
     """
+    if fp8 == "mx":
+        PA, eA = mx.quantize(np.asarray(A, np.float32))
+        PB, eB = mx.quantize(np.ascontiguousarray(np.asarray(B, np.float32).T))
+        return mx.matmul_nt(PA, eA, PB, eB).astype(np.float32)
     if not fp8:
         return np.matmul(A, B)
     QA, sA = nm.quantize_e4m3(A, axis=1)

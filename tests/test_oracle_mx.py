@@ -103,3 +103,33 @@ def test_matmul_triple_loop():
             for k in range(64):
                 ref += float(PA[m, k]) * 2.0 ** eA[m, k // 32] * float(PB[n, k]) * 2.0 ** eB[n, k // 32]
             assert C[m, n] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+def test_block_gemm_mx_mode_axes():
+    """oracle.block.mm(A, B, "mx") quantises A along its rows and B down its
+    columns (the contracted axis of both): operands that are already MXFP8
+    along those axes come back as the exact product; quantising B along its
+    rows instead would have changed it."""
+    from oracle import block as ob
+    rng = np.random.default_rng(9)
+
+    def mx_rows(rows, nblocks):
+        # E4M3 values with a block maximum in [256, 448], times 2^e, e small
+        big = VALUES[np.abs(VALUES) >= 256]
+        X = np.empty((rows, 32 * nblocks))
+        for r in range(rows):
+            for b in range(nblocks):
+                top = rng.choice(big)
+                blk = np.concatenate([[top], rng.choice(VALUES[np.abs(VALUES) <= abs(top)], size=31)])
+                rng.shuffle(blk)
+                X[r, 32 * b:32 * b + 32] = blk * 2.0 ** rng.integers(-12, -6)
+        return X.astype(np.float32)
+
+    A = mx_rows(5, 3)                            # [5, 96], MXFP8 along K
+    Bt = mx_rows(64, 3)                          # B = Bt^T [96, 64], MXFP8 down its columns
+    B = np.ascontiguousarray(Bt.T)
+    got = ob.mm(A, B, "mx")
+    ref = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(got, ref)
+    P, e = mx.quantize(B)                        # the wrong axis: blocks along B's rows
+    assert not np.array_equal(mx.dequantize(P, e), B.astype(np.float64))
