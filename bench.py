@@ -30,7 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA, published
 HBM_GBPS = 8000.0
 
 
@@ -70,7 +70,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="cfg2", choices=("cfg2", "cfg3", "cfg5"))
-    ap.add_argument("--precision", default=None, choices=("bf16", "fp8"))
+    ap.add_argument("--precision", default=None, choices=("bf16", "fp8", "mxfp8"),
+                    help="GEMM operands: bf16, E4M3 with per-row / per-column amax scales (fp8), or E4M3 with "
+                         "one E8M0 exponent per 32 values of the contracted axis (mxfp8)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
@@ -140,6 +142,10 @@ def mx_leg(warmup, steps):
             "per_row_col_fp8_layer_ms": round(rowcol_ms, 4)}
 
 
+OPERANDS = {False: "", True: " with E4M3 operands (per-row / per-column amax scales)",
+            "mx": " with MXFP8 operands (E4M3, one E8M0 exponent per 32 values)"}
+
+
 def cpu_baseline(shape_full, seed, rows, fp8):
     """The oracle (numpy, contract mode) forward + backward on the first
     `rows` tokens of the same workload, timed on the host cores."""
@@ -157,7 +163,7 @@ def cpu_baseline(shape_full, seed, rows, fp8):
     return {"value": round((fwd + bwd) / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{rows} of {shape_full.M} token rows of the same workload, block fwd+bwd, numpy "
-                      f"float32 contract mode{' with E4M3 operands' if fp8 else ''}, {dt:.1f} s"}
+                      f"float32 contract mode{OPERANDS[fp8]}, {dt:.1f} s"}
 
 
 def main():
@@ -173,7 +179,7 @@ def main():
     cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[args.config]
     seed = ci.SEEDS[args.config]
     precision = args.precision or ("fp8" if args.config == "cfg5" else "bf16")
-    fp8 = precision == "fp8"
+    fp8 = {"bf16": False, "fp8": True, "mxfp8": "mx"}[precision]
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, seed, args.cpu_rows or cfg.M, fp8)
@@ -190,7 +196,7 @@ def main():
     to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
     params = {k: to(v, torch.float32 if k in ("g1", "g2", "gq", "gk") else torch.bfloat16) for k, v in P.items()}
     del P
-    prec = coda.PREC_FP8 if fp8 else coda.PREC_BF16
+    prec = {"bf16": coda.PREC_BF16, "fp8": coda.PREC_FP8, "mxfp8": coda.PREC_MXFP8}[precision]
     torch.cuda.synchronize()
     t_prep = time.perf_counter()
     blk = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, theta=cfg.theta, eps=cfg.eps, precision=prec)

@@ -16,7 +16,7 @@ from typing import Iterable, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (CODA_BF16, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8,
+from ._lib import (CODA_BF16, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
 
@@ -24,7 +24,7 @@ __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "ro
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
-           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8"]
+           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8"]
 
 
 class CodaError(RuntimeError):
@@ -90,6 +90,19 @@ class Weight:
         self.s_fwd = torch.empty(N, dtype=torch.float32, device=dev)
         self.q_bwd = torch.empty((K, N), dtype=torch.float8_e4m3fn, device=dev)
         self.s_bwd = torch.empty(K, dtype=torch.float32, device=dev)
+        quantize_weight(self)
+        return self
+
+    def prepare_mxfp8(self):
+        """Allocate and fill the two block-scaled E4M3 copies
+        (coda_quantize_weight): q_fwd [N, K] with exponents along K_in and
+        q_bwd [K, N] with exponents along N_out, both in word layout."""
+        K, N = self.w.shape
+        dev = self.w.device
+        self.q_fwd = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=dev)
+        self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
+        self.q_bwd = torch.empty((K, N), dtype=torch.float8_e4m3fn, device=dev)
+        self.s_bwd = torch.empty(((N + 127) // 128, 4 * K), dtype=torch.uint8, device=dev)
         quantize_weight(self)
         return self
 

@@ -55,21 +55,78 @@ coda_status run_quant(const void* X, int64_t ldx, int64_t R, int64_t C, int axis
   return check_launch("quantize_e4m3");
 }
 
-// Activation operand of a GEMM in fp8: quantised into the workspace.
+// Activation operand of a GEMM in fp8: quantised into the workspace, either
+// with one amax scale per row of the operand (q.s) or, for MXFP8, with one
+// E8M0 exponent per 32 values of the contracted axis (e, word layout: ceil(L /
+// 128) word rows of 4 rows bytes, stride e_ld).
 struct ActQ {
   Q8 q;
   float* amax;
   float* parts;
+  bool mx;
+  uint8_t* e;
+  int64_t e_ld;
 };
-ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis) {
-  ActQ a;
+ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis, bool mx = false) {
+  ActQ a{};
+  a.mx = mx;
+  if (mx) {
+    const int64_t rows = axis == 1 ? R : C, L = axis == 1 ? C : R;
+    a.q.ld = (L + 15) / 16 * 16;
+    a.q.q = cv.take<uint8_t>((size_t)rows * a.q.ld);
+    a.q.s = nullptr;
+    a.e_ld = 4 * rows;
+    a.e = cv.take<uint8_t>((size_t)((L + 127) / 128) * a.e_ld);
+    return a;
+  }
   a.q = take_q8(cv, R, C, axis);
   if (axis == 1) { a.amax = cv.take<float>(R); a.parts = nullptr; }
   else { a.amax = cv.take<float>(C); a.parts = cv.take<float>((size_t)((R + 255) / 256) * C); }
   return a;
 }
+coda_status run_quant_mx(const void* X, int64_t ldx, int64_t R, int64_t C, int axis, uint8_t* Q, int64_t ldq,
+                         uint8_t* E, int64_t lde, hipStream_t s) {
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, x, ldx, (int)R, (int)C,
+                       Q, ldq, E, lde);
+  else
+    hipLaunchKernelGGL(quant_mx_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)), dim3(256),
+                       0, s, x, ldx, (int)R, (int)C, Q, ldq, E, lde);
+  return check_launch("quantize_mxfp8");
+}
 coda_status quant_act(const ActQ& a, const void* X, int64_t ldx, int64_t R, int64_t C, int axis, hipStream_t s) {
+  if (a.mx) return run_quant_mx(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
   return run_quant(X, ldx, R, C, axis, a.q.q, a.q.ld, a.q.s, a.amax, a.parts, s);
+}
+// MXFP8: the exponents of both operands go with the GEMM; the epilogue applies
+// no dequantisation scales
+void mx_args(GemmArgs* g, EpiArgs* e, const void* ea, int64_t lda_e, const coda_mat* eb) {
+  g->sA = ea;
+  g->lds_a = lda_e;
+  g->sB = eb->ptr;
+  g->lds_b = eb->rows > 1 ? eb->ld : eb->cols;
+  e->rowscale = nullptr;
+  e->colscale = nullptr;
+}
+
+// E8M0 block exponents of an operand with `nrows` rows and a contracted
+// axis of L values, in word layout: ceil(L / 128) word rows of 4 nrows
+// bytes; byte (g, 4 r + j) is the exponent of block 4 g + j of row r.
+// Word rows are whole 4-byte words (ld % 4 == 0, pointer 4-byte aligned):
+// the GEMM moves the exponents of 128 K values of a row as one word.
+coda_status check_scales(const coda_mat* S, const char* name, int64_t nrows, int64_t L) {
+  if (!present(S)) return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
+  if (S->dtype != CODA_E8M0) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected E8M0", name, S->dtype);
+  const int64_t rows = (L + 127) / 128, cols = 4 * nrows;
+  if (S->rows != rows || S->cols != cols)
+    return fail(CODA_ERR_SHAPE, "%s: %lld x %lld, expected %lld x %lld (word layout)", name, (long long)S->rows,
+                (long long)S->cols, (long long)rows, (long long)cols);
+  if (reinterpret_cast<uintptr_t>(S->ptr) % 4 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 4-byte aligned", name);
+  if (S->rows > 1 && (S->ld < S->cols || S->ld % 4 != 0))
+    return fail(CODA_ERR_LAYOUT, "%s: ld must be >= cols and a multiple of 4", name);
+  return CODA_OK;
 }
 
 coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int64_t N, int precision) {
@@ -80,13 +137,20 @@ coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int
     TRY(check_vec(&wt->s_fwd, "s_fwd", CODA_F32, N));
     TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E4M3, K, N));
     TRY(check_vec(&wt->s_bwd, "s_bwd", CODA_F32, K));
+  } else if (precision == CODA_PREC_MXFP8) {
+    if (K % 128 != 0 || N % 128 != 0)
+      return fail(CODA_ERR_SHAPE, "%s: MXFP8 needs both weight dimensions to be multiples of 128", name);
+    TRY(check_mat(&wt->q_fwd, "q_fwd", CODA_E4M3, N, K));
+    TRY(check_scales(&wt->s_fwd, "s_fwd", N, K));
+    TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E4M3, K, N));
+    TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
   } else if (precision != CODA_PREC_BF16) {
     return fail(CODA_ERR_VALUE, "precision %d", precision);
   }
   return CODA_OK;
 }
 coda_status check_precision(int p) {
-  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8) return fail(CODA_ERR_VALUE, "precision %d", p);
+  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8) return fail(CODA_ERR_VALUE, "precision %d", p);
   return CODA_OK;
 }
 
@@ -236,6 +300,15 @@ extern "C" coda_status coda_quantize_weight_workspace(const coda_weight* wt, siz
 extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream) {
   if (!wt) return fail(CODA_ERR_NULL, "quantize_weight: NULL weight");
   const int64_t K = wt->w.rows, N = wt->w.cols;
+  if (wt->s_fwd.dtype == CODA_E8M0) {
+    // MXFP8 copies: q_fwd [N, K] with blocks along K_in, q_bwd [K, N] with
+    // blocks along N_out, exponents in word layout
+    TRY(check_weight(wt, "W", K, N, CODA_PREC_MXFP8));
+    TRY(run_quant_mx(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
+                     static_cast<uint8_t*>(wt->s_fwd.ptr), wt->s_fwd.ld, S(stream)));
+    return run_quant_mx(wt->w.ptr, wt->w.ld, K, N, 1, static_cast<uint8_t*>(wt->q_bwd.ptr), wt->q_bwd.ld,
+                        static_cast<uint8_t*>(wt->s_bwd.ptr), wt->s_bwd.ld, S(stream));
+  }
   TRY(check_weight(wt, "W", K, N, CODA_PREC_FP8));
   Carver cv(ws);
   float* amax = cv.take<float>(std::max(K, N));
@@ -319,23 +392,6 @@ coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, i
   return CODA_OK;
 }
 
-// E8M0 block exponents of an operand with `nrows` rows and a contracted
-// axis of L values, in word layout: ceil(L / 128) word rows of 4 nrows
-// bytes; byte (g, 4 r + j) is the exponent of block 4 g + j of row r.
-// Word rows are whole 4-byte words (ld % 4 == 0, pointer 4-byte aligned):
-// the GEMM moves the exponents of 128 K values of a row as one word.
-coda_status check_scales(const coda_mat* S, const char* name, int64_t nrows, int64_t L) {
-  if (!present(S)) return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
-  if (S->dtype != CODA_E8M0) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected E8M0", name, S->dtype);
-  const int64_t rows = (L + 127) / 128, cols = 4 * nrows;
-  if (S->rows != rows || S->cols != cols)
-    return fail(CODA_ERR_SHAPE, "%s: %lld x %lld, expected %lld x %lld (word layout)", name, (long long)S->rows,
-                (long long)S->cols, (long long)rows, (long long)cols);
-  if (reinterpret_cast<uintptr_t>(S->ptr) % 4 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 4-byte aligned", name);
-  if (S->rows > 1 && (S->ld < S->cols || S->ld % 4 != 0))
-    return fail(CODA_ERR_LAYOUT, "%s: ld must be >= cols and a multiple of 4", name);
-  return CODA_OK;
-}
 }  // namespace
 
 extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
@@ -423,16 +479,16 @@ extern "C" coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, in
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision == CODA_PREC_FP8) take_act(cv, M, K, 1);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
   *bytes = cv.off;
   return CODA_OK;
 }
 
 namespace {
 // Sizes and carves what an fp8 activation operand of the forward needs.
-size_t fwd_fp8_bytes(int64_t M, int64_t K) {
+size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx) {
   Carver cv(nullptr);
-  take_act(cv, M, K, 1);
+  take_act(cv, M, K, 1, mx);
   return cv.off;
 }
 }  // namespace
@@ -449,7 +505,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   Carver cv(size_only ? nullptr : ws);
   float* sumsq = cv.take<float>(M);
   ActQ aq{};
-  if (precision == CODA_PREC_FP8) aq = take_act(cv, M, K, 1);
+  if (precision != CODA_PREC_BF16) aq = take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
@@ -465,12 +521,13 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   e.rowvec_out = present(r_out) ? static_cast<float*>(r_out->ptr) : nullptr;
   GemmArgs g;
   int layout;
-  const bool fp8 = precision == CODA_PREC_FP8;
+  const bool fp8 = precision != CODA_PREC_BF16;
   if (fp8) {
     TRY(quant_act(aq, x->ptr, x->ld, M, K, 1, s));
     g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, K);
     e.rowscale = aq.q.s;
     e.colscale = fptr(&Wgu->s_fwd);
+    if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wgu->s_fwd);
     layout = LAYOUT_NT;
   } else {
     g = gemm_args(x->ptr, x->ld, Wgu->w.ptr, Wgu->w.ld, M, N, K);
@@ -513,7 +570,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   (void)N;
-  *bytes = precision == CODA_PREC_FP8 ? fwd_fp8_bytes(M, K) : 0;
+  *bytes = precision != CODA_PREC_BF16 ? fwd_fp8_bytes(M, K, precision == CODA_PREC_MXFP8) : 0;
   return CODA_OK;
 }
 
@@ -532,8 +589,8 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
   if (present(P_out) && P_out->rows > 1 && P_out->ld != M) return fail(CODA_ERR_LAYOUT, "partials: ld must be M");
   Carver cv(ws);
   ActQ aq{};
-  const bool fp8 = precision == CODA_PREC_FP8;
-  if (fp8) aq = take_act(cv, M, K, 1);
+  const bool fp8 = precision != CODA_PREC_BF16;
+  if (fp8) aq = take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   EpiArgs e = epi0();
@@ -547,6 +604,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
     TRY(quant_act(aq, a->ptr, a->ld, M, K, 1, s));
     g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, K);
     e.rowscale = aq.q.s; e.colscale = fptr(&W->s_fwd);
+    if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &W->s_fwd);
     layout = LAYOUT_NT;
   } else {
     g = gemm_args(a->ptr, a->ld, W->w.ptr, W->w.ld, M, N, K);
@@ -561,7 +619,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t 
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision == CODA_PREC_FP8) take_act(cv, M, D, 1);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, D, 1, precision == CODA_PREC_MXFP8);
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -593,9 +651,9 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
   Carver cv(ws);
   float* sumsq = cv.take<float>(M);
-  const bool fp8 = precision == CODA_PREC_FP8;
+  const bool fp8 = precision != CODA_PREC_BF16;
   ActQ aq{};
-  if (fp8) aq = take_act(cv, M, D, 1);
+  if (fp8) aq = take_act(cv, M, D, 1, precision == CODA_PREC_MXFP8);
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   if (!present(P)) TRY(row_sumsq_launch(x->ptr, x->ld, M, D, sumsq, s));
@@ -620,6 +678,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
     TRY(quant_act(aq, x->ptr, x->ld, M, D, 1, s));
     g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, D);
     e.rowscale = aq.q.s; e.colscale = fptr(&Wqkv->s_fwd);
+    if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wqkv->s_fwd);
     layout = LAYOUT_NT;
   } else {
     g = gemm_args(x->ptr, x->ld, Wqkv->w.ptr, Wqkv->w.ld, M, 3 * D, D);
@@ -646,6 +705,7 @@ static coda_status dgrad_args(bool fp8, const ActQ* grow, const void* G, int64_t
     *g = gemm_args(grow->q.q, grow->q.ld, W->q_bwd.ptr, W->q_bwd.ld, M, Kin, Nout);
     e->rowscale = grow->q.s;
     e->colscale = fptr(&W->s_bwd);
+    if (grow->mx) mx_args(g, e, grow->e, grow->e_ld, &W->s_bwd);
   } else {
     *g = gemm_args(G, ldG, W->w.ptr, W->w.ld, M, Kin, Nout);
   }
@@ -658,6 +718,11 @@ static void wgrad_args(bool fp8, const Bwd8& q8, const void* X, int64_t ldX, con
     *g = gemm_args(q8.xcol.q.q, q8.xcol.q.ld, q8.gcol.q.q, q8.gcol.q.ld, Kin, Nout, M);
     e->rowscale = q8.xcol.q.s;
     e->colscale = q8.gcol.q.s;
+    if (q8.xcol.mx) {
+      g->sA = q8.xcol.e; g->lds_a = q8.xcol.e_ld;
+      g->sB = q8.gcol.e; g->lds_b = q8.gcol.e_ld;
+      e->rowscale = nullptr; e->colscale = nullptr;
+    }
     *layout = LAYOUT_NT;
   } else {
     *g = gemm_args(X, ldX, G, ldG, Kin, Nout, M);
@@ -675,7 +740,7 @@ struct Split {
   int64_t kchunk;    // tokens per slice
 };
 
-static Split wgrad_split(int64_t Kin, int64_t Nout, int64_t M) {
+static Split wgrad_split(int64_t Kin, int64_t Nout, int64_t M, int64_t align = 64) {
   Split sp;
   sp.kchunk = M;
   const int64_t tiles = ((Kin + 255) / 256) * ((Nout + 255) / 256);
@@ -683,7 +748,7 @@ static Split wgrad_split(int64_t Kin, int64_t Nout, int64_t M) {
   if (tiles * 4 <= 256 && M >= 4096) want = 4;
   else if (tiles * 2 <= 256 && M >= 2048) want = 2;
   if (want > 1) {
-    sp.kchunk = ((M + want - 1) / want + 63) / 64 * 64;
+    sp.kchunk = ((M + want - 1) / want + align - 1) / align * align;   // MXFP8: whole 128-token words
     sp.n = (int)((M + sp.kchunk - 1) / sp.kchunk);
   }
   return sp;
@@ -728,23 +793,24 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   // F is the width of the activation's output; the pre-activations are 2F
   // wide for SwiGLU (packed gate/up) and F wide for the sigmoid
   const int64_t N2 = act == Act::SwiGLU ? 2 * F : F;
-  const bool fp8 = precision == CODA_PREC_FP8;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
   Carver cv(size_only ? nullptr : ws);
   const int nT2 = (int)coda_partials_cols(F);
   const int nTg = (int)coda_partials_cols(N2);
   float* T2 = cv.take<float>((size_t)nT2 * M);
   float* T2c = cv.take<float>(M);
-  const Split sp = wgrad_split(D, N2, M);
+  const Split sp = wgrad_split(D, N2, M, mx ? 128 : 64);
   float* dgp = cv.take<float>((size_t)sp.n * nTg * D);
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N2) : nullptr;
   uint16_t* dh = present(dh_out) ? nullptr : cv.take<uint16_t>((size_t)M * N2);
   Bwd8 q8{};
   ActQ dYrow{};
   if (fp8) {
-    dYrow = take_act(cv, M, D, 1);
-    q8.grow = take_act(cv, M, N2, 1);
-    q8.xcol = take_act(cv, M, D, 0);
-    q8.gcol = take_act(cv, M, N2, 0);
+    dYrow = take_act(cv, M, D, 1, mx);
+    q8.grow = take_act(cv, M, N2, 1, mx);
+    q8.xcol = take_act(cv, M, D, 0, mx);
+    q8.gcol = take_act(cv, M, N2, 0, mx);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
@@ -853,12 +919,13 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   Carver cv(nullptr);
-  if (precision == CODA_PREC_FP8) {
-    take_act(cv, M, N, 1);
-    take_act(cv, M, K, 0);
-    take_act(cv, M, N, 0);
+  const bool mx = precision == CODA_PREC_MXFP8;
+  if (precision != CODA_PREC_BF16) {
+    take_act(cv, M, N, 1, mx);
+    take_act(cv, M, K, 0, mx);
+    take_act(cv, M, N, 0, mx);
   }
-  const Split sp = wgrad_split(K, N, M);
+  const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   if (sp.n > 1) cv.take<float>((size_t)sp.n * K * N);
   *bytes = cv.off;
   return CODA_OK;
@@ -876,15 +943,16 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   TRY(check_weight(W, "W", K, N, precision));
   TRY(check_mat(da, "da", CODA_BF16, M, K, true));
   TRY(check_mat(dW, "dW", CODA_F32, K, N));
-  const bool fp8 = precision == CODA_PREC_FP8;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
   Carver cv(ws);
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N, 1);
-    q8.xcol = take_act(cv, M, K, 0);
-    q8.gcol = take_act(cv, M, N, 0);
+    q8.grow = take_act(cv, M, N, 1, mx);
+    q8.xcol = take_act(cv, M, K, 0, mx);
+    q8.gcol = take_act(cv, M, N, 0, mx);
   }
-  const Split sp = wgrad_split(K, N, M);
+  const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * K * N) : nullptr;
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
@@ -916,7 +984,8 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
                                const coda_mat* dW, const coda_mat* dg, const coda_mat* dgq, const coda_mat* dgk,
                                float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
                                void* stream, int64_t M, int64_t D, bool size_only, size_t* bytes) {
-  const bool fp8 = precision == CODA_PREC_FP8;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
   const int64_t N3 = 3 * D;
   const int rows_per_wave = 4;
   const int nblk = (int)((M + 4 * rows_per_wave - 1) / (4 * rows_per_wave));
@@ -931,14 +1000,14 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
   float* pgq = cv.take<float>((size_t)std::max(nblk, 1) * 128);
   float* pgk = cv.take<float>((size_t)std::max(nblk, 1) * 128);
   const int nTg = (int)coda_partials_cols(N3);
-  const Split sp = wgrad_split(D, N3, M);
+  const Split sp = wgrad_split(D, N3, M, mx ? 128 : 64);
   float* dgp = cv.take<float>((size_t)sp.n * nTg * D);
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N3) : nullptr;
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N3, 1);
-    q8.xcol = take_act(cv, M, D, 0);
-    q8.gcol = take_act(cv, M, N3, 0);
+    q8.grow = take_act(cv, M, N3, 1, mx);
+    q8.xcol = take_act(cv, M, D, 0, mx);
+    q8.gcol = take_act(cv, M, N3, 0, mx);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
@@ -1063,7 +1132,7 @@ extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const co
                                                      const coda_mat* n_bad, int32_t precision, void* ws,
                                                      size_t ws_bytes, void* stream) {
   TRY(check_precision(precision));
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(h, "h", CODA_BF16, -1, -1));
   const int64_t M = h->rows, D = h->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
@@ -1113,7 +1182,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_
                                                                int32_t precision, size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   (void)D;
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
   Carver cv(nullptr);
   float* sc;
@@ -1129,7 +1198,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
                                                      int64_t chunk_rows, int32_t precision, void* ws, size_t ws_bytes,
                                                      void* stream) {
   TRY(check_precision(precision));
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(h, "h", CODA_BF16, -1, -1));
   const int64_t M = h->rows, D = h->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
@@ -1207,7 +1276,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd_workspace(int64_t M
                                                                        size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   (void)D;
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   Carver cv(nullptr);
   float *a, *b, *c, *d, *e, *f;
   int* st;
@@ -1221,7 +1290,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
     int32_t ignore_index, const coda_mat* loss, const coda_mat* lse, const coda_mat* per_row, const coda_mat* n_valid,
     const coda_mat* n_bad, const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_precision(precision));
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(y, "y", CODA_BF16, -1, -1));
   const int64_t M = y->rows, D = y->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
@@ -1294,7 +1363,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M
                                                                        int64_t chunk_rows, int32_t precision,
                                                                        size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
   Carver cv(nullptr);
   float *sc, *Tp, *Tc, *dgp;
@@ -1310,7 +1379,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
     const coda_mat* dres, const coda_mat* dy, const coda_mat* dW, const coda_mat* dg, float beta, int64_t chunk_rows,
     int32_t precision, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_precision(precision));
-  if (precision == CODA_PREC_FP8) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
+  if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(y, "y", CODA_BF16, -1, -1));
   const int64_t M = y->rows, D = y->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");

@@ -27,7 +27,8 @@ hipError_t launch_gemm_fp8(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) 
 }
 
 hipError_t launch_gemm(Prog p, int layout, bool fp8, GemmArgs g, const EpiArgs& e, hipStream_t s) {
-  if (fp8) return layout == LAYOUT_NT ? launch_gemm_fp8(p, g, e, s) : hipErrorInvalidValue;
+  // E4M3 operands: block-scaled when the exponents come with the operands
+  if (fp8) return layout != LAYOUT_NT ? hipErrorInvalidValue : g.sA ? launch_gemm_mx(p, g, e, s) : launch_gemm_fp8(p, g, e, s);
   switch (layout) {
     case LAYOUT_NN: return launch_gemm_nn(p, g, e, s);
     case LAYOUT_NT: return launch_gemm_nt(p, g, e, s);

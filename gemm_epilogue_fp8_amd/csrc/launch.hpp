@@ -42,8 +42,8 @@ hipError_t launch_gemm_nn(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 hipError_t launch_gemm_nt(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 hipError_t launch_gemm_tn(Prog p, int layout, GemmArgs g, const EpiArgs& e, hipStream_t s);
 hipError_t launch_gemm_fp8(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
-// MXFP8 operands (g.sA, g.sB set): Store, StoreF32, RowColStore, Resid,
-// ResidSumsq and SwiGLU
+// MXFP8 operands (g.sA, g.sB set): the programs of the generic entry point
+// and of the block's forward and backward
 hipError_t launch_gemm_mx(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 
 template <class Cfg, class Epi>

@@ -69,7 +69,11 @@ typedef enum coda_dtype { CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 =
 /* GEMM operand precision of the functional entry points. */
 typedef enum coda_precision {
   CODA_PREC_BF16 = 0, /* bf16 operands, fp32 accumulate */
-  CODA_PREC_FP8 = 1   /* OCP E4M3 operands with amax scales, fp32 accumulate */
+  CODA_PREC_FP8 = 1,  /* OCP E4M3 operands with amax scales, fp32 accumulate */
+  CODA_PREC_MXFP8 = 2 /* E4M3 operands with one E8M0 scale per 32 values of the
+                         contracted axis (OCP MX), fp32 accumulate; every
+                         contracted size (hidden, MLP width, tokens of a
+                         backward) a multiple of 128 */
 } coda_precision;
 
 typedef struct coda_mat {
@@ -83,6 +87,10 @@ typedef struct coda_mat {
  * by coda_quantize_weight: q_fwd [N_out, K_in] with one scale per output
  * channel (forward GEMM, contracted axis K_in contiguous) and q_bwd
  * [K_in, N_out] with one scale per input channel (input-gradient GEMM).
+ * For MXFP8 precision the same two copies carry E8M0 block exponents in
+ * word layout instead (see coda_quantize_mxfp8): s_fwd [K_in / 128,
+ * 4 N_out] (blocks along K_in) and s_bwd [N_out / 128, 4 K_in] (blocks
+ * along N_out); coda_quantize_weight makes them when s_fwd has dtype E8M0.
  * bf16 precision reads only `w`. */
 typedef struct coda_weight {
   coda_mat w;

@@ -11,7 +11,7 @@ import pytest
 import coda_inputs as ci
 from oracle import block as ob
 from tests.helpers import assert_bf16, assert_grad, to_dev, to_np, unpack_gu
-from tests.test_gpu_parity import check_block_fp8
+from tests.test_gpu_parity import check_block_fp8, check_block_mx
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -43,6 +43,9 @@ def _block_gpu(shape, P, precision):
 def _check_block(shape, P, f, b, fp8):
     F = ob.block_forward_contract(P, shape, fp8=fp8)
     B = ob.block_backward_contract(P, F, shape, fp8=fp8)
+    if fp8 == "mx":
+        check_block_mx(f, b, F, B)
+        return
     if fp8:
         check_block_fp8(shape, f, b, F, B)
         return
@@ -88,6 +91,16 @@ def test_block_full_size_fp8():
     P = ci.block_inputs(shape, ci.SEEDS["cfg5"])
     f, b = _block_gpu(shape, P, coda.PREC_FP8)
     _check_block(shape, P, f, b, fp8=True)
+
+
+@pytest.mark.timeout(1200)
+def test_block_full_size_mxfp8():
+    """Hidden 8192, MLP 28672, 64 heads, M = 4096 with every GEMM operand in
+    MXFP8 (E4M3, one E8M0 exponent per 32 values of the contracted axis)."""
+    shape = ci.CFG5
+    P = ci.block_inputs(shape, ci.SEEDS["cfg5"])
+    f, b = _block_gpu(shape, P, coda.PREC_MXFP8)
+    _check_block(shape, P, f, b, fp8="mx")
 
 
 @pytest.mark.timeout(900)

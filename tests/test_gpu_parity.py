@@ -460,6 +460,45 @@ def check_block_fp8(shape, f, b, F, B):
         assert rel_norm(v, B[k]) <= 2e-2, (k, rel_norm(v, B[k]))
 
 
+def check_block_mx(f, b, F, B):
+    """MXFP8 block parity: every bf16 output within the fp8 bound
+    6e-2 (1 + |ref|) and 2e-2 norm-wise; the weight and gain gradients within
+    2e-2 norm-wise.  A one-ulp bf16 difference between the sides (fp32 sums
+    in different orders) moves the shared exponent only of the 32-value block
+    whose maximum it is, so no whole row moves as with per-row amax scales."""
+    from tests.helpers import FP8_TOL
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    hg, hu = unpack_gu(f["hgu"])
+    D = f["q"].shape[1]
+    outs = dict(q=f["q"], k=f["k"], v=f["v"], h1=f["h1"], q_pre=f["qk_pre"][:, :D], k_pre=f["qk_pre"][:, D:],
+                hg=hg, hu=hu, a=f["a"], y=f["y"], dht_gu=np.concatenate([dg_, du_], axis=1),
+                dht_qkv=b["dht_qkv"], dh1=b["dh1"], do=b["do"], dx=b["dx"])
+    refs = dict(q=F["q"], k=F["k"], v=F["v"], h1=F["h1"], q_pre=F["q_pre"], k_pre=F["k_pre"], hg=F["hg"],
+                hu=F["hu"], a=F["a"], y=F["y"], dht_gu=B["dht_gu"], dht_qkv=B["dht_qkv"], dh1=B["dh1"],
+                do=B["do"], dx=B["dx"])
+    for k in outs:
+        assert_bf16(k, outs[k], refs[k], tol=FP8_TOL, norm_rel=2e-2)
+    dWg, dWu = unpack_gu(b["dWgu"])
+    grads = dict(dWg=dWg, dWu=dWu, dWqkv=b["dWqkv"], dWo=b["dWo"], dWd=b["dWd"], dg1=b["dg1"], dg2=b["dg2"],
+                 dgq=b["dgq"], dgk=b["dgk"])
+    for k, v in grads.items():
+        assert np.all(np.isfinite(v)), k
+        assert rel_norm(v, B[k]) <= 2e-2, (k, rel_norm(v, B[k]))
+
+
+@pytest.mark.parametrize("shape,seed", [(ci.BlockShape(M=256, D=256, F=384, seq_len=128), 7),
+                                        (ci.BlockShape(M=384, D=384, F=640, seq_len=128), 8)])
+def test_block_mxfp8_forward_backward(shape, seed):
+    """The whole block with every GEMM operand in MXFP8 (E4M3 elements, one
+    E8M0 exponent per 32 values of the contracted axis, applied by the
+    scaled MFMA), against the oracle's contract evaluation in the same
+    format."""
+    P, f, b = _run_block(shape, seed, precision=coda.PREC_MXFP8)
+    F = ob.block_forward_contract(P, shape, fp8="mx")
+    B = ob.block_backward_contract(P, F, shape, fp8="mx")
+    check_block_mx(f, b, F, B)
+
+
 @pytest.mark.parametrize("shape,seed", [(ci.BlockShape(M=4096, D=256, F=352, seq_len=2048), 5)])
 def test_block_backward_split_k(shape, seed):
     """Many tokens, small weights: every weight-gradient GEMM has at most 3
