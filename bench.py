@@ -40,11 +40,16 @@ def block_flops(M, D, F):
     return fwd, 2 * fwd
 
 
+# The sources the dominant kernel (bf16 gate/up GEMM + SwiGLU epilogue) is built from
+DOMINANT_KERNEL_SOURCES = ("coda_device.hpp", "gemm_core.hpp", "epilogues.hpp", "launch.hpp", "gemm_nn.hip")
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources, to tell whether stored counter data is current."""
+    """Hash of the dominant kernel's HIP sources, to tell whether stored
+    counter data is current."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gemm_epilogue_fp8_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in DOMINANT_KERNEL_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -373,17 +373,34 @@ __global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, c
   if ((C & 15) != 0 && lane == 0) *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + C) = uint2{0u, 0u};
 }
 
+// The 64 x 64 bf16 tile X[r0 .., c0 ..] as floats in LDS (positions outside
+// the matrix read 0), for the transposing quantisers: 16-byte loads along X's
+// rows (C % 8 == 0, so a chunk of 8 is wholly in or out), two a thread of
+// 256.  Thread i fills row i / 8, columns 8 (i % 8) .. + 7; with a row stride
+// of 65 floats the 64 lanes of one store instruction hit 64 distinct banks.
+__device__ __forceinline__ void load_tile_t(const uint16_t* X, int64_t ld, int R, int C, int r0, int c0,
+                                            float (*tile)[65]) {
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) {
+    const int rr = i >> 3, cc = (i & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    uint4 w = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[rr][cc + 2 * j] = bf_lo(v[j]);
+      tile[rr][cc + 2 * j + 1] = bf_hi(v[j]);
+    }
+  }
+  __syncthreads();
+}
+
 __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
                                     uint8_t* QT, int64_t ldq, float* scale) {
   // 64 x 64 tile through LDS: read X[r0.., c0..] rows, write QT[c][r0..r0+63]
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 256 threads: 64 x 4
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = r0 + rr, c = c0 + tx;
-    tile[rr][tx] = (r < R && c < C) ? bf2f(X[(int64_t)r * ld + c]) : 0.0f;
-  }
-  __syncthreads();
+  load_tile_t(X, ld, R, C, r0, c0, tile);
   // thread -> (column cc, 16 consecutive rows)
   const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
   const int c = c0 + cc;
@@ -457,12 +474,7 @@ __global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int
                                        uint8_t* S, int64_t lds) {
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = r0 + rr, c = c0 + tx;
-    tile[rr][tx] = (r < R && c < C) ? bf2f(X[(int64_t)r * ld + c]) : 0.0f;
-  }
-  __syncthreads();
+  load_tile_t(X, ld, R, C, r0, c0, tile);
   const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
   float v[16];
   float m = 0.0f;
