@@ -59,7 +59,10 @@ def mat(t: Optional[torch.Tensor]) -> _lib.CodaMat:
         ld = t.stride(0) if rows > 1 else cols
     else:
         raise ValueError("only 1-D and 2-D tensors")
-    m.ptr = t.data_ptr() if t.numel() > 0 or t.data_ptr() else None
+    # an empty view keeps the address of the storage it views (torch reports
+    # 0 for it), so an empty required argument is not taken as absent
+    ptr = t.data_ptr() or (t.untyped_storage().data_ptr() if t.numel() == 0 else 0)
+    m.ptr = ptr or None
     m.dtype, m.rows, m.cols, m.ld = _DT[t.dtype], rows, cols, ld
     return m
 

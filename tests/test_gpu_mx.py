@@ -247,3 +247,28 @@ def test_gemm_mx_full_size_sampled():
     got = out[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), float(np.max(np.abs(got - ref) - bound))
     assert_bf16("sampled out", got, nm.bf16(ref))
+
+
+def test_gemm_mx_degenerate_shapes():
+    """Empty M or N (empty views of allocated buffers: the C ABI takes a NULL
+    pointer as an absent argument) is a no-op that leaves D untouched; a single
+    row and the smallest K (one 128-value word of exponents) still match the
+    oracle."""
+    rng = np.random.default_rng(29)
+    K = 128
+    sentinel = torch.full((64, 64), 3.0, dtype=BF, device=DEV)
+    for M, N in ((0, 64), (64, 0)):
+        A = torch.empty((max(M, 1), K), dtype=torch.float8_e4m3fn, device=DEV)[:M]
+        B = torch.empty((max(N, 1), K), dtype=torch.float8_e4m3fn, device=DEV)[:N]
+        SA = torch.empty((1, 4 * max(M, 1)), dtype=torch.uint8, device=DEV)[:, :4 * M]
+        SB = torch.empty((1, 4 * max(N, 1)), dtype=torch.uint8, device=DEV)[:, :4 * N]
+        coda.gemm_mx([(coda.EPI_STORE_BF16, 0, 0.0)], A, SA, B, SB, sentinel[:M, :N])
+    torch.cuda.synchronize()
+    assert bool((sentinel == 3.0).all())
+    ca, sa = random_mx(rng, 1, K)
+    cb, sb = random_mx(rng, 40, K)
+    D = torch.empty((1, 40), dtype=torch.float32, device=DEV)
+    coda.gemm_mx([(coda.EPI_ACCUM_F32, 0, 0.0)], e4m3_dev(ca), u8(to_words(sa)), e4m3_dev(cb), u8(to_words(sb)), D)
+    torch.cuda.synchronize()
+    A, B = mx_values(ca, sa), mx_values(cb, sb)
+    assert np.all(np.abs(to_np(D) - A @ B.T) <= mfma_fp8_bound(A, B))
