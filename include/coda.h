@@ -236,6 +236,19 @@ coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const 
 
 /* ===================================================================== functional: forward */
 
+/* Precision of the functional entry points (forward and backward alike):
+ *   CODA_PREC_BF16   bf16 GEMM operands;
+ *   CODA_PREC_FP8    E4M3 operands, one amax scale per row of each operand's
+ *                    non-contracted axis, applied by the epilogue; the weight
+ *                    carries coda_quantize_weight's two per-channel copies;
+ *   CODA_PREC_MXFP8  E4M3 operands, one E8M0 exponent per 32 values of the
+ *                    contracted axis, applied by the scaled MFMA; the weight
+ *                    carries the two block-scaled copies; every contracted
+ *                    size must be a multiple of 128 (CODA_ERR_SHAPE otherwise).
+ * Activations are quantised per call into the workspace (the *_workspace
+ * queries size it for the given precision).  The cross-entropy entry points
+ * take CODA_PREC_BF16 only (CODA_ERR_UNSUPPORTED otherwise). */
+
 /* RMSNorm -> Linear -> SwiGLU (config-1 op and the block's gate/up GEMM):
  *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r * (x W~_gu),
  *   out = SiLU(h_gate) * h_up
