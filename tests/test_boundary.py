@@ -168,3 +168,40 @@ def test_mx_validation_codes():
               fake(BF, M, N)) == 2                                             # A not E4M3
     assert gm(fake(E4, M, 256), fake(E8, 2, 4 * M), fake(E4, N, 256), fake(E8, 2, 4 * N),
               fake(BF, M, N + 8)) == 3                                         # D shape
+
+
+def test_mxfp8_functional_validation():
+    """MXFP8 precision: weight dimensions must be multiples of 128, the
+    block-scaled copies must carry E8M0 exponents in word layout, and the
+    tokens of a backward must be a multiple of 128."""
+    L = g.lib()
+    BF, F32, E4, E8 = _lib.CODA_BF16, _lib.CODA_F32, _lib.CODA_E4M3, _lib.CODA_E8M0
+    MX = _lib.PREC_MXFP8
+
+    def weight(K, N, sdt=E8):
+        w = _lib.CodaWeight()
+        w.w = fake(BF, K, N)
+        w.q_fwd, w.q_bwd = fake(E4, N, K), fake(E4, K, N)
+        if sdt == E8:
+            w.s_fwd, w.s_bwd = fake(E8, (K + 127) // 128, 4 * N), fake(E8, (N + 127) // 128, 4 * K)
+        else:
+            w.s_fwd, w.s_bwd = fake(F32, 1, N), fake(F32, 1, K)
+        return w
+
+    def fwd(M, K, N, w):
+        a, z, out = fake(BF, M, K), fake(BF, M, N), fake(BF, M, N)
+        return L.coda_linear_rmsnorm_residual_fwd(C.byref(a), C.byref(w), C.byref(z), C.byref(out), None, MX,
+                                                  None, 0, None)
+
+    assert fwd(64, 192, 256, weight(192, 256)) == 3          # K_in = 192: not a multiple of 128
+    assert fwd(64, 256, 192, weight(256, 192)) == 3          # N_out = 192
+    assert fwd(64, 256, 256, weight(256, 256, F32)) == 2     # per-channel scales given for MXFP8
+    w = weight(256, 256)
+    w.s_bwd = fake(E8, 3, 4 * 256)                           # one word row too many
+    assert fwd(64, 256, 256, w) == 3
+    assert fwd(64, 256, 256, weight(256, 256)) == 6          # valid; the activation copy needs a workspace
+    # backward with 200 tokens
+    d_out, a, dW = fake(BF, 200, 256), fake(BF, 200, 256), fake(F32, 256, 256)
+    st = L.coda_linear_rmsnorm_residual_bwd(C.byref(d_out), C.byref(a), C.byref(weight(256, 256)), None,
+                                            C.byref(dW), 0.0, MX, None, 0, None)
+    assert st == 3
