@@ -82,6 +82,7 @@ def parse():
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
     ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
+    ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -149,6 +150,63 @@ def mx_leg(warmup, steps):
 
 OPERANDS = {False: "", True: " with E4M3 operands (per-row / per-column amax scales)",
             "mx": " with MXFP8 operands (E4M3, one E8M0 exponent per 32 values)"}
+
+
+def ce_leg(warmup, steps):
+    """Linear + cross-entropy forward and backward at h [8192, 2048],
+    W_vocab [2048, 128256] with 410 ignored rows (the logits are never
+    materialised; the backward recomputes them), plain and with the final
+    RMSNorm folded in.  Synthetic inputs drawn on the device from a seeded
+    generator: h ~ N(0, 1), W ~ N(0, 1/2048), labels uniform in [0, V)."""
+    import torch
+    import gemm_epilogue_fp8_amd as coda
+    M, D, V = 8192, 2048, 128256
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev).manual_seed(11)
+    h = torch.randn((M, D), generator=gen, device=dev).to(torch.bfloat16)
+    W = (torch.randn((D, V), generator=gen, device=dev) * D ** -0.5).to(torch.bfloat16)
+    labels = torch.randint(0, V, (M,), generator=gen, device=dev, dtype=torch.int32)
+    labels[torch.randperm(M, generator=gen, device=dev)[:410]] = -100
+    g = (1 + 0.1 * torch.randn(D, generator=gen, device=dev)).float()
+    Wt = coda.fold_gain(W, g, torch.empty_like(W))
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    loss, lse, nv, r = f32(1), f32(M), torch.empty(1, dtype=torch.int32, device=dev), f32(M)
+    dh = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    dW, dg = f32(D, V), f32(D)
+
+    def ev_ms(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    fwd = lambda: coda.linear_cross_entropy_fwd(h, W, labels, loss, lse, nv)
+    out = {"workload": f"linear + cross-entropy, h [{M}, {D}], W_vocab [{D}, {V}], 410 ignored rows",
+           "model_gflop": round(3 * 2 * M * D * V / 1e9, 1), "with_recompute_gflop": round(4 * 2 * M * D * V / 1e9, 1)}
+    out["fwd_ms"] = round(ev_ms(fwd), 4)
+    for chunk in (0, 1024):
+        bwd = lambda: coda.linear_cross_entropy_bwd(h, W, labels, lse, nv, 1.0, dh, dW, beta=1.0, chunk_rows=chunk)
+        ms = ev_ms(bwd)
+        out[f"bwd_ms_chunk{chunk}"] = round(ms, 4)
+    best = min(out["bwd_ms_chunk0"], out["bwd_ms_chunk1024"])
+    tot = out["fwd_ms"] + best
+    out["fwd_bwd_ms"] = round(tot, 4)
+    out["model_tflops"] = round(3 * 2 * M * D * V / (tot * 1e-3) / 1e12, 1)
+    out["hw_tflops"] = round(4 * 2 * M * D * V / (tot * 1e-3) / 1e12, 1)
+    nfwd = lambda: coda.linear_rmsnorm_cross_entropy_fwd(h, Wt, 1e-6, labels, loss, lse, nv, r_out=r)
+    out["norm_fwd_ms"] = round(ev_ms(nfwd), 4)
+    nbwd = lambda: coda.linear_rmsnorm_cross_entropy_bwd(h, r, Wt, W, g, labels, lse, nv, 1.0, dh, dW, dg, beta=1.0,
+                                                        chunk_rows=0)
+    out["norm_bwd_ms"] = round(ev_ms(nbwd), 4)
+    del h, W, Wt, dW, dh
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(shape_full, seed, rows, fp8):
@@ -303,6 +361,7 @@ def main():
 
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
     mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
+    ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
     fwd, bwd = block_flops(M, cfg.D, cfg.F)
     tflops = (fwd + bwd) / (ms * 1e-3) / 1e12
     f3_flop = 2 * M * (2 * cfg.F) * cfg.D
@@ -337,6 +396,7 @@ def main():
                      "flop_per_launch": f3_flop, "traffic": stored_traffic(args.config, precision)},
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,
+        "cross_entropy": ce,
     }
     print(json.dumps(out))
 
