@@ -298,6 +298,15 @@ __global__ void ce_finish_loss_kernel(const float* per_row, const int* status, i
   }
 }
 
+// out[r, c] = bf16(X[r, c]) for fp32 X (C % 4 == 0), 4 values a thread
+__global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, int64_t ldo, int R, int C) {
+  const int r = blockIdx.y;
+  for (int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4; c < C; c += gridDim.x * blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(X + (int64_t)r * ldx + c);
+    *reinterpret_cast<uint2*>(out + (int64_t)r * ldo + c) = uint2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+  }
+}
+
 __global__ void ce_scale_kernel(const int* n_valid, float dloss, float* scale) {
   const int n = *n_valid;
   *scale = n > 0 ? dloss / (float)n : 0.0f;

@@ -55,6 +55,8 @@ __global__ void ce_finish_loss_kernel(const float* per_row, const int* status, i
                                       int* n_valid, int* n_bad);
 // scale[0] = dloss / n_valid (0 when n_valid == 0)
 __global__ void ce_scale_kernel(const int* n_valid, float dloss, float* scale);
+// out = bf16(X), fp32 [R, C] -> bf16 (C % 4 == 0); grid (x, R)
+__global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, int64_t ldo, int R, int C);
 // E4M3 quantisation with amax over the contracted axis.
 //   axis 1: Q[r, c] with one scale per row  r  (Q keeps the [R, C] layout)
 //   axis 0: Q^T[c, r] with one scale per column c (Q written transposed, so the

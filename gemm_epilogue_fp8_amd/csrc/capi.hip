@@ -1172,22 +1172,36 @@ extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const co
   return check_launch("cross_entropy_fwd: loss");
 }
 
-static size_t ce_bwd_layout(Carver& cv, int64_t M, int64_t V, int64_t chunk, float** scale, uint16_t** G) {
+// The backward recomputes the logits into a bf16 buffer G.  With chunk_rows
+// = 0 (or >= M) G holds all M x V values and one pass of three GEMMs does the
+// work.  Otherwise G is bounded by chunk_rows x V values and the recompute
+// runs over vocabulary slices of vc columns (a multiple of 256): each slice's
+// weight-gradient GEMM writes its own columns of dW (no read-modify-write of
+// dW across slices) and its dh GEMM accumulates into an fp32 [M, D] buffer,
+// rounded to bf16 once at the end.
+static int64_t ce_slice_cols(int64_t M, int64_t V, int64_t chunk_rows) {
+  if (chunk_rows <= 0 || chunk_rows >= M) return V;
+  const int64_t vc = chunk_rows * V / M / 256 * 256;
+  return std::min(V, std::max<int64_t>(vc, 256));
+}
+
+static size_t ce_bwd_layout(Carver& cv, int64_t M, int64_t D, int64_t V, int64_t vc, float** scale, uint16_t** G,
+                            float** dh_acc) {
   *scale = cv.take<float>(1);
-  *G = cv.take<uint16_t>((size_t)chunk * ((V + 7) / 8 * 8));
+  *G = cv.take<uint16_t>((size_t)M * ((vc + 7) / 8 * 8));
+  *dh_acc = vc < V ? cv.take<float>((size_t)M * D) : nullptr;
   return cv.off;
 }
 
 extern "C" coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
                                                                int32_t precision, size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
-  (void)D;
   if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
-  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
   Carver cv(nullptr);
   float* sc;
   uint16_t* G;
-  ce_bwd_layout(cv, M, V, chunk, &sc, &G);
+  float* acc;
+  ce_bwd_layout(cv, M, D, V, ce_slice_cols(M, V, chunk_rows), &sc, &G, &acc);
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -1210,44 +1224,59 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
   TRY(check_mat(dh, "dh", CODA_BF16, M, D));
   TRY(check_mat(dW, "dW", CODA_F32, D, V));
   if (ignore_index != -100) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy_bwd: ignore_index must be -100 in this build");
-  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  const int64_t vc = ce_slice_cols(M, V, chunk_rows);
   Carver cv(ws);
   float* scale;
   uint16_t* G;
-  ce_bwd_layout(cv, M, V, chunk, &scale, &G);
+  float* dh_acc;
+  ce_bwd_layout(cv, M, D, V, vc, &scale, &G, &dh_acc);
   TRY(ws_check(cv, ws_bytes, ws));
+  if (M == 0) return CODA_OK;
   hipStream_t s = S(stream);
-  const int64_t ldG = (V + 7) / 8 * 8;
+  const int64_t ldG = (vc + 7) / 8 * 8;
   hipLaunchKernelGGL(ce_scale_kernel, dim3(1), dim3(1), 0, s, static_cast<const int*>(n_valid->ptr), dloss, scale);
   TRY(check_launch("cross_entropy_bwd: scale"));
   const uint16_t* hp = static_cast<const uint16_t*>(h->ptr);
+  const uint16_t* Wp = static_cast<const uint16_t*>(W->w.ptr);
   const int* lab = static_cast<const int*>(labels->ptr);
   const float* lsep = static_cast<const float*>(lse->ptr);
-  for (int64_t c0 = 0; c0 < M; c0 += chunk) {
-    const int64_t mc = std::min(chunk, M - c0);
-    {  // recompute the logits of the chunk into G
+  for (int64_t v0 = 0; v0 < V; v0 += vc) {
+    const int64_t nv = std::min(vc, V - v0);
+    {  // recompute the logits of the slice into G: G = bf16(exp(z - lse) - onehot)
       EpiArgs e = epi0();
       e.out = G; e.ld_out = ldG;
-      e.labels = lab + c0;
-      e.rowvec = lsep + c0;
-      GemmArgs g = gemm_args(hp + c0 * h->ld, h->ld, W->w.ptr, W->w.ld, mc, V, D);
+      e.labels = lab;
+      e.rowvec = lsep;
+      e.col_offset = (int)v0;
+      GemmArgs g = gemm_args(hp, h->ld, Wp + v0, W->w.ld, M, nv, D);
       TRY(launched(launch_gemm(Prog::CrossEntropyG, LAYOUT_NN, false, g, e, s), "cross_entropy_bwd: G"));
     }
-    {  // dh = s G W^T
+    {  // dh = s G W^T (bf16 at once with one slice, else accumulated in fp32)
       EpiArgs e = epi0();
-      e.out = static_cast<uint16_t*>(dh->ptr) + c0 * dh->ld; e.ld_out = dh->ld;
       e.alpha_dev = scale;
-      GemmArgs g = gemm_args(G, ldG, W->w.ptr, W->w.ld, mc, D, V);
-      TRY(launched(launch_gemm(Prog::StoreAlphaDev, LAYOUT_NT, false, g, e, s), "cross_entropy_bwd: dh"));
+      GemmArgs g = gemm_args(G, ldG, Wp + v0, W->w.ld, M, D, nv);
+      if (vc == V) {
+        e.out = dh->ptr; e.ld_out = dh->ld;
+        TRY(launched(launch_gemm(Prog::StoreAlphaDev, LAYOUT_NT, false, g, e, s), "cross_entropy_bwd: dh"));
+      } else {
+        e.out = dh_acc; e.ld_out = D;
+        e.beta = v0 == 0 ? 0.0f : 1.0f;
+        TRY(launched(launch_gemm(Prog::F32AlphaDev, LAYOUT_NT, false, g, e, s), "cross_entropy_bwd: dh"));
+      }
     }
-    {  // dW = beta dW + s h^T G
+    {  // dW[:, v0 : v0 + nv] = beta dW + s h^T G
       EpiArgs e = epi0();
-      e.out = dW->ptr; e.ld_out = dW->ld;
-      e.beta = c0 == 0 ? beta : 1.0f;
+      e.out = static_cast<float*>(dW->ptr) + v0; e.ld_out = dW->ld;
+      e.beta = beta;
       e.alpha_dev = scale;
-      GemmArgs g = gemm_args(hp + c0 * h->ld, h->ld, G, ldG, D, V, mc);
+      GemmArgs g = gemm_args(hp, h->ld, G, ldG, D, nv, M);
       TRY(launched(launch_gemm(Prog::F32AlphaDev, LAYOUT_TN, false, g, e, s), "cross_entropy_bwd: dW"));
     }
+  }
+  if (vc < V) {
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((D / 4 + 255) / 256), (unsigned)M), dim3(256), 0, s,
+                       dh_acc, D, static_cast<uint16_t*>(dh->ptr), dh->ld, (int)M, (int)D);
+    TRY(check_launch("cross_entropy_bwd: dh"));
   }
   return CODA_OK;
 }

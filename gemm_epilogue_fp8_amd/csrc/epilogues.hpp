@@ -67,6 +67,7 @@ struct EpiArgs {
   float* rowvec_out2;                  // second row vector output (CE forward through a norm: r)
   int64_t split_stride;                // split K: fp32 elements between the slices' outputs
   int64_t split_pstride;               // split K: floats between the slices' row partials
+  int col_offset;                      // CE gradient: global index of the tile's column 0 minus n0
 };
 
 template <class Cfg>
@@ -976,7 +977,7 @@ struct EpiCrossEntropyGrad {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             zv[t] = NORM ? r * acc.c[i][j][4 * q + t] : acc.c[i][j][4 * q + t];
-            const float p = __expf(zv[t] - lse) - (n + t == y ? 1.0f : 0.0f);
+            const float p = __expf(zv[t] - lse) - (n + e.col_offset + t == y ? 1.0f : 0.0f);
             gv[t] = valid ? (NORM ? r * p : p) : 0.0f;
           }
           const uint2 pk = pack_bf4(gv);

@@ -12,6 +12,7 @@ hipError_t launch_gemm_nt(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
     case Prog::DSigmoid: return launch_one<CfgNT, EpiDSigmoid<CfgNT>>(g, e, s);
     case Prog::NormCorr: return launch_one<CfgNT, EpiNormCorrection<CfgNT>>(g, e, s);
     case Prog::StoreAlphaDev: return launch_one<CfgNT, EpiLinear<CfgNT, EL_ALPHADEV>>(g, e, s);
+    case Prog::F32AlphaDev: return launch_one<CfgNT, EpiLinear<CfgNT, EL_F32OUT | EL_ALPHADEV>>(g, e, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -357,9 +357,15 @@ coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* 
                                           const coda_mat* n_bad, int32_t precision, void* ws, size_t ws_bytes,
                                           void* stream);
 
-/* Backward: recompute z per chunk of `chunk_rows` rows (0 = all rows),
- * G = bf16(exp(z - lse) - onehot(label)) (0 on ignored rows), s = dloss / n_valid,
- *   dh = bf16(s * G W^T) [M, D],  dW = beta dW + s * h^T G (fp32 [D, V]). */
+/* Backward: recompute z, G = bf16(exp(z - lse) - onehot(label)) (0 on
+ * ignored rows), s = dloss / n_valid,
+ *   dh = bf16(s * G W^T) [M, D],  dW = beta dW + s * h^T G (fp32 [D, V]).
+ * chunk_rows bounds the recomputed logits: 0 (or >= M) recomputes all M x V
+ * at once; otherwise the buffer holds about chunk_rows x V values and the
+ * recompute runs over vocabulary slices of that many values (a multiple of
+ * 256 columns), each slice writing its own columns of dW, with dh summed in
+ * fp32 over the slices and rounded to bf16 once (the workspace then also
+ * holds an fp32 [M, D] buffer). */
 coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
                                                     int32_t precision, size_t* bytes);
 coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
