@@ -201,9 +201,10 @@ def ce_leg(warmup, steps):
     out["hw_tflops"] = round(4 * 2 * M * D * V / (tot * 1e-3) / 1e12, 1)
     nfwd = lambda: coda.linear_rmsnorm_cross_entropy_fwd(h, Wt, 1e-6, labels, loss, lse, nv, r_out=r)
     out["norm_fwd_ms"] = round(ev_ms(nfwd), 4)
-    nbwd = lambda: coda.linear_rmsnorm_cross_entropy_bwd(h, r, Wt, W, g, labels, lse, nv, 1.0, dh, dW, dg, beta=1.0,
-                                                        chunk_rows=0)
-    out["norm_bwd_ms"] = round(ev_ms(nbwd), 4)
+    for chunk in (0, 1024):
+        nbwd = lambda: coda.linear_rmsnorm_cross_entropy_bwd(h, r, Wt, W, g, labels, lse, nv, 1.0, dh, dW, dg,
+                                                            beta=1.0, chunk_rows=chunk)
+        out[f"norm_bwd_ms_chunk{chunk}"] = round(ev_ms(nbwd), 4)
     del h, W, Wt, dW, dh
     torch.cuda.empty_cache()
     return out

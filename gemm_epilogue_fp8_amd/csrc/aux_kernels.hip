@@ -300,10 +300,28 @@ __global__ void ce_finish_loss_kernel(const float* per_row, const int* status, i
 
 // out[r, c] = bf16(X[r, c]) for fp32 X (C % 4 == 0), 4 values a thread
 __global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, int64_t ldo, int R, int C) {
-  const int r = blockIdx.y;
-  for (int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4; c < C; c += gridDim.x * blockDim.x * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(X + (int64_t)r * ldx + c);
-    *reinterpret_cast<uint2*>(out + (int64_t)r * ldo + c) = uint2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+  for (int r = blockIdx.y; r < R; r += gridDim.y)
+    for (int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4; c < C; c += gridDim.x * blockDim.x * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(X + (int64_t)r * ldx + c);
+      *reinterpret_cast<uint2*>(out + (int64_t)r * ldo + c) = uint2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+    }
+}
+
+__global__ void norm_corr_finish_kernel(const float* acc, int64_t lda, const uint16_t* y, int64_t ldy, const float* cr,
+                                        const float* scale, const uint16_t* res, int64_t ldr, uint16_t* out,
+                                        int64_t ldo, int R, int C) {
+  for (int r = blockIdx.y; r < R; r += gridDim.y) {
+    const float sc = *scale * cr[r];
+    for (int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4; c < C; c += gridDim.x * blockDim.x * 4) {
+      const float4 a = *reinterpret_cast<const float4*>(acc + (int64_t)r * lda + c);
+      const uint2 yw = *reinterpret_cast<const uint2*>(y + (int64_t)r * ldy + c);
+      float v[4] = {a.x - sc * bf_lo(yw.x), a.y - sc * bf_hi(yw.x), a.z - sc * bf_lo(yw.y), a.w - sc * bf_hi(yw.y)};
+      if (res) {
+        const uint2 rw = *reinterpret_cast<const uint2*>(res + (int64_t)r * ldr + c);
+        v[0] += bf_lo(rw.x); v[1] += bf_hi(rw.x); v[2] += bf_lo(rw.y); v[3] += bf_hi(rw.y);
+      }
+      *reinterpret_cast<uint2*>(out + (int64_t)r * ldo + c) = uint2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+    }
   }
 }
 

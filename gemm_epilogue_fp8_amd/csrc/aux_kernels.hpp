@@ -57,6 +57,12 @@ __global__ void ce_finish_loss_kernel(const float* per_row, const int* status, i
 __global__ void ce_scale_kernel(const int* n_valid, float dloss, float* scale);
 // out = bf16(X), fp32 [R, C] -> bf16 (C % 4 == 0); grid (x, R)
 __global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, int64_t ldo, int R, int C);
+// RMSNorm backward correction after a product accumulated in fp32 over
+// slices: out[r][c] = bf16(acc[r][c] - (*scale) cr[r] y[r][c] + res[r][c])
+// (res optional), with acc already scaled; grid (x, R), C % 4 == 0.
+__global__ void norm_corr_finish_kernel(const float* acc, int64_t lda, const uint16_t* y, int64_t ldy, const float* cr,
+                                        const float* scale, const uint16_t* res, int64_t ldr, uint16_t* out,
+                                        int64_t ldo, int R, int C);
 // E4M3 quantisation with amax over the contracted axis.
 //   axis 1: Q[r, c] with one scale per row  r  (Q keeps the [R, C] layout)
 //   axis 0: Q^T[c, r] with one scale per column c (Q written transposed, so the

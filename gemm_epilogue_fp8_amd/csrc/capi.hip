@@ -1179,6 +1179,9 @@ extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const co
 // weight-gradient GEMM writes its own columns of dW (no read-modify-write of
 // dW across slices) and its dh GEMM accumulates into an fp32 [M, D] buffer,
 // rounded to bf16 once at the end.
+// rows of a (x, rows) grid whose kernel strides over rows by gridDim.y
+static unsigned row_grid(int64_t rows) { return (unsigned)std::min<int64_t>(rows, 65535); }
+
 static int64_t ce_slice_cols(int64_t M, int64_t V, int64_t chunk_rows) {
   if (chunk_rows <= 0 || chunk_rows >= M) return V;
   const int64_t vc = chunk_rows * V / M / 256 * 256;
@@ -1274,7 +1277,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
     }
   }
   if (vc < V) {
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((D / 4 + 255) / 256), (unsigned)M), dim3(256), 0, s,
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((D / 4 + 255) / 256), row_grid(M)), dim3(256), 0, s,
                        dh_acc, D, static_cast<uint16_t*>(dh->ptr), dh->ld, (int)M, (int)D);
     TRY(check_launch("cross_entropy_bwd: dh"));
   }
@@ -1378,13 +1381,14 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
   return check_launch("rmsnorm_cross_entropy_fwd: loss");
 }
 
-static size_t nce_bwd_layout(Carver& cv, int64_t M, int64_t D, int64_t V, int64_t chunk, float** scale, uint16_t** G,
-                             float** Tp, float** Tc, float** dgp) {
+static size_t nce_bwd_layout(Carver& cv, int64_t M, int64_t D, int64_t V, int64_t vc, float** scale, uint16_t** G,
+                             float** Tp, float** Tc, float** dgp, float** dy_acc) {
   *scale = cv.take<float>(1);
-  *G = cv.take<uint16_t>((size_t)chunk * ((V + 7) / 8 * 8));
-  *Tp = cv.take<float>((size_t)coda_partials_cols(V) * chunk);
-  *Tc = cv.take<float>(chunk);
+  *G = cv.take<uint16_t>((size_t)M * ((vc + 7) / 8 * 8));
+  *Tp = cv.take<float>((size_t)coda_partials_cols(V) * M);
+  *Tc = cv.take<float>(M);
   *dgp = cv.take<float>((size_t)coda_partials_cols(V) * D);
+  *dy_acc = vc < V ? cv.take<float>((size_t)M * D) : nullptr;
   return cv.off;
 }
 
@@ -1393,11 +1397,10 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M
                                                                        size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
-  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
   Carver cv(nullptr);
-  float *sc, *Tp, *Tc, *dgp;
+  float *sc, *Tp, *Tc, *dgp, *acc;
   uint16_t* G;
-  nce_bwd_layout(cv, M, D, V, chunk, &sc, &G, &Tp, &Tc, &dgp);
+  nce_bwd_layout(cv, M, D, V, ce_slice_cols(M, V, chunk_rows), &sc, &G, &Tp, &Tc, &dgp, &acc);
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -1426,64 +1429,91 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
   TRY(check_vec(dg, "dg", CODA_F32, D));
   if (ignore_index != -100)
     return fail(CODA_ERR_UNSUPPORTED, "rmsnorm_cross_entropy_bwd: ignore_index must be -100 in this build");
-  const int64_t chunk = (chunk_rows <= 0 || chunk_rows > M) ? M : chunk_rows;
+  const int64_t vc = ce_slice_cols(M, V, chunk_rows);
   Carver cv(ws);
-  float *scale, *Tp, *Tc, *dgp;
+  float *scale, *Tp, *Tc, *dgp, *dy_acc;
   uint16_t* G;
-  nce_bwd_layout(cv, M, D, V, chunk, &scale, &G, &Tp, &Tc, &dgp);
+  nce_bwd_layout(cv, M, D, V, vc, &scale, &G, &Tp, &Tc, &dgp, &dy_acc);
   TRY(ws_check(cv, ws_bytes, ws));
+  if (M == 0) return CODA_OK;
   hipStream_t s = S(stream);
-  const int64_t ldG = (V + 7) / 8 * 8;
+  const int64_t ldG = (vc + 7) / 8 * 8;
   const int nT = (int)coda_partials_cols(V);
   hipLaunchKernelGGL(ce_scale_kernel, dim3(1), dim3(1), 0, s, static_cast<const int*>(n_valid->ptr), dloss, scale);
   TRY(check_launch("rmsnorm_cross_entropy_bwd: scale"));
   const uint16_t* yp = static_cast<const uint16_t*>(y->ptr);
+  const uint16_t* Wp = static_cast<const uint16_t*>(W->w.ptr);
+  const uint16_t* Wu = static_cast<const uint16_t*>(W_unfolded->ptr);
   const int* lab = static_cast<const int*>(labels->ptr);
   const float* lsep = static_cast<const float*>(lse->ptr);
   const float* rp = static_cast<const float*>(r->ptr);
-  for (int64_t c0 = 0; c0 < M; c0 += chunk) {
-    const int64_t mc = std::min(chunk, M - c0);
-    {  // recompute z = r (y W~) for the chunk: G~ = bf16(r (p - onehot)), T partials
+  const uint16_t* dresp = present(dres) ? static_cast<const uint16_t*>(dres->ptr) : nullptr;
+  // One pass when the whole G~ fits: the dy GEMM then needs T complete first.
+  // Over vocabulary slices (vc a multiple of the 256-column partial tiles),
+  // each slice adds its share of s G~ W~^T into an fp32 [M, D] buffer and
+  // writes its own columns of dW and its own T and gain partial columns; T
+  // and the correction come after the last slice.
+  for (int64_t v0 = 0; v0 < V; v0 += vc) {
+    const int64_t nv = std::min(vc, V - v0);
+    const int64_t pc = v0 / kBN;   // first partial column of the slice
+    {  // recompute z = r (y W~) for the slice: G~ = bf16(r (p - onehot)), T partials
       EpiArgs e = epi0();
       e.out = G; e.ld_out = ldG;
-      e.labels = lab + c0;
-      e.rowvec = lsep + c0;
-      e.rowvec2 = rp + c0;
-      e.partial_out = Tp;
-      GemmArgs g = gemm_args(yp + c0 * y->ld, y->ld, W->w.ptr, W->w.ld, mc, V, D);
+      e.labels = lab;
+      e.rowvec = lsep;
+      e.rowvec2 = rp;
+      e.col_offset = (int)v0;
+      e.partial_out = Tp + pc * M;
+      GemmArgs g = gemm_args(yp, y->ld, Wp + v0, W->w.ld, M, nv, D);
       TRY(launched(launch_gemm(Prog::CrossEntropyGNorm, LAYOUT_NN, false, g, e, s), "rmsnorm_cross_entropy_bwd: G"));
     }
-    hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((mc + 255) / 256)), dim3(256), 0, s, Tp, nT, (int)mc, 0,
-                       (const float*)nullptr, 0, 0.0f, Tc);
-    TRY(check_launch("rmsnorm_cross_entropy_bwd: finish T"));
-    {  // dy = s (G~ W~^T - (r T / D) y) + dres
+    if (vc == V) {
+      hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, Tp, nT, (int)M, 0,
+                         (const float*)nullptr, 0, 0.0f, Tc);
+      TRY(check_launch("rmsnorm_cross_entropy_bwd: finish T"));
+      // dy = s (G~ W~^T - (r T / D) y) + dres
       EpiArgs e = epi0();
-      e.out = static_cast<uint16_t*>(dy->ptr) + c0 * dy->ld; e.ld_out = dy->ld;
-      e.aux0 = yp + c0 * y->ld; e.ld_aux0 = y->ld;
-      if (present(dres)) { e.aux1 = static_cast<const uint16_t*>(dres->ptr) + c0 * dres->ld; e.ld_aux1 = dres->ld; }
-      e.rowvec = rp + c0;
+      e.out = dy->ptr; e.ld_out = dy->ld;
+      e.aux0 = yp; e.ld_aux0 = y->ld;
+      if (dresp) { e.aux1 = dresp; e.ld_aux1 = dres->ld; }
+      e.rowvec = rp;
       e.row_partials = Tc;
       e.n_row_partials = 1;
       e.norm_dim = (int)D;
       e.alpha_dev = scale;
-      GemmArgs g = gemm_args(G, ldG, W->w.ptr, W->w.ld, mc, D, V);
+      GemmArgs g = gemm_args(G, ldG, Wp, W->w.ld, M, D, V);
       TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, false, g, e, s), "rmsnorm_cross_entropy_bwd: dy"));
-    }
-    const float b = c0 == 0 ? beta : 1.0f;
-    {  // dW = b dW + s g (y^T G~), gain partials s sum_v W (y^T G~)
+    } else {  // dy_acc (+)= s G~ W~^T over the slice
       EpiArgs e = epi0();
-      e.out = dW->ptr; e.ld_out = dW->ld;
-      e.beta = b;
-      e.aux0 = W_unfolded->ptr; e.ld_aux0 = W_unfolded->ld;
-      e.rowvec = fptr(gvec);
-      e.partial_out = dgp;
+      e.out = dy_acc; e.ld_out = D;
+      e.beta = v0 == 0 ? 0.0f : 1.0f;
       e.alpha_dev = scale;
-      GemmArgs g = gemm_args(yp + c0 * y->ld, y->ld, G, ldG, D, V, mc);
+      GemmArgs g = gemm_args(G, ldG, Wp + v0, W->w.ld, M, D, nv);
+      TRY(launched(launch_gemm(Prog::F32AlphaDev, LAYOUT_NT, false, g, e, s), "rmsnorm_cross_entropy_bwd: dy"));
+    }
+    {  // dW[:, v0 : v0 + nv] = beta dW + s g (y^T G~), gain partials s sum_v W (y^T G~)
+      EpiArgs e = epi0();
+      e.out = static_cast<float*>(dW->ptr) + v0; e.ld_out = dW->ld;
+      e.beta = beta;
+      e.aux0 = Wu + v0; e.ld_aux0 = W_unfolded->ld;
+      e.rowvec = fptr(gvec);
+      e.partial_out = dgp + pc * D;
+      e.alpha_dev = scale;
+      GemmArgs g = gemm_args(yp, y->ld, G, ldG, D, nv, M);
       TRY(launched(launch_gemm(Prog::WgradGain, LAYOUT_TN, false, g, e, s), "rmsnorm_cross_entropy_bwd: dW"));
     }
-    TRY(sum_partials_launch(dgp, nT, (int)D, b, static_cast<float*>(dg->ptr), s));
   }
-  return CODA_OK;
+  if (vc < V && M > 0) {
+    // c = r T / D, then dy = dy_acc - s c y + dres
+    hipLaunchKernelGGL(rows_finish_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, Tp, nT, (int)M, 2, rp,
+                       (int)D, 0.0f, Tc);
+    TRY(check_launch("rmsnorm_cross_entropy_bwd: finish T"));
+    hipLaunchKernelGGL(norm_corr_finish_kernel, dim3((unsigned)((D / 4 + 255) / 256), row_grid(M)), dim3(256), 0, s,
+                       dy_acc, D, yp, y->ld, Tc, scale, dresp, dresp ? dres->ld : 0, static_cast<uint16_t*>(dy->ptr),
+                       dy->ld, (int)M, (int)D);
+    TRY(check_launch("rmsnorm_cross_entropy_bwd: dy"));
+  }
+  return sum_partials_launch(dgp, nT, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }
 
 // ======================================================================== RMSNorm -> Linear -> sigmoid

@@ -427,12 +427,18 @@ coda_status coda_linear_rmsnorm_cross_entropy_fwd(const coda_mat* y, const coda_
                                                   const coda_mat* n_bad, const coda_mat* r_out, int32_t precision,
                                                   void* ws, size_t ws_bytes, void* stream);
 
-/* Backward, recomputing z per chunk of `chunk_rows` rows (0 = all rows):
+/* Backward, recomputing z:
  *   G~ = bf16(r (exp(z - lse) - onehot)) (0 on ignored rows), s = dloss / n_valid,
  *   T = s sum_v G~ z,  dy = bf16(s G~ W~^T - (r T / D) y + dres),
  *   dW = beta dW + s g (y^T G~) (fp32 [D, V]),  dg = beta dg + s sum_v W (y^T G~) (fp32 1 x D).
  * r: the forward's r_out; W_unfolded: W without the gain; g: fp32 1 x D;
  * dres: optional bf16 [M, D] gradient arriving along the residual stream.
+ * chunk_rows bounds the recomputed logits as in coda_linear_cross_entropy_bwd:
+ * 0 (or >= M) recomputes all M x V at once; otherwise the recompute runs over
+ * vocabulary slices of about chunk_rows x V values (a multiple of 256
+ * columns), each writing its own columns of dW, with s G~ W~^T summed in
+ * fp32 over the slices and the correction and rounding applied once after
+ * the last (the workspace then also holds an fp32 [M, D] buffer).
  * With M = 0, dW and dg are left unchanged.  ignore_index must be -100. */
 coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
                                                             int32_t precision, size_t* bytes);

@@ -172,7 +172,8 @@ def test_cross_entropy_full_size():
 def test_rmsnorm_cross_entropy_full_size():
     """The cross-entropy workload with the final RMSNorm folded in: y
     [8192, 2048] (the h of the cross-entropy inputs), gain 1 + 0.1 N(0, 1),
-    W_vocab [2048, 128256], 410 ignored rows, chunks of 1024 rows."""
+    W_vocab [2048, 128256], 410 ignored rows, the recomputed logits bounded
+    to 1024 rows' worth (vocabulary slices of 15872 columns)."""
     from tests.test_gpu_parity import run_rmsnorm_ce
     shape = ci.CFG4
     P = ci.ce_inputs(shape, ci.SEEDS["cfg4"])

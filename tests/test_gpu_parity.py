@@ -330,11 +330,14 @@ def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_
                 n_bad=int(nbad.item()), r=to_np(r), dy=to_np(dy), dW=to_np(dW), dg=to_np(dg))
 
 
-@pytest.mark.parametrize("M,D,V,chunk,use_partials", [(300, 256, 1000, 0, False), (260, 128, 784, 100, True)])
+@pytest.mark.parametrize("M,D,V,chunk,use_partials",
+                         [(300, 256, 1000, 0, False), (300, 256, 1000, 150, False), (260, 128, 784, 100, True)])
 def test_rmsnorm_cross_entropy(M, D, V, chunk, use_partials):
-    """Final RMSNorm folded into the LM head: z = r (y W~).  The ragged case
-    recomputes the logits in 3 chunks, takes 3 given sum-of-squares partials,
-    adds a residual-stream gradient and accumulates onto fp32 priors."""
+    """Final RMSNorm folded into the LM head: z = r (y W~).  A bounded
+    logits buffer (chunk > 0) makes the backward recompute over 4
+    vocabulary slices of 256 columns (the last one ragged: 232 or 16).  The
+    last case also takes 3 given sum-of-squares partials, adds a
+    residual-stream gradient and accumulates onto fp32 priors."""
     V = V - V % 8
     rng = np.random.default_rng(M)
     y = rand_bf16(rng, M, D)
