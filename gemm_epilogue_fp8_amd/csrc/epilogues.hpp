@@ -145,14 +145,34 @@ struct StageF32 {
 // Workgroup-wide row-contiguous moves between a staging tile and global
 // memory.  dst(m_local, n_local) returns the global address of the 16-byte
 // chunk that starts at local (row, column), or nullptr to skip it.
+// The store reads a batch of chunks from LDS before storing any of them, so
+// one LDS round trip serves the whole batch instead of each store waiting
+// for its own read.
 template <class Cfg, int R, int C, class Dst>
 __device__ __forceinline__ void stage_store_bf(const char* s, int tid, Dst dst) {
   using S = StageBF<R, C>;
-#pragma unroll 4
-  for (int id = tid; id < R * S::CPR; id += Cfg::T) {
-    const int r = id / S::CPR, ch = id % S::CPR;
-    uint16_t* p = dst(r, ch * 8);
-    if (p) *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(s + S::off(r, ch));
+  constexpr int ITER = R * S::CPR / Cfg::T;           // chunks a thread stores
+  static_assert(R * S::CPR % Cfg::T == 0, "whole rounds of 16-byte chunks");
+  constexpr int NB = ITER < 8 ? ITER : 8;             // LDS reads in flight
+  static_assert(ITER % NB == 0, "whole batches");
+#pragma unroll
+  for (int k0 = 0; k0 < ITER; k0 += NB) {
+    uint4 v[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int id = tid + (k0 + k) * Cfg::T;
+      v[k] = *reinterpret_cast<const uint4*>(s + S::off(id / S::CPR, id % S::CPR));
+    }
+    // pins every read here: left alone, the compiler sinks each read into
+    // its conditional store, which serialises them again
+#pragma unroll
+    for (int k = 0; k < NB; ++k) asm volatile("" : "+v"(v[k].x), "+v"(v[k].y), "+v"(v[k].z), "+v"(v[k].w));
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int id = tid + (k0 + k) * Cfg::T;
+      uint16_t* p = dst(id / S::CPR, (id % S::CPR) * 8);
+      if (p) *reinterpret_cast<uint4*>(p) = v[k];
+    }
   }
 }
 template <class Cfg, int R, int C, class Src>
