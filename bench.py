@@ -83,6 +83,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
     ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
+    ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -150,6 +151,36 @@ def mx_leg(warmup, steps):
 
 OPERANDS = {False: "", True: " with E4M3 operands (per-row / per-column amax scales)",
             "mx": " with MXFP8 operands (E4M3, one E8M0 exponent per 32 values)"}
+
+
+def mfma_loop_leg(f3_tflops):
+    """The achievable matrix-core rate: an MFMA-only loop (no memory traffic,
+    no barriers) on every compute unit, timed with HIP events on the current
+    stream, with the engine clock it ran at."""
+    import torch
+    import gemm_epilogue_fp8_amd as coda
+    out = {"workload": "MFMA-only loop, 1024 workgroups of 8 waves, 4 independent 32x32 accumulator chains a wave"}
+    for name, dt, iters in (("bf16", coda.CODA_BF16, 256), ("fp8", coda.CODA_E4M3, 128)):
+        blocks = 1024
+        buf = torch.zeros(blocks * 3, dtype=torch.float32, device="cuda")
+        coda.probe_mfma_loop(dt, blocks, iters, buf)   # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            flops, res = coda.probe_mfma_loop(dt, blocks, iters, buf)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        cyc, ticks = res[:, 1].double(), res[:, 2].double()
+        ghz = float(torch.median(cyc / ticks.clamp(min=1.0)) * 0.1)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"{name}_tflops"] = round(tf, 1)
+        out[f"{name}_frac_of_published"] = round(tf / PEAK_TFLOPS[name], 4)
+        out[f"{name}_engine_clock_ghz"] = round(ghz, 3)
+    out["dominant_kernel_frac_of_achievable"] = round(f3_tflops / out["bf16_tflops"], 4)
+    return out
 
 
 def ce_leg(warmup, steps):
@@ -368,6 +399,9 @@ def main():
     f3_flop = 2 * M * (2 * cfg.F) * cfg.D
     f3_tflops = f3_flop / (f3_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[precision]
+    mloop = None if args.no_mfma_loop else mfma_loop_leg(f3_tflops)
+    if mloop is not None and precision != "bf16":
+        mloop["dominant_kernel_frac_of_achievable"] = round(f3_tflops / mloop["fp8_tflops"], 4)
     out = {
         "metric": "fused GEMM+epilogue TFLOP/s & % MFMA peak; block fwd+bwd ms, hidden 2048/4096",
         "value": round(tflops, 2),
@@ -398,6 +432,7 @@ def main():
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,
         "cross_entropy": ce,
+        "mfma_loop": mloop,
     }
     print(json.dumps(out))
 

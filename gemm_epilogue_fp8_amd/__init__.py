@@ -382,3 +382,16 @@ def linear_sigmoid_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg
                                      _p(W_unfolded), _p(g), _p(dres), _p(du), _p(dW), _p(dg), beta, _p(dh_out),
                                      precision, ws, n, _stream()))
     return du, dW, dg
+
+
+def probe_mfma_loop(dtype: int, blocks: int, iters: int, out=None):
+    """MFMA-only loop (include/coda_probe.h): `blocks` workgroups of 8
+    waves, `iters` rounds of 4 independent MFMA chains a wave.  Returns
+    (flops, out) with out fp32 [blocks, 3] = (checksum, engine-clock
+    cycles, 100 MHz ticks) per workgroup; the caller times the launch."""
+    L = lib()
+    if out is None:
+        out = torch.zeros(blocks * 3, dtype=torch.float32, device="cuda")
+    fl = C.c_double(0.0)
+    _check(L.coda_probe_mfma_loop(dtype, blocks, iters, C.byref(mat(out.view(1, -1))), C.byref(fl), _stream()))
+    return fl.value, out.view(blocks, 3)

@@ -100,6 +100,8 @@ SIGNATURES = {
     "coda_unfused_qknorm_rope_fwd": [M_, M_, M_, M_, i32, f32, M_, M_, vp],
     "coda_unfused_qknorm_rope_bwd_workspace": [i64, i64, szp],
     "coda_unfused_qknorm_rope_bwd": [M_, M_, M_, M_, M_, M_, M_, i32, f32, M_, M_, M_, f32, vp, sz, vp],
+    # measurement helper (include/coda_probe.h)
+    "coda_probe_mfma_loop": [i32, i32, i32, M_, C.POINTER(C.c_double), vp],
 }
 _RET = {"coda_status_string": C.c_char_p, "coda_last_error": C.c_char_p, "coda_partials_cols": C.c_int64}
 

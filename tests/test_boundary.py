@@ -1,5 +1,5 @@
 """The C-ABI library loads on a GPU-less host, exports every function that
-include/coda.h declares, and rejects bad arguments before any HIP call.
+the headers under include/ declare, and rejects bad arguments before any HIP call.
 
 No compute call is made here: every call fails host-side validation (fake,
 never-dereferenced device pointers are used for the shape checks)."""
@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("coda.h", "coda_unfused.h"))
+    text = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("coda.h", "coda_unfused.h", "coda_probe.h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", text)))
 
@@ -205,3 +205,18 @@ def test_mxfp8_functional_validation():
     st = L.coda_linear_rmsnorm_residual_bwd(C.byref(d_out), C.byref(a), C.byref(weight(256, 256)), None,
                                             C.byref(dW), 0.0, MX, None, 0, None)
     assert st == 3
+
+
+def test_probe_validation_codes():
+    """The MFMA-loop probe rejects bad arguments before any launch."""
+    L = g.lib()
+    fl = C.c_double(0.0)
+    out = fake(_lib.CODA_F32, 1, 12)
+    call = lambda dt, b, it, o=out, f=C.byref(fl): L.coda_probe_mfma_loop(dt, b, it, C.byref(o) if o else None, f, None)
+    assert call(_lib.CODA_F32, 4, 10) == 2                       # dtype
+    assert call(_lib.CODA_BF16, 0, 10) == 3                      # blocks
+    assert call(_lib.CODA_BF16, 4, 0) == 3                       # iters
+    assert call(_lib.CODA_BF16, 4, 1 << 21) == 3
+    assert call(_lib.CODA_BF16, 4, 10, f=None) == 1              # flops pointer
+    assert call(_lib.CODA_BF16, 4, 10, o=None) == 1              # out
+    assert call(_lib.CODA_BF16, 5, 10) == 3                      # out holds 3 values a block

@@ -608,3 +608,19 @@ def test_unfused_baseline_block():
     for k, g in (("dWg", dWg), ("dWu", dWu), ("dWqkv", got["dWqkv"]), ("dWo", got["dWo"]), ("dWd", got["dWd"]),
                  ("dg1", got["dg1"]), ("dg2", got["dg2"]), ("dgq", got["dgq"]), ("dgk", got["dgk"])):
         assert_grad(k, g, B[k])
+
+
+@pytest.mark.parametrize("dtype,per_instr", [("bf16", 32768), ("fp8", 131072)])
+def test_mfma_loop_probe(dtype, per_instr):
+    """The MFMA-only loop behind the bench's achievable-rate figure: the flop
+    count it reports is 4 chains x iters x 8 waves x blocks instructions of
+    the stated size, every workgroup writes a positive checksum (all
+    operands are non-negative, some positive) and a positive cycle count."""
+    blocks, iters = 16, 32
+    dt = coda.CODA_BF16 if dtype == "bf16" else coda.CODA_E4M3
+    flops, res = coda.probe_mfma_loop(dt, blocks, iters)
+    torch.cuda.synchronize()
+    assert flops == per_instr * 4 * iters * 8 * blocks
+    r = res.cpu().numpy()
+    assert np.all(np.isfinite(r)) and np.all(r[:, 0] > 0)
+    assert np.all(r[:, 1] > 0) and np.all(r[:, 2] > 0)
