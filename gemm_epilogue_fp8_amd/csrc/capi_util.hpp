@@ -59,6 +59,10 @@ coda_status check_mat(const coda_mat* m, const char* name, int dtype, int64_t ro
     const int v = vec_elems(dtype);
     if (m->cols % v != 0 || m->ld % v != 0)
       return fail(CODA_ERR_LAYOUT, "%s: cols and ld must be multiples of %d elements", name, v);
+    // a tile spans at most 256 rows, addressed by 32-bit byte offsets
+    if (m->ld * esize(dtype) >= (int64_t(1) << 24))
+      return fail(CODA_ERR_LAYOUT, "%s: row stride of %lld bytes, at most 16 MiB - 1 supported", name,
+                  (long long)(m->ld * esize(dtype)));
   }
   if (m->rows > 0x7FFFFFFF || m->cols > 0x7FFFFFFF) return fail(CODA_ERR_SHAPE, "%s: too large", name);
   return CODA_OK;

@@ -35,6 +35,8 @@
  *  - Contiguous rows: bf16 matrices need cols % 8 == 0 and ld % 8 == 0,
  *    fp32 matrices cols % 4 == 0 and ld % 4 == 0, E4M3 matrices
  *    cols % 16 == 0 and ld % 16 == 0; every pointer 16-byte aligned.
+ *    A matrix with more than one row needs a row stride (ld x element size)
+ *    below 16 MiB: the kernels address a tile's rows by 32-bit offsets.
  *  - Results are bitwise deterministic: reductions run in a fixed order.
  */
 #ifndef CODA_H_

@@ -220,3 +220,14 @@ def test_probe_validation_codes():
     assert call(_lib.CODA_BF16, 4, 10, f=None) == 1              # flops pointer
     assert call(_lib.CODA_BF16, 4, 10, o=None) == 1              # out
     assert call(_lib.CODA_BF16, 5, 10) == 3                      # out holds 3 values a block
+
+
+def test_row_stride_limit():
+    """A matrix whose row stride reaches 16 MiB is rejected (tile rows are
+    addressed by 32-bit offsets); one byte row below the limit passes the
+    stride check."""
+    BF, F32 = _lib.CODA_BF16, _lib.CODA_F32
+    big = (1 << 23)                                    # bf16 elements: 16 MiB a row
+    assert call_sumsq(fake(BF, 4, 8, ld=big), fake(F32, 1, 4)) == 4          # layout
+    ok = call_sumsq(fake(BF, 4, 8, ld=big - 8), fake(F32, 1, 3))           # passes the stride check,
+    assert ok == 3                                                          # then fails on the output shape
