@@ -16,7 +16,7 @@ from typing import Iterable, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (CODA_BF16, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
+from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
 
@@ -219,6 +219,23 @@ def quantize_mxfp8(X, axis: int, Q=None, S=None):
     if S is None:
         S = torch.empty(((L + 127) // 128, 4 * rows), dtype=torch.uint8, device=X.device)
     _check(lib().coda_quantize_mxfp8(_p(X), axis, _p(Q), _p(S), _stream()))
+    return Q, S
+
+
+def quantize_mxfp4(X, axis: int, Q=None, S=None):
+    """MXFP4 copy of X [R, C] (bf16): axis 1 -> Q [R, C / 2] bytes with the
+    exponents of R rows; axis 0 -> Q [C, R / 2] (transposed) with those of
+    C rows.  Q holds two E2M1 codes a byte (element 2i in the low nibble), S
+    E8M0 codes in word layout, [ceil(L/128), 4 rows] (see coda.h)."""
+    R, Cc = X.shape
+    rows, L = (R, Cc) if axis == 1 else (Cc, R)
+    if Q is None:
+        Q = torch.empty((rows, L // 2), dtype=torch.uint8, device=X.device)
+    if S is None:
+        S = torch.empty(((L + 127) // 128, 4 * rows), dtype=torch.uint8, device=X.device)
+    q = mat(Q)
+    q.dtype = CODA_E2M1X2
+    _check(lib().coda_quantize_mxfp4(_p(X), axis, C.byref(q), _p(S), _stream()))
     return Q, S
 
 

@@ -522,4 +522,83 @@ __global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int
   if ((part & 1) == 0) S[(int64_t)(b >> 2) * lds + 4 * c + (b & 3)] = (uint8_t)(e + 127);
 }
 
+// ---------------------------------------------------------------- MXFP4 (block-scaled E2M1)
+// OCP MX v1.0 FP4 E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+// negatives) under one E8M0 exponent per 32 values:
+// e = floor(log2(max |v|)) - 2 (2 = the exponent of 4, E2M1's largest power
+// of two), clamped to [-127, 127], -127 for a zero or subnormal maximum.
+__device__ __forceinline__ int mx4_exponent(float amax) {
+  const int be = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  return be == 0 ? -127 : min(max(be - 127 - 2, -127), 127);
+}
+
+// E2M1 code of v (already divided by the block scale): the nearest value,
+// ties to the even mantissa, saturated at 6; a value that rounds to zero is
+// code 0.  Each comparison climbs one step of the value ladder; its
+// threshold is the midpoint of the two neighbours, passed strictly (>) when
+// the lower neighbour has the even mantissa and inclusively (>=) when the
+// upper one has.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((v < 0.0f && c != 0u) ? 8u : 0u);
+}
+
+// 8 values scaled by 2^-e (exact) -> 8 packed codes, value k in nibble k
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* v, int e) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= e2m1_code(ldexpf(v[k], -e)) << (4 * k);
+  return w;
+}
+
+// Blocks along the columns: X [R, C] -> Q [R, C / 2] bytes, exponents of R
+// rows in word layout (C % 32 == 0).  One wave a row, 8 values a lane, a
+// block = 4 consecutive lanes.
+__global__ void quant_mx4_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                      uint8_t* S, int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;                      // r is uniform over the wave
+  for (int c = lane * 8; c < C; c += 512) {
+    // C % 32 == 0: the 4 lanes of a block run the same iterations
+    const uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    float m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, 0.0f))));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int e = mx4_exponent(m);
+    const float v[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+    *reinterpret_cast<uint32_t*>(Q + (int64_t)r * ldq + c / 2) = pack8_e2m1(v, e);
+    const int b = c / 32;
+    if ((lane & 3) == 0) S[(int64_t)(b >> 2) * lds + 4 * r + (b & 3)] = (uint8_t)(e + 127);
+  }
+}
+
+// Blocks along the rows, written transposed: X [R, C] -> Q^T [C, R / 2]
+// bytes, exponents of C rows (R % 32 == 0).  As quant_mx_cols_t_kernel: a
+// 64 x 64 tile through LDS, thread (column cc, part) encodes rows
+// [16 part, 16 part + 16) of its column, a block is one lane pair.
+__global__ void quant_mx4_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                        uint8_t* S, int64_t lds) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  load_tile_t(X, ld, R, C, r0, c0, tile);
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    v[k] = tile[part * 16 + k][cc];
+    m = fmaxf(m, fabsf(v[k]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));      // every lane is still active here
+  const int e = mx4_exponent(m);
+  const int c = c0 + cc, rbase = r0 + part * 16;
+  if (c >= C || rbase >= R) return;        // R % 32 == 0: rows rbase .. rbase + 15 all exist
+  *reinterpret_cast<uint2*>(QT + (int64_t)c * ldq + rbase / 2) = uint2{pack8_e2m1(v, e), pack8_e2m1(v + 8, e)};
+  const int b = rbase / 32;
+  if ((part & 1) == 0) S[(int64_t)(b >> 2) * lds + 4 * c + (b & 3)] = (uint8_t)(e + 127);
+}
+
 }  // namespace coda

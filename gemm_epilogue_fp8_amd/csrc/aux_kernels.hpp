@@ -82,5 +82,12 @@ __global__ void quant_mx_rows_kernel(const uint16_t* X, int64_t ld, int R, int C
                                      uint8_t* S, int64_t lds);
 __global__ void quant_mx_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
                                        uint8_t* S, int64_t lds);
+// MXFP4 (E2M1 elements, packed two a byte, element 2i in the low nibble)
+// with E8M0 exponents in word layout; same shapes and launches as the MXFP8
+// quantisers above, with Q holding C / 2 (or R / 2) bytes a row.
+__global__ void quant_mx4_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                      uint8_t* S, int64_t lds);
+__global__ void quant_mx4_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                        uint8_t* S, int64_t lds);
 
 }  // namespace coda

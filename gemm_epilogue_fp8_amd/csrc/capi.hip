@@ -443,6 +443,30 @@ extern "C" coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, cons
   return check_launch("quantize_mxfp8");
 }
 
+extern "C" coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* Sc,
+                                           void* stream) {
+  TRY(check_mat(X, "X", CODA_BF16, -1, -1));
+  if (axis != 0 && axis != 1) return fail(CODA_ERR_VALUE, "axis must be 0 or 1");
+  const int64_t R = X->rows, C = X->cols;
+  const int64_t L = axis == 1 ? C : R;     // length of the blocked (contracted) axis
+  if (L % 32 != 0) return fail(CODA_ERR_SHAPE, "quantize_mxfp4: the blocked axis (%lld) must be a multiple of 32",
+                               (long long)L);
+  const int64_t rows = axis == 1 ? R : C;
+  TRY(check_mat(Q, "Q", CODA_E2M1X2, rows, L / 2));
+  TRY(check_scales(Sc, "S", rows, L));
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X->ptr);
+  uint8_t* q = static_cast<uint8_t*>(Q->ptr);
+  uint8_t* sc = static_cast<uint8_t*>(Sc->ptr);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx4_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, S(stream), x, X->ld,
+                       (int)R, (int)C, q, Q->ld, sc, Sc->ld);
+  else
+    hipLaunchKernelGGL(quant_mx4_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),
+                       dim3(256), 0, S(stream), x, X->ld, (int)R, (int)C, q, Q->ld, sc, Sc->ld);
+  return check_launch("quantize_mxfp4");
+}
+
 extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                                     const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
                                     uint32_t n_aux, void* stream) {

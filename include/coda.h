@@ -65,8 +65,14 @@ typedef enum coda_status {
 } coda_status;
 
 /* CODA_E8M0: one byte 2^(code - 127) (code 255 = NaN, never written here),
- * the shared block scale of the OCP Microscaling (MX) formats. */
-typedef enum coda_dtype { CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4, CODA_E8M0 = 5 } coda_dtype;
+ * the shared block scale of the OCP Microscaling (MX) formats.
+ * CODA_E2M1X2: two FP4 E2M1 codes a byte (the MX specification's FP4
+ * element: sign, 2 exponent bits with bias 1, 1 mantissa bit; values 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6), element 2i in the low nibble of byte i; a matrix of
+ * them counts cols and ld in bytes. */
+typedef enum coda_dtype {
+  CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4, CODA_E8M0 = 5, CODA_E2M1X2 = 6
+} coda_dtype;
 
 /* GEMM operand precision of the functional entry points. */
 typedef enum coda_precision {
@@ -218,6 +224,21 @@ coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32
  * workspace.  Errors: CODA_ERR_SHAPE when the blocked axis is not a
  * multiple of 32 or S is not ceil(L / 128) x 4n. */
 coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
+                                void* stream);
+
+/* MXFP4 copy of X (bf16 [R, C]), OCP MX v1.0 FP4: blocks of 32 values along
+ * the contracted axis share the E8M0 exponent e = floor(log2 max|v|) - 2
+ * (2 = the exponent of E2M1's largest power of two, 6 = 1.5 * 2^2), clamped
+ * to [-127, 127] (-127 for an all-zero block); an element is the nearest
+ * E2M1 value to v / 2^e, ties to the even mantissa, saturated at +-6; a
+ * value that rounds to zero is stored as code 0 (+0).
+ *   axis 1: Q [R, C / 2] (E2M1X2), exponents of R rows (C % 32 == 0);
+ *   axis 0: Q [C, R / 2] (E2M1X2, written transposed), exponents of C rows
+ *           (R % 32 == 0).
+ * S: E8M0 in word layout as for coda_quantize_mxfp8, [ceil(L / 128), 4 rows].
+ * Errors: CODA_ERR_SHAPE when the blocked axis is not a multiple of 32 or a
+ * shape does not match; CODA_ERR_LAYOUT / CODA_ERR_ALIGN as for matrices. */
+coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
                                 void* stream);
 
 /* D = epilogue(sum_k A~[m, k] B~[n, k]) with MXFP8 operands

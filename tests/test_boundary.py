@@ -231,3 +231,20 @@ def test_row_stride_limit():
     assert call_sumsq(fake(BF, 4, 8, ld=big), fake(F32, 1, 4)) == 4          # layout
     ok = call_sumsq(fake(BF, 4, 8, ld=big - 8), fake(F32, 1, 3))           # passes the stride check,
     assert ok == 3                                                          # then fails on the output shape
+
+
+def test_mxfp4_quantiser_validation_codes():
+    """coda_quantize_mxfp4 checks axis, block multiple, the packed Q shape and
+    dtype, and the exponent layout before any launch."""
+    L = g.lib()
+    BF, E4, E2, E8 = _lib.CODA_BF16, _lib.CODA_E4M3, _lib.CODA_E2M1X2, _lib.CODA_E8M0
+    X = fake(BF, 64, 96)
+    q_ok, s_ok = fake(E2, 64, 48), fake(E8, 1, 256)
+    call = lambda x, ax, q, s: L.coda_quantize_mxfp4(C.byref(x), ax, C.byref(q), C.byref(s), None)
+    assert call(X, 2, q_ok, s_ok) == 9                                   # axis
+    assert call(fake(BF, 64, 80), 1, fake(E2, 64, 40), s_ok) == 3        # 80 not a multiple of 32
+    assert call(X, 1, fake(E4, 64, 48), s_ok) == 2                       # Q dtype
+    assert call(X, 1, fake(E2, 64, 96), s_ok) == 3                       # Q holds C / 2 bytes a row
+    assert call(X, 1, q_ok, fake(E8, 2, 256)) == 3                       # word rows: ceil(96 / 128) = 1
+    # transposed shapes pass the Q and S shape checks and stop at S's alignment
+    assert call(X, 0, fake(E2, 96, 32), fake(E8, 1, 384, ptr=FAKE + 2)) == 5

@@ -272,3 +272,45 @@ def test_gemm_mx_degenerate_shapes():
     torch.cuda.synchronize()
     A, B = mx_values(ca, sa), mx_values(cb, sb)
     assert np.all(np.abs(to_np(D) - A @ B.T) <= mfma_fp8_bound(A, B))
+
+
+# ---------------------------------------------------------------- MXFP4 quantiser
+def fp4_ladder_bf16(rng, R, C, axis):
+    """varied_bf16 plus, in every fourth block along `axis`, the E2M1 ties:
+    a block maximum of exactly 4 (so e = 0 after scaling by the block's power
+    of two) and elements on every midpoint of the value ladder, both signs,
+    and small negatives that round to zero."""
+    X = varied_bf16(rng, R, C, axis)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0,
+                     -0.1, -0.2, 4.0, 0.0], np.float32)
+    Xt = X if axis == 1 else X.T
+    nb = Xt.shape[1] // 32
+    for r in range(0, Xt.shape[0], 3):
+        for b in range(0, nb, 4):
+            s = np.float32(2.0 ** int(rng.integers(-10, 10)))
+            blk = np.resize(ties, 32) * s
+            blk[rng.integers(0, 32)] = 4.0 * s
+            Xt[r, 32 * b:32 * b + 32] = blk
+    return ci.to_bf16_values(X if axis == 1 else Xt.T)
+
+
+@pytest.mark.parametrize("axis,R,C", [(1, 300, 480), (1, 5, 32), (0, 480, 296), (0, 64, 7 * 8)])
+def test_mxfp4_quantiser_bit_exact(axis, R, C):
+    """Packed E2M1 codes and E8M0 exponents equal the oracle's (oracle/mx_small.py)
+    bit for bit, in both orientations, with ragged tiles, an all-zero block,
+    a block of very large values and every rounding tie of the E2M1 ladder."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(40 + axis)
+    X = fp4_ladder_bf16(rng, R, C, axis)
+    Q, S = coda.quantize_mxfp4(bf(X), axis)
+    torch.cuda.synchronize()
+    Xr = X if axis == 1 else np.ascontiguousarray(X.T)       # blocks along the rows of Xr
+    P, e = ms.quantize(Xr, "e2m1")
+    want_q = ms.pack_fp4(ms.encode(P, "e2m1"))
+    got_q = to_np(Q).astype(np.uint8)
+    rows, L = Xr.shape
+    assert got_q.shape == (rows, L // 2)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, (bad[:5], got_q[tuple(bad[0])], want_q[tuple(bad[0])])
+    got_e = from_words(to_np(S), rows, L // 32)
+    np.testing.assert_array_equal(got_e, (e + 127).astype(np.uint8))
