@@ -251,6 +251,20 @@ def gemm_mx(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     return D
 
 
+def gemm_mx4(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
+    """D = epilogue(A~ B~^T) with MXFP4 operands A [M, K/2], B [N, K/2]
+    (uint8, two E2M1 codes a byte, from quantize_mxfp4) and their E8M0
+    exponents SA [K/128, 4M], SB [K/128, 4N] in word layout."""
+    prog = _program(program)
+    aux = list(aux)
+    arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    a, b = mat(A), mat(B)
+    a.dtype = b.dtype = CODA_E2M1X2
+    _check(lib().coda_gemm_mx(C.byref(prog), C.byref(a), _p(SA), C.byref(b), _p(SB), _p(D),
+                              arr if aux else None, len(aux), _stream()))
+    return D
+
+
 # ---------------------------------------------------------------- forward
 def linear_swiglu_fwd(x, Wgu, eps, out, sumsq_partials=None, save_hgu=None, r_out=None,
                       precision: int = PREC_BF16):

@@ -471,11 +471,15 @@ extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat
                                     const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
                                     uint32_t n_aux, void* stream) {
   if (!prog) return fail(CODA_ERR_NULL, "gemm_mx: NULL program");
-  TRY(check_mat(A, "A", CODA_E4M3, -1, -1));
-  TRY(check_mat(B, "B", CODA_E4M3, -1, -1));
-  const int64_t M = A->rows, K = A->cols, N = B->rows;
-  if (B->cols != K) return fail(CODA_ERR_SHAPE, "gemm_mx: inner sizes %lld and %lld differ", (long long)K,
-                                (long long)B->cols);
+  // E2M1 operands (two values a byte) when A says so; B must match
+  const bool fp4 = present(A) && A->dtype == CODA_E2M1X2;
+  const int odt = fp4 ? CODA_E2M1X2 : CODA_E4M3;
+  TRY(check_mat(A, "A", odt, -1, -1));
+  TRY(check_mat(B, "B", odt, -1, -1));
+  const int64_t M = A->rows, Kb = A->cols, N = B->rows;
+  const int64_t K = fp4 ? 2 * Kb : Kb;     // contracted length in values
+  if (B->cols != Kb) return fail(CODA_ERR_SHAPE, "gemm_mx: inner sizes %lld and %lld differ", (long long)Kb,
+                                 (long long)B->cols);
   if (K <= 0 || K % 128 != 0) return fail(CODA_ERR_SHAPE, "gemm_mx: K (%lld) must be a positive multiple of 128",
                                           (long long)K);
   TRY(check_scales(SA, "SA", M, K));
@@ -488,12 +492,12 @@ extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat
   TRY(check_mat(D, "D", out_dtype, M, out_cols));
   e.out = D->ptr;
   e.ld_out = D->ld;
-  GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
+  GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, Kb);   // the mainloop counts bytes
   g.sA = SA->ptr;
   g.sB = SB->ptr;
   g.lds_a = SA->rows > 1 ? SA->ld : SA->cols;
   g.lds_b = SB->rows > 1 ? SB->ld : SB->cols;
-  return launched(launch_gemm_mx(p, g, e, S(stream)), "gemm_mx");
+  return launched(fp4 ? launch_gemm_mx4(p, g, e, S(stream)) : launch_gemm_mx(p, g, e, S(stream)), "gemm_mx");
 }
 
 // ======================================================================== functional forward

@@ -1036,9 +1036,10 @@ __global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e)
     g.K = min(g.kchunk, g.K - kb);
     g.A = static_cast<const char*>(g.A) + (Cfg::A_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.lda * Cfg::ESIZE);
     g.B = static_cast<const char*>(g.B) + (Cfg::B_KC ? (int64_t)kb * Cfg::ESIZE : (int64_t)kb * g.ldb * Cfg::ESIZE);
-    if constexpr (Cfg::MX) {   // kchunk is a multiple of 128: whole word rows
-      g.sA = static_cast<const char*>(g.sA) + (kb / 128) * g.lds_a;
-      g.sB = static_cast<const char*>(g.sB) + (kb / 128) * g.lds_b;
+    if constexpr (Cfg::MX) {   // kchunk covers whole word rows: 128 bytes (E4M3) or 64 (E2M1)
+      constexpr int WB = Cfg::FP4 ? 64 : 128;
+      g.sA = static_cast<const char*>(g.sA) + (kb / WB) * g.lds_a;
+      g.sB = static_cast<const char*>(g.sB) + (kb / WB) * g.lds_b;
     }
     e.out = static_cast<float*>(e.out) + blockIdx.y * e.split_stride;
     if (e.partial_out) e.partial_out += blockIdx.y * e.split_pstride;

@@ -97,25 +97,30 @@ __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
 }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool A_KC_, bool B_KC_, bool FP8_ = false,
-          bool MX_ = false>
+          bool MX_ = false, bool FP4_ = false>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NWAVES = WAVES_M * WAVES_N, T = 64 * NWAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr bool A_KC = A_KC_, B_KC = B_KC_, FP8 = FP8_, MX = MX_;
+  // FP4: the byte operands hold two E2M1 values each; K, the tiles and the
+  // copies count bytes, and only the MFMA sees values
+  static constexpr bool FP4 = FP4_;
+  static constexpr int WPP = FP4 ? 2 : 1;          // MX: exponent word rows a stage pair
   static constexpr int ESIZE = FP8 ? 1 : 2;
   static constexpr int BK = kRowBytes / ESIZE;     // K per stage: 32 bf16 or 64 fp8
   static constexpr int NS = 4;                     // LDS stages
   static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
-  // MXFP8: two slots of (BM + BN) 4-byte scale words after the stages
+  // MX: two slots of WPP x (BM + BN) 4-byte exponent words after the stages
   static constexpr int SCALE_OFF = NS * STAGE_BYTES;
-  static constexpr int SCALE_SLOT = (BM + BN) * 4;
+  static constexpr int SCALE_SLOT = WPP * (BM + BN) * 4;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + (MX ? 2 * SCALE_SLOT : 0);
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(WAVES_M == 2, "the two wave groups are the two row halves of the tile");
   static_assert(!FP8 || (A_KC && B_KC), "fp8 operands are K-contiguous");
   static_assert(!MX || FP8, "block scales come with E4M3 operands");
+  static_assert(!FP4 || MX, "E2M1 operands are block-scaled");
 };
 
 struct GemmArgs {
@@ -274,11 +279,19 @@ struct Frags {
 };
 
 template <class Cfg>
-constexpr int substeps() { return Cfg::FP8 ? 1 : 2; }
+constexpr int substeps() { return Cfg::FP8 && !Cfg::FP4 ? 1 : 2; }
 
 template <class Cfg, bool KC, int R>
 __device__ __forceinline__ typename Frags<Cfg>::T read_frag(const char* tile, int r0, int s, int lane) {
-  if constexpr (Cfg::FP8) {
+  if constexpr (Cfg::FP4) {
+    // MFMA s of the stage: lanes 0-31 hold all 32 values (16 bytes) of K
+    // block 2 s of their row, lanes 32-63 those of block 2 s + 1, one
+    // 16-byte chunk; the matrix core reads E2M1 operands from the low 4
+    // registers only
+    const int row = r0 + (lane & 31);
+    i32x4_t v = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 * s + (lane >> 5)));
+    return i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+  } else if constexpr (Cfg::FP8) {
     // K bytes [16 h, 16 h + 16) and [32 + 16 h, 32 + 16 h + 16) of the row,
     // h = lane >> 5: the matrix core reads a lane's first 16 bytes as part of
     // K block 0 (of 32) and its last 16 as part of block 1, and scales block
@@ -353,7 +366,8 @@ __device__ __forceinline__ void load_scales(const char* slot, Scales<Cfg>& sc, i
 // B's scale goes with the instruction's first operand.
 template <class Cfg, int S, int I, int J>
 __device__ __forceinline__ void mma_mx_one(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc) {
-  acc.c[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[J], f.a[I], acc.c[I][J], 0, 0,
+  constexpr int FMT = Cfg::FP4 ? 4 : 0;   // operand formats: 0 = E4M3, 4 = E2M1
+  acc.c[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[J], f.a[I], acc.c[I][J], FMT, FMT,
                                                                 2 * S + (J & 1), sc.b[J >> 1],
                                                                 2 * S + (I & 1), sc.a[I >> 1]);
 }
@@ -444,6 +458,9 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
   // [64 w, 64 w + 64) of this group's operand tile, from word row p; wave w
   // of group 1 copies the words of exactly the B rows that wave w of each
   // group reads
+  // E2M1 (FP4): a stage of 64 bytes holds 128 values, so each stage has a
+  // word row of its own and a pair copies two (WPP); a word row past the
+  // last one (an odd stage count) gets an empty buffer range and reads as 0
   auto issue_scales = [&](int p) {
     if constexpr (Cfg::MX) {
       const bool a = grp == 0;
@@ -451,15 +468,22 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
       const int64_t ld = a ? g.lds_a : g.lds_b;
       const int row0 = a ? m0 : n0, nrows = a ? g.M : g.N;
       const int r = 64 * w + lane;
-      const auto rs = make_rsrc(base + (int64_t)p * ld + 4 * (int64_t)row0, 4 * (uint64_t)(nrows - row0));
+      const int nwords = Cfg::FP4 ? nk : np;
       const uint32_t off = (row0 + r < nrows) ? (uint32_t)(4 * r) : kOobOffset;
-      char* dst = smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT + (a ? 0 : 4 * Cfg::BM) + 256 * w;
-      raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (int)off, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < Cfg::WPP; ++t) {
+        const int wr = Cfg::WPP * p + t;
+        const auto rs = make_rsrc(base + (int64_t)wr * ld + 4 * (int64_t)row0,
+                                  wr < nwords ? 4 * (uint64_t)(nrows - row0) : 0);
+        char* dst = smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT + t * (Cfg::BM + Cfg::BN) * 4 +
+                    (a ? 0 : 4 * Cfg::BM) + 256 * w;
+        raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 4, (int)off, 0, 0, 0);
+      }
     }
   };
   auto issue_pair = [&](int p) { issue_stage(2 * p); issue_stage(2 * p + 1); issue_scales(p); };
   // copies a wave issues per stage pair
-  constexpr int PAIR_LOADS = 2 * LPS + (Cfg::MX ? 1 : 0);
+  constexpr int PAIR_LOADS = 2 * LPS + (Cfg::MX ? Cfg::WPP : 0);
   static_assert(!Cfg::MX || (Cfg::BM == 256 && Cfg::BN == 256 && Cfg::WAVES_N == 4),
                 "one 64-row scale instruction per wave covers a 256-row tile");
 
@@ -484,8 +508,13 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S0, S0 + Cfg::BM * kRowBytes, s, f[s], wm0, wn0, lane);
 #pragma unroll
     for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, f[SUB + s], wm0, wn0, lane);
-    Scales<Cfg> sc;
-    if constexpr (Cfg::MX) load_scales<Cfg>(smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT, sc, wm0, wn0, lane);
+    Scales<Cfg> sc[Cfg::WPP];              // one set a word row: the pair (E4M3) or each stage (E2M1)
+    if constexpr (Cfg::MX) {
+#pragma unroll
+      for (int t = 0; t < Cfg::WPP; ++t)
+        load_scales<Cfg>(smem + Cfg::SCALE_OFF + (p & 1) * Cfg::SCALE_SLOT + t * (Cfg::BM + Cfg::BN) * 4, sc[t],
+                         wm0, wn0, lane);
+    }
     // Pair p + 1 must land before the barrier that ends the phase in which
     // group 1 reads pair p (group 0 reads pair p + 1 in the next one).
     if (grp == 0) {
@@ -508,9 +537,16 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     }
     phase_barrier();
     // ---- compute phase
-    if constexpr (Cfg::MX) {
-      mma_frags_mx<Cfg, 0>(f[0], sc, acc);
-      mma_frags_mx<Cfg, 1>(f[1], sc, acc);
+    if constexpr (Cfg::MX && Cfg::FP4) {
+      // f[2 t + s]: stage t, MFMA s; blocks 2 s and 2 s + 1 of stage t's word
+      mma_frags_mx<Cfg, 0>(f[0], sc[0], acc);
+      mma_frags_mx<Cfg, 1>(f[1], sc[0], acc);
+      mma_frags_mx<Cfg, 0>(f[2], sc[Cfg::WPP - 1], acc);
+      mma_frags_mx<Cfg, 1>(f[3], sc[Cfg::WPP - 1], acc);
+    } else if constexpr (Cfg::MX) {
+      // f[t]: stage t, K blocks 2 t and 2 t + 1 of the pair's word
+      mma_frags_mx<Cfg, 0>(f[0], sc[0], acc);
+      mma_frags_mx<Cfg, 1>(f[1], sc[0], acc);
     } else {
 #pragma unroll
       for (int s = 0; s < 2 * SUB; ++s) mma_frags<Cfg>(f[s], acc);

@@ -45,6 +45,9 @@ hipError_t launch_gemm_fp8(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 // MXFP8 operands (g.sA, g.sB set): the programs of the generic entry point
 // and of the block's forward and backward
 hipError_t launch_gemm_mx(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
+// MXFP4 operands (E2M1 packed two a byte; g.K counts bytes): the programs of
+// the generic entry point
+hipError_t launch_gemm_mx4(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 
 template <class Cfg, class Epi>
 hipError_t launch_one(GemmArgs g, const EpiArgs& e, hipStream_t s) {

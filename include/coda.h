@@ -252,7 +252,12 @@ coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat*
  * COL_SCALE STORE_BF16, ADD_TILE STORE_BF16 [ROW_SUMSQ_PARTIAL], the two
  * SWIGLU chains), with D shaped as there.  Errors as coda_gemm_epi, plus
  * CODA_ERR_DTYPE / CODA_ERR_SHAPE / CODA_ERR_ALIGN / CODA_ERR_LAYOUT for the
- * scale matrices. */
+ * scale matrices.
+ * MXFP4: with A of dtype CODA_E2M1X2 the operands are E2M1 (as written by
+ * coda_quantize_mxfp4), A [M, K / 2 bytes] and B [N, K / 2 bytes], same
+ * exponent layout and K rule (K counts values); the epilogue program is one
+ * of STORE_BF16, ACCUM_F32, ROW_SCALE COL_SCALE STORE_BF16, ADD_TILE
+ * STORE_BF16 [ROW_SUMSQ_PARTIAL] and the SWIGLU chains. */
 coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                          const coda_mat* B, const coda_mat* SB, const coda_mat* D,
                          const coda_mat* aux, uint32_t n_aux, void* stream);

@@ -314,3 +314,92 @@ def test_mxfp4_quantiser_bit_exact(axis, R, C):
     assert bad.size == 0, (bad[:5], got_q[tuple(bad[0])], want_q[tuple(bad[0])])
     got_e = from_words(to_np(S), rows, L // 32)
     np.testing.assert_array_equal(got_e, (e + 127).astype(np.uint8))
+
+
+# ---------------------------------------------------------------- MXFP4 GEMM
+def random_mx4(rng, rows, K, emin=117, emax=137):
+    """An MXFP4 operand drawn directly: uniform E2M1 codes (all 16) and E8M0
+    codes uniform in [emin, emax], independent per block; returns the codes
+    [rows, K] and the exponent bytes [rows, K / 32]."""
+    codes = rng.integers(0, 16, size=(rows, K)).astype(np.uint8)
+    scales = rng.integers(emin, emax + 1, size=(rows, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def mx4_values(codes, scales):
+    from oracle import mx_small as ms
+    return ms.dequantize(ms.decode(codes, "e2m1"), scales.astype(np.int64) - 127)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 384), (517, 520, 1024), (64, 8, 128)])
+def test_gemm_mxfp4_accum_and_store(M, N, K):
+    """E2M1 operands through the same epilogues: fp32 accumulate onto a prior
+    and bf16 store, against the oracle's float64 product of the dequantised
+    operands.  K 384 has an odd number of 64-byte stages (the last pair's
+    second exponent row lies past the operand), K 128 a single stage."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(M + N + K + 1)
+    ca, sa = random_mx4(rng, M, K)
+    cb, sb = random_mx4(rng, N, K)
+    A, B = mx4_values(ca, sa), mx4_values(cb, sb)
+    ref = A @ B.T
+    qa, qb = u8(ms.pack_fp4(ca)), u8(ms.pack_fp4(cb))
+    prior = ci.fp32_prior((M, N), 5)
+    D32 = f32(prior)
+    coda.gemm_mx4([(coda.EPI_ACCUM_F32, 0, 1.0)], qa, u8(to_words(sa)), qb, u8(to_words(sb)), D32)
+    D16 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx4([(coda.EPI_STORE_BF16, 0, 0.0)], qa, u8(to_words(sa)), qb, u8(to_words(sb)), D16)
+    torch.cuda.synchronize()
+    bound = mfma_fp8_bound(A, B)
+    got32 = to_np(D32).astype(np.float64) - prior
+    assert np.all(np.abs(got32 - ref) <= bound + 2.0 ** -23 * (np.abs(ref) + np.abs(prior))), \
+        float(np.max(np.abs(got32 - ref) - bound))
+    got16 = to_np(D16).astype(np.float64)
+    assert np.all(np.abs(got16 - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), \
+        float(np.max(np.abs(got16 - ref) - bound))
+    assert np.linalg.norm(got32 - ref) <= 1e-3 * np.linalg.norm(ref)
+
+
+def test_gemm_mxfp4_one_scale_per_block():
+    """Exponents that differ between every block of a row and between rows:
+    a scale taken from the wrong block, stage or row moves the result by a
+    power of two."""
+    rng = np.random.default_rng(19)
+    M, N, K = 256, 256, 512
+    ca, _ = random_mx4(rng, M, K)
+    cb, _ = random_mx4(rng, N, K)
+    sa = (120 + (np.arange(K // 32)[None, :] * 3 + np.arange(M)[:, None]) % 15).astype(np.uint8)
+    sb = (121 + (np.arange(K // 32)[None, :] * 5 + 2 * np.arange(N)[:, None]) % 13).astype(np.uint8)
+    from oracle import mx_small as ms
+    A, B = mx4_values(ca, sa), mx4_values(cb, sb)
+    D32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    coda.gemm_mx4([(coda.EPI_ACCUM_F32, 0, 0.0)], u8(ms.pack_fp4(ca)), u8(to_words(sa)), u8(ms.pack_fp4(cb)),
+                  u8(to_words(sb)), D32)
+    torch.cuda.synchronize()
+    ref = A @ B.T
+    assert np.all(np.abs(to_np(D32) - ref) <= mfma_fp8_bound(A, B))
+    assert np.linalg.norm(to_np(D32) - ref) <= 1e-3 * np.linalg.norm(ref)
+
+
+def test_gemm_mxfp4_from_bf16_residual():
+    """bf16 inputs quantised by the library (bit-exact against the oracle, as
+    tested above), then the residual program out = z + a W on the MXFP4
+    product, against the oracle's product of its own quantisation."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(29)
+    M, N, K = 300, 520, 640
+    a = ci.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = ci.to_bf16_values((rng.standard_normal((N, K)) * K ** -0.5).astype(np.float32))
+    z = ci.to_bf16_values(rng.standard_normal((M, N)).astype(np.float32))
+    QA, SA = coda.quantize_mxfp4(bf(a), 1)
+    QB, SB = coda.quantize_mxfp4(bf(w), 1)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx4([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)], QA, SA, QB, SB, out, aux=[bf(z)])
+    torch.cuda.synchronize()
+    PA, eA = ms.quantize(a, "e2m1")
+    PB, eB = ms.quantize(w, "e2m1")
+    A, B = ms.dequantize(PA, eA), ms.dequantize(PB, eB)
+    ref = z.astype(np.float64) + A @ B.T
+    got = to_np(out).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1.01 * mfma_fp8_bound(A, B) + 2.0 ** -8 * np.abs(ref) + 1e-30)
+    assert np.linalg.norm(got - nm.bf16(ref)) <= 3e-3 * np.linalg.norm(ref)
