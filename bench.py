@@ -30,7 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "fp4": 10100.0}   # MI355X dense MFMA, published
 HBM_GBPS = 8000.0
 
 
@@ -107,8 +107,9 @@ def mx_leg(warmup, steps):
     """The block-scaled E4M3 GEMM (one E8M0 scale per 32 K values, applied by
     the scaled MFMA) with the residual epilogue, out = z + a W, at the
     hidden-8192 down-projection shape (M 4096, K 28672, N 8192), against the
-    per-token x per-channel amax-scaled E4M3 path of the same layer; both
-    include the quantisation of the activation a.  Synthetic inputs drawn on
+    per-token x per-channel amax-scaled E4M3 path of the same layer (which
+    includes the quantisation of the activation a), and the same layer with
+    MXFP4 (E2M1) operands.  Synthetic inputs drawn on
     the device from a seeded generator."""
     import torch
     import gemm_epilogue_fp8_amd as coda
@@ -140,13 +141,22 @@ def mx_leg(warmup, steps):
     rowcol_ms = ev_ms(lambda: coda.linear_rmsnorm_residual_fwd(a, wt, z, out, precision=coda.PREC_FP8))
     flop = 2 * M * N * K
     tf = flop / (gemm_ms * 1e-3) / 1e12
-    del a, W, z, out, Qw, Sw, Qa, Sa, wt
+    del Qw, Sw, Qa, Sa, wt
+    # the same layer with MXFP4 (E2M1) operands
+    Q4w, S4w = coda.quantize_mxfp4(W, 0)
+    Q4a, S4a = coda.quantize_mxfp4(a, 1)
+    fp4_ms = ev_ms(lambda: coda.gemm_mx4(prog, Q4a, S4a, Q4w, S4w, out, aux=[z]))
+    quant4_ms = ev_ms(lambda: coda.quantize_mxfp4(a, 1, Q4a, S4a))
+    tf4 = flop / (fp4_ms * 1e-3) / 1e12
+    del a, W, z, out, Q4w, S4w, Q4a, S4a
     torch.cuda.empty_cache()
     return {"workload": f"out = z + a W, M {M}, K {K}, N {N}, MXFP8 operands (E4M3, E8M0 per 32 K)",
             "gemm_ms": round(gemm_ms, 4), "tflops": round(tf, 1), "frac_of_fp8_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
             "quantize_a_ms": round(quant_ms, 4),
             "gemm_plus_quantize_ms": round(gemm_ms + quant_ms, 4),
-            "per_row_col_fp8_layer_ms": round(rowcol_ms, 4)}
+            "per_row_col_fp8_layer_ms": round(rowcol_ms, 4),
+            "mxfp4_gemm_ms": round(fp4_ms, 4), "mxfp4_tflops": round(tf4, 1),
+            "mxfp4_frac_of_fp4_peak": round(tf4 / PEAK_TFLOPS["fp4"], 4), "mxfp4_quantize_a_ms": round(quant4_ms, 4)}
 
 
 OPERANDS = {False: "", True: " with E4M3 operands (per-row / per-column amax scales)",
@@ -160,7 +170,8 @@ def mfma_loop_leg(f3_tflops):
     import torch
     import gemm_epilogue_fp8_amd as coda
     out = {"workload": "MFMA-only loop, 1024 workgroups of 8 waves, 4 independent 32x32 accumulator chains a wave"}
-    for name, dt, iters in (("bf16", coda.CODA_BF16, 256), ("fp8", coda.CODA_E4M3, 128)):
+    for name, dt, iters in (("bf16", coda.CODA_BF16, 256), ("fp8", coda.CODA_E4M3, 128),
+                            ("fp4", coda.CODA_E2M1X2, 64)):
         blocks = 1024
         buf = torch.zeros(blocks * 3, dtype=torch.float32, device="cuda")
         coda.probe_mfma_loop(dt, blocks, iters, buf)   # warm-up

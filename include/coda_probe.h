@@ -25,7 +25,8 @@ extern "C" {
  * 32 x 32 accumulator chains with operands held in registers:
  *   dtype CODA_BF16: v_mfma_f32_32x32x16_bf16, 32768 flops an instruction;
  *   dtype CODA_E4M3: v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands
- *                    and unit block scales, 131072 flops an instruction.
+ *                    and unit block scales, 131072 flops an instruction;
+ *   dtype CODA_E2M1X2: the same instruction with E2M1 (FP4) operands.
  * out: fp32 1 x (3 blocks), caller-owned device memory.  Workgroup b writes
  * out[3b] = a sum of its first lane's accumulators (keeps the loop live),
  * out[3b + 1] = engine-clock cycles and out[3b + 2] = 100 MHz constant-clock

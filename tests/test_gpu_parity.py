@@ -610,14 +610,14 @@ def test_unfused_baseline_block():
         assert_grad(k, g, B[k])
 
 
-@pytest.mark.parametrize("dtype,per_instr", [("bf16", 32768), ("fp8", 131072)])
+@pytest.mark.parametrize("dtype,per_instr", [("bf16", 32768), ("fp8", 131072), ("fp4", 131072)])
 def test_mfma_loop_probe(dtype, per_instr):
     """The MFMA-only loop behind the bench's achievable-rate figure: the flop
     count it reports is 4 chains x iters x 8 waves x blocks instructions of
     the stated size, every workgroup writes a positive checksum (all
     operands are non-negative, some positive) and a positive cycle count."""
     blocks, iters = 16, 32
-    dt = coda.CODA_BF16 if dtype == "bf16" else coda.CODA_E4M3
+    dt = {"bf16": coda.CODA_BF16, "fp8": coda.CODA_E4M3, "fp4": coda.CODA_E2M1X2}[dtype]
     flops, res = coda.probe_mfma_loop(dt, blocks, iters)
     torch.cuda.synchronize()
     assert flops == per_instr * 4 * iters * 8 * blocks
