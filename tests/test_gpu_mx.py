@@ -403,3 +403,65 @@ def test_gemm_mxfp4_from_bf16_residual():
     got = to_np(out).astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1.01 * mfma_fp8_bound(A, B) + 2.0 ** -8 * np.abs(ref) + 1e-30)
     assert np.linalg.norm(got - nm.bf16(ref)) <= 3e-3 * np.linalg.norm(ref)
+
+
+def test_gemm_mxfp4_full_size_sampled():
+    """The MXFP4 layer the bench times: M 4096, K 28672, N 8192 with residual;
+    the library quantises a and W; 128 sampled outputs are recomputed by the
+    oracle from its own MXFP4 copies of the sampled rows of a and columns of
+    W (whose packed codes and exponents must equal the library's bit for bit)."""
+    from oracle import mx_small as msm
+    M, K, N = 4096, 28672, 8192
+    rng = np.random.default_rng(73)
+    a = ci.to_bf16_values(rng.standard_normal((M, K), dtype=np.float32))
+    W = ci.to_bf16_values(rng.standard_normal((K, N), dtype=np.float32) * np.float32(K ** -0.5))
+    z = ci.to_bf16_values(rng.standard_normal((M, N), dtype=np.float32))
+    ag, Wg, zg = bf(a), bf(W), bf(z)
+    Qa, Sa = coda.quantize_mxfp4(ag, 1)
+    Qw, Sw = coda.quantize_mxfp4(Wg, 0)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx4([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)], Qa, Sa, Qw, Sw, out, aux=[zg])
+    torch.cuda.synchronize()
+    ms = rng.integers(0, M, 128)
+    ns = rng.integers(0, N, 128)
+    um, un = np.unique(ms), np.unique(ns)
+    Pa, ea = msm.quantize(a[um], "e2m1")
+    Pw, ew = msm.quantize(W[:, un].T.copy(), "e2m1")
+    assert np.array_equal(Qa[torch.from_numpy(um).to(DEV)].cpu().numpy(), msm.pack_fp4(msm.encode(Pa, "e2m1")))
+    assert np.array_equal(from_words(Sa.cpu().numpy(), M, K // 32)[um], (ea + 127).astype(np.uint8))
+    assert np.array_equal(Qw[torch.from_numpy(un).to(DEV)].cpu().numpy(), msm.pack_fp4(msm.encode(Pw, "e2m1")))
+    assert np.array_equal(from_words(Sw.cpu().numpy(), N, K // 32)[un], (ew + 127).astype(np.uint8))
+    Ad, Bd = msm.dequantize(Pa, ea), msm.dequantize(Pw, ew)
+    im, jn = np.searchsorted(um, ms), np.searchsorted(un, ns)
+    acc = np.einsum("ik,ik->i", Ad[im], Bd[jn])
+    bound = 2.0 ** -10 * np.einsum("ik,ik->i", np.abs(Ad[im]), np.abs(Bd[jn]))
+    ref = z[ms, ns].astype(np.float64) + acc
+    got = out[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), float(np.max(np.abs(got - ref) - bound))
+    assert_bf16("sampled out", got, nm.bf16(ref))
+
+
+def test_gemm_mxfp4_degenerate_shapes():
+    """Empty M or N is a no-op that leaves D untouched; a single row and the
+    smallest K (128 values: one 64-byte stage, one exponent word row) match
+    the oracle."""
+    from oracle import mx_small as msm
+    rng = np.random.default_rng(31)
+    sentinel = torch.full((64, 64), 3.0, dtype=BF, device=DEV)
+    for M, N in ((0, 64), (64, 0)):
+        qa = torch.empty((max(M, 1), 64), dtype=torch.uint8, device=DEV)[:M]
+        qb = torch.empty((max(N, 1), 64), dtype=torch.uint8, device=DEV)[:N]
+        sa = torch.empty((1, 4 * max(M, 1)), dtype=torch.uint8, device=DEV)[:, :4 * M]
+        sb = torch.empty((1, 4 * max(N, 1)), dtype=torch.uint8, device=DEV)[:, :4 * N]
+        coda.gemm_mx4([(coda.EPI_STORE_BF16, 0, 0.0)], qa, sa, qb, sb, sentinel[:M, :N])
+    torch.cuda.synchronize()
+    assert bool((sentinel == 3.0).all())
+    ca, sa = random_mx4(rng, 1, 128)
+    cb, sb = random_mx4(rng, 40, 128)
+    D = torch.empty((1, 40), dtype=torch.float32, device=DEV)
+    coda.gemm_mx4([(coda.EPI_ACCUM_F32, 0, 0.0)], u8(msm.pack_fp4(ca)), u8(to_words(sa)), u8(msm.pack_fp4(cb)),
+                  u8(to_words(sb)), D)
+    torch.cuda.synchronize()
+    A, B = mx4_values(ca, sa), mx4_values(cb, sb)
+    ref = A @ B.T
+    assert np.all(np.abs(to_np(D) - ref) <= mfma_fp8_bound(A, B) + 1e-30)
