@@ -248,3 +248,25 @@ def test_mxfp4_quantiser_validation_codes():
     assert call(X, 1, q_ok, fake(E8, 2, 256)) == 3                       # word rows: ceil(96 / 128) = 1
     # transposed shapes pass the Q and S shape checks and stop at S's alignment
     assert call(X, 0, fake(E2, 96, 32), fake(E8, 1, 384, ptr=FAKE + 2)) == 5
+
+
+def test_mxfp4_gemm_validation_codes():
+    """coda_gemm_mx with E2M1X2 operands: both operands must be E2M1X2, K
+    (twice the byte count) a multiple of 128, and the exponents sized for K
+    values, all checked before any launch."""
+    L = g.lib()
+    BF, E4, E2, E8 = _lib.CODA_BF16, _lib.CODA_E4M3, _lib.CODA_E2M1X2, _lib.CODA_E8M0
+    prog = _lib.EpiProgram()
+    prog.n_ops = 1
+    prog.ops[0].op = _lib.EPI_STORE_BF16
+    gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
+                                                C.byref(D), None, 0, None)
+    M, N = 64, 32
+    assert gm(fake(E2, M, 128), fake(E8, 2, 4 * M), fake(E4, N, 128), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 2                                             # B is not E2M1X2
+    assert gm(fake(E2, M, 96), fake(E8, 2, 4 * M), fake(E2, N, 96), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 3                                             # K = 192 values
+    assert gm(fake(E2, M, 128), fake(E8, 1, 4 * M), fake(E2, N, 128), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 3                                             # 256 values need 2 word rows
+    assert gm(fake(E2, M, 128), fake(E8, 2, 4 * M), fake(E2, N, 128), fake(E8, 2, 4 * N),
+              fake(BF, M, N + 8)) == 3                                         # D shape
