@@ -17,6 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
+                   PREC_MXFP4,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
 
@@ -24,7 +25,7 @@ __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "ro
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
-           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8"]
+           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4"]
 
 
 class CodaError(RuntimeError):
@@ -77,10 +78,14 @@ class Weight:
     def __init__(self, w: torch.Tensor, q_fwd=None, s_fwd=None, q_bwd=None, s_bwd=None):
         self.w, self.q_fwd, self.s_fwd, self.q_bwd, self.s_bwd = w, q_fwd, s_fwd, q_bwd, s_bwd
 
+    fp4 = False    # q_fwd holds E2M1 codes two a byte (prepare_mxfp4)
+
     def c(self) -> _lib.CodaWeight:
         cw = _lib.CodaWeight()
         cw.w = mat(self.w)
         cw.q_fwd, cw.s_fwd = mat(self.q_fwd), mat(self.s_fwd)
+        if self.fp4:
+            cw.q_fwd.dtype = CODA_E2M1X2
         cw.q_bwd, cw.s_bwd = mat(self.q_bwd), mat(self.s_bwd)
         return cw
 
@@ -106,6 +111,20 @@ class Weight:
         self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
         self.q_bwd = torch.empty((K, N), dtype=torch.float8_e4m3fn, device=dev)
         self.s_bwd = torch.empty(((N + 127) // 128, 4 * K), dtype=torch.uint8, device=dev)
+        quantize_weight(self)
+        return self
+
+    def prepare_mxfp4(self):
+        """Allocate and fill the block-scaled E2M1 forward copy
+        (coda_quantize_weight): q_fwd [N, K/2] bytes (two codes a byte) with
+        exponents along K_in in word layout; MXFP4 is forward-only, so there
+        is no backward copy."""
+        K, N = self.w.shape
+        dev = self.w.device
+        self.fp4 = True
+        self.q_fwd = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
+        self.q_bwd = self.s_bwd = None
         quantize_weight(self)
         return self
 

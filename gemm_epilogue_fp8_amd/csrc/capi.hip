@@ -64,15 +64,17 @@ struct ActQ {
   float* amax;
   float* parts;
   bool mx;
+  bool fp4;      // MXFP4: E2M1 codes, two a byte (q.ld counts bytes)
   uint8_t* e;
   int64_t e_ld;
 };
-ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis, bool mx = false) {
+ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis, bool mx = false, bool fp4 = false) {
   ActQ a{};
   a.mx = mx;
+  a.fp4 = fp4;
   if (mx) {
     const int64_t rows = axis == 1 ? R : C, L = axis == 1 ? C : R;
-    a.q.ld = (L + 15) / 16 * 16;
+    a.q.ld = ((fp4 ? L / 2 : L) + 15) / 16 * 16;
     a.q.q = cv.take<uint8_t>((size_t)rows * a.q.ld);
     a.q.s = nullptr;
     a.e_ld = 4 * rows;
@@ -96,11 +98,28 @@ coda_status run_quant_mx(const void* X, int64_t ldx, int64_t R, int64_t C, int a
                        0, s, x, ldx, (int)R, (int)C, Q, ldq, E, lde);
   return check_launch("quantize_mxfp8");
 }
+coda_status run_quant_mx4(const void* X, int64_t ldx, int64_t R, int64_t C, int axis, uint8_t* Q, int64_t ldq,
+                          uint8_t* E, int64_t lde, hipStream_t s) {
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx4_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, x, ldx, (int)R, (int)C,
+                       Q, ldq, E, lde);
+  else
+    hipLaunchKernelGGL(quant_mx4_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),
+                       dim3(256), 0, s, x, ldx, (int)R, (int)C, Q, ldq, E, lde);
+  return check_launch("quantize_mxfp4");
+}
 coda_status quant_act(const ActQ& a, const void* X, int64_t ldx, int64_t R, int64_t C, int axis, hipStream_t s) {
+  if (a.fp4) return run_quant_mx4(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
   if (a.mx) return run_quant_mx(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
   return run_quant(X, ldx, R, C, axis, a.q.q, a.q.ld, a.q.s, a.amax, a.parts, s);
 }
-// MXFP8: the exponents of both operands go with the GEMM; the epilogue applies
+// A forward GEMM: MXFP4 operands go to their own instantiations (K in bytes)
+hipError_t launch_fwd(Prog p, int layout, bool fp8, bool fp4, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  return fp4 ? launch_gemm_mx4(p, g, e, s) : launch_gemm(p, layout, fp8, g, e, s);
+}
+// MXFP8 / MXFP4: the exponents of both operands go with the GEMM; the epilogue applies
 // no dequantisation scales
 void mx_args(GemmArgs* g, EpiArgs* e, const void* ea, int64_t lda_e, const coda_mat* eb) {
   g->sA = ea;
@@ -144,15 +163,24 @@ coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int
     TRY(check_scales(&wt->s_fwd, "s_fwd", N, K));
     TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E4M3, K, N));
     TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
+  } else if (precision == CODA_PREC_MXFP4) {
+    // forward copy only: q_fwd [N, K / 2 bytes] with blocks along K_in
+    if (K % 128 != 0) return fail(CODA_ERR_SHAPE, "%s: MXFP4 needs K_in to be a multiple of 128", name);
+    TRY(check_mat(&wt->q_fwd, "q_fwd", CODA_E2M1X2, N, K / 2));
+    TRY(check_scales(&wt->s_fwd, "s_fwd", N, K));
   } else if (precision != CODA_PREC_BF16) {
     return fail(CODA_ERR_VALUE, "precision %d", precision);
   }
   return CODA_OK;
 }
 coda_status check_precision(int p) {
+  if (p == CODA_PREC_MXFP4) return fail(CODA_ERR_UNSUPPORTED, "MXFP4 operands are forward-only in this build");
   if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8) return fail(CODA_ERR_VALUE, "precision %d", p);
   return CODA_OK;
 }
+// the forward entry points also take MXFP4 operands
+coda_status check_precision_fwd(int p) { return p == CODA_PREC_MXFP4 ? CODA_OK : check_precision(p); }
+bool is_mx(int p) { return p == CODA_PREC_MXFP8 || p == CODA_PREC_MXFP4; }
 
 
 // Forward-direction GEMM of an activation a [M, K] with a weight [K, N].
@@ -300,6 +328,12 @@ extern "C" coda_status coda_quantize_weight_workspace(const coda_weight* wt, siz
 extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream) {
   if (!wt) return fail(CODA_ERR_NULL, "quantize_weight: NULL weight");
   const int64_t K = wt->w.rows, N = wt->w.cols;
+  if (wt->q_fwd.dtype == CODA_E2M1X2) {
+    // MXFP4 forward copy: q_fwd [N, K / 2 bytes] with blocks along K_in
+    TRY(check_weight(wt, "W", K, N, CODA_PREC_MXFP4));
+    return run_quant_mx4(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
+                         static_cast<uint8_t*>(wt->s_fwd.ptr), wt->s_fwd.ld, S(stream));
+  }
   if (wt->s_fwd.dtype == CODA_E8M0) {
     // MXFP8 copies: q_fwd [N, K] with blocks along K_in, q_bwd [K, N] with
     // blocks along N_out, exponents in word layout
@@ -507,16 +541,16 @@ extern "C" coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, in
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision != CODA_PREC_BF16) take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
   *bytes = cv.off;
   return CODA_OK;
 }
 
 namespace {
 // Sizes and carves what an fp8 activation operand of the forward needs.
-size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx) {
+size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx, bool fp4) {
   Carver cv(nullptr);
-  take_act(cv, M, K, 1, mx);
+  take_act(cv, M, K, 1, mx, fp4);
   return cv.off;
 }
 }  // namespace
@@ -533,7 +567,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   Carver cv(size_only ? nullptr : ws);
   float* sumsq = cv.take<float>(M);
   ActQ aq{};
-  if (precision != CODA_PREC_BF16) aq = take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
+  if (precision != CODA_PREC_BF16) aq = take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
@@ -552,7 +586,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   const bool fp8 = precision != CODA_PREC_BF16;
   if (fp8) {
     TRY(quant_act(aq, x->ptr, x->ld, M, K, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, K);
+    g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, aq.fp4 ? K / 2 : K);
     e.rowscale = aq.q.s;
     e.colscale = fptr(&Wgu->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wgu->s_fwd);
@@ -562,13 +596,14 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
     layout = LAYOUT_NN;
   }
   (void)F;
-  if (act == Act::Sigmoid) return launched(launch_gemm(Prog::Sigmoid, layout, fp8, g, e, s), "linear_sigmoid_fwd");
-  return launched(launch_gemm(Prog::SwiGLU, layout, fp8, g, e, s), "linear_swiglu_fwd");
+  if (act == Act::Sigmoid)
+    return launched(launch_fwd(Prog::Sigmoid, layout, fp8, aq.fp4, g, e, s), "linear_sigmoid_fwd");
+  return launched(launch_fwd(Prog::SwiGLU, layout, fp8, aq.fp4, g, e, s), "linear_swiglu_fwd");
 }
 
 static coda_status swiglu_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, const coda_mat* out,
                                     const coda_mat* save, const coda_mat* r_out, int precision) {
-  TRY(check_precision(precision));
+  TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, K = x->cols;
   if (!Wgu) return fail(CODA_ERR_NULL, "Wgu: NULL");
@@ -598,14 +633,14 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   (void)N;
-  *bytes = precision != CODA_PREC_BF16 ? fwd_fp8_bytes(M, K, precision == CODA_PREC_MXFP8) : 0;
+  *bytes = precision != CODA_PREC_BF16 ? fwd_fp8_bytes(M, K, is_mx(precision), precision == CODA_PREC_MXFP4) : 0;
   return CODA_OK;
 }
 
 extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weight* W, const coda_mat* residual,
                                                         const coda_mat* out, const coda_mat* P_out, int32_t precision,
                                                         void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_precision(precision));
+  TRY(check_precision_fwd(precision));
   TRY(check_mat(a, "a", CODA_BF16, -1, -1));
   const int64_t M = a->rows, K = a->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
@@ -618,7 +653,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
   Carver cv(ws);
   ActQ aq{};
   const bool fp8 = precision != CODA_PREC_BF16;
-  if (fp8) aq = take_act(cv, M, K, 1, precision == CODA_PREC_MXFP8);
+  if (fp8) aq = take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   EpiArgs e = epi0();
@@ -630,7 +665,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
   int layout;
   if (fp8) {
     TRY(quant_act(aq, a->ptr, a->ld, M, K, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, K);
+    g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, aq.fp4 ? K / 2 : K);
     e.rowscale = aq.q.s; e.colscale = fptr(&W->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &W->s_fwd);
     layout = LAYOUT_NT;
@@ -638,7 +673,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
     g = gemm_args(a->ptr, a->ld, W->w.ptr, W->w.ld, M, N, K);
     layout = LAYOUT_NN;
   }
-  return launched(launch_gemm(prog, layout, fp8, g, e, s), "linear_rmsnorm_residual_fwd");
+  return launched(launch_fwd(prog, layout, fp8, aq.fp4, g, e, s), "linear_rmsnorm_residual_fwd");
 }
 
 extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t D, int32_t have_partials,
@@ -647,7 +682,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t 
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision != CODA_PREC_BF16) take_act(cv, M, D, 1, precision == CODA_PREC_MXFP8);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, D, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -657,7 +692,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
                                                    int32_t seq_len, float eps, const coda_mat* q, const coda_mat* k,
                                                    const coda_mat* v, const coda_mat* save, const coda_mat* r_out,
                                                    int32_t precision, void* ws, size_t ws_bytes, void* stream) {
-  TRY(check_precision(precision));
+  TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, D = x->cols;
   if (D % 128 != 0) return fail(CODA_ERR_SHAPE, "qknorm_rope: D must be a multiple of 128");
@@ -681,7 +716,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   float* sumsq = cv.take<float>(M);
   const bool fp8 = precision != CODA_PREC_BF16;
   ActQ aq{};
-  if (fp8) aq = take_act(cv, M, D, 1, precision == CODA_PREC_MXFP8);
+  if (fp8) aq = take_act(cv, M, D, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   if (!present(P)) TRY(row_sumsq_launch(x->ptr, x->ld, M, D, sumsq, s));
@@ -704,7 +739,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   int layout;
   if (fp8) {
     TRY(quant_act(aq, x->ptr, x->ld, M, D, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, D);
+    g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, aq.fp4 ? D / 2 : D);
     e.rowscale = aq.q.s; e.colscale = fptr(&Wqkv->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wqkv->s_fwd);
     layout = LAYOUT_NT;
@@ -712,7 +747,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
     g = gemm_args(x->ptr, x->ld, Wqkv->w.ptr, Wqkv->w.ld, M, 3 * D, D);
     layout = LAYOUT_NN;
   }
-  return launched(launch_gemm(Prog::QKRope, layout, fp8, g, e, s), "linear_qknorm_rope_fwd");
+  return launched(launch_fwd(Prog::QKRope, layout, fp8, aq.fp4, g, e, s), "linear_qknorm_rope_fwd");
 }
 
 // ======================================================================== functional backward
@@ -1547,7 +1582,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
 // ======================================================================== RMSNorm -> Linear -> sigmoid
 static coda_status sigmoid_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* W, const coda_mat* out,
                                      const coda_mat* save, const coda_mat* r_out, int precision) {
-  TRY(check_precision(precision));
+  TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, K = x->cols;
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");

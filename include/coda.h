@@ -78,10 +78,18 @@ typedef enum coda_dtype {
 typedef enum coda_precision {
   CODA_PREC_BF16 = 0, /* bf16 operands, fp32 accumulate */
   CODA_PREC_FP8 = 1,  /* OCP E4M3 operands with amax scales, fp32 accumulate */
-  CODA_PREC_MXFP8 = 2 /* E4M3 operands with one E8M0 scale per 32 values of the
-                         contracted axis (OCP MX), fp32 accumulate; every
-                         contracted size (hidden, MLP width, tokens of a
-                         backward) a multiple of 128 */
+  CODA_PREC_MXFP8 = 2, /* E4M3 operands with one E8M0 scale per 32 values of the
+                          contracted axis (OCP MX), fp32 accumulate; every
+                          contracted size (hidden, MLP width, tokens of a
+                          backward) a multiple of 128 */
+  CODA_PREC_MXFP4 = 3  /* E2M1 operands (two a byte) with one E8M0 scale per 32
+                          values of the contracted axis, fp32 accumulate;
+                          forward entry points only (linear_swiglu,
+                          linear_rmsnorm_residual, linear_qknorm_rope,
+                          linear_sigmoid _fwd), the others return
+                          CODA_ERR_UNSUPPORTED; the weight needs only w, q_fwd
+                          (E2M1X2 [N, K/2]) and s_fwd (word layout); K_in a
+                          multiple of 128 */
 } coda_precision;
 
 typedef struct coda_mat {
@@ -272,7 +280,9 @@ coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const 
  *   CODA_PREC_MXFP8  E4M3 operands, one E8M0 exponent per 32 values of the
  *                    contracted axis, applied by the scaled MFMA; the weight
  *                    carries the two block-scaled copies; every contracted
- *                    size must be a multiple of 128 (CODA_ERR_SHAPE otherwise).
+ *                    size must be a multiple of 128 (CODA_ERR_SHAPE otherwise);
+ *   CODA_PREC_MXFP4  E2M1 operands under the same exponents, forward entry
+ *                    points only; the weight carries the forward copy only.
  * Activations are quantised per call into the workspace (the *_workspace
  * queries size it for the given precision).  The cross-entropy entry points
  * take CODA_PREC_BF16 only (CODA_ERR_UNSUPPORTED otherwise). */

@@ -36,6 +36,7 @@ from typing import Callable, Dict, Optional
 import numpy as np
 
 from . import mx
+from . import mx_small
 from . import numerics as nm
 from . import ops
 
@@ -56,7 +57,14 @@ def mm(A, B, fp8=False):
     E8M0 scale per 32 consecutive values of the contracted axis K: along the
     rows of A and down the columns of B; OCP Microscaling Formats v1.0) and the
     product of the dequantised operands is taken in float64, then float32.
+
+    With fp8 = "mx4", the same with MXFP4 operands (E2M1 elements,
+    oracle/mx_small.py).
     """
+    if fp8 == "mx4":
+        PA, eA = mx_small.quantize(np.asarray(A, np.float32), "e2m1")
+        PB, eB = mx_small.quantize(np.ascontiguousarray(np.asarray(B, np.float32).T), "e2m1")
+        return mx_small.matmul_nt(PA, eA, PB, eB).astype(np.float32)
     if fp8 == "mx":
         PA, eA = mx.quantize(np.asarray(A, np.float32))
         PB, eB = mx.quantize(np.ascontiguousarray(np.asarray(B, np.float32).T))

@@ -624,3 +624,42 @@ def test_mfma_loop_probe(dtype, per_instr):
     r = res.cpu().numpy()
     assert np.all(np.isfinite(r)) and np.all(r[:, 0] > 0)
     assert np.all(r[:, 1] > 0) and np.all(r[:, 2] > 0)
+
+
+def test_block_mxfp4_forward_same_inputs():
+    """The MXFP4 (E2M1 operands, one E8M0 exponent per 32 values) forward,
+    one call at a time from identical inputs: the QKV + QK-norm + RoPE and
+    O-proj + residual calls from the block's inputs, the gate/up + SwiGLU
+    call from the library's own h1 and the down + residual call from its own
+    a, so that every quantiser on both sides sees the same bits (an E2M1
+    code is coarse: one bf16 ulp of an input can move a value by a whole
+    step).  Held to the MXFP8 rule.  The backward is not built for MXFP4 and
+    refuses with CODA_ERR_UNSUPPORTED."""
+    from tests.helpers import FP8_TOL
+    from oracle import ops
+    shape = ci.BlockShape(M=300, D=256, F=384, seq_len=128)
+    P = ci.block_inputs(shape, 9)
+    params = {k: (f32(v) if k in ("g1", "g2", "gq", "gk") else bf(v)) for k, v in P.items()}
+    blk = Block(params, shape.D, shape.F, seq_len=shape.seq_len, theta=shape.theta, eps=shape.eps,
+                precision=coda.PREC_MXFP4)
+    f = blk.forward(params["x"], params["o"])
+    torch.cuda.synchronize()
+    f = {k: to_np(v) for k, v in f.items()}
+    F = ob.block_forward_contract(P, shape, fp8="mx4")
+    D = shape.D
+    for k in ("q", "k", "v", "h1"):
+        assert_bf16(k, f[k], F[k], tol=FP8_TOL, norm_rel=2e-2)
+    assert_bf16("q_pre", f["qk_pre"][:, :D], F["q_pre"], tol=FP8_TOL, norm_rel=2e-2)
+    c = {k: np.asarray(v, np.float32) for k, v in P.items()}
+    W = ob.fold_weights(c)
+    h1 = f["h1"].astype(np.float32)
+    r2 = ops.inv_rms(h1, shape.eps)[:, None]
+    hg = r2 * ob.mm(h1, W["Wg_t"], "mx4")
+    hu = r2 * ob.mm(h1, W["Wu_t"], "mx4")
+    a_ref = nm.bf16(ops.swiglu(hg, hu))
+    assert_bf16("a", f["a"], a_ref, tol=FP8_TOL, norm_rel=2e-2)
+    y_ref = nm.bf16(h1 + ob.mm(f["a"].astype(np.float32), c["Wd"], "mx4"))
+    assert_bf16("y", f["y"], y_ref, tol=FP8_TOL, norm_rel=2e-2)
+    fwd = blk.forward(params["x"], params["o"])
+    with pytest.raises(coda.CodaError):
+        blk.backward(params["x"], params["o"], fwd, params["dY"], params["dq"], params["dk"], params["dv"])

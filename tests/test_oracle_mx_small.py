@@ -124,3 +124,30 @@ def test_matmul_triple_loop():
             for k in range(64):
                 ref += float(PA[m, k]) * 2.0 ** eA[m, k // 32] * float(PB[n, k]) * 2.0 ** eB[n, k // 32]
             assert C[m, n] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+def test_block_gemm_mx4_mode_axes():
+    """oracle.block.mm(A, B, "mx4") quantises A along its rows and B down its
+    columns: operands that are already MXFP4 along those axes come back as
+    the exact product; quantising B along its rows instead changes it."""
+    from oracle import block as ob
+    rng = np.random.default_rng(11)
+    vals = ms.decode(all_codes("e2m1"), "e2m1")
+    top = vals[np.abs(vals) >= 4]
+
+    def mx4_rows(rows, nblocks):
+        X = np.empty((rows, 32 * nblocks))
+        for r in range(rows):
+            for b in range(nblocks):
+                blk = np.concatenate([[rng.choice(top)], rng.choice(vals, size=31)])
+                rng.shuffle(blk)
+                X[r, 32 * b:32 * b + 32] = blk * 2.0 ** rng.integers(-6, 2)
+        return X.astype(np.float32)
+
+    A = mx4_rows(5, 3)
+    B = np.ascontiguousarray(mx4_rows(64, 3).T)       # [96, 64], MXFP4 down its columns
+    got = ob.mm(A, B, "mx4")
+    ref = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(got, ref)
+    P, e = ms.quantize(B, "e2m1")
+    assert not np.array_equal(ms.dequantize(P, e), B.astype(np.float64))
