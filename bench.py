@@ -403,6 +403,15 @@ def main():
                    "speedup_fused_over_unfused": round(ums / ms, 4)}
 
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
+    fp4_fwd = None
+    if not args.no_mx:
+        # the same block forward (inference) with MXFP4 operands: weights
+        # quantised once, activations per call, outputs into the same buffers
+        blk4 = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, precision=coda.PREC_MXFP4)
+        ms4 = timed(lambda: blk4.forward(x, o, f), max(1, args.steps // 2))
+        fp4_fwd = {"block_fwd_ms": round(ms4, 4), "tflops": round(block_flops(M, cfg.D, cfg.F)[0] / (ms4 * 1e-3) / 1e12, 1),
+                   f"speedup_over_{precision}_fwd": round(fwd_ms / ms4, 4)}
+        del blk4
     mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
     ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
     fwd, bwd = block_flops(M, cfg.D, cfg.F)
@@ -442,6 +451,7 @@ def main():
                      "flop_per_launch": f3_flop, "traffic": stored_traffic(args.config, precision)},
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,
+        "mxfp4_block_forward": fp4_fwd,
         "cross_entropy": ce,
         "mfma_loop": mloop,
     }
