@@ -215,6 +215,35 @@ def test_sigmoid_fp8():
         assert rel_norm(got[k], B[k]) <= 2e-2, (k, rel_norm(got[k], B[k]))
 
 
+def test_sigmoid_mxfp4_forward():
+    """RMSNorm -> Linear -> sigmoid with MXFP4 operands (forward only): the
+    same bf16 x and folded weight are quantised identically on both sides,
+    so only the accumulation differs; held to the MXFP8 rule.  The backward
+    refuses MXFP4."""
+    from tests.helpers import FP8_TOL
+    rng = np.random.default_rng(14)
+    M, D, N = 300, 256, 352
+    x, W = rand_bf16(rng, M, D), rand_bf16(rng, D, N, std=D ** -0.5)
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    Wu = bf(W)
+    Wt = coda.Weight(coda.fold_gain(Wu, f32(g), torch.empty_like(Wu))).prepare_mxfp4()
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    h = torch.empty((M, N), dtype=BF, device=DEV)
+    r = torch.empty(M, dtype=torch.float32, device=DEV)
+    coda.linear_sigmoid_fwd(bf(x), Wt, 1e-6, out, save_h=h, r_out=r, precision=coda.PREC_MXFP4)
+    torch.cuda.synchronize()
+    F = ob.sigmoid_forward_contract(x, g, W, 1e-6, fp8="mx4")
+    assert_bf16("h", to_np(h), F["h"], tol=FP8_TOL, norm_rel=2e-2)
+    assert_bf16("a", to_np(out), F["a"], tol=FP8_TOL, norm_rel=2e-2)
+    assert_grad("r", to_np(r), F["r"])
+    du = torch.empty((M, D), dtype=BF, device=DEV)
+    with pytest.raises(coda.CodaError):
+        Wn = coda.Weight(bf(rand_bf16(rng, N, D, std=N ** -0.5)))
+        coda.linear_sigmoid_bwd(bf(x), Wn, h, r, bf(x), Wt, Wu, f32(g), None, du,
+                                torch.empty((D, N), dtype=torch.float32, device=DEV),
+                                torch.empty(D, dtype=torch.float32, device=DEV), precision=coda.PREC_MXFP4)
+
+
 # ------------------------------------------------------------------ block forward / backward
 SMALL = ci.BlockShape(M=300, D=256, F=352, seq_len=128)
 MEDIUM = ci.BlockShape(M=520, D=384, F=480, seq_len=200)
