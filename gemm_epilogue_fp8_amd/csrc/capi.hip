@@ -1289,7 +1289,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
   TRY(check_vec(n_valid, "n_valid", CODA_I32, 1));
   TRY(check_mat(dh, "dh", CODA_BF16, M, D));
   TRY(check_mat(dW, "dW", CODA_F32, D, V));
-  if (ignore_index != -100) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy_bwd: ignore_index must be -100 in this build");
+  if (ignore_index >= 0 && ignore_index < V) return fail(CODA_ERR_VALUE, "ignore_index must lie outside [0, V)");
   const int64_t vc = ce_slice_cols(M, V, chunk_rows);
   Carver cv(ws);
   float* scale;
@@ -1314,6 +1314,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
       e.labels = lab;
       e.rowvec = lsep;
       e.col_offset = (int)v0;
+      e.vocab = (int)V;
       GemmArgs g = gemm_args(hp, h->ld, Wp + v0, W->w.ld, M, nv, D);
       TRY(launched(launch_gemm(Prog::CrossEntropyG, LAYOUT_NN, false, g, e, s), "cross_entropy_bwd: G"));
     }
@@ -1490,8 +1491,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
   TRY(check_mat(dy, "dy", CODA_BF16, M, D));
   TRY(check_mat(dW, "dW", CODA_F32, D, V));
   TRY(check_vec(dg, "dg", CODA_F32, D));
-  if (ignore_index != -100)
-    return fail(CODA_ERR_UNSUPPORTED, "rmsnorm_cross_entropy_bwd: ignore_index must be -100 in this build");
+  if (ignore_index >= 0 && ignore_index < V) return fail(CODA_ERR_VALUE, "ignore_index must lie outside [0, V)");
   const int64_t vc = ce_slice_cols(M, V, chunk_rows);
   Carver cv(ws);
   float *scale, *Tp, *Tc, *dgp, *dy_acc;
@@ -1526,6 +1526,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
       e.rowvec = lsep;
       e.rowvec2 = rp;
       e.col_offset = (int)v0;
+      e.vocab = (int)V;
       e.partial_out = Tp + pc * M;
       GemmArgs g = gemm_args(yp, y->ld, Wp + v0, W->w.ld, M, nv, D);
       TRY(launched(launch_gemm(Prog::CrossEntropyGNorm, LAYOUT_NN, false, g, e, s), "rmsnorm_cross_entropy_bwd: G"));

@@ -968,7 +968,8 @@ struct EpiCrossEntropy {
 };
 
 // --- cross-entropy backward recompute: G = bf16(exp(z - lse) - [n == y]) on
-// rows whose label is not ignored, 0 on ignored rows.
+// rows whose label lies in [0, vocab), 0 on every other row (the ignore index
+// and labels out of range alike: the forward leaves both out of the mean).
 // NORM: z = r acc with the given r (rowvec2); the stored tile is
 // G~ = bf16(r (p - onehot)) and T[tn][m] = sum over the tile of G~ z is
 // written as row partials (the RMSNorm-backward statistic).
@@ -985,7 +986,7 @@ struct EpiCrossEntropyGrad {
       part[i] = 0.0f;
       const int m = c.row(i);
       const int y = e.labels[c.rowc(i)];
-      const bool valid = m < c.M && y != -100;
+      const bool valid = m < c.M && y >= 0 && y < e.vocab;
       const float lse = e.rowvec[c.rowc(i)];
       const float r = NORM ? e.rowvec2[c.rowc(i)] : 1.0f;
 #pragma unroll

@@ -380,13 +380,18 @@ coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const coda_mat* dk, 
 
 /* ===================================================================== cross-entropy */
 
-/* Linear + cross-entropy forward without materialising the logits:
+/* Linear + cross-entropy forward without materialising the logits (the
+ * running-state primitive of the CODA paper, §3.1 item 5: an online
+ * log-sum-exp carried across N tiles, finished by a light merge step):
  *   z = h W (per N tile: online max / sum-exp partials, label-logit gather),
  *   lse[m], per-row loss, loss = sum_valid / n_valid (NaN if n_valid = 0).
- * h: bf16 [M, D]; W: [D, V]; labels: int32 1 x M; rows whose label equals
- * ignore_index are skipped.  Outputs: loss fp32 1 x 1, lse fp32 1 x M,
- * per_row fp32 1 x M (optional), n_valid int32 1 x 1 (required),
- * n_bad int32 1 x 1 (optional; count of labels outside [0, V)). */
+ * h: bf16 [M, D]; W: [D, V]; labels: int32 1 x M.  A row is valid when its
+ * label lies in [0, V); rows whose label equals ignore_index (which must lie
+ * outside [0, V), else CODA_ERR_VALUE) are skipped, and any other label
+ * outside [0, V) is a data error: the row is skipped too and counted in
+ * n_bad.  Outputs: loss fp32 1 x 1, lse fp32 1 x M, per_row fp32 1 x M
+ * (optional, 0 on skipped rows), n_valid int32 1 x 1 (required), n_bad int32
+ * 1 x 1 (optional). */
 coda_status coda_linear_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t precision,
                                                     size_t* bytes);
 coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
@@ -395,15 +400,17 @@ coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* 
                                           const coda_mat* n_bad, int32_t precision, void* ws, size_t ws_bytes,
                                           void* stream);
 
-/* Backward: recompute z, G = bf16(exp(z - lse) - onehot(label)) (0 on
- * ignored rows), s = dloss / n_valid,
+/* Backward: recompute z, G = bf16(exp(z - lse) - onehot(label)) on valid
+ * rows, exactly 0 on every row whose label lies outside [0, V) (ignored or
+ * bad, as counted by the forward), s = dloss / n_valid,
  *   dh = bf16(s * G W^T) [M, D],  dW = beta dW + s * h^T G (fp32 [D, V]).
  * chunk_rows bounds the recomputed logits: 0 (or >= M) recomputes all M x V
  * at once; otherwise the buffer holds about chunk_rows x V values and the
  * recompute runs over vocabulary slices of that many values (a multiple of
  * 256 columns), each slice writing its own columns of dW, with dh summed in
  * fp32 over the slices and rounded to bf16 once (the workspace then also
- * holds an fp32 [M, D] buffer). */
+ * holds an fp32 [M, D] buffer).  ignore_index must lie outside [0, V) as in
+ * the forward. */
 coda_status coda_linear_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
                                                     int32_t precision, size_t* bytes);
 coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
@@ -466,7 +473,8 @@ coda_status coda_linear_rmsnorm_cross_entropy_fwd(const coda_mat* y, const coda_
                                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Backward, recomputing z:
- *   G~ = bf16(r (exp(z - lse) - onehot)) (0 on ignored rows), s = dloss / n_valid,
+ *   G~ = bf16(r (exp(z - lse) - onehot)) (0 on rows whose label lies outside
+ *   [0, V)), s = dloss / n_valid,
  *   T = s sum_v G~ z,  dy = bf16(s G~ W~^T - (r T / D) y + dres),
  *   dW = beta dW + s g (y^T G~) (fp32 [D, V]),  dg = beta dg + s sum_v W (y^T G~) (fp32 1 x D).
  * r: the forward's r_out; W_unfolded: W without the gain; g: fp32 1 x D;
@@ -477,7 +485,8 @@ coda_status coda_linear_rmsnorm_cross_entropy_fwd(const coda_mat* y, const coda_
  * columns), each writing its own columns of dW, with s G~ W~^T summed in
  * fp32 over the slices and the correction and rounding applied once after
  * the last (the workspace then also holds an fp32 [M, D] buffer).
- * With M = 0, dW and dg are left unchanged.  ignore_index must be -100. */
+ * With M = 0, dW and dg are left unchanged.  ignore_index must lie outside
+ * [0, V) as in the forward. */
 coda_status coda_linear_rmsnorm_cross_entropy_bwd_workspace(int64_t M, int64_t D, int64_t V, int64_t chunk_rows,
                                                             int32_t precision, size_t* bytes);
 coda_status coda_linear_rmsnorm_cross_entropy_bwd(const coda_mat* y, const coda_mat* r, const coda_weight* W,

@@ -271,14 +271,15 @@ def ce_forward_contract(h, W, labels, ignore_index=-100, fp8: bool = False):
 def ce_backward_contract(h, W, labels, lse, n_valid, dloss=1.0, ignore_index=-100,
                          rnd: Callable = nm.bf16, fp8: bool = False,
                          dW_prior=None, beta: float = 0.0):
-    """G = bf16(exp(z - lse) - onehot(label)) on valid rows (0 on ignored rows),
-    then dh = rnd(s * G W^T) and dW = beta * prior + s * h^T G with the float32
-    scale s = dloss / n_valid."""
+    """G = bf16(exp(z - lse) - onehot(label)) on valid rows, those whose label
+    lies in [0, V) (0 on ignored rows and on rows with a label out of range,
+    which the forward leaves out of the mean), then dh = rnd(s * G W^T) and
+    dW = beta * prior + s * h^T G with the float32 scale s = dloss / n_valid."""
     h = np.asarray(h, np.float32)
     W = np.asarray(W, np.float32)
     labels = np.asarray(labels)
     z = mm(h, W, fp8)
-    valid = labels != ignore_index
+    valid = (labels >= 0) & (labels < W.shape[1])
     p = np.exp(z - np.asarray(lse, np.float32)[:, None]).astype(np.float32)
     rows = np.nonzero(valid)[0]
     p[rows, labels[rows]] -= np.float32(1.0)
@@ -387,7 +388,8 @@ def norm_ce_backward_contract(y, g, W, labels, lse, r, n_valid, eps, dloss=1.0, 
     """Reparameterised backward with the fused path's rounding points.
 
     z is recomputed as r (y W~).  The stored gradient tile is
-    G~ = rnd(r (exp(z - lse) - onehot)) on valid rows (0 on ignored rows);
+    G~ = rnd(r (exp(z - lse) - onehot)) on valid rows (label in [0, V); 0 on
+    every other row);
     with s = dloss / n_valid (float32) and T = s sum_v G~ z (from the stored
     G~), dy = rnd(s G~ W~^T - (r T / D) y + dres), dW = beta prior +
     s g (y^T G~) and dg = beta prior + s sum_v W (y^T G~).
@@ -399,7 +401,7 @@ def norm_ce_backward_contract(y, g, W, labels, lse, r, n_valid, eps, dloss=1.0, 
     labels = np.asarray(labels)
     r = np.asarray(r, dt)
     z = r[:, None] * mm(y, Wt)
-    valid = labels != ignore_index
+    valid = (labels >= 0) & (labels < W.shape[1])     # ignored and out-of-range rows get 0
     p = np.exp(z - np.asarray(lse, dt)[:, None]).astype(dt)
     rows = np.nonzero(valid)[0]
     p[rows, labels[rows]] -= dt(1.0)

@@ -68,47 +68,38 @@ def amax_flip_rows(pairs):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def assert_fp8_rows(name, got, ref, flagged, tol=FP8_TOL, flagged_tol=0.25, norm_rel=2e-2):
-    """The elementwise fp8 bound on every row whose quantiser inputs agree on
-    both sides; rows in `flagged` (an upstream amax moved by one ulp) only
-    need |d| <= flagged_tol (1 + |ref|)."""
+# A row whose E4M3 row scale moved between the two sides (its amax differs by
+# one bf16 ulp, about 0.4-0.8%) has about one code in ten re-rounded to the
+# neighbouring E4M3 value (a step of 6-12% of the element); a downstream GEMM
+# output of that row then carries an error of roughly 2e-2 (1 + |ref|) per
+# element, whose tail over a full row set reaches about 0.12.  Such rows may
+# exceed the fp8 bound up to this value, and only a few of them may.
+FP8_FLAGGED_TOL = 0.15
+FP8_MAX_OVER_FRAC = 0.01   # share of rows allowed over the fp8 bound (all of them flagged)
+
+
+def assert_fp8_rows(name, got, ref, flagged, tol=FP8_TOL, flagged_tol=FP8_FLAGGED_TOL, norm_rel=2e-2,
+                    max_over_frac=FP8_MAX_OVER_FRAC):
+    """The elementwise fp8 bound |d| <= tol (1 + |ref|) on every row, except
+    rows in `flagged` (an upstream row amax moved by one ulp), which may exceed
+    it up to flagged_tol.  Every row over the bound must be flagged, and at
+    most max(1, max_over_frac * rows) rows may be over it.  The counts are
+    printed."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     d = np.abs(got - ref) / (1.0 + np.abs(ref))
-    keep = np.ones(got.shape[0], bool)
-    keep[flagged] = False
-    if keep.any():
-        assert d[keep].max() <= tol, f"{name}: max |d|/(1+|ref|) = {d[keep].max():.3e} > {tol} on unflagged rows"
-    if not keep.all():
-        assert d[~keep].max() <= flagged_tol, f"{name}: flagged rows reach {d[~keep].max():.3e}"
-    r = rel_norm(got, ref)
-    assert r <= norm_rel, f"{name}: norm-wise relative error {r:.3e} > {norm_rel}"
-
-
-def amax_flip_cols(pairs):
-    """Columns where the column amax (over rows) differs between the two
-    sides: the E4M3 column quantisers of a weight-gradient GEMM's operands."""
-    return amax_flip_rows([(np.asarray(g).T, np.asarray(r).T) for g, r in pairs])
-
-
-def assert_fp8_grad(name, got, ref, flag_rows, flag_cols, tol=FP8_TOL, flagged_tol=0.5, norm_rel=2e-2):
-    """The fp8 bound on every gradient element whose row and column quantisers
-    saw the same amax on both sides; elements in a flagged row or column only
-    need |d| <= flagged_tol (1 + |ref|).  A vector gradient is one row."""
-    got = np.atleast_2d(np.asarray(got, np.float64))
-    ref = np.atleast_2d(np.asarray(ref, np.float64))
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    d = np.abs(got - ref) / (1.0 + np.abs(ref))
-    keep = np.ones(got.shape, bool)
-    keep[np.asarray(flag_rows, np.int64), :] = False
-    keep[:, np.asarray(flag_cols, np.int64)] = False
-    if keep.any():
-        assert d[keep].max() <= tol, f"{name}: max |d|/(1+|ref|) = {d[keep].max():.3e} > {tol} on unflagged elements"
-    if not keep.all():
-        assert d[~keep].max() <= flagged_tol, f"{name}: flagged elements reach {d[~keep].max():.3e}"
+    rows = got.shape[0]
+    flagged = np.asarray(flagged, np.int64)
+    over = np.nonzero(d.max(axis=1) > tol)[0]
+    print(f"{name}: {len(flagged)} of {rows} rows flagged ({len(flagged) / max(rows, 1):.2%}), "
+          f"{len(over)} over the fp8 bound, max |d|/(1+|ref|) {d.max():.3e}")
+    stray = np.setdiff1d(over, flagged)
+    assert len(stray) == 0, f"{name}: rows {stray[:8].tolist()} exceed {tol} with no moved amax upstream"
+    assert len(over) <= max(1, int(max_over_frac * rows)), f"{name}: {len(over)} rows over the fp8 bound"
+    if len(flagged):
+        assert d[flagged].max() <= flagged_tol, f"{name}: flagged rows reach {d[flagged].max():.3e}"
     r = rel_norm(got, ref)
     assert r <= norm_rel, f"{name}: norm-wise relative error {r:.3e} > {norm_rel}"
 

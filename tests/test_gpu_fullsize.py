@@ -11,7 +11,7 @@ import pytest
 import coda_inputs as ci
 from oracle import block as ob
 from tests.helpers import assert_bf16, assert_grad, to_dev, to_np, unpack_gu
-from tests.test_gpu_parity import check_block_fp8, check_block_mx
+from tests.test_gpu_parity import check_block_canonical, check_block_fp8, check_block_mx
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -47,7 +47,7 @@ def _check_block(shape, P, f, b, fp8):
         check_block_mx(f, b, F, B)
         return
     if fp8:
-        check_block_fp8(shape, f, b, F, B)
+        check_block_fp8(shape, f, b, F, B, P)
         return
     D = shape.D
     for k in ("q", "k", "v", "h1", "a", "y"):
@@ -82,6 +82,11 @@ def test_block_full_size_bf16(name):
     P = ci.block_inputs(shape, ci.SEEDS[name])
     f, b = _block_gpu(shape, P, coda.PREC_BF16)
     _check_block(shape, P, f, b, fp8=False)
+    if name == "cfg2":
+        # against the plain definition too; at 67 M elements a product like
+        # SiLU(hg) hu magnifies the bf16 pipeline's own rounding past 2e-2 in
+        # its tail, so the full size takes the comparison with the exact result
+        check_block_canonical(P, shape, f, b, direct=False)
 
 
 @pytest.mark.timeout(1200)

@@ -194,25 +194,34 @@ def test_sigmoid_forward_backward(M, D, N, beta):
 
 
 def test_sigmoid_fp8():
-    """E4M3 operands.  The backward reference starts from the device's saved
-    h and r, so dh~ differs only where the two sides round dY Wn^T sums taken
-    in different orders to bf16; rows where that moved dh~'s amax are
-    flagged for dx."""
-    from tests.helpers import amax_flip_rows, assert_fp8_rows
+    """E4M3 operands, forward then backward, against the oracle's own chained
+    evaluation (its forward feeds its backward).  dh~ is rounded from fp32
+    sums taken in different orders on the two sides; rows where that moved
+    dh~'s row amax are flagged for dx (its dgrad quantises dh~ per row).  The
+    weight and gain gradients are held to 2e-2 norm-wise; a stage check from
+    identical inputs (the device's dh~) holds them to the elementwise fp8
+    bound."""
+    from tests.helpers import FP8_TOL, amax_flip_rows, assert_fp8_rows
     M, D, N = 304, 256, 352
     P, got = _run_sigmoid(M, D, N, 12, coda.PREC_FP8)
     F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6, fp8=True)
     none = np.zeros(0, np.int64)
     assert_fp8_rows("h", got["h"], F["h"], none)
     assert_fp8_rows("a", got["a"], F["a"], none)
-    Fg = dict(F, h=got["h"], r=got["r"])
-    B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], Fg, 1e-6, dres=P["dres"],
+    assert_grad("r", got["r"], F["r"])
+    B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], F, 1e-6, dres=P["dres"],
                                      fp8=True)
-    assert_fp8_rows("dh~", got["dht"], B["dht"], none)
-    assert_fp8_rows("dx", got["du"], B["dx"], amax_flip_rows([(got["dht"], B["dht"])]))
+    fl_h = amax_flip_rows([(got["h"], F["h"])])
+    assert_fp8_rows("dh~", got["dht"], B["dht"], fl_h)
+    assert_fp8_rows("dx", got["du"], B["dx"], np.union1d(fl_h, amax_flip_rows([(got["dht"], B["dht"])])))
     for k in ("dW", "dg"):
         assert np.all(np.isfinite(got[k])), k
         assert rel_norm(got[k], B[k]) <= 2e-2, (k, rel_norm(got[k], B[k]))
+    # stage check: the weight-gradient GEMM from the device's own dh~
+    x = P["x"].astype(np.float32)
+    acc = ob.mm(x.T.copy(), got["dht"].astype(np.float32), fp8=True)
+    assert_bf16("dW (same dh~)", got["dW"], P["g"][:, None] * acc, tol=FP8_TOL, norm_rel=1e-3)
+    assert_grad("dg (same dh~)", got["dg"], np.sum(P["W"] * acc, axis=1, dtype=np.float32))
 
 
 def test_sigmoid_mxfp4_forward():
@@ -290,6 +299,61 @@ def test_block_forward_backward(shape, seed):
         assert_grad(k, b[k], B[k])
 
 
+def check_block_canonical(P, shape, f, b, direct=True):
+    """The fused block against the plain definition: the canonical unfused
+    evaluation (RMSNorm, GEMM, QK-norm, RoPE, SwiGLU, residual and their
+    analytic gradients).
+
+    * direct: every bf16 output within 2e-2 (1 + |ref|) of the canonical
+      evaluation with each operator output rounded to bf16 (the
+      operator-by-operator pipeline a framework runs);
+    * every output and gradient at least as close to the exact (float64)
+      canonical result as that bf16 pipeline, within a factor 1.25 norm-wise
+      and elementwise (the CODA paper reports the reparameterisation's error
+      as comparable to the PyTorch reference's, sometimes smaller), and
+      within 2e-2 (1 + |ref|) of it elementwise wherever the bf16 pipeline
+      itself is."""
+    Fc = ob.block_forward_canonical(P, shape, dt=np.float32, rnd=nm.bf16)
+    Bc = ob.block_backward_canonical(P, Fc, shape, dt=np.float32, rnd=nm.bf16)
+    Fi = ob.block_forward_canonical(P, shape)
+    Bi = ob.block_backward_canonical(P, Fi, shape)
+
+    def dmax(g, r):
+        g = np.asarray(g, np.float64)
+        return float((np.abs(g - r) / (1.0 + np.abs(r))).max())
+
+    outs = dict(q=f["q"], k=f["k"], v=f["v"], h1=f["h1"], a=f["a"], y=f["y"], dx=b["dx"], do=b["do"])
+    for k, g in outs.items():
+        can, ide = (Fc[k], Fi[k]) if k in Fc else (Bc[k], Bi[k])
+        if direct:
+            assert_bf16(k + " vs canonical bf16", g, can, norm_rel=None)
+        e_gpu, e_can = dmax(g, ide), dmax(can, ide)
+        n_gpu, n_can = rel_norm(g, ide), rel_norm(can, ide)
+        print(f"{k}: vs exact max {e_gpu:.3e} norm {n_gpu:.3e}; bf16 pipeline max {e_can:.3e} norm {n_can:.3e}")
+        assert e_gpu <= max(BF16_TOL, 1.25 * e_can), (k, e_gpu, e_can)
+        assert n_gpu <= 1.25 * n_can, (k, n_gpu, n_can)
+    dWg, dWu = unpack_gu(b["dWgu"])
+    grads = dict(dWg=dWg, dWu=dWu, dWqkv=b["dWqkv"], dWo=b["dWo"], dWd=b["dWd"], dg1=b["dg1"], dg2=b["dg2"],
+                 dgq=b["dgq"], dgk=b["dgk"])
+    for k, g in grads.items():
+        n_gpu, n_can = rel_norm(g, Bi[k]), rel_norm(Bc[k], Bi[k])
+        print(f"{k}: vs exact norm {n_gpu:.3e}; bf16 pipeline {n_can:.3e}")
+        assert n_gpu <= 1.25 * n_can, (k, n_gpu, n_can)
+
+
+@pytest.mark.parametrize("shape,seed,direct", [(SMALL, 0, True), (MEDIUM, 1, False)])
+def test_block_against_canonical(shape, seed, direct):
+    """At the small size every output is also within 2e-2 (1 + |ref|) of the
+    bf16 operator-by-operator pipeline.  Beyond it, a = SiLU(hg) hu is not:
+    each side rounds the GEMM inputs of hu differently (the folded weight here,
+    the normalised activation there), and that absolute error of hu, about
+    2^-9 of its spread, is multiplied by SiLU(hg) where hu is near 0 and hg is
+    large; the tail of that product passes 2e-2 (2.9e-2 at 520 tokens) for
+    both pipelines against the exact result alike."""
+    P, f, b = _run_block(shape, seed)
+    check_block_canonical(P, shape, f, b, direct=direct)
+
+
 def test_block_deterministic():
     _, f1, b1 = _run_block(SMALL, 4)
     _, f2, b2 = _run_block(SMALL, 4)
@@ -333,7 +397,8 @@ def test_cross_entropy(M, D, V, chunk):
     assert np.all(to_np(dh)[ignored] == 0)
 
 
-def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_dg=None, beta=0.0):
+def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_dg=None, beta=0.0,
+                   ignore_index=-100):
     """GPU final RMSNorm -> LM head -> CE forward and backward; returns host arrays."""
     M, D = y.shape
     V = W.shape[1]
@@ -348,12 +413,13 @@ def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_
     r = torch.empty(M, dtype=torch.float32, device=DEV)
     P = f32(partials) if partials is not None else None
     coda.linear_rmsnorm_cross_entropy_fwd(yd, Wt, 1e-6, lab, loss, lse, nv, sumsq_partials=P, per_row=per_row,
-                                          n_bad=nbad, r_out=r)
+                                          n_bad=nbad, r_out=r, ignore_index=ignore_index)
     dy = torch.empty((M, D), dtype=BF, device=DEV)
     dW = f32(prior_dW) if prior_dW is not None else torch.empty((D, V), dtype=torch.float32, device=DEV)
     dg = f32(prior_dg) if prior_dg is not None else torch.empty(D, dtype=torch.float32, device=DEV)
     coda.linear_rmsnorm_cross_entropy_bwd(yd, r, Wt, Wd, gd, lab, lse, nv, 1.0, dy, dW, dg,
-                                          dres=bf(dres) if dres is not None else None, beta=beta, chunk_rows=chunk)
+                                          dres=bf(dres) if dres is not None else None, beta=beta, chunk_rows=chunk,
+                                          ignore_index=ignore_index)
     torch.cuda.synchronize()
     return dict(loss=loss.item(), lse=to_np(lse), per_row=to_np(per_row), n_valid=int(nv.item()),
                 n_bad=int(nbad.item()), r=to_np(r), dy=to_np(dy), dW=to_np(dW), dg=to_np(dg))
@@ -414,6 +480,59 @@ def test_cross_entropy_bad_label_and_empty():
     assert nbad.item() == 2
 
 
+@pytest.mark.parametrize("chunk,ignore_index", [(0, -100), (100, -1), (0, 1 << 20)])
+def test_cross_entropy_out_of_range_labels(chunk, ignore_index):
+    """Labels outside [0, V) other than the ignore index: the forward counts
+    them in n_bad and leaves them out of n_valid and the loss, and the
+    backward gives their rows G = 0 - their dh rows are exactly 0 and dW
+    equals the oracle's with those rows masked to the ignore index.  Both
+    directions take the same ignore index (any value outside [0, V)).  The
+    last case also runs the final-RMSNorm form."""
+    M, D, V = 300, 256, 1000
+    rng = np.random.default_rng(31 + chunk)
+    hn, Wn = rand_bf16(rng, M, D), rand_bf16(rng, D, V, std=D ** -0.5)
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[[0, 7, 200]] = ignore_index
+    bad_rows = [3, 4, 150, 299]
+    labels[bad_rows] = [V, -3, -100 if ignore_index != -100 else V + 5, 1 << 30]
+    masked = labels.copy()
+    masked[bad_rows] = -100
+    masked[masked == ignore_index] = -100
+    skipped = [0, 7, 200] + bad_rows
+    h, W, lab = bf(hn), bf(Wn), to_dev(labels)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(M, dtype=torch.float32, device=DEV)
+    per_row = torch.empty(M, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    nbad = torch.empty(1, dtype=torch.int32, device=DEV)
+    coda.linear_cross_entropy_fwd(h, W, lab, loss, lse, nv, per_row=per_row, n_bad=nbad, ignore_index=ignore_index)
+    dh = torch.empty((M, D), dtype=BF, device=DEV)
+    dW = torch.empty((D, V), dtype=torch.float32, device=DEV)
+    coda.linear_cross_entropy_bwd(h, W, lab, lse, nv, 1.0, dh, dW, chunk_rows=chunk, ignore_index=ignore_index)
+    torch.cuda.synchronize()
+    Fr = ob.ce_forward_contract(hn, Wn, masked)
+    assert int(nv.item()) == Fr["n_valid"] == M - len(skipped)
+    assert int(nbad.item()) == len(bad_rows)
+    assert abs(loss.item() - Fr["loss"]) <= 1e-4 * abs(Fr["loss"])
+    assert np.all(to_np(per_row)[skipped] == 0)
+    Br = ob.ce_backward_contract(hn, Wn, masked, Fr["lse"], Fr["n_valid"])
+    got_dh = to_np(dh)
+    assert np.all(got_dh[skipped] == 0)
+    assert_bf16("dh", got_dh, Br["dh"])
+    assert_grad("dW", to_np(dW), Br["dW"])
+    if ignore_index == 1 << 20:
+        g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+        got = run_rmsnorm_ce(hn, g, Wn, labels, None, chunk, None, ignore_index=ignore_index)
+        F = ob.norm_ce_forward_contract(hn, g, Wn, masked, 1e-6)
+        assert got["n_valid"] == F["n_valid"] and got["n_bad"] == len(bad_rows)
+        assert abs(got["loss"] - F["loss"]) <= 1e-4 * abs(F["loss"])
+        B = ob.norm_ce_backward_contract(hn, g, Wn, masked, F["lse"], F["r"], F["n_valid"], 1e-6)
+        assert np.all(got["dy"][skipped] == 0)
+        assert_bf16("dy", got["dy"], B["dy"])
+        assert_grad("dW", got["dW"], B["dW"])
+        assert_grad("dg", got["dg"], B["dg"])
+
+
 # ------------------------------------------------------------------ fp8 quantiser
 @pytest.mark.parametrize("axis", [1, 0])
 def test_quantize_e4m3_bit_exact(axis):
@@ -439,18 +558,27 @@ def test_block_fp8_forward_backward(shape, seed):
     P, f, b = _run_block(shape, seed, precision=coda.PREC_FP8)
     F = ob.block_forward_contract(P, shape, fp8=True)
     B = ob.block_backward_contract(P, F, shape, fp8=True)
-    check_block_fp8(shape, f, b, F, B)
+    check_block_fp8(shape, f, b, F, B, P)
 
 
-def check_block_fp8(shape, f, b, F, B):
-    """fp8 block parity.  The tensors that feed E4M3 row quantisers (h1, a,
-    dh~_gu, dh1, dh~_qkv) are bf16 on both sides, rounded from fp32 sums taken
-    in different orders, so a rare element differs by one ulp; where that
-    element is its row's amax, every code of the row moves.  Each output's
-    rows that sit downstream of such a moved amax are flagged and held to a
-    looser bound; all its other rows meet the fp8 bound."""
-    from tests.helpers import amax_flip_rows, assert_fp8_rows
-    D = shape.D
+def check_block_fp8(shape, f, b, F, B, P):
+    """fp8 block parity against the oracle's own chained evaluation.
+
+    The tensors that feed E4M3 row quantisers (h1, a, dh~_gu, dh1, dh~_qkv)
+    are bf16 on both sides, rounded from fp32 sums taken in different orders,
+    so a rare element differs by one ulp; where that element is its row's
+    amax, the row's scale moves and about one code in ten of the row is
+    re-rounded.  Each output's rows downstream of such a moved amax are
+    flagged: every row over the fp8 bound must be flagged, at most 1% of the
+    rows may be over it and none beyond 0.15 (1 + |ref|) (assert_fp8_rows).
+
+    The weight and gain gradients sum all tokens of operands quantised per
+    column, so the chain's flipped codes add up in them: they are held to
+    2e-2 norm-wise against the chain, and each weight-gradient stage is held
+    to the elementwise fp8 bound 6e-2 (1 + |ref|) on every element against
+    the oracle fed the device's own bf16 operands (identical quantiser
+    inputs on both sides)."""
+    from tests.helpers import FP8_TOL, amax_flip_rows, assert_fp8_rows
     dg_, du_ = unpack_gu(b["dht_gu"])
     dht_gu = np.concatenate([dg_, du_], axis=1)
     u = np.union1d
@@ -461,6 +589,7 @@ def check_block_fp8(shape, f, b, F, B):
     fl_do = u(fl_dh1, amax_flip_rows([(b["dh1"], B["dh1"])]))
     fl_dx = u(fl_dh1, amax_flip_rows([(b["dht_qkv"], B["dht_qkv"])]))
     none = np.zeros(0, np.int64)
+    D = shape.D
     for k in ("q", "k", "v", "h1"):
         assert_fp8_rows(k, f[k], F[k], none)
     assert_fp8_rows("q_pre", f["qk_pre"][:, :D], F["q_pre"], none)
@@ -468,6 +597,7 @@ def check_block_fp8(shape, f, b, F, B):
     hg, hu = unpack_gu(f["hgu"])
     assert_fp8_rows("hg", hg, F["hg"], fl_h1)
     assert_fp8_rows("hu", hu, F["hu"], fl_h1)
+    del hg, hu
     assert_fp8_rows("a", f["a"], F["a"], fl_h1)
     assert_fp8_rows("y", f["y"], F["y"], fl_a)
     assert_fp8_rows("dh~_gu", dht_gu, B["dht_gu"], fl_dht_gu)
@@ -475,21 +605,30 @@ def check_block_fp8(shape, f, b, F, B):
     assert_fp8_rows("dh1", b["dh1"], B["dh1"], fl_dh1)
     assert_fp8_rows("do", b["do"], B["do"], fl_do)
     assert_fp8_rows("dx", b["dx"], B["dx"], fl_dx)
-    # Weight and gain gradients sum over all tokens of operands quantised per
-    # column.  A flipped E4M3 code (a one-ulp bf16 difference, from a different
-    # fp32 summation order, that crosses a code boundary) moves every output of
-    # its row by about 1e-3, which flips the bf16 rounding of a good part of
-    # that row; the next quantiser turns those into more code flips, and a
-    # gradient collects them over all tokens and through whole-column amax
-    # moves.  The single-stage tests from identical inputs hold the elementwise
-    # fp8 bound on every element; here the chained gradients are held to
-    # 2e-2 norm-wise.
     dWg, dWu = unpack_gu(b["dWgu"])
     grads = dict(dWg=dWg, dWu=dWu, dWqkv=b["dWqkv"], dWo=b["dWo"], dWd=b["dWd"], dg1=b["dg1"], dg2=b["dg2"],
                  dgq=b["dgq"], dgk=b["dgk"])
     for k, v in grads.items():
         assert np.all(np.isfinite(v)), k
-        assert rel_norm(v, B[k]) <= 2e-2, (k, rel_norm(v, B[k]))
+        r = rel_norm(v, B[k])
+        print(f"{k}: chained norm-wise {r:.3e}")
+        assert r <= 2e-2, (k, r)
+    # each weight-gradient stage from the device's own bf16 operands
+    c = {k: np.asarray(v, np.float32) for k, v in P.items()}
+    g32 = lambda a: np.ascontiguousarray(np.asarray(a, np.float32))
+    Fw = c["Wg"].shape[1]
+    acc = ob.mm(g32(f["h1"].T), g32(dht_gu), fp8=True)
+    stage = dict(dWg=(dWg, c["g2"][:, None] * acc[:, :Fw]), dWu=(dWu, c["g2"][:, None] * acc[:, Fw:]),
+                 dg2=(b["dg2"], np.sum(c["Wg"] * acc[:, :Fw], axis=1) + np.sum(c["Wu"] * acc[:, Fw:], axis=1)))
+    del acc
+    stage["dWd"] = (b["dWd"], ob.mm(g32(f["a"].T), c["dY"], fp8=True))
+    stage["dWo"] = (b["dWo"], ob.mm(g32(c["o"].T), g32(b["dh1"]), fp8=True))
+    acc = ob.mm(g32(c["x"].T), g32(b["dht_qkv"]), fp8=True)
+    stage["dWqkv"] = (b["dWqkv"], c["g1"][:, None] * acc)
+    stage["dg1"] = (b["dg1"], np.sum(c["Wqkv"] * acc, axis=1))
+    del acc
+    for k, (got, ref) in stage.items():
+        assert_bf16(k + " (stage)", got, ref, tol=FP8_TOL, norm_rel=1e-3)
 
 
 def check_block_mx(f, b, F, B):
@@ -655,17 +794,18 @@ def test_mfma_loop_probe(dtype, per_instr):
     assert np.all(r[:, 1] > 0) and np.all(r[:, 2] > 0)
 
 
-def test_block_mxfp4_forward_same_inputs():
-    """The MXFP4 (E2M1 operands, one E8M0 exponent per 32 values) forward,
-    one call at a time from identical inputs: the QKV + QK-norm + RoPE and
-    O-proj + residual calls from the block's inputs, the gate/up + SwiGLU
-    call from the library's own h1 and the down + residual call from its own
-    a, so that every quantiser on both sides sees the same bits (an E2M1
-    code is coarse: one bf16 ulp of an input can move a value by a whole
-    step).  Held to the MXFP8 rule.  The backward is not built for MXFP4 and
-    refuses with CODA_ERR_UNSUPPORTED."""
+def test_block_mxfp4_forward():
+    """The MXFP4 (E2M1 operands, one E8M0 exponent per 32 values) block
+    forward against the oracle's own chained evaluation in the same format,
+    held to the fp8 rule; then each GEMM call again from identical inputs
+    (the gate/up call from the device's h1, the down call from its a), so
+    that every quantiser on both sides sees the same bits.  A chained E2M1
+    code can move by a whole step when a one-ulp bf16 difference upstream
+    crosses a rounding midpoint; the test prints how many rows of h1 and a
+    quantise differently on the two sides.  The backward is not built for
+    MXFP4 and refuses with CODA_ERR_UNSUPPORTED."""
     from tests.helpers import FP8_TOL
-    from oracle import ops
+    from oracle import mx_small, ops
     shape = ci.BlockShape(M=300, D=256, F=384, seq_len=128)
     P = ci.block_inputs(shape, 9)
     params = {k: (f32(v) if k in ("g1", "g2", "gq", "gk") else bf(v)) for k, v in P.items()}
@@ -676,9 +816,15 @@ def test_block_mxfp4_forward_same_inputs():
     f = {k: to_np(v) for k, v in f.items()}
     F = ob.block_forward_contract(P, shape, fp8="mx4")
     D = shape.D
-    for k in ("q", "k", "v", "h1"):
+    for name in ("h1", "a"):
+        pg, eg = mx_small.quantize(f[name].astype(np.float32), "e2m1")
+        pr, er = mx_small.quantize(F[name].astype(np.float32), "e2m1")
+        print(f"{name}: {int(np.sum(np.any(pg != pr, axis=1) | np.any(eg != er, axis=1)))} of {shape.M} rows "
+              f"quantise differently")
+    for k in ("q", "k", "v", "h1", "a", "y"):
         assert_bf16(k, f[k], F[k], tol=FP8_TOL, norm_rel=2e-2)
     assert_bf16("q_pre", f["qk_pre"][:, :D], F["q_pre"], tol=FP8_TOL, norm_rel=2e-2)
+    # the same calls from identical inputs
     c = {k: np.asarray(v, np.float32) for k, v in P.items()}
     W = ob.fold_weights(c)
     h1 = f["h1"].astype(np.float32)
@@ -686,9 +832,9 @@ def test_block_mxfp4_forward_same_inputs():
     hg = r2 * ob.mm(h1, W["Wg_t"], "mx4")
     hu = r2 * ob.mm(h1, W["Wu_t"], "mx4")
     a_ref = nm.bf16(ops.swiglu(hg, hu))
-    assert_bf16("a", f["a"], a_ref, tol=FP8_TOL, norm_rel=2e-2)
+    assert_bf16("a (same h1)", f["a"], a_ref, tol=FP8_TOL, norm_rel=2e-2)
     y_ref = nm.bf16(h1 + ob.mm(f["a"].astype(np.float32), c["Wd"], "mx4"))
-    assert_bf16("y", f["y"], y_ref, tol=FP8_TOL, norm_rel=2e-2)
+    assert_bf16("y (same a)", f["y"], y_ref, tol=FP8_TOL, norm_rel=2e-2)
     fwd = blk.forward(params["x"], params["o"])
     with pytest.raises(coda.CodaError):
         blk.backward(params["x"], params["o"], fwd, params["dY"], params["dq"], params["dk"], params["dv"])

@@ -238,6 +238,47 @@ def test_ce_contract_matches_canonical():
     np.testing.assert_allclose(lse_c, ops.logsumexp_rows(z), rtol=1e-13)
 
 
+def test_ce_backward_out_of_range_labels_are_skipped():
+    """A label outside [0, V) that is not the ignore index is a data error:
+    the forward raises on it (the device path counts it instead) and leaves
+    the row out of the mean, and the backward treats the row like an ignored
+    one - its G row and dh row are exactly 0 and it adds nothing to dW.  So
+    the backward with bad labels equals the backward with those rows set to
+    the ignore index, which torch's float64 cross-entropy (ignore_index=-100)
+    pins: dz and dW match its autograd with the rows masked."""
+    rng = np.random.default_rng(14)
+    M, D, V = 24, 16, 50
+    h = ci.to_bf16_values(rng.standard_normal((M, D)).astype(np.float32))
+    W = ci.to_bf16_values((rng.standard_normal((D, V)) / math.sqrt(D)).astype(np.float32))
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[[1, 5]] = -100
+    bad = labels.copy()
+    bad[[3, 8, 9]] = [V, -3, 2 ** 30]
+    with pytest.raises(ValueError):
+        ob.ce_forward_contract(h, W, bad)
+    masked = bad.copy()
+    masked[[3, 8, 9]] = -100
+    f = ob.ce_forward_contract(h, W, masked)
+    assert f["n_valid"] == M - 5
+    b_bad = ob.ce_backward_contract(h, W, bad, f["lse"], f["n_valid"], rnd=_ident)
+    b_msk = ob.ce_backward_contract(h, W, masked, f["lse"], f["n_valid"], rnd=_ident)
+    for k in ("G", "dh", "dW"):
+        assert np.array_equal(b_bad[k], b_msk[k]), k
+    assert np.all(b_bad["G"][[1, 3, 5, 8, 9]] == 0) and np.all(b_bad["dh"][[1, 3, 5, 8, 9]] == 0)
+    H, Wt = torch.tensor(h.astype(np.float64), requires_grad=True), torch.tensor(W.astype(np.float64),
+                                                                                  requires_grad=True)
+    torch.nn.functional.cross_entropy(H @ Wt, torch.tensor(masked.astype(np.int64)), ignore_index=-100).backward()
+    np.testing.assert_allclose(b_bad["dW"], Wt.grad.numpy(), rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(b_bad["dh"], H.grad.numpy(), rtol=1e-4, atol=1e-6)
+    # the final-norm form skips them the same way
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    F = ob.norm_ce_forward_contract(h, g, W, masked, 1e-6, rnd=_ident)
+    n_bad = ob.norm_ce_backward_contract(h, g, W, bad, F["lse"], F["r"], F["n_valid"], 1e-6, rnd=_ident)
+    n_msk = ob.norm_ce_backward_contract(h, g, W, masked, F["lse"], F["r"], F["n_valid"], 1e-6, rnd=_ident)
+    for k in ("G", "dy", "dW", "dg"):
+        assert np.array_equal(n_bad[k], n_msk[k]), k
+
+
 # ------------------------------------------------------------------ final RMSNorm -> LM head -> CE
 def _norm_ce_tiny(seed=21, M=12, D=16, V=40):
     rng = np.random.default_rng(seed)
