@@ -370,6 +370,16 @@ def linear_cross_entropy_fwd(h, W, labels, loss, lse, n_valid, per_row=None, n_b
     return loss
 
 
+def linear_cross_entropy_fwd_noalloc(h, W, labels, loss, lse, n_valid, per_row=None, n_bad=None,
+                                     ignore_index=-100):
+    """bf16 linear + cross-entropy forward through the entry point that takes
+    no workspace (its partials live in the library's per-GPU scratch array)."""
+    wc = W if isinstance(W, Weight) else Weight(W)
+    _check(lib().coda_linear_cross_entropy_fwd_noalloc(_p(h), C.byref(wc.c()), _p(labels), ignore_index, _p(loss),
+                                                       _p(lse), _p(per_row), _p(n_valid), _p(n_bad), _stream()))
+    return loss
+
+
 def linear_cross_entropy_bwd(h, W, labels, lse, n_valid, dloss, dh, dW, beta=0.0, chunk_rows=0, ignore_index=-100,
                              precision: int = PREC_BF16):
     L = lib()

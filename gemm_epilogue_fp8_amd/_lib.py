@@ -80,6 +80,7 @@ SIGNATURES = {
                                     M_, M_, M_, M_, M_, f32, M_, i32, vp, sz, vp],
     "coda_linear_cross_entropy_fwd_workspace": [i64, i64, i64, i32, szp],
     "coda_linear_cross_entropy_fwd": [M_, W_, M_, i32, M_, M_, M_, M_, M_, i32, vp, sz, vp],
+    "coda_linear_cross_entropy_fwd_noalloc": [M_, W_, M_, i32, M_, M_, M_, M_, M_, vp],
     "coda_linear_cross_entropy_bwd_workspace": [i64, i64, i64, i64, i32, szp],
     "coda_linear_cross_entropy_bwd": [M_, W_, M_, i32, M_, M_, f32, M_, M_, f32, i64, i32, vp, sz, vp],
     "coda_linear_sigmoid_fwd_workspace": [i64, i64, i32, i32, szp],

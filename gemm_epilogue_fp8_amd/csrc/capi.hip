@@ -1,6 +1,8 @@
 // C ABI of the GEMM+epilogue library: host-side validation, workspace
 // carving and the launch sequences of the functional entry points.  See
 // include/coda.h for the contract of every entry point.
+#include <mutex>
+
 #include "capi_util.hpp"
 #include "aux_kernels.hpp"
 #include "launch.hpp"
@@ -1177,6 +1179,11 @@ static size_t ce_fwd_layout(Carver& cv, int64_t M, int64_t V, int64_t D, int pre
   return cv.off;
 }
 
+static coda_status ce_fwd_impl(const coda_mat* h, const coda_weight* W, const coda_mat* labels, int32_t ignore_index,
+                               const coda_mat* loss, const coda_mat* lse, const coda_mat* per_row,
+                               const coda_mat* n_valid, const coda_mat* n_bad, int32_t precision, void* ws,
+                               size_t ws_bytes, void* stream, const char* who);
+
 extern "C" coda_status coda_linear_cross_entropy_fwd_workspace(int64_t M, int64_t D, int64_t V, int32_t precision,
                                                                size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
@@ -1194,6 +1201,66 @@ extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const co
                                                      const coda_mat* per_row, const coda_mat* n_valid,
                                                      const coda_mat* n_bad, int32_t precision, void* ws,
                                                      size_t ws_bytes, void* stream) {
+  return ce_fwd_impl(h, W, labels, ignore_index, loss, lse, per_row, n_valid, n_bad, precision, ws, ws_bytes, stream,
+                     "cross_entropy_fwd");
+}
+
+// ---- the same forward without a workspace argument, for callers that cannot
+// allocate.  Its partial (max, sum-exp) rows, label logits and row status live
+// in this file-scope device array, one copy per GPU, held until the process
+// ends.  Every element the forward reads there is written earlier in the same
+// call (each (N tile, row) partial by its tile, each row's status by the row
+// finish), so nothing needs clearing between calls; calls that overlap on one
+// GPU share the array and race.
+static __device__ __align__(256) char scratch[CODA_CE_FWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current device's copy of `scratch` (the array's
+// name in host code is only a stand-in for it).
+coda_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CODA_ERR_LAUNCH, "cross_entropy_fwd_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy_fwd_noalloc: device %d", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return fail(CODA_ERR_LAUNCH, "cross_entropy_fwd_noalloc: hipGetSymbolAddress: %s",
+                hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return CODA_OK;
+}
+}  // namespace
+
+extern "C" coda_status coda_linear_cross_entropy_fwd_noalloc(const coda_mat* h, const coda_weight* W,
+                                                             const coda_mat* labels, int32_t ignore_index,
+                                                             const coda_mat* loss, const coda_mat* lse,
+                                                             const coda_mat* per_row, const coda_mat* n_valid,
+                                                             const coda_mat* n_bad, void* stream) {
+  TRY(check_mat(h, "h", CODA_BF16, -1, -1));
+  if (!W) return fail(CODA_ERR_NULL, "W: NULL");
+  size_t need = 0;
+  TRY(coda_linear_cross_entropy_fwd_workspace(h->rows, h->cols, W->w.cols, CODA_PREC_BF16, &need));
+  if (need > sizeof(scratch))
+    return fail(CODA_ERR_WORKSPACE,
+                "cross_entropy_fwd_noalloc: M = %lld, V = %lld needs %zu bytes of scratch, at most %zu available",
+                (long long)h->rows, (long long)W->w.cols, need, sizeof(scratch));
+  void* ptr = nullptr;
+  TRY(scratch_ptr(&ptr));
+  return ce_fwd_impl(h, W, labels, ignore_index, loss, lse, per_row, n_valid, n_bad, CODA_PREC_BF16, ptr,
+                     sizeof(scratch), stream, "cross_entropy_fwd_noalloc");
+}
+
+static coda_status ce_fwd_impl(const coda_mat* h, const coda_weight* W, const coda_mat* labels, int32_t ignore_index,
+                               const coda_mat* loss, const coda_mat* lse, const coda_mat* per_row,
+                               const coda_mat* n_valid, const coda_mat* n_bad, int32_t precision, void* ws,
+                               size_t ws_bytes, void* stream, const char* who) {
   TRY(check_precision(precision));
   if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(h, "h", CODA_BF16, -1, -1));
@@ -1224,15 +1291,15 @@ extern "C" coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const co
     e.rowvec_out = zy;
     e.vocab = (int)V;
     GemmArgs g = gemm_args(h->ptr, h->ld, W->w.ptr, W->w.ld, M, V, D);
-    TRY(launched(launch_gemm(Prog::CrossEntropy, LAYOUT_NN, false, g, e, s), "cross_entropy_fwd: logits"));
+    TRY(launched(launch_gemm(Prog::CrossEntropy, LAYOUT_NN, false, g, e, s), who));
     hipLaunchKernelGGL(ce_finish_rows_kernel, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, Pm, Ps,
                        (int)coda_partials_cols(V), (int)M, zy, static_cast<const int*>(labels->ptr), (int)V,
                        ignore_index, static_cast<float*>(lse->ptr), per, st);
-    TRY(check_launch("cross_entropy_fwd: rows"));
+    TRY(check_launch(who));
   }
   hipLaunchKernelGGL(ce_finish_loss_kernel, dim3(1), dim3(1024), 0, s, per, st, (int)M, static_cast<float*>(loss->ptr),
                      static_cast<int*>(n_valid->ptr), present(n_bad) ? static_cast<int*>(n_bad->ptr) : nullptr);
-  return check_launch("cross_entropy_fwd: loss");
+  return check_launch(who);
 }
 
 // The backward recomputes the logits into a bf16 buffer G.  With chunk_rows

@@ -400,6 +400,23 @@ coda_status coda_linear_cross_entropy_fwd(const coda_mat* h, const coda_weight* 
                                           const coda_mat* n_bad, int32_t precision, void* ws, size_t ws_bytes,
                                           void* stream);
 
+/* The same forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument, bf16 operands only.  The partials live
+ * in a library-owned device array of CODA_CE_FWD_NOALLOC_SCRATCH_BYTES, one
+ * copy per GPU, held until the process ends; the call allocates nothing.
+ * Shapes whose partials need more (2 ceil(V / 256) M + 3 M floats, about
+ * 33 MB at M = 8192, V = 128256) return CODA_ERR_WORKSPACE.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the
+ * caller.  Arguments, outputs and errors otherwise as in
+ * coda_linear_cross_entropy_fwd; the results are bitwise those of it. */
+#define CODA_CE_FWD_NOALLOC_SCRATCH_BYTES (48u << 20)
+coda_status coda_linear_cross_entropy_fwd_noalloc(const coda_mat* h, const coda_weight* W, const coda_mat* labels,
+                                                  int32_t ignore_index, const coda_mat* loss, const coda_mat* lse,
+                                                  const coda_mat* per_row, const coda_mat* n_valid,
+                                                  const coda_mat* n_bad, void* stream);
+
 /* Backward: recompute z, G = bf16(exp(z - lse) - onehot(label)) on valid
  * rows, exactly 0 on every row whose label lies outside [0, V) (ignored or
  * bad, as counted by the forward), s = dloss / n_valid,
