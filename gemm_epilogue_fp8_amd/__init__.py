@@ -19,7 +19,10 @@ from . import _lib
 from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
                    PREC_MXFP4,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
-                   EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS)
+                   EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS, EPI_STORE_ROW_VEC,
+                   EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU, EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION,
+                   EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL, EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV,
+                   EPI_DEQUANT_E4M3)
 
 __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "rope_table", "row_sumsq",
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
@@ -209,20 +212,30 @@ def partials_cols(N: int) -> int:
 
 # ---------------------------------------------------------------- generic
 def gemm_epi(program: Sequence[tuple], A, transA: int, B, transB: int, D, aux: Iterable = ()):
-    """program: sequence of (opcode, slot, fparam) tuples (see coda.h)."""
+    """program: sequence of (opcode, slot, fparam) or (opcode, (slot, slot2,
+    slot3), fparam) tuples (see coda.h); D may be None for chains that store
+    nothing.  E4M3 operands (torch.float8_e4m3fn) when the program starts
+    with EPI_DEQUANT_E4M3."""
     prog = _program(program)
     aux = list(aux)
     arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    M = A.shape[1] if transA else A.shape[0]
+    N = B.shape[0] if transB else B.shape[1]
+    K = A.shape[0] if transA else A.shape[1]
+    ws, n = _ws_call(lib().coda_gemm_epi_workspace, (C.byref(prog), M, N, K), A.device)
     _check(lib().coda_gemm_epi(C.byref(prog), _p(A), transA, _p(B), transB, _p(D),
-                               arr if aux else None, len(aux), _stream()))
+                               arr if aux else None, len(aux), ws, n, _stream()))
     return D
 
 
 def _program(program):
     prog = _lib.EpiProgram()
     prog.n_ops = len(program)
-    for i, (op, slot, fparam) in enumerate(program):
-        prog.ops[i].op, prog.ops[i].slot, prog.ops[i].fparam = op, slot, fparam
+    for i, (op, slots, fparam) in enumerate(program):
+        slots = tuple(slots) if isinstance(slots, (tuple, list)) else (slots,)
+        slots = slots + (0,) * (3 - len(slots))
+        o = prog.ops[i]
+        o.op, o.slot, o.slot2, o.slot3, o.fparam = op, slots[0], slots[1], slots[2], fparam
     return prog
 
 
@@ -265,8 +278,9 @@ def gemm_mx(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     prog = _program(program)
     aux = list(aux)
     arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    ws, n = _ws_call(lib().coda_gemm_epi_workspace, (C.byref(prog), A.shape[0], B.shape[0], A.shape[1]), A.device)
     _check(lib().coda_gemm_mx(C.byref(prog), _p(A), _p(SA), _p(B), _p(SB), _p(D),
-                              arr if aux else None, len(aux), _stream()))
+                              arr if aux else None, len(aux), ws, n, _stream()))
     return D
 
 
@@ -279,8 +293,10 @@ def gemm_mx4(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
     a, b = mat(A), mat(B)
     a.dtype = b.dtype = CODA_E2M1X2
+    ws, n = _ws_call(lib().coda_gemm_epi_workspace, (C.byref(prog), A.shape[0], B.shape[0], 2 * A.shape[1]),
+                     A.device)
     _check(lib().coda_gemm_mx(C.byref(prog), C.byref(a), _p(SA), C.byref(b), _p(SB), _p(D),
-                              arr if aux else None, len(aux), _stream()))
+                              arr if aux else None, len(aux), ws, n, _stream()))
     return D
 
 

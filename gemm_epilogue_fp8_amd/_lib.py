@@ -20,6 +20,9 @@ STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_DTYPE", 3: "CODA_ERR_SH
 
 EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE = 1, 2, 3, 4
 EPI_ADD_TILE, EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS = 5, 6, 7, 8
+EPI_STORE_ROW_VEC, EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU = 9, 10, 11, 12
+EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION, EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL = 13, 14, 15, 16
+EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV, EPI_DEQUANT_E4M3 = 17, 18, 19, 20, 21
 MAX_EPI_OPS = 8
 
 
@@ -34,8 +37,8 @@ class CodaWeight(C.Structure):
 
 
 class EpiOp(C.Structure):
-    _fields_ = [("op", C.c_uint16), ("slot", C.c_uint16), ("flags", C.c_uint16),
-                ("reserved", C.c_uint16), ("fparam", C.c_float)]
+    _fields_ = [("op", C.c_uint16), ("slot", C.c_uint16), ("slot2", C.c_uint16),
+                ("slot3", C.c_uint16), ("fparam", C.c_float)]
 
 
 class EpiProgram(C.Structure):
@@ -61,10 +64,11 @@ SIGNATURES = {
     "coda_quantize_e4m3": [M_, i32, M_, M_, vp, sz, vp],
     "coda_quantize_weight_workspace": [W_, szp],
     "coda_quantize_weight": [W_, vp, sz, vp],
-    "coda_gemm_epi": [C.POINTER(EpiProgram), M_, i32, M_, i32, M_, M_, C.c_uint32, vp],
+    "coda_gemm_epi_workspace": [C.POINTER(EpiProgram), i64, i64, i64, szp],
+    "coda_gemm_epi": [C.POINTER(EpiProgram), M_, i32, M_, i32, M_, M_, C.c_uint32, vp, sz, vp],
     "coda_quantize_mxfp8": [M_, i32, M_, M_, vp],
     "coda_quantize_mxfp4": [M_, i32, M_, M_, vp],
-    "coda_gemm_mx": [C.POINTER(EpiProgram), M_, M_, M_, M_, M_, M_, C.c_uint32, vp],
+    "coda_gemm_mx": [C.POINTER(EpiProgram), M_, M_, M_, M_, M_, M_, C.c_uint32, vp, sz, vp],
     "coda_linear_swiglu_fwd_workspace": [i64, i64, i32, i32, szp],
     "coda_linear_swiglu_fwd": [M_, M_, W_, f32, M_, M_, M_, i32, vp, sz, vp],
     "coda_linear_rmsnorm_residual_fwd_workspace": [i64, i64, i64, i32, szp],

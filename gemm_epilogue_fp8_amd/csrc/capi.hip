@@ -360,98 +360,426 @@ extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, siz
 
 // ======================================================================== generic
 namespace {
-// Decodes an epilogue program for a product C [M, N] with contracted size K
-// into the compiled program, its epilogue arguments and the shape and type of
-// D.  Checks the program's auxiliary operands.
-coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, int64_t K, const coda_mat* aux,
-                           uint32_t n_aux, const char* who, Prog* p_out, EpiArgs* e_out, int64_t* out_cols,
-                           int* out_dtype) {
+// The compiled epilogue chains of the generic entry point.  A program is
+// first matched against these opcode patterns (an element may have an
+// alternative opcode and may be optional); the matched ops then bind their
+// aux operands, each checked, into the epilogue arguments of that chain.
+enum : uint16_t {
+  OP_STORE = CODA_EPI_STORE_BF16, OP_ACCUM = CODA_EPI_ACCUM_F32, OP_ROW = CODA_EPI_ROW_SCALE,
+  OP_COL = CODA_EPI_COL_SCALE, OP_ADD = CODA_EPI_ADD_TILE, OP_SUMSQ = CODA_EPI_ROW_SUMSQ_PARTIAL,
+  OP_SWIGLU = CODA_EPI_SWIGLU, OP_RMS = CODA_EPI_ROW_RMS_FROM_PARTIALS, OP_ROWOUT = CODA_EPI_STORE_ROW_VEC,
+  OP_SAVE = CODA_EPI_SAVE_PRE, OP_QKROPE = CODA_EPI_QKNORM_ROPE, OP_DSWIGLU = CODA_EPI_DSWIGLU,
+  OP_DOT = CODA_EPI_ROW_DOT_PARTIAL, OP_NORMCORR = CODA_EPI_NORM_CORRECTION, OP_WGRAD = CODA_EPI_WGRAD_GAIN,
+  OP_CELSE = CODA_EPI_CE_LSE_PARTIAL, OP_CEGRAD = CODA_EPI_CE_GRAD, OP_SIGMOID = CODA_EPI_SIGMOID,
+  OP_DSIGMOID = CODA_EPI_DSIGMOID, OP_SDEV = CODA_EPI_SCALE_DEV, OP_DEQUANT = CODA_EPI_DEQUANT_E4M3,
+};
+
+struct PatEl { uint16_t op, alt; bool opt; };
+struct ChainDef {
+  Prog prog;
+  int n;
+  PatEl el[6];
+};
+constexpr PatEl R(uint16_t o, uint16_t a = 0) { return PatEl{o, a, false}; }
+constexpr PatEl O(uint16_t o) { return PatEl{o, 0, true}; }
+
+// Chains whose prologue or map differ get their own entries, in the order
+// they are tried; a chain matches when every op is consumed in order.
+const ChainDef kChains[] = {
+    {Prog::Store, 1, {R(OP_STORE)}},
+    {Prog::StoreF32, 1, {R(OP_ACCUM)}},
+    {Prog::RowColStore, 3, {R(OP_ROW), R(OP_COL), R(OP_STORE)}},
+    {Prog::ResidSumsq, 3, {R(OP_ADD), R(OP_STORE), R(OP_SUMSQ)}},
+    {Prog::Resid, 2, {R(OP_ADD), R(OP_STORE)}},
+    {Prog::SwiGLU, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_SWIGLU), R(OP_STORE)}},
+    {Prog::Sigmoid, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_SIGMOID), R(OP_STORE)}},
+    {Prog::QKRope, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_QKROPE), R(OP_STORE)}},
+    {Prog::DSwiGLU, 4, {R(OP_DSWIGLU), R(OP_ROW), R(OP_STORE), R(OP_DOT)}},
+    {Prog::DSigmoid, 4, {R(OP_DSIGMOID), R(OP_ROW), R(OP_STORE), R(OP_DOT)}},
+    {Prog::NormCorr, 4, {R(OP_NORMCORR), O(OP_SDEV), O(OP_ADD), R(OP_STORE)}},
+    {Prog::WgradGain, 2, {O(OP_SDEV), R(OP_WGRAD)}},
+    {Prog::CrossEntropyNorm, 3, {R(OP_RMS), O(OP_ROWOUT), R(OP_CELSE)}},
+    {Prog::CrossEntropy, 1, {R(OP_CELSE)}},
+    {Prog::CrossEntropyG, 2, {R(OP_CEGRAD), R(OP_STORE)}},
+    {Prog::CrossEntropyGNorm, 4, {R(OP_ROW), R(OP_CEGRAD), R(OP_STORE), R(OP_DOT)}},
+    {Prog::StoreAlphaDev, 2, {R(OP_SDEV), R(OP_STORE)}},
+    {Prog::F32AlphaDev, 2, {R(OP_SDEV), R(OP_ACCUM)}},
+};
+
+// Matches ops[0..n) against a chain; at[i] is the op of pattern element i or null.
+bool match_chain(const ChainDef& c, const coda_epi_op* ops, uint32_t n, const coda_epi_op** at) {
+  uint32_t k = 0;
+  for (int i = 0; i < c.n; ++i) {
+    const PatEl& p = c.el[i];
+    if (k < n && (ops[k].op == p.op || (p.alt && ops[k].op == p.alt))) {
+      at[i] = &ops[k++];
+    } else if (p.opt) {
+      at[i] = nullptr;
+    } else {
+      return false;
+    }
+  }
+  return k == n;
+}
+
+// Splits off a leading DEQUANT_E4M3 and finds the compiled chain.
+coda_status find_chain(const coda_epi_program* prog, const char* who, const ChainDef** chain,
+                       const coda_epi_op** at, const coda_epi_op** dequant) {
   if (!prog) return fail(CODA_ERR_NULL, "%s: NULL program", who);
   if (prog->n_ops == 0 || prog->n_ops > CODA_MAX_EPI_OPS)
     return fail(CODA_ERR_UNSUPPORTED, "%s: empty or too long program", who);
-  const coda_epi_op* op = prog->ops;
-  const uint32_t n = prog->n_ops;
-  auto auxm = [&](uint16_t slot) -> const coda_mat* { return (aux && slot < n_aux) ? &aux[slot] : nullptr; };
-  for (uint32_t i = 0; i < n; ++i)
-    if (op[i].flags != 0) return fail(CODA_ERR_UNSUPPORTED, "%s: op %u has flags set", who, i);
-  EpiArgs e = epi0();
-  Prog p;
-  *out_cols = N;
-  *out_dtype = CODA_BF16;
-  if (n == 1 && op[0].op == CODA_EPI_STORE_BF16) {
-    p = Prog::Store;
-  } else if (n == 1 && op[0].op == CODA_EPI_ACCUM_F32) {
-    p = Prog::StoreF32; e.beta = op[0].fparam; *out_dtype = CODA_F32;
-  } else if (n == 3 && op[0].op == CODA_EPI_ROW_SCALE && op[1].op == CODA_EPI_COL_SCALE && op[2].op == CODA_EPI_STORE_BF16) {
-    p = Prog::RowColStore;
-    TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
-    TRY(check_vec(auxm(op[1].slot), "col scale", CODA_F32, N));
-    e.rowvec = fptr(auxm(op[0].slot));
-    e.colvec = fptr(auxm(op[1].slot));
-  } else if ((n == 2 || n == 3) && op[0].op == CODA_EPI_ADD_TILE && op[1].op == CODA_EPI_STORE_BF16 &&
-             (n == 2 || op[2].op == CODA_EPI_ROW_SUMSQ_PARTIAL)) {
-    p = Prog::ResidSumsq;
-    TRY(check_mat(auxm(op[0].slot), "tile", CODA_BF16, M, N));
-    e.aux0 = auxm(op[0].slot)->ptr;
-    e.ld_aux0 = auxm(op[0].slot)->ld;
-    if (n == 3) {
-      TRY(check_mat(auxm(op[2].slot), "partials", CODA_F32, coda_partials_cols(N), M));
-      if (auxm(op[2].slot)->rows > 1 && auxm(op[2].slot)->ld != M)
-        return fail(CODA_ERR_LAYOUT, "%s: partials ld must be M", who);
-      e.partial_out = static_cast<float*>(auxm(op[2].slot)->ptr);
-    } else {
-      p = Prog::Resid;
-    }
-  } else if (n == 3 && (op[0].op == CODA_EPI_ROW_SCALE || op[0].op == CODA_EPI_ROW_RMS_FROM_PARTIALS) &&
-             op[1].op == CODA_EPI_SWIGLU && op[2].op == CODA_EPI_STORE_BF16) {
-    p = Prog::SwiGLU;
-    if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "%s: SWIGLU needs N %% 64 == 0", who);
-    *out_cols = N / 2;
-    if (op[0].op == CODA_EPI_ROW_SCALE) {
-      TRY(check_vec(auxm(op[0].slot), "row scale", CODA_F32, M));
-      e.rowvec = fptr(auxm(op[0].slot));
-    } else {
-      const coda_mat* P = auxm(op[0].slot);
-      TRY(check_mat(P, "partials", CODA_F32, -1, M));
-      if (P->rows < 1 || P->rows > kProloguePartials || P->ld != M)
-        return fail(CODA_ERR_SHAPE, "%s: partials must be [1..8, M] with ld == M", who);
-      e.row_partials = fptr(P);
-      e.n_row_partials = (int)P->rows;
-      e.norm_dim = (int)K;
-      e.eps = op[0].fparam;
-    }
-  } else {
-    return fail(CODA_ERR_UNSUPPORTED, "%s: epilogue program not in the compiled set", who);
+  const coda_epi_op* ops = prog->ops;
+  uint32_t n = prog->n_ops;
+  *dequant = nullptr;
+  if (ops[0].op == OP_DEQUANT) {
+    *dequant = &ops[0];
+    ++ops;
+    --n;
   }
-  *p_out = p;
-  *e_out = e;
+  for (const ChainDef& c : kChains)
+    if (match_chain(c, ops, n, at)) {
+      *chain = &c;
+      return CODA_OK;
+    }
+  char buf[96];
+  int o = 0;
+  for (uint32_t i = 0; i < prog->n_ops && o < 80; ++i) o += snprintf(buf + o, sizeof(buf) - o, " %u", prog->ops[i].op);
+  return fail(CODA_ERR_UNSUPPORTED, "%s: epilogue program (opcodes%s) not in the compiled set", who, o ? buf : "");
+}
+
+bool has_partial_merge(const ChainDef& c, const coda_epi_op* const* at) {
+  for (int i = 0; i < c.n; ++i)
+    if (at[i] && (at[i]->op == OP_RMS || at[i]->op == OP_NORMCORR)) return true;
+  return false;
+}
+
+// What a decoded program launches: the chain, its arguments, D's shape and type.
+struct Decoded {
+  Prog p;
+  EpiArgs e;
+  int64_t out_cols;
+  int out_dtype;            // CODA_BF16, CODA_F32, or 0: D unused
+  bool e4m3;
+  const float* merge_src;   // partial rows to merge to one before the GEMM (n > 8)
+  int merge_n;
+  const float** merge_dst;  // where the merged row goes (e.row_partials)
+};
+
+constexpr int kMaxPartialRows = 32;
+
+// Decodes and checks a program for the product C [M, N] with contracted
+// size K into `d`.  `mx`: the operands carry block exponents (coda_gemm_mx).
+coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, int64_t K, const coda_mat* aux,
+                           uint32_t n_aux, const char* who, bool mx, Decoded* d) {
+  const ChainDef* c;
+  const coda_epi_op* at[6];
+  const coda_epi_op* dq;
+  TRY(find_chain(prog, who, &c, at, &dq));
+  if (dq && mx) return fail(CODA_ERR_UNSUPPORTED, "%s: DEQUANT_E4M3 does not apply to block-scaled operands", who);
+  EpiArgs& e = d->e;
+  e = epi0();
+  d->p = c->prog;
+  d->out_cols = N;
+  d->out_dtype = CODA_BF16;
+  d->e4m3 = dq != nullptr;
+  d->merge_src = nullptr;
+  d->merge_n = 0;
+  d->merge_dst = nullptr;
+  const int64_t tn = coda_partials_cols(N);
+  // operand of `slot` (slot index into aux), checked
+  auto A_ = [&](uint16_t slot) -> const coda_mat* { return (aux && slot < n_aux) ? &aux[slot] : nullptr; };
+  auto vec = [&](uint16_t slot, const char* name, int dt, int64_t n, const coda_mat** out) -> coda_status {
+    TRY(check_vec(A_(slot), name, dt, n));
+    *out = A_(slot);
+    return CODA_OK;
+  };
+  auto tile = [&](uint16_t slot, const char* name, int dt, int64_t rows, int64_t cols,
+                  const coda_mat** out) -> coda_status {
+    TRY(check_mat(A_(slot), name, dt, rows, cols));
+    *out = A_(slot);
+    return CODA_OK;
+  };
+  // fp32 partials [rows, M] (rows < 0: 1..kMaxPartialRows), ld == M
+  auto partials = [&](uint16_t slot, const char* name, int64_t rows, const coda_mat** out) -> coda_status {
+    const coda_mat* P = A_(slot);
+    TRY(check_mat(P, name, CODA_F32, rows, M));
+    if (rows < 0 && (P->rows < 1 || P->rows > kMaxPartialRows))
+      return fail(CODA_ERR_SHAPE, "%s: %s must have 1..%d rows", who, name, kMaxPartialRows);
+    if (P->rows > 1 && P->ld != M) return fail(CODA_ERR_LAYOUT, "%s: %s ld must be M", who, name);
+    *out = P;
+    return CODA_OK;
+  };
+  const coda_mat* m;
+  const coda_mat* m2;
+  const coda_mat* m3;
+  // the row factor of a pre-norm chain: given (ROW_SCALE) or finished from partials
+  auto row_factor = [&](const coda_epi_op* op) -> coda_status {
+    if (op->op == OP_ROW) {
+      TRY(vec(op->slot, "row scale", CODA_F32, M, &m));
+      e.rowvec = fptr(m);
+    } else {
+      TRY(partials(op->slot, "row partials", -1, &m));
+      if (!(op->fparam >= 0.0f)) return fail(CODA_ERR_VALUE, "%s: eps must be >= 0", who);
+      e.row_partials = fptr(m);
+      e.n_row_partials = (int)m->rows;
+      e.norm_dim = (int)K;
+      e.eps = op->fparam;
+      if (m->rows > kProloguePartials) {
+        d->merge_src = fptr(m);
+        d->merge_n = (int)m->rows;
+        d->merge_dst = &e.row_partials;
+      }
+    }
+    return CODA_OK;
+  };
+  auto row_out = [&](const coda_epi_op* op, float** dst) -> coda_status {
+    if (!op) return CODA_OK;
+    TRY(vec(op->slot, "row vector output", CODA_F32, M, &m));
+    *dst = static_cast<float*>(m->ptr);
+    return CODA_OK;
+  };
+  auto save = [&](const coda_epi_op* op, int64_t cols) -> coda_status {
+    if (!op) return CODA_OK;
+    TRY(tile(op->slot, "save", CODA_BF16, M, cols, &m));
+    e.save = m->ptr;
+    e.ld_save = m->ld;
+    return CODA_OK;
+  };
+  auto dev_scale = [&](const coda_epi_op* op) -> coda_status {
+    if (!op) return CODA_OK;
+    TRY(vec(op->slot, "device scale", CODA_F32, 1, &m));
+    e.alpha_dev = fptr(m);
+    return CODA_OK;
+  };
+  switch (c->prog) {
+    case Prog::Store: break;
+    case Prog::StoreF32:
+      e.beta = at[0]->fparam;
+      d->out_dtype = CODA_F32;
+      break;
+    case Prog::RowColStore:
+      TRY(vec(at[0]->slot, "row scale", CODA_F32, M, &m));
+      TRY(vec(at[1]->slot, "col scale", CODA_F32, N, &m2));
+      e.rowvec = fptr(m);
+      e.colvec = fptr(m2);
+      break;
+    case Prog::ResidSumsq:
+      TRY(partials(at[2]->slot, "sumsq partials", tn, &m2));
+      e.partial_out = static_cast<float*>(m2->ptr);
+      [[fallthrough]];
+    case Prog::Resid:
+      TRY(tile(at[0]->slot, "tile", CODA_BF16, M, N, &m));
+      e.aux0 = m->ptr;
+      e.ld_aux0 = m->ld;
+      break;
+    case Prog::SwiGLU:
+    case Prog::Sigmoid:
+    case Prog::QKRope: {
+      TRY(row_factor(at[0]));
+      TRY(row_out(at[1], &e.rowvec_out));
+      if (c->prog == Prog::SwiGLU) {
+        if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "%s: SWIGLU needs N %% 64 == 0 (packed gate/up)", who);
+        d->out_cols = N / 2;
+        TRY(save(at[2], N));
+      } else if (c->prog == Prog::Sigmoid) {
+        TRY(save(at[2], N));
+      } else {
+        if (N % 384 != 0) return fail(CODA_ERR_SHAPE, "%s: QKNORM_ROPE needs N = 3 x a multiple of 128", who);
+        const coda_epi_op* q = at[3];
+        TRY(tile(q->slot, "qk gains", CODA_F32, 2, 128, &m));
+        TRY(check_mat(A_(q->slot2), "rope table", CODA_F32, -1, 128));
+        m2 = A_(q->slot2);
+        if (m2->rows < 1) return fail(CODA_ERR_SHAPE, "%s: empty RoPE table", who);
+        if (m2->rows > 1 && m2->ld != 128) return fail(CODA_ERR_LAYOUT, "%s: RoPE table ld must be 128", who);
+        if (!(q->fparam >= 0.0f)) return fail(CODA_ERR_VALUE, "%s: eps must be >= 0", who);
+        if (at[0]->op == OP_RMS && at[0]->fparam != q->fparam)
+          return fail(CODA_ERR_VALUE, "%s: the row norm and the QK-norm take one eps", who);
+        e.eps = q->fparam;
+        e.colvec = fptr(m);
+        e.colvec2 = fptr(m) + (m->rows > 1 ? m->ld : 128);
+        e.table = fptr(m2);
+        e.seq_len = (int)m2->rows;
+        e.region = (int)(N / 3);
+        TRY(save(at[2], 2 * N / 3));
+      }
+      break;
+    }
+    case Prog::DSwiGLU:
+    case Prog::DSigmoid: {
+      const bool sw = c->prog == Prog::DSwiGLU;
+      if (sw && N % 32 != 0) return fail(CODA_ERR_SHAPE, "%s: DSWIGLU needs N %% 32 == 0", who);
+      TRY(tile(at[0]->slot, "saved pre-activation", CODA_BF16, M, sw ? 2 * N : N, &m));
+      e.aux0 = m->ptr;
+      e.ld_aux0 = m->ld;
+      TRY(vec(at[1]->slot, "row scale", CODA_F32, M, &m2));
+      e.rowvec = fptr(m2);
+      TRY(partials(at[3]->slot, "dot partials", tn, &m3));
+      e.partial_out = static_cast<float*>(m3->ptr);
+      if (sw) d->out_cols = 2 * N;
+      break;
+    }
+    case Prog::NormCorr: {
+      const coda_epi_op* q = at[0];
+      TRY(tile(q->slot, "u", CODA_BF16, M, N, &m));
+      TRY(vec(q->slot2, "r", CODA_F32, M, &m2));
+      TRY(partials(q->slot3, "T partials", -1, &m3));
+      e.aux0 = m->ptr;
+      e.ld_aux0 = m->ld;
+      e.rowvec = fptr(m2);
+      e.row_partials = fptr(m3);
+      e.n_row_partials = (int)m3->rows;
+      e.norm_dim = (int)N;
+      if (m3->rows > kProloguePartials) {
+        d->merge_src = fptr(m3);
+        d->merge_n = (int)m3->rows;
+        d->merge_dst = &e.row_partials;
+      }
+      TRY(dev_scale(at[1]));
+      if (at[2]) {
+        TRY(tile(at[2]->slot, "tile", CODA_BF16, M, N, &m));
+        e.aux1 = m->ptr;
+        e.ld_aux1 = m->ld;
+      }
+      break;
+    }
+    case Prog::WgradGain: {
+      TRY(dev_scale(at[0]));
+      const coda_epi_op* q = at[1];
+      TRY(tile(q->slot, "W", CODA_BF16, M, N, &m));
+      TRY(vec(q->slot2, "g", CODA_F32, M, &m2));
+      TRY(partials(q->slot3, "gain partials", tn, &m3));
+      e.aux0 = m->ptr;
+      e.ld_aux0 = m->ld;
+      e.rowvec = fptr(m2);
+      e.partial_out = static_cast<float*>(m3->ptr);
+      e.beta = q->fparam;
+      d->out_dtype = CODA_F32;
+      break;
+    }
+    case Prog::CrossEntropyNorm:
+    case Prog::CrossEntropy: {
+      const bool norm = c->prog == Prog::CrossEntropyNorm;
+      if (norm) {
+        TRY(row_factor(at[0]));
+        TRY(row_out(at[1], &e.rowvec_out2));
+      }
+      const coda_epi_op* q = at[norm ? 2 : 0];
+      TRY(vec(q->slot, "labels", CODA_I32, M, &m));
+      TRY(partials(q->slot2, "lse partials", 2 * tn, &m2));
+      TRY(vec(q->slot3, "label logit", CODA_F32, M, &m3));
+      e.labels = static_cast<const int*>(m->ptr);
+      e.partial_out = static_cast<float*>(m2->ptr);
+      e.partial_out2 = static_cast<float*>(m2->ptr) + tn * M;
+      e.rowvec_out = static_cast<float*>(m3->ptr);
+      e.vocab = (int)N;
+      d->out_dtype = 0;
+      break;
+    }
+    case Prog::CrossEntropyG:
+    case Prog::CrossEntropyGNorm: {
+      const bool norm = c->prog == Prog::CrossEntropyGNorm;
+      const coda_epi_op* q = at[norm ? 1 : 0];
+      TRY(vec(q->slot, "labels", CODA_I32, M, &m));
+      TRY(vec(q->slot2, "lse", CODA_F32, M, &m2));
+      e.labels = static_cast<const int*>(m->ptr);
+      e.rowvec = fptr(m2);
+      e.vocab = (int)N;
+      e.col_offset = 0;
+      if (norm) {
+        TRY(vec(at[0]->slot, "row scale", CODA_F32, M, &m3));
+        e.rowvec2 = fptr(m3);
+        TRY(partials(at[3]->slot, "dot partials", tn, &m));
+        e.partial_out = static_cast<float*>(m->ptr);
+      }
+      break;
+    }
+    case Prog::StoreAlphaDev:
+      TRY(dev_scale(at[0]));
+      break;
+    case Prog::F32AlphaDev:
+      TRY(dev_scale(at[0]));
+      e.beta = at[1]->fparam;
+      d->out_dtype = CODA_F32;
+      break;
+  }
+  if (dq) {
+    TRY(vec(dq->slot, "row dequantisation scales", CODA_F32, M, &m));
+    TRY(vec(dq->slot2, "column dequantisation scales", CODA_F32, N, &m2));
+    e.rowscale = fptr(m);
+    e.colscale = fptr(m2);
+  }
   return CODA_OK;
+}
+
+size_t epi_ws_bytes(int64_t M) {
+  Carver cv(nullptr);
+  cv.take<float>((size_t)M);
+  return cv.off;
+}
+
+// Checks D, carves the workspace, merges wide partials and launches.
+coda_status run_decoded(Decoded& d, int64_t M, const coda_mat* D, GemmArgs g, int layout, bool fp8, bool fp4,
+                        void* ws, size_t ws_bytes, hipStream_t s, const char* who) {
+  if (d.out_dtype != 0) {
+    TRY(check_mat(D, "D", d.out_dtype, M, d.out_cols));
+    d.e.out = D->ptr;
+    d.e.ld_out = D->ld;
+    if (d.p == Prog::QKRope) {   // q | k | v are the three column thirds of D
+      const int64_t w = d.out_cols / 3;
+      d.e.out2 = static_cast<uint16_t*>(D->ptr) + w;
+      d.e.out3 = static_cast<uint16_t*>(D->ptr) + 2 * w;
+      d.e.ld_out2 = d.e.ld_out3 = D->ld;
+    }
+  }
+  Carver cv(ws);
+  float* tmp = d.merge_src ? cv.take<float>((size_t)M) : nullptr;
+  TRY(ws_check(cv, ws_bytes, ws));
+  if (d.merge_src) {
+    const float* P = d.merge_src;
+    int nP = d.merge_n;
+    TRY(narrow_partials(&P, &nP, M, tmp, s));
+    *d.merge_dst = P;
+    d.e.n_row_partials = nP;
+  }
+  hipError_t err = fp4 ? launch_gemm_mx4(d.p, g, d.e, s) : launch_gemm(d.p, layout, fp8, g, d.e, s);
+  if (err == hipErrorInvalidValue)
+    return fail(CODA_ERR_UNSUPPORTED, "%s: this epilogue chain is not compiled for these operands", who);
+  return launched(err, who);
 }
 
 }  // namespace
 
+extern "C" coda_status coda_gemm_epi_workspace(const coda_epi_program* prog, int64_t M, int64_t N, int64_t K,
+                                               size_t* bytes) {
+  if (!bytes) return fail(CODA_ERR_NULL, "gemm_epi_workspace: NULL bytes");
+  (void)N;
+  (void)K;
+  const ChainDef* c;
+  const coda_epi_op* at[6];
+  const coda_epi_op* dq;
+  TRY(find_chain(prog, "gemm_epi_workspace", &c, at, &dq));
+  *bytes = (has_partial_merge(*c, at) && M > 0) ? epi_ws_bytes(M) : 0;
+  return CODA_OK;
+}
+
 extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
                                      const coda_mat* B, int32_t transB, const coda_mat* D, const coda_mat* aux,
-                                     uint32_t n_aux, void* stream) {
+                                     uint32_t n_aux, void* ws, size_t ws_bytes, void* stream) {
   if (!prog) return fail(CODA_ERR_NULL, "gemm_epi: NULL program");
-  TRY(check_mat(A, "A", CODA_BF16, -1, -1));
-  TRY(check_mat(B, "B", CODA_BF16, -1, -1));
+  const bool e4m3 = prog->n_ops > 0 && prog->n_ops <= CODA_MAX_EPI_OPS && prog->ops[0].op == OP_DEQUANT;
+  const int odt = e4m3 ? CODA_E4M3 : CODA_BF16;
+  TRY(check_mat(A, "A", odt, -1, -1));
+  TRY(check_mat(B, "B", odt, -1, -1));
+  if (e4m3 && (transA != 0 || transB != 1))
+    return fail(CODA_ERR_LAYOUT, "gemm_epi: E4M3 operands are A [M, K] and B [N, K] (transA 0, transB 1)");
   const int64_t M = transA ? A->cols : A->rows, K = transA ? A->rows : A->cols;
   const int64_t Kb = transB ? B->cols : B->rows, N = transB ? B->rows : B->cols;
   if (K != Kb) return fail(CODA_ERR_SHAPE, "gemm_epi: inner sizes %lld and %lld differ", (long long)K, (long long)Kb);
   const int layout = (transA ? 2 : 0) + (transB ? 1 : 0);
-  Prog p;
-  EpiArgs e;
-  int64_t out_cols;
-  int out_dtype;
-  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_epi", &p, &e, &out_cols, &out_dtype));
-  if (p != Prog::Store && p != Prog::StoreF32 && layout != LAYOUT_NN)
-    return fail(CODA_ERR_UNSUPPORTED, "gemm_epi: this program is compiled for transA = transB = 0 only");
-  TRY(check_mat(D, "D", out_dtype, M, out_cols));
-  e.out = D->ptr;
-  e.ld_out = D->ld;
+  Decoded d;
+  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_epi", false, &d));
   GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
-  return launched(launch_gemm(p, layout, false, g, e, S(stream)), "gemm_epi");
+  return run_decoded(d, M, D, g, layout, e4m3, false, ws, ws_bytes, S(stream), "gemm_epi");
 }
 
 // ======================================================================== MXFP8
@@ -505,7 +833,7 @@ extern "C" coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, cons
 
 extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                                     const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
-                                    uint32_t n_aux, void* stream) {
+                                    uint32_t n_aux, void* ws, size_t ws_bytes, void* stream) {
   if (!prog) return fail(CODA_ERR_NULL, "gemm_mx: NULL program");
   // E2M1 operands (two values a byte) when A says so; B must match
   const bool fp4 = present(A) && A->dtype == CODA_E2M1X2;
@@ -520,20 +848,14 @@ extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat
                                           (long long)K);
   TRY(check_scales(SA, "SA", M, K));
   TRY(check_scales(SB, "SB", N, K));
-  Prog p;
-  EpiArgs e;
-  int64_t out_cols;
-  int out_dtype;
-  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_mx", &p, &e, &out_cols, &out_dtype));
-  TRY(check_mat(D, "D", out_dtype, M, out_cols));
-  e.out = D->ptr;
-  e.ld_out = D->ld;
+  Decoded d;
+  TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_mx", true, &d));
   GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, Kb);   // the mainloop counts bytes
   g.sA = SA->ptr;
   g.sB = SB->ptr;
   g.lds_a = SA->rows > 1 ? SA->ld : SA->cols;
   g.lds_b = SB->rows > 1 ? SB->ld : SB->cols;
-  return launched(fp4 ? launch_gemm_mx4(p, g, e, S(stream)) : launch_gemm_mx(p, g, e, S(stream)), "gemm_mx");
+  return run_decoded(d, M, D, g, LAYOUT_NT, true, fp4, ws, ws_bytes, S(stream), "gemm_mx");
 }
 
 // ======================================================================== functional forward

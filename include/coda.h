@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CODA_ABI_VERSION 1
+#define CODA_ABI_VERSION 2
 
 typedef enum coda_status {
   CODA_OK = 0,
@@ -158,34 +158,121 @@ coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_byte
 
 /* ===================================================================== generic GEMM + epilogue */
 
-/* One epilogue primitive.  Programs are ordered chains; the library checks a
- * program against the set it has compiled and returns CODA_ERR_UNSUPPORTED
- * otherwise.  Compiled chains (A: [M,K] (transA 0) or [K,M] (transA 1),
- * B: [K,N] (transB 0) or [N,K] (transB 1), bf16):
- *   STORE_BF16                                       D bf16 [M,N]
- *   ACCUM_F32(beta)                                  D fp32 = beta D + acc
- *   ROW_SCALE(v) COL_SCALE(w) STORE_BF16              NN only
- *   ADD_TILE(z) STORE_BF16 [ROW_SUMSQ_PARTIAL(P)]     NN only (residual + next-norm partials)
- *   ROW_SCALE(r) SWIGLU STORE_BF16                    NN only, D [M, N/2]
- *   ROW_RMS_FROM_PARTIALS(P, fparam = eps) SWIGLU STORE_BF16   NN only, P [1..8, M]
- * `slot` indexes the aux array; ROW_SUMSQ_PARTIAL writes P[tiles_n][M] with
- * tiles_n = ceil(N / 256) (see coda_partials_cols). */
+/* The generic entry point: one GEMM whose output tile passes through an
+ * epilogue program before (or instead of) its store.
+ *
+ * The CODA paper (§3.1) builds every epilogue from five primitive classes:
+ *   P1 elementwise and pairwise maps, P2 rank-1 vector loads and stores,
+ *   P3 rank-2 tile loads and stores, P4 tile row reductions written as
+ *   partials and merged later, P5 running state (online log-sum-exp);
+ * §2.2 confines an epilogue to its tile, its accumulator and auxiliaries
+ * indexed like it.  A program is an ordered chain of such primitives.  The
+ * library compiles a fixed set of chains (each one instantiation of the
+ * fixed mainloop with a fused epilogue, no run-time code generation), checks
+ * a program against that set op by op before any HIP call, and returns
+ * CODA_ERR_UNSUPPORTED for any other chain or for a chain not compiled for
+ * the given operand layout or type.
+ *
+ * An op names its primitive, up to three operands by index into the `aux`
+ * array (slot, slot2, slot3; unused ones are ignored) and one float
+ * parameter.  M, N, K are the product's sizes; tiles_n = ceil(N / 256)
+ * (coda_partials_cols(N)); a partials operand [n, M] is fp32 with ld == M.
+ *
+ *   op                     class  operands                                   meaning
+ *   STORE_BF16             P3     -                                          store the tile in bf16 to D
+ *   ACCUM_F32              P3     fparam = beta                              D (fp32) = beta D + value
+ *   ROW_SCALE              P2     slot: fp32 1 x M (r)                       value *= r[m]
+ *   COL_SCALE              P2     slot: fp32 1 x N                           value *= c[n]
+ *   ADD_TILE               P3     slot: bf16 [M, N]                          value += Z[m, n]
+ *   ROW_SUMSQ_PARTIAL      P4     slot: partials [tiles_n, M]                sum over the tile's columns of bf16(stored)^2
+ *   SWIGLU                 P1     -                                          SiLU(gate) * up over packed column pairs
+ *   ROW_RMS_FROM_PARTIALS  P2+P4  slot: partials [n, M] (n <= 32);           r = (sum_t P[t, m] / K + eps)^-1/2 finished in
+ *                                 fparam = eps                               the prologue (n > 8: merged in the workspace);
+ *                                                                            value *= r[m]
+ *   STORE_ROW_VEC          P2     slot: fp32 1 x M                           store the row factor r just finished or given
+ *   SAVE_PRE               P3     slot: bf16 tile                            store the values as they stand (pre-activation)
+ *   QKNORM_ROPE            P1     slot: fp32 [2, 128] gains (q, k);          per 128-column head of the q and k thirds:
+ *                                 slot2: fp32 [seq_len, 128] RoPE table      RMSNorm (eps, gain), then rotation of the
+ *                                 (coda_rope_table); fparam = eps            adjacent pairs at position m mod seq_len
+ *   DSWIGLU                P3+P1  slot: bf16 [M, 2N] saved gate/up (packed)  dhg = da hu s (1 + hg (1 - s)), dhu = da hg s,
+ *                                                                            s = sigmoid(hg); D [M, 2N] packed
+ *   ROW_DOT_PARTIAL        P4     slot: partials [tiles_n, M]                sum over the tile of stored * the map's input
+ *                                                                            (the saved pre-activation, or the logit)
+ *   NORM_CORRECTION        P2+P3  slot: bf16 u [M, N]; slot2: fp32 r 1 x M; value = acc - (r[m] T[m] / N) u[m, n],
+ *                                 slot3: partials T [n, M] (n <= 32)         T = sum_t P[t, m] (RMSNorm backward)
+ *   WGRAD_GAIN             P2+P3+ slot: bf16 W [M, N] (unfolded weight);     D (fp32) = beta D + g[m] value,
+ *                          P4     slot2: fp32 g 1 x M; slot3: partials       P[tn, m] = sum over the tile of W value
+ *                                 [tiles_n, M]; fparam = beta                (the folded gain's gradient)
+ *   CE_LSE_PARTIAL         P5     slot: int32 labels 1 x M; slot2: partials  per (N tile, row): max and sum of exp(z - max)
+ *                                 [2 tiles_n, M] (max rows, then sum rows);  over the columns < N, and the logit of
+ *                                 slot3: fp32 1 x M label logit              column labels[m] gathered; nothing stored to D
+ *   CE_GRAD                P1     slot: int32 labels 1 x M; slot2: fp32      value = exp(z - lse[m]) - [n == labels[m]] on
+ *                                 lse 1 x M                                  rows with a label in [0, N), else 0
+ *   SIGMOID                P1     -                                          value = sigmoid(value)
+ *   DSIGMOID               P3+P1  slot: bf16 [M, N] saved h                  value = da s (1 - s), s = sigmoid(h)
+ *   SCALE_DEV              P2     slot: fp32 1 x 1 device scalar             value *= s
+ *   DEQUANT_E4M3           P2     slot: fp32 1 x M; slot2: fp32 1 x N        E4M3 operands: value = acc sA[m] sB[n]
+ *
+ * Compiled chains ([x] optional, a|b alternatives), and the operand forms
+ * each is compiled for (bf16 layouts NN, NT, TN, TT as transA/transB; E4M3:
+ * A [M, K], B [N, K] with DEQUANT_E4M3 as the program's first op; MX:
+ * coda_gemm_mx):
+ *   STORE_BF16                                              NN NT TN TT E4M3 MX
+ *   ACCUM_F32                                               NN NT TN TT E4M3 MX
+ *   ROW_SCALE COL_SCALE STORE_BF16                          NN MX
+ *   ADD_TILE STORE_BF16 [ROW_SUMSQ_PARTIAL]                 NN E4M3 MX        residual + next-norm partials
+ *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] SWIGLU STORE_BF16
+ *                                                           NN E4M3 MX        D [M, N/2], N % 64 == 0
+ *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] SIGMOID STORE_BF16
+ *                                                           NN E4M3 MX
+ *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] QKNORM_ROPE STORE_BF16
+ *                                                           NN E4M3 MX        D [M, N] = q | k | v, N % 384 == 0;
+ *                                                                             SAVE_PRE [M, 2N/3] = q | k before the norm
+ *   DSWIGLU ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL            NT E4M3 MX        N % 32 == 0
+ *   DSIGMOID ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL           NT E4M3 MX
+ *   NORM_CORRECTION [SCALE_DEV] [ADD_TILE] STORE_BF16       NT E4M3 MX        value = s (acc - c u) + Z
+ *   [SCALE_DEV] WGRAD_GAIN                                  TN E4M3 MX        s scales D's new term and P
+ *   ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] CE_LSE_PARTIAL    NN                z = r acc (final norm folded)
+ *   CE_LSE_PARTIAL                                          NN E4M3
+ *   CE_GRAD STORE_BF16                                      NN E4M3
+ *   ROW_SCALE CE_GRAD STORE_BF16 ROW_DOT_PARTIAL            NN                z = r acc, stored r (p - onehot),
+ *                                                                             T = sum stored * z
+ *   SCALE_DEV STORE_BF16                                    NT E4M3
+ *   SCALE_DEV ACCUM_F32                                     NT TN E4M3
+ * In a chain with ROW_RMS_FROM_PARTIALS and QKNORM_ROPE both eps must be
+ * equal (one eps per epilogue).  Errors: CODA_ERR_UNSUPPORTED (chain or
+ * form not compiled), CODA_ERR_SHAPE / DTYPE / LAYOUT / ALIGN on an operand,
+ * CODA_ERR_VALUE on a parameter, CODA_ERR_WORKSPACE when the workspace is
+ * smaller than coda_gemm_epi_workspace asks. */
 typedef enum coda_epi_opcode {
-  CODA_EPI_STORE_BF16 = 1,            /* P3 store */
-  CODA_EPI_ACCUM_F32 = 2,             /* fp32 beta-accumulate (fparam = beta) */
-  CODA_EPI_ROW_SCALE = 3,             /* P2 row vector (fp32 1 x M) */
-  CODA_EPI_COL_SCALE = 4,             /* P2 column vector (fp32 1 x N) */
-  CODA_EPI_ADD_TILE = 5,              /* P3 tile load (bf16 [M, N]) and add */
-  CODA_EPI_ROW_SUMSQ_PARTIAL = 6,     /* P4 row partial of bf16(value)^2 (fp32 [tiles_n, M]) */
-  CODA_EPI_SWIGLU = 7,                /* P1 pairwise gate/up (packed layout) */
-  CODA_EPI_ROW_RMS_FROM_PARTIALS = 8  /* P2 row vector finished from P4 partials ([n, M]) */
+  CODA_EPI_STORE_BF16 = 1,
+  CODA_EPI_ACCUM_F32 = 2,
+  CODA_EPI_ROW_SCALE = 3,
+  CODA_EPI_COL_SCALE = 4,
+  CODA_EPI_ADD_TILE = 5,
+  CODA_EPI_ROW_SUMSQ_PARTIAL = 6,
+  CODA_EPI_SWIGLU = 7,
+  CODA_EPI_ROW_RMS_FROM_PARTIALS = 8,
+  CODA_EPI_STORE_ROW_VEC = 9,
+  CODA_EPI_SAVE_PRE = 10,
+  CODA_EPI_QKNORM_ROPE = 11,
+  CODA_EPI_DSWIGLU = 12,
+  CODA_EPI_ROW_DOT_PARTIAL = 13,
+  CODA_EPI_NORM_CORRECTION = 14,
+  CODA_EPI_WGRAD_GAIN = 15,
+  CODA_EPI_CE_LSE_PARTIAL = 16,
+  CODA_EPI_CE_GRAD = 17,
+  CODA_EPI_SIGMOID = 18,
+  CODA_EPI_DSIGMOID = 19,
+  CODA_EPI_SCALE_DEV = 20,
+  CODA_EPI_DEQUANT_E4M3 = 21
 } coda_epi_opcode;
 
 typedef struct coda_epi_op {
   uint16_t op;     /* coda_epi_opcode */
-  uint16_t slot;   /* aux index */
-  uint16_t flags;  /* reserved, 0 */
-  uint16_t reserved;
+  uint16_t slot;   /* first aux operand */
+  uint16_t slot2;  /* second aux operand */
+  uint16_t slot3;  /* third aux operand */
   float fparam;
 } coda_epi_op;
 
@@ -198,9 +285,21 @@ typedef struct coda_epi_program {
 /* Number of N tiles (partial rows) an epilogue reduction writes for N columns. */
 int64_t coda_partials_cols(int64_t N);
 
+/* Workspace bytes coda_gemm_epi and coda_gemm_mx need for `prog` at M x N
+ * x K: room to merge more than 8 partial rows (ROW_RMS_FROM_PARTIALS,
+ * NORM_CORRECTION) to one before the GEMM; 0 for other chains.
+ * CODA_ERR_UNSUPPORTED for a chain outside the compiled set. */
+coda_status coda_gemm_epi_workspace(const coda_epi_program* prog, int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/* D = epilogue(op(A) op(B)).  A: bf16 [M, K] (transA 0) or [K, M] (transA
+ * 1), or E4M3 [M, K] when the program starts with DEQUANT_E4M3; B: bf16
+ * [K, N] (transB 0) or [N, K] (transB 1), or E4M3 [N, K].  D as the chain
+ * says (NULL for CE_LSE_PARTIAL chains).  aux: the operands the ops name.
+ * ws: caller-owned device workspace of at least coda_gemm_epi_workspace
+ * bytes (256-byte aligned; NULL when 0).  Asynchronous on `stream`. */
 coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_mat* A, int32_t transA,
                           const coda_mat* B, int32_t transB, const coda_mat* D,
-                          const coda_mat* aux, uint32_t n_aux, void* stream);
+                          const coda_mat* aux, uint32_t n_aux, void* ws, size_t ws_bytes, void* stream);
 
 /* ===================================================================== MXFP8 block-scaled operands */
 
@@ -255,20 +354,21 @@ coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat*
  *        scaled by SB (E8M0 [K / 128, 4 N], word layout);
  * products and sums in fp32 on the matrix cores, the block scales applied
  * by the scaled MFMA.  K must be a positive multiple of 128 (the exponents
- * of 128 K values travel as one 4-byte word).  The epilogue program is any of
- * the chains coda_gemm_epi compiles (STORE_BF16, ACCUM_F32, ROW_SCALE
- * COL_SCALE STORE_BF16, ADD_TILE STORE_BF16 [ROW_SUMSQ_PARTIAL], the two
- * SWIGLU chains), with D shaped as there.  Errors as coda_gemm_epi, plus
- * CODA_ERR_DTYPE / CODA_ERR_SHAPE / CODA_ERR_ALIGN / CODA_ERR_LAYOUT for the
- * scale matrices.
+ * of 128 K values travel as one 4-byte word).  The epilogue program is any
+ * chain coda_gemm_epi compiles for MX operands (its table, column MX), with
+ * D and the aux operands shaped as there, and the same workspace
+ * (coda_gemm_epi_workspace).  Errors as coda_gemm_epi, plus CODA_ERR_DTYPE
+ * / CODA_ERR_SHAPE / CODA_ERR_ALIGN / CODA_ERR_LAYOUT for the scale
+ * matrices.
  * MXFP4: with A of dtype CODA_E2M1X2 the operands are E2M1 (as written by
  * coda_quantize_mxfp4), A [M, K / 2 bytes] and B [N, K / 2 bytes], same
  * exponent layout and K rule (K counts values); the epilogue program is one
  * of STORE_BF16, ACCUM_F32, ROW_SCALE COL_SCALE STORE_BF16, ADD_TILE
- * STORE_BF16 [ROW_SUMSQ_PARTIAL] and the SWIGLU chains. */
+ * STORE_BF16 [ROW_SUMSQ_PARTIAL] and the SWIGLU, SIGMOID and QKNORM_ROPE
+ * chains. */
 coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
-                         const coda_mat* B, const coda_mat* SB, const coda_mat* D,
-                         const coda_mat* aux, uint32_t n_aux, void* stream);
+                         const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
+                         uint32_t n_aux, void* ws, size_t ws_bytes, void* stream);
 
 /* ===================================================================== functional: forward */
 
@@ -287,7 +387,11 @@ coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const 
  * queries size it for the given precision).  The cross-entropy entry points
  * take CODA_PREC_BF16 only (CODA_ERR_UNSUPPORTED otherwise). */
 
-/* RMSNorm -> Linear -> SwiGLU (config-1 op and the block's gate/up GEMM):
+/* RMSNorm -> Linear -> SwiGLU (config-1 op and the block's gate/up GEMM).
+ * Passages: the CODA paper §3.2.1 and Fig. 4 (the GEMM-residual-RMSNorm-GEMM
+ * identity: the norm's per-row factor r moves behind the next GEMM as a row
+ * scale, its gain folds into the weight) and §3.1 item 1 (a pairwise map, here
+ * SiLU(gate) * up; the papers.ananclaw.com guide lists it as linear_swiglu):
  *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r * (x W~_gu),
  *   out = SiLU(h_gate) * h_up
  * x: bf16 [M, K].  sumsq_partials: fp32 [n, M] sum-of-squares partials of x
@@ -305,9 +409,12 @@ coda_status coda_linear_swiglu_fwd(const coda_mat* x, const coda_mat* sumsq_part
                                    const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
                                    void* stream);
 
-/* Residual linear (O-projection, down-projection): out = residual + a W,
- * stored bf16, plus the sum-of-squares partials of the stored out for the
- * next RMSNorm (fp32 [coda_partials_cols(N), M], optional). */
+/* Residual linear (O-projection, down-projection).  Passage: the CODA paper
+ * §3.2.1 (the residual add is tile-local and the next norm's statistic is a
+ * row reduction written as per-tile partials, §3.1 item 4; the guide's
+ * linear_rmsnorm_residual): out = residual + a W, stored bf16, plus the
+ * sum-of-squares partials of the stored out for the next RMSNorm
+ * (fp32 [coda_partials_cols(N), M], optional). */
 coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
                                                        size_t* bytes);
 coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weight* W, const coda_mat* residual,
@@ -315,7 +422,9 @@ coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const coda_weigh
                                              int32_t precision, void* ws, size_t ws_bytes, void* stream);
 
 /* QKV projection with the delayed RMSNorm factor, per-head QK-RMSNorm and
- * RoPE (MHA, head_dim 128, D = heads * 128):
+ * RoPE (MHA, head_dim 128, D = heads * 128).  Passages: the CODA paper
+ * §3.2.1 (delayed r) and §3.1 item 1 (pairwise maps: the RoPE rotation of
+ * adjacent column pairs); the guide lists it as linear_qknorm_rope:
  *   h = r1 * (x W~_qkv) [M, 3D];  q = RoPE(QKnorm(h_q; gq)), k likewise, v = h_v
  * positions p = m mod seq_len.  rope: coda_rope_table output.  Optional
  * saves: qk_pre bf16 [M, 2D] (pre-norm q | k), r_out fp32 1 x M.
@@ -332,7 +441,11 @@ coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda_mat* sumsq
 /* ===================================================================== functional: backward */
 
 /* Backward of RMSNorm -> gate/up Linear -> SwiGLU, fused behind the GEMM
- * that produces the SwiGLU output gradient da = dY Wd^T (never materialised):
+ * that produces the SwiGLU output gradient da = dY Wd^T (never materialised).
+ * Passages: the CODA paper §3.2 (a tile-local forward keeps the
+ * GEMM-epilogue form in the backward) and the KuCoin news summary's results
+ * section (the SwiGLU backward among the fused kernels); the formulas are
+ * the analytic gradients of the reparameterised forward:
  *   dSwiGLU with the saved (packed) hg/hu, dh~ = bf16(r * [dhg, dhu]),
  *   T = sum_j dh~ h,  c = r T / D,
  *   du = dh~ W~_gu^T - c u + dres          (bf16 [M, D]; dres optional)
@@ -350,7 +463,8 @@ coda_status coda_linear_swiglu_bwd(const coda_mat* dY, const coda_weight* Wd, co
                                    const coda_mat* dh_gu_out, int32_t precision, void* ws, size_t ws_bytes,
                                    void* stream);
 
-/* Backward of a residual linear out = residual + a W:
+/* Backward of a residual linear out = residual + a W (the CODA paper §3.2;
+ * the fp32 weight-gradient accumulation is an epilogue store, §3.1 item 3):
  *   dW = beta dW + a^T d_out (fp32 [K, N]);  da = d_out W^T (bf16 [M, K], optional). */
 coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int64_t K, int64_t N, int32_t precision,
                                                        size_t* bytes);
@@ -358,8 +472,9 @@ coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, const coda_m
                                              const coda_mat* da, const coda_mat* dW, float beta,
                                              int32_t precision, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward of the QKV projection with QK-norm and RoPE, given the attention
- * gradients dq, dk (of the rotated q, k) and dv:
+/* Backward of the QKV projection with QK-norm and RoPE (the CODA paper §3.2
+ * and §3.2.1, as for coda_linear_swiglu_bwd), given the attention gradients
+ * dq, dk (of the rotated q, k) and dv:
  *   inverse RoPE, per-head RMSNorm backward from the saved pre-norm q, k,
  *   dh~ = bf16(r1 [dq_pre, dk_pre, dv]),  T = sum_j dh~ h,  c = r1 T / D,
  *   dx = dh~ W~^T - c x + dres (bf16 [M, D]),

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"{n} declared in coda.h but not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
-    assert L.coda_abi_version() == 1
+    assert L.coda_abi_version() == 2
 
 
 def test_status_strings():
@@ -73,14 +73,115 @@ def test_gemm_epi_rejects_unknown_programs():
     prog.n_ops = 2
     prog.ops[0].op = _lib.EPI_SWIGLU
     prog.ops[1].op = _lib.EPI_ROW_SCALE
-    st = L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None)
+    st = L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None, 0, None)
     assert st == 7 and b"not in the compiled set" in L.coda_last_error()
     prog.n_ops = 0
-    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None) == 7
+    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(B), 0, C.byref(D), None, 0, None, 0, None) == 7
     prog.n_ops = 1
     prog.ops[0].op = _lib.EPI_STORE_BF16
     Bbad = fake(BF, 32, 64)
-    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(Bbad), 0, C.byref(D), None, 0, None) == 3
+    assert L.coda_gemm_epi(C.byref(prog), C.byref(A), 0, C.byref(Bbad), 0, C.byref(D), None, 0, None, 0, None) == 3
+
+
+def _prog(ops):
+    prog = _lib.EpiProgram()
+    prog.n_ops = len(ops)
+    for i, (op, slots, fp) in enumerate(ops):
+        slots = tuple(slots) + (0,) * (3 - len(slots))
+        prog.ops[i].op, prog.ops[i].slot, prog.ops[i].slot2, prog.ops[i].slot3 = op, *slots
+        prog.ops[i].fparam = fp
+    return prog
+
+
+def test_epilogue_descriptor_chains_and_operand_checks():
+    """Every compiled chain is recognised (the workspace query accepts it) and
+    its operands are checked before any launch: each case below is one
+    chain with one wrong operand and the status it must return."""
+    L = g.lib()
+    BF, F32, I32, E4 = _lib.CODA_BF16, _lib.CODA_F32, _lib.CODA_I32, _lib.CODA_E4M3
+    E = _lib
+    M, N, K = 64, 768, 128
+    tn = (N + 255) // 256
+    n = C.c_size_t(123)
+    chains = {
+        "swiglu": [(E.EPI_ROW_RMS_FROM_PARTIALS, (0,), 1e-6), (E.EPI_STORE_ROW_VEC, (1,), 0), (E.EPI_SAVE_PRE, (2,), 0),
+                   (E.EPI_SWIGLU, (), 0), (E.EPI_STORE_BF16, (), 0)],
+        "sigmoid": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_SIGMOID, (), 0), (E.EPI_STORE_BF16, (), 0)],
+        "qkrope": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_SAVE_PRE, (1,), 0), (E.EPI_QKNORM_ROPE, (2, 3), 1e-6),
+                   (E.EPI_STORE_BF16, (), 0)],
+        "dswiglu": [(E.EPI_DSWIGLU, (0,), 0), (E.EPI_ROW_SCALE, (1,), 0), (E.EPI_STORE_BF16, (), 0),
+                    (E.EPI_ROW_DOT_PARTIAL, (2,), 0)],
+        "dsigmoid": [(E.EPI_DSIGMOID, (0,), 0), (E.EPI_ROW_SCALE, (1,), 0), (E.EPI_STORE_BF16, (), 0),
+                     (E.EPI_ROW_DOT_PARTIAL, (2,), 0)],
+        "normcorr": [(E.EPI_NORM_CORRECTION, (0, 1, 2), 0), (E.EPI_SCALE_DEV, (3,), 0), (E.EPI_ADD_TILE, (4,), 0),
+                     (E.EPI_STORE_BF16, (), 0)],
+        "wgrad": [(E.EPI_SCALE_DEV, (0,), 0), (E.EPI_WGRAD_GAIN, (1, 2, 3), 1.0)],
+        "ce": [(E.EPI_CE_LSE_PARTIAL, (0, 1, 2), 0)],
+        "ce_norm": [(E.EPI_ROW_RMS_FROM_PARTIALS, (0,), 1e-6), (E.EPI_CE_LSE_PARTIAL, (1, 2, 3), 0)],
+        "ce_grad": [(E.EPI_CE_GRAD, (0, 1), 0), (E.EPI_STORE_BF16, (), 0)],
+        "ce_grad_norm": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_CE_GRAD, (1, 2), 0), (E.EPI_STORE_BF16, (), 0),
+                         (E.EPI_ROW_DOT_PARTIAL, (3,), 0)],
+        "store_dev": [(E.EPI_SCALE_DEV, (0,), 0), (E.EPI_STORE_BF16, (), 0)],
+        "f32_dev": [(E.EPI_SCALE_DEV, (0,), 0), (E.EPI_ACCUM_F32, (), 1.0)],
+        "fp8_resid": [(E.EPI_DEQUANT_E4M3, (0, 1), 0), (E.EPI_ADD_TILE, (2,), 0), (E.EPI_STORE_BF16, (), 0)],
+    }
+    for name, ops in chains.items():
+        pr = _prog(ops)
+        assert L.coda_gemm_epi_workspace(C.byref(pr), M, N, K, C.byref(n)) == 0, (name, L.coda_last_error())
+        need = n.value
+        assert need == (M * 4 if name in ("swiglu", "normcorr", "ce_norm") else 0), (name, need)
+    pr = _prog([(E.EPI_SWIGLU, (), 0), (E.EPI_ROW_SCALE, (0,), 0)])
+    assert L.coda_gemm_epi_workspace(C.byref(pr), M, N, K, C.byref(n)) == 7
+    A, B, Bt = fake(BF, M, K), fake(BF, K, N), fake(BF, N, K)
+
+    def run(ops, aux, D=fake(BF, M, N), A=A, B=B, tB=0, ws=None, nws=0):
+        arr = (_lib.CodaMat * len(aux))(*aux)
+        return L.coda_gemm_epi(C.byref(_prog(ops)), C.byref(A), 0, C.byref(B), tB, C.byref(D) if D else None,
+                               arr, len(aux), ws, nws, None)
+
+    v = lambda dt, k: fake(dt, 1, k)
+    part = lambda rows: fake(F32, rows, M)
+    # SwiGLU: partials with 33 rows; then the workspace missing for 12 rows
+    sw = chains["swiglu"]
+    assert run(sw, [part(33), v(F32, M), fake(BF, M, N)], D=fake(BF, M, N // 2)) == 3
+    assert run(sw, [part(12), v(F32, M), fake(BF, M, N)], D=fake(BF, M, N // 2)) == 6
+    assert run(sw, [part(4), v(F32, M), fake(BF, M, N + 8)], D=fake(BF, M, N // 2)) == 3      # save shape
+    assert run(sw, [part(4), v(F32, M), fake(BF, M, N)], D=fake(BF, M, N)) == 3               # D is [M, N/2]
+    # QK-norm + RoPE: gains [2, 128], table [seq, 128]; N must be 3 x 128 k
+    qk = chains["qkrope"]
+    good_qk = [v(F32, M), fake(BF, M, 2 * N // 3), fake(F32, 2, 128), fake(F32, 16, 128)]
+    assert run(qk, [v(F32, M), fake(BF, M, 2 * N // 3), fake(F32, 1, 128), fake(F32, 16, 128)]) == 3
+    assert run(qk, good_qk[:3] + [fake(F32, 16, 64)]) == 3
+    assert run(qk, good_qk, D=fake(BF, M, 512), B=fake(BF, K, 512)) == 3                      # 512 % 384
+    bad_eps = list(qk)
+    bad_eps[0] = (E.EPI_ROW_RMS_FROM_PARTIALS, (0,), 1e-5)
+    assert run(bad_eps, [part(1)] + good_qk[1:]) == 9                                        # two eps
+    # dSwiGLU: saved [M, 2N], D [M, 2N], partials [tiles_n, M]
+    ds = chains["dswiglu"]
+    assert run(ds, [fake(BF, M, N), v(F32, M), part(tn)], D=fake(BF, M, 2 * N), B=Bt, tB=1) == 3
+    assert run(ds, [fake(BF, M, 2 * N), v(F32, M), part(tn + 1)], D=fake(BF, M, 2 * N), B=Bt, tB=1) == 3
+    # norm correction: u, r, T; r of the wrong length; a 2-element device scale
+    nc = chains["normcorr"]
+    assert run(nc, [fake(BF, M, N), v(F32, M + 1), part(2), v(F32, 1), fake(BF, M, N)], B=Bt, tB=1) == 3
+    assert run(nc, [fake(BF, M, N), v(F32, M), part(2), v(F32, 2), fake(BF, M, N)], B=Bt, tB=1) == 3
+    # weight gradient through the gain: D must be fp32
+    wg = chains["wgrad"]
+    At = fake(BF, K, M)
+    arr = (_lib.CodaMat * 4)(v(F32, 1), fake(BF, M, N), v(F32, M), part(tn))
+    assert L.coda_gemm_epi(C.byref(_prog(wg)), C.byref(At), 1, C.byref(B), 0, C.byref(fake(BF, M, N)), arr, 4,
+                           None, 0, None) == 2
+    # cross-entropy: labels int32, partials [2 tiles_n, M], D unused
+    ce = chains["ce"]
+    assert run(ce, [v(F32, M), part(2 * tn), v(F32, M)], D=None) == 2                        # labels dtype
+    assert run(ce, [v(I32, M), part(tn), v(F32, M)], D=None) == 3                            # one partial set
+    # a chain that exists but is not compiled for the layout: sigmoid on NT operands
+    assert run(chains["sigmoid"], [v(F32, M)], B=Bt, tB=1) == 7
+    # E4M3: A [M, K], B [N, K] only, scales [M] and [N]
+    f8 = chains["fp8_resid"]
+    A8, B8 = fake(E4, M, K), fake(E4, N, K)
+    assert run(f8, [v(F32, M), v(F32, N), fake(BF, M, N)], A=A8, B=fake(E4, K, N), tB=0) == 4   # B layout
+    assert run(f8, [v(F32, M), v(F32, N + 4), fake(BF, M, N)], A=A8, B=B8, tB=1) == 3
+    assert run(f8, [v(F32, M), v(F32, N), fake(BF, M, N)], A=fake(BF, M, K), B=B8, tB=1) == 2    # A not E4M3
 
 
 def test_functional_validation():
@@ -154,7 +255,7 @@ def test_mx_validation_codes():
     prog.n_ops = 1
     prog.ops[0].op = _lib.EPI_STORE_BF16
     gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
-                                                C.byref(D), None, 0, None)
+                                                C.byref(D), None, 0, None, 0, None)
     M, N = 64, 32
     assert gm(fake(E4, M, 192), fake(E8, 2, 4 * M), fake(E4, N, 192), fake(E8, 2, 4 * N),
               fake(BF, M, N)) == 3                                             # K = 192: not a multiple of 128
@@ -260,7 +361,7 @@ def test_mxfp4_gemm_validation_codes():
     prog.n_ops = 1
     prog.ops[0].op = _lib.EPI_STORE_BF16
     gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
-                                                C.byref(D), None, 0, None)
+                                                C.byref(D), None, 0, None, 0, None)
     M, N = 64, 32
     assert gm(fake(E2, M, 128), fake(E8, 2, 4 * M), fake(E4, N, 128), fake(E8, 2, 4 * N),
               fake(BF, M, N)) == 2                                             # B is not E2M1X2
