@@ -84,6 +84,7 @@ def parse():
     ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
+    ap.add_argument("--no-h4096", action="store_true", help="skip the hidden-4096 block leg of the default run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -272,32 +273,37 @@ def cpu_baseline(shape_full, seed, rows, fp8):
                       f"float32 contract mode{OPERANDS[fp8]}, {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
-              f"run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    import coda_inputs as ci
-    cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[args.config]
-    seed = ci.SEEDS[args.config]
-    precision = args.precision or ("fp8" if args.config == "cfg5" else "bf16")
-    fp8 = {"bf16": False, "fp8": True, "mxfp8": "mx"}[precision]
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(cfg, seed, args.cpu_rows or cfg.M, fp8)
+def partial_bytes(M, D, F):
+    """Algorithmic HBM bytes of the cross-N-tile partial-reduction buffers of
+    one block step (fp32, each written once by the producing epilogue and read
+    once by its finish): the forward's sum-of-squares rows, the backward's T
+    rows and the gain-gradient rows."""
+    nt = lambda n: (n + 255) // 256
+    f = 4
+    fwd = {"P_x sumsq(x)": 2 * M * f, "P2 sumsq(h1)": 2 * nt(D) * M * f, "P4 sumsq(y)": 2 * nt(D) * M * f,
+           "r1, r2 saves": 2 * M * f}
+    bwd = {"T2 partials": 2 * nt(F) * M * f + 2 * M * f, "dg2 partials": 2 * nt(2 * F) * D * f,
+           "T1": 2 * M * f, "dg1 partials": 2 * nt(3 * D) * D * f, "dgq, dgk partials": 4 * 128 * f * (M // 256 + 1)}
+    return {"fwd": fwd, "bwd": bwd, "total_bytes": sum(fwd.values()) + sum(bwd.values())}
 
+
+def block_leg(name, precision, args, breakdown=True):
+    """One block configuration: fused forward + backward step time (HIP events
+    on torch's current stream, which the library launches on), forward time,
+    the dominant kernel's (gate/up GEMM + SwiGLU) average duration, the warm
+    per-weight-update preparation (fold, pack, RoPE table, fp8 copies), the
+    unfused baseline and a per-call breakdown."""
     import numpy as np
     import torch
+    import coda_inputs as ci
     import gemm_epilogue_fp8_amd as coda
     from gemm_epilogue_fp8_amd.block import Block
     from gemm_epilogue_fp8_amd.unfused import UnfusedBlock
 
     dev = "cuda:0"
-    torch.cuda.set_device(0)
+    cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[name]
+    seed = ci.SEEDS[name]
+    fp8 = {"bf16": False, "fp8": True, "mxfp8": "mx"}[precision]
     P = ci.block_inputs(cfg, seed)
     to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
     params = {k: to(v, torch.float32 if k in ("g1", "g2", "gq", "gk") else torch.bfloat16) for k, v in P.items()}
@@ -307,7 +313,7 @@ def main():
     t_prep = time.perf_counter()
     blk = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, theta=cfg.theta, eps=cfg.eps, precision=prec)
     torch.cuda.synchronize()
-    prep_ms = (time.perf_counter() - t_prep) * 1e3
+    prep_cold_ms = (time.perf_counter() - t_prep) * 1e3
     M = cfg.M
     f = blk.alloc_forward(M, dev)
     g = blk.alloc_backward(M, dev)
@@ -371,18 +377,23 @@ def main():
         step()
     ms = timed(lambda: step(record=True), args.steps)
     f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
+    fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
+    # the per-weight-update preparation, warm (no allocation: same buffers)
+    blk.prepare(params)
+    prep_ms = timed(lambda: blk.prepare(params), 5)
 
-    # per-call breakdown (one extra, untimed-for-the-metric step)
-    evs = []
-    torch.cuda.synchronize()
-    for name, fn in calls:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        evs.append((name, a, b))
-    torch.cuda.synchronize()
-    breakdown = {n: round(a.elapsed_time(b), 4) for n, a, b in evs}
+    bd = None
+    if breakdown:   # per-call breakdown (one extra, untimed-for-the-metric step)
+        evs = []
+        torch.cuda.synchronize()
+        for name, fn in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((name, a, b))
+        torch.cuda.synchronize()
+        bd = {n: round(a.elapsed_time(b), 4) for n, a, b in evs}
 
     unfused = None
     if not args.no_unfused and not fp8:
@@ -400,31 +411,100 @@ def main():
         ums = timed(ustep, args.steps)
         ufwd = timed(lambda: ub.forward(x, o, bufs), max(1, args.steps // 2))
         unfused = {"block_fwd_bwd_ms": round(ums, 4), "fwd_ms": round(ufwd, 4),
-                   "speedup_fused_over_unfused": round(ums / ms, 4)}
+                   "speedup_fused_over_unfused": round(ums / ms, 4),
+                   "speedup_with_weight_prep_every_step": round(ums / (ms + prep_ms), 4)}
+        del ub, bufs
 
-    fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
-    fp4_fwd = None
-    if not args.no_mx:
-        # the same block forward (inference) with MXFP4 operands: weights
-        # quantised once, activations per call, outputs into the same buffers
-        blk4 = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, precision=coda.PREC_MXFP4)
-        ms4 = timed(lambda: blk4.forward(x, o, f), max(1, args.steps // 2))
-        fp4_fwd = {"block_fwd_ms": round(ms4, 4), "tflops": round(block_flops(M, cfg.D, cfg.F)[0] / (ms4 * 1e-3) / 1e12, 1),
-                   f"speedup_over_{precision}_fwd": round(fwd_ms / ms4, 4)}
-        del blk4
-    mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
-    ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
-    fwd, bwd = block_flops(M, cfg.D, cfg.F)
-    tflops = (fwd + bwd) / (ms * 1e-3) / 1e12
+    fwd_fl, bwd_fl = block_flops(M, cfg.D, cfg.F)
+    tflops = (fwd_fl + bwd_fl) / (ms * 1e-3) / 1e12
     f3_flop = 2 * M * (2 * cfg.F) * cfg.D
     f3_tflops = f3_flop / (f3_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[precision]
+    out = {
+        "workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}, MLP {cfg.F}, "
+                    f"{cfg.heads}x128 heads, {M} tokens",
+        "block_fwd_bwd_ms": round(ms, 4), "block_fwd_ms": round(fwd_ms, 4),
+        "tflops": round(tflops, 2), "pct_of_peak": round(100 * tflops / peak, 2),
+        "unfused_baseline": unfused,
+        "weight_prep_ms": round(prep_ms, 4), "weight_prep_cold_ms": round(prep_cold_ms, 3),
+        "breakdown_ms": bd,
+        "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU epilogue (M x 2F x D)",
+                     "achieved": round(f3_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4),
+                     "flop_per_launch": f3_flop, "traffic": stored_traffic(name, precision)},
+        "partial_buffers": partial_bytes(M, cfg.D, cfg.F),
+    }
+    del blk, f, g, params, calls
+    torch.cuda.empty_cache()
+    return out, f3_tflops
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
+              f"run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import coda_inputs as ci
+    cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[args.config]
+    seed = ci.SEEDS[args.config]
+    precision = args.precision or ("fp8" if args.config == "cfg5" else "bf16")
+    fp8 = {"bf16": False, "fp8": True, "mxfp8": "mx"}[precision]
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, seed, args.cpu_rows or cfg.M, fp8)
+
+    import torch
+    import gemm_epilogue_fp8_amd as coda
+    from gemm_epilogue_fp8_amd.block import Block
+    import numpy as np
+
+    torch.cuda.set_device(0)
+    head, f3_tflops = block_leg(args.config, precision, args)
+    ms = head["block_fwd_bwd_ms"]
+    # hidden 4096 (the size the metric names beside 2048) in the same run
+    h4096 = None
+    if args.config == "cfg2" and not args.no_h4096:
+        h4096, _ = block_leg("cfg3", precision, args)
+
+    fp4_fwd = None
+    if not args.no_mx and not fp8:
+        # the same block forward (inference) with MXFP4 operands: weights
+        # quantised once, activations per call
+        dev = "cuda:0"
+        P = ci.block_inputs(cfg, seed)
+        to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+        params = {k: to(v, torch.float32 if k in ("g1", "g2", "gq", "gk") else torch.bfloat16) for k, v in P.items()}
+        del P
+        blk4 = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, precision=coda.PREC_MXFP4)
+        fo = blk4.alloc_forward(cfg.M, dev)
+        blk4.forward(params["x"], params["o"], fo)
+        reps = max(1, args.steps // 2)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            blk4.forward(params["x"], params["o"], fo)
+        b.record()
+        torch.cuda.synchronize()
+        ms4 = a.elapsed_time(b) / reps
+        fp4_fwd = {"block_fwd_ms": round(ms4, 4),
+                   "tflops": round(block_flops(cfg.M, cfg.D, cfg.F)[0] / (ms4 * 1e-3) / 1e12, 1),
+                   f"speedup_over_{precision}_fwd": round(head["block_fwd_ms"] / ms4, 4)}
+        del blk4, fo, params
+        torch.cuda.empty_cache()
+    mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
+    ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
     peak = PEAK_TFLOPS[precision]
     mloop = None if args.no_mfma_loop else mfma_loop_leg(f3_tflops)
     if mloop is not None and precision != "bf16":
         mloop["dominant_kernel_frac_of_achievable"] = round(f3_tflops / mloop["fp8_tflops"], 4)
     out = {
         "metric": "fused GEMM+epilogue TFLOP/s & % MFMA peak; block fwd+bwd ms, hidden 2048/4096",
-        "value": round(tflops, 2),
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -435,20 +515,19 @@ def main():
         "vs_baseline": None,
         "dtype": precision,
         "data": "synthetic",
-        "config": {"workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}, "
-                               f"MLP {cfg.F}, {cfg.heads}x128 heads, {M} tokens",
-                   "tokens": M, "hidden": cfg.D, "mlp": cfg.F, "heads": cfg.heads, "head_dim": 128,
+        "config": {"workload": head["workload"],
+                   "tokens": cfg.M, "hidden": cfg.D, "mlp": cfg.F, "heads": cfg.heads, "head_dim": 128,
                    "seq_len": cfg.seq_len, "grad_accumulate_beta": 1.0},
         "block_fwd_bwd_ms": round(ms, 4),
-        "block_fwd_ms": round(fwd_ms, 4),
-        "pct_of_peak": round(100 * tflops / peak, 2),
-        "unfused_baseline": unfused,
-        "weight_prep_ms": round(prep_ms, 3),
-        "breakdown_ms": breakdown,
-        "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU epilogue (M x 2F x D)",
-                     "achieved": round(f3_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4),
-                     "flop_per_launch": f3_flop, "traffic": stored_traffic(args.config, precision)},
+        "block_fwd_ms": head["block_fwd_ms"],
+        "pct_of_peak": head["pct_of_peak"],
+        "unfused_baseline": head["unfused_baseline"],
+        "weight_prep_ms": head["weight_prep_ms"],
+        "weight_prep_cold_ms": head["weight_prep_cold_ms"],
+        "breakdown_ms": head["breakdown_ms"],
+        "roofline": head["roofline"],
+        "partial_buffers": head["partial_buffers"],
+        "hidden_4096": h4096,
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,
         "mxfp4_block_forward": fp4_fwd,
