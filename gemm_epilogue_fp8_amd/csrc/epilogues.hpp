@@ -406,6 +406,14 @@ __device__ __forceinline__ void finish_inv_rms(const EpiArgs& e, const Ctx<Cfg>&
   if (r_out && c.tn == 0 && c.tid < Cfg::BM && c.m0 + c.tid < c.M) r_out[c.m0 + c.tid] = rv[c.tid];
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes
+// have completed; its global stores and global->LDS copies may still be in
+// flight (__syncthreads would wait for those too).
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkmcnt0();
+  phase_barrier();
+}
+
 // ================================================================ programs
 
 // --- Linear chain: [row scale] [col scale] [alpha] [+ tile] -> store [+ sum-of-squares partial]
@@ -444,6 +452,16 @@ struct EpiLinear {
       const int m = c.row(i);
       float rv = 1.0f;
       if constexpr (FLAGS & EL_ROWVEC) rv = e.rowvec[c.rowc(i)];
+      // the block's residual values are all read before any output replaces
+      // them in place: one LDS round trip a block, not one per 4 columns
+      uint2 z[Cfg::TN][4];
+      if constexpr (ADD) {
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            z[j][q] = *reinterpret_cast<const uint2*>(c.stage() + S::off4(c.lrow(i), c.lcol(j, q)));
+      }
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
@@ -454,7 +472,7 @@ struct EpiLinear {
           if constexpr (FLAGS & EL_COLVEC)
             v = v * *reinterpret_cast<const f32x4_t*>(e.colvec + c.colc(j, q));
           v = v * alpha;
-          if constexpr (ADD) v = v + S::get4(c.stage(), c.lrow(i), c.lcol(j, q));
+          if constexpr (ADD) v = v + unpack_bf4(z[j][q]);
           if constexpr (!(FLAGS & EL_F32OUT)) {
             const uint2 pk = pack_bf4(v);
             if constexpr (FLAGS & EL_SUMSQ) {
@@ -689,31 +707,46 @@ struct EpiDSwiGLU {
 
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
     apply_fp8_scales<Cfg>(e, c, acc);
-    float part[Cfg::TM];
+    float part[Cfg::TM], rr[Cfg::TM];
 #pragma unroll
-    for (int i = 0; i < Cfg::TM; ++i) part[i] = 0.0f;
+    for (int i = 0; i < Cfg::TM; ++i) {
+      part[i] = 0.0f;
+      rr[i] = e.rowvec[c.rowc(i)];
+    }
     char* s = c.stage();
     const int grp = c.wm0 / Cfg::WM;
     const int F2 = 2 * c.N;
+    __syncthreads();   // the pipeline stages are free
+    stage_dma_bf<Cfg, HR, PC>(s, e.aux0, e.ld_aux0, c.m0, 2 * c.n0, c.M, F2, c.tid);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      __syncthreads();   // the staging area is free
-      stage_dma_bf<Cfg, HR, PC>(s, e.aux0, e.ld_aux0, c.m0 + h * HR, 2 * c.n0, c.M, F2, c.tid);
+      // this half's saved tile has landed (with the previous half's stores,
+      // which drained while it was in flight)
       wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
       if (grp == h) {
 #pragma unroll
         for (int i = 0; i < Cfg::TM; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
           const int lr = c.lrow(i) - h * HR;
           const int m = c.row(i);
-          const float r = e.rowvec[c.rowc(i)];
+          const float r = rr[i];
 #pragma unroll
-          for (int j = 0; j < Cfg::TN; ++j)
+          for (int j = 0; j < Cfg::TN; ++j) {
+            // every saved value of the 32 x 32 tile first, then its outputs in
+            // place: one LDS round trip a tile, not one per 4 columns
+            uint2 g[4], u[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int pg = packed_gate(c.lcol(j, q));
-              const f32x4_t hg = S::get4(s, lr, pg);
-              const f32x4_t hu = S::get4(s, lr, pg + 32);
+              g[q] = *reinterpret_cast<const uint2*>(s + S::off4(lr, pg));
+              u[q] = *reinterpret_cast<const uint2*>(s + S::off4(lr, pg + 32));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int pg = packed_gate(c.lcol(j, q));
+              const f32x4_t hg = unpack_bf4(g[q]);
+              const f32x4_t hu = unpack_bf4(u[q]);
               const f32x4_t da = frag(acc, i, j, q);
               f32x4_t dg, du;
 #pragma unroll
@@ -731,11 +764,19 @@ struct EpiDSwiGLU {
               S::put4p(s, lr, pg, pdg);
               S::put4p(s, lr, pg + 32, pdu);
             }
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
+      lds_barrier();
       stage_store_bf<Cfg, HR, PC>(s, c.tid,
           MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0 + h * HR, 2 * c.n0, c.M, F2});
+      if (h == 0) {
+        // every wave has read the first half out of LDS: the second half's
+        // copy may land there while those stores are still in flight
+        lds_barrier();
+        stage_dma_bf<Cfg, HR, PC>(s, e.aux0, e.ld_aux0, c.m0 + HR, 2 * c.n0, c.M, F2, c.tid);
+      }
     }
     float* tot = c.rowv();
     row_sum_tile<Cfg>(c, part, tot);
@@ -758,18 +799,25 @@ struct EpiDSigmoid {
     stage_dma_bf<Cfg, Cfg::BM, Cfg::BN>(s, e.aux0, e.ld_aux0, c.m0, c.n0, c.M, c.N, c.tid);
     wait_vmcnt<0>();
     __syncthreads();
-    float part[Cfg::TM];
+    float part[Cfg::TM], rr[Cfg::TM];
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) rr[i] = e.rowvec[c.rowc(i)];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       part[i] = 0.0f;
       const int m = c.row(i);
-      const float r = e.rowvec[c.rowc(i)];
+      const float r = rr[i];
+      uint2 hs[Cfg::TN][4];   // the block's saved values first, then the outputs in place
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hs[j][q] = *reinterpret_cast<const uint2*>(s + S::off4(c.lrow(i), c.lcol(j, q)));
 #pragma unroll
       for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4_t h = S::get4(s, c.lrow(i), c.lcol(j, q));
+          const f32x4_t h = unpack_bf4(hs[j][q]);
           const f32x4_t da = frag(acc, i, j, q);
           f32x4_t d;
 #pragma unroll
