@@ -90,6 +90,8 @@ class Weight:
         if self.fp4:
             cw.q_fwd.dtype = CODA_E2M1X2
         cw.q_bwd, cw.s_bwd = mat(self.q_bwd), mat(self.s_bwd)
+        if self.fp4 and self.q_bwd is not None:
+            cw.q_bwd.dtype = CODA_E2M1X2
         return cw
 
     def prepare_fp8(self):
@@ -117,17 +119,21 @@ class Weight:
         quantize_weight(self)
         return self
 
-    def prepare_mxfp4(self):
-        """Allocate and fill the block-scaled E2M1 forward copy
-        (coda_quantize_weight): q_fwd [N, K/2] bytes (two codes a byte) with
-        exponents along K_in in word layout; MXFP4 is forward-only, so there
-        is no backward copy."""
+    def prepare_mxfp4(self, backward: bool = True):
+        """Allocate and fill the block-scaled E2M1 copies (coda_quantize_weight):
+        q_fwd [N, K/2] bytes (two codes a byte) with exponents along K_in and,
+        unless backward is False (an inference-only weight), q_bwd [K, N/2]
+        bytes with exponents along N_out, both in word layout."""
         K, N = self.w.shape
         dev = self.w.device
         self.fp4 = True
         self.q_fwd = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
         self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
-        self.q_bwd = self.s_bwd = None
+        if backward and N % 128 == 0:
+            self.q_bwd = torch.empty((K, N // 2), dtype=torch.uint8, device=dev)
+            self.s_bwd = torch.empty(((N + 127) // 128, 4 * K), dtype=torch.uint8, device=dev)
+        else:
+            self.q_bwd = self.s_bwd = None
         quantize_weight(self)
         return self
 

@@ -63,7 +63,7 @@ class Block:
         elif self.precision == PREC_MXFP8:
             for w in self.w.values():
                 w.prepare_mxfp8()
-        elif self.precision == PREC_MXFP4:      # forward only: backward() raises CodaError (unsupported)
+        elif self.precision == PREC_MXFP4:
             for w in self.w.values():
                 w.prepare_mxfp4()
 

@@ -121,6 +121,17 @@ coda_status quant_act(const ActQ& a, const void* X, int64_t ldx, int64_t R, int6
 hipError_t launch_fwd(Prog p, int layout, bool fp8, bool fp4, GemmArgs g, const EpiArgs& e, hipStream_t s) {
   return fp4 ? launch_gemm_mx4(p, g, e, s) : launch_gemm(p, layout, fp8, g, e, s);
 }
+// A GEMM at a functional precision: MXFP4 operands go to their own
+// instantiations, whose mainloop counts the contracted axis (K and a split's
+// kchunk) in bytes, two E2M1 values a byte
+hipError_t launch_prec(Prog p, int layout, int prec, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  if (prec == CODA_PREC_MXFP4) {
+    g.K /= 2;
+    g.kchunk /= 2;
+    return launch_gemm_mx4(p, g, e, s);
+  }
+  return launch_gemm(p, layout, prec != CODA_PREC_BF16, g, e, s);
+}
 // MXFP8 / MXFP4: the exponents of both operands go with the GEMM; the epilogue applies
 // no dequantisation scales
 void mx_args(GemmArgs* g, EpiArgs* e, const void* ea, int64_t lda_e, const coda_mat* eb) {
@@ -166,22 +177,28 @@ coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int
     TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E4M3, K, N));
     TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
   } else if (precision == CODA_PREC_MXFP4) {
-    // forward copy only: q_fwd [N, K / 2 bytes] with blocks along K_in
+    // forward copy q_fwd [N, K / 2 bytes] with blocks along K_in; the
+    // input-gradient copy q_bwd [K, N / 2 bytes] with blocks along N_out is
+    // optional (a forward-only weight has none; dgrad refuses such a weight)
     if (K % 128 != 0) return fail(CODA_ERR_SHAPE, "%s: MXFP4 needs K_in to be a multiple of 128", name);
     TRY(check_mat(&wt->q_fwd, "q_fwd", CODA_E2M1X2, N, K / 2));
     TRY(check_scales(&wt->s_fwd, "s_fwd", N, K));
+    if (present(&wt->q_bwd)) {
+      if (N % 128 != 0) return fail(CODA_ERR_SHAPE, "%s: an MXFP4 backward copy needs N_out to be a multiple of 128", name);
+      TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E2M1X2, K, N / 2));
+      TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
+    }
   } else if (precision != CODA_PREC_BF16) {
     return fail(CODA_ERR_VALUE, "precision %d", precision);
   }
   return CODA_OK;
 }
 coda_status check_precision(int p) {
-  if (p == CODA_PREC_MXFP4) return fail(CODA_ERR_UNSUPPORTED, "MXFP4 operands are forward-only in this build");
-  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8) return fail(CODA_ERR_VALUE, "precision %d", p);
+  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8 && p != CODA_PREC_MXFP4)
+    return fail(CODA_ERR_VALUE, "precision %d", p);
   return CODA_OK;
 }
-// the forward entry points also take MXFP4 operands
-coda_status check_precision_fwd(int p) { return p == CODA_PREC_MXFP4 ? CODA_OK : check_precision(p); }
+coda_status check_precision_fwd(int p) { return check_precision(p); }
 bool is_mx(int p) { return p == CODA_PREC_MXFP8 || p == CODA_PREC_MXFP4; }
 
 
@@ -333,8 +350,12 @@ extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, siz
   if (wt->q_fwd.dtype == CODA_E2M1X2) {
     // MXFP4 forward copy: q_fwd [N, K / 2 bytes] with blocks along K_in
     TRY(check_weight(wt, "W", K, N, CODA_PREC_MXFP4));
-    return run_quant_mx4(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
-                         static_cast<uint8_t*>(wt->s_fwd.ptr), wt->s_fwd.ld, S(stream));
+    TRY(run_quant_mx4(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
+                      static_cast<uint8_t*>(wt->s_fwd.ptr), wt->s_fwd.ld, S(stream)));
+    if (!present(&wt->q_bwd)) return CODA_OK;
+    // input-gradient copy: q_bwd [K, N / 2 bytes] with blocks along N_out
+    return run_quant_mx4(wt->w.ptr, wt->w.ld, K, N, 1, static_cast<uint8_t*>(wt->q_bwd.ptr), wt->q_bwd.ld,
+                         static_cast<uint8_t*>(wt->s_bwd.ptr), wt->s_bwd.ld, S(stream));
   }
   if (wt->s_fwd.dtype == CODA_E8M0) {
     // MXFP8 copies: q_fwd [N, K] with blocks along K_in, q_bwd [K, N] with
@@ -1089,6 +1110,8 @@ struct Bwd8 {
 static coda_status dgrad_args(bool fp8, const ActQ* grow, const void* G, int64_t ldG, const coda_weight* W,
                               int64_t M, int64_t Kin, int64_t Nout, GemmArgs* g, EpiArgs* e) {
   if (fp8) {
+    if (!present(&W->q_bwd))
+      return fail(CODA_ERR_NULL, "the weight has no input-gradient copy (q_bwd) for this precision");
     *g = gemm_args(grow->q.q, grow->q.ld, W->q_bwd.ptr, W->q_bwd.ld, M, Kin, Nout);
     e->rowscale = grow->q.s;
     e->colscale = fptr(&W->s_bwd);
@@ -1145,9 +1168,9 @@ static Split wgrad_split(int64_t Kin, int64_t Nout, int64_t M, int64_t align = 6
 // (fp32, e->out / e->ld_out / e->beta) and, optionally, row partials
 // (e->partial_out, `pstride` floats per slice).  With sp.n > 1 the slices go
 // to `part` (sp.n x Kin x Nout floats) and split_sum_kernel finishes D.
-static coda_status launch_wgrad(Prog p, int layout, bool fp8, GemmArgs g, EpiArgs e, const Split& sp, float* part,
+static coda_status launch_wgrad(Prog p, int layout, int prec, GemmArgs g, EpiArgs e, const Split& sp, float* part,
                                 int64_t pstride, hipStream_t s, const char* what) {
-  if (sp.n <= 1) return launched(launch_gemm(p, layout, fp8, g, e, s), what);
+  if (sp.n <= 1) return launched(launch_prec(p, layout, prec, g, e, s), what);
   float* out = static_cast<float*>(e.out);
   const int64_t ld = e.ld_out;
   const float beta = e.beta;
@@ -1158,7 +1181,7 @@ static coda_status launch_wgrad(Prog p, int layout, bool fp8, GemmArgs g, EpiArg
   e.split_stride = slice;
   e.split_pstride = pstride;
   g.kchunk = (int)sp.kchunk;
-  TRY(launched(launch_gemm(p, layout, fp8, g, e, s), what));
+  TRY(launched(launch_prec(p, layout, prec, g, e, s), what));
   const int64_t quads = slice / 4;
   hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, part, sp.n, slice, g.M,
                      g.N, beta, out, ld);
@@ -1180,8 +1203,8 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   // F is the width of the activation's output; the pre-activations are 2F
   // wide for SwiGLU (packed gate/up) and F wide for the sigmoid
   const int64_t N2 = act == Act::SwiGLU ? 2 * F : F;
-  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
-  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   Carver cv(size_only ? nullptr : ws);
   const int nT2 = (int)coda_partials_cols(F);
   const int nTg = (int)coda_partials_cols(N2);
@@ -1194,10 +1217,10 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   Bwd8 q8{};
   ActQ dYrow{};
   if (fp8) {
-    dYrow = take_act(cv, M, D, 1, mx);
-    q8.grow = take_act(cv, M, N2, 1, mx);
-    q8.xcol = take_act(cv, M, D, 0, mx);
-    q8.gcol = take_act(cv, M, N2, 0, mx);
+    dYrow = take_act(cv, M, D, 1, mx, fp4);
+    q8.grow = take_act(cv, M, N2, 1, mx, fp4);
+    q8.xcol = take_act(cv, M, D, 0, mx, fp4);
+    q8.gcol = take_act(cv, M, N2, 0, mx, fp4);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
@@ -1214,7 +1237,7 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     GemmArgs g;
     if (fp8) TRY(quant_act(dYrow, dY->ptr, dY->ld, M, D, 1, s));
     dgrad_args(fp8, &dYrow, dY->ptr, dY->ld, Wd, M, F, D, &g, &e);
-    TRY(launched(launch_gemm(act == Act::SwiGLU ? Prog::DSwiGLU : Prog::DSigmoid, LAYOUT_NT, fp8, g, e, s),
+    TRY(launched(launch_prec(act == Act::SwiGLU ? Prog::DSwiGLU : Prog::DSigmoid, LAYOUT_NT, precision, g, e, s),
                  "swiglu_bwd: activation backward"));
   }
   // collapse the T partials (F / 256 of them) to one per row
@@ -1239,7 +1262,7 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     e.norm_dim = (int)D;
     GemmArgs g;
     dgrad_args(fp8, &q8.grow, dhp, lddh, Wgu, M, D, N2, &g, &e);
-    TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, fp8, g, e, s), "swiglu_bwd: du"));
+    TRY(launched(launch_prec(Prog::NormCorr, LAYOUT_NT, precision, g, e, s), "swiglu_bwd: du"));
   }
   // B4: dW = beta dW + g (u^T dh~), gain partials
   {
@@ -1252,7 +1275,7 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     GemmArgs g;
     int layout;
     wgrad_args(fp8, q8, u->ptr, u->ld, dhp, lddh, M, D, N2, &g, &e, &layout);
-    TRY(launch_wgrad(Prog::WgradGain, layout, fp8, g, e, sp, part, (int64_t)nTg * D, s, "swiglu_bwd: dW"));
+    TRY(launch_wgrad(Prog::WgradGain, layout, precision, g, e, sp, part, (int64_t)nTg * D, s, "swiglu_bwd: dW"));
   }
   return sum_partials_launch(dgp, sp.n * nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }
@@ -1306,11 +1329,11 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   Carver cv(nullptr);
-  const bool mx = precision == CODA_PREC_MXFP8;
+  const bool mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
   if (precision != CODA_PREC_BF16) {
-    take_act(cv, M, N, 1, mx);
-    take_act(cv, M, K, 0, mx);
-    take_act(cv, M, N, 0, mx);
+    take_act(cv, M, N, 1, mx, fp4);
+    take_act(cv, M, K, 0, mx, fp4);
+    take_act(cv, M, N, 0, mx, fp4);
   }
   const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   if (sp.n > 1) cv.take<float>((size_t)sp.n * K * N);
@@ -1330,14 +1353,14 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   TRY(check_weight(W, "W", K, N, precision));
   TRY(check_mat(da, "da", CODA_BF16, M, K, true));
   TRY(check_mat(dW, "dW", CODA_F32, K, N));
-  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
-  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   Carver cv(ws);
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N, 1, mx);
-    q8.xcol = take_act(cv, M, K, 0, mx);
-    q8.gcol = take_act(cv, M, N, 0, mx);
+    q8.grow = take_act(cv, M, N, 1, mx, fp4);
+    q8.xcol = take_act(cv, M, K, 0, mx, fp4);
+    q8.gcol = take_act(cv, M, N, 0, mx, fp4);
   }
   const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * K * N) : nullptr;
@@ -1353,7 +1376,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
     e.out = da->ptr; e.ld_out = da->ld;
     GemmArgs g;
     dgrad_args(fp8, &q8.grow, d_out->ptr, d_out->ld, W, M, K, N, &g, &e);
-    TRY(launched(launch_gemm(Prog::Store, LAYOUT_NT, fp8, g, e, s), "rmsnorm_residual_bwd: da"));
+    TRY(launched(launch_prec(Prog::Store, LAYOUT_NT, precision, g, e, s), "rmsnorm_residual_bwd: da"));
   }
   EpiArgs e = epi0();
   e.out = dW->ptr; e.ld_out = dW->ld;
@@ -1361,7 +1384,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   GemmArgs g;
   int layout;
   wgrad_args(fp8, q8, a->ptr, a->ld, d_out->ptr, d_out->ld, M, K, N, &g, &e, &layout);
-  return launch_wgrad(Prog::StoreF32, layout, fp8, g, e, sp, part, 0, s, "rmsnorm_residual_bwd: dW");
+  return launch_wgrad(Prog::StoreF32, layout, precision, g, e, sp, part, 0, s, "rmsnorm_residual_bwd: dW");
 }
 
 static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const coda_mat* dv, const coda_mat* x,
@@ -1371,8 +1394,8 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
                                const coda_mat* dW, const coda_mat* dg, const coda_mat* dgq, const coda_mat* dgk,
                                float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
                                void* stream, int64_t M, int64_t D, bool size_only, size_t* bytes) {
-  const bool fp8 = precision != CODA_PREC_BF16, mx = precision == CODA_PREC_MXFP8;
-  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MXFP8 backward: the token count must be a multiple of 128");
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   const int64_t N3 = 3 * D;
   const int rows_per_wave = 4;
   const int nblk = (int)((M + 4 * rows_per_wave - 1) / (4 * rows_per_wave));
@@ -1392,9 +1415,9 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N3) : nullptr;
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N3, 1, mx);
-    q8.xcol = take_act(cv, M, D, 0, mx);
-    q8.gcol = take_act(cv, M, N3, 0, mx);
+    q8.grow = take_act(cv, M, N3, 1, mx, fp4);
+    q8.xcol = take_act(cv, M, D, 0, mx, fp4);
+    q8.gcol = take_act(cv, M, N3, 0, mx, fp4);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
@@ -1425,7 +1448,7 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
     e.norm_dim = (int)D;
     GemmArgs g;
     dgrad_args(fp8, &q8.grow, dh, ldh, Wqkv, M, D, N3, &g, &e);
-    TRY(launched(launch_gemm(Prog::NormCorr, LAYOUT_NT, fp8, g, e, s), "qknorm_rope_bwd: dx"));
+    TRY(launched(launch_prec(Prog::NormCorr, LAYOUT_NT, precision, g, e, s), "qknorm_rope_bwd: dx"));
   }
   {
     EpiArgs e = epi0();
@@ -1437,7 +1460,7 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
     GemmArgs g;
     int layout;
     wgrad_args(fp8, q8, x->ptr, x->ld, dh, ldh, M, D, N3, &g, &e, &layout);
-    TRY(launch_wgrad(Prog::WgradGain, layout, fp8, g, e, sp, part, (int64_t)nTg * D, s, "qknorm_rope_bwd: dW"));
+    TRY(launch_wgrad(Prog::WgradGain, layout, precision, g, e, sp, part, (int64_t)nTg * D, s, "qknorm_rope_bwd: dW"));
   }
   return sum_partials_launch(dgp, sp.n * nTg, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }

@@ -83,13 +83,12 @@ typedef enum coda_precision {
                           contracted size (hidden, MLP width, tokens of a
                           backward) a multiple of 128 */
   CODA_PREC_MXFP4 = 3  /* E2M1 operands (two a byte) with one E8M0 scale per 32
-                          values of the contracted axis, fp32 accumulate;
-                          forward entry points only (linear_swiglu,
-                          linear_rmsnorm_residual, linear_qknorm_rope,
-                          linear_sigmoid _fwd), the others return
-                          CODA_ERR_UNSUPPORTED; the weight needs only w, q_fwd
-                          (E2M1X2 [N, K/2]) and s_fwd (word layout); K_in a
-                          multiple of 128 */
+                          values of the contracted axis, fp32 accumulate; the
+                          forward entry points need w, q_fwd (E2M1X2 [N, K/2])
+                          and s_fwd (word layout), the backward ones also
+                          q_bwd (E2M1X2 [K, N/2]) and s_bwd (blocks along
+                          N_out); every contracted size a multiple of 128;
+                          the cross-entropy entry points refuse it */
 } coda_precision;
 
 typedef struct coda_mat {
@@ -151,8 +150,11 @@ coda_status coda_quantize_e4m3_workspace(const coda_mat* X, int32_t axis, size_t
 coda_status coda_quantize_e4m3(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* scale,
                                void* ws, size_t ws_bytes, void* stream);
 
-/* Fills wt->q_fwd/s_fwd (per output channel, Q transposed) and
- * wt->q_bwd/s_bwd (per input channel) from wt->w. */
+/* Fills the quantised copies of wt->w that the precision of q_fwd / s_fwd
+ * selects: E4M3 with fp32 scales (per output channel, Q transposed, and per
+ * input channel), MXFP8 (E8M0 scales: blocks along K_in for q_fwd [N, K],
+ * along N_out for q_bwd [K, N]) or MXFP4 (q_fwd of dtype CODA_E2M1X2: the same
+ * blocks, two codes a byte; q_bwd is optional, NULL for a forward-only weight). */
 coda_status coda_quantize_weight_workspace(const coda_weight* wt, size_t* bytes);
 coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream);
 
@@ -381,8 +383,10 @@ coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const 
  *                    contracted axis, applied by the scaled MFMA; the weight
  *                    carries the two block-scaled copies; every contracted
  *                    size must be a multiple of 128 (CODA_ERR_SHAPE otherwise);
- *   CODA_PREC_MXFP4  E2M1 operands under the same exponents, forward entry
- *                    points only; the weight carries the forward copy only.
+ *   CODA_PREC_MXFP4  E2M1 operands under the same exponents; the weight
+ *                    carries the forward copy and, for the backward entry
+ *                    points, the input-gradient copy (a weight without it is
+ *                    refused with CODA_ERR_NULL there).
  * Activations are quantised per call into the workspace (the *_workspace
  * queries size it for the given precision).  The cross-entropy entry points
  * take CODA_PREC_BF16 only (CODA_ERR_UNSUPPORTED otherwise). */

@@ -225,10 +225,10 @@ def test_sigmoid_fp8():
 
 
 def test_sigmoid_mxfp4_forward():
-    """RMSNorm -> Linear -> sigmoid with MXFP4 operands (forward only): the
-    same bf16 x and folded weight are quantised identically on both sides,
-    so only the accumulation differs; held to the MXFP8 rule.  The backward
-    refuses MXFP4."""
+    """RMSNorm -> Linear -> sigmoid with MXFP4 operands: the same bf16 x and
+    folded weight are quantised identically on both sides, so only the
+    accumulation differs; held to the MXFP8 rule.  The backward refuses a
+    consumer weight that carries no E2M1 copies."""
     from tests.helpers import FP8_TOL
     rng = np.random.default_rng(14)
     M, D, N = 300, 256, 352
@@ -686,6 +686,31 @@ def test_block_backward_split_k(shape, seed):
     assert_bf16("dx", b["dx"], B["dx"])
 
 
+@pytest.mark.parametrize("precision,fmt", [(2, "mx"), (3, "mx4")])
+def test_mx_residual_backward_split_k_same_inputs(precision, fmt):
+    """Block-scaled backward of a residual linear from identical seeded
+    inputs (MXFP8 and MXFP4): da = d_out W^T through the weight's
+    input-gradient copy, and dW = a^T d_out with both operands quantised
+    along the 4096 tokens, which the library cuts into 4 slices of 1024
+    (split K over whole exponent words) and adds in order onto a seeded fp32
+    prior.  Every quantiser sees the same bits on both sides, so each element
+    meets the fp8 rule."""
+    from tests.helpers import FP8_TOL
+    rng = np.random.default_rng(43 + precision)
+    M, K, N = 4096, 256, 384
+    dout, a = rand_bf16(rng, M, N, std=0.1), rand_bf16(rng, M, K)
+    W = rand_bf16(rng, K, N, std=K ** -0.5)
+    prior = ci.fp32_prior((K, N), 13)
+    wt = coda.Weight(bf(W))
+    wt.prepare_mxfp8() if precision == coda.PREC_MXFP8 else wt.prepare_mxfp4()
+    dW = f32(prior)
+    da = torch.empty((M, K), dtype=BF, device=DEV)
+    coda.linear_rmsnorm_residual_bwd(bf(dout), bf(a), wt, dW, da=da, beta=1.0, precision=precision)
+    torch.cuda.synchronize()
+    assert_bf16("dW", to_np(dW), prior + ob.mm(a.T.copy(), dout, fmt), tol=FP8_TOL, norm_rel=1e-3)
+    assert_bf16("da", to_np(da), nm.bf16(ob.mm(dout, W.T.copy(), fmt)), tol=FP8_TOL, norm_rel=3e-3)
+
+
 @pytest.mark.parametrize("precision", [0, 1])
 def test_residual_backward_split_k_ragged(precision):
     """4100 tokens (slices of 1088, 1088, 1088 and 836) with beta = 1 over a
@@ -802,8 +827,7 @@ def test_block_mxfp4_forward():
     that every quantiser on both sides sees the same bits.  A chained E2M1
     code can move by a whole step when a one-ulp bf16 difference upstream
     crosses a rounding midpoint; the test prints how many rows of h1 and a
-    quantise differently on the two sides.  The backward is not built for
-    MXFP4 and refuses with CODA_ERR_UNSUPPORTED."""
+    quantise differently on the two sides."""
     from tests.helpers import FP8_TOL
     from oracle import mx_small, ops
     shape = ci.BlockShape(M=300, D=256, F=384, seq_len=128)
@@ -835,6 +859,33 @@ def test_block_mxfp4_forward():
     assert_bf16("a (same h1)", f["a"], a_ref, tol=FP8_TOL, norm_rel=2e-2)
     y_ref = nm.bf16(h1 + ob.mm(f["a"].astype(np.float32), c["Wd"], "mx4"))
     assert_bf16("y (same a)", f["y"], y_ref, tol=FP8_TOL, norm_rel=2e-2)
-    fwd = blk.forward(params["x"], params["o"])
-    with pytest.raises(coda.CodaError):
-        blk.backward(params["x"], params["o"], fwd, params["dY"], params["dq"], params["dk"], params["dv"])
+
+
+def test_block_mxfp4_forward_backward():
+    """The whole block, forward and backward, with every GEMM operand in
+    MXFP4 (E2M1 elements, one E8M0 exponent per 32 values of the contracted
+    axis; the weight carries an input-gradient copy blocked along N_out, the
+    weight-gradient operands are quantised along the tokens), against the
+    oracle's chained evaluation in the same format: bf16 outputs within the
+    fp8 rule, gradients within 2e-2 norm-wise (as for MXFP8), and every
+    weight-gradient stage from the device's own bf16 operands within the
+    fp8 rule element by element."""
+    from tests.helpers import FP8_TOL
+    shape = ci.BlockShape(M=256, D=256, F=384, seq_len=128)
+    P, f, b = _run_block(shape, 9, precision=coda.PREC_MXFP4)
+    F = ob.block_forward_contract(P, shape, fp8="mx4")
+    B = ob.block_backward_contract(P, F, shape, fp8="mx4")
+    check_block_mx(f, b, F, B)
+    c = {k: np.asarray(v, np.float32) for k, v in P.items()}
+    g32 = lambda a: np.ascontiguousarray(np.asarray(a, np.float32))
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    dht_gu = np.concatenate([dg_, du_], axis=1)
+    Fw = c["Wg"].shape[1]
+    acc = ob.mm(g32(f["h1"].T), g32(dht_gu), "mx4")
+    dWg, dWu = unpack_gu(b["dWgu"])
+    stage = dict(dWg=(dWg, c["g2"][:, None] * acc[:, :Fw]), dWu=(dWu, c["g2"][:, None] * acc[:, Fw:]),
+                 dWd=(b["dWd"], ob.mm(g32(f["a"].T), c["dY"], "mx4")),
+                 dWo=(b["dWo"], ob.mm(g32(c["o"].T), g32(b["dh1"]), "mx4")),
+                 dWqkv=(b["dWqkv"], c["g1"][:, None] * ob.mm(g32(c["x"].T), g32(b["dht_qkv"]), "mx4")))
+    for k, (got, ref) in stage.items():
+        assert_bf16(k + " (stage)", got, ref, tol=FP8_TOL, norm_rel=2e-3)
