@@ -30,7 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "fp4": 10100.0}   # MI355X dense MFMA, published
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "fp6": 10100.0, "fp4": 10100.0}   # MI355X dense MFMA, published
 HBM_GBPS = 8000.0
 
 
@@ -110,7 +110,7 @@ def mx_leg(warmup, steps):
     hidden-8192 down-projection shape (M 4096, K 28672, N 8192), against the
     per-token x per-channel amax-scaled E4M3 path of the same layer (which
     includes the quantisation of the activation a), and the same layer with
-    MXFP4 (E2M1) operands.  Synthetic inputs drawn on
+    MXFP4 (E2M1) and MXFP6 (E2M3) operands.  Synthetic inputs drawn on
     the device from a seeded generator."""
     import torch
     import gemm_epilogue_fp8_amd as coda
@@ -149,7 +149,13 @@ def mx_leg(warmup, steps):
     fp4_ms = ev_ms(lambda: coda.gemm_mx4(prog, Q4a, S4a, Q4w, S4w, out, aux=[z]))
     quant4_ms = ev_ms(lambda: coda.quantize_mxfp4(a, 1, Q4a, S4a))
     tf4 = flop / (fp4_ms * 1e-3) / 1e12
-    del a, W, z, out, Q4w, S4w, Q4a, S4a
+    del Q4w, S4w, Q4a, S4a
+    # and with MXFP6 (E2M3) operands
+    Q6w, S6w = coda.quantize_mxfp6(W, 0, "e2m3")
+    Q6a, S6a = coda.quantize_mxfp6(a, 1, "e2m3")
+    fp6_ms = ev_ms(lambda: coda.gemm_mx6(prog, "e2m3", Q6a, S6a, Q6w, S6w, out, aux=[z]))
+    tf6 = flop / (fp6_ms * 1e-3) / 1e12
+    del a, W, z, out, Q6w, S6w, Q6a, S6a
     torch.cuda.empty_cache()
     return {"workload": f"out = z + a W, M {M}, K {K}, N {N}, MXFP8 operands (E4M3, E8M0 per 32 K)",
             "gemm_ms": round(gemm_ms, 4), "tflops": round(tf, 1), "frac_of_fp8_peak": round(tf / PEAK_TFLOPS["fp8"], 4),
@@ -157,7 +163,9 @@ def mx_leg(warmup, steps):
             "gemm_plus_quantize_ms": round(gemm_ms + quant_ms, 4),
             "per_row_col_fp8_layer_ms": round(rowcol_ms, 4),
             "mxfp4_gemm_ms": round(fp4_ms, 4), "mxfp4_tflops": round(tf4, 1),
-            "mxfp4_frac_of_fp4_peak": round(tf4 / PEAK_TFLOPS["fp4"], 4), "mxfp4_quantize_a_ms": round(quant4_ms, 4)}
+            "mxfp4_frac_of_fp4_peak": round(tf4 / PEAK_TFLOPS["fp4"], 4), "mxfp4_quantize_a_ms": round(quant4_ms, 4),
+            "mxfp6_e2m3_gemm_ms": round(fp6_ms, 4), "mxfp6_e2m3_tflops": round(tf6, 1),
+            "mxfp6_e2m3_frac_of_fp6_peak": round(tf6 / PEAK_TFLOPS["fp6"], 4)}
 
 
 OPERANDS = {False: "", True: " with E4M3 operands (per-row / per-column amax scales)",

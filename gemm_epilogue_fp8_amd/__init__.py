@@ -16,7 +16,7 @@ from typing import Iterable, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
+from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E2M3, CODA_E3M2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
                    PREC_MXFP4,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS, EPI_STORE_ROW_VEC,
@@ -277,6 +277,27 @@ def quantize_mxfp4(X, axis: int, Q=None, S=None):
     return Q, S
 
 
+_FP6 = {"e2m3": CODA_E2M3, "e3m2": CODA_E3M2}
+
+
+def quantize_mxfp6(X, axis: int, fmt: str, Q=None, S=None):
+    """MXFP6 copy of X [R, C] (bf16) in format fmt ("e2m3" or "e3m2"): axis
+    1 -> Q [R, C] bytes with the exponents of R rows; axis 0 -> Q [C, R]
+    (transposed) with those of C rows.  Each 32-value block of Q is 24 bytes
+    of packed six-bit codes and 8 zero bytes; S holds E8M0 codes in word
+    layout, [ceil(L/128), 4 rows] (see coda.h)."""
+    R, Cc = X.shape
+    rows, L = (R, Cc) if axis == 1 else (Cc, R)
+    if Q is None:
+        Q = torch.empty((rows, L), dtype=torch.uint8, device=X.device)
+    if S is None:
+        S = torch.empty(((L + 127) // 128, 4 * rows), dtype=torch.uint8, device=X.device)
+    q = mat(Q)
+    q.dtype = _FP6[fmt]
+    _check(lib().coda_quantize_mxfp6(_p(X), axis, C.byref(q), _p(S), _stream()))
+    return Q, S
+
+
 def gemm_mx(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     """D = epilogue(A~ B~^T) with MXFP8 operands A [M, K], B [N, K] and their
     E8M0 block exponents SA [K/128, 4M], SB [K/128, 4N] in word layout;
@@ -301,6 +322,21 @@ def gemm_mx4(program: Sequence[tuple], A, SA, B, SB, D, aux: Iterable = ()):
     a.dtype = b.dtype = CODA_E2M1X2
     ws, n = _ws_call(lib().coda_gemm_epi_workspace, (C.byref(prog), A.shape[0], B.shape[0], 2 * A.shape[1]),
                      A.device)
+    _check(lib().coda_gemm_mx(C.byref(prog), C.byref(a), _p(SA), C.byref(b), _p(SB), _p(D),
+                              arr if aux else None, len(aux), ws, n, _stream()))
+    return D
+
+
+def gemm_mx6(program: Sequence[tuple], fmt: str, A, SA, B, SB, D, aux: Iterable = ()):
+    """D = epilogue(A~ B~^T) with MXFP6 operands of format fmt ("e2m3" or
+    "e3m2"), A [M, K], B [N, K] (uint8, from quantize_mxfp6) and their E8M0
+    exponents SA [K/128, 4M], SB [K/128, 4N] in word layout."""
+    prog = _program(program)
+    aux = list(aux)
+    arr = (_lib.CodaMat * max(len(aux), 1))(*[mat(a) for a in aux])
+    a, b = mat(A), mat(B)
+    a.dtype = b.dtype = _FP6[fmt]
+    ws, n = _ws_call(lib().coda_gemm_epi_workspace, (C.byref(prog), A.shape[0], B.shape[0], A.shape[1]), A.device)
     _check(lib().coda_gemm_mx(C.byref(prog), C.byref(a), _p(SA), C.byref(b), _p(SB), _p(D),
                               arr if aux else None, len(aux), ws, n, _stream()))
     return D

@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcoda.so")
 
 CODA_BF16, CODA_F32, CODA_E4M3, CODA_I32, CODA_E8M0, CODA_E2M1X2 = 1, 2, 3, 4, 5, 6
+CODA_E2M3, CODA_E3M2 = 7, 8
 PREC_BF16, PREC_FP8, PREC_MXFP8, PREC_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_DTYPE", 3: "CODA_ERR_SHAPE",
           4: "CODA_ERR_LAYOUT", 5: "CODA_ERR_ALIGN", 6: "CODA_ERR_WORKSPACE",
@@ -68,6 +69,7 @@ SIGNATURES = {
     "coda_gemm_epi": [C.POINTER(EpiProgram), M_, i32, M_, i32, M_, M_, C.c_uint32, vp, sz, vp],
     "coda_quantize_mxfp8": [M_, i32, M_, M_, vp],
     "coda_quantize_mxfp4": [M_, i32, M_, M_, vp],
+    "coda_quantize_mxfp6": [M_, i32, M_, M_, vp],
     "coda_gemm_mx": [C.POINTER(EpiProgram), M_, M_, M_, M_, M_, M_, C.c_uint32, vp, sz, vp],
     "coda_linear_swiglu_fwd_workspace": [i64, i64, i32, i32, szp],
     "coda_linear_swiglu_fwd": [M_, M_, W_, f32, M_, M_, M_, i32, vp, sz, vp],

@@ -601,4 +601,128 @@ __global__ void quant_mx4_cols_t_kernel(const uint16_t* X, int64_t ld, int R, in
   if ((part & 1) == 0) S[(int64_t)(b >> 2) * lds + 4 * c + (b & 3)] = (uint8_t)(e + 127);
 }
 
+// ---------------------------------------------------------------- MXFP6 (block-scaled E2M3 / E3M2)
+// OCP MX v1.0 FP6 elements under one E8M0 exponent per 32 values: E2M3 (bias
+// 1, largest 7.5 = 1.875 * 2^2) and E3M2 (bias 3, largest 28 = 1.75 * 2^4),
+// e = floor(log2(max |v|)) - emax with emax = 2 or 4, clamped to
+// [-127, 127], -127 for a zero or subnormal maximum.  A block's 32 codes are
+// packed into 24 bytes, code v at bits [6 v, 6 v + 6) of one little-endian
+// 192-bit number, followed by 8 zero bytes: a row of L values is L bytes and
+// every block starts on a 32-byte boundary.
+template <int EB, int MB>
+struct Fp6Fmt {
+  static constexpr int BIAS = (1 << (EB - 1)) - 1;
+  static constexpr int EMAX = (1 << EB) - 1 - BIAS;
+};
+
+template <int EB, int MB>
+__device__ __forceinline__ int mx6_exponent(float amax) {
+  const int be = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  return be == 0 ? -127 : min(max(be - 127 - Fp6Fmt<EB, MB>::EMAX, -127), 127);
+}
+
+// FP6 code of v (already divided by the block scale): nearest value, ties to
+// the even mantissa, saturated at the largest.  With k = floor(log2 |v|),
+// raised to the exponent of the smallest normal so that subnormals share the
+// lowest binade's step 2^(k - MB), r = |v| / 2^(k - MB) rounded half to even
+// is the significand in units of that step; the code's magnitude is then
+// (k + BIAS - 1) 2^MB + r, which carries into the next binade when r reaches
+// 2^(MB + 1) and is the plain subnormal code when k is the lowest exponent.
+template <int EB, int MB>
+__device__ __forceinline__ uint32_t fp6_code(float v) {
+  constexpr int B = Fp6Fmt<EB, MB>::BIAS;
+  const float a = fabsf(v);
+  const int k = max((int)((__float_as_uint(a) >> 23) & 0xFF) - 127, 1 - B);
+  const int r = (int)rintf(ldexpf(a, MB - k));
+  const uint32_t c = (uint32_t)min(((k + B - 1) << MB) + r, 31);
+  return c | ((v < 0.0f && c != 0u) ? 32u : 0u);
+}
+
+// 8 values scaled by 2^-e (exact) -> 48 bits, value k at bits [6 k, 6 k + 6)
+template <int EB, int MB>
+__device__ __forceinline__ uint64_t pack8_fp6(const float* v, int e) {
+  uint64_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= (uint64_t)fp6_code<EB, MB>(ldexpf(v[k], -e)) << (6 * k);
+  return w;
+}
+
+// two 48-bit groups (lo first) -> the three words of their 96 bits
+__device__ __forceinline__ void store96(uint8_t* dst, uint64_t lo, uint64_t hi) {
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  d[0] = (uint32_t)lo;
+  d[1] = (uint32_t)(lo >> 32) | (uint32_t)(hi << 16);
+  d[2] = (uint32_t)(hi >> 16);
+}
+
+// Blocks along the columns: X [R, C] -> Q [R, C] bytes.  One wave a row, 8
+// values a lane, a block = 4 consecutive lanes; lane q of a block packs
+// values 8 q .. 8 q + 7 into 48 bits, and the even lane of each pair stores
+// the pair's 96 bits (bytes 12 (q / 2) .. of the block).
+template <int EB, int MB>
+__device__ __forceinline__ void quant_mx6_rows(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                               uint8_t* S, int64_t lds) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (r >= R) return;                      // r is uniform over the wave
+  for (int c = lane * 8; c < C; c += 512) {
+    // C % 32 == 0: the 4 lanes of a block run the same iterations
+    const uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    float m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, 0.0f))));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const int e = mx6_exponent<EB, MB>(m);
+    const float v[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+    const uint64_t p = pack8_fp6<EB, MB>(v, e);
+    const uint32_t nlo = __shfl_xor((uint32_t)p, 1, 64), nhi = __shfl_xor((uint32_t)(p >> 32), 1, 64);
+    const int q = lane & 3;
+    uint8_t* blk = Q + (int64_t)r * ldq + (c - 8 * q);
+    if ((q & 1) == 0) store96(blk + 12 * (q >> 1), p, ((uint64_t)nhi << 32) | nlo);
+    if (q == 3) *reinterpret_cast<uint2*>(blk + 24) = uint2{0u, 0u};
+    const int b = c / 32;
+    if (q == 0) S[(int64_t)(b >> 2) * lds + 4 * r + (b & 3)] = (uint8_t)(e + 127);
+  }
+}
+
+// Blocks along the rows, written transposed: X [R, C] -> Q^T [C, R] bytes.
+// As quant_mx_cols_t_kernel: a 64 x 64 tile through LDS, thread (column cc,
+// part) encodes rows [16 part, 16 part + 16) of its column into 96 bits, a
+// block is one lane pair, and the odd part also writes the block's padding.
+template <int EB, int MB>
+__device__ __forceinline__ void quant_mx6_cols_t(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT,
+                                                 int64_t ldq, uint8_t* S, int64_t lds, float (*tile)[65]) {
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  load_tile_t(X, ld, R, C, r0, c0, tile);
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    v[k] = tile[part * 16 + k][cc];
+    m = fmaxf(m, fabsf(v[k]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));      // every lane is still active here
+  const int e = mx6_exponent<EB, MB>(m);
+  const int c = c0 + cc, rbase = r0 + part * 16;
+  if (c >= C || rbase >= R) return;        // R % 32 == 0: rows rbase .. rbase + 15 all exist
+  uint8_t* blk = QT + (int64_t)c * ldq + (rbase - 16 * (part & 1));
+  store96(blk + 12 * (part & 1), pack8_fp6<EB, MB>(v, e), pack8_fp6<EB, MB>(v + 8, e));
+  if (part & 1) *reinterpret_cast<uint2*>(blk + 24) = uint2{0u, 0u};
+  const int b = rbase / 32;
+  if ((part & 1) == 0) S[(int64_t)(b >> 2) * lds + 4 * c + (b & 3)] = (uint8_t)(e + 127);
+}
+
+__global__ void quant_mx6_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                      uint8_t* S, int64_t lds, int f6) {
+  if (f6 == 2) quant_mx6_rows<2, 3>(X, ld, R, C, Q, ldq, S, lds);
+  else quant_mx6_rows<3, 2>(X, ld, R, C, Q, ldq, S, lds);
+}
+
+__global__ void quant_mx6_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                        uint8_t* S, int64_t lds, int f6) {
+  __shared__ float tile[64][65];
+  if (f6 == 2) quant_mx6_cols_t<2, 3>(X, ld, R, C, QT, ldq, S, lds, tile);
+  else quant_mx6_cols_t<3, 2>(X, ld, R, C, QT, ldq, S, lds, tile);
+}
+
 }  // namespace coda

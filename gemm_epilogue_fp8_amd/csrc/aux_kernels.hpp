@@ -89,5 +89,12 @@ __global__ void quant_mx4_rows_kernel(const uint16_t* X, int64_t ld, int R, int 
                                       uint8_t* S, int64_t lds);
 __global__ void quant_mx4_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
                                         uint8_t* S, int64_t lds);
+// MXFP6 (f6 = 2: E2M3, f6 = 3: E3M2), a 32-value block packed into 24 bytes
+// then 8 zero bytes, so Q rows hold as many bytes as values; same shapes and
+// launches as the MXFP8 quantisers.
+__global__ void quant_mx6_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                      uint8_t* S, int64_t lds, int f6);
+__global__ void quant_mx6_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* QT, int64_t ldq,
+                                        uint8_t* S, int64_t lds, int f6);
 
 }  // namespace coda

@@ -739,7 +739,9 @@ size_t epi_ws_bytes(int64_t M) {
 }
 
 // Checks D, carves the workspace, merges wide partials and launches.
-coda_status run_decoded(Decoded& d, int64_t M, const coda_mat* D, GemmArgs g, int layout, bool fp8, bool fp4,
+// elem: the MX element format of the operands as the scaled MFMA codes it
+// (2 = E2M3, 3 = E3M2, 4 = E2M1), 0 for bf16 / E4M3 ones.
+coda_status run_decoded(Decoded& d, int64_t M, const coda_mat* D, GemmArgs g, int layout, bool fp8, int elem,
                         void* ws, size_t ws_bytes, hipStream_t s, const char* who) {
   if (d.out_dtype != 0) {
     TRY(check_mat(D, "D", d.out_dtype, M, d.out_cols));
@@ -762,7 +764,9 @@ coda_status run_decoded(Decoded& d, int64_t M, const coda_mat* D, GemmArgs g, in
     *d.merge_dst = P;
     d.e.n_row_partials = nP;
   }
-  hipError_t err = fp4 ? launch_gemm_mx4(d.p, g, d.e, s) : launch_gemm(d.p, layout, fp8, g, d.e, s);
+  hipError_t err = elem == 4   ? launch_gemm_mx4(d.p, g, d.e, s)
+                   : elem != 0 ? launch_gemm_mx6(d.p, elem, g, d.e, s)
+                               : launch_gemm(d.p, layout, fp8, g, d.e, s);
   if (err == hipErrorInvalidValue)
     return fail(CODA_ERR_UNSUPPORTED, "%s: this epilogue chain is not compiled for these operands", who);
   return launched(err, who);
@@ -800,7 +804,7 @@ extern "C" coda_status coda_gemm_epi(const coda_epi_program* prog, const coda_ma
   Decoded d;
   TRY(decode_program(prog, M, N, K, aux, n_aux, "gemm_epi", false, &d));
   GemmArgs g = gemm_args(A->ptr, A->ld, B->ptr, B->ld, M, N, K);
-  return run_decoded(d, M, D, g, layout, e4m3, false, ws, ws_bytes, S(stream), "gemm_epi");
+  return run_decoded(d, M, D, g, layout, e4m3, 0, ws, ws_bytes, S(stream), "gemm_epi");
 }
 
 // ======================================================================== MXFP8
@@ -852,13 +856,44 @@ extern "C" coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, cons
   return check_launch("quantize_mxfp4");
 }
 
+extern "C" coda_status coda_quantize_mxfp6(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* Sc,
+                                           void* stream) {
+  TRY(check_mat(X, "X", CODA_BF16, -1, -1));
+  if (axis != 0 && axis != 1) return fail(CODA_ERR_VALUE, "axis must be 0 or 1");
+  if (!Q) return fail(CODA_ERR_NULL, "Q: NULL");
+  if (Q->dtype != CODA_E2M3 && Q->dtype != CODA_E3M2)
+    return fail(CODA_ERR_DTYPE, "quantize_mxfp6: Q must be CODA_E2M3 or CODA_E3M2 (got %d)", (int)Q->dtype);
+  const int f6 = Q->dtype == CODA_E2M3 ? 2 : 3;
+  const int64_t R = X->rows, C = X->cols;
+  const int64_t L = axis == 1 ? C : R;     // length of the blocked (contracted) axis
+  if (L % 32 != 0) return fail(CODA_ERR_SHAPE, "quantize_mxfp6: the blocked axis (%lld) must be a multiple of 32",
+                               (long long)L);
+  const int64_t rows = axis == 1 ? R : C;
+  TRY(check_mat(Q, "Q", Q->dtype, rows, L));
+  TRY(check_scales(Sc, "S", rows, L));
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X->ptr);
+  uint8_t* q = static_cast<uint8_t*>(Q->ptr);
+  uint8_t* sc = static_cast<uint8_t*>(Sc->ptr);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx6_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, S(stream), x, X->ld,
+                       (int)R, (int)C, q, Q->ld, sc, Sc->ld, f6);
+  else
+    hipLaunchKernelGGL(quant_mx6_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),
+                       dim3(256), 0, S(stream), x, X->ld, (int)R, (int)C, q, Q->ld, sc, Sc->ld, f6);
+  return check_launch("quantize_mxfp6");
+}
+
 extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                                     const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
                                     uint32_t n_aux, void* ws, size_t ws_bytes, void* stream) {
   if (!prog) return fail(CODA_ERR_NULL, "gemm_mx: NULL program");
-  // E2M1 operands (two values a byte) when A says so; B must match
-  const bool fp4 = present(A) && A->dtype == CODA_E2M1X2;
-  const int odt = fp4 ? CODA_E2M1X2 : CODA_E4M3;
+  // E2M1 operands (two values a byte) or FP6 ones (E2M3 / E3M2, a byte a
+  // value with the block padding) when A says so; B must match
+  const int odt = present(A) && (A->dtype == CODA_E2M1X2 || A->dtype == CODA_E2M3 || A->dtype == CODA_E3M2)
+                      ? A->dtype : CODA_E4M3;
+  const bool fp4 = odt == CODA_E2M1X2;
+  const int elem = odt == CODA_E2M1X2 ? 4 : odt == CODA_E2M3 ? 2 : odt == CODA_E3M2 ? 3 : 0;
   TRY(check_mat(A, "A", odt, -1, -1));
   TRY(check_mat(B, "B", odt, -1, -1));
   const int64_t M = A->rows, Kb = A->cols, N = B->rows;
@@ -876,7 +911,7 @@ extern "C" coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat
   g.sB = SB->ptr;
   g.lds_a = SA->rows > 1 ? SA->ld : SA->cols;
   g.lds_b = SB->rows > 1 ? SB->ld : SB->cols;
-  return run_decoded(d, M, D, g, LAYOUT_NT, true, fp4, ws, ws_bytes, S(stream), "gemm_mx");
+  return run_decoded(d, M, D, g, LAYOUT_NT, true, elem, ws, ws_bytes, S(stream), "gemm_mx");
 }
 
 // ======================================================================== functional forward

@@ -34,7 +34,11 @@ coda_status fail(coda_status st, const char* fmt, ...) {
     if (_s != CODA_OK) return _s;          \
   } while (0)
 
-int esize(int dt) { return dt == CODA_BF16 ? 2 : (dt == CODA_E4M3 || dt == CODA_E8M0 || dt == CODA_E2M1X2) ? 1 : 4; }
+int esize(int dt) {
+  return dt == CODA_BF16 ? 2
+         : (dt == CODA_E4M3 || dt == CODA_E8M0 || dt == CODA_E2M1X2 || dt == CODA_E2M3 || dt == CODA_E3M2) ? 1
+                                                                                                            : 4;
+}
 int vec_elems(int dt) { return 16 / esize(dt); }
 
 bool present(const coda_mat* m) { return m != nullptr && m->ptr != nullptr; }

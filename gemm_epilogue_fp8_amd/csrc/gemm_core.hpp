@@ -97,7 +97,7 @@ __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
 }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool A_KC_, bool B_KC_, bool FP8_ = false,
-          bool MX_ = false, bool FP4_ = false>
+          bool MX_ = false, bool FP4_ = false, int F6_ = 0>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NWAVES = WAVES_M * WAVES_N, T = 64 * NWAVES;
@@ -107,6 +107,11 @@ struct GemmCfg {
   // FP4: the byte operands hold two E2M1 values each; K, the tiles and the
   // copies count bytes, and only the MFMA sees values
   static constexpr bool FP4 = FP4_;
+  // FP6 (F6 = the MFMA format code: 2 = E2M3, 3 = E3M2; 0 = none): a 32-value
+  // block is 24 bytes of packed codes and 8 bytes of padding, so K, the tiles
+  // and the copies count bytes exactly as for E4M3
+  static constexpr int F6 = F6_;
+  static constexpr bool FP6 = F6 != 0;
   static constexpr int WPP = FP4 ? 2 : 1;          // MX: exponent word rows a stage pair
   static constexpr int ESIZE = FP8 ? 1 : 2;
   static constexpr int BK = kRowBytes / ESIZE;     // K per stage: 32 bf16 or 64 fp8
@@ -121,6 +126,7 @@ struct GemmCfg {
   static_assert(!FP8 || (A_KC && B_KC), "fp8 operands are K-contiguous");
   static_assert(!MX || FP8, "block scales come with E4M3 operands");
   static_assert(!FP4 || MX, "E2M1 operands are block-scaled");
+  static_assert(!FP6 || (MX && !FP4 && (F6 == 2 || F6 == 3)), "FP6 operands are block-scaled E2M3 or E3M2");
 };
 
 struct GemmArgs {
@@ -291,6 +297,16 @@ __device__ __forceinline__ typename Frags<Cfg>::T read_frag(const char* tile, in
     const int row = r0 + (lane & 31);
     i32x4_t v = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 * s + (lane >> 5)));
     return i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+  } else if constexpr (Cfg::FP6) {
+    // lanes 0-31 hold K block 0 of their row, lanes 32-63 block 1: the 24
+    // packed bytes (value v at bits [6 v, 6 v + 6)) at the start of the
+    // block's 32, in the low 6 registers, which are all the matrix core reads
+    const int row = r0 + (lane & 31);
+    const int h = lane >> 5;
+    (void)s;
+    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 * h));
+    i32x2_t up = *reinterpret_cast<const i32x2_t*>(tile + lds_off(row, 2 * h + 1));
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], 0, 0};
   } else if constexpr (Cfg::FP8) {
     // K bytes [16 h, 16 h + 16) and [32 + 16 h, 32 + 16 h + 16) of the row,
     // h = lane >> 5: the matrix core reads a lane's first 16 bytes as part of
@@ -366,7 +382,8 @@ __device__ __forceinline__ void load_scales(const char* slot, Scales<Cfg>& sc, i
 // B's scale goes with the instruction's first operand.
 template <class Cfg, int S, int I, int J>
 __device__ __forceinline__ void mma_mx_one(const Frags<Cfg>& f, const Scales<Cfg>& sc, Acc<Cfg>& acc) {
-  constexpr int FMT = Cfg::FP4 ? 4 : 0;   // operand formats: 0 = E4M3, 4 = E2M1
+  // operand formats: 0 = E4M3, 2 = E2M3, 3 = E3M2, 4 = E2M1
+  constexpr int FMT = Cfg::FP4 ? 4 : Cfg::F6;
   acc.c[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[J], f.a[I], acc.c[I][J], FMT, FMT,
                                                                 2 * S + (J & 1), sc.b[J >> 1],
                                                                 2 * S + (I & 1), sc.a[I >> 1]);

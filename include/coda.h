@@ -69,9 +69,17 @@ typedef enum coda_status {
  * CODA_E2M1X2: two FP4 E2M1 codes a byte (the MX specification's FP4
  * element: sign, 2 exponent bits with bias 1, 1 mantissa bit; values 0, 0.5,
  * 1, 1.5, 2, 3, 4, 6), element 2i in the low nibble of byte i; a matrix of
- * them counts cols and ld in bytes. */
+ * them counts cols and ld in bytes.
+ * CODA_E2M3 / CODA_E3M2: the MX specification's FP6 elements (sign, 2
+ * exponent bits with bias 1 and 3 mantissa bits, largest 7.5; or 3 exponent
+ * bits with bias 3 and 2 mantissa bits, largest 28).  Each block of 32
+ * consecutive values of a row is 32 bytes: the 32 six-bit codes packed into
+ * the first 24 (code v at bits [6 v, 6 v + 6) of the block read as one
+ * little-endian 192-bit number), then 8 zero bytes; a matrix of them counts
+ * cols and ld in bytes, which equal values. */
 typedef enum coda_dtype {
-  CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4, CODA_E8M0 = 5, CODA_E2M1X2 = 6
+  CODA_BF16 = 1, CODA_F32 = 2, CODA_E4M3 = 3, CODA_I32 = 4, CODA_E8M0 = 5, CODA_E2M1X2 = 6,
+  CODA_E2M3 = 7, CODA_E3M2 = 8
 } coda_dtype;
 
 /* GEMM operand precision of the functional entry points. */
@@ -350,6 +358,22 @@ coda_status coda_quantize_mxfp8(const coda_mat* X, int32_t axis, const coda_mat*
 coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
                                 void* stream);
 
+/* MXFP6 copy of X (bf16 [R, C]), OCP MX v1.0 FP6 with the element format
+ * Q's dtype names (CODA_E2M3 or CODA_E3M2): blocks of 32 values along the
+ * contracted axis share the E8M0 exponent e = floor(log2 max|v|) - emax
+ * (emax = 2 for E2M3, 4 for E3M2: the exponent of the format's largest
+ * power of two), clamped to [-127, 127] (-127 for an all-zero block); an
+ * element is the nearest FP6 value to v / 2^e, ties to the even mantissa,
+ * saturated at the largest (7.5 or 28); a value that rounds to zero is code
+ * 0 (+0).  Blocks are packed as the dtype comment above says.
+ *   axis 1: Q [R, C], exponents of R rows (C % 32 == 0);
+ *   axis 0: Q [C, R] (written transposed), exponents of C rows (R % 32 == 0).
+ * S: E8M0 in word layout as for coda_quantize_mxfp8, [ceil(L / 128), 4 rows].
+ * Errors: CODA_ERR_DTYPE when Q is neither FP6 dtype; otherwise as
+ * coda_quantize_mxfp4. */
+coda_status coda_quantize_mxfp6(const coda_mat* X, int32_t axis, const coda_mat* Q, const coda_mat* S,
+                                void* stream);
+
 /* D = epilogue(sum_k A~[m, k] B~[n, k]) with MXFP8 operands
  *   A~ = A (E4M3 [M, K]) scaled by SA (E8M0 [K / 128, 4 M], word layout),
  *   B~ = B (E4M3 [N, K], i.e. the second operand stored with K contiguous)
@@ -367,7 +391,11 @@ coda_status coda_quantize_mxfp4(const coda_mat* X, int32_t axis, const coda_mat*
  * exponent layout and K rule (K counts values); the epilogue program is one
  * of STORE_BF16, ACCUM_F32, ROW_SCALE COL_SCALE STORE_BF16, ADD_TILE
  * STORE_BF16 [ROW_SUMSQ_PARTIAL] and the SWIGLU, SIGMOID and QKNORM_ROPE
- * chains. */
+ * chains.
+ * MXFP6: with A of dtype CODA_E2M3 or CODA_E3M2 (as written by
+ * coda_quantize_mxfp6) the operands are FP6 of that format, A [M, K] and
+ * B [N, K] in bytes, B of the same dtype (CODA_ERR_DTYPE otherwise), same
+ * exponent layout and K rule, and the same programs as MXFP4. */
 coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                          const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
                          uint32_t n_aux, void* ws, size_t ws_bytes, void* stream);

@@ -19,7 +19,10 @@ so E2M1 (B = 1) holds 0, 0.5, 1, 1.5, 2, 3, 4, 6; E2M3 (B = 1) tops out
 at 7.5 and E3M2 (B = 3) at 28.  Codes are sign | exponent | mantissa, from
 the high bit down.  FP4 codes are packed two to a byte, element 2i in the low
 nibble of byte i (a reading: the specification leaves packing to the
-implementation).
+implementation).  FP6 codes of a 32-element block are packed into 24 bytes,
+element v at bits [6 v, 6 v + 6) of the block read as one little-endian
+192-bit number, followed by 8 zero bytes, so a row of L elements takes L
+bytes (a reading too: the padding keeps every block on a 32-byte boundary).
 
 The CODA paper names only the trend towards FP8 and FP4 operands (§1); the
 formats and the conversion are the MX specification's.
@@ -119,6 +122,37 @@ def unpack_fp4(b) -> np.ndarray:
     out[:, 0::2] = b & 0xF
     out[:, 1::2] = b >> 4
     return out
+
+
+def pack_fp6(codes) -> np.ndarray:
+    """[R, C] FP6 codes (C a multiple of 32) -> [R, C] bytes: each block of 32
+    codes becomes 24 bytes holding code v at bits [6 v, 6 v + 6) of a
+    little-endian 192-bit number, then 8 zero bytes."""
+    c = np.asarray(codes, dtype=np.uint64) & 0x3F
+    R, C = c.shape
+    assert C % 32 == 0, "FP6 rows are whole 32-element blocks"
+    blk = c.reshape(R, C // 32, 32)
+    out = np.zeros((R, C // 32, 32), dtype=np.uint8)
+    for v in range(32):                      # value v starts at bit 6 v
+        byte, shift = divmod(6 * v, 8)
+        bits = blk[:, :, v] << np.uint64(shift)          # at most 13 bits
+        out[:, :, byte] |= (bits & 0xFF).astype(np.uint8)
+        if shift > 2:
+            out[:, :, byte + 1] |= ((bits >> np.uint64(8)) & 0xFF).astype(np.uint8)
+    return out.reshape(R, C)
+
+
+def unpack_fp6(b) -> np.ndarray:
+    """Inverse of pack_fp6 (the pad bytes are ignored)."""
+    b = np.asarray(b, dtype=np.uint8)
+    R, C = b.shape
+    blk = b.reshape(R, C // 32, 32).astype(np.uint64)
+    out = np.empty((R, C // 32, 32), dtype=np.uint8)
+    for v in range(32):
+        byte, shift = divmod(6 * v, 8)
+        w = blk[:, :, byte] | ((blk[:, :, byte + 1] << np.uint64(8)) if byte + 1 < 24 else np.uint64(0))
+        out[:, :, v] = ((w >> np.uint64(shift)) & np.uint64(0x3F)).astype(np.uint8)
+    return out.reshape(R, C)
 
 
 def dequantize(P, e, block: int = BLOCK) -> np.ndarray:

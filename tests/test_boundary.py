@@ -351,6 +351,47 @@ def test_mxfp4_quantiser_validation_codes():
     assert call(X, 0, fake(E2, 96, 32), fake(E8, 1, 384, ptr=FAKE + 2)) == 5
 
 
+def test_mxfp6_quantiser_validation_codes():
+    """coda_quantize_mxfp6 takes its format from Q's dtype (E2M3 or E3M2) and
+    checks axis, block multiple, Q's shape (a byte a value) and the exponent
+    layout before any launch."""
+    L = g.lib()
+    BF, E4, E8 = _lib.CODA_BF16, _lib.CODA_E4M3, _lib.CODA_E8M0
+    X = fake(BF, 64, 96)
+    s_ok = fake(E8, 1, 256)
+    call = lambda x, ax, q, s: L.coda_quantize_mxfp6(C.byref(x), ax, C.byref(q), C.byref(s), None)
+    for F6 in (_lib.CODA_E2M3, _lib.CODA_E3M2):
+        q_ok = fake(F6, 64, 96)
+        assert call(X, 2, q_ok, s_ok) == 9                               # axis
+        assert call(fake(BF, 64, 80), 1, fake(F6, 64, 80), s_ok) == 3    # 80 not a multiple of 32
+        assert call(X, 1, fake(F6, 64, 48), s_ok) == 3                   # Q holds C bytes a row
+        assert call(X, 1, q_ok, fake(E8, 2, 256)) == 3                   # word rows: ceil(96 / 128) = 1
+        assert call(X, 0, fake(F6, 96, 64), fake(E8, 1, 384, ptr=FAKE + 2)) == 5   # transposed: S alignment
+    assert call(X, 1, fake(E4, 64, 96), s_ok) == 2                       # Q neither FP6 dtype
+    assert call(X, 1, fake(_lib.CODA_E2M1X2, 64, 48), s_ok) == 2
+
+
+def test_mxfp6_gemm_validation_codes():
+    """coda_gemm_mx with FP6 operands: B must carry A's FP6 dtype, K a
+    multiple of 128 and the exponents sized for K values."""
+    L = g.lib()
+    BF, E8, E23, E32 = _lib.CODA_BF16, _lib.CODA_E8M0, _lib.CODA_E2M3, _lib.CODA_E3M2
+    prog = _lib.EpiProgram()
+    prog.n_ops = 1
+    prog.ops[0].op = _lib.EPI_STORE_BF16
+    gm = lambda A, SA, B, SB, D: L.coda_gemm_mx(C.byref(prog), C.byref(A), C.byref(SA), C.byref(B), C.byref(SB),
+                                                C.byref(D), None, 0, None, 0, None)
+    M, N = 64, 32
+    assert gm(fake(E23, M, 256), fake(E8, 2, 4 * M), fake(E32, N, 256), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 2                                             # formats differ
+    assert gm(fake(E32, M, 96), fake(E8, 1, 4 * M), fake(E32, N, 96), fake(E8, 1, 4 * N),
+              fake(BF, M, N)) == 3                                             # K = 96
+    assert gm(fake(E23, M, 256), fake(E8, 1, 4 * M), fake(E23, N, 256), fake(E8, 2, 4 * N),
+              fake(BF, M, N)) == 3                                             # 256 values need 2 word rows
+    assert gm(fake(E23, M, 256), fake(E8, 2, 4 * M), fake(E23, N, 256), fake(E8, 2, 4 * N),
+              fake(BF, M, N + 8)) == 3                                         # D shape
+
+
 def test_mxfp4_gemm_validation_codes():
     """coda_gemm_mx with E2M1X2 operands: both operands must be E2M1X2, K
     (twice the byte count) a multiple of 128, and the exponents sized for K

@@ -465,3 +465,226 @@ def test_gemm_mxfp4_degenerate_shapes():
     A, B = mx4_values(ca, sa), mx4_values(cb, sb)
     ref = A @ B.T
     assert np.all(np.abs(to_np(D) - ref) <= mfma_fp8_bound(A, B) + 1e-30)
+
+
+# ---------------------------------------------------------------- MXFP6
+FP6 = ("e2m3", "e3m2")
+
+
+def fp6_ladder_bf16(rng, R, C, axis, fmt):
+    """varied_bf16 plus, in every fourth block along `axis`, the FP6 ties of
+    `fmt`: a block maximum of exactly 2^emax (so the block's exponent is the
+    power of two it was scaled by) and elements on every midpoint between
+    neighbouring values of the format, both signs, values past the largest
+    (which saturate) and small negatives that round to zero."""
+    from oracle import mx_small as ms
+    _, _, _, emax, vmax = ms.fmt_params(fmt)
+    E, M, _ = ms.FORMATS[fmt]
+    vals = np.unique(np.abs(ms.decode(np.arange(2 ** (1 + E + M)), fmt)))
+    mids = (vals[:-1] + vals[1:]) / 2
+    over = np.array([vmax + 2.0 ** (emax - M - 1), (vmax + 2.0 ** (emax + 1)) / 2])
+    ties = np.concatenate([mids, -mids, over, -over, [-vals[1] / 4, 0.0]]).astype(np.float32)
+    X = varied_bf16(rng, R, C, axis)
+    Xt = X if axis == 1 else X.T
+    nb = Xt.shape[1] // 32
+    k = 0
+    for r in range(1, Xt.shape[0], 3):        # row 0 keeps its all-zero block
+        for b in range(0, nb, 4):
+            s = np.float32(2.0 ** int(rng.integers(-10, 10)))
+            blk = ties[(32 * k + np.arange(32)) % ties.size] * s
+            blk[rng.integers(0, 32)] = 2.0 ** emax * s
+            Xt[r, 32 * b:32 * b + 32] = blk
+            k += 1
+    return ci.to_bf16_values(X if axis == 1 else Xt.T)
+
+
+@pytest.mark.parametrize("fmt", FP6)
+@pytest.mark.parametrize("axis,R,C", [(1, 300, 480), (1, 5, 32), (0, 480, 296), (0, 64, 7 * 8)])
+def test_mxfp6_quantiser_bit_exact(fmt, axis, R, C):
+    """Packed FP6 codes (with their zero padding) and E8M0 exponents equal the
+    oracle's (oracle/mx_small.py) bit for bit, in both orientations, with
+    ragged tiles, an all-zero block, a block of very large values and every
+    rounding tie and saturation of the format."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(60 + axis + 2 * FP6.index(fmt))
+    X = fp6_ladder_bf16(rng, R, C, axis, fmt)
+    Q, S = coda.quantize_mxfp6(bf(X), axis, fmt)
+    torch.cuda.synchronize()
+    Xr = X if axis == 1 else np.ascontiguousarray(X.T)
+    P, e = ms.quantize(Xr, fmt)
+    want_q = ms.pack_fp6(ms.encode(P, fmt))
+    got_q = to_np(Q).astype(np.uint8)
+    rows, L = Xr.shape
+    assert got_q.shape == (rows, L)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, (bad[:5], got_q[tuple(bad[0])], want_q[tuple(bad[0])])
+    got_e = from_words(to_np(S), rows, L // 32)
+    np.testing.assert_array_equal(got_e, (e + 127).astype(np.uint8))
+
+
+def random_mx6(rng, rows, K, fmt, emin=117, emax=137):
+    """An MXFP6 operand drawn directly: uniform codes (all 64) and E8M0 codes
+    uniform in [emin, emax], independent per block; returns the codes
+    [rows, K] and the exponent bytes [rows, K / 32]."""
+    codes = rng.integers(0, 64, size=(rows, K)).astype(np.uint8)
+    scales = rng.integers(emin, emax + 1, size=(rows, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def mx6_values(codes, scales, fmt):
+    from oracle import mx_small as ms
+    return ms.dequantize(ms.decode(codes, fmt), scales.astype(np.int64) - 127)
+
+
+@pytest.mark.parametrize("fmt", FP6)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 384), (517, 520, 1024), (64, 8, 128)])
+def test_gemm_mxfp6_accum_and_store(fmt, M, N, K):
+    """FP6 operands through the fp32 accumulate and bf16 store epilogues,
+    against the oracle's float64 product of the dequantised operands; K 384
+    has an odd number of 64-value stages, K 128 a single stage pair."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(M + N + K + 3 + FP6.index(fmt))
+    ca, sa = random_mx6(rng, M, K, fmt)
+    cb, sb = random_mx6(rng, N, K, fmt)
+    A, B = mx6_values(ca, sa, fmt), mx6_values(cb, sb, fmt)
+    ref = A @ B.T
+    qa, qb = u8(ms.pack_fp6(ca)), u8(ms.pack_fp6(cb))
+    prior = ci.fp32_prior((M, N), 6)
+    D32 = f32(prior)
+    coda.gemm_mx6([(coda.EPI_ACCUM_F32, 0, 1.0)], fmt, qa, u8(to_words(sa)), qb, u8(to_words(sb)), D32)
+    D16 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(coda.EPI_STORE_BF16, 0, 0.0)], fmt, qa, u8(to_words(sa)), qb, u8(to_words(sb)), D16)
+    torch.cuda.synchronize()
+    bound = mfma_fp8_bound(A, B)
+    got32 = to_np(D32).astype(np.float64) - prior
+    assert np.all(np.abs(got32 - ref) <= bound + 2.0 ** -23 * (np.abs(ref) + np.abs(prior))), \
+        float(np.max(np.abs(got32 - ref) - bound))
+    got16 = to_np(D16).astype(np.float64)
+    assert np.all(np.abs(got16 - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), \
+        float(np.max(np.abs(got16 - ref) - bound))
+    assert np.linalg.norm(got32 - ref) <= 1e-3 * np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_gemm_mxfp6_one_scale_per_block(fmt):
+    """Exponents that differ between every block of a row and between rows
+    (a scale from the wrong block, stage or row moves the result by a power
+    of two), and padding bytes that are not zero (the matrix core must not
+    read them)."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(23 + FP6.index(fmt))
+    M, N, K = 256, 256, 512
+    ca, _ = random_mx6(rng, M, K, fmt)
+    cb, _ = random_mx6(rng, N, K, fmt)
+    sa = (120 + (np.arange(K // 32)[None, :] * 3 + np.arange(M)[:, None]) % 15).astype(np.uint8)
+    sb = (121 + (np.arange(K // 32)[None, :] * 5 + 2 * np.arange(N)[:, None]) % 13).astype(np.uint8)
+    A, B = mx6_values(ca, sa, fmt), mx6_values(cb, sb, fmt)
+    pa, pb = ms.pack_fp6(ca), ms.pack_fp6(cb)
+    pad = (np.arange(K) % 32) >= 24
+    pa[:, pad] = 0xA5
+    pb[:, pad] = 0x5A
+    D32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    coda.gemm_mx6([(coda.EPI_ACCUM_F32, 0, 0.0)], fmt, u8(pa), u8(to_words(sa)), u8(pb), u8(to_words(sb)), D32)
+    torch.cuda.synchronize()
+    ref = A @ B.T
+    assert np.all(np.abs(to_np(D32) - ref) <= mfma_fp8_bound(A, B))
+    assert np.linalg.norm(to_np(D32) - ref) <= 1e-3 * np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_gemm_mxfp6_from_bf16_epilogues(fmt):
+    """bf16 inputs quantised by the library (bit-exact against the oracle, as
+    tested above), then the residual program out = z + a W and the SwiGLU
+    program with given row factors on the MXFP6 product, against the
+    oracle's product of its own quantisation."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(37 + FP6.index(fmt))
+    M, N, K = 300, 576, 640       # SwiGLU packs gate/up in 64-column groups
+    a = ci.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = ci.to_bf16_values((rng.standard_normal((N, K)) * K ** -0.5).astype(np.float32))
+    z = ci.to_bf16_values(rng.standard_normal((M, N)).astype(np.float32))
+    QA, SA = coda.quantize_mxfp6(bf(a), 1, fmt)
+    QB, SB = coda.quantize_mxfp6(bf(w), 1, fmt)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)], fmt, QA, SA, QB, SB, out,
+                  aux=[bf(z)])
+    r = rng.uniform(0.5, 2, M).astype(np.float32)
+    D3 = torch.empty((M, N // 2), dtype=BF, device=DEV)
+    coda.gemm_mx6([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_SWIGLU, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)],
+                  fmt, QA, SA, QB, SB, D3, aux=[f32(r)])
+    torch.cuda.synchronize()
+    PA, eA = ms.quantize(a, fmt)
+    PB, eB = ms.quantize(w, fmt)
+    A, B = ms.dequantize(PA, eA), ms.dequantize(PB, eB)
+    acc = A @ B.T
+    ref = z.astype(np.float64) + acc
+    got = to_np(out).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1.01 * mfma_fp8_bound(A, B) + 2.0 ** -8 * np.abs(ref) + 1e-30)
+    assert np.linalg.norm(got - nm.bf16(ref)) <= 3e-3 * np.linalg.norm(ref)
+    hg, hu = unpack_gu(r[:, None] * acc)
+    assert_bf16("swiglu", to_np(D3), nm.bf16(ops.swiglu(hg, hu)))
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_gemm_mxfp6_degenerate_shapes(fmt):
+    """Empty M or N is a no-op that leaves D untouched; a single row and the
+    smallest K (128 values: one stage pair, one exponent word row) match the
+    oracle."""
+    from oracle import mx_small as msm
+    rng = np.random.default_rng(41 + FP6.index(fmt))
+    sentinel = torch.full((64, 64), 3.0, dtype=BF, device=DEV)
+    for M, N in ((0, 64), (64, 0)):
+        qa = torch.empty((max(M, 1), 128), dtype=torch.uint8, device=DEV)[:M]
+        qb = torch.empty((max(N, 1), 128), dtype=torch.uint8, device=DEV)[:N]
+        sa = torch.empty((1, 4 * max(M, 1)), dtype=torch.uint8, device=DEV)[:, :4 * M]
+        sb = torch.empty((1, 4 * max(N, 1)), dtype=torch.uint8, device=DEV)[:, :4 * N]
+        coda.gemm_mx6([(coda.EPI_STORE_BF16, 0, 0.0)], fmt, qa, sa, qb, sb, sentinel[:M, :N])
+    torch.cuda.synchronize()
+    assert bool((sentinel == 3.0).all())
+    ca, sa = random_mx6(rng, 1, 128, fmt)
+    cb, sb = random_mx6(rng, 40, 128, fmt)
+    D = torch.empty((1, 40), dtype=torch.float32, device=DEV)
+    coda.gemm_mx6([(coda.EPI_ACCUM_F32, 0, 0.0)], fmt, u8(msm.pack_fp6(ca)), u8(to_words(sa)),
+                  u8(msm.pack_fp6(cb)), u8(to_words(sb)), D)
+    torch.cuda.synchronize()
+    A, B = mx6_values(ca, sa, fmt), mx6_values(cb, sb, fmt)
+    ref = A @ B.T
+    assert np.all(np.abs(to_np(D) - ref) <= mfma_fp8_bound(A, B) + 1e-30)
+
+
+def test_gemm_mxfp6_full_size_sampled():
+    """The MXFP4 full-size layer with E2M3 operands: M 4096, K 28672, N 8192
+    with residual; the library quantises a and W; 128 sampled outputs are
+    recomputed by the oracle from its own MXFP6 copies of the sampled rows
+    of a and columns of W (whose packed codes and exponents must equal the
+    library's bit for bit)."""
+    from oracle import mx_small as msm
+    fmt = "e2m3"
+    M, K, N = 4096, 28672, 8192
+    rng = np.random.default_rng(79)
+    a = ci.to_bf16_values(rng.standard_normal((M, K), dtype=np.float32))
+    W = ci.to_bf16_values(rng.standard_normal((K, N), dtype=np.float32) * np.float32(K ** -0.5))
+    z = ci.to_bf16_values(rng.standard_normal((M, N), dtype=np.float32))
+    ag, Wg, zg = bf(a), bf(W), bf(z)
+    Qa, Sa = coda.quantize_mxfp6(ag, 1, fmt)
+    Qw, Sw = coda.quantize_mxfp6(Wg, 0, fmt)
+    out = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(coda.EPI_ADD_TILE, 0, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)], fmt, Qa, Sa, Qw, Sw, out, aux=[zg])
+    torch.cuda.synchronize()
+    ms = rng.integers(0, M, 128)
+    ns = rng.integers(0, N, 128)
+    um, un = np.unique(ms), np.unique(ns)
+    Pa, ea = msm.quantize(a[um], fmt)
+    Pw, ew = msm.quantize(W[:, un].T.copy(), fmt)
+    assert np.array_equal(Qa[torch.from_numpy(um).to(DEV)].cpu().numpy(), msm.pack_fp6(msm.encode(Pa, fmt)))
+    assert np.array_equal(from_words(Sa.cpu().numpy(), M, K // 32)[um], (ea + 127).astype(np.uint8))
+    assert np.array_equal(Qw[torch.from_numpy(un).to(DEV)].cpu().numpy(), msm.pack_fp6(msm.encode(Pw, fmt)))
+    assert np.array_equal(from_words(Sw.cpu().numpy(), N, K // 32)[un], (ew + 127).astype(np.uint8))
+    Ad, Bd = msm.dequantize(Pa, ea), msm.dequantize(Pw, ew)
+    im, jn = np.searchsorted(um, ms), np.searchsorted(un, ns)
+    acc = np.einsum("ik,ik->i", Ad[im], Bd[jn])
+    bound = 2.0 ** -10 * np.einsum("ik,ik->i", np.abs(Ad[im]), np.abs(Bd[jn]))
+    ref = z[ms, ns].astype(np.float64) + acc
+    got = out[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), float(np.max(np.abs(got - ref) - bound))
+    assert_bf16("sampled out", got, nm.bf16(ref))

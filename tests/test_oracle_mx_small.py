@@ -111,6 +111,25 @@ def test_fp4_packing_order():
     np.testing.assert_array_equal(ms.unpack_fp4(b), codes)
 
 
+def test_fp6_packing_order():
+    # worked by hand: code 1 at bits 0-5, code 2 at bits 6-11, code 3 at 12-17
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, :3] = [1, 2, 3]
+    b = ms.pack_fp6(codes)
+    assert b[0, :3].tolist() == [0x81, 0x30, 0x00]
+    assert np.all(b[0, 3:] == 0)
+    # the last code sits in the top six bits of byte 23; bytes 24-31 stay zero
+    codes = np.zeros((2, 64), dtype=np.uint8)
+    codes[0, 31] = 0x3F
+    codes[1, 32:] = 0x3F
+    b = ms.pack_fp6(codes)
+    assert b[0, 23] == 0xFC and np.count_nonzero(b[0]) == 1
+    assert np.all(b[1, :32] == 0) and np.all(b[1, 32:56] == 0xFF) and np.all(b[1, 56:] == 0)
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 64, size=(3, 96)).astype(np.uint8)
+    np.testing.assert_array_equal(ms.unpack_fp6(ms.pack_fp6(c)), c)
+
+
 def test_matmul_triple_loop():
     rng = np.random.default_rng(8)
     A = rng.standard_normal((3, 64)).astype(np.float32)
