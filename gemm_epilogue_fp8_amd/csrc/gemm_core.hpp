@@ -182,11 +182,28 @@ struct TileKC {
   // out-of-range offset.  One vector register instead of one per
   // instruction keeps the block-scaled mainloop (which also holds scale
   // words) free of spills; elsewhere the per-instruction offsets measured
-  // 3.5% faster.
+  // 3.5% faster.  A stage whose rows and K chunks all exist (every stage of
+  // an interior tile) takes one resource and moves the 16-row group step
+  // into the scalar offset: 2.5% off the MXFP8 GEMM at M 4096, K 28672,
+  // N 8192 (the same path is 6% slower than per-instruction offsets for
+  // per-row-scaled E4M3, so those keep theirs).
   __device__ __forceinline__ static void issue_lean(const char* base, int64_t ld_bytes, int row0, int nrows,
                                                     int64_t kbyte0, int64_t kbytes, char* lds, int w, int lane) {
     const int rl = lane >> 2;
     const int chunk = (lane & 3) ^ ((rl >> 2) & 3);    // = the chunk of row 16 q + rl at this slot, any q
+    if (row0 + R <= nrows && kbyte0 + kRowBytes <= kbytes) {
+      // every row and chunk of the stage exists: one resource for the
+      // stage, the 16-row group step in the scalar offset
+      const uint32_t v = (uint32_t)(rl * ld_bytes + chunk * 16);
+      const int64_t rem = (int64_t)(nrows - row0 - 1) * ld_bytes + (kbytes - kbyte0);
+      const auto rs = make_rsrc(base + (int64_t)row0 * ld_bytes + kbyte0, (uint64_t)rem);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int q = NI * w + i;
+        raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)v, (int)(16 * q * ld_bytes), 0, 0);
+      }
+      return;
+    }
     const uint32_t voff = (kbyte0 + chunk * 16 < kbytes) ? (uint32_t)(rl * ld_bytes + chunk * 16) : kOobOffset;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
