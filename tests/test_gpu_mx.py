@@ -688,3 +688,69 @@ def test_gemm_mxfp6_full_size_sampled():
     got = out[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= 1.01 * bound + 2.0 ** -8 * np.abs(ref)), float(np.max(np.abs(got - ref) - bound))
     assert_bf16("sampled out", got, nm.bf16(ref))
+
+
+@pytest.mark.parametrize("fmt", FP6)
+def test_gemm_mxfp6_remaining_chains(fmt):
+    """The other forward programs compiled for FP6 operands, on operands the
+    library quantised (bit-exact against the oracle, as tested above):
+    row/column scales, residual + sum-of-squares partials, sigmoid with its
+    saved pre-activation, and RMS-from-partials + QK-norm + RoPE on a QKV
+    layer (two heads of 128), against the oracle's float64 product of its
+    own quantisation with the same epilogue formulas."""
+    from oracle import mx_small as ms
+    rng = np.random.default_rng(47 + FP6.index(fmt))
+    M, K, Dh, seq = 300, 256, 256, 100
+    N = 3 * Dh
+    x = ci.to_bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    W = ci.to_bf16_values((rng.standard_normal((N, K)) * K ** -0.5).astype(np.float32))   # stored [N, K]
+    QA, SA = coda.quantize_mxfp6(bf(x), 1, fmt)
+    QB, SB = coda.quantize_mxfp6(bf(W), 1, fmt)
+    PA, eA = ms.quantize(x, fmt)
+    PB, eB = ms.quantize(W, fmt)
+    acc = ms.dequantize(PA, eA) @ ms.dequantize(PB, eB).T
+    E = coda
+
+    rv = rng.uniform(0.5, 2, M).astype(np.float32)
+    cv = rng.uniform(0.5, 2, N).astype(np.float32)
+    D1 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(E.EPI_ROW_SCALE, 0, 0.0), (E.EPI_COL_SCALE, 1, 0.0), (E.EPI_STORE_BF16, 0, 0.0)], fmt,
+                  QA, SA, QB, SB, D1, aux=[f32(rv), f32(cv)])
+    Z = ci.to_bf16_values(rng.standard_normal((M, N)).astype(np.float32))
+    P = torch.empty((coda.partials_cols(N), M), dtype=torch.float32, device=DEV)
+    D2 = torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(E.EPI_ADD_TILE, 0, 0.0), (E.EPI_STORE_BF16, 0, 0.0), (E.EPI_ROW_SUMSQ_PARTIAL, 1, 0.0)], fmt,
+                  QA, SA, QB, SB, D2, aux=[bf(Z), P])
+    r = rng.uniform(0.5, 2, M).astype(np.float32)
+    D3, h = torch.empty((M, N), dtype=BF, device=DEV), torch.empty((M, N), dtype=BF, device=DEV)
+    coda.gemm_mx6([(E.EPI_ROW_SCALE, 0, 0.0), (E.EPI_SAVE_PRE, 1, 0.0), (E.EPI_SIGMOID, 0, 0.0),
+                   (E.EPI_STORE_BF16, 0, 0.0)], fmt, QA, SA, QB, SB, D3, aux=[f32(r), h])
+    gains = (1 + 0.1 * rng.standard_normal((2, 128))).astype(np.float32)
+    table = torch.empty((seq, 128), dtype=torch.float32, device=DEV)
+    coda.rope_table(seq, table)
+    Px = np.stack([(x.astype(np.float64) ** 2)[:, :K // 2].sum(axis=1),
+                   (x.astype(np.float64) ** 2)[:, K // 2:].sum(axis=1)]).astype(np.float32)
+    D4, r4, save = (torch.empty((M, N), dtype=BF, device=DEV), torch.empty(M, dtype=torch.float32, device=DEV),
+                    torch.empty((M, 2 * Dh), dtype=BF, device=DEV))
+    coda.gemm_mx6([(E.EPI_ROW_RMS_FROM_PARTIALS, 0, 1e-6), (E.EPI_STORE_ROW_VEC, 1, 0.0), (E.EPI_SAVE_PRE, 2, 0.0),
+                   (E.EPI_QKNORM_ROPE, (3, 4), 1e-6), (E.EPI_STORE_BF16, 0, 0.0)], fmt, QA, SA, QB, SB, D4,
+                  aux=[f32(Px), r4, save, f32(gains), table])
+    torch.cuda.synchronize()
+
+    assert_bf16("row/col scaled", to_np(D1), nm.bf16((acc * rv[:, None]) * cv[None, :]))
+    y = nm.bf16(Z + acc)
+    assert_bf16("residual", to_np(D2), y)
+    assert_grad("sumsq partials", to_np(P), ob.tile_partials(y.astype(np.float64) ** 2, 256))
+    hh = r[:, None] * acc
+    assert_bf16("sigmoid h", to_np(h), nm.bf16(hh))
+    assert_bf16("sigmoid", to_np(D3), nm.bf16(ops.sigmoid(hh)))
+    rr = ops.inv_rms(x, 1e-6)
+    assert_grad("r", to_np(r4), rr)
+    t = rr[:, None] * acc
+    cos, sin = ops.rope_tables(seq, 128, 5e5)
+    pos = np.arange(M) % seq
+    got = to_np(D4)
+    assert_bf16("q", got[:, :Dh], nm.bf16(ops.rope(ops.qk_norm(t[:, :Dh], gains[0], 1e-6), pos, cos, sin)))
+    assert_bf16("k", got[:, Dh:2 * Dh], nm.bf16(ops.rope(ops.qk_norm(t[:, Dh:2 * Dh], gains[1], 1e-6), pos, cos, sin)))
+    assert_bf16("v", got[:, 2 * Dh:], nm.bf16(t[:, 2 * Dh:]))
+    assert_bf16("q_pre|k_pre", to_np(save), nm.bf16(t[:, :2 * Dh]))
