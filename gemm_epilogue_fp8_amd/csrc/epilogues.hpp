@@ -643,29 +643,46 @@ struct EpiQKNormRope {
     const int w0 = (c.wn / WPH) * WPH;
     const float* g = reg == 0 ? e.colvec : e.colvec2;
     if (reg < 2) {
+      // The gains of this lane's columns, and the cos/sin of a row's column
+      // pairs, are loaded as whole batches (one row ahead), so that each row
+      // waits for one round of table loads rather than one per column group.
+      f32x4_t gg[Cfg::TN][4], cs[2][Cfg::TN][4];
+      auto load_cs = [&](int i, f32x4_t (&d)[Cfg::TN][4]) {
+        const int m = c.row(i);
+        const int pos = (m < c.M ? m : 0) % e.seq_len;
+        const float* t = e.table + (int64_t)pos * 128;
+#pragma unroll
+        for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[j][q] = *reinterpret_cast<const f32x4_t*>(t + (c.col(j, q) & 127));
+      };
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gg[j][q] = *reinterpret_cast<const f32x4_t*>(g + (c.col(j, q) & 127));
+      load_cs(0, cs[0]);
 #pragma unroll
       for (int i = 0; i < Cfg::TM; ++i) {
-        const int m = c.row(i);
+        if (i + 1 < Cfg::TM) load_cs(i + 1, cs[(i + 1) & 1]);
         float ss = 0.0f;
 #pragma unroll
         for (int w = 0; w < WPH; ++w) ss += red[(w0 + w) * Cfg::BM + c.lrow(i)];
         const float rho = rsqrtf(ss / 128.0f + e.eps);
-        const int pos = (m < c.M ? m : 0) % e.seq_len;
 #pragma unroll
         for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int cc = c.col(j, q) & 127;                // column inside the head
             f32x4_t h = frag(acc, i, j, q);
-            f32x4_t gg = *reinterpret_cast<const f32x4_t*>(g + cc);
-            f32x4_t y = h * rho * gg;
-            // pairs (cc, cc+1) and (cc+2, cc+3) -> frequencies cc/2, cc/2 + 1
-            f32x4_t cs = *reinterpret_cast<const f32x4_t*>(e.table + ((int64_t)pos * 64 + (cc >> 1)) * 2);
+            f32x4_t y = h * rho * gg[j][q];
+            // pairs (cc, cc+1) and (cc+2, cc+3) of column cc = col & 127 ->
+            // frequencies cc/2 and cc/2 + 1, whose (cos, sin) pairs are the
+            // 4 floats at 2 (cc/2) = cc of the position's table row
+            const f32x4_t cs4 = cs[i & 1][j][q];
             f32x4_t o;
-            o[0] = y[0] * cs[0] - y[1] * cs[1];
-            o[1] = y[0] * cs[1] + y[1] * cs[0];
-            o[2] = y[2] * cs[2] - y[3] * cs[3];
-            o[3] = y[2] * cs[3] + y[3] * cs[2];
+            o[0] = y[0] * cs4[0] - y[1] * cs4[1];
+            o[1] = y[0] * cs4[1] + y[1] * cs4[0];
+            o[2] = y[2] * cs4[2] - y[3] * cs4[3];
+            o[3] = y[2] * cs4[3] + y[3] * cs4[2];
             set_frag(acc, i, j, q, o);
           }
       }
