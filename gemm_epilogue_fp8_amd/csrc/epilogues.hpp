@@ -286,15 +286,36 @@ __device__ __forceinline__ void store_f32_tile(const EpiArgs& e, const Ctx<Cfg>&
           *reinterpret_cast<f32x4_t*>(s + S::off(r, c.lcol(j, q) >> 2)) = frag(acc, i, j, q);
     }
     __syncthreads();
-#pragma unroll 4
-    for (int id = c.tid; id < HR * S::CPR; id += Cfg::T) {
-      const int r = id / S::CPR, ch = id % S::CPR;
-      const int m = c.m0 + h * HR + r, n = c.n0 + ch * 4;
-      if (m >= c.M || n >= c.N) continue;
-      f32x4_t v = *reinterpret_cast<const f32x4_t*>(s + S::off(r, ch));
-      f32x4_t* p = reinterpret_cast<f32x4_t*>(out + (int64_t)m * e.ld_out + n);
-      if (e.beta != 0.0f) v = v + e.beta * *p;
-      *p = v;
+    // Batches of NB chunks: every prior value of a batch is loaded before
+    // any of its stores, so the batch waits for one round trip (a loop that
+    // loads, adds and stores chunk by chunk compiles to one exposed round
+    // trip per chunk, the compiler being unable to move a load above the
+    // previous chunk's store).
+    constexpr int ITER = HR * S::CPR / Cfg::T;
+    static_assert(HR * S::CPR % Cfg::T == 0, "whole rounds of 16-byte chunks");
+    constexpr int NB = ITER < 4 ? ITER : 4;
+    static_assert(ITER % NB == 0, "whole batches");
+#pragma unroll
+    for (int k0 = 0; k0 < ITER; k0 += NB) {
+      f32x4_t v[NB], prior[NB];
+      f32x4_t* p[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int id = c.tid + (k0 + k) * Cfg::T;
+        const int r = id / S::CPR, ch = id % S::CPR;
+        const int m = c.m0 + h * HR + r, n = c.n0 + ch * 4;
+        p[k] = (m < c.M && n < c.N) ? reinterpret_cast<f32x4_t*>(out + (int64_t)m * e.ld_out + n) : nullptr;
+        v[k] = *reinterpret_cast<const f32x4_t*>(s + S::off(r, ch));
+      }
+      if (e.beta != 0.0f) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) prior[k] = p[k] ? *p[k] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < NB; ++k) v[k] = v[k] + e.beta * prior[k];
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (p[k]) *p[k] = v[k];
     }
   }
 }
