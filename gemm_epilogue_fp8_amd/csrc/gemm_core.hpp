@@ -317,12 +317,16 @@ __device__ __forceinline__ typename Frags<Cfg>::T read_frag(const char* tile, in
   } else if constexpr (Cfg::FP6) {
     // lanes 0-31 hold K block 0 of their row, lanes 32-63 block 1: the 24
     // packed bytes (value v at bits [6 v, 6 v + 6)) at the start of the
-    // block's 32, in the low 6 registers, which are all the matrix core reads
+    // block's 32, in the low 6 registers, which are all the matrix core reads.
+    // Both chunks are read whole: 16-byte reads are served 16 lanes at a
+    // time, so the swizzle keeps them conflict-free, whereas an 8-byte read
+    // of the second chunk (32 lanes a pass) puts rows r and r + 16 on the
+    // same banks.
     const int row = r0 + (lane & 31);
     const int h = lane >> 5;
     (void)s;
     i32x4_t lo = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 * h));
-    i32x2_t up = *reinterpret_cast<const i32x2_t*>(tile + lds_off(row, 2 * h + 1));
+    i32x4_t up = *reinterpret_cast<const i32x4_t*>(tile + lds_off(row, 2 * h + 1));
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], up[0], up[1], 0, 0};
   } else if constexpr (Cfg::FP8) {
     // K bytes [16 h, 16 h + 16) and [32 + 16 h, 32 + 16 h + 16) of the row,
