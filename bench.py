@@ -478,31 +478,33 @@ def main():
     if args.config == "cfg2" and not args.no_h4096:
         h4096, _ = block_leg("cfg3", precision, args)
 
-    fp4_fwd = None
+    small_fwd = {}
     if not args.no_mx and not fp8:
-        # the same block forward (inference) with MXFP4 operands: weights
-        # quantised once, activations per call
+        # the same block forward (inference) with MXFP4 and MXFP6 (E2M3)
+        # operands: weights quantised once, activations per call
         dev = "cuda:0"
         P = ci.block_inputs(cfg, seed)
         to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
         params = {k: to(v, torch.float32 if k in ("g1", "g2", "gq", "gk") else torch.bfloat16) for k, v in P.items()}
         del P
-        blk4 = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, precision=coda.PREC_MXFP4)
-        fo = blk4.alloc_forward(cfg.M, dev)
-        blk4.forward(params["x"], params["o"], fo)
-        reps = max(1, args.steps // 2)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            blk4.forward(params["x"], params["o"], fo)
-        b.record()
-        torch.cuda.synchronize()
-        ms4 = a.elapsed_time(b) / reps
-        fp4_fwd = {"block_fwd_ms": round(ms4, 4),
-                   "tflops": round(block_flops(cfg.M, cfg.D, cfg.F)[0] / (ms4 * 1e-3) / 1e12, 1),
-                   f"speedup_over_{precision}_fwd": round(head["block_fwd_ms"] / ms4, 4)}
-        del blk4, fo, params
+        for key, prec in (("mxfp4_block_forward", coda.PREC_MXFP4), ("mxfp6_e2m3_block_forward", coda.PREC_MXFP6_E2M3)):
+            blk = Block(params, cfg.D, cfg.F, seq_len=cfg.seq_len, precision=prec)
+            fo = blk.alloc_forward(cfg.M, dev)
+            blk.forward(params["x"], params["o"], fo)
+            reps = max(1, args.steps // 2)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                blk.forward(params["x"], params["o"], fo)
+            b.record()
+            torch.cuda.synchronize()
+            msq = a.elapsed_time(b) / reps
+            small_fwd[key] = {"block_fwd_ms": round(msq, 4),
+                              "tflops": round(block_flops(cfg.M, cfg.D, cfg.F)[0] / (msq * 1e-3) / 1e12, 1),
+                              f"speedup_over_{precision}_fwd": round(head["block_fwd_ms"] / msq, 4)}
+            del blk, fo
+        del params
         torch.cuda.empty_cache()
     mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
     ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
@@ -538,7 +540,8 @@ def main():
         "hidden_4096": h4096,
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,
-        "mxfp4_block_forward": fp4_fwd,
+        "mxfp4_block_forward": small_fwd.get("mxfp4_block_forward"),
+        "mxfp6_e2m3_block_forward": small_fwd.get("mxfp6_e2m3_block_forward"),
         "cross_entropy": ce,
         "mfma_loop": mloop,
     }

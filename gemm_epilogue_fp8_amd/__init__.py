@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E2M3, CODA_E3M2, CODA_E4M3, CODA_E8M0, CODA_F32, CODA_I32, PREC_BF16, PREC_FP8, PREC_MXFP8,
-                   PREC_MXFP4,
+                   PREC_MXFP4, PREC_MXFP6_E2M3, PREC_MXFP6_E3M2,
                    EPI_STORE_BF16, EPI_ACCUM_F32, EPI_ROW_SCALE, EPI_COL_SCALE, EPI_ADD_TILE,
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS, EPI_STORE_ROW_VEC,
                    EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU, EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION,
@@ -28,7 +28,8 @@ __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "ro
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
-           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4"]
+           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4",
+           "PREC_MXFP6_E2M3", "PREC_MXFP6_E3M2"]
 
 
 class CodaError(RuntimeError):
@@ -81,17 +82,23 @@ class Weight:
     def __init__(self, w: torch.Tensor, q_fwd=None, s_fwd=None, q_bwd=None, s_bwd=None):
         self.w, self.q_fwd, self.s_fwd, self.q_bwd, self.s_bwd = w, q_fwd, s_fwd, q_bwd, s_bwd
 
-    fp4 = False    # q_fwd holds E2M1 codes two a byte (prepare_mxfp4)
+    # dtype of the uint8 copies: CODA_E2M1X2 (prepare_mxfp4), CODA_E2M3 or
+    # CODA_E3M2 (prepare_mxfp6); None for the E4M3 copies
+    elem_dtype = None
+
+    @property
+    def fp4(self) -> bool:
+        return self.elem_dtype == CODA_E2M1X2
 
     def c(self) -> _lib.CodaWeight:
         cw = _lib.CodaWeight()
         cw.w = mat(self.w)
         cw.q_fwd, cw.s_fwd = mat(self.q_fwd), mat(self.s_fwd)
-        if self.fp4:
-            cw.q_fwd.dtype = CODA_E2M1X2
+        if self.elem_dtype is not None:
+            cw.q_fwd.dtype = self.elem_dtype
         cw.q_bwd, cw.s_bwd = mat(self.q_bwd), mat(self.s_bwd)
-        if self.fp4 and self.q_bwd is not None:
-            cw.q_bwd.dtype = CODA_E2M1X2
+        if self.elem_dtype is not None and self.q_bwd is not None:
+            cw.q_bwd.dtype = self.elem_dtype
         return cw
 
     def prepare_fp8(self):
@@ -126,11 +133,30 @@ class Weight:
         bytes with exponents along N_out, both in word layout."""
         K, N = self.w.shape
         dev = self.w.device
-        self.fp4 = True
+        self.elem_dtype = CODA_E2M1X2
         self.q_fwd = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
         self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
         if backward and N % 128 == 0:
             self.q_bwd = torch.empty((K, N // 2), dtype=torch.uint8, device=dev)
+            self.s_bwd = torch.empty(((N + 127) // 128, 4 * K), dtype=torch.uint8, device=dev)
+        else:
+            self.q_bwd = self.s_bwd = None
+        quantize_weight(self)
+        return self
+
+    def prepare_mxfp6(self, fmt: str = "e2m3", backward: bool = True):
+        """Allocate and fill the block-scaled FP6 copies in format fmt
+        ("e2m3" or "e3m2", coda_quantize_weight): q_fwd [N, K] bytes (32-value
+        blocks of 24 packed bytes and 8 of padding) with exponents along K_in
+        and, unless backward is False, q_bwd [K, N] with exponents along
+        N_out, both in word layout."""
+        K, N = self.w.shape
+        dev = self.w.device
+        self.elem_dtype = _FP6[fmt]
+        self.q_fwd = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        self.s_fwd = torch.empty(((K + 127) // 128, 4 * N), dtype=torch.uint8, device=dev)
+        if backward and N % 128 == 0:
+            self.q_bwd = torch.empty((K, N), dtype=torch.uint8, device=dev)
             self.s_bwd = torch.empty(((N + 127) // 128, 4 * K), dtype=torch.uint8, device=dev)
         else:
             self.q_bwd = self.s_bwd = None

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libcoda.so")
 CODA_BF16, CODA_F32, CODA_E4M3, CODA_I32, CODA_E8M0, CODA_E2M1X2 = 1, 2, 3, 4, 5, 6
 CODA_E2M3, CODA_E3M2 = 7, 8
 PREC_BF16, PREC_FP8, PREC_MXFP8, PREC_MXFP4 = 0, 1, 2, 3
+PREC_MXFP6_E2M3, PREC_MXFP6_E3M2 = 4, 5
 STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_DTYPE", 3: "CODA_ERR_SHAPE",
           4: "CODA_ERR_LAYOUT", 5: "CODA_ERR_ALIGN", 6: "CODA_ERR_WORKSPACE",
           7: "CODA_ERR_UNSUPPORTED", 8: "CODA_ERR_LAUNCH", 9: "CODA_ERR_VALUE"}

@@ -23,7 +23,7 @@ from typing import Dict
 
 import torch
 
-from . import (PREC_BF16, PREC_FP8, PREC_MXFP4, PREC_MXFP8, Weight, fold_gain, linear_qknorm_rope_bwd, linear_qknorm_rope_fwd,
+from . import (PREC_BF16, PREC_FP8, PREC_MXFP4, PREC_MXFP6_E2M3, PREC_MXFP6_E3M2, PREC_MXFP8, Weight, fold_gain, linear_qknorm_rope_bwd, linear_qknorm_rope_fwd,
                linear_rmsnorm_residual_bwd, linear_rmsnorm_residual_fwd, linear_swiglu_bwd, linear_swiglu_fwd,
                pack_gate_up, partials_cols, rope_table, row_sumsq)
 
@@ -66,6 +66,10 @@ class Block:
         elif self.precision == PREC_MXFP4:
             for w in self.w.values():
                 w.prepare_mxfp4()
+        elif self.precision in (PREC_MXFP6_E2M3, PREC_MXFP6_E3M2):
+            fmt = "e2m3" if self.precision == PREC_MXFP6_E2M3 else "e3m2"
+            for w in self.w.values():
+                w.prepare_mxfp6(fmt)
 
     def alloc_forward(self, M: int, device) -> Dict[str, torch.Tensor]:
         D, F = self.D, self.F

@@ -66,17 +66,20 @@ struct ActQ {
   float* amax;
   float* parts;
   bool mx;
-  bool fp4;      // MXFP4: E2M1 codes, two a byte (q.ld counts bytes)
+  // block-scaled element format as the scaled MFMA codes it: 0 = E4M3,
+  // 2 = E2M3 and 3 = E3M2 (FP6, a byte a value with the block padding),
+  // 4 = E2M1 (two codes a byte; q.ld counts bytes)
+  int elem;
   uint8_t* e;
   int64_t e_ld;
 };
-ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis, bool mx = false, bool fp4 = false) {
+ActQ take_act(Carver& cv, int64_t R, int64_t C, int axis, bool mx = false, int elem = 0) {
   ActQ a{};
   a.mx = mx;
-  a.fp4 = fp4;
+  a.elem = elem;
   if (mx) {
     const int64_t rows = axis == 1 ? R : C, L = axis == 1 ? C : R;
-    a.q.ld = ((fp4 ? L / 2 : L) + 15) / 16 * 16;
+    a.q.ld = ((elem == 4 ? L / 2 : L) + 15) / 16 * 16;
     a.q.q = cv.take<uint8_t>((size_t)rows * a.q.ld);
     a.q.s = nullptr;
     a.e_ld = 4 * rows;
@@ -112,14 +115,31 @@ coda_status run_quant_mx4(const void* X, int64_t ldx, int64_t R, int64_t C, int 
                        dim3(256), 0, s, x, ldx, (int)R, (int)C, Q, ldq, E, lde);
   return check_launch("quantize_mxfp4");
 }
+coda_status run_quant_mx6(const void* X, int64_t ldx, int64_t R, int64_t C, int axis, uint8_t* Q, int64_t ldq,
+                          uint8_t* E, int64_t lde, int f6, hipStream_t s) {
+  if (f6 != 2 && f6 != 3) return fail(CODA_ERR_VALUE, "quantize_mxfp6: element format %d", f6);
+  if (R == 0 || C == 0) return CODA_OK;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (axis == 1)
+    hipLaunchKernelGGL(quant_mx6_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, x, ldx, (int)R, (int)C,
+                       Q, ldq, E, lde, f6);
+  else
+    hipLaunchKernelGGL(quant_mx6_cols_t_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)),
+                       dim3(256), 0, s, x, ldx, (int)R, (int)C, Q, ldq, E, lde, f6);
+  return check_launch("quantize_mxfp6");
+}
 coda_status quant_act(const ActQ& a, const void* X, int64_t ldx, int64_t R, int64_t C, int axis, hipStream_t s) {
-  if (a.fp4) return run_quant_mx4(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
+  if (a.elem == 4) return run_quant_mx4(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
+  if (a.elem) return run_quant_mx6(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, a.elem, s);
   if (a.mx) return run_quant_mx(X, ldx, R, C, axis, a.q.q, a.q.ld, a.e, a.e_ld, s);
   return run_quant(X, ldx, R, C, axis, a.q.q, a.q.ld, a.q.s, a.amax, a.parts, s);
 }
-// A forward GEMM: MXFP4 operands go to their own instantiations (K in bytes)
-hipError_t launch_fwd(Prog p, int layout, bool fp8, bool fp4, GemmArgs g, const EpiArgs& e, hipStream_t s) {
-  return fp4 ? launch_gemm_mx4(p, g, e, s) : launch_gemm(p, layout, fp8, g, e, s);
+// A forward GEMM: MXFP4 and MXFP6 operands go to their own instantiations
+// (for MXFP4 K counts bytes); elem as in ActQ
+hipError_t launch_fwd(Prog p, int layout, bool fp8, int elem, GemmArgs g, const EpiArgs& e, hipStream_t s) {
+  if (elem == 4) return launch_gemm_mx4(p, g, e, s);
+  if (elem) return launch_gemm_mx6(p, elem, g, e, s);
+  return launch_gemm(p, layout, fp8, g, e, s);
 }
 // A GEMM at a functional precision: MXFP4 operands go to their own
 // instantiations, whose mainloop counts the contracted axis (K and a split's
@@ -130,6 +150,8 @@ hipError_t launch_prec(Prog p, int layout, int prec, GemmArgs g, const EpiArgs& 
     g.kchunk /= 2;
     return launch_gemm_mx4(p, g, e, s);
   }
+  if (prec == CODA_PREC_MXFP6_E2M3) return launch_gemm_mx6(p, 2, g, e, s);
+  if (prec == CODA_PREC_MXFP6_E3M2) return launch_gemm_mx6(p, 3, g, e, s);
   return launch_gemm(p, layout, prec != CODA_PREC_BF16, g, e, s);
 }
 // MXFP8 / MXFP4: the exponents of both operands go with the GEMM; the epilogue applies
@@ -188,18 +210,38 @@ coda_status check_weight(const coda_weight* wt, const char* name, int64_t K, int
       TRY(check_mat(&wt->q_bwd, "q_bwd", CODA_E2M1X2, K, N / 2));
       TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
     }
+  } else if (precision == CODA_PREC_MXFP6_E2M3 || precision == CODA_PREC_MXFP6_E3M2) {
+    // forward copy q_fwd [N, K] of the precision's FP6 dtype with blocks
+    // along K_in; the input-gradient copy q_bwd [K, N] (blocks along N_out)
+    // is optional as for MXFP4
+    const int dt = precision == CODA_PREC_MXFP6_E2M3 ? CODA_E2M3 : CODA_E3M2;
+    if (K % 128 != 0) return fail(CODA_ERR_SHAPE, "%s: MXFP6 needs K_in to be a multiple of 128", name);
+    TRY(check_mat(&wt->q_fwd, "q_fwd", dt, N, K));
+    TRY(check_scales(&wt->s_fwd, "s_fwd", N, K));
+    if (present(&wt->q_bwd)) {
+      if (N % 128 != 0) return fail(CODA_ERR_SHAPE, "%s: an MXFP6 backward copy needs N_out to be a multiple of 128", name);
+      TRY(check_mat(&wt->q_bwd, "q_bwd", dt, K, N));
+      TRY(check_scales(&wt->s_bwd, "s_bwd", K, N));
+    }
   } else if (precision != CODA_PREC_BF16) {
     return fail(CODA_ERR_VALUE, "precision %d", precision);
   }
   return CODA_OK;
 }
 coda_status check_precision(int p) {
-  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8 && p != CODA_PREC_MXFP4)
+  if (p != CODA_PREC_BF16 && p != CODA_PREC_FP8 && p != CODA_PREC_MXFP8 && p != CODA_PREC_MXFP4 &&
+      p != CODA_PREC_MXFP6_E2M3 && p != CODA_PREC_MXFP6_E3M2)
     return fail(CODA_ERR_VALUE, "precision %d", p);
   return CODA_OK;
 }
 coda_status check_precision_fwd(int p) { return check_precision(p); }
-bool is_mx(int p) { return p == CODA_PREC_MXFP8 || p == CODA_PREC_MXFP4; }
+bool is_mx(int p) {
+  return p == CODA_PREC_MXFP8 || p == CODA_PREC_MXFP4 || p == CODA_PREC_MXFP6_E2M3 || p == CODA_PREC_MXFP6_E3M2;
+}
+// the ActQ element code of a precision (0 for E4M3 and bf16)
+int prec_elem(int p) {
+  return p == CODA_PREC_MXFP4 ? 4 : p == CODA_PREC_MXFP6_E2M3 ? 2 : p == CODA_PREC_MXFP6_E3M2 ? 3 : 0;
+}
 
 
 // Forward-direction GEMM of an activation a [M, K] with a weight [K, N].
@@ -347,6 +389,17 @@ extern "C" coda_status coda_quantize_weight_workspace(const coda_weight* wt, siz
 extern "C" coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream) {
   if (!wt) return fail(CODA_ERR_NULL, "quantize_weight: NULL weight");
   const int64_t K = wt->w.rows, N = wt->w.cols;
+  if (wt->q_fwd.dtype == CODA_E2M3 || wt->q_fwd.dtype == CODA_E3M2) {
+    // MXFP6 copies of the q_fwd dtype's format: q_fwd [N, K] with blocks
+    // along K_in, the optional q_bwd [K, N] with blocks along N_out
+    const bool e23 = wt->q_fwd.dtype == CODA_E2M3;
+    TRY(check_weight(wt, "W", K, N, e23 ? CODA_PREC_MXFP6_E2M3 : CODA_PREC_MXFP6_E3M2));
+    TRY(run_quant_mx6(wt->w.ptr, wt->w.ld, K, N, 0, static_cast<uint8_t*>(wt->q_fwd.ptr), wt->q_fwd.ld,
+                      static_cast<uint8_t*>(wt->s_fwd.ptr), wt->s_fwd.ld, e23 ? 2 : 3, S(stream)));
+    if (!present(&wt->q_bwd)) return CODA_OK;
+    return run_quant_mx6(wt->w.ptr, wt->w.ld, K, N, 1, static_cast<uint8_t*>(wt->q_bwd.ptr), wt->q_bwd.ld,
+                         static_cast<uint8_t*>(wt->s_bwd.ptr), wt->s_bwd.ld, e23 ? 2 : 3, S(stream));
+  }
   if (wt->q_fwd.dtype == CODA_E2M1X2) {
     // MXFP4 forward copy: q_fwd [N, K / 2 bytes] with blocks along K_in
     TRY(check_weight(wt, "W", K, N, CODA_PREC_MXFP4));
@@ -921,16 +974,16 @@ extern "C" coda_status coda_linear_swiglu_fwd_workspace(int64_t M, int64_t K, in
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision != CODA_PREC_BF16) take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, K, 1, is_mx(precision), prec_elem(precision));
   *bytes = cv.off;
   return CODA_OK;
 }
 
 namespace {
 // Sizes and carves what an fp8 activation operand of the forward needs.
-size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx, bool fp4) {
+size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx, int elem) {
   Carver cv(nullptr);
-  take_act(cv, M, K, 1, mx, fp4);
+  take_act(cv, M, K, 1, mx, elem);
   return cv.off;
 }
 }  // namespace
@@ -947,7 +1000,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   Carver cv(size_only ? nullptr : ws);
   float* sumsq = cv.take<float>(M);
   ActQ aq{};
-  if (precision != CODA_PREC_BF16) aq = take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
+  if (precision != CODA_PREC_BF16) aq = take_act(cv, M, K, 1, is_mx(precision), prec_elem(precision));
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
@@ -966,7 +1019,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   const bool fp8 = precision != CODA_PREC_BF16;
   if (fp8) {
     TRY(quant_act(aq, x->ptr, x->ld, M, K, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, aq.fp4 ? K / 2 : K);
+    g = gemm_args(aq.q.q, aq.q.ld, Wgu->q_fwd.ptr, Wgu->q_fwd.ld, M, N, aq.elem == 4 ? K / 2 : K);
     e.rowscale = aq.q.s;
     e.colscale = fptr(&Wgu->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wgu->s_fwd);
@@ -977,8 +1030,8 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   }
   (void)F;
   if (act == Act::Sigmoid)
-    return launched(launch_fwd(Prog::Sigmoid, layout, fp8, aq.fp4, g, e, s), "linear_sigmoid_fwd");
-  return launched(launch_fwd(Prog::SwiGLU, layout, fp8, aq.fp4, g, e, s), "linear_swiglu_fwd");
+    return launched(launch_fwd(Prog::Sigmoid, layout, fp8, aq.elem, g, e, s), "linear_sigmoid_fwd");
+  return launched(launch_fwd(Prog::SwiGLU, layout, fp8, aq.elem, g, e, s), "linear_swiglu_fwd");
 }
 
 static coda_status swiglu_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, const coda_mat* out,
@@ -1013,7 +1066,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   (void)N;
-  *bytes = precision != CODA_PREC_BF16 ? fwd_fp8_bytes(M, K, is_mx(precision), precision == CODA_PREC_MXFP4) : 0;
+  *bytes = precision != CODA_PREC_BF16 ? fwd_fp8_bytes(M, K, is_mx(precision), prec_elem(precision)) : 0;
   return CODA_OK;
 }
 
@@ -1033,7 +1086,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
   Carver cv(ws);
   ActQ aq{};
   const bool fp8 = precision != CODA_PREC_BF16;
-  if (fp8) aq = take_act(cv, M, K, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
+  if (fp8) aq = take_act(cv, M, K, 1, is_mx(precision), prec_elem(precision));
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   EpiArgs e = epi0();
@@ -1045,7 +1098,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
   int layout;
   if (fp8) {
     TRY(quant_act(aq, a->ptr, a->ld, M, K, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, aq.fp4 ? K / 2 : K);
+    g = gemm_args(aq.q.q, aq.q.ld, W->q_fwd.ptr, W->q_fwd.ld, M, N, aq.elem == 4 ? K / 2 : K);
     e.rowscale = aq.q.s; e.colscale = fptr(&W->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &W->s_fwd);
     layout = LAYOUT_NT;
@@ -1053,7 +1106,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_fwd(const coda_mat* a, const
     g = gemm_args(a->ptr, a->ld, W->w.ptr, W->w.ld, M, N, K);
     layout = LAYOUT_NN;
   }
-  return launched(launch_fwd(prog, layout, fp8, aq.fp4, g, e, s), "linear_rmsnorm_residual_fwd");
+  return launched(launch_fwd(prog, layout, fp8, aq.elem, g, e, s), "linear_rmsnorm_residual_fwd");
 }
 
 extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t D, int32_t have_partials,
@@ -1062,7 +1115,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd_workspace(int64_t M, int64_t 
   Carver cv(nullptr);
   (void)have_partials;
   cv.take<float>(M);   // row sum of squares, or the merged partials
-  if (precision != CODA_PREC_BF16) take_act(cv, M, D, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
+  if (precision != CODA_PREC_BF16) take_act(cv, M, D, 1, is_mx(precision), prec_elem(precision));
   *bytes = cv.off;
   return CODA_OK;
 }
@@ -1096,7 +1149,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   float* sumsq = cv.take<float>(M);
   const bool fp8 = precision != CODA_PREC_BF16;
   ActQ aq{};
-  if (fp8) aq = take_act(cv, M, D, 1, is_mx(precision), precision == CODA_PREC_MXFP4);
+  if (fp8) aq = take_act(cv, M, D, 1, is_mx(precision), prec_elem(precision));
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
   if (!present(P)) TRY(row_sumsq_launch(x->ptr, x->ld, M, D, sumsq, s));
@@ -1119,7 +1172,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   int layout;
   if (fp8) {
     TRY(quant_act(aq, x->ptr, x->ld, M, D, 1, s));
-    g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, aq.fp4 ? D / 2 : D);
+    g = gemm_args(aq.q.q, aq.q.ld, Wqkv->q_fwd.ptr, Wqkv->q_fwd.ld, M, 3 * D, aq.elem == 4 ? D / 2 : D);
     e.rowscale = aq.q.s; e.colscale = fptr(&Wqkv->s_fwd);
     if (aq.mx) mx_args(&g, &e, aq.e, aq.e_ld, &Wqkv->s_fwd);
     layout = LAYOUT_NT;
@@ -1127,7 +1180,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
     g = gemm_args(x->ptr, x->ld, Wqkv->w.ptr, Wqkv->w.ld, M, 3 * D, D);
     layout = LAYOUT_NN;
   }
-  return launched(launch_fwd(Prog::QKRope, layout, fp8, aq.fp4, g, e, s), "linear_qknorm_rope_fwd");
+  return launched(launch_fwd(Prog::QKRope, layout, fp8, aq.elem, g, e, s), "linear_qknorm_rope_fwd");
 }
 
 // ======================================================================== functional backward
@@ -1238,7 +1291,8 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   // F is the width of the activation's output; the pre-activations are 2F
   // wide for SwiGLU (packed gate/up) and F wide for the sigmoid
   const int64_t N2 = act == Act::SwiGLU ? 2 * F : F;
-  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision);
+  const int elem = prec_elem(precision);
   if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   Carver cv(size_only ? nullptr : ws);
   const int nT2 = (int)coda_partials_cols(F);
@@ -1252,10 +1306,10 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   Bwd8 q8{};
   ActQ dYrow{};
   if (fp8) {
-    dYrow = take_act(cv, M, D, 1, mx, fp4);
-    q8.grow = take_act(cv, M, N2, 1, mx, fp4);
-    q8.xcol = take_act(cv, M, D, 0, mx, fp4);
-    q8.gcol = take_act(cv, M, N2, 0, mx, fp4);
+    dYrow = take_act(cv, M, D, 1, mx, elem);
+    q8.grow = take_act(cv, M, N2, 1, mx, elem);
+    q8.xcol = take_act(cv, M, D, 0, mx, elem);
+    q8.gcol = take_act(cv, M, N2, 0, mx, elem);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
@@ -1364,11 +1418,12 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd_workspace(int64_t M, int
                                                                   size_t* bytes) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   Carver cv(nullptr);
-  const bool mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  const bool mx = is_mx(precision);
+  const int elem = prec_elem(precision);
   if (precision != CODA_PREC_BF16) {
-    take_act(cv, M, N, 1, mx, fp4);
-    take_act(cv, M, K, 0, mx, fp4);
-    take_act(cv, M, N, 0, mx, fp4);
+    take_act(cv, M, N, 1, mx, elem);
+    take_act(cv, M, K, 0, mx, elem);
+    take_act(cv, M, N, 0, mx, elem);
   }
   const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   if (sp.n > 1) cv.take<float>((size_t)sp.n * K * N);
@@ -1388,14 +1443,15 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   TRY(check_weight(W, "W", K, N, precision));
   TRY(check_mat(da, "da", CODA_BF16, M, K, true));
   TRY(check_mat(dW, "dW", CODA_F32, K, N));
-  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision);
+  const int elem = prec_elem(precision);
   if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   Carver cv(ws);
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N, 1, mx, fp4);
-    q8.xcol = take_act(cv, M, K, 0, mx, fp4);
-    q8.gcol = take_act(cv, M, N, 0, mx, fp4);
+    q8.grow = take_act(cv, M, N, 1, mx, elem);
+    q8.xcol = take_act(cv, M, K, 0, mx, elem);
+    q8.gcol = take_act(cv, M, N, 0, mx, elem);
   }
   const Split sp = wgrad_split(K, N, M, mx ? 128 : 64);
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * K * N) : nullptr;
@@ -1429,7 +1485,8 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
                                const coda_mat* dW, const coda_mat* dg, const coda_mat* dgq, const coda_mat* dgk,
                                float beta, const coda_mat* dh_out, int precision, void* ws, size_t ws_bytes,
                                void* stream, int64_t M, int64_t D, bool size_only, size_t* bytes) {
-  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision), fp4 = precision == CODA_PREC_MXFP4;
+  const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision);
+  const int elem = prec_elem(precision);
   if (mx && M % 128 != 0) return fail(CODA_ERR_SHAPE, "MX backward: the token count must be a multiple of 128");
   const int64_t N3 = 3 * D;
   const int rows_per_wave = 4;
@@ -1450,9 +1507,9 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * D * N3) : nullptr;
   Bwd8 q8{};
   if (fp8) {
-    q8.grow = take_act(cv, M, N3, 1, mx, fp4);
-    q8.xcol = take_act(cv, M, D, 0, mx, fp4);
-    q8.gcol = take_act(cv, M, N3, 0, mx, fp4);
+    q8.grow = take_act(cv, M, N3, 1, mx, elem);
+    q8.xcol = take_act(cv, M, D, 0, mx, elem);
+    q8.gcol = take_act(cv, M, N3, 0, mx, elem);
   }
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));

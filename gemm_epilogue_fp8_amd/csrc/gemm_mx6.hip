@@ -2,7 +2,7 @@
 // bytes, B stored [N, K] bytes), a 32-value block packed into 24 bytes and 8
 // bytes of padding, each block with one E8M0 scale applied by the scaled
 // MFMA; the epilogue sees the dequantised fp32 product.  The programs are
-// the forward ones of the generic entry point.
+// those of the generic entry point and of the block's forward and backward.
 #include "launch.hpp"
 
 namespace coda {
@@ -21,6 +21,10 @@ static hipError_t launch_mx6(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s
     case Prog::SwiGLU: return launch_one<C, EpiSwiGLU<C>>(g, e, s);
     case Prog::Sigmoid: return launch_one<C, EpiSigmoid<C>>(g, e, s);
     case Prog::QKRope: return launch_one<C, EpiQKNormRope<C>>(g, e, s);
+    case Prog::DSwiGLU: return launch_one<C, EpiDSwiGLU<C>>(g, e, s);
+    case Prog::DSigmoid: return launch_one<C, EpiDSigmoid<C>>(g, e, s);
+    case Prog::NormCorr: return launch_one<C, EpiNormCorrection<C>>(g, e, s);
+    case Prog::WgradGain: return launch_one<C, EpiWgradGain<C>>(g, e, s);
     default: return hipErrorInvalidValue;
   }
 }

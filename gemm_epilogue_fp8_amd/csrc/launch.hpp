@@ -50,7 +50,7 @@ hipError_t launch_gemm_mx(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 hipError_t launch_gemm_mx4(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s);
 // MXFP6 operands (f6 = 2: E2M3, 3: E3M2; 32-value blocks of 24 packed bytes
 // and 8 bytes of padding, so g.K counts values and bytes alike): the forward
-// programs of the generic entry point
+// programs of the generic entry point and of the block
 hipError_t launch_gemm_mx6(Prog p, int f6, GemmArgs g, const EpiArgs& e, hipStream_t s);
 
 template <class Cfg, class Epi>

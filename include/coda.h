@@ -90,13 +90,18 @@ typedef enum coda_precision {
                           contracted axis (OCP MX), fp32 accumulate; every
                           contracted size (hidden, MLP width, tokens of a
                           backward) a multiple of 128 */
-  CODA_PREC_MXFP4 = 3  /* E2M1 operands (two a byte) with one E8M0 scale per 32
+  CODA_PREC_MXFP4 = 3, /* E2M1 operands (two a byte) with one E8M0 scale per 32
                           values of the contracted axis, fp32 accumulate; the
                           forward entry points need w, q_fwd (E2M1X2 [N, K/2])
                           and s_fwd (word layout), the backward ones also
                           q_bwd (E2M1X2 [K, N/2]) and s_bwd (blocks along
                           N_out); every contracted size a multiple of 128;
                           the cross-entropy entry points refuse it */
+  CODA_PREC_MXFP6_E2M3 = 4, /* FP6 E2M3 operands (CODA_E2M3, a byte a value with
+                               the block padding) under the same exponents;
+                               q_fwd [N, K] and q_bwd [K, N] of dtype
+                               CODA_E2M3, otherwise as MXFP4 */
+  CODA_PREC_MXFP6_E3M2 = 5  /* the same with FP6 E3M2 operands (CODA_E3M2) */
 } coda_precision;
 
 typedef struct coda_mat {
@@ -162,7 +167,9 @@ coda_status coda_quantize_e4m3(const coda_mat* X, int32_t axis, const coda_mat* 
  * selects: E4M3 with fp32 scales (per output channel, Q transposed, and per
  * input channel), MXFP8 (E8M0 scales: blocks along K_in for q_fwd [N, K],
  * along N_out for q_bwd [K, N]) or MXFP4 (q_fwd of dtype CODA_E2M1X2: the same
- * blocks, two codes a byte; q_bwd is optional, NULL for a forward-only weight). */
+ * blocks, two codes a byte; q_bwd is optional, NULL for a forward-only weight)
+ * or MXFP6 (q_fwd of dtype CODA_E2M3 or CODA_E3M2: the same blocks in that
+ * format, a byte a value; q_bwd optional as for MXFP4). */
 coda_status coda_quantize_weight_workspace(const coda_weight* wt, size_t* bytes);
 coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_bytes, void* stream);
 
@@ -414,7 +421,11 @@ coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const 
  *   CODA_PREC_MXFP4  E2M1 operands under the same exponents; the weight
  *                    carries the forward copy and, for the backward entry
  *                    points, the input-gradient copy (a weight without it is
- *                    refused with CODA_ERR_NULL there).
+ *                    refused with CODA_ERR_NULL there);
+ *   CODA_PREC_MXFP6_E2M3, CODA_PREC_MXFP6_E3M2  FP6 operands of that format
+ *                    under the same exponents, every activation quantised in
+ *                    the weight's format; weight copies as for MXFP4 with the
+ *                    FP6 dtype (one byte a value).
  * Activations are quantised per call into the workspace (the *_workspace
  * queries size it for the given precision).  The cross-entropy entry points
  * take CODA_PREC_BF16 only (CODA_ERR_UNSUPPORTED otherwise). */

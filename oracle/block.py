@@ -59,11 +59,14 @@ def mm(A, B, fp8=False):
     product of the dequantised operands is taken in float64, then float32.
 
     With fp8 = "mx4", the same with MXFP4 operands (E2M1 elements,
-    oracle/mx_small.py).
+    oracle/mx_small.py), and with fp8 = "mx6_e2m3" / "mx6_e3m2" with MXFP6
+    operands of that element format.
     """
-    if fp8 == "mx4":
-        PA, eA = mx_small.quantize(np.asarray(A, np.float32), "e2m1")
-        PB, eB = mx_small.quantize(np.ascontiguousarray(np.asarray(B, np.float32).T), "e2m1")
+    small = {"mx4": "e2m1", "mx6_e2m3": "e2m3", "mx6_e3m2": "e3m2"}
+    if fp8 in small:
+        fmt = small[fp8]
+        PA, eA = mx_small.quantize(np.asarray(A, np.float32), fmt)
+        PB, eB = mx_small.quantize(np.ascontiguousarray(np.asarray(B, np.float32).T), fmt)
         return mx_small.matmul_nt(PA, eA, PB, eB).astype(np.float32)
     if fp8 == "mx":
         PA, eA = mx.quantize(np.asarray(A, np.float32))

@@ -199,7 +199,7 @@ def test_functional_validation():
     st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 0, None, 0, None)
     assert st == 6
     # bad precision
-    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 5, None, 0, None)
+    st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 9, None, 0, None)
     assert st == 9
     # fp8 without quantised copies
     st = L.coda_linear_swiglu_fwd(C.byref(x), None, C.byref(w), 1e-6, C.byref(out), None, None, 1, None, 0, None)
@@ -412,3 +412,33 @@ def test_mxfp4_gemm_validation_codes():
               fake(BF, M, N)) == 3                                             # 256 values need 2 word rows
     assert gm(fake(E2, M, 128), fake(E8, 2, 4 * M), fake(E2, N, 128), fake(E8, 2, 4 * N),
               fake(BF, M, N + 8)) == 3                                         # D shape
+
+
+def test_mxfp6_weight_validation_codes():
+    """The MXFP6 precisions check the weight copies before any launch: q_fwd
+    [N, K] of the precision's FP6 dtype with exponents of N rows along K_in
+    (K_in a multiple of 128), the optional q_bwd [K, N] likewise along N_out."""
+    L = g.lib()
+    BF, E8 = _lib.CODA_BF16, _lib.CODA_E8M0
+    E23, E32 = _lib.CODA_E2M3, _lib.CODA_E3M2
+    M, K, N = 64, 256, 128
+
+    def weight(qdt, qf=(N, K), qb=(K, N), K_=K):
+        w = _lib.CodaWeight()
+        w.w = fake(BF, K_, N)
+        w.q_fwd, w.s_fwd = fake(qdt, *qf), fake(E8, (K_ + 127) // 128, 4 * N)
+        w.q_bwd, w.s_bwd = fake(qdt, *qb), fake(E8, (N + 127) // 128, 4 * K_)
+        return w
+
+    def call(w, prec, K_=K):
+        a, res, out = fake(BF, M, K_), fake(BF, M, N), fake(BF, M, N)
+        return L.coda_linear_rmsnorm_residual_fwd(C.byref(a), C.byref(w), C.byref(res), C.byref(out), None, prec,
+                                                  None, 0, None)
+
+    for prec, dt, other in ((_lib.PREC_MXFP6_E2M3, E23, E32), (_lib.PREC_MXFP6_E3M2, E32, E23)):
+        assert call(weight(dt), prec) == 6                                # valid weight; stops at the workspace
+        assert call(weight(other), prec) == 2                             # the other FP6 format
+        assert call(weight(_lib.CODA_E2M1X2, qf=(N, K // 2)), prec) == 2   # E2M1 copies
+        assert call(weight(dt, qf=(N, K // 2)), prec) == 3                # FP6 is a byte a value
+        assert call(weight(dt, qb=(K, N // 2)), prec) == 3                # input-gradient copy shape
+        assert call(weight(dt, K_=192), prec, K_=192) == 3                # K_in not a multiple of 128

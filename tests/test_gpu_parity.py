@@ -686,10 +686,10 @@ def test_block_backward_split_k(shape, seed):
     assert_bf16("dx", b["dx"], B["dx"])
 
 
-@pytest.mark.parametrize("precision,fmt", [(2, "mx"), (3, "mx4")])
+@pytest.mark.parametrize("precision,fmt", [(2, "mx"), (3, "mx4"), (4, "mx6_e2m3"), (5, "mx6_e3m2")])
 def test_mx_residual_backward_split_k_same_inputs(precision, fmt):
     """Block-scaled backward of a residual linear from identical seeded
-    inputs (MXFP8 and MXFP4): da = d_out W^T through the weight's
+    inputs (MXFP8, MXFP4, MXFP6): da = d_out W^T through the weight's
     input-gradient copy, and dW = a^T d_out with both operands quantised
     along the 4096 tokens, which the library cuts into 4 slices of 1024
     (split K over whole exponent words) and adds in order onto a seeded fp32
@@ -702,7 +702,12 @@ def test_mx_residual_backward_split_k_same_inputs(precision, fmt):
     W = rand_bf16(rng, K, N, std=K ** -0.5)
     prior = ci.fp32_prior((K, N), 13)
     wt = coda.Weight(bf(W))
-    wt.prepare_mxfp8() if precision == coda.PREC_MXFP8 else wt.prepare_mxfp4()
+    if precision == coda.PREC_MXFP8:
+        wt.prepare_mxfp8()
+    elif precision == coda.PREC_MXFP4:
+        wt.prepare_mxfp4()
+    else:
+        wt.prepare_mxfp6(fmt[4:])
     dW = f32(prior)
     da = torch.empty((M, K), dtype=BF, device=DEV)
     coda.linear_rmsnorm_residual_bwd(bf(dout), bf(a), wt, dW, da=da, beta=1.0, precision=precision)
@@ -887,5 +892,35 @@ def test_block_mxfp4_forward_backward():
                  dWd=(b["dWd"], ob.mm(g32(f["a"].T), c["dY"], "mx4")),
                  dWo=(b["dWo"], ob.mm(g32(c["o"].T), g32(b["dh1"]), "mx4")),
                  dWqkv=(b["dWqkv"], c["g1"][:, None] * ob.mm(g32(c["x"].T), g32(b["dht_qkv"]), "mx4")))
+    for k, (got, ref) in stage.items():
+        assert_bf16(k + " (stage)", got, ref, tol=FP8_TOL, norm_rel=2e-3)
+
+
+@pytest.mark.parametrize("precision,mode", [(coda.PREC_MXFP6_E2M3, "mx6_e2m3"), (coda.PREC_MXFP6_E3M2, "mx6_e3m2")])
+def test_block_mxfp6_forward_backward(precision, mode):
+    """The whole block, forward and backward, with every GEMM operand in
+    MXFP6 of one element format (weights with forward and input-gradient
+    copies, activations and weight-gradient operands quantised per call),
+    against the oracle's chained evaluation in the same format: bf16 outputs
+    within the fp8 rule, gradients within 2e-2 norm-wise, and every
+    weight-gradient stage from the device's own bf16 operands within the fp8
+    rule element by element."""
+    from tests.helpers import FP8_TOL
+    shape = ci.BlockShape(M=256, D=256, F=384, seq_len=128)
+    P, f, b = _run_block(shape, 10 + precision, precision=precision)
+    F = ob.block_forward_contract(P, shape, fp8=mode)
+    B = ob.block_backward_contract(P, F, shape, fp8=mode)
+    check_block_mx(f, b, F, B)
+    c = {k: np.asarray(v, np.float32) for k, v in P.items()}
+    g32 = lambda a: np.ascontiguousarray(np.asarray(a, np.float32))
+    dg_, du_ = unpack_gu(b["dht_gu"])
+    dht_gu = np.concatenate([dg_, du_], axis=1)
+    Fw = c["Wg"].shape[1]
+    acc = ob.mm(g32(f["h1"].T), g32(dht_gu), mode)
+    dWg, dWu = unpack_gu(b["dWgu"])
+    stage = dict(dWg=(dWg, c["g2"][:, None] * acc[:, :Fw]), dWu=(dWu, c["g2"][:, None] * acc[:, Fw:]),
+                 dWd=(b["dWd"], ob.mm(g32(f["a"].T), c["dY"], mode)),
+                 dWo=(b["dWo"], ob.mm(g32(c["o"].T), g32(b["dh1"]), mode)),
+                 dWqkv=(b["dWqkv"], c["g1"][:, None] * ob.mm(g32(c["x"].T), g32(b["dht_qkv"]), mode)))
     for k, (got, ref) in stage.items():
         assert_bf16(k + " (stage)", got, ref, tol=FP8_TOL, norm_rel=2e-3)

@@ -145,14 +145,17 @@ def test_matmul_triple_loop():
             assert C[m, n] == pytest.approx(ref, rel=1e-12, abs=1e-12)
 
 
-def test_block_gemm_mx4_mode_axes():
-    """oracle.block.mm(A, B, "mx4") quantises A along its rows and B down its
-    columns: operands that are already MXFP4 along those axes come back as
-    the exact product; quantising B along its rows instead changes it."""
+@pytest.mark.parametrize("mode,fmt", [("mx4", "e2m1"), ("mx6_e2m3", "e2m3"), ("mx6_e3m2", "e3m2")])
+def test_block_gemm_mx_small_mode_axes(mode, fmt):
+    """oracle.block.mm(A, B, mode) quantises A along its rows and B down its
+    columns in the mode's element format: operands that are already MX in
+    that format along those axes come back as the exact product; quantising
+    B along its rows instead changes it."""
     from oracle import block as ob
     rng = np.random.default_rng(11)
-    vals = ms.decode(all_codes("e2m1"), "e2m1")
-    top = vals[np.abs(vals) >= 4]
+    vals = ms.decode(all_codes(fmt), fmt)
+    emax = ms.fmt_params(fmt)[3]
+    top = vals[np.abs(vals) >= 2.0 ** emax]     # a block maximum in the top binade keeps the exponent
 
     def mx4_rows(rows, nblocks):
         X = np.empty((rows, 32 * nblocks))
@@ -164,9 +167,9 @@ def test_block_gemm_mx4_mode_axes():
         return X.astype(np.float32)
 
     A = mx4_rows(5, 3)
-    B = np.ascontiguousarray(mx4_rows(64, 3).T)       # [96, 64], MXFP4 down its columns
-    got = ob.mm(A, B, "mx4")
+    B = np.ascontiguousarray(mx4_rows(64, 3).T)       # [96, 64], MX down its columns
+    got = ob.mm(A, B, mode)
     ref = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
     np.testing.assert_array_equal(got, ref)
-    P, e = ms.quantize(B, "e2m1")
+    P, e = ms.quantize(B, fmt)
     assert not np.array_equal(ms.dequantize(P, e), B.astype(np.float64))
