@@ -395,14 +395,12 @@ coda_status coda_quantize_mxfp6(const coda_mat* X, int32_t axis, const coda_mat*
  * matrices.
  * MXFP4: with A of dtype CODA_E2M1X2 the operands are E2M1 (as written by
  * coda_quantize_mxfp4), A [M, K / 2 bytes] and B [N, K / 2 bytes], same
- * exponent layout and K rule (K counts values); the epilogue program is one
- * of STORE_BF16, ACCUM_F32, ROW_SCALE COL_SCALE STORE_BF16, ADD_TILE
- * STORE_BF16 [ROW_SUMSQ_PARTIAL] and the SWIGLU, SIGMOID and QKNORM_ROPE
- * chains.
+ * exponent layout and K rule (K counts values), and every chain of the MX
+ * column.
  * MXFP6: with A of dtype CODA_E2M3 or CODA_E3M2 (as written by
  * coda_quantize_mxfp6) the operands are FP6 of that format, A [M, K] and
  * B [N, K] in bytes, B of the same dtype (CODA_ERR_DTYPE otherwise), same
- * exponent layout and K rule, and the same programs as MXFP4. */
+ * exponent layout and K rule, and every chain of the MX column. */
 coda_status coda_gemm_mx(const coda_epi_program* prog, const coda_mat* A, const coda_mat* SA,
                          const coda_mat* B, const coda_mat* SB, const coda_mat* D, const coda_mat* aux,
                          uint32_t n_aux, void* ws, size_t ws_bytes, void* stream);
