@@ -342,3 +342,51 @@ def test_chain_mxfp8_norm_correction():
     c = r * Tp.sum(axis=0, dtype=np.float32) / np.float32(N)
     ref = nm.bf16(ob.mm(A, B, "mx") - c[:, None] * u + res)
     assert_bf16("out", to_np(out), ref, tol=FP8_TOL)
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e2m3", "e3m2"])
+def test_chain_mx_small_backward_chains(fmt):
+    """Two backward chains of the MX column on MXFP4 and MXFP6 operands
+    through the descriptor: NORM_CORRECTION ADD_TILE STORE_BF16, and
+    SCALE_DEV WGRAD_GAIN accumulating onto a prior (both operands quantised
+    along the contracted axis), against the oracle's product in the same
+    format."""
+    rng = np.random.default_rng(117)
+    mode = {"e2m1": "mx4", "e2m3": "mx6_e2m3", "e3m2": "mx6_e3m2"}[fmt]
+
+    def q(X, axis):
+        return coda.quantize_mxfp4(bf(X), axis) if fmt == "e2m1" else coda.quantize_mxfp6(bf(X), axis, fmt)
+
+    def gemm(prog, QA, SA, QB, SB, D, aux):
+        if fmt == "e2m1":
+            return coda.gemm_mx4(prog, QA, SA, QB, SB, D, aux=aux)
+        return coda.gemm_mx6(prog, fmt, QA, SA, QB, SB, D, aux=aux)
+
+    M, K, N = 300, 384, 264
+    A, B = rnd(rng, M, K, std=0.1), rnd(rng, K, N, std=K ** -0.5)
+    u, res = rnd(rng, M, N), rnd(rng, M, N, std=0.1)
+    r = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    Tp = (0.1 * rng.standard_normal((3, M))).astype(np.float32)
+    QA, SA = q(A, 1)
+    QB, SB = q(B, 0)
+    out = empty(M, N, dt=BF)
+    gemm([(coda.EPI_NORM_CORRECTION, (0, 1, 2), 0.0), (coda.EPI_ADD_TILE, 3, 0.0), (coda.EPI_STORE_BF16, 0, 0.0)],
+         QA, SA, QB, SB, out, [bf(u), f32(r), f32(Tp), bf(res)])
+    # weight-gradient form: D[Kin, N] += s g[k] (X^T G)[k, n] over Mt tokens
+    Mt, Kin = 256, 264
+    X, G = rnd(rng, Mt, Kin), rnd(rng, Mt, N, std=0.1)
+    W = rnd(rng, Kin, N, std=Kin ** -0.5)
+    g = (1 + 0.1 * rng.standard_normal(Kin)).astype(np.float32)
+    prior = rng.standard_normal((Kin, N)).astype(np.float32)
+    s = np.float32(0.5)
+    QX, SX = q(X, 0)          # [Kin, Mt]: blocks along the tokens
+    QG, SG = q(G, 0)          # [N, Mt]
+    Dw, P = f32(prior), empty(coda.partials_cols(N), Kin)
+    gemm([(coda.EPI_SCALE_DEV, 0, 0.0), (coda.EPI_WGRAD_GAIN, (1, 2, 3), 1.0)], QX, SX, QG, SG, Dw,
+         [f32([s]), bf(W), f32(g), P])
+    torch.cuda.synchronize()
+    c = r * Tp.sum(axis=0, dtype=np.float32) / np.float32(N)
+    assert_bf16("norm correction", to_np(out), nm.bf16(ob.mm(A, B, mode) - c[:, None] * u + res), tol=FP8_TOL)
+    acc = ob.mm(X.T.copy(), G, mode)
+    assert_grad("dW", to_np(Dw), prior + s * (g[:, None] * acc), rel=2e-3)
+    assert_grad("gain partials", to_np(P), ob.tile_partials(s * (W.astype(np.float64) * acc), 256), rel=2e-3)
