@@ -251,12 +251,25 @@ __device__ __forceinline__ void put_tile(const Ctx<Cfg>& c, const Acc<Cfg>& acc)
 template <class Cfg>
 struct RowBlock {
   uint2 v[Cfg::TN][4];
+  // Rows m0 + lrow(i) of the bf16 matrix at base (row stride ld elements),
+  // this lane's columns, through a buffer resource that starts at the tile's
+  // first row: one offset register for the block, the column steps in the
+  // instructions' immediate offsets.  Rows past M read as zero; columns
+  // past N read what lies there (other rows or padding, inside the
+  // resource), which reaches only positions that are never stored or are
+  // masked out of the reductions.
   __device__ __forceinline__ void load(const void* base, int64_t ld, const Ctx<Cfg>& c, int i) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + (int64_t)c.rowc(i) * ld;
+    const char* b = static_cast<const char*>(base) + (int64_t)c.m0 * ld * 2;
+    const int64_t bytes = ((int64_t)(c.M - c.m0 - 1) * ld + c.N) * 2;
+    const auto rs = make_rsrc(b, bytes > 0 ? (uint64_t)bytes : 0);
+    const uint32_t off = (uint32_t)(((int64_t)c.lrow(i) * ld + c.col(0, 0)) * 2);
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[j][q] = *reinterpret_cast<const uint2*>(p + c.colc(j, q));
+      for (int q = 0; q < 4; ++q) {
+        const i32x2_t w = buf_load8(rs, off + (uint32_t)(64 * j + 16 * q));   // 32 j + 8 q columns on
+        v[j][q] = uint2{(uint32_t)w[0], (uint32_t)w[1]};
+      }
   }
   __device__ __forceinline__ f32x4_t get(int j, int q) const {
     return f32x4_t{bf_lo(v[j][q].x), bf_hi(v[j][q].x), bf_lo(v[j][q].y), bf_hi(v[j][q].y)};
