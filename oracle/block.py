@@ -299,43 +299,53 @@ def ce_backward_contract(h, W, labels, lse, n_valid, dloss=1.0, ignore_index=-10
 # --------------------------------------------------------------------------- RMSNorm -> Linear -> sigmoid
 # A pre-norm sigmoid layer h = RMSNorm(x, g) W, a = sigmoid(h), read by a
 # consumer linear a Wn whose output joins the residual stream: the elementwise
-# map of the CODA paper's §3.1 item 1 in place of SwiGLU.
-def sigmoid_layer_canonical(x, g, W, Wn, dY, eps, dres=None, dt=np.float64):
+# map of the CODA paper's §3.1 item 1 in place of SwiGLU.  The same layer with
+# a = GELU(h) (act="gelu") is the second elementwise activation.
+_ACTS = {"sigmoid": (ops.sigmoid, ops.sigmoid_grad), "gelu": (ops.gelu, ops.gelu_grad)}
+
+
+def sigmoid_layer_canonical(x, g, W, Wn, dY, eps, dres=None, dt=np.float64, act: str = "sigmoid"):
     """Canonical evaluation and gradients: given dY = dL/d(a Wn), da = dY Wn^T,
-    dh = da sigmoid'(h), dxn = dh W^T, dW = xn^T dh, then the RMSNorm
-    backward for (dx, dg); dx also receives dres."""
+    dh = da act'(h), dxn = dh W^T, dW = xn^T dh, then the RMSNorm backward
+    for (dx, dg); dx also receives dres.  act is "sigmoid" or "gelu"."""
     x, g, W, Wn, dY = (np.asarray(t, dt) for t in (x, g, W, Wn, dY))
+    f, df = _ACTS[act]
     xn = ops.rms_norm(x, g, eps)
     h = xn @ W
-    a = ops.sigmoid(h)
+    a = f(h)
     da = dY @ Wn.T
-    dh = da * a * (dt(1) - a)
+    dh = da * a * (dt(1) - a) if act == "sigmoid" else da * df(h)
     dx, dg = ops.rms_norm_bwd(x, g, eps, dh @ W.T)
     if dres is not None:
         dx = dx + np.asarray(dres, dt)
     return dict(h=h, a=a, dx=dx, dW=xn.T @ dh, dg=dg)
 
 
-def sigmoid_forward_contract(x, g, W, eps, fp8: bool = False, rnd: Callable = nm.bf16, dt=np.float32):
-    """W~ = rnd(g W), r = inv_rms(x), h = r (x W~); stored a = rnd(sigmoid(h))
+def sigmoid_forward_contract(x, g, W, eps, fp8: bool = False, rnd: Callable = nm.bf16, dt=np.float32,
+                             act: str = "sigmoid"):
+    """W~ = rnd(g W), r = inv_rms(x), h = r (x W~); stored a = rnd(act(h))
     and the saved pre-activation rnd(h)."""
     x = np.asarray(x, dt)
     Wt = rnd(np.asarray(g, dt)[:, None] * np.asarray(W, dt))
     r = ops.inv_rms(x, eps)
     h = r[:, None] * mm(x, Wt, fp8)
-    return dict(a=rnd(ops.sigmoid(h)), h=rnd(h), r=r, Wt=Wt)
+    return dict(a=rnd(_ACTS[act][0](h)), h=rnd(h), r=r, Wt=Wt)
 
 
 def sigmoid_backward_contract(x, g, W, Wn, dY, F, eps, dres=None, fp8: bool = False, rnd: Callable = nm.bf16,
-                              priors=None, beta: float = 0.0, dt=np.float32):
-    """With the saved h and s = sigmoid(h): dh~ = rnd(r (dY Wn^T) s (1 - s)),
-    T = sum_j dh~ h, dx = rnd(dh~ W~^T - (r T / D) x + dres),
+                              priors=None, beta: float = 0.0, dt=np.float32, act: str = "sigmoid"):
+    """With the saved h: dh~ = rnd(r (dY Wn^T) act'(h)) (for the sigmoid
+    act'(h) = s (1 - s), s = sigmoid(h)), T = sum_j dh~ h,
+    dx = rnd(dh~ W~^T - (r T / D) x + dres),
     dW = beta prior + g (x^T dh~), dg = beta prior + sum_n W (x^T dh~)."""
     x, g, W, Wn, dY = (np.asarray(t, dt) for t in (x, g, W, Wn, dY))
     r = np.asarray(F["r"], dt)[:, None]
     h = np.asarray(F["h"], dt)
-    s = ops.sigmoid(h)
-    dht = rnd(r * mm(dY, Wn.T, fp8) * s * (dt(1) - s))
+    if act == "sigmoid":
+        s = ops.sigmoid(h)
+        dht = rnd(r * mm(dY, Wn.T, fp8) * s * (dt(1) - s))
+    else:
+        dht = rnd(r * mm(dY, Wn.T, fp8) * _ACTS[act][1](h))
     T = np.sum(dht * h, axis=1, dtype=dt)[:, None]
     dx = mm(dht, F["Wt"].T, fp8) - r * T / dt(x.shape[1]) * x
     if dres is not None:

@@ -8,7 +8,9 @@ Sources: the CODA paper (arXiv 2605.19269), §3.1 (the five epilogue primitive
 classes: maps, vector loads, tile loads, tile reductions, state transitions)
 and §3.2.1 (RMSNorm written as the per-row inverse RMS factor r times the
 gain); the RMSNorm, SwiGLU, RoPE and softmax cross-entropy definitions are the
-standard ones that the paper's reparameterisations start from.
+standard ones that the paper's reparameterisations start from, and GELU is
+the exact (error-function) form of Hendrycks and Gimpel's definition, the
+second elementwise activation map beside the sigmoid.
 """
 from __future__ import annotations
 
@@ -49,6 +51,36 @@ def rms_norm_bwd(u, g, eps: float, dy):
 def sigmoid(t):
     one = t.dtype.type(1.0)
     return one / (one + np.exp(-t))
+
+
+def sigmoid_grad(t):
+    """sigmoid'(t) = s (1 - s) with s = sigmoid(t)."""
+    s = sigmoid(t)
+    return s * (t.dtype.type(1.0) - s)
+
+
+# ----------------------------------------------------------------- GELU
+def gelu(t):
+    """GELU(t) = t Phi(t), Phi the standard normal CDF written through the
+    error function: Phi(t) = (1 + erf(t / sqrt 2)) / 2 (the exact form, not
+    the tanh approximation)."""
+    t = np.asarray(t)
+    half = t.dtype.type(0.5)
+    return half * t * (t.dtype.type(1.0) + _erf(t / t.dtype.type(np.sqrt(2.0))))
+
+
+def gelu_grad(t):
+    """GELU'(t) = Phi(t) + t phi(t), phi(t) = exp(-t^2 / 2) / sqrt(2 pi)."""
+    t = np.asarray(t)
+    one, half = t.dtype.type(1.0), t.dtype.type(0.5)
+    cdf = half * (one + _erf(t / t.dtype.type(np.sqrt(2.0))))
+    pdf = np.exp(-half * t * t) / t.dtype.type(np.sqrt(2.0 * np.pi))
+    return cdf + t * pdf
+
+
+def _erf(t):
+    from scipy.special import erf
+    return erf(t).astype(t.dtype)
 
 
 def silu(t):

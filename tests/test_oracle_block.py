@@ -379,3 +379,53 @@ def test_sigmoid_special_values():
     np.testing.assert_allclose(s[::-1], 1 - s, atol=1e-15)
     h = 1e-6
     assert abs((ops.sigmoid(np.array(h)) - ops.sigmoid(np.array(-h))) / (2 * h) - 0.25) < 1e-9
+
+
+# ------------------------------------------------------------------ RMSNorm -> Linear -> GELU
+def test_gelu_layer_canonical_matches_torch_autograd():
+    """The GELU layer against torch's exact (erf) GELU under float64 autograd."""
+    x, g, W, Wn, dY, dres = _sigmoid_tiny(33)
+    C = ob.sigmoid_layer_canonical(x, g, W, Wn, dY, 1e-6, dres=dres, act="gelu")
+    X, G_, W_ = (torch.tensor(a, requires_grad=True) for a in (x, g, W))
+    r = torch.rsqrt((X * X).mean(dim=1, keepdim=True) + 1e-6)
+    h = (X * r * G_) @ W_
+    a = torch.nn.functional.gelu(h, approximate="none")
+    np.testing.assert_allclose(C["a"], a.detach().numpy(), rtol=1e-13, atol=1e-15)
+    ((a @ torch.tensor(Wn) * torch.tensor(dY)).sum() + (X * torch.tensor(dres)).sum()).backward()
+    np.testing.assert_allclose(C["dx"], X.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dW"], W_.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(C["dg"], G_.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_gelu_reparameterised_equals_canonical():
+    x, g, W, Wn, dY, dres = _sigmoid_tiny(34)
+    C = ob.sigmoid_layer_canonical(x, g, W, Wn, dY, 1e-6, dres=dres, act="gelu")
+    F = ob.sigmoid_forward_contract(x, g, W, 1e-6, rnd=_ident, dt=np.float64, act="gelu")
+    np.testing.assert_allclose(F["a"], C["a"], rtol=1e-13, atol=1e-15)
+    B = ob.sigmoid_backward_contract(x, g, W, Wn, dY, F, 1e-6, dres=dres, rnd=_ident, dt=np.float64, act="gelu")
+    for k in ("dx", "dW", "dg"):
+        np.testing.assert_allclose(B[k], C[k], rtol=1e-10, atol=1e-14, err_msg=k)
+
+
+def test_gelu_special_values():
+    """GELU(t) = t Phi(t): GELU(0) = 0 with slope 1/2; GELU(1) = Phi(1) and
+    GELU(-1) = Phi(1) - 1 from the normal table; GELU(t) - GELU(-t) = t, so
+    GELU'(t) + GELU'(-t) = 1; GELU(t) -> t for large t and -> 0 for large -t."""
+    phi1 = 0.8413447460685429     # standard normal CDF at 1
+    assert ops.gelu(np.array(0.0)) == 0.0
+    assert abs(ops.gelu_grad(np.array(0.0)) - 0.5) < 1e-16
+    assert abs(ops.gelu(np.array(1.0)) - phi1) < 1e-15
+    assert abs(ops.gelu(np.array(-1.0)) - (phi1 - 1.0)) < 1e-15
+    t = np.linspace(-6, 6, 121)
+    np.testing.assert_allclose(ops.gelu(t) - ops.gelu(-t), t, atol=1e-14)
+    np.testing.assert_allclose(ops.gelu_grad(t) + ops.gelu_grad(-t), 1.0, atol=1e-14)
+    assert abs(ops.gelu(np.array(10.0)) - 10.0) < 1e-12 and abs(ops.gelu(np.array(-10.0))) < 1e-12
+    e = 1e-6    # the derivative against central differences of the function
+    np.testing.assert_allclose(ops.gelu_grad(t), (ops.gelu(t + e) - ops.gelu(t - e)) / (2 * e), atol=1e-8)
+    assert ops.gelu(np.float32([1.5])).dtype == np.float32
+
+
+def test_sigmoid_grad_matches_differences():
+    t = np.linspace(-8, 8, 81)
+    e = 1e-6
+    np.testing.assert_allclose(ops.sigmoid_grad(t), (ops.sigmoid(t + e) - ops.sigmoid(t - e)) / (2 * e), atol=1e-9)
