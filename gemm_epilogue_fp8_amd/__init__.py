@@ -22,13 +22,14 @@ from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E2M3, CODA_E3M2, CODA_E4M3, CODA
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS, EPI_STORE_ROW_VEC,
                    EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU, EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION,
                    EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL, EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV,
-                   EPI_DEQUANT_E4M3)
+                   EPI_DEQUANT_E4M3, EPI_GELU, EPI_DGELU)
 
 __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "rope_table", "row_sumsq",
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
-           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4",
+           "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "linear_sigmoid_fwd", "linear_sigmoid_bwd",
+           "linear_gelu_fwd", "linear_gelu_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4",
            "PREC_MXFP6_E2M3", "PREC_MXFP6_E3M2"]
 
 
@@ -503,29 +504,46 @@ def linear_rmsnorm_cross_entropy_bwd(y, r, W, W_unfolded, g, labels, lse, n_vali
     return dy, dW, dg
 
 
-# ---------------------------------------------------------------- RMSNorm -> Linear -> sigmoid
-def linear_sigmoid_fwd(x, W, eps, out, sumsq_partials=None, save_h=None, r_out=None, precision: int = PREC_BF16):
+# ---------------------------------------------------------------- RMSNorm -> Linear -> sigmoid | GELU
+def _map_fwd(act, x, W, eps, out, sumsq_partials, save_h, r_out, precision):
     L = lib()
     wc = W if isinstance(W, Weight) else Weight(W)
     M, K = x.shape
-    ws, n = _ws_call(L.coda_linear_sigmoid_fwd_workspace, (M, K, int(sumsq_partials is not None), precision),
-                     x.device)
-    _check(L.coda_linear_sigmoid_fwd(_p(x), _p(sumsq_partials), C.byref(wc.c()), eps, _p(out), _p(save_h),
-                                     _p(r_out), precision, ws, n, _stream()))
+    ws, n = _ws_call(getattr(L, f"coda_linear_{act}_fwd_workspace"),
+                     (M, K, int(sumsq_partials is not None), precision), x.device)
+    _check(getattr(L, f"coda_linear_{act}_fwd")(_p(x), _p(sumsq_partials), C.byref(wc.c()), eps, _p(out),
+                                               _p(save_h), _p(r_out), precision, ws, n, _stream()))
     return out
 
 
-def linear_sigmoid_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta=0.0, dh_out=None,
-                       precision: int = PREC_BF16):
+def _map_bwd(act, dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision):
     L = lib()
     wn = Wn if isinstance(Wn, Weight) else Weight(Wn)
     wc = W if isinstance(W, Weight) else Weight(W)
     M, D = dY.shape
-    ws, n = _ws_call(L.coda_linear_sigmoid_bwd_workspace, (M, D, wn.w.shape[0], precision), dY.device)
-    _check(L.coda_linear_sigmoid_bwd(_p(dY), C.byref(wn.c()), _p(saved_h), _p(r), _p(u), C.byref(wc.c()),
-                                     _p(W_unfolded), _p(g), _p(dres), _p(du), _p(dW), _p(dg), beta, _p(dh_out),
-                                     precision, ws, n, _stream()))
+    ws, n = _ws_call(getattr(L, f"coda_linear_{act}_bwd_workspace"), (M, D, wn.w.shape[0], precision), dY.device)
+    _check(getattr(L, f"coda_linear_{act}_bwd")(_p(dY), C.byref(wn.c()), _p(saved_h), _p(r), _p(u),
+                                               C.byref(wc.c()), _p(W_unfolded), _p(g), _p(dres), _p(du), _p(dW),
+                                               _p(dg), beta, _p(dh_out), precision, ws, n, _stream()))
     return du, dW, dg
+
+
+def linear_sigmoid_fwd(x, W, eps, out, sumsq_partials=None, save_h=None, r_out=None, precision: int = PREC_BF16):
+    return _map_fwd("sigmoid", x, W, eps, out, sumsq_partials, save_h, r_out, precision)
+
+
+def linear_sigmoid_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta=0.0, dh_out=None,
+                       precision: int = PREC_BF16):
+    return _map_bwd("sigmoid", dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision)
+
+
+def linear_gelu_fwd(x, W, eps, out, sumsq_partials=None, save_h=None, r_out=None, precision: int = PREC_BF16):
+    return _map_fwd("gelu", x, W, eps, out, sumsq_partials, save_h, r_out, precision)
+
+
+def linear_gelu_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta=0.0, dh_out=None,
+                    precision: int = PREC_BF16):
+    return _map_bwd("gelu", dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision)
 
 
 def probe_mfma_loop(dtype: int, blocks: int, iters: int, out=None):

@@ -25,6 +25,7 @@ EPI_ADD_TILE, EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS = 5, 
 EPI_STORE_ROW_VEC, EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU = 9, 10, 11, 12
 EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION, EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL = 13, 14, 15, 16
 EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV, EPI_DEQUANT_E4M3 = 17, 18, 19, 20, 21
+EPI_GELU, EPI_DGELU = 22, 23
 MAX_EPI_OPS = 8
 
 
@@ -94,6 +95,10 @@ SIGNATURES = {
     "coda_linear_sigmoid_fwd": [M_, M_, W_, f32, M_, M_, M_, i32, vp, sz, vp],
     "coda_linear_sigmoid_bwd_workspace": [i64, i64, i64, i32, szp],
     "coda_linear_sigmoid_bwd": [M_, W_, M_, M_, M_, W_, M_, M_, M_, M_, M_, M_, f32, M_, i32, vp, sz, vp],
+    "coda_linear_gelu_fwd_workspace": [i64, i64, i32, i32, szp],
+    "coda_linear_gelu_fwd": [M_, M_, W_, f32, M_, M_, M_, i32, vp, sz, vp],
+    "coda_linear_gelu_bwd_workspace": [i64, i64, i64, i32, szp],
+    "coda_linear_gelu_bwd": [M_, W_, M_, M_, M_, W_, M_, M_, M_, M_, M_, M_, f32, M_, i32, vp, sz, vp],
     "coda_linear_rmsnorm_cross_entropy_fwd_workspace": [i64, i64, i64, i32, i32, szp],
     "coda_linear_rmsnorm_cross_entropy_fwd": [M_, M_, W_, f32, M_, i32, M_, M_, M_, M_, M_, M_, i32, vp, sz, vp],
     "coda_linear_rmsnorm_cross_entropy_bwd_workspace": [i64, i64, i64, i64, i32, szp],

@@ -446,6 +446,7 @@ enum : uint16_t {
   OP_DOT = CODA_EPI_ROW_DOT_PARTIAL, OP_NORMCORR = CODA_EPI_NORM_CORRECTION, OP_WGRAD = CODA_EPI_WGRAD_GAIN,
   OP_CELSE = CODA_EPI_CE_LSE_PARTIAL, OP_CEGRAD = CODA_EPI_CE_GRAD, OP_SIGMOID = CODA_EPI_SIGMOID,
   OP_DSIGMOID = CODA_EPI_DSIGMOID, OP_SDEV = CODA_EPI_SCALE_DEV, OP_DEQUANT = CODA_EPI_DEQUANT_E4M3,
+  OP_GELU = CODA_EPI_GELU, OP_DGELU = CODA_EPI_DGELU,
 };
 
 struct PatEl { uint16_t op, alt; bool opt; };
@@ -467,9 +468,11 @@ const ChainDef kChains[] = {
     {Prog::Resid, 2, {R(OP_ADD), R(OP_STORE)}},
     {Prog::SwiGLU, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_SWIGLU), R(OP_STORE)}},
     {Prog::Sigmoid, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_SIGMOID), R(OP_STORE)}},
+    {Prog::Gelu, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_GELU), R(OP_STORE)}},
     {Prog::QKRope, 5, {R(OP_ROW, OP_RMS), O(OP_ROWOUT), O(OP_SAVE), R(OP_QKROPE), R(OP_STORE)}},
     {Prog::DSwiGLU, 4, {R(OP_DSWIGLU), R(OP_ROW), R(OP_STORE), R(OP_DOT)}},
     {Prog::DSigmoid, 4, {R(OP_DSIGMOID), R(OP_ROW), R(OP_STORE), R(OP_DOT)}},
+    {Prog::DGelu, 4, {R(OP_DGELU), R(OP_ROW), R(OP_STORE), R(OP_DOT)}},
     {Prog::NormCorr, 4, {R(OP_NORMCORR), O(OP_SDEV), O(OP_ADD), R(OP_STORE)}},
     {Prog::WgradGain, 2, {O(OP_SDEV), R(OP_WGRAD)}},
     {Prog::CrossEntropyNorm, 3, {R(OP_RMS), O(OP_ROWOUT), R(OP_CELSE)}},
@@ -648,6 +651,7 @@ coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, i
       break;
     case Prog::SwiGLU:
     case Prog::Sigmoid:
+    case Prog::Gelu:
     case Prog::QKRope: {
       TRY(row_factor(at[0]));
       TRY(row_out(at[1], &e.rowvec_out));
@@ -655,7 +659,7 @@ coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, i
         if (N % 64 != 0) return fail(CODA_ERR_SHAPE, "%s: SWIGLU needs N %% 64 == 0 (packed gate/up)", who);
         d->out_cols = N / 2;
         TRY(save(at[2], N));
-      } else if (c->prog == Prog::Sigmoid) {
+      } else if (c->prog == Prog::Sigmoid || c->prog == Prog::Gelu) {
         TRY(save(at[2], N));
       } else {
         if (N % 384 != 0) return fail(CODA_ERR_SHAPE, "%s: QKNORM_ROPE needs N = 3 x a multiple of 128", who);
@@ -679,7 +683,8 @@ coda_status decode_program(const coda_epi_program* prog, int64_t M, int64_t N, i
       break;
     }
     case Prog::DSwiGLU:
-    case Prog::DSigmoid: {
+    case Prog::DSigmoid:
+    case Prog::DGelu: {
       const bool sw = c->prog == Prog::DSwiGLU;
       if (sw && N % 32 != 0) return fail(CODA_ERR_SHAPE, "%s: DSWIGLU needs N %% 32 == 0", who);
       TRY(tile(at[0]->slot, "saved pre-activation", CODA_BF16, M, sw ? 2 * N : N, &m));
@@ -989,8 +994,8 @@ size_t fwd_fp8_bytes(int64_t M, int64_t K, bool mx, int elem) {
 }  // namespace
 
 // The pre-norm activation layers: SwiGLU over packed gate/up columns, or an
-// elementwise sigmoid.
-enum class Act { SwiGLU, Sigmoid };
+// elementwise sigmoid or GELU.
+enum class Act { SwiGLU, Sigmoid, Gelu };
 
 static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const coda_weight* Wgu, float eps,
                                    const coda_mat* out, const coda_mat* save, const coda_mat* r_out, int precision,
@@ -1031,6 +1036,7 @@ static coda_status swiglu_fwd_impl(const coda_mat* x, const coda_mat* P, const c
   (void)F;
   if (act == Act::Sigmoid)
     return launched(launch_fwd(Prog::Sigmoid, layout, fp8, aq.elem, g, e, s), "linear_sigmoid_fwd");
+  if (act == Act::Gelu) return launched(launch_fwd(Prog::Gelu, layout, fp8, aq.elem, g, e, s), "linear_gelu_fwd");
   return launched(launch_fwd(Prog::SwiGLU, layout, fp8, aq.elem, g, e, s), "linear_swiglu_fwd");
 }
 
@@ -1289,7 +1295,7 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
                                    void* stream, int64_t M, int64_t D, int64_t F, bool size_only, size_t* bytes,
                                    Act act = Act::SwiGLU) {
   // F is the width of the activation's output; the pre-activations are 2F
-  // wide for SwiGLU (packed gate/up) and F wide for the sigmoid
+  // wide for SwiGLU (packed gate/up) and F wide for the elementwise maps
   const int64_t N2 = act == Act::SwiGLU ? 2 * F : F;
   const bool fp8 = precision != CODA_PREC_BF16, mx = is_mx(precision);
   const int elem = prec_elem(precision);
@@ -1326,7 +1332,8 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
     GemmArgs g;
     if (fp8) TRY(quant_act(dYrow, dY->ptr, dY->ld, M, D, 1, s));
     dgrad_args(fp8, &dYrow, dY->ptr, dY->ld, Wd, M, F, D, &g, &e);
-    TRY(launched(launch_prec(act == Act::SwiGLU ? Prog::DSwiGLU : Prog::DSigmoid, LAYOUT_NT, precision, g, e, s),
+    const Prog back = act == Act::SwiGLU ? Prog::DSwiGLU : act == Act::Sigmoid ? Prog::DSigmoid : Prog::DGelu;
+    TRY(launched(launch_prec(back, LAYOUT_NT, precision, g, e, s),
                  "swiglu_bwd: activation backward"));
   }
   // collapse the T partials (F / 256 of them) to one per row
@@ -2084,9 +2091,9 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
   return sum_partials_launch(dgp, nT, (int)D, beta, static_cast<float*>(dg->ptr), s);
 }
 
-// ======================================================================== RMSNorm -> Linear -> sigmoid
-static coda_status sigmoid_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* W, const coda_mat* out,
-                                     const coda_mat* save, const coda_mat* r_out, int precision) {
+// ======================================================================== RMSNorm -> Linear -> sigmoid | GELU
+static coda_status map_fwd_check(const coda_mat* x, const coda_mat* P, const coda_weight* W, const coda_mat* out,
+                                 const coda_mat* save, const coda_mat* r_out, int precision) {
   TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, K = x->cols;
@@ -2102,35 +2109,25 @@ static coda_status sigmoid_fwd_check(const coda_mat* x, const coda_mat* P, const
   return CODA_OK;
 }
 
-extern "C" coda_status coda_linear_sigmoid_fwd_workspace(int64_t M, int64_t K, int32_t have_partials,
-                                                         int32_t precision, size_t* bytes) {
-  return coda_linear_swiglu_fwd_workspace(M, K, have_partials, precision, bytes);
-}
-
-extern "C" coda_status coda_linear_sigmoid_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
-                                               float eps, const coda_mat* out, const coda_mat* save_h,
-                                               const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
-                                               void* stream) {
-  TRY(sigmoid_fwd_check(x, sumsq_partials, W, out, save_h, r_out, precision));
+static coda_status map_fwd(const coda_mat* x, const coda_mat* P, const coda_weight* W, float eps, const coda_mat* out,
+                           const coda_mat* save_h, const coda_mat* r_out, int32_t precision, void* ws,
+                           size_t ws_bytes, void* stream, Act act) {
+  TRY(map_fwd_check(x, P, W, out, save_h, r_out, precision));
   if (!(eps >= 0.0f)) return fail(CODA_ERR_VALUE, "eps must be >= 0");
-  return swiglu_fwd_impl(x, sumsq_partials, W, eps, out, save_h, r_out, precision, ws, ws_bytes, stream, false,
-                         nullptr, Act::Sigmoid);
+  return swiglu_fwd_impl(x, P, W, eps, out, save_h, r_out, precision, ws, ws_bytes, stream, false, nullptr, act);
 }
 
-extern "C" coda_status coda_linear_sigmoid_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision,
-                                                         size_t* bytes) {
+static coda_status map_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision, size_t* bytes, Act act) {
   if (!bytes) return fail(CODA_ERR_NULL, "NULL bytes");
   return swiglu_bwd_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                         nullptr, nullptr, 0.0f, nullptr, precision, nullptr, 0, nullptr, M, D, N, true, bytes,
-                         Act::Sigmoid);
+                         nullptr, nullptr, 0.0f, nullptr, precision, nullptr, 0, nullptr, M, D, N, true, bytes, act);
 }
 
-extern "C" coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
-                                               const coda_mat* r, const coda_mat* u, const coda_weight* W,
-                                               const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
-                                               const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
-                                               const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
-                                               void* stream) {
+static coda_status map_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h, const coda_mat* r,
+                           const coda_mat* u, const coda_weight* W, const coda_mat* W_unfolded, const coda_mat* g,
+                           const coda_mat* dres, const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                           const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes, void* stream,
+                           Act act) {
   TRY(check_precision(precision));
   TRY(check_mat(dY, "dY", CODA_BF16, -1, -1));
   const int64_t M = dY->rows, D = dY->cols;
@@ -2149,5 +2146,59 @@ extern "C" coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_we
   TRY(check_vec(dg, "dg", CODA_F32, D));
   TRY(check_mat(dh_out, "dh_out", CODA_BF16, M, N, true));
   return swiglu_bwd_impl(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision, ws,
-                         ws_bytes, stream, M, D, N, false, nullptr, Act::Sigmoid);
+                         ws_bytes, stream, M, D, N, false, nullptr, act);
+}
+
+extern "C" coda_status coda_linear_sigmoid_fwd_workspace(int64_t M, int64_t K, int32_t have_partials,
+                                                         int32_t precision, size_t* bytes) {
+  return coda_linear_swiglu_fwd_workspace(M, K, have_partials, precision, bytes);
+}
+
+extern "C" coda_status coda_linear_sigmoid_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
+                                               float eps, const coda_mat* out, const coda_mat* save_h,
+                                               const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  return map_fwd(x, sumsq_partials, W, eps, out, save_h, r_out, precision, ws, ws_bytes, stream, Act::Sigmoid);
+}
+
+extern "C" coda_status coda_linear_sigmoid_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision,
+                                                         size_t* bytes) {
+  return map_bwd_workspace(M, D, N, precision, bytes, Act::Sigmoid);
+}
+
+extern "C" coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
+                                               const coda_mat* r, const coda_mat* u, const coda_weight* W,
+                                               const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
+                                               const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                                               const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  return map_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision, ws, ws_bytes,
+                 stream, Act::Sigmoid);
+}
+
+extern "C" coda_status coda_linear_gelu_fwd_workspace(int64_t M, int64_t K, int32_t have_partials, int32_t precision,
+                                                      size_t* bytes) {
+  return coda_linear_swiglu_fwd_workspace(M, K, have_partials, precision, bytes);
+}
+
+extern "C" coda_status coda_linear_gelu_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
+                                            float eps, const coda_mat* out, const coda_mat* save_h,
+                                            const coda_mat* r_out, int32_t precision, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  return map_fwd(x, sumsq_partials, W, eps, out, save_h, r_out, precision, ws, ws_bytes, stream, Act::Gelu);
+}
+
+extern "C" coda_status coda_linear_gelu_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision,
+                                                      size_t* bytes) {
+  return map_bwd_workspace(M, D, N, precision, bytes, Act::Gelu);
+}
+
+extern "C" coda_status coda_linear_gelu_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
+                                            const coda_mat* r, const coda_mat* u, const coda_weight* W,
+                                            const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
+                                            const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                                            const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  return map_bwd(dY, Wn, saved_h, r, u, W, W_unfolded, g, dres, du, dW, dg, beta, dh_out, precision, ws, ws_bytes,
+                 stream, Act::Gelu);
 }

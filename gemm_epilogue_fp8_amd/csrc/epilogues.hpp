@@ -585,10 +585,30 @@ struct EpiSwiGLU {
   }
 };
 
-// --- row scale r from partials (or a given vector), then the sigmoid map:
-// h = r acc, out = sigmoid(h), optional save of h (for the backward).
-template <class Cfg>
-struct EpiSigmoid {
+// Elementwise maps of the pre-norm activation layer: the value f(h) and the
+// backward factor da f'(h).
+struct MapSigmoid {
+  __device__ static float f(float h) { return sigmoidf_(h); }
+  __device__ static float back(float da, float h) {
+    const float sg = sigmoidf_(h);
+    return da * sg * (1.0f - sg);
+  }
+};
+// GELU(h) = h Phi(h) with the normal CDF Phi(h) = (1 + erf(h / sqrt 2)) / 2
+// (the exact form); GELU'(h) = Phi(h) + h phi(h), phi the normal density.
+struct MapGelu {
+  __device__ static float f(float h) { return 0.5f * h * (1.0f + erff(h * 0.70710678118654752f)); }
+  __device__ static float back(float da, float h) {
+    const float cdf = 0.5f * (1.0f + erff(h * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __expf(-0.5f * h * h);
+    return da * (cdf + h * pdf);
+  }
+};
+
+// --- row scale r from partials (or a given vector), then an elementwise map:
+// h = r acc, out = f(h), optional save of h (for the backward).
+template <class Cfg, class Map>
+struct EpiActMap {
   struct Pro { RowPartials<Cfg> rp; };
   __device__ static void issue(const EpiArgs& e, const Ctx<Cfg>& c, Pro& p) {
     p.rp.issue(e.row_partials, e.n_row_partials, c);
@@ -608,7 +628,7 @@ struct EpiSigmoid {
           const f32x4_t h = frag(acc, i, j, q) * r;
           f32x4_t a;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) a[t] = sigmoidf_(h[t]);
+          for (int t = 0; t < 4; ++t) a[t] = Map::f(h[t]);
           S::put4(s, c.lrow(i), c.lcol(j, q), a);
           set_frag(acc, i, j, q, h);
         }
@@ -835,12 +855,12 @@ struct EpiDSwiGLU {
   }
 };
 
-// --- sigmoid backward in the epilogue of da = dY Wn^T: with the saved h
-// (copied into the staging tile) and s = sigmoid(h), dh~ = bf16(r da s (1 - s))
-// replaces h in place and is stored; T[tn][m] = sum over the tile of dh~ h is
-// written as row partials.
-template <class Cfg>
-struct EpiDSigmoid {
+// --- backward of the elementwise map in the epilogue of da = dY Wn^T: with
+// the saved h (copied into the staging tile), dh~ = bf16(r da f'(h)) replaces
+// h in place and is stored; T[tn][m] = sum over the tile of dh~ h is written
+// as row partials.
+template <class Cfg, class Map>
+struct EpiActMapBack {
   struct Pro {};
   __device__ static void issue(const EpiArgs&, const Ctx<Cfg>&, Pro&) {}
   __device__ static void apply(const EpiArgs& e, const Ctx<Cfg>& c, Acc<Cfg>& acc, Pro&) {
@@ -872,10 +892,7 @@ struct EpiDSigmoid {
           const f32x4_t da = frag(acc, i, j, q);
           f32x4_t d;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float sg = sigmoidf_(h[t]);
-            d[t] = r * (da[t] * sg * (1.0f - sg));
-          }
+          for (int t = 0; t < 4; ++t) d[t] = r * Map::back(da[t], h[t]);
           const uint2 pk = pack_bf4(d);
           const f32x4_t dr = unpack_bf4(pk);   // the stored values
           if (m < c.M && c.col(j, q) < c.N) part[i] += dr[0] * h[0] + dr[1] * h[1] + dr[2] * h[2] + dr[3] * h[3];
@@ -889,6 +906,11 @@ struct EpiDSigmoid {
     stage_store_bf<Cfg, Cfg::BM, Cfg::BN>(s, c.tid, MatBF{static_cast<uint16_t*>(e.out), e.ld_out, c.m0, c.n0, c.M, c.N});
   }
 };
+
+template <class Cfg> using EpiSigmoid = EpiActMap<Cfg, MapSigmoid>;
+template <class Cfg> using EpiDSigmoid = EpiActMapBack<Cfg, MapSigmoid>;
+template <class Cfg> using EpiGelu = EpiActMap<Cfg, MapGelu>;
+template <class Cfg> using EpiDGelu = EpiActMapBack<Cfg, MapGelu>;
 
 // --- RMSNorm-backward correction: out = acc - c[m] u[m,n] + res[m,n] with
 // c = r T / D, T finished from the row partials in the prologue.

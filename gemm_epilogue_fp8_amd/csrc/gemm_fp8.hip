@@ -13,9 +13,11 @@ hipError_t launch_gemm_fp8(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) 
     case Prog::Resid: return launch_one<Cfg8, EpiLinear<Cfg8, EL_TILEADD>>(g, e, s);
     case Prog::SwiGLU: return launch_one<Cfg8, EpiSwiGLU<Cfg8>>(g, e, s);
     case Prog::Sigmoid: return launch_one<Cfg8, EpiSigmoid<Cfg8>>(g, e, s);
+    case Prog::Gelu: return launch_one<Cfg8, EpiGelu<Cfg8>>(g, e, s);
     case Prog::QKRope: return launch_one<Cfg8, EpiQKNormRope<Cfg8>>(g, e, s);
     case Prog::DSwiGLU: return launch_one<Cfg8, EpiDSwiGLU<Cfg8>>(g, e, s);
     case Prog::DSigmoid: return launch_one<Cfg8, EpiDSigmoid<Cfg8>>(g, e, s);
+    case Prog::DGelu: return launch_one<Cfg8, EpiDGelu<Cfg8>>(g, e, s);
     case Prog::NormCorr: return launch_one<Cfg8, EpiNormCorrection<Cfg8>>(g, e, s);
     case Prog::WgradGain: return launch_one<Cfg8, EpiWgradGain<Cfg8>>(g, e, s);
     case Prog::CrossEntropy: return launch_one<Cfg8, EpiCrossEntropy<Cfg8>>(g, e, s);

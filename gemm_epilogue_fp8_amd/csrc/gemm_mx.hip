@@ -15,9 +15,11 @@ hipError_t launch_gemm_mx(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
     case Prog::Resid: return launch_one<CfgMX, EpiLinear<CfgMX, EL_TILEADD>>(g, e, s);
     case Prog::SwiGLU: return launch_one<CfgMX, EpiSwiGLU<CfgMX>>(g, e, s);
     case Prog::Sigmoid: return launch_one<CfgMX, EpiSigmoid<CfgMX>>(g, e, s);
+    case Prog::Gelu: return launch_one<CfgMX, EpiGelu<CfgMX>>(g, e, s);
     case Prog::QKRope: return launch_one<CfgMX, EpiQKNormRope<CfgMX>>(g, e, s);
     case Prog::DSwiGLU: return launch_one<CfgMX, EpiDSwiGLU<CfgMX>>(g, e, s);
     case Prog::DSigmoid: return launch_one<CfgMX, EpiDSigmoid<CfgMX>>(g, e, s);
+    case Prog::DGelu: return launch_one<CfgMX, EpiDGelu<CfgMX>>(g, e, s);
     case Prog::NormCorr: return launch_one<CfgMX, EpiNormCorrection<CfgMX>>(g, e, s);
     case Prog::WgradGain: return launch_one<CfgMX, EpiWgradGain<CfgMX>>(g, e, s);
     default: return hipErrorInvalidValue;

@@ -17,9 +17,11 @@ hipError_t launch_gemm_mx4(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) 
     case Prog::Resid: return launch_one<CfgMX4, EpiLinear<CfgMX4, EL_TILEADD>>(g, e, s);
     case Prog::SwiGLU: return launch_one<CfgMX4, EpiSwiGLU<CfgMX4>>(g, e, s);
     case Prog::Sigmoid: return launch_one<CfgMX4, EpiSigmoid<CfgMX4>>(g, e, s);
+    case Prog::Gelu: return launch_one<CfgMX4, EpiGelu<CfgMX4>>(g, e, s);
     case Prog::QKRope: return launch_one<CfgMX4, EpiQKNormRope<CfgMX4>>(g, e, s);
     case Prog::DSwiGLU: return launch_one<CfgMX4, EpiDSwiGLU<CfgMX4>>(g, e, s);
     case Prog::DSigmoid: return launch_one<CfgMX4, EpiDSigmoid<CfgMX4>>(g, e, s);
+    case Prog::DGelu: return launch_one<CfgMX4, EpiDGelu<CfgMX4>>(g, e, s);
     case Prog::NormCorr: return launch_one<CfgMX4, EpiNormCorrection<CfgMX4>>(g, e, s);
     case Prog::WgradGain: return launch_one<CfgMX4, EpiWgradGain<CfgMX4>>(g, e, s);
     default: return hipErrorInvalidValue;

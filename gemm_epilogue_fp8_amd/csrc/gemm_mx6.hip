@@ -20,9 +20,11 @@ static hipError_t launch_mx6(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s
     case Prog::Resid: return launch_one<C, EpiLinear<C, EL_TILEADD>>(g, e, s);
     case Prog::SwiGLU: return launch_one<C, EpiSwiGLU<C>>(g, e, s);
     case Prog::Sigmoid: return launch_one<C, EpiSigmoid<C>>(g, e, s);
+    case Prog::Gelu: return launch_one<C, EpiGelu<C>>(g, e, s);
     case Prog::QKRope: return launch_one<C, EpiQKNormRope<C>>(g, e, s);
     case Prog::DSwiGLU: return launch_one<C, EpiDSwiGLU<C>>(g, e, s);
     case Prog::DSigmoid: return launch_one<C, EpiDSigmoid<C>>(g, e, s);
+    case Prog::DGelu: return launch_one<C, EpiDGelu<C>>(g, e, s);
     case Prog::NormCorr: return launch_one<C, EpiNormCorrection<C>>(g, e, s);
     case Prog::WgradGain: return launch_one<C, EpiWgradGain<C>>(g, e, s);
     default: return hipErrorInvalidValue;

@@ -16,6 +16,7 @@ hipError_t launch_gemm_nn(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
     case Prog::CrossEntropy: return launch_one<CfgNN, EpiCrossEntropy<CfgNN>>(g, e, s);
     case Prog::CrossEntropyG: return launch_one<CfgNN, EpiCrossEntropyGrad<CfgNN>>(g, e, s);
     case Prog::Sigmoid: return launch_one<CfgNN, EpiSigmoid<CfgNN>>(g, e, s);
+    case Prog::Gelu: return launch_one<CfgNN, EpiGelu<CfgNN>>(g, e, s);
     case Prog::CrossEntropyNorm: return launch_one<CfgNN, EpiCrossEntropy<CfgNN, true>>(g, e, s);
     case Prog::CrossEntropyGNorm: return launch_one<CfgNN, EpiCrossEntropyGrad<CfgNN, true>>(g, e, s);
     default: return hipErrorInvalidValue;

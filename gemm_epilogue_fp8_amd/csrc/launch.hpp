@@ -28,6 +28,8 @@ enum class Prog : int {
   CrossEntropyGNorm,  // z = r acc (given r), G~ = r (exp(z - lse) - onehot), T partials
   Sigmoid,        // row scale (finished from partials or given), sigmoid, store, save h
   DSigmoid,       // sigmoid backward with the saved h, r scale, store dh~, T partials
+  Gelu,           // as Sigmoid with the GELU map
+  DGelu,          // as DSigmoid with the GELU derivative
 };
 
 constexpr int kBM = 256, kBN = 256;

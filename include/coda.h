@@ -227,6 +227,10 @@ coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_byte
  *                                 lse 1 x M                                  rows with a label in [0, N), else 0
  *   SIGMOID                P1     -                                          value = sigmoid(value)
  *   DSIGMOID               P3+P1  slot: bf16 [M, N] saved h                  value = da s (1 - s), s = sigmoid(h)
+ *   GELU                   P1     -                                          value = GELU(value) = value Phi(value),
+ *                                                                            Phi the normal CDF (erf form)
+ *   DGELU                  P3+P1  slot: bf16 [M, N] saved h                  value = da (Phi(h) + h phi(h)), phi the
+ *                                                                            normal density
  *   SCALE_DEV              P2     slot: fp32 1 x 1 device scalar             value *= s
  *   DEQUANT_E4M3           P2     slot: fp32 1 x M; slot2: fp32 1 x N        E4M3 operands: value = acc sA[m] sB[n]
  *
@@ -240,13 +244,13 @@ coda_status coda_quantize_weight(const coda_weight* wt, void* ws, size_t ws_byte
  *   ADD_TILE STORE_BF16 [ROW_SUMSQ_PARTIAL]                 NN E4M3 MX        residual + next-norm partials
  *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] SWIGLU STORE_BF16
  *                                                           NN E4M3 MX        D [M, N/2], N % 64 == 0
- *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] SIGMOID STORE_BF16
+ *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] SIGMOID|GELU STORE_BF16
  *                                                           NN E4M3 MX
  *   ROW_SCALE|ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] [SAVE_PRE] QKNORM_ROPE STORE_BF16
  *                                                           NN E4M3 MX        D [M, N] = q | k | v, N % 384 == 0;
  *                                                                             SAVE_PRE [M, 2N/3] = q | k before the norm
  *   DSWIGLU ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL            NT E4M3 MX        N % 32 == 0
- *   DSIGMOID ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL           NT E4M3 MX
+ *   DSIGMOID|DGELU ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL     NT E4M3 MX
  *   NORM_CORRECTION [SCALE_DEV] [ADD_TILE] STORE_BF16       NT E4M3 MX        value = s (acc - c u) + Z
  *   [SCALE_DEV] WGRAD_GAIN                                  TN E4M3 MX        s scales D's new term and P
  *   ROW_RMS_FROM_PARTIALS [STORE_ROW_VEC] CE_LSE_PARTIAL    NN                z = r acc (final norm folded)
@@ -282,7 +286,9 @@ typedef enum coda_epi_opcode {
   CODA_EPI_SIGMOID = 18,
   CODA_EPI_DSIGMOID = 19,
   CODA_EPI_SCALE_DEV = 20,
-  CODA_EPI_DEQUANT_E4M3 = 21
+  CODA_EPI_DEQUANT_E4M3 = 21,
+  CODA_EPI_GELU = 22,
+  CODA_EPI_DGELU = 23
 } coda_epi_opcode;
 
 typedef struct coda_epi_op {
@@ -620,6 +626,36 @@ coda_status coda_linear_sigmoid_bwd(const coda_mat* dY, const coda_weight* Wn, c
                                     const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
                                     const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/* ===================================================================== RMSNorm -> Linear -> GELU */
+
+/* The same layer with GELU as the elementwise map (the guide's linear_sigmoid
+ * names one member of a family of activation epilogues; GELU is taken as the
+ * second, in its exact form):
+ *   r = (sum_t P[t, m] / K + eps)^(-1/2),  h = r (x W~),
+ *   out = GELU(h) = h Phi(h),  Phi(h) = (1 + erf(h / sqrt 2)) / 2.
+ * Arguments, shapes, precisions, workspace and errors as in
+ * coda_linear_sigmoid_fwd. */
+coda_status coda_linear_gelu_fwd_workspace(int64_t M, int64_t K, int32_t have_partials, int32_t precision,
+                                           size_t* bytes);
+coda_status coda_linear_gelu_fwd(const coda_mat* x, const coda_mat* sumsq_partials, const coda_weight* W,
+                                 float eps, const coda_mat* out, const coda_mat* save_h, const coda_mat* r_out,
+                                 int32_t precision, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward fused behind the consumer GEMM da = dY Wn^T, as
+ * coda_linear_sigmoid_bwd with GELU'(h) = Phi(h) + h phi(h) (phi the normal
+ * density) in place of s (1 - s):
+ *   dh~ = bf16(r da GELU'(h)),  T = sum_j dh~ h,  c = r T / D,
+ *   du = dh~ W~^T - c u + dres,  dW = beta dW + g (u^T dh~),
+ *   dg = beta dg + sum_n W (u^T dh~).
+ * Arguments as in coda_linear_sigmoid_bwd. */
+coda_status coda_linear_gelu_bwd_workspace(int64_t M, int64_t D, int64_t N, int32_t precision, size_t* bytes);
+coda_status coda_linear_gelu_bwd(const coda_mat* dY, const coda_weight* Wn, const coda_mat* saved_h,
+                                 const coda_mat* r, const coda_mat* u, const coda_weight* W,
+                                 const coda_mat* W_unfolded, const coda_mat* g, const coda_mat* dres,
+                                 const coda_mat* du, const coda_mat* dW, const coda_mat* dg, float beta,
+                                 const coda_mat* dh_out, int32_t precision, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* ===================================================================== final RMSNorm -> LM head -> CE */
 

@@ -107,12 +107,15 @@ def test_epilogue_descriptor_chains_and_operand_checks():
         "swiglu": [(E.EPI_ROW_RMS_FROM_PARTIALS, (0,), 1e-6), (E.EPI_STORE_ROW_VEC, (1,), 0), (E.EPI_SAVE_PRE, (2,), 0),
                    (E.EPI_SWIGLU, (), 0), (E.EPI_STORE_BF16, (), 0)],
         "sigmoid": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_SIGMOID, (), 0), (E.EPI_STORE_BF16, (), 0)],
+        "gelu": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_SAVE_PRE, (1,), 0), (E.EPI_GELU, (), 0), (E.EPI_STORE_BF16, (), 0)],
         "qkrope": [(E.EPI_ROW_SCALE, (0,), 0), (E.EPI_SAVE_PRE, (1,), 0), (E.EPI_QKNORM_ROPE, (2, 3), 1e-6),
                    (E.EPI_STORE_BF16, (), 0)],
         "dswiglu": [(E.EPI_DSWIGLU, (0,), 0), (E.EPI_ROW_SCALE, (1,), 0), (E.EPI_STORE_BF16, (), 0),
                     (E.EPI_ROW_DOT_PARTIAL, (2,), 0)],
         "dsigmoid": [(E.EPI_DSIGMOID, (0,), 0), (E.EPI_ROW_SCALE, (1,), 0), (E.EPI_STORE_BF16, (), 0),
                      (E.EPI_ROW_DOT_PARTIAL, (2,), 0)],
+        "dgelu": [(E.EPI_DGELU, (0,), 0), (E.EPI_ROW_SCALE, (1,), 0), (E.EPI_STORE_BF16, (), 0),
+                  (E.EPI_ROW_DOT_PARTIAL, (2,), 0)],
         "normcorr": [(E.EPI_NORM_CORRECTION, (0, 1, 2), 0), (E.EPI_SCALE_DEV, (3,), 0), (E.EPI_ADD_TILE, (4,), 0),
                      (E.EPI_STORE_BF16, (), 0)],
         "wgrad": [(E.EPI_SCALE_DEV, (0,), 0), (E.EPI_WGRAD_GAIN, (1, 2, 3), 1.0)],
@@ -176,6 +179,10 @@ def test_epilogue_descriptor_chains_and_operand_checks():
     assert run(ce, [v(I32, M), part(tn), v(F32, M)], D=None) == 3                            # one partial set
     # a chain that exists but is not compiled for the layout: sigmoid on NT operands
     assert run(chains["sigmoid"], [v(F32, M)], B=Bt, tB=1) == 7
+    assert run(chains["dgelu"], [fake(BF, M, N), v(F32, M), part(tn)], tB=0) == 7       # DGELU on NN operands
+    # GELU: the saved pre-activation must be [M, N]; DGELU: the saved h [M, N]
+    assert run(chains["gelu"], [v(F32, M), fake(BF, M, N + 8)]) == 3
+    assert run(chains["dgelu"], [fake(BF, M, 2 * N), v(F32, M), part(tn)], B=Bt, tB=1) == 3
     # E4M3: A [M, K], B [N, K] only, scales [M] and [N]
     f8 = chains["fp8_resid"]
     A8, B8 = fake(E4, M, K), fake(E4, N, K)

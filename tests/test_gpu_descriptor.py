@@ -69,19 +69,21 @@ def test_chain_rms_swiglu_with_saves():
     assert_bf16("saved hu", hu, nm.bf16(rr[:, None] * ob.mm(x, nm.bf16(g[:, None] * Wu))))
 
 
-def test_chain_row_scale_sigmoid():
-    """ROW_SCALE SAVE_PRE SIGMOID STORE_BF16 with a given row factor."""
+@pytest.mark.parametrize("act", ["sigmoid", "gelu"])
+def test_chain_row_scale_sigmoid(act):
+    """ROW_SCALE SAVE_PRE SIGMOID|GELU STORE_BF16 with a given row factor."""
     rng = np.random.default_rng(102)
     M, K, N = 300, 264, 352
     x, W = rnd(rng, M, K), rnd(rng, K, N, std=K ** -0.5)
     r = rng.uniform(0.5, 2.0, M).astype(np.float32)
     out, h = empty(M, N, dt=BF), empty(M, N, dt=BF)
-    coda.gemm_epi([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_SAVE_PRE, 1, 0.0), (coda.EPI_SIGMOID, 0, 0.0),
+    op, f = (coda.EPI_SIGMOID, ops.sigmoid) if act == "sigmoid" else (coda.EPI_GELU, ops.gelu)
+    coda.gemm_epi([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_SAVE_PRE, 1, 0.0), (op, 0, 0.0),
                    (coda.EPI_STORE_BF16, 0, 0.0)], bf(x), 0, bf(W), 0, out, aux=[f32(r), h])
     torch.cuda.synchronize()
     hh = r[:, None] * ob.mm(x, W)
     assert_bf16("h", to_np(h), nm.bf16(hh))
-    assert_bf16("sigmoid", to_np(out), nm.bf16(ops.sigmoid(hh)))
+    assert_bf16(act, to_np(out), nm.bf16(f(hh)))
 
 
 def test_chain_rms_qknorm_rope():
@@ -114,9 +116,9 @@ def test_chain_rms_qknorm_rope():
     assert_grad("r", to_np(r), rr)
 
 
-@pytest.mark.parametrize("which", ["dswiglu", "dsigmoid"])
+@pytest.mark.parametrize("which", ["dswiglu", "dsigmoid", "dgelu"])
 def test_chain_activation_backward(which):
-    """DSWIGLU|DSIGMOID ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL behind
+    """DSWIGLU|DSIGMOID|DGELU ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL behind
     da = dY Wn^T (B stored [N, K]): dh~ = bf16(r dact(da, saved)), and the
     partials T[t, m] = sum over tile t of dh~ * saved."""
     rng = np.random.default_rng(104)
@@ -127,7 +129,7 @@ def test_chain_activation_backward(which):
     saved = rnd(rng, M, 2 * N if sw else N, std=2.0)
     tn = coda.partials_cols(N)
     out, T = empty(M, 2 * N if sw else N, dt=BF), empty(tn, M)
-    op = coda.EPI_DSWIGLU if sw else coda.EPI_DSIGMOID
+    op = dict(dswiglu=coda.EPI_DSWIGLU, dsigmoid=coda.EPI_DSIGMOID, dgelu=coda.EPI_DGELU)[which]
     coda.gemm_epi([(op, 0, 0.0), (coda.EPI_ROW_SCALE, 1, 0.0), (coda.EPI_STORE_BF16, 0, 0.0),
                    (coda.EPI_ROW_DOT_PARTIAL, 2, 0.0)], bf(dY), 0, bf(Wn), 1, out, aux=[bf(saved), f32(r), T])
     torch.cuda.synchronize()
@@ -141,8 +143,11 @@ def test_chain_activation_backward(which):
         # each 256-column tile of da covers the packed columns [512 t, 512 t + 512)
         Tref = ob.tile_partials(to_np(out).astype(np.float64) * saved.astype(np.float64), 512)
     else:
-        s = ops.sigmoid(saved)
-        ref = nm.bf16(r[:, None] * (da * s * (1 - s)))
+        if which == "dsigmoid":
+            s = ops.sigmoid(saved)
+            ref = nm.bf16(r[:, None] * (da * s * (1 - s)))
+        else:
+            ref = nm.bf16(r[:, None] * (da * ops.gelu_grad(saved)))
         got = to_np(out)
         Tref = ob.tile_partials(ref.astype(np.float64) * saved.astype(np.float64), 256)
     assert_bf16("dh~", got, ref)
@@ -390,3 +395,50 @@ def test_chain_mx_small_backward_chains(fmt):
     acc = ob.mm(X.T.copy(), G, mode)
     assert_grad("dW", to_np(Dw), prior + s * (g[:, None] * acc), rel=2e-3)
     assert_grad("gain partials", to_np(P), ob.tile_partials(s * (W.astype(np.float64) * acc), 256), rel=2e-3)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "e2m3", "e3m2"])
+def test_chain_mx_gelu(fmt):
+    """GELU forward (ROW_SCALE SAVE_PRE GELU STORE_BF16) and backward (DGELU
+    ROW_SCALE STORE_BF16 ROW_DOT_PARTIAL behind da = dY Wn^T) on MXFP8, MXFP4
+    and both MXFP6 operands the library quantised, against the oracle's
+    product in the same format."""
+    rng = np.random.default_rng(118)
+    mode = {"e4m3": "mx", "e2m1": "mx4", "e2m3": "mx6_e2m3", "e3m2": "mx6_e3m2"}[fmt]
+
+    def q(X, axis):
+        if fmt == "e4m3":
+            return coda.quantize_mxfp8(bf(X), axis)
+        return coda.quantize_mxfp4(bf(X), axis) if fmt == "e2m1" else coda.quantize_mxfp6(bf(X), axis, fmt)
+
+    def gemm(prog, QA, SA, QB, SB, D, aux):
+        if fmt == "e4m3":
+            return coda.gemm_mx(prog, QA, SA, QB, SB, D, aux=aux)
+        if fmt == "e2m1":
+            return coda.gemm_mx4(prog, QA, SA, QB, SB, D, aux=aux)
+        return coda.gemm_mx6(prog, fmt, QA, SA, QB, SB, D, aux=aux)
+
+    M, K, N = 300, 384, 264
+    x, W = rnd(rng, M, K), rnd(rng, K, N, std=K ** -0.5)
+    r = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    QA, SA = q(x, 1)
+    QB, SB = q(W, 0)
+    out, h = empty(M, N, dt=BF), empty(M, N, dt=BF)
+    gemm([(coda.EPI_ROW_SCALE, 0, 0.0), (coda.EPI_SAVE_PRE, 1, 0.0), (coda.EPI_GELU, 0, 0.0),
+          (coda.EPI_STORE_BF16, 0, 0.0)], QA, SA, QB, SB, out, [f32(r), h])
+    Dm = 256
+    dY, Wn = rnd(rng, M, Dm, std=0.1), rnd(rng, N, Dm, std=Dm ** -0.5)
+    saved = rnd(rng, M, N, std=2.0)
+    QY, SY = q(dY, 1)
+    QW, SW = q(Wn, 1)          # [N, Dm]: blocks along the contracted axis
+    dh, T = empty(M, N, dt=BF), empty(coda.partials_cols(N), M)
+    gemm([(coda.EPI_DGELU, 0, 0.0), (coda.EPI_ROW_SCALE, 1, 0.0), (coda.EPI_STORE_BF16, 0, 0.0),
+          (coda.EPI_ROW_DOT_PARTIAL, 2, 0.0)], QY, SY, QW, SW, dh, [bf(saved), f32(r), T])
+    torch.cuda.synchronize()
+    hh = r[:, None] * ob.mm(x, W, mode)
+    assert_bf16("h", to_np(h), nm.bf16(hh), tol=FP8_TOL)
+    assert_bf16("gelu", to_np(out), nm.bf16(ops.gelu(hh)), tol=FP8_TOL)
+    ref = nm.bf16(r[:, None] * (ob.mm(dY, Wn.T.copy(), mode) * ops.gelu_grad(saved)))
+    assert_bf16("dh~", to_np(dh), ref, tol=FP8_TOL)
+    assert_grad("T partials", to_np(T), ob.tile_partials(ref.astype(np.float64) * saved.astype(np.float64), 256),
+                rel=2e-3)

@@ -146,9 +146,9 @@ def test_swiglu_many_partials(n_partials):
 
 
 # ------------------------------------------------------------------ RMSNorm -> Linear -> sigmoid
-def _run_sigmoid(M, D, N, seed, precision, beta=0.0):
-    """Forward then the backward behind the consumer GEMM dY Wn^T; returns the
-    host inputs and every device result."""
+def _run_sigmoid(M, D, N, seed, precision, beta=0.0, act="sigmoid"):
+    """Forward then the backward behind the consumer GEMM dY Wn^T (act is
+    "sigmoid" or "gelu"); returns the host inputs and every device result."""
     rng = np.random.default_rng(seed)
     P = dict(x=rand_bf16(rng, M, D), W=rand_bf16(rng, D, N, std=D ** -0.5),
              Wn=rand_bf16(rng, N, D, std=N ** -0.5), dY=rand_bf16(rng, M, D, std=0.1),
@@ -166,34 +166,43 @@ def _run_sigmoid(M, D, N, seed, precision, beta=0.0):
     out = torch.empty((M, N), dtype=BF, device=DEV)
     h = torch.empty((M, N), dtype=BF, device=DEV)
     r = torch.empty(M, dtype=torch.float32, device=DEV)
-    coda.linear_sigmoid_fwd(x, Wt, 1e-6, out, save_h=h, r_out=r, precision=precision)
+    fwd, bwd = ((coda.linear_sigmoid_fwd, coda.linear_sigmoid_bwd) if act == "sigmoid"
+                else (coda.linear_gelu_fwd, coda.linear_gelu_bwd))
+    fwd(x, Wt, 1e-6, out, save_h=h, r_out=r, precision=precision)
     du = torch.empty((M, D), dtype=BF, device=DEV)
     dW, dg = f32(P["dW0"]), f32(P["dg0"])
     dht = torch.empty((M, N), dtype=BF, device=DEV)
-    coda.linear_sigmoid_bwd(bf(P["dY"]), Wn, h, r, x, Wt, Wu, g, bf(P["dres"]), du, dW, dg, beta=beta,
-                            dh_out=dht, precision=precision)
+    bwd(bf(P["dY"]), Wn, h, r, x, Wt, Wu, g, bf(P["dres"]), du, dW, dg, beta=beta, dh_out=dht, precision=precision)
     torch.cuda.synchronize()
     got = dict(a=to_np(out), h=to_np(h), r=to_np(r), du=to_np(du), dW=to_np(dW), dg=to_np(dg), dht=to_np(dht))
     return P, got
 
 
+@pytest.mark.parametrize("act", ["sigmoid", "gelu"])
 @pytest.mark.parametrize("M,D,N,beta", [(333, 264, 352, 0.0), (520, 384, 600, 1.0)])
-def test_sigmoid_forward_backward(M, D, N, beta):
-    P, got = _run_sigmoid(M, D, N, 11, coda.PREC_BF16, beta)
-    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6)
+def test_sigmoid_forward_backward(M, D, N, beta, act):
+    P, got = _run_sigmoid(M, D, N, 11, coda.PREC_BF16, beta, act=act)
+    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6, act=act)
     for k in ("a", "h"):
         assert_bf16(k, got[k], F[k])
     assert_grad("r", got["r"], F["r"])
     priors = dict(dW=P["dW0"], dg=P["dg0"])
     B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], F, 1e-6, dres=P["dres"],
-                                     priors=priors, beta=beta)
+                                     priors=priors, beta=beta, act=act)
     assert_bf16("dh~", got["dht"], B["dht"])
     assert_bf16("dx", got["du"], B["dx"])
     assert_grad("dW", got["dW"], B["dW"])
     assert_grad("dg", got["dg"], B["dg"])
+    # against the plain definition (fp64 autograd-checked canonical layer)
+    C = ob.sigmoid_layer_canonical(P["x"], P["g"], P["W"], P["Wn"], P["dY"], 1e-6, dres=P["dres"], act=act)
+    assert_bf16("a vs canonical", got["a"], C["a"], norm_rel=None)
+    assert_bf16("dx vs canonical", got["du"], C["dx"], norm_rel=None)
+    assert rel_norm(got["dW"] - beta * P["dW0"], C["dW"]) <= 2e-2
+    assert rel_norm(got["dg"] - beta * P["dg0"], C["dg"]) <= 2e-2
 
 
-def test_sigmoid_fp8():
+@pytest.mark.parametrize("act", ["sigmoid", "gelu"])
+def test_sigmoid_fp8(act):
     """E4M3 operands, forward then backward, against the oracle's own chained
     evaluation (its forward feeds its backward).  dh~ is rounded from fp32
     sums taken in different orders on the two sides; rows where that moved
@@ -203,14 +212,14 @@ def test_sigmoid_fp8():
     bound."""
     from tests.helpers import FP8_TOL, amax_flip_rows, assert_fp8_rows
     M, D, N = 304, 256, 352
-    P, got = _run_sigmoid(M, D, N, 12, coda.PREC_FP8)
-    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6, fp8=True)
+    P, got = _run_sigmoid(M, D, N, 12, coda.PREC_FP8, act=act)
+    F = ob.sigmoid_forward_contract(P["x"], P["g"], P["W"], 1e-6, fp8=True, act=act)
     none = np.zeros(0, np.int64)
     assert_fp8_rows("h", got["h"], F["h"], none)
     assert_fp8_rows("a", got["a"], F["a"], none)
     assert_grad("r", got["r"], F["r"])
     B = ob.sigmoid_backward_contract(P["x"], P["g"], P["W"], P["Wn"], P["dY"], F, 1e-6, dres=P["dres"],
-                                     fp8=True)
+                                     fp8=True, act=act)
     fl_h = amax_flip_rows([(got["h"], F["h"])])
     assert_fp8_rows("dh~", got["dht"], B["dht"], fl_h)
     assert_fp8_rows("dx", got["du"], B["dx"], np.union1d(fl_h, amax_flip_rows([(got["dht"], B["dht"])])))
