@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
     ap.add_argument("--no-h4096", action="store_true", help="skip the hidden-4096 block leg of the default run")
+    ap.add_argument("--no-coresident", action="store_true",
+                    help="skip the block step under the co-resident gate/up schedule")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device-to-device copies of 1 GiB (the reference kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -358,14 +360,15 @@ def block_leg(name, precision, args, breakdown=True):
     ]
     f3_events = []
 
-    def step(record=False):
+    def step(record=None):
+        """One step; with a list, the gate/up kernel's events are appended to it."""
         for name, fn in calls:
-            if record and name.startswith("F3"):
+            if record is not None and name.startswith("F3"):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 fn()
                 e1.record()
-                f3_events.append((e0, e1))
+                record.append((e0, e1))
             else:
                 fn()
 
@@ -383,9 +386,26 @@ def block_leg(name, precision, args, breakdown=True):
 
     for _ in range(args.warmup):
         step()
-    ms = timed(lambda: step(record=True), args.steps)
+    ms = timed(lambda: step(f3_events), args.steps)
     f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
+    # The same step with the gate/up GEMM + SwiGLU under the co-resident
+    # schedule (two 128 x 256 workgroups a compute unit, one's epilogue
+    # overlapping the other's matrix work), and that kernel's own time.
+    cores = None
+    if precision == "bf16" and not args.no_coresident:
+        cev = []
+        with coda.schedule(coda.SCHED_CORESIDENT):
+            for _ in range(max(1, args.warmup)):
+                step()
+            cms = timed(lambda: step(cev), args.steps)
+        c3 = sum(a.elapsed_time(b) for a, b in cev) / len(cev)
+        c3_flop = 2 * cfg.M * (2 * cfg.F) * cfg.D
+        cores = {"schedule": "gate/up GEMM + SwiGLU as 128 x 256 tiles, two 4-wave workgroups a compute unit",
+                 "block_fwd_bwd_ms": round(cms, 4), "gate_up_swiglu_ms": round(c3, 4),
+                 "gate_up_swiglu_tflops": round(c3_flop / (c3 * 1e-3) / 1e12, 2),
+                 "pingpong_gate_up_swiglu_ms": round(f3_ms, 4),
+                 "speedup_over_pingpong_gate_up": round(f3_ms / c3, 4)}
     # the per-weight-update preparation, warm (no allocation: same buffers)
     blk.prepare(params)
     prep_ms = timed(lambda: blk.prepare(params), 5)
@@ -441,6 +461,7 @@ def block_leg(name, precision, args, breakdown=True):
                      "frac": round(f3_tflops / peak, 4), "avg_ms": round(f3_ms, 4),
                      "flop_per_launch": f3_flop, "traffic": stored_traffic(name, precision)},
         "partial_buffers": partial_bytes(M, cfg.D, cfg.F),
+        "coresident_schedule": cores,
     }
     del blk, f, g, params, calls
     torch.cuda.empty_cache()
@@ -537,6 +558,7 @@ def main():
         "breakdown_ms": head["breakdown_ms"],
         "roofline": head["roofline"],
         "partial_buffers": head["partial_buffers"],
+        "coresident_schedule": head["coresident_schedule"],
         "hidden_4096": h4096,
         "cpu_baseline": cpu,
         "mxfp8_gemm": mx,

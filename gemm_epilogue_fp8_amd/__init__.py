@@ -22,14 +22,15 @@ from ._lib import (CODA_BF16, CODA_E2M1X2, CODA_E2M3, CODA_E3M2, CODA_E4M3, CODA
                    EPI_ROW_SUMSQ_PARTIAL, EPI_SWIGLU, EPI_ROW_RMS_FROM_PARTIALS, EPI_STORE_ROW_VEC,
                    EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU, EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION,
                    EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL, EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV,
-                   EPI_DEQUANT_E4M3, EPI_GELU, EPI_DGELU)
+                   EPI_DEQUANT_E4M3, EPI_GELU, EPI_DGELU, SCHED_PINGPONG, SCHED_CORESIDENT)
 
 __all__ = ["CodaError", "Weight", "lib", "mat", "fold_gain", "pack_gate_up", "rope_table", "row_sumsq",
            "quantize_e4m3", "quantize_weight", "gemm_epi", "partials_cols", "quantize_mxfp8", "gemm_mx",
            "linear_swiglu_fwd", "linear_swiglu_bwd", "linear_rmsnorm_residual_fwd",
            "linear_rmsnorm_residual_bwd", "linear_qknorm_rope_fwd", "linear_qknorm_rope_bwd",
            "linear_cross_entropy_fwd", "linear_cross_entropy_bwd", "linear_sigmoid_fwd", "linear_sigmoid_bwd",
-           "linear_gelu_fwd", "linear_gelu_bwd", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4",
+           "linear_gelu_fwd", "linear_gelu_bwd", "set_schedule", "get_schedule", "schedule",
+           "SCHED_PINGPONG", "SCHED_CORESIDENT", "PREC_BF16", "PREC_FP8", "PREC_MXFP8", "PREC_MXFP4",
            "PREC_MXFP6_E2M3", "PREC_MXFP6_E3M2"]
 
 
@@ -194,6 +195,32 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 def _check(st: int):
     if st != 0:
         raise CodaError(st, lib().coda_last_error().decode())
+
+
+def set_schedule(sched: int):
+    """Process-wide launch schedule of the bf16 SwiGLU GEMM (coda_set_schedule)."""
+    _check(lib().coda_set_schedule(sched))
+
+
+def get_schedule() -> int:
+    return lib().coda_get_schedule()
+
+
+class schedule:
+    """Context manager: `with schedule(SCHED_CORESIDENT): ...` restores the
+    previous schedule on exit."""
+
+    def __init__(self, sched: int):
+        self.sched, self.prev = sched, None
+
+    def __enter__(self):
+        self.prev = get_schedule()
+        set_schedule(self.sched)
+        return self
+
+    def __exit__(self, *exc):
+        set_schedule(self.prev)
+        return False
 
 
 def _ws_call(size_fn, size_args, device):

@@ -26,6 +26,7 @@ EPI_STORE_ROW_VEC, EPI_SAVE_PRE, EPI_QKNORM_ROPE, EPI_DSWIGLU = 9, 10, 11, 12
 EPI_ROW_DOT_PARTIAL, EPI_NORM_CORRECTION, EPI_WGRAD_GAIN, EPI_CE_LSE_PARTIAL = 13, 14, 15, 16
 EPI_CE_GRAD, EPI_SIGMOID, EPI_DSIGMOID, EPI_SCALE_DEV, EPI_DEQUANT_E4M3 = 17, 18, 19, 20, 21
 EPI_GELU, EPI_DGELU = 22, 23
+SCHED_PINGPONG, SCHED_CORESIDENT = 0, 1
 MAX_EPI_OPS = 8
 
 
@@ -58,6 +59,8 @@ SIGNATURES = {
     "coda_abi_version": [],
     "coda_status_string": [C.c_int],
     "coda_last_error": [],
+    "coda_set_schedule": [i32],
+    "coda_get_schedule": [],
     "coda_partials_cols": [i64],
     "coda_fold_gain": [M_, M_, M_, vp],
     "coda_pack_gate_up": [M_, M_, M_, M_, vp],

@@ -1,6 +1,7 @@
 // C ABI of the GEMM+epilogue library: host-side validation, workspace
 // carving and the launch sequences of the functional entry points.  See
 // include/coda.h for the contract of every entry point.
+#include <atomic>
 #include <mutex>
 
 #include "capi_util.hpp"
@@ -274,6 +275,20 @@ extern "C" const char* coda_status_string(int st) {
 }
 
 extern "C" const char* coda_last_error(void) { return coda::last_error_slot().c_str(); }
+
+namespace coda {
+static std::atomic<int> g_schedule{CODA_SCHED_PINGPONG};
+bool coresident_schedule() { return g_schedule.load(std::memory_order_relaxed) == CODA_SCHED_CORESIDENT; }
+}  // namespace coda
+
+extern "C" coda_status coda_set_schedule(int32_t schedule) {
+  if (schedule != CODA_SCHED_PINGPONG && schedule != CODA_SCHED_CORESIDENT)
+    return fail(CODA_ERR_VALUE, "unknown schedule %d", (int)schedule);
+  coda::g_schedule.store(schedule, std::memory_order_relaxed);
+  return CODA_OK;
+}
+
+extern "C" int32_t coda_get_schedule(void) { return coda::g_schedule.load(std::memory_order_relaxed); }
 
 extern "C" int64_t coda_partials_cols(int64_t N) { return (N + kBN - 1) / kBN; }
 

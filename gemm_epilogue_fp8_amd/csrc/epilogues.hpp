@@ -1147,8 +1147,10 @@ struct EpiCrossEntropyGrad {
 
 // ================================================================ the kernel
 // One output tile per workgroup; the XCD-aware tile order lives in tile_coord.
+// The single-group (4-wave) tile asks for two waves a SIMD, which keeps a
+// wave within 256 registers so that two workgroups share a compute unit.
 template <class Cfg, class Epi>
-__global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e) {
+__global__ __launch_bounds__(Cfg::T, Cfg::WAVES_M == 1 ? 2 : 1) void gemm_epi_kernel(GemmArgs g, EpiArgs e) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES + scratch_bytes<Cfg>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (gridDim.y > 1) {
@@ -1182,7 +1184,10 @@ __global__ __launch_bounds__(Cfg::T) void gemm_epi_kernel(GemmArgs g, EpiArgs e)
   typename Epi::Pro pro;
   Epi::issue(e, c, pro);
   Acc<Cfg> acc;
-  mainloop<Cfg>(g, smem, acc, c.m0, c.n0, c.wm0, c.wn0, tid, lane);
+  if constexpr (Cfg::WAVES_M == 1)
+    mainloop_solo<Cfg>(g, smem, acc, c.m0, c.n0, c.wm0, c.wn0, tid, lane);
+  else
+    mainloop<Cfg>(g, smem, acc, c.m0, c.n0, c.wm0, c.wn0, tid, lane);
   Epi::apply(e, c, acc, pro);
 }
 

@@ -115,14 +115,17 @@ struct GemmCfg {
   static constexpr int WPP = FP4 ? 2 : 1;          // MX: exponent word rows a stage pair
   static constexpr int ESIZE = FP8 ? 1 : 2;
   static constexpr int BK = kRowBytes / ESIZE;     // K per stage: 32 bf16 or 64 fp8
-  static constexpr int NS = 4;                     // LDS stages
+  // LDS stages: four (two pairs) for the two-group tile; three for the
+  // single-group tile, whose workgroup leaves room for a second one a CU
+  static constexpr int NS = WAVES_M == 1 ? 3 : 4;
   static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
   // MX: two slots of WPP x (BM + BN) 4-byte exponent words after the stages
   static constexpr int SCALE_OFF = NS * STAGE_BYTES;
   static constexpr int SCALE_SLOT = WPP * (BM + BN) * 4;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + (MX ? 2 * SCALE_SLOT : 0);
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(WAVES_M == 2, "the two wave groups are the two row halves of the tile");
+  static_assert(WAVES_M == 2 || (WAVES_M == 1 && A_KC && !FP8),
+                "two wave groups (the two row halves of the tile), or one bf16 group with K-contiguous A");
   static_assert(!FP8 || (A_KC && B_KC), "fp8 operands are K-contiguous");
   static_assert(!MX || FP8, "block scales come with E4M3 operands");
   static_assert(!FP4 || MX, "E2M1 operands are block-scaled");
@@ -593,6 +596,79 @@ __device__ __forceinline__ void mainloop(const GemmArgs& g, char* smem, Acc<Cfg>
     phase_barrier();
   }
   if (grp == 0) phase_barrier();           // realign: both groups have passed 2 np + 1 barriers
+}
+
+// Single wave group (WAVES_M == 1, the co-resident schedule): every wave
+// copies its share of both operand tiles of a stage and computes its
+// WM x WN block.  Three stages: while stage kt is multiplied, stage kt + 1
+// has landed (its fragments are read into the second register set) and
+// stage kt + 2 is in flight.  One barrier a stage.  The workgroup (4 waves,
+// 3 stages, at most 256 registers a lane) is sized so that two share a
+// compute unit: while one runs its epilogue or drains its stores, the
+// other's matrix instructions keep the cores busy, which is the
+// co-residency form of hiding one tile's epilogue under another tile's
+// mainloop.
+template <class Cfg>
+__device__ __forceinline__ void mainloop_solo(const GemmArgs& g, char* smem, Acc<Cfg>& acc,
+                                              int m0, int n0, int wm0, int wn0, int tid, int lane) {
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.0f;
+
+  static_assert(Cfg::WAVES_M == 1 && Cfg::NS == 3 && !Cfg::FP8, "one bf16 wave group, three stages");
+  const char* A = static_cast<const char*>(g.A);
+  const char* B = static_cast<const char*>(g.B);
+  const int64_t lda_b = g.lda * Cfg::ESIZE, ldb_b = g.ldb * Cfg::ESIZE;
+  const int64_t kbytes = (int64_t)g.K * Cfg::ESIZE;
+  const int nk = (g.K + Cfg::BK - 1) / Cfg::BK;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int SUB = substeps<Cfg>();
+  // copies a wave issues a stage: its share of the A tile and of the B tile
+  constexpr int LPS = TileKC<Cfg, Cfg::BM>::NI + (Cfg::B_KC ? TileKC<Cfg, Cfg::BN>::NI : TileMN<Cfg, Cfg::BN>::NI);
+
+  auto issue_stage = [&](int kt, int slot) {
+    char* As = smem + slot * Cfg::STAGE_BYTES;
+    char* Bs = As + Cfg::BM * kRowBytes;
+    const int64_t kb0 = (int64_t)kt * Cfg::BK * Cfg::ESIZE;
+    TileKC<Cfg, Cfg::BM>::issue(A, lda_b, m0, g.M, kb0, kbytes, As, w, lane);
+    if constexpr (Cfg::B_KC)
+      TileKC<Cfg, Cfg::BN>::issue(B, ldb_b, n0, g.N, kb0, kbytes, Bs, w, lane);
+    else
+      TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, kt * Cfg::BK, g.K, n0, g.N, Bs, w, lane);
+  };
+
+  issue_stage(0, 0);
+  if (nk > 1) issue_stage(1, 1);
+  Frags<Cfg> f[2][SUB];
+  if (nk > 1) wait_vmcnt<LPS>(); else wait_vmcnt<0>();
+  phase_barrier();                         // stage 0 has landed for every wave
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) load_frags<Cfg>(smem, smem + Cfg::BM * kRowBytes, s, f[0][s], wm0, wn0, lane);
+  int nx = 1;                              // slot of stage kt + 1
+  auto step = [&](int kt, Frags<Cfg>(&cur)[SUB], Frags<Cfg>(&nxt)[SUB]) {
+    wait_vmcnt<0>();                       // this wave's copies of stage kt + 1 have landed
+    wait_lgkmcnt0();                       // cur (stage kt) is in registers
+    // every wave's copies of stage kt + 1 have landed and every wave has read
+    // stage kt, so the slot of stage kt - 1 is free for stage kt + 2
+    phase_barrier();
+    if (kt + 2 < nk) issue_stage(kt + 2, nx == 2 ? 0 : nx + 1);
+    if (kt + 1 < nk) {
+      const char* S1 = smem + nx * Cfg::STAGE_BYTES;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, nxt[s], wm0, wn0, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) mma_frags<Cfg>(cur[s], acc);
+    nx = nx == 2 ? 0 : nx + 1;
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, f[0], f[1]);
+    if (kt + 1 < nk) step(kt + 1, f[1], f[0]);
+  }
+  phase_barrier();                         // every wave is done reading LDS before the epilogue reuses it
 }
 
 }  // namespace coda

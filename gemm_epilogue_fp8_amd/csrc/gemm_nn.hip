@@ -3,6 +3,9 @@
 
 namespace coda {
 using CfgNN = GemmCfg<kBM, kBN, 2, 4, true, false>;
+// the co-resident schedule: 128 x 256 tile, one group of 4 waves, two
+// workgroups a compute unit
+using CfgNN1 = GemmCfg<128, kBN, 1, 4, true, false>;
 
 hipError_t launch_gemm_nn(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
   switch (p) {
@@ -11,7 +14,9 @@ hipError_t launch_gemm_nn(Prog p, GemmArgs g, const EpiArgs& e, hipStream_t s) {
     case Prog::RowColStore: return launch_one<CfgNN, EpiLinear<CfgNN, EL_ROWVEC | EL_COLVEC>>(g, e, s);
     case Prog::ResidSumsq: return launch_one<CfgNN, EpiLinear<CfgNN, EL_TILEADD | EL_SUMSQ>>(g, e, s);
     case Prog::Resid: return launch_one<CfgNN, EpiLinear<CfgNN, EL_TILEADD>>(g, e, s);
-    case Prog::SwiGLU: return launch_one<CfgNN, EpiSwiGLU<CfgNN>>(g, e, s);
+    case Prog::SwiGLU:
+      if (coresident_schedule()) return launch_one<CfgNN1, EpiSwiGLU<CfgNN1>>(g, e, s);
+      return launch_one<CfgNN, EpiSwiGLU<CfgNN>>(g, e, s);
     case Prog::QKRope: return launch_one<CfgNN, EpiQKNormRope<CfgNN>>(g, e, s);
     case Prog::CrossEntropy: return launch_one<CfgNN, EpiCrossEntropy<CfgNN>>(g, e, s);
     case Prog::CrossEntropyG: return launch_one<CfgNN, EpiCrossEntropyGrad<CfgNN>>(g, e, s);

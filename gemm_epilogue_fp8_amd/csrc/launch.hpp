@@ -34,6 +34,10 @@ enum class Prog : int {
 
 constexpr int kBM = 256, kBN = 256;
 
+// The process-wide launch schedule of the bf16 SwiGLU program (coda_schedule):
+// true selects the co-resident 128 x 256 single-group tile.
+bool coresident_schedule();
+
 inline int tiles(int n, int b) { return (n + b - 1) / b; }
 
 // Launches program `p` with the given layout and precision; returns

@@ -130,6 +130,30 @@ int coda_abi_version(void);
 const char* coda_status_string(int status);
 const char* coda_last_error(void);
 
+/* Launch schedule of the bf16 gate/up GEMM with the SwiGLU epilogue (the
+ * generic entry point's SwiGLU chain on NN operands and the bf16
+ * coda_linear_swiglu_fwd).  The CODA paper (arXiv 2605.19269), §1, hides a
+ * tile's epilogue under other tiles' mainloops (ping-pong warp groups,
+ * tensor memory); the co-resident schedule is that overlap on this chip:
+ *   CODA_SCHED_PINGPONG   (default) one 256 x 256 tile a workgroup, two
+ *                         8-wave groups alternating copies and matrix work,
+ *                         one workgroup a compute unit; every tile's
+ *                         epilogue runs after its own mainloop.
+ *   CODA_SCHED_CORESIDENT 128 x 256 tiles, 4-wave workgroups, three LDS
+ *                         stages, two workgroups a compute unit, so one's
+ *                         epilogue and stores overlap the other's matrix
+ *                         instructions.  Same results up to the order of
+ *                         fp32 sums; slower on this chip (the smaller tile
+ *                         copies 1.5 times the operand bytes a flop).
+ * The setting is process-wide and read at each launch; changing it while
+ * another thread launches is a race.  CODA_ERR_VALUE for an unknown value. */
+typedef enum coda_schedule {
+  CODA_SCHED_PINGPONG = 0,
+  CODA_SCHED_CORESIDENT = 1
+} coda_schedule;
+coda_status coda_set_schedule(int32_t schedule);
+int32_t coda_get_schedule(void);
+
 /* ===================================================================== prep */
 
 /* W_out[k, n] = bf16(g[k] * W[k, n]): the RMSNorm gain folded into the weight

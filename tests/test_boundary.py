@@ -449,3 +449,17 @@ def test_mxfp6_weight_validation_codes():
         assert call(weight(dt, qf=(N, K // 2)), prec) == 3                # FP6 is a byte a value
         assert call(weight(dt, qb=(K, N // 2)), prec) == 3                # input-gradient copy shape
         assert call(weight(dt, K_=192), prec, K_=192) == 3                # K_in not a multiple of 128
+
+
+def test_schedule_setting():
+    """The launch schedule is process-wide: set, read back, unknown values refused."""
+    L = g.lib()
+    assert L.coda_get_schedule() == _lib.SCHED_PINGPONG
+    assert L.coda_set_schedule(_lib.SCHED_CORESIDENT) == 0
+    assert L.coda_get_schedule() == _lib.SCHED_CORESIDENT
+    assert L.coda_set_schedule(2) == 9 and L.coda_set_schedule(-1) == 9
+    assert L.coda_get_schedule() == _lib.SCHED_CORESIDENT
+    with g.schedule(_lib.SCHED_PINGPONG):
+        assert L.coda_get_schedule() == _lib.SCHED_PINGPONG
+    assert L.coda_get_schedule() == _lib.SCHED_CORESIDENT
+    assert L.coda_set_schedule(_lib.SCHED_PINGPONG) == 0

@@ -138,6 +138,33 @@ def test_swiglu_ragged_with_partials_and_saves():
     _swiglu_case(ci.SwiGLUShape(M=333, K=264, F=352), 3, use_partials=True, saves=True)
 
 
+@pytest.mark.parametrize("M,K,F,n_partials", [(333, 264, 352, 1), (100, 136, 96, 3), (1040, 512, 480, 12)])
+def test_swiglu_coresident_schedule(M, K, F, n_partials):
+    """The co-resident schedule (128 x 256 tiles, two 4-wave workgroups a
+    compute unit) against the oracle: ragged rows and columns, a K tail,
+    partials merged in the prologue or first, saves on."""
+    with coda.schedule(coda.SCHED_CORESIDENT):
+        _swiglu_case(ci.SwiGLUShape(M=M, K=K, F=F), 21, use_partials=True, saves=True, n_partials=n_partials)
+    assert coda.get_schedule() == coda.SCHED_PINGPONG
+
+
+def test_swiglu_schedules_agree():
+    """Both schedules on the same inputs: outputs within one bf16 rounding of
+    each other (the fp32 sums differ only in order)."""
+    shape = ci.SwiGLUShape(M=520, K=384, F=608)
+    P = ci.swiglu_inputs(shape, 22)
+    Wgu = torch.empty((shape.K, 2 * shape.F), dtype=BF, device=DEV)
+    coda.pack_gate_up(bf(P["Wg"]), bf(P["Wu"]), f32(P["g"]), Wgu)
+    outs = []
+    for sched in (coda.SCHED_PINGPONG, coda.SCHED_CORESIDENT):
+        out = torch.empty((shape.M, shape.F), dtype=BF, device=DEV)
+        with coda.schedule(sched):
+            coda.linear_swiglu_fwd(bf(P["x"]), Wgu, shape.eps, out)
+        torch.cuda.synchronize()
+        outs.append(to_np(out))
+    assert_bf16("co-resident vs ping-pong", outs[1], outs[0])
+
+
 @pytest.mark.parametrize("n_partials", [8, 12, 32])
 def test_swiglu_many_partials(n_partials):
     """Up to 8 partial rows are reduced in the GEMM prologue; more are merged
@@ -278,9 +305,11 @@ def _run_block(shape, seed, precision=coda.PREC_BF16):
     return P, {k: to_np(v) for k, v in f.items()}, {k: to_np(v) for k, v in b.items()}
 
 
-@pytest.mark.parametrize("shape,seed", [(SMALL, 0), (MEDIUM, 1)])
-def test_block_forward_backward(shape, seed):
-    P, f, b = _run_block(shape, seed)
+@pytest.mark.parametrize("shape,seed,sched", [(SMALL, 0, 0), (MEDIUM, 1, 0), (MEDIUM, 1, 1)])
+def test_block_forward_backward(shape, seed, sched):
+    """sched 1 runs the gate/up GEMM under the co-resident schedule."""
+    with coda.schedule(sched):
+        P, f, b = _run_block(shape, seed)
     F = ob.block_forward_contract(P, shape)
     B = ob.block_backward_contract(P, F, shape)
     D = shape.D
