@@ -307,6 +307,18 @@ __global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, i
     }
 }
 
+__global__ void fill_f32_kernel(float* out, int n, float v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) out[i] = v;
+}
+
+__global__ void scale_f32_kernel(float* out, int64_t ld, int R, int C, float beta) {
+  for (int r = blockIdx.y; r < R; r += gridDim.y)
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < C; c += gridDim.x * blockDim.x) {
+      float* p = out + (int64_t)r * ld + c;
+      *p = beta != 0.0f ? beta * *p : 0.0f;
+    }
+}
+
 __global__ void norm_corr_finish_kernel(const float* acc, int64_t lda, const uint16_t* y, int64_t ldy, const float* cr,
                                         const float* scale, const uint16_t* res, int64_t ldr, uint16_t* out,
                                         int64_t ldo, int R, int C) {

@@ -57,6 +57,10 @@ __global__ void ce_finish_loss_kernel(const float* per_row, const int* status, i
 __global__ void ce_scale_kernel(const int* n_valid, float dloss, float* scale);
 // out = bf16(X), fp32 [R, C] -> bf16 (C % 4 == 0); grid (x, R)
 __global__ void f32_to_bf16_kernel(const float* X, int64_t ldx, uint16_t* out, int64_t ldo, int R, int C);
+// out[i] = v for i < n
+__global__ void fill_f32_kernel(float* out, int n, float v);
+// out[r][c] = beta out[r][c] (beta 0 writes zeros without reading); grid (x, R)
+__global__ void scale_f32_kernel(float* out, int64_t ld, int R, int C, float beta);
 // RMSNorm backward correction after a product accumulated in fp32 over
 // slices: out[r][c] = bf16(acc[r][c] - (*scale) cr[r] y[r][c] + res[r][c])
 // (res optional), with acc already scaled; grid (x, R), C % 4 == 0.

@@ -41,7 +41,13 @@ float* take_amax_ws(Carver& cv, int64_t R, int64_t C, int axis) {
 
 coda_status run_quant(const void* X, int64_t ldx, int64_t R, int64_t C, int axis, uint8_t* Q, int64_t ldq,
                       float* scale, float* amax, float* parts, hipStream_t s) {
-  if (R == 0 || C == 0) return CODA_OK;
+  const int64_t ns = axis == 1 ? R : C;   // one scale per row (axis 1) or per column (axis 0)
+  if (R == 0 || C == 0) {
+    // an empty contracted axis has amax 0, whose scale is 1 (no codes to scale)
+    if (ns == 0) return CODA_OK;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, scale, (int)ns, 1.0f);
+    return check_launch("quantize_e4m3: empty axis");
+  }
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if (axis == 1) {
     hipLaunchKernelGGL(amax_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, amax);
@@ -1060,6 +1066,7 @@ static coda_status swiglu_fwd_check(const coda_mat* x, const coda_mat* P, const 
   TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, K = x->cols;
+  if (K == 0) return fail(CODA_ERR_SHAPE, "x: the normalised rows are empty (K = 0)");
   if (!Wgu) return fail(CODA_ERR_NULL, "Wgu: NULL");
   const int64_t N = Wgu->w.cols;
   TRY(check_weight(Wgu, "Wgu", K, N, precision));
@@ -1149,6 +1156,7 @@ extern "C" coda_status coda_linear_qknorm_rope_fwd(const coda_mat* x, const coda
   TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, D = x->cols;
+  if (D == 0) return fail(CODA_ERR_SHAPE, "x: the normalised rows are empty (D = 0)");
   if (D % 128 != 0) return fail(CODA_ERR_SHAPE, "qknorm_rope: D must be a multiple of 128");
   if (!Wqkv) return fail(CODA_ERR_NULL, "Wqkv: NULL");
   TRY(check_weight(Wqkv, "Wqkv", D, 3 * D, precision));
@@ -1303,6 +1311,16 @@ static coda_status sum_partials_launch(const float* P, int nP, int K, float beta
   return check_launch("sum_partials");
 }
 
+// An empty token batch (M = 0) adds nothing to a gradient accumulator, so the
+// backward entry points only apply D = beta D (beta 0 clears D without
+// reading it, as the epilogues do) and launch no GEMM.
+static coda_status scale_accum(const coda_mat* D, float beta, hipStream_t s, const char* what) {
+  if (!present(D) || beta == 1.0f || D->rows == 0 || D->cols == 0) return CODA_OK;
+  hipLaunchKernelGGL(scale_f32_kernel, dim3((unsigned)((D->cols + 255) / 256), (unsigned)std::min<int64_t>(D->rows, 65535)),
+                     dim3(256), 0, s, static_cast<float*>(D->ptr), D->ld, (int)D->rows, (int)D->cols, beta);
+  return check_launch(what);
+}
+
 static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, const coda_mat* hgu, const coda_mat* r,
                                    const coda_mat* u, const coda_weight* Wgu, const coda_mat* Wunf, const coda_mat* gvec,
                                    const coda_mat* dres, const coda_mat* du, const coda_mat* dWgu, const coda_mat* dg,
@@ -1335,6 +1353,10 @@ static coda_status swiglu_bwd_impl(const coda_mat* dY, const coda_weight* Wd, co
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
+  if (M == 0) {
+    TRY(scale_accum(dWgu, beta, s, "swiglu_bwd: dW of no tokens"));
+    return scale_accum(dg, beta, s, "swiglu_bwd: dg of no tokens");
+  }
   void* dhp = present(dh_out) ? dh_out->ptr : dh;
   const int64_t lddh = present(dh_out) ? dh_out->ld : N2;
   // B1: da = dY Wd^T with dSwiGLU, r scale, T partials
@@ -1432,6 +1454,7 @@ extern "C" coda_status coda_linear_swiglu_bwd(const coda_mat* dY, const coda_wei
   int64_t M, D, F;
   TRY(swiglu_bwd_check(dY, Wd, saved_hgu, r, u, Wgu, Wgu_unfolded, g, dres, du, dWgu, dg, dh_gu_out, precision, &M,
                        &D, &F));
+  if (D == 0) return fail(CODA_ERR_SHAPE, "u: the normalised rows are empty (D = 0)");
   return swiglu_bwd_impl(dY, Wd, saved_hgu, r, u, Wgu, Wgu_unfolded, g, dres, du, dWgu, dg, beta, dh_gu_out,
                          precision, ws, ws_bytes, stream, M, D, F, false, nullptr);
 }
@@ -1479,6 +1502,7 @@ extern "C" coda_status coda_linear_rmsnorm_residual_bwd(const coda_mat* d_out, c
   float* part = sp.n > 1 ? cv.take<float>((size_t)sp.n * K * N) : nullptr;
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
+  if (M == 0) return scale_accum(dW, beta, s, "rmsnorm_residual_bwd: dW of no tokens");
   if (fp8) {
     if (present(da)) TRY(quant_act(q8.grow, d_out->ptr, d_out->ld, M, N, 1, s));
     TRY(quant_act(q8.xcol, a->ptr, a->ld, M, K, 0, s));
@@ -1536,7 +1560,13 @@ static coda_status qk_bwd_impl(const coda_mat* dq, const coda_mat* dk, const cod
   if (size_only) { *bytes = cv.off; return CODA_OK; }
   TRY(ws_check(cv, ws_bytes, ws));
   hipStream_t s = S(stream);
-  if (M > 0) {
+  if (M == 0) {
+    TRY(scale_accum(dW, beta, s, "qknorm_rope_bwd: dW of no tokens"));
+    TRY(scale_accum(dg, beta, s, "qknorm_rope_bwd: dg of no tokens"));
+    TRY(scale_accum(dgq, beta, s, "qknorm_rope_bwd: dgq of no tokens"));
+    return scale_accum(dgk, beta, s, "qknorm_rope_bwd: dgk of no tokens");
+  }
+  {
     hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(nblk), dim3(256), 0, s, static_cast<const uint16_t*>(dq->ptr),
                        static_cast<const uint16_t*>(dk->ptr), static_cast<const uint16_t*>(dv->ptr), dq->ld,
                        static_cast<const uint16_t*>(qk_pre->ptr), qk_pre->ld, static_cast<const uint16_t*>(v->ptr),
@@ -1598,6 +1628,7 @@ extern "C" coda_status coda_linear_qknorm_rope_bwd(const coda_mat* dq, const cod
   TRY(check_precision(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, D = x->cols;
+  if (D == 0) return fail(CODA_ERR_SHAPE, "x: the normalised rows are empty (D = 0)");
   if (D % 128 != 0) return fail(CODA_ERR_SHAPE, "D must be a multiple of 128");
   TRY(check_mat(dq, "dq", CODA_BF16, M, D));
   TRY(check_mat(dk, "dk", CODA_BF16, M, D));
@@ -1823,7 +1854,7 @@ extern "C" coda_status coda_linear_cross_entropy_bwd(const coda_mat* h, const co
   float* dh_acc;
   ce_bwd_layout(cv, M, D, V, vc, &scale, &G, &dh_acc);
   TRY(ws_check(cv, ws_bytes, ws));
-  if (M == 0) return CODA_OK;
+  if (M == 0) return scale_accum(dW, beta, S(stream), "cross_entropy_bwd: dW of no tokens");
   hipStream_t s = S(stream);
   const int64_t ldG = (vc + 7) / 8 * 8;
   hipLaunchKernelGGL(ce_scale_kernel, dim3(1), dim3(1), 0, s, static_cast<const int*>(n_valid->ptr), dloss, scale);
@@ -1915,6 +1946,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_fwd(
   if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(y, "y", CODA_BF16, -1, -1));
   const int64_t M = y->rows, D = y->cols;
+  if (D == 0) return fail(CODA_ERR_SHAPE, "y: the normalised rows are empty (D = 0)");
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
   const int64_t V = W->w.cols;
   TRY(check_weight(W, "W", D, V, precision));
@@ -2004,6 +2036,7 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
   if (precision != CODA_PREC_BF16) return fail(CODA_ERR_UNSUPPORTED, "cross_entropy: fp8 not compiled in this build");
   TRY(check_mat(y, "y", CODA_BF16, -1, -1));
   const int64_t M = y->rows, D = y->cols;
+  if (D == 0) return fail(CODA_ERR_SHAPE, "y: the normalised rows are empty (D = 0)");
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
   const int64_t V = W->w.cols;
   TRY(check_weight(W, "W", D, V, precision));
@@ -2024,7 +2057,10 @@ extern "C" coda_status coda_linear_rmsnorm_cross_entropy_bwd(
   uint16_t* G;
   nce_bwd_layout(cv, M, D, V, vc, &scale, &G, &Tp, &Tc, &dgp, &dy_acc);
   TRY(ws_check(cv, ws_bytes, ws));
-  if (M == 0) return CODA_OK;
+  if (M == 0) {
+    TRY(scale_accum(dW, beta, S(stream), "rmsnorm_cross_entropy_bwd: dW of no tokens"));
+    return scale_accum(dg, beta, S(stream), "rmsnorm_cross_entropy_bwd: dg of no tokens");
+  }
   hipStream_t s = S(stream);
   const int64_t ldG = (vc + 7) / 8 * 8;
   const int nT = (int)coda_partials_cols(V);
@@ -2112,6 +2148,7 @@ static coda_status map_fwd_check(const coda_mat* x, const coda_mat* P, const cod
   TRY(check_precision_fwd(precision));
   TRY(check_mat(x, "x", CODA_BF16, -1, -1));
   const int64_t M = x->rows, K = x->cols;
+  if (K == 0) return fail(CODA_ERR_SHAPE, "x: the normalised rows are empty (K = 0)");
   if (!W) return fail(CODA_ERR_NULL, "W: NULL");
   const int64_t N = W->w.cols;
   TRY(check_weight(W, "W", K, N, precision));
@@ -2146,6 +2183,7 @@ static coda_status map_bwd(const coda_mat* dY, const coda_weight* Wn, const coda
   TRY(check_precision(precision));
   TRY(check_mat(dY, "dY", CODA_BF16, -1, -1));
   const int64_t M = dY->rows, D = dY->cols;
+  if (D == 0) return fail(CODA_ERR_SHAPE, "u: the normalised rows are empty (D = 0)");
   if (!Wn || !W) return fail(CODA_ERR_NULL, "weights: NULL");
   const int64_t N = Wn->w.rows;
   TRY(check_weight(Wn, "Wn", N, D, precision));

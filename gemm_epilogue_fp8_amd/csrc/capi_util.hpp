@@ -49,7 +49,11 @@ coda_status check_mat(const coda_mat* m, const char* name, int dtype, int64_t ro
                       bool optional = false) {
   if (!present(m)) {
     if (optional) return CODA_OK;
-    return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
+    // a matrix with no elements needs no memory: its pointer may be NULL
+    // (it is then checked like any other and never dereferenced); a NULL
+    // descriptor of the wrong type (e.g. all zeros) counts as missing
+    if (m == nullptr || (m->rows != 0 && m->cols != 0) || m->dtype != dtype)
+      return fail(CODA_ERR_NULL, "%s: required pointer is NULL", name);
   }
   if (m->dtype != dtype) return fail(CODA_ERR_DTYPE, "%s: dtype %d, expected %d", name, m->dtype, dtype);
   if (m->rows < 0 || m->cols < 0) return fail(CODA_ERR_SHAPE, "%s: negative size", name);
@@ -58,7 +62,7 @@ coda_status check_mat(const coda_mat* m, const char* name, int dtype, int64_t ro
   if (cols >= 0 && m->cols != cols)
     return fail(CODA_ERR_SHAPE, "%s: %lld cols, expected %lld", name, (long long)m->cols, (long long)cols);
   if (reinterpret_cast<uintptr_t>(m->ptr) % 16 != 0) return fail(CODA_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
-  if (m->rows > 1) {
+  if (m->rows > 1 && m->cols > 0) {   // rows of no elements have no layout
     if (m->ld < m->cols) return fail(CODA_ERR_LAYOUT, "%s: ld %lld < cols %lld", name, (long long)m->ld, (long long)m->cols);
     const int v = vec_elems(dtype);
     if (m->cols % v != 0 || m->ld % v != 0)

@@ -38,6 +38,11 @@
  *    A matrix with more than one row needs a row stride (ld x element size)
  *    below 16 MiB: the kernels address a tile's rows by 32-bit offsets.
  *  - Results are bitwise deterministic: reductions run in a fixed order.
+ *  - Empty token batches (M = 0 rows of activations) are valid: a forward
+ *    call writes nothing, and a backward call applies D = beta D to its
+ *    fp32 gradient accumulators (beta 0 clears them without reading them)
+ *    and launches no GEMM.  A normalised row of width 0 (the K or D that an
+ *    RMSNorm divides by) has no root mean square: CODA_ERR_SHAPE.
  */
 #ifndef CODA_H_
 #define CODA_H_

@@ -463,3 +463,28 @@ def test_schedule_setting():
         assert L.coda_get_schedule() == _lib.SCHED_PINGPONG
     assert L.coda_get_schedule() == _lib.SCHED_CORESIDENT
     assert L.coda_set_schedule(_lib.SCHED_PINGPONG) == 0
+
+
+def test_empty_normalised_rows_and_null_empty_matrices():
+    """A normalised row of width 0 has no RMS: the RMSNorm entry points refuse
+    it before any HIP call.  An empty required matrix may carry a NULL
+    pointer, and a non-empty one may not."""
+    L = g.lib()
+    BF, F32 = _lib.CODA_BF16, _lib.CODA_F32
+    M, N = 16, 128
+    w = _lib.CodaWeight()
+    w.w = fake(BF, 0, N)
+    x0 = fake(BF, M, 0)
+    st = L.coda_linear_swiglu_fwd(C.byref(x0), None, C.byref(w), 1e-6, C.byref(fake(BF, M, N // 2)), None, None,
+                                  0, None, 0, None)
+    assert st == 3 and b"K = 0" in L.coda_last_error()
+    for fn in (L.coda_linear_sigmoid_fwd, L.coda_linear_gelu_fwd):
+        assert fn(C.byref(x0), None, C.byref(w), 1e-6, C.byref(fake(BF, M, N)), None, None, 0, None, 0, None) == 3
+    # a required input with rows but no pointer
+    w.w = fake(BF, 64, N)
+    st = L.coda_linear_sigmoid_fwd(C.byref(fake(BF, M, 64, ptr=None)), None, C.byref(w), 1e-6,
+                                   C.byref(fake(BF, M, N)), None, None, 0, None, 0, None)
+    assert st == 1
+    # M = 0 with NULL pointers passes validation (its sizes are still checked)
+    assert L.coda_linear_sigmoid_fwd(C.byref(fake(BF, 0, 64, ptr=None)), None, C.byref(w), 1e-6,
+                                     C.byref(fake(BF, 0, N + 8, ptr=None)), None, None, 0, None, 0, None) == 3

@@ -305,6 +305,92 @@ def _run_block(shape, seed, precision=coda.PREC_BF16):
     return P, {k: to_np(v) for k, v in f.items()}, {k: to_np(v) for k, v in b.items()}
 
 
+@pytest.mark.parametrize("precision", [coda.PREC_BF16, coda.PREC_FP8, coda.PREC_MXFP8])
+def test_block_empty_token_batch(precision):
+    """M = 0 tokens (0-element tensors, whose data pointers are NULL): the
+    forward writes nothing, and the backward leaves beta x each fp32 gradient
+    accumulator: beta 0 clears even NaN priors, beta 0.5 halves them."""
+    shape = ci.BlockShape(M=8, D=256, F=256, seq_len=16)
+    P = ci.block_inputs(shape, 5)
+    params = {k: (f32(v) if k in ("g1", "g2", "gq", "gk") else bf(v)) for k, v in P.items()}
+    blk = Block(params, shape.D, shape.F, seq_len=shape.seq_len, theta=shape.theta, eps=shape.eps,
+                precision=precision)
+    e = lambda *sh: torch.empty(sh, dtype=BF, device=DEV)
+    x, o, dY, dq, dk, dv = (e(0, shape.D) for _ in range(6))
+    f = blk.forward(x, o)
+    assert all(t.numel() == 0 for t in f.values()), {k: t.shape for k, t in f.items()}
+    for beta, fill in ((0.0, float("nan")), (0.5, 3.0)):
+        g = blk.alloc_backward(0, DEV)
+        for k in ("dWqkv", "dWo", "dWgu", "dWd", "dg1", "dg2", "dgq", "dgk"):
+            g[k].fill_(fill)
+        blk.backward(x, o, f, dY, dq, dk, dv, grads=g, beta=beta)
+        torch.cuda.synchronize()
+        for k in ("dWqkv", "dWo", "dWgu", "dWd", "dg1", "dg2", "dgq", "dgk"):
+            want = 0.0 if beta == 0.0 else beta * fill
+            assert bool((g[k] == want).all()), (k, beta)
+
+
+def test_empty_token_batch_other_layers():
+    """M = 0 through the sigmoid / GELU layers and both cross-entropy entry
+    points: the forward gives n_valid = 0 (loss 0 / 0), the backward beta x
+    the accumulators."""
+    D, N, V = 256, 256, 512
+    rng = np.random.default_rng(6)
+    Wt = coda.Weight(bf(rand_bf16(rng, D, N, std=D ** -0.5)))
+    Wn = coda.Weight(bf(rand_bf16(rng, N, D, std=N ** -0.5)))
+    Wu, g = bf(rand_bf16(rng, D, N)), f32(np.ones(D, np.float32))
+    e0 = lambda c, dt=BF: torch.empty((0, c), dtype=dt, device=DEV)
+    v0 = lambda dt=torch.float32: torch.empty(0, dtype=dt, device=DEV)
+    for fwd, bwd in ((coda.linear_sigmoid_fwd, coda.linear_sigmoid_bwd), (coda.linear_gelu_fwd, coda.linear_gelu_bwd)):
+        fwd(e0(D), Wt, 1e-6, e0(N), save_h=e0(N), r_out=v0())
+        dW, dg = torch.full((D, N), 2.0, device=DEV), torch.full((D,), 2.0, device=DEV)
+        bwd(e0(D), Wn, e0(N), v0(), e0(D), Wt, Wu, g, e0(D), e0(D), dW, dg, beta=0.5)
+        torch.cuda.synchronize()
+        assert bool((dW == 1.0).all()) and bool((dg == 1.0).all())
+    Wv = coda.Weight(bf(rand_bf16(rng, D, V, std=D ** -0.5)))
+    loss, nv, nb = (torch.full((1,), 7.0, device=DEV), torch.full((1,), 7, dtype=torch.int32, device=DEV),
+                    torch.full((1,), 7, dtype=torch.int32, device=DEV))
+    coda.linear_cross_entropy_fwd(e0(D), Wv, v0(torch.int32), loss, v0(), nv, n_bad=nb)
+    torch.cuda.synchronize()
+    assert nv.item() == 0 and nb.item() == 0 and math.isnan(loss.item())
+    dW = torch.full((D, V), float("nan"), device=DEV)
+    coda.linear_cross_entropy_bwd(e0(D), Wv, v0(torch.int32), v0(), nv, 1.0, e0(D), dW, beta=0.0)
+    torch.cuda.synchronize()
+    assert bool((dW == 0.0).all())
+    loss.fill_(7.0)
+    nv.fill_(7)
+    coda.linear_rmsnorm_cross_entropy_fwd(e0(D), Wv, 1e-6, v0(torch.int32), loss, v0(), nv, r_out=v0())
+    torch.cuda.synchronize()
+    assert nv.item() == 0 and math.isnan(loss.item())
+    dW, dg = torch.full((D, V), 4.0, device=DEV), torch.full((D,), 4.0, device=DEV)
+    coda.linear_rmsnorm_cross_entropy_bwd(e0(D), v0(), Wv, bf(rand_bf16(rng, D, V)), g, v0(torch.int32), v0(), nv,
+                                          1.0, e0(D), dW, dg, beta=0.5)
+    torch.cuda.synchronize()
+    assert bool((dW == 2.0).all()) and bool((dg == 2.0).all())
+
+
+def test_empty_contracted_axis():
+    """K = 0: E4M3 quantisation of [R, 0] gives unit scales (amax 0), and
+    residual layers whose contracted axis is empty return the residual
+    exactly, in bf16 and E4M3."""
+    R, N = 40, 64
+    rng = np.random.default_rng(7)
+    Q = torch.empty((R, 0), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.full((R,), float("nan"), device=DEV)
+    coda.quantize_e4m3(torch.empty((R, 0), dtype=BF, device=DEV), 1, Q, s)
+    torch.cuda.synchronize()
+    assert bool((s == 1.0).all())
+    z = bf(rand_bf16(rng, R, N))
+    for prec in (coda.PREC_BF16, coda.PREC_FP8):
+        W = coda.Weight(torch.empty((0, N), dtype=BF, device=DEV))
+        if prec == coda.PREC_FP8:
+            W.prepare_fp8()
+        out = torch.full((R, N), float("nan"), dtype=BF, device=DEV)
+        coda.linear_rmsnorm_residual_fwd(torch.empty((R, 0), dtype=BF, device=DEV), W, z, out, precision=prec)
+        torch.cuda.synchronize()
+        assert bool((out == z).all()), prec
+
+
 @pytest.mark.parametrize("shape,seed,sched", [(SMALL, 0, 0), (MEDIUM, 1, 0), (MEDIUM, 1, 1)])
 def test_block_forward_backward(shape, seed, sched):
     """sched 1 runs the gate/up GEMM under the co-resident schedule."""
