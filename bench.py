@@ -85,6 +85,7 @@ def parse():
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
     ap.add_argument("--no-h4096", action="store_true", help="skip the hidden-4096 block leg of the default run")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the block step")
     ap.add_argument("--no-coresident", action="store_true",
                     help="skip the block step under the co-resident gate/up schedule")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -389,6 +390,25 @@ def block_leg(name, precision, args, breakdown=True):
     ms = timed(lambda: step(f3_events), args.steps)
     f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
+    # The same step captured once as a HIP graph and replayed (the library
+    # launches on the caller's stream and allocates nothing, so every kernel
+    # of the step is captured; the workspaces were sized by the steps above).
+    graph_ms = None
+    if not getattr(args, "no_graph", False):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        graph_ms = timed(graph.replay, args.steps)
+        del graph
     # The same step with the gate/up GEMM + SwiGLU under the co-resident
     # schedule (two 128 x 256 workgroups a compute unit, one's epilogue
     # overlapping the other's matrix work), and that kernel's own time.
@@ -452,6 +472,7 @@ def block_leg(name, precision, args, breakdown=True):
         "workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}, MLP {cfg.F}, "
                     f"{cfg.heads}x128 heads, {M} tokens",
         "block_fwd_bwd_ms": round(ms, 4), "block_fwd_ms": round(fwd_ms, 4),
+        "block_fwd_bwd_graph_ms": None if graph_ms is None else round(graph_ms, 4),
         "tflops": round(tflops, 2), "pct_of_peak": round(100 * tflops / peak, 2),
         "unfused_baseline": unfused,
         "weight_prep_ms": round(prep_ms, 4), "weight_prep_cold_ms": round(prep_cold_ms, 3),
@@ -551,6 +572,7 @@ def main():
                    "seq_len": cfg.seq_len, "grad_accumulate_beta": 1.0},
         "block_fwd_bwd_ms": round(ms, 4),
         "block_fwd_ms": head["block_fwd_ms"],
+        "block_fwd_bwd_graph_ms": head["block_fwd_bwd_graph_ms"],
         "pct_of_peak": head["pct_of_peak"],
         "unfused_baseline": head["unfused_baseline"],
         "weight_prep_ms": head["weight_prep_ms"],

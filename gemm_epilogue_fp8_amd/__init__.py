@@ -179,14 +179,19 @@ def _stream():
 
 
 _WS = {}
+_WS_RETIRED = []
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
     """A per-device workspace buffer, grown on demand and reused by calls
-    that run in order on one stream."""
+    that run in order on one stream.  A buffer that is outgrown stays
+    allocated: a HIP graph captured while it was current keeps using its
+    address on every replay."""
     key = str(device)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
+        if buf is not None:
+            _WS_RETIRED.append(buf)
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
