@@ -9,6 +9,7 @@ import pytest
 import coda_inputs as ci
 from oracle import block as ob
 from oracle import numerics as nm
+from oracle import ops as oops
 from tests.helpers import (BF16_TOL, assert_bf16, assert_grad, rel_norm, to_dev, to_np, unpack_gu)
 
 torch = pytest.importorskip("torch")
@@ -519,6 +520,14 @@ def test_cross_entropy(M, D, V, chunk):
     assert_grad("dW", to_np(dW), Br["dW"])
     ignored = labels == -100
     assert np.all(to_np(dh)[ignored] == 0)
+    # against the plain definition: fp64 cross-entropy of z = h W and its
+    # analytic gradients (oracle/ops.py, pinned to torch's cross_entropy)
+    hh, WW = P["h"].astype(np.float64), P["W"].astype(np.float64)
+    loss_c, _, lse_c, nv_c, dz = oops.cross_entropy(hh @ WW, labels)
+    assert int(nv.item()) == nv_c and abs(loss.item() - loss_c) <= 1e-3 * abs(loss_c)
+    assert_grad("lse vs canonical", to_np(lse), lse_c)
+    assert rel_norm(to_np(dh), dz @ WW.T) <= 2e-2
+    assert rel_norm(to_np(dW) - prior, hh.T @ dz) <= 2e-2
 
 
 def run_rmsnorm_ce(y, g, W, labels, dres, chunk, partials, prior_dW=None, prior_dg=None, beta=0.0,
@@ -584,6 +593,13 @@ def test_rmsnorm_cross_entropy(M, D, V, chunk, use_partials):
     assert_bf16("dy", got["dy"], B["dy"])
     assert_grad("dW", got["dW"], B["dW"])
     assert_grad("dg", got["dg"], B["dg"])
+    # against the plain definition (fp64 RMSNorm -> matmul -> cross-entropy)
+    Cc = ob.norm_ce_canonical(y, g, W, labels, 1e-6, dres=dres)
+    assert abs(got["loss"] - Cc["loss"]) <= 1e-3 * abs(Cc["loss"])
+    assert_grad("lse vs canonical", got["lse"], Cc["lse"])
+    assert rel_norm(got["dy"], Cc["dy"]) <= 2e-2
+    assert rel_norm(got["dW"] - (beta * pW if use_partials else 0.0), Cc["dW"]) <= 2e-2
+    assert rel_norm(got["dg"] - (beta * pg if use_partials else 0.0), Cc["dg"]) <= 2e-2
 
 
 def test_cross_entropy_bad_label_and_empty():
