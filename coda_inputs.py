@@ -154,3 +154,20 @@ def fp32_prior(shape, seed: int, std: float = 1e-3) -> np.ndarray:
     """A seeded fp32 tensor used as the prior value of an accumulated gradient."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7777])))
     return _normal(rng, shape, std)
+
+
+def rolled_rows(seed: int, K: int, shifts) -> "RolledRows":
+    """Rows of a very long matrix without storing it on the host: one seeded
+    bf16 row of K values ~N(0,1), and row i is that row rotated left by
+    ``shifts[i]`` places (numpy.roll by -shift)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4242])))
+    return RolledRows(to_bf16_values(_normal(rng, (K,), 1.0)), tuple(int(s) for s in shifts))
+
+
+@dataclasses.dataclass(frozen=True)
+class RolledRows:
+    base: np.ndarray
+    shifts: tuple
+
+    def row(self, i: int) -> np.ndarray:
+        return np.roll(self.base, -self.shifts[i])

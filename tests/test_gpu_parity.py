@@ -63,6 +63,39 @@ def test_gemm_store_layouts(transA, transB, M, N, K):
     assert_bf16("D", to_np(D), ref)
 
 
+def test_gemm_largest_row_stride():
+    """The largest row stride the C ABI accepts (just under 16 MiB: bf16 K =
+    8388600), on K-contiguous operands of a 256-row tile, whose last row's
+    copy offset is then just under 4 GiB: A [256, K] and B [24, K] (the NT
+    form), fp32 output sampled at tile rows 0, 1, 127, 128, 254, 255 against
+    float64 dot products.  Rows are rotations of one seeded row, so the host
+    never holds the 4 GiB operand."""
+    K, M, N = 8388600, 256, 24
+    shifts_a = [7919 * m + 13 for m in range(M)]
+    shifts_b = [104729 * n + 5 for n in range(N)]
+    ra, rb = ci.rolled_rows(31, K, shifts_a), ci.rolled_rows(32, K, shifts_b)
+    A = torch.empty((M, K), dtype=BF, device=DEV)
+    B = torch.empty((N, K), dtype=BF, device=DEV)
+    a0, b0 = bf(ra.base), bf(rb.base)
+    for m in range(M):
+        A[m].copy_(torch.roll(a0, -shifts_a[m]))
+    for n in range(N):
+        B[n].copy_(torch.roll(b0, -shifts_b[n]))
+    D = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    coda.gemm_epi([(coda.EPI_ACCUM_F32, 0, 0.0)], A, 0, B, 1, D)
+    torch.cuda.synchronize()
+    assert torch.equal(A[255].cpu().float(), torch.from_numpy(ra.row(255)))   # the upload matches the oracle's rows
+    got = to_np(D)
+    Bh = np.stack([rb.row(n) for n in range(N)]).astype(np.float64)
+    Bsq = Bh * Bh
+    for m in (0, 1, 127, 128, 254, 255):
+        a = ra.row(m).astype(np.float64)
+        ref, scale = Bh @ a, np.sqrt(Bsq @ (a * a))
+        assert np.all(np.abs(got[m] - ref) <= 1e-3 * scale), (m, got[m], ref)
+    del A, B
+    torch.cuda.empty_cache()
+
+
 def test_gemm_accum_f32_beta():
     rng = np.random.default_rng(5)
     M, N, K = 264, 136, 330
