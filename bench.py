@@ -363,8 +363,8 @@ def block_leg(name, precision, args, breakdown=True):
 
     def step(record=None):
         """One step; with a list, the gate/up kernel's events are appended to it."""
-        for name, fn in calls:
-            if record is not None and name.startswith("F3"):
+        for call, fn in calls:
+            if record is not None and call.startswith("F3"):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 fn()
@@ -434,12 +434,12 @@ def block_leg(name, precision, args, breakdown=True):
     if breakdown:   # per-call breakdown (one extra, untimed-for-the-metric step)
         evs = []
         torch.cuda.synchronize()
-        for name, fn in calls:
+        for call, fn in calls:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
             b.record()
-            evs.append((name, a, b))
+            evs.append((call, a, b))
         torch.cuda.synchronize()
         bd = {n: round(a.elapsed_time(b), 4) for n, a, b in evs}
 
