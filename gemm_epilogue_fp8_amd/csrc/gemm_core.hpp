@@ -640,10 +640,15 @@ __device__ __forceinline__ void mainloop_solo(const GemmArgs& g, char* smem, Acc
       TileMN<Cfg, Cfg::BN>::issue(B, ldb_b, kt * Cfg::BK, g.K, n0, g.N, Bs, w, lane);
   };
 
+  // No branches in the loop: stages past K are copied as zeros (every chunk
+  // out of the buffer range) and the loop runs over an even number of
+  // stages, so the reads, copies and MFMAs of a step form one block that
+  // the scheduler can interleave.
+  const int nk2 = (nk + 1) & ~1;
   issue_stage(0, 0);
-  if (nk > 1) issue_stage(1, 1);
+  issue_stage(1, 1);
   Frags<Cfg> f[2][SUB];
-  if (nk > 1) wait_vmcnt<LPS>(); else wait_vmcnt<0>();
+  wait_vmcnt<LPS>();
   phase_barrier();                         // stage 0 has landed for every wave
 #pragma unroll
   for (int s = 0; s < SUB; ++s) load_frags<Cfg>(smem, smem + Cfg::BM * kRowBytes, s, f[0][s], wm0, wn0, lane);
@@ -651,23 +656,40 @@ __device__ __forceinline__ void mainloop_solo(const GemmArgs& g, char* smem, Acc
   auto step = [&](int kt, Frags<Cfg>(&cur)[SUB], Frags<Cfg>(&nxt)[SUB]) {
     wait_vmcnt<0>();                       // this wave's copies of stage kt + 1 have landed
     wait_lgkmcnt0();                       // cur (stage kt) is in registers
-    // every wave's copies of stage kt + 1 have landed and every wave has read
-    // stage kt, so the slot of stage kt - 1 is free for stage kt + 2
+    // every wave's copies of stage kt + 1 have landed and every wave has
+    // read stage kt, so the slot of stage kt - 1 is free for stage kt + 2
     phase_barrier();
-    if (kt + 2 < nk) issue_stage(kt + 2, nx == 2 ? 0 : nx + 1);
-    if (kt + 1 < nk) {
-      const char* S1 = smem + nx * Cfg::STAGE_BYTES;
+    // the fragment reads go ahead of the copies: the compiler waits for
+    // every copy in flight before a transposed LDS read, so a copy issued
+    // ahead of them would be waited for at once
+    const char* S1 = smem + nx * Cfg::STAGE_BYTES;
 #pragma unroll
-      for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, nxt[s], wm0, wn0, lane);
-    }
+    for (int s = 0; s < SUB; ++s) load_frags<Cfg>(S1, S1 + Cfg::BM * kRowBytes, s, nxt[s], wm0, wn0, lane);
+    issue_stage(kt + 2, nx == 2 ? 0 : nx + 1);
 #pragma unroll
     for (int s = 0; s < SUB; ++s) mma_frags<Cfg>(cur[s], acc);
+    // order: the DS reads (0x100) and the copies (0x020, which write LDS and
+    // so stay behind the reads) go out within the first MFMAs (0x008), so
+    // the copies have the rest of the step to land
+    constexpr int NMMA = SUB * Cfg::TM * Cfg::TN;
+    constexpr int NRD = SUB * (Cfg::TM + (Cfg::B_KC ? 1 : 2) * Cfg::TN);
+    static_assert(NMMA > 3, "MFMAs to hide the reads and copies behind");
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD - NRD / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMMA - 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
     nx = nx == 2 ? 0 : nx + 1;
   };
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = 0; kt < nk2; kt += 2) {
     step(kt, f[0], f[1]);
-    if (kt + 1 < nk) step(kt + 1, f[1], f[0]);
+    step(kt + 1, f[1], f[0]);
   }
+  wait_vmcnt<0>();                         // the zero stages past the end have landed too
+  wait_lgkmcnt0();
   phase_barrier();                         // every wave is done reading LDS before the epilogue reuses it
 }
 
