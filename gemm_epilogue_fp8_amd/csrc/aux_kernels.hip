@@ -354,19 +354,6 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
   return (uint32_t)w;
 }
 
-__global__ void amax_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, float* amax) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (r >= R) return;
-  float m = 0.0f;
-  for (int c = lane * 8; c < C; c += 512) {
-    uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
-    m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, m))));
-  }
-  m = wave_max(m);
-  if (lane == 0) amax[r] = m;
-}
-
 __global__ void amax_cols_partial_kernel(const uint16_t* X, int64_t ld, int R, int C, int rows_per_block,
                                          float* part) {
   // thread owns 2 columns; block covers 512 columns x rows_per_block rows
@@ -391,17 +378,25 @@ __global__ void amax_cols_finish_kernel(const float* part, int nparts, int C, fl
   amax[c] = m;
 }
 
-__global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
-                                  uint8_t* Q, int64_t ldq, float* scale) {
+__global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                  float* scale) {
+  // one wave a row: the row's amax, then its codes; the second read of the
+  // row comes from cache, not from a second pass over the whole matrix
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (r >= R) return;
-  float a = amax[r];
+  const uint16_t* x = X + (int64_t)r * ld;
+  float m = 0.0f;
+  for (int c = lane * 8; c < C; c += 512) {
+    uint4 w = *reinterpret_cast<const uint4*>(x + c);
+    m = absmax_bf2(w.x, absmax_bf2(w.y, absmax_bf2(w.z, absmax_bf2(w.w, m))));
+  }
+  float a = wave_max(m);
   if (!(a > 0.0f)) a = 448.0f;
   const float mult = 448.0f / a;
   if (lane == 0) scale[r] = a / 448.0f;
   for (int c = lane * 8; c < C; c += 512) {
-    uint4 w = *reinterpret_cast<const uint4*>(X + (int64_t)r * ld + c);
+    uint4 w = *reinterpret_cast<const uint4*>(x + c);
     uint32_t lo = cvt4_e4m3(bf_lo(w.x) * mult, bf_hi(w.x) * mult, bf_lo(w.y) * mult, bf_hi(w.y) * mult);
     uint32_t hi = cvt4_e4m3(bf_lo(w.z) * mult, bf_hi(w.z) * mult, bf_lo(w.w) * mult, bf_hi(w.w) * mult);
     *reinterpret_cast<uint2*>(Q + (int64_t)r * ldq + c) = uint2{lo, hi};

@@ -68,15 +68,15 @@ __global__ void norm_corr_finish_kernel(const float* acc, int64_t lda, const uin
                                         const float* scale, const uint16_t* res, int64_t ldr, uint16_t* out,
                                         int64_t ldo, int R, int C);
 // E4M3 quantisation with amax over the contracted axis.
-//   axis 1: Q[r, c] with one scale per row  r  (Q keeps the [R, C] layout)
+//   axis 1: Q[r, c] with one scale per row  r  (Q keeps the [R, C] layout),
+//           amax and codes in one kernel (a wave a row)
 //   axis 0: Q^T[c, r] with one scale per column c (Q written transposed, so the
 //           GEMM's contracted axis is contiguous)
-__global__ void amax_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, float* amax);
 __global__ void amax_cols_partial_kernel(const uint16_t* X, int64_t ld, int R, int C, int rows_per_block,
                                          float* part);
 __global__ void amax_cols_finish_kernel(const float* part, int nparts, int C, float* amax);
-__global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
-                                  uint8_t* Q, int64_t ldq, float* scale);
+__global__ void quant_rows_kernel(const uint16_t* X, int64_t ld, int R, int C, uint8_t* Q, int64_t ldq,
+                                  float* scale);
 __global__ void quant_cols_t_kernel(const uint16_t* X, int64_t ld, int R, int C, const float* amax,
                                     uint8_t* QT, int64_t ldq, float* scale);
 // MXFP8 quantisation (E4M3 elements, one E8M0 scale per 32 values of the

@@ -50,8 +50,7 @@ coda_status run_quant(const void* X, int64_t ldx, int64_t R, int64_t C, int axis
   }
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if (axis == 1) {
-    hipLaunchKernelGGL(amax_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, amax);
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, amax, Q, ldq, scale);
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, x, ldx, (int)R, (int)C, Q, ldq, scale);
   } else {
     const int rpb = 256;
     const int nparts = (int)((R + rpb - 1) / rpb);
