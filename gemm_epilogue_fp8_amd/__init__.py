@@ -190,9 +190,11 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     key = str(device)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
+        size = max(nbytes, 1 << 20)
         if buf is not None:
             _WS_RETIRED.append(buf)
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            size = max(size, 2 * buf.numel())   # doubling: the retired buffers add up to less than the live one
+        buf = torch.empty(size, dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
 
