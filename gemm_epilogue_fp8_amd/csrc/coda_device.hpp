@@ -20,6 +20,16 @@ namespace coda {
 constexpr uint32_t kOobOffset = 0xFFFFFFF0u;
 constexpr uint32_t kMaxRecords = 0xFFFFFFE0u;
 
+// The lane index, computed at the point of use by an instruction pair the
+// compiler may not move or merge (volatile asm, no memory access).  Values
+// derived from it inside a loop are then recomputed there instead of being
+// held in a register across the loop (or spilled, when registers run out).
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   uint32_t n = bytes > kMaxRecords ? kMaxRecords : (uint32_t)bytes;
   // dword3 0x00020000: raw (untyped) buffer access on the gfx9 family
