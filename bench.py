@@ -82,6 +82,7 @@ def parse():
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
     ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
+    ap.add_argument("--no-small", action="store_true", help="skip the small SwiGLU layer's latency leg")
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
     ap.add_argument("--no-h4096", action="store_true", help="skip the hidden-4096 block leg of the default run")
@@ -105,6 +106,40 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 3}))
+
+
+def small_layer_leg(warmup=20, calls=200):
+    """The small SwiGLU layer (x [256, 512], gate and up weights [512, 1024]
+    each, RMSNorm over x folded in): one linear_swiglu_fwd call, r computed
+    inside the call.  At 0.54 GFLOP it is far below the ridge point, so its
+    figure is latency: median and minimum of per-call HIP events."""
+    import numpy as np
+    import torch
+    import coda_inputs as ci
+    import gemm_epilogue_fp8_amd as coda
+
+    dev = "cuda:0"
+    shape = ci.CFG1
+    P = ci.swiglu_inputs(shape, ci.SEEDS["cfg1"])
+    to = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    x = to(P["x"], torch.bfloat16)
+    Wgu = torch.empty((shape.K, 2 * shape.F), dtype=torch.bfloat16, device=dev)
+    coda.pack_gate_up(to(P["Wg"], torch.bfloat16), to(P["Wu"], torch.bfloat16), to(P["g"], torch.float32), Wgu)
+    out = torch.empty((shape.M, shape.F), dtype=torch.bfloat16, device=dev)
+    fn = lambda: coda.linear_swiglu_fwd(x, Wgu, shape.eps, out)
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"workload": f"SwiGLU layer, x [{shape.M}, {shape.K}], gate/up [{shape.K}, {shape.F}] each, bf16",
+            "gflop": round(2 * shape.M * 2 * shape.F * shape.K / 1e9, 3),
+            "us_median": round(t[len(t) // 2], 2), "us_min": round(t[0], 2)}
 
 
 def mx_leg(warmup, steps):
@@ -387,7 +422,18 @@ def block_leg(name, precision, args, breakdown=True):
 
     for _ in range(args.warmup):
         step()
-    ms = timed(lambda: step(f3_events), args.steps)
+    # an event at the start of each timed step gives K - 1 per-step times
+    # (median and minimum beside the mean)
+    starts = []
+
+    def step_marked():
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        starts.append(ev)
+        step(f3_events)
+
+    ms = timed(step_marked, args.steps)
+    per_step = sorted(a.elapsed_time(b) for a, b in zip(starts[:-1], starts[1:]))
     f3_ms = sum(a.elapsed_time(b) for a, b in f3_events) / len(f3_events)
     fwd_ms = timed(lambda: [fn() for n, fn in calls[:5]], max(1, args.steps // 2))
     # The same step captured once as a HIP graph and replayed (the library
@@ -472,6 +518,8 @@ def block_leg(name, precision, args, breakdown=True):
         "workload": f"LLaMA-style non-attention block forward+backward, hidden {cfg.D}, MLP {cfg.F}, "
                     f"{cfg.heads}x128 heads, {M} tokens",
         "block_fwd_bwd_ms": round(ms, 4), "block_fwd_ms": round(fwd_ms, 4),
+        "step_ms_median": round(per_step[len(per_step) // 2], 4) if per_step else None,
+        "step_ms_min": round(per_step[0], 4) if per_step else None,
         "block_fwd_bwd_graph_ms": None if graph_ms is None else round(graph_ms, 4),
         "tflops": round(tflops, 2), "pct_of_peak": round(100 * tflops / peak, 2),
         "unfused_baseline": unfused,
@@ -549,6 +597,7 @@ def main():
         del params
         torch.cuda.empty_cache()
     mx = None if args.no_mx else mx_leg(max(1, args.warmup), max(3, args.steps // 2))
+    small = None if args.no_small else small_layer_leg()
     ce = None if args.no_ce else ce_leg(1, max(2, args.steps // 5))
     peak = PEAK_TFLOPS[precision]
     mloop = None if args.no_mfma_loop else mfma_loop_leg(f3_tflops)
@@ -572,6 +621,8 @@ def main():
                    "seq_len": cfg.seq_len, "grad_accumulate_beta": 1.0},
         "block_fwd_bwd_ms": round(ms, 4),
         "block_fwd_ms": head["block_fwd_ms"],
+        "step_ms_median": head["step_ms_median"],
+        "step_ms_min": head["step_ms_min"],
         "block_fwd_bwd_graph_ms": head["block_fwd_bwd_graph_ms"],
         "pct_of_peak": head["pct_of_peak"],
         "unfused_baseline": head["unfused_baseline"],
@@ -588,6 +639,7 @@ def main():
         "mxfp6_e2m3_block_forward": small_fwd.get("mxfp6_e2m3_block_forward"),
         "cross_entropy": ce,
         "mfma_loop": mloop,
+        "small_swiglu_layer": small,
     }
     print(json.dumps(out))
 
