@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the CPU-oracle sample (0 = all)")
     ap.add_argument("--no-mx", action="store_true", help="skip the block-scaled (MXFP8) GEMM leg")
     ap.add_argument("--no-small", action="store_true", help="skip the small SwiGLU layer's latency leg")
+    ap.add_argument("--ce-only", action="store_true",
+                    help="run only the linear + cross-entropy leg and print its JSON object (for per-kernel counters)")
     ap.add_argument("--no-ce", action="store_true", help="skip the linear + cross-entropy leg")
     ap.add_argument("--no-mfma-loop", action="store_true", help="skip the MFMA-only achievable-rate leg")
     ap.add_argument("--no-h4096", action="store_true", help="skip the hidden-4096 block leg of the default run")
@@ -546,6 +548,9 @@ def main():
         print(f"bench.py runs on one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
               f"run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.ce_only:
+        print(json.dumps({"cross_entropy": ce_leg(1, max(2, args.steps // 5))}))
+        return
     import coda_inputs as ci
     cfg = {"cfg2": ci.CFG2, "cfg3": ci.CFG3, "cfg5": ci.CFG5}[args.config]
     seed = ci.SEEDS[args.config]
