@@ -522,7 +522,9 @@ def test_block_deterministic():
 
 
 # ------------------------------------------------------------------ cross-entropy
-@pytest.mark.parametrize("M,D,V,chunk", [(300, 256, 1000, 0), (257, 128, 777 + 7, 100)])
+@pytest.mark.parametrize("M,D,V,chunk", [(300, 256, 1000, 0), (257, 128, 777 + 7, 100),
+                                         # bound 1024 columns: slices of 1024, 1024 and a ragged 56
+                                         (256, 128, 2104, 125)])
 def test_cross_entropy(M, D, V, chunk):
     V = V - V % 8
     shape = ci.CEShape(M=M, D=D, V=V)
