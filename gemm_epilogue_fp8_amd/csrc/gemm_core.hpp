@@ -159,75 +159,23 @@ struct TileKC {
 
   __device__ __forceinline__ static void issue(const char* base, int64_t ld_bytes, int row0, int nrows,
                                                int64_t kbyte0, int64_t kbytes, char* lds, int w, int lane) {
-    if constexpr (Cfg::MX && Cfg::FP6) {
-      issue_lean(base, ld_bytes, row0, nrows, kbyte0, kbytes, lds, w, lane);
-    } else {
-      // the block-scaled mainloops (which also hold scale words) derive the
-      // per-instruction offsets at each issue from the lane index instead of
-      // holding them through the K loop: no spill, and 1.6% off the MXFP8
-      // and MXFP4 GEMMs against the one-offset copy below
-      if constexpr (Cfg::MX) lane = lane_here();
-      const char* p = base + (int64_t)row0 * ld_bytes + kbyte0;
-      const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld_bytes + (uint64_t)(kbytes - kbyte0);
-      const auto rs = make_rsrc(p, rem);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int q = NI * w + i;                        // 16 rows per instruction; wave w: rows [R/4 w, R/4 (w+1))
-        const int row = 16 * q + (lane >> 2);
-        const int chunk = (lane & 3) ^ kc_swz(row);      // the chunk that lives at this slot
-        const bool ok = (row0 + row < nrows) && (kbyte0 + chunk * 16 < kbytes);
-        const uint32_t off = ok ? (uint32_t)(row * ld_bytes + chunk * 16) : kOobOffset;
-        raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)off, 0, 0, 0);
-      }
-    }
-  }
-
-  // The same copy with one lane offset for every instruction: a lane reads
-  // row lane / 4 of a 16-row group and the chunk that lives at its slot,
-  // which does not depend on the group.  The group's first row moves into
-  // the buffer resource (base and record count, scalar arithmetic), whose
-  // range check turns rows past the matrix into zeros; K-tail chunks get the
-  // out-of-range offset.  One vector register instead of one per
-  // instruction, used by the FP6 mainloop; elsewhere the per-instruction
-  // offsets measured 3.5% faster.  A stage whose rows and K chunks all exist (every stage of
-  // an interior tile) takes one resource and moves the 16-row group step
-  // into the scalar offset: 2.5% off the MXFP8 GEMM at M 4096, K 28672,
-  // N 8192 (the same path is 6% slower than per-instruction offsets for
-  // per-row-scaled E4M3, so those keep theirs).
-  __device__ __forceinline__ static void issue_lean(const char* base, int64_t ld_bytes, int row0, int nrows,
-                                                    int64_t kbyte0, int64_t kbytes, char* lds, int w, int lane) {
-    const int rl = lane >> 2;
-    const int chunk = (lane & 3) ^ ((rl >> 2) & 3);    // = the chunk of row 16 q + rl at this slot, any q
-    if (row0 + R <= nrows && kbyte0 + kRowBytes <= kbytes) {
-      // every row and chunk of the stage exists: one resource for the
-      // stage, the 16-row group step in the scalar offset
-      const uint32_t v = (uint32_t)(rl * ld_bytes + chunk * 16);
-      const int64_t rem = (int64_t)(nrows - row0 - 1) * ld_bytes + (kbytes - kbyte0);
-      const auto rs = make_rsrc(base + (int64_t)row0 * ld_bytes + kbyte0, (uint64_t)rem);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int q = NI * w + i;
-        raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)v, (int)(16 * q * ld_bytes), 0, 0);
-      }
-      return;
-    }
-    // an edge stage (ragged rows or the K tail): for E4M3 and E2M1 operands
-    // the lane's chunk is derived here again rather than kept live through
-    // the K loop, where it would exceed the register budget (a spill whose
-    // reload waits for every copy in flight: MXFP4 GEMM 8% slower); the FP6
-    // loop has the register room and runs 2% faster keeping it
-    const int ln = Cfg::FP6 ? lane : lane_here();
-    const int erl = ln >> 2;
-    const int echunk = (ln & 3) ^ ((erl >> 2) & 3);
-    const uint32_t voff = (kbyte0 + echunk * 16 < kbytes) ? (uint32_t)(erl * ld_bytes + echunk * 16) : kOobOffset;
+    // the block-scaled mainloops (which also hold scale words) derive the
+    // per-instruction offsets at each issue from the lane index instead of
+    // holding them through the K loop: no spill, and faster than one lane
+    // offset for all instructions with the group step in the buffer
+    // resource (MXFP8 and MXFP4 GEMMs 1.6%, MXFP6 4.5%)
+    if constexpr (Cfg::MX) lane = lane_here();
+    const char* p = base + (int64_t)row0 * ld_bytes + kbyte0;
+    const uint64_t rem = (uint64_t)(nrows - row0 - 1) * (uint64_t)ld_bytes + (uint64_t)(kbytes - kbyte0);
+    const auto rs = make_rsrc(p, rem);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int q = NI * w + i;
-      const int r0 = row0 + 16 * q;
-      // bytes from the group's first row to the end of the last row's K range
-      const int64_t rem = (int64_t)(nrows - r0 - 1) * ld_bytes + (kbytes - kbyte0);
-      const auto rs = make_rsrc(base + (int64_t)r0 * ld_bytes + kbyte0, rem > 0 ? (uint64_t)rem : 0);
-      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)voff, 0, 0, 0);
+      const int q = NI * w + i;                        // 16 rows per instruction; wave w: rows [R/4 w, R/4 (w+1))
+      const int row = 16 * q + (lane >> 2);
+      const int chunk = (lane & 3) ^ kc_swz(row);      // the chunk that lives at this slot
+      const bool ok = (row0 + row < nrows) && (kbyte0 + chunk * 16 < kbytes);
+      const uint32_t off = ok ? (uint32_t)(row * ld_bytes + chunk * 16) : kOobOffset;
+      raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + q * 1024), 16, (int)off, 0, 0, 0);
     }
   }
 };
